@@ -1,0 +1,293 @@
+"""Seeded synthetic inputs for the CSA2 read path.
+
+This module only makes inputs: random draws, the write-side encoders that store them in
+the cache formats (bf16, E4M3, E2M1 with an E4M3 scale per 16 channels), and planted
+high-affinity positions. It holds none of the read path's arithmetic (no decoding, no
+scoring, no selection, no attention) and is imported by the tests, the benchmark and
+users who want the same workloads; the oracle never imports it.
+
+Every draw comes from a torch.Generator seeded from (seed, tensor name, sequence) on the
+device that will hold the tensor, so a workload is reproducible on a given device type.
+Small workloads are drawn on the host; large ones on the GPU and copied to the host only
+for the sequences a check samples.
+
+Workloads (sizes are those of the decode and prefill settings the pages describe:
+64 heads x 512 main queries, 32 x 128 indexer queries, Top-512, SWA-128, 8-position
+blocks, 2,048 pool blocks):
+  tiny_decode_4k    1 query, 4,096 entries, Full only, 16 planted positions.
+  decode_32k        16 queries x 32,768 entries, Full only, 64 planted per query.
+  decode_256k       32 queries x 262,144 entries; Full (+pool), Reindex, 3 x Reuse.
+  prefill_128k_m2   4,096 causal queries over one sequence of 131,072 entries at
+                    compression ratio 2 (entry e covers source tokens 2e and 2e+1 and is
+                    visible from token p when 2e+1 <= p); Full only.
+  decode_1m         64 queries x 1,048,576 entries; Full (+pool), Reindex, 3 x Reuse;
+                    64 needles per query at evenly spaced positions.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+N_HEADS, HEAD_DIM = 64, 512
+IDX_HEADS, IDX_DIM = 32, 128
+TOPK, WINDOW = 512, 128
+BLOCK, POOL_BLOCKS = 8, 2048
+SOFTMAX_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+PLANT_SHIFT = 3.0
+
+DECODE_LAYERS = ("full", "reindex", "reuse", "reuse", "reuse")
+
+
+@dataclass
+class LayerInputs:
+    mode: str                       # "full", "reindex" or "reuse"
+    q: torch.Tensor                 # bf16 [n_q, 64, 512]
+    window_kv: torch.Tensor         # uint8 [rows, 512] E4M3
+    swa_start: torch.Tensor         # int64 [n_q]
+    n_swa: torch.Tensor             # int32 [n_q]
+    q_idx: torch.Tensor | None = None   # bf16 [n_q, 32, 128]
+    w: torch.Tensor | None = None       # float32 [n_q, 32]
+
+
+@dataclass
+class Workload:
+    name: str
+    n_q: int
+    n_ctx: int                      # largest visible count
+    kv_start: torch.Tensor          # int64 [n_q]
+    n_visible: torch.Tensor         # int32 [n_q]
+    k_cache: torch.Tensor           # uint8 [E, 128] E4M3
+    kv_fp4: torch.Tensor            # uint8 [E, 256] two E2M1 codes per byte
+    kv_scale: torch.Tensor          # uint8 [E, 32] E4M3
+    layers: list = field(default_factory=list)
+    with_pool: bool = False
+    planted: torch.Tensor | None = None  # int64 [n_q, n_plant] positions (or None)
+    softmax_scale: float = SOFTMAX_SCALE
+
+    @property
+    def n_entries(self) -> int:
+        return int(self.k_cache.shape[0])
+
+
+# ----------------------------------------------------------------------------- encoders
+
+def to_bf16(x: torch.Tensor) -> torch.Tensor:
+    """Round to bfloat16 (nearest even)."""
+    return x.to(torch.bfloat16)
+
+
+def encode_e4m3(x: torch.Tensor) -> torch.Tensor:
+    """Round to OCP E4M3FN (nearest even, saturating at +-448); returns the bytes."""
+    return x.float().clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _e4m3_bytes_to_float(b: torch.Tensor) -> torch.Tensor:
+    return b.view(torch.float8_e4m3fn).float()
+
+
+def encode_fp4_rows(x: torch.Tensor):
+    """Encode rows of 512 values as E2M1 codes with one E4M3 scale per 16 channels.
+
+    Per group of 16: scale = E4M3(amax / 6); each value x/scale is rounded to the E2M1
+    grid {0, .5, 1, 1.5, 2, 3, 4, 6} (nearest, ties to the even code, saturating at 6).
+    A zero scale gives zero codes. Codes 2m and 2m+1 share byte m, low nibble first.
+    Returns (payload uint8 [..., 256], scales uint8 [..., 32]).
+    """
+    x = x.float()
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // 16, 16)
+    amax = g.abs().amax(dim=-1)
+    s_code = encode_e4m3(amax / 6.0)
+    s = _e4m3_bytes_to_float(s_code)
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    a = (g / safe.unsqueeze(-1)).abs()
+    code = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8) + (a > 1.25).to(torch.uint8)
+            + (a >= 1.75).to(torch.uint8) + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
+            + (a > 5.0).to(torch.uint8))
+    code = torch.where((s > 0).unsqueeze(-1), code, torch.zeros_like(code))
+    sign = ((g < 0) & (code > 0)).to(torch.uint8) << 3
+    code = (code | sign).reshape(x.shape)
+    payload = code[..., 0::2] | (code[..., 1::2] << 4)
+    return payload.contiguous(), s_code.contiguous()
+
+
+# ----------------------------------------------------------------------------- random draws
+
+def _seed(seed: int, *names) -> int:
+    h = hashlib.sha256(repr((seed,) + tuple(names)).encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def _gen(device, seed, *names) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(seed, *names))
+    return g
+
+
+def _randn(shape, device, seed, *names):
+    return torch.randn(shape, generator=_gen(device, seed, *names), device=device,
+                       dtype=torch.float32)
+
+
+def _rand(shape, device, seed, *names):
+    return torch.rand(shape, generator=_gen(device, seed, *names), device=device,
+                      dtype=torch.float32)
+
+
+def _unit(v: torch.Tensor) -> torch.Tensor:
+    return v / v.norm().clamp_min(1e-30)
+
+
+def _make_layer(mode, n_q, device, seed, li, window_rows=None, swa_start=None, n_swa=None):
+    q = to_bf16(_randn((n_q, N_HEADS, HEAD_DIM), device, seed, "q_main", li))
+    if window_rows is None:
+        window_rows = n_q * WINDOW
+        swa_start = torch.arange(n_q, dtype=torch.int64, device=device) * WINDOW
+        n_swa = torch.full((n_q,), WINDOW, dtype=torch.int32, device=device)
+    window_kv = encode_e4m3(_randn((window_rows, HEAD_DIM), device, seed, "swa", li))
+    layer = LayerInputs(mode=mode, q=q, window_kv=window_kv, swa_start=swa_start, n_swa=n_swa)
+    if mode in ("full", "reindex"):
+        layer.q_idx = to_bf16(_randn((n_q, IDX_HEADS, IDX_DIM), device, seed, "q_idx", li))
+        layer.w = _rand((n_q, IDX_HEADS), device, seed, "w_idx", li)
+    return layer
+
+
+def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, plant_pos,
+                    full_layer: LayerInputs):
+    """Draw the indexer-K and latent rows of every sequence, planting at plant_pos."""
+    k_cache = torch.empty((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
+    kv_fp4 = torch.empty((n_entries, HEAD_DIM // 2), dtype=torch.uint8, device=device)
+    kv_scale = torch.empty((n_entries, HEAD_DIM // 16), dtype=torch.uint8, device=device)
+    starts = kv_start.tolist()
+    counts = n_visible.tolist()
+    shared = len(set(starts)) == 1 and n_q > 1
+    seqs = [(0, starts[0], max(counts))] if shared else list(zip(range(n_q), starts, counts))
+    for t, start, n in seqs:
+        if n <= 0:
+            continue
+        k = _randn((n, IDX_DIM), device, seed, "k_idx", t)
+        lat = _randn((n, HEAD_DIM), device, seed, "latent", t)
+        if plant_pos is not None and not shared:
+            pos = plant_pos[t]
+            pos = pos[pos < n]
+            qi = full_layer.q_idx[t].float()
+            u = _unit((full_layer.w[t].float()[:, None] * qi).sum(0))
+            v = _unit(full_layer.q[t].float().sum(0))
+            k[pos] += PLANT_SHIFT * u
+            lat[pos] += PLANT_SHIFT * v
+        k_cache[start:start + n] = encode_e4m3(k)
+        p, s = encode_fp4_rows(lat)
+        kv_fp4[start:start + n] = p
+        kv_scale[start:start + n] = s
+    return k_cache, kv_fp4, kv_scale
+
+
+def make_decode(name, n_q, n_ctx, layers, with_pool, n_plant, needles="random",
+                device="cpu", seed=0, n_visible=None, kv_gap=0):
+    """Decode batch: every query owns a sequence of n_visible[t] entries (default n_ctx),
+    laid out one after the other with kv_gap spare rows between them."""
+    if n_visible is None:
+        n_visible = [n_ctx] * n_q
+    n_visible_t = torch.tensor(n_visible, dtype=torch.int32)
+    stride = [int(v) + kv_gap for v in n_visible]
+    starts = [0]
+    for s in stride[:-1]:
+        starts.append(starts[-1] + s)
+    n_entries = max(1, starts[-1] + stride[-1]) if n_q else 1
+    kv_start_t = torch.tensor(starts[:n_q], dtype=torch.int64)
+    lay = [_make_layer(m, n_q, device, seed, li) for li, m in enumerate(layers)]
+    planted = None
+    if n_plant > 0 and n_q > 0:
+        rows = []
+        for t in range(n_q):
+            n = int(n_visible[t])
+            if n <= 0:
+                rows.append(torch.zeros(n_plant, dtype=torch.int64))
+                continue
+            if needles == "even":
+                i = torch.arange(n_plant, dtype=torch.float64)
+                rows.append(((i + 0.5) * n / n_plant).floor().to(torch.int64))
+            else:
+                g = _gen("cpu", seed, "plant", t)
+                rows.append(torch.randperm(n, generator=g)[:n_plant].sort().values)
+        planted = torch.stack([r[:n_plant] if r.numel() >= n_plant else
+                               torch.cat([r, r.new_full((n_plant - r.numel(),), 0)]) for r in rows])
+    k_cache, kv_fp4, kv_scale = _fill_sequences(
+        n_q, n_ctx, kv_start_t, n_visible_t, n_entries, device, seed,
+        None if planted is None else planted.to(device), lay[0])
+    return Workload(name=name, n_q=n_q, n_ctx=max(n_visible) if n_q else 0,
+                    kv_start=kv_start_t.to(device), n_visible=n_visible_t.to(device),
+                    k_cache=k_cache, kv_fp4=kv_fp4, kv_scale=kv_scale, layers=lay,
+                    with_pool=with_pool, planted=planted)
+
+
+def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
+                 device="cpu", seed=0):
+    """Chunked prefill: the last n_q source tokens of a sequence of ratio*n_entries tokens
+    query one shared cache; query i sits at token p = ratio*n_entries - n_q + i and sees
+    the entries whose source tokens are all at or before p: n_visible = (p+1)//ratio.
+    SWA: a buffer of n_q + 127 rows, query i reads rows i .. i+127."""
+    p0 = ratio * n_entries - n_q
+    n_visible = [(p0 + i + 1) // ratio for i in range(n_q)]
+    n_visible_t = torch.tensor(n_visible, dtype=torch.int32)
+    kv_start_t = torch.zeros(n_q, dtype=torch.int64)
+    rows = n_q + WINDOW - 1
+    swa_start = torch.arange(n_q, dtype=torch.int64, device=device)
+    n_swa = torch.full((n_q,), WINDOW, dtype=torch.int32, device=device)
+    lay = [_make_layer("full", n_q, device, seed, 0, rows, swa_start, n_swa)]
+    k_cache, kv_fp4, kv_scale = _fill_sequences(
+        n_q, n_entries, kv_start_t, n_visible_t, n_entries, device, seed, None, lay[0])
+    return Workload(name=name, n_q=n_q, n_ctx=max(n_visible), kv_start=kv_start_t.to(device),
+                    n_visible=n_visible_t.to(device), k_cache=k_cache, kv_fp4=kv_fp4,
+                    kv_scale=kv_scale, layers=lay, with_pool=False, planted=None)
+
+
+def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
+    """One of the named workloads; n_q (optional) keeps only the first n_q queries."""
+    if name == "tiny_decode_4k":
+        return make_decode(name, n_q or 1, 4096, ("full",), False, 16, device=device, seed=seed)
+    if name == "decode_32k":
+        return make_decode(name, n_q or 16, 32768, ("full",), False, 64, device=device, seed=seed)
+    if name == "decode_256k":
+        return make_decode(name, n_q or 32, 262144, DECODE_LAYERS, True, 64, device=device,
+                           seed=seed)
+    if name == "prefill_128k_m2":
+        return make_prefill(name, n_q=n_q or 4096, device=device, seed=seed)
+    if name == "decode_1m":
+        return make_decode(name, n_q or 64, 1048576, DECODE_LAYERS, True, 64, needles="even",
+                           device=device, seed=seed)
+    raise ValueError(f"unknown workload {name!r}")
+
+
+WORKLOADS = ("tiny_decode_4k", "decode_32k", "decode_256k", "prefill_128k_m2", "decode_1m")
+
+
+def sequence_to_host(wl: Workload, t: int):
+    """Host numpy copies of what query t reads: its rows of the caches (re-based so the
+    sequence starts at row 0) and its inputs of every layer."""
+    start = int(wl.kv_start[t])
+    n = int(wl.n_visible[t])
+    sl = slice(start, start + max(n, 0))
+    seq = {
+        "n_visible": n,
+        "k_cache": wl.k_cache[sl].cpu().numpy(),
+        "kv_fp4": wl.kv_fp4[sl].cpu().numpy(),
+        "kv_scale": wl.kv_scale[sl].cpu().numpy(),
+        "layers": [],
+    }
+    for lay in wl.layers:
+        s0 = int(lay.swa_start[t])
+        ns = int(lay.n_swa[t])
+        d = {
+            "mode": lay.mode,
+            "q": lay.q[t].view(torch.int16).cpu().numpy().view("uint16"),
+            "window_kv": lay.window_kv[s0:s0 + max(0, min(ns, WINDOW))].cpu().numpy(),
+            "n_swa": ns,
+        }
+        if lay.q_idx is not None:
+            d["q_idx"] = lay.q_idx[t].view(torch.int16).cpu().numpy().view("uint16")
+            d["w"] = lay.w[t].cpu().numpy()
+        seq["layers"].append(d)
+    return seq

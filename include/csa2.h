@@ -1,0 +1,199 @@
+/*
+ * csa2.h - C ABI of the CSA2 sparse-attention read path for AMD gfx950 (MI355X).
+ *
+ * The read path of one CSA2 attention layer, as the pages on DeepSeek-V4.1-Flash
+ * describe it, is:
+ *   1. the lightning indexer scores the shared compressed cache with a per-layer
+ *      indexer query (32 heads x 128) and per-head weights;
+ *   2. a Top-512 of those scores is taken;
+ *   3. in the decoder's Full layer, the same scores are reduced to 8-position block
+ *      maxima and the best 2,048 blocks form the candidate pool that later Reindex
+ *      layers are restricted to (the Hierarchical Sparse Indexer);
+ *   4. 64-head attention with head dim 512 runs over the selected entries of the
+ *      shared FP4 latent together with the 128-entry FP8 sliding window, in one
+ *      softmax, with key = value = the latent.
+ * Sources, cited by page title and section:
+ *   [V41F-ARCH]  "DeepSeek-V4.1-Flash - Architecture" (reading notes), sections
+ *                2 (CSA2 modes, layer schedule, main attention settings),
+ *                3 (Hierarchical Sparse Indexer) and 4 (KV cache formats).
+ *   [V41F-BLOG]  "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression",
+ *                sections 2.3.1-2.3.4 (CSA2, modes, HSI), 2.4.4 (FP4 main KV),
+ *                3.1 (cache entries), 3.3.2 (the readout of one layer).
+ *
+ * Conventions shared by every call
+ *   - Every call is stateless and re-entrant and returns an int status (CSA2_OK = 0).
+ *   - Tensor arguments are caller-owned DEVICE pointers. The library never allocates,
+ *     frees or keeps them past the enqueued work. Scratch memory is a caller-owned
+ *     device workspace of at least csa2_workspace_bytes(...) bytes (NULL/0 allowed
+ *     when that function returns 0).
+ *   - Layouts are dense row-major with the leading dimensions given. bf16 values are
+ *     passed as their 16-bit patterns; FP8 E4M3 and FP4 E2M1 as bytes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only
+ *     enqueue work: buffers must stay alive until the stream has been synchronised.
+ *   - All argument checks run on the host before any HIP call. On any error status
+ *     nothing has been launched and no output has been written; csa2_last_error()
+ *     returns a message (thread-local, valid until the next call on that thread).
+ *   - Device-resident index arguments (kv_start, n_visible, pool blocks, Top-K
+ *     indices, SWA rows) cannot be checked on the host. Kernels check every row they
+ *     would touch against the row counts passed in; an entry whose row falls outside
+ *     its cache is treated as absent (score -inf, never selected, not attended).
+ *   - Inputs are finite by contract (the FP8 codes 0x7F/0xFF, NaN, are not expected).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model constants [V41F-ARCH] sections 2-4; the names follow the configuration keys the
+ * blog page quotes (index_topk, sliding_window, head_dim, candidate_block_size,
+ * candidate_topk_blocks). */
+#define CSA2_N_HEADS 64                  /* main query heads */
+#define CSA2_HEAD_DIM 512                /* latent width = head dim, key = value */
+#define CSA2_IDX_HEADS 32                /* indexer query heads */
+#define CSA2_IDX_DIM 128                 /* indexer head dim */
+#define CSA2_INDEX_TOPK 512              /* entries selected per query */
+#define CSA2_SLIDING_WINDOW 128          /* SWA entries per query */
+#define CSA2_CANDIDATE_BLOCK_SIZE 8      /* positions per HSI block */
+#define CSA2_CANDIDATE_TOPK_BLOCKS 2048  /* HSI pool blocks (16,384 positions) */
+#define CSA2_FP4_ROW_BYTES 256           /* 512 E2M1 codes, two per byte */
+#define CSA2_SCALE_ROW_BYTES 32          /* one E4M3 scale per 16 channels */
+#define CSA2_KIDX_ROW_BYTES 128          /* 128 E4M3 indexer-K channels */
+#define CSA2_SWA_ROW_BYTES 512           /* 512 E4M3 SWA channels */
+#define CSA2_MAX_K 2048                  /* largest k / n_keep accepted */
+
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1, CSA2_REUSE = 2 } csa2_mode_t;
+
+enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad leading dim, alignment */
+  CSA2_ERR_UNSUPPORTED = 2, /* a dimension other than the compiled constants */
+  CSA2_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  CSA2_ERR_HIP = 4          /* a HIP launch failed (message names it) */
+};
+
+/* Workspace sizing. `op` is one of the CSA2_OP_* values; `n_q` queries, `max_cols` the
+ * largest row length (scores columns or block count) and `k` the selection size the
+ * call will be made with. Returns 0 when the op needs no workspace. The workspace must
+ * be zero-filled once when it is allocated; every call leaves it zero-filled again. */
+enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BLOCK_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
+size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);
+
+/* Lightning-indexer score ([V41F-BLOG] 2.3.1 and 3.3.2; [V41F-ARCH] 2 and 3).
+ * For query t the score of cache position j is
+ *     s[t,j] = sum_{h<32} w[t,h] * ReLU( q_idx[t,h,:] . k_idx[kv_start[t]+j, :] )
+ * (the indexer Q, the shared indexer K and a per-head weight; the unprinted scale
+ * factor is omitted because selection is invariant to a positive scale).
+ *   mode = CSA2_FULL: slot j in [0, ld_scores) holds s[t,j] for j < n_visible[t];
+ *       every other slot holds -inf. pool_blocks must be NULL.
+ *   mode = CSA2_REINDEX: slot r in [0, n_pool*block_size) holds the score of position
+ *       p = pool_blocks[t*n_pool + r/block_size]*block_size + r%block_size, or -inf when
+ *       that block id is negative or p >= n_visible[t]; slots >= n_pool*block_size
+ *       hold -inf. Requires ld_scores >= n_pool*block_size.
+ *   mode = CSA2_REUSE: rejected (CSA2_ERR_INVALID_ARG): a Reuse layer does no scoring.
+ * Arguments
+ *   n_q                 queries (rows of q_idx, w, scores); 0 is a no-op.
+ *   n_heads, d_idx      must be 32 and 128.
+ *   q_idx    [n_q,32,128] bf16, 16-byte aligned.        w [n_q,32] f32.
+ *   k_cache  [n_entries,128] E4M3, 16-byte aligned rows of 128 bytes.
+ *   kv_start [n_q] int64 first cache row of query t's sequence; n_visible [n_q] int32.
+ *   pool_blocks [n_q,n_pool] int32 (REINDEX), block ids with -1 padding.
+ *   block_size          must be 8.
+ *   scores   [n_q,ld_scores] f32 output.
+ *   block_max [n_q,ld_block_max] f32 output, may be NULL: block_max[t,b] is the max of
+ *       scores[t, 8b .. 8b+7] over the slots that exist; requires
+ *       ld_block_max >= ceil(ld_scores/8). These maxima are what csa2_block_pool ranks,
+ *       and csa2_topk uses them to skip blocks that cannot hold a winner. */
+int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+                     const void* q_idx, const float* w,
+                     const void* k_cache, int64_t n_entries,
+                     const int64_t* kv_start, const int32_t* n_visible,
+                     const int32_t* pool_blocks, int n_pool, int block_size,
+                     float* scores, int64_t ld_scores,
+                     float* block_max, int64_t ld_block_max,
+                     void* stream);
+
+/* HSI candidate pool ([V41F-BLOG] 2.3.4 "How does the Full Mode layer build the
+ * candidate pool"; [V41F-ARCH] 3). For query t with n = n_visible[t] > 0 there are
+ * nb = ceil(n/8) visible blocks whose scores are block_max[t, 0..nb) (the last block's
+ * missing tail counts as -inf). The block holding position n-1 is forced to +inf so it
+ * always takes one of the kept slots; the min(n_keep, nb) blocks with the largest
+ * values are kept, ties broken towards the lower block id; blocks whose value is -inf
+ * are never kept. pool_blocks[t, 0..n_keep) receives the kept ids in ascending order,
+ * then -1. n = 0 gives an all -1 row.
+ *   block_max [n_q,ld_bm] f32 (as written by csa2_index_score FULL), n_visible [n_q].
+ *   block_size must be 8; 1 <= n_keep <= CSA2_MAX_K; ld_pool >= n_keep.
+ *   Positions of the pool are {8b .. 8b+7} of every kept block b, clipped to n. */
+int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm,
+                    const int32_t* n_visible, int block_size, int n_keep,
+                    int32_t* pool_blocks, int64_t ld_pool,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Top-K selection ([V41F-BLOG] 2.3.4 and 3.3.1; [V41F-ARCH] 2 "Top-K global entries").
+ * For query t the candidates are slots r < n_cols (and r < n_valid[t] when n_valid is
+ * not NULL) whose score is finite or +inf (-inf and NaN are never selected). The
+ * min(k, #candidates) slots with the largest scores are chosen, ties broken towards
+ * the lower slot. Each chosen slot is mapped to a cache position: identity when
+ * pool_blocks is NULL, else pool_blocks[t*n_pool + r/block_size]*block_size
+ * + r%block_size. topk_idx[t, 0..k) receives the positions in ascending order of
+ * slot, then -1.
+ *   scores [n_q,ld_scores] f32; n_cols <= ld_scores.
+ *   block_max [n_q,ld_block_max] f32, may be NULL: when given it must hold the maxima
+ *       of 8-slot blocks of these scores (as csa2_index_score writes them); it lets the
+ *       kernel examine only blocks that can hold a winner. The result is identical.
+ *   1 <= k <= CSA2_MAX_K; ld_idx >= k; block_size must be 8. */
+int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
+              const int32_t* n_valid,
+              const float* block_max, int64_t ld_block_max,
+              int k, const int32_t* pool_blocks, int n_pool, int block_size,
+              int32_t* topk_idx, int64_t ld_idx,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Joint sparse attention over the selected entries and the sliding window
+ * ([V41F-BLOG] 2.2.2, 3.3.1 and 3.3.2 "the readout"; [V41F-ARCH] 2 and 4).
+ * For query t let S be {valid positions in topk_idx[t, 0..k)} plus the SWA rows
+ * swa_start[t] .. swa_start[t]+n_swa[t]-1. Each entry c_j is a 512-vector used both
+ * as key and as value:
+ *   main entry at position p, row R = kv_start[t]+p:
+ *       c[i] = E2M1(code i of kv_fp4 row R) * E4M3(kv_scale[R, i/16]); code 2m sits in
+ *       the low nibble of byte m, code 2m+1 in the high nibble;
+ *   SWA row:  c[i] = E4M3(window_kv[row, i]).
+ * For head h: l_j = softmax_scale * q[t,h,:] . c_j,  p = softmax over S (one softmax
+ * for main and window entries), out[t,h,:] = sum_j p_j c_j (bf16, round to nearest
+ * even), lse[t,h] = log sum_j exp(l_j) (f32). An empty S gives out = 0, lse = -inf.
+ * Entries of topk_idx that are negative or whose row is outside [0, n_entries) are
+ * skipped, as are SWA rows outside [0, n_window_rows). Duplicated positions are
+ * attended as many times as they occur. Reuse layers call this with the indices
+ * published by the latest Full or Reindex layer.
+ *   n_heads, head_dim must be 64 and 512.
+ *   q [n_q,64,512] bf16 (16-byte aligned);
+ *   kv_fp4 rows of 256 bytes at kv_fp4_stride bytes (>= 256, multiple of 16);
+ *   kv_scale rows of 32 bytes at kv_scale_stride bytes (>= 32, multiple of 16);
+ *   topk_idx [n_q,ld_idx] int32 with 0 <= k <= CSA2_MAX_K;
+ *   window_kv [n_window_rows,512] E4M3; swa_start [n_q] int64; n_swa [n_q] int32 (values
+ *   above 128 are clamped to 128);
+ *   out [n_q,64,512] bf16; lse [n_q,64] f32 or NULL. */
+int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q,
+                     const void* kv_fp4, int64_t kv_fp4_stride,
+                     const void* kv_scale, int64_t kv_scale_stride, int64_t n_entries,
+                     const int64_t* kv_start, const int32_t* topk_idx, int64_t ld_idx, int k,
+                     const void* window_kv, int64_t n_window_rows,
+                     const int64_t* swa_start, const int32_t* n_swa,
+                     float softmax_scale, void* out, float* lse,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Library version string (static storage). */
+const char* csa2_version(void);
+
+/* Message of the last failed call on this thread ("" when none). */
+const char* csa2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

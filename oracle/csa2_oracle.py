@@ -1,0 +1,316 @@
+"""Plain fp64 CPU oracle of the CSA2 read path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link this
+module: only the test suite, the smoke check of the graft entry point and the CPU
+baseline leg of the benchmark do. It shares no code with the HIP library and does not
+import the input generator; it receives plain numpy arrays.
+
+Every function is the plain definition of one step, written from the pages:
+  [V41F-ARCH] "DeepSeek-V4.1-Flash - Architecture" (reading notes), section 2 (CSA2 modes,
+              layer schedule, main attention settings), section 3 (Hierarchical Sparse
+              Indexer), section 4 (KV cache formats and storage).
+  [V41F-BLOG] "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression",
+              2.3.1 (indexer, compressor), 2.3.2 (Full / Reindex / Reuse modes),
+              2.3.4 (HSI and its block-max pool), 2.4.4 (FP4 main KV cache),
+              3.1 (what one cache entry holds), 3.3.1-3.3.2 (the readout of one layer).
+Where the pages are silent or garbled, the reading taken is named in the docstring
+(R-numbers follow the readings table of the design notes).
+
+Arithmetic is float64. Codes are decoded from their bit definitions; a decode table is
+only the closed form evaluated at every code and then indexed. Parity status: every
+function below is pinned by a CPU test (exhaustive codec checks, brute force on tiny
+inputs, library cross-checks, closed forms and invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+# --------------------------------------------------------------------------------------
+# Formats
+# --------------------------------------------------------------------------------------
+
+
+def e4m3_value(code: int) -> float:
+    """OCP FP8 E4M3FN: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+
+    [V41F-BLOG] 2.4.4 and [V41F-ARCH] 4: the FP4 main KV keeps one E4M3 scale per 16
+    channels, and the SWA cache stays in FP8. Exponent field 0 is subnormal
+    (m/8 * 2^-6); S.1111.111 is NaN; there is no infinity, so the largest value is 448.
+    """
+    code = int(code) & 0xFF
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e2m1_value(code: int) -> float:
+    """FP4 E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+
+    [V41F-BLOG] 2.4.4 and [V41F-ARCH] 4: main-KV values are E2M1 codes. Exponent field 0
+    is subnormal (0.5*m); the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    code = int(code) & 0xF
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * 0.5 * m
+    return s * (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Decode an array of E4M3 bytes to float64 (e4m3_value at every element)."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """Decode an array of 4-bit E2M1 codes (0..15) to float64."""
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to float64: they are the top half of a float32."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def fp4_latent_decode(payload: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Main-KV latent rows to float64: c[i] = E2M1(code i) * E4M3(scale[i // 16]).
+
+    [V41F-BLOG] 2.4.4 / [V41F-ARCH] 4: E2M1 values, one E4M3 scale per 16 channels and no
+    second-level global scale. Reading R4 (the pages give no packing): channel 2m is the
+    low nibble of byte m, channel 2m+1 the high nibble.
+    payload [..., 256] uint8, scales [..., 32] uint8 -> [..., 512] float64.
+    """
+    payload = np.asarray(payload, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    lo = payload & 0xF
+    hi = payload >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(payload.shape[:-1] + (payload.shape[-1] * 2,))
+    values = e2m1_decode(codes)
+    scale_per_channel = np.repeat(e4m3_decode(scales), 16, axis=-1)
+    return values * scale_per_channel
+
+
+# --------------------------------------------------------------------------------------
+# Indexer
+# --------------------------------------------------------------------------------------
+
+
+def index_score_rows(q_idx: np.ndarray, w: np.ndarray, k_rows: np.ndarray) -> np.ndarray:
+    """Lightning-indexer score of some cache rows for one query.
+
+    [V41F-BLOG] 3.3.2 (the indexer query, a per-head weight, and the shared indexer K
+    produce the score of every entry) with [V41F-ARCH] 2 (32 indexer heads of dim 128).
+    The printed formula is lost; reading R1 takes the DSA lightning indexer form
+        s_j = sum_h w_h * ReLU(q_h . k_j)
+    with no extra scale (a positive scale changes no selection).
+    q_idx [32,128] float64, w [32] float64, k_rows [n,128] float64 -> [n] float64.
+    """
+    dots = k_rows @ q_idx.T                    # [n, 32]: q_h . k_j
+    return np.maximum(dots, 0.0) @ w           # sum_h w_h ReLU(.)
+
+
+def full_scores(q_idx: np.ndarray, w: np.ndarray, k_cache_codes: np.ndarray,
+                kv_start: int, n_visible: int, ld: int) -> np.ndarray:
+    """Full mode: score every causally visible position 0 <= j < n_visible of one query.
+
+    [V41F-BLOG] 2.3.4 (a Full layer scores all causally visible main-KV positions) and
+    2.3.2 (Full mode runs the indexer itself). Slots at or beyond n_visible are -inf.
+    q_idx [32,128] bf16 bits, w [32] float32, k_cache_codes [E,128] E4M3 bytes.
+    """
+    out = np.full(ld, NEG_INF)
+    n = min(int(n_visible), int(ld))
+    if n > 0:
+        rows = e4m3_decode(k_cache_codes[kv_start:kv_start + n])
+        out[:n] = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), rows)
+    return out
+
+
+def reindex_scores(q_idx: np.ndarray, w: np.ndarray, k_cache_codes: np.ndarray,
+                   kv_start: int, n_visible: int, pool_blocks: np.ndarray,
+                   block_size: int = 8) -> np.ndarray:
+    """Reindex mode: score only the positions of the candidate pool.
+
+    [V41F-BLOG] 2.3.2 (Reindex computes its own indexer Q and rescores the reused keys)
+    and 2.3.4 (later index layers score only the pool of their query). Slot r stands for
+    position pool_blocks[r // 8]*8 + r % 8; a negative block id or a position at or
+    beyond n_visible gives -inf.
+    """
+    pool_blocks = np.asarray(pool_blocks, dtype=np.int64)
+    n_slots = pool_blocks.shape[0] * block_size
+    out = np.full(n_slots, NEG_INF)
+    slot = np.arange(n_slots)
+    block = pool_blocks[slot // block_size]
+    pos = block * block_size + slot % block_size
+    ok = (block >= 0) & (pos < n_visible)
+    if ok.any():
+        rows = e4m3_decode(k_cache_codes[kv_start + pos[ok]])
+        out[ok] = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), rows)
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Selection
+# --------------------------------------------------------------------------------------
+
+
+def topk_slots(scores: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, #candidates) slots with the largest scores, in ascending slot order.
+
+    [V41F-BLOG] 2.3.4 and [V41F-ARCH] 2: keep index_topk = 512 entries per query.
+    Readings R9/R10: -inf (not visible) and NaN are never candidates; ties go to the
+    lower slot, i.e. the order is (score descending, slot ascending).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    cand = np.nonzero(~np.isnan(scores) & (scores > NEG_INF))[0]
+    order = np.lexsort((cand, -scores[cand]))          # primary -score, secondary slot
+    return np.sort(cand[order[:k]])
+
+
+def slots_to_positions(slots: np.ndarray, pool_blocks: np.ndarray | None,
+                       block_size: int = 8) -> np.ndarray:
+    """Map selected slots to cache positions: identity in Full mode, through the pool
+    (block id * 8 + offset) in Reindex mode ([V41F-BLOG] 2.3.4)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    if pool_blocks is None:
+        return slots
+    pool_blocks = np.asarray(pool_blocks, dtype=np.int64)
+    return pool_blocks[slots // block_size] * block_size + slots % block_size
+
+
+def block_max(scores: np.ndarray, block_size: int = 8) -> np.ndarray:
+    """Maximum of each block of 8 consecutive slots, the last block padded with -inf.
+
+    [V41F-BLOG] 2.3.4: the Full layer pads its scores with -inf up to a multiple of the
+    block size, splits them into blocks of 8 and takes the max of each block.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    nb = -(-scores.shape[0] // block_size)
+    padded = np.full(nb * block_size, NEG_INF)
+    padded[:scores.shape[0]] = scores
+    return padded.reshape(nb, block_size).max(axis=1)
+
+
+def hsi_pool(scores: np.ndarray, n_visible: int, block_size: int = 8,
+             n_keep: int = 2048) -> np.ndarray:
+    """HSI candidate pool of one query: the kept block ids in ascending order.
+
+    [V41F-BLOG] 2.3.4 ("How does the Full Mode layer build the candidate pool") and
+    [V41F-ARCH] 3: block max over the visible scores, the block holding the latest
+    visible position forced to +inf (reading R13) so it always occupies a slot, then the
+    top min(2048, #blocks) blocks (ties to the lower block id, reading R10; -inf blocks
+    are never kept). The pool's positions are the union of the kept blocks, clipped to
+    the visible width.
+    """
+    n = int(n_visible)
+    if n <= 0:
+        return np.zeros(0, dtype=np.int64)
+    bm = block_max(np.asarray(scores, dtype=np.float64)[:n], block_size)
+    bm[(n - 1) // block_size] = np.inf
+    return topk_slots(bm, n_keep)
+
+
+def pool_bitmap(blocks: np.ndarray, n_visible: int, block_size: int = 8) -> np.ndarray:
+    """The pool as a position bitmap: each kept block's flag repeated 8 times and cut to
+    the visible width ([V41F-BLOG] 2.3.4)."""
+    nb = -(-int(n_visible) // block_size)
+    flags = np.zeros(nb, dtype=bool)
+    flags[np.asarray(blocks, dtype=np.int64)] = True
+    return np.repeat(flags, block_size)[:int(n_visible)]
+
+
+# --------------------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------------------
+
+
+def sparse_attention(q: np.ndarray, entries: np.ndarray, softmax_scale: float):
+    """Joint softmax attention of all heads of one query over a set of entries.
+
+    [V41F-BLOG] 3.3.1-3.3.2: the selected main-KV entries and the SWA entries are
+    concatenated into one attention, and each entry serves as key and as value (the
+    output is a convex combination of the attended vectors). [V41F-ARCH] 2: 64 heads of
+    dim 512. Reading R6: logits are softmax_scale * q_h . c_j (the pages lose the
+    constant; 1/sqrt(512) is passed in by the callers).
+    q [64,512] float64, entries [n,512] float64 -> (out [64,512], lse [64]).
+    An empty set gives out = 0 and lse = -inf.
+    """
+    n_heads = q.shape[0]
+    if entries.shape[0] == 0:
+        return np.zeros((n_heads, entries.shape[1])), np.full(n_heads, NEG_INF)
+    logits = softmax_scale * (q @ entries.T)                 # [heads, n]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    out = p @ entries
+    lse = (mx + np.log(z))[:, 0]
+    return out, lse
+
+
+def gather_attention_entries(topk_pos: np.ndarray, kv_fp4: np.ndarray, kv_scale: np.ndarray,
+                             kv_start: int, window_kv: np.ndarray, swa_start: int,
+                             n_swa: int) -> np.ndarray:
+    """The attended set of one query: decoded main entries at the selected positions
+    (skipping -1 padding) followed by the SWA rows ([V41F-BLOG] 3.3.2; reading R8: the
+    window is FP8 without a scale and is not de-duplicated against the selection)."""
+    pos = np.asarray(topk_pos, dtype=np.int64)
+    pos = pos[pos >= 0]
+    rows = kv_start + pos
+    main = fp4_latent_decode(kv_fp4[rows], kv_scale[rows]) if rows.size else np.zeros((0, 512))
+    n_swa = max(0, min(int(n_swa), 128))
+    win = e4m3_decode(window_kv[swa_start:swa_start + n_swa])
+    return np.concatenate([main, win.reshape(-1, 512)], axis=0)
+
+
+# --------------------------------------------------------------------------------------
+# One layer of each mode ([V41F-BLOG] 2.3.2, 3.3.3; [V41F-ARCH] 2 "CSA2 modes")
+# --------------------------------------------------------------------------------------
+
+
+def full_layer(q_idx, w, k_cache, kv_start, n_visible, q, kv_fp4, kv_scale, window_kv,
+               swa_start, n_swa, softmax_scale, k=512, with_pool=False):
+    """Full mode for one query: score everything visible, take the Top-K, optionally
+    build the HSI pool from the same scores, and attend. Returns a dict."""
+    scores = full_scores(q_idx, w, k_cache, kv_start, n_visible, n_visible)
+    idx = slots_to_positions(topk_slots(scores, k), None)
+    res = {"scores": scores, "idx": idx}
+    if with_pool:
+        res["pool"] = hsi_pool(scores, n_visible)
+    ents = gather_attention_entries(idx, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa)
+    res["out"], res["lse"] = sparse_attention(bf16_decode(q), ents, softmax_scale)
+    return res
+
+
+def reindex_layer(q_idx, w, k_cache, kv_start, n_visible, pool, q, kv_fp4, kv_scale,
+                  window_kv, swa_start, n_swa, softmax_scale, k=512):
+    """Reindex mode for one query: rescore only the pool with this layer's indexer
+    query, take its own Top-K inside the pool, and attend."""
+    padded = np.full(2048, -1, dtype=np.int64)
+    padded[:len(pool)] = pool
+    scores = reindex_scores(q_idx, w, k_cache, kv_start, n_visible, padded)
+    idx = slots_to_positions(topk_slots(scores, k), padded)
+    ents = gather_attention_entries(idx, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa)
+    out, lse = sparse_attention(bf16_decode(q), ents, softmax_scale)
+    return {"scores": scores, "idx": idx, "out": out, "lse": lse}
+
+
+def reuse_layer(idx, q, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa,
+                softmax_scale):
+    """Reuse mode for one query: no scoring and no selection; attend with the latest
+    published indices and this layer's own query and window."""
+    ents = gather_attention_entries(idx, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa)
+    out, lse = sparse_attention(bf16_decode(q), ents, softmax_scale)
+    return {"idx": np.asarray(idx), "out": out, "lse": lse}

@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each test ties one oracle function to something it cannot agree with by construction:
+published format tables (tests/golden), library routines (torch casts, scaled dot-product
+attention, scipy logsumexp), a literal transcription of the pool construction the blog
+page describes in PyTorch terms, brute force with pure-Python loops on tiny inputs,
+closed forms and invariants (convex hull, Reuse/Reindex identities, scale invariance).
+"""
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.csa2_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ------------------------------------------------------------------------------ codecs
+
+def test_e4m3_exhaustive_matches_torch_cast():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_anchor_codes():
+    for code, val in _golden("e4m3_anchors.txt"):
+        assert O.e4m3_value(int(code, 16)) == float(val), code
+    # monotone over the positive codes, and the negative half mirrors it
+    pos = O.e4m3_decode(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(O.e4m3_decode(np.arange(0x80, 0xFF)), -pos)
+
+
+def test_e2m1_table_matches_published_magnitudes():
+    for code, val in _golden("e2m1_magnitudes.txt"):
+        c = int(code)
+        assert O.e2m1_value(c) == float(val)
+        assert O.e2m1_value(c | 8) == -float(val)
+    # largest magnitude of an FP4 value with an E4M3 scale: 6 * 448
+    assert O.e2m1_value(7) * O.e4m3_value(0x7E) == 2688.0
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    x = torch.from_numpy(rng.standard_normal(4096).astype(np.float32) * 50).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_decode(bits), x.to(torch.float64).numpy())
+
+
+def test_fp4_latent_nibble_order_and_scale_groups():
+    payload = np.zeros((1, 256), np.uint8)
+    payload[0, 0] = 0x71          # channel 0 <- code 1 (0.5), channel 1 <- code 7 (6.0)
+    payload[0, 8] = 0xA3          # channel 16 <- code 3 (1.5), channel 17 <- code 10 (-1.0)
+    scales = np.zeros((1, 32), np.uint8)
+    scales[0, 0] = 0x38           # 1.0 for channels 0..15
+    scales[0, 1] = 0x40           # 2.0 for channels 16..31
+    c = O.fp4_latent_decode(payload, scales)[0]
+    assert c[0] == 0.5 and c[1] == 6.0
+    assert c[16] == 3.0 and c[17] == -2.0
+    assert np.count_nonzero(c) == 4
+
+
+def test_fp4_roundtrip_with_generator_encoder():
+    """Encoder of the input generator and decoder of the oracle invert each other."""
+    from compressed_kv_cache_csa2_amd import synth
+    # every (code, scale) product that the format can hold is reproduced exactly
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 16, size=(64, 512))
+    codes[:, ::16] = 7            # each group reaches |6| so amax/6 is the scale itself
+    scale_codes = rng.integers(0x20, 0x60, size=(64, 32)).astype(np.uint8)
+    exact = O.e2m1_decode(codes) * np.repeat(O.e4m3_decode(scale_codes), 16, axis=-1)
+    payload, scales = synth.encode_fp4_rows(torch.from_numpy(exact).float())
+    back = O.fp4_latent_decode(payload.numpy(), scales.numpy())
+    assert np.array_equal(back, exact)
+    # random values: error within half an E2M1 step of the group scale (no saturation)
+    x = rng.standard_normal((256, 512))
+    payload, scales = synth.encode_fp4_rows(torch.from_numpy(x).float())
+    back = O.fp4_latent_decode(payload.numpy(), scales.numpy())
+    s = np.repeat(O.e4m3_decode(scales.numpy()), 16, axis=-1)
+    step = np.where(np.abs(x) / s < 2, 0.5, np.where(np.abs(x) / s < 4, 1.0, 2.0))
+    assert np.all(np.abs(back - x) <= 0.5 * step * s + 1e-6 * np.abs(x) + s * 0.02)
+
+
+# ------------------------------------------------------------------------------ indexer
+
+def _bf16_py(bits):
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def test_index_score_brute_force_loops():
+    rng = np.random.default_rng(2)
+    q = torch.from_numpy(rng.standard_normal((32, 128)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().view(np.uint16)
+    w = rng.random(32).astype(np.float32)
+    k = rng.integers(0, 256, size=(7, 128)).astype(np.uint8)
+    k[k == 0x7F] = 0x7E
+    k[k == 0xFF] = 0xFE
+    got = O.full_scores(q_bits, w, k, 0, 7, 9)
+    for j in range(7):
+        s = 0.0
+        for h in range(32):
+            dot = 0.0
+            for d in range(128):
+                dot += _bf16_py(q_bits[h, d]) * O.e4m3_value(k[j, d])
+            s += float(w[h]) * max(dot, 0.0)
+        assert math.isclose(got[j], s, rel_tol=1e-12, abs_tol=1e-12)
+    assert got[7] == -np.inf and got[8] == -np.inf
+
+
+def test_index_score_relu_and_weight_scaling():
+    rng = np.random.default_rng(3)
+    k = O.e4m3_decode(rng.integers(0, 0x70, size=(5, 128)))       # all positive rows
+    q = np.abs(rng.standard_normal((32, 128)))
+    w = rng.random(32)
+    # every head negative -> every ReLU is zero
+    assert np.all(O.index_score_rows(-q, w, k) == 0.0)
+    # one head flipped -> it drops out, the others add up
+    q2 = q.copy()
+    q2[5] = -q2[5]
+    w2 = w.copy()
+    w2[5] = 0.0
+    assert np.allclose(O.index_score_rows(q2, w, k), O.index_score_rows(q, w2, k))
+    # positive scale of w scales the scores and leaves the Top-K unchanged
+    s1 = O.index_score_rows(q, w, k)
+    s2 = O.index_score_rows(q, 3.5 * w, k)
+    assert np.allclose(s2, 3.5 * s1)
+    assert np.array_equal(O.topk_slots(s1, 3), O.topk_slots(s2, 3))
+
+
+# ------------------------------------------------------------------------------ Top-K
+
+def _brute_topk(s, k):
+    cand = [j for j in range(len(s)) if not math.isnan(s[j]) and s[j] > -math.inf]
+    return sorted(sorted(cand, key=lambda j: (-s[j], j))[:k])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties_and_masks(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 300))
+    s = rng.integers(-5, 6, size=n).astype(np.float64)    # many ties
+    s[rng.random(n) < 0.2] = -np.inf
+    s[rng.random(n) < 0.05] = np.inf
+    s[rng.random(n) < 0.05] = np.nan
+    for k in (1, 7, 64, 512):
+        assert O.topk_slots(s, k).tolist() == _brute_topk(s.tolist(), k)
+
+
+def test_topk_sizes_and_order_property():
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal(5000)
+    s[4000:] = -np.inf
+    sel = O.topk_slots(s, 512)
+    assert len(sel) == 512 and np.all(np.diff(sel) > 0)
+    rest = np.setdiff1d(np.arange(4000), sel)
+    assert s[sel].min() >= s[rest].max()
+    assert len(O.topk_slots(s[:100], 512)) == 100
+    assert len(O.topk_slots(np.full(10, -np.inf), 512)) == 0
+
+
+# ------------------------------------------------------------------------------ HSI pool
+
+def _pool_bitmap_torch(logits, width, block_size, n_keep):
+    """The pool construction as the blog page spells it in PyTorch calls: pad with -inf,
+    split into blocks, amax, force the latest block, keep the best blocks, expand."""
+    import torch.nn.functional as F
+    scores = F.pad(logits, (0, -width % block_size), value=-torch.inf)
+    bm = scores.unflatten(-1, (-1, block_size)).amax(dim=-1)
+    bm[..., (width - 1) // block_size] = torch.inf
+    keep = torch.topk(bm, min(n_keep, bm.shape[-1]), dim=-1).indices
+    flags = torch.zeros_like(bm, dtype=torch.bool)
+    flags[keep] = True
+    return flags.repeat_interleave(block_size, dim=-1)[..., :width]
+
+
+@pytest.mark.parametrize("width,n_keep", [(21, 2), (64, 3), (1000, 40), (8, 5), (3, 1), (4099, 100)])
+def test_pool_matches_pytorch_transcription(width, n_keep):
+    rng = np.random.default_rng(width)
+    logits = rng.standard_normal(width)           # continuous -> no ties
+    ref = _pool_bitmap_torch(torch.from_numpy(logits), width, 8, n_keep).numpy()
+    blocks = O.hsi_pool(logits, width, 8, n_keep)
+    assert np.array_equal(O.pool_bitmap(blocks, width, 8), ref)
+    assert np.all(np.diff(blocks) > 0)
+
+
+def test_pool_properties():
+    rng = np.random.default_rng(11)
+    n = 40000
+    s = rng.standard_normal(n)
+    blocks = O.hsi_pool(s, n)
+    assert len(blocks) == 2048 and (n - 1) // 8 in blocks
+    bitmap = O.pool_bitmap(blocks, n)
+    assert bitmap.sum() == 2048 * 8
+    # the Full Top-512 lies inside the pool (each winner's block max beats the rest)
+    assert bitmap[O.topk_slots(s, 512)].all()
+    # short context: every block is kept
+    assert np.array_equal(O.hsi_pool(s[:1000], 1000), np.arange(125))
+    assert len(O.hsi_pool(s, 0)) == 0
+
+
+def test_reindex_with_full_query_reproduces_full_topk():
+    rng = np.random.default_rng(12)
+    n = 30001
+    k_cache = rng.integers(0, 0x7E, size=(n, 128)).astype(np.uint8) ^ (rng.integers(0, 2, size=(n, 128)).astype(np.uint8) << 7)
+    q = torch.from_numpy(rng.standard_normal((32, 128)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().view(np.uint16)
+    w = rng.random(32).astype(np.float32)
+    s = O.full_scores(q_bits, w, k_cache, 0, n, n)
+    full_idx = O.topk_slots(s, 512)
+    pool = O.hsi_pool(s, n)
+    padded = np.full(2048, -1)
+    padded[:len(pool)] = pool
+    rs = O.reindex_scores(q_bits, w, k_cache, 0, n, padded)
+    re_idx = O.slots_to_positions(O.topk_slots(rs, 512), padded)
+    assert np.array_equal(np.sort(re_idx), full_idx)
+
+
+# ------------------------------------------------------------------------------ attention
+
+def test_attention_matches_library_sdpa():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((64, 512))
+    ents = rng.standard_normal((37, 512))
+    out, lse = O.sparse_attention(q, ents, 1 / math.sqrt(512))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(ents)[None, None].expand(1, 64, 37, 512),
+        torch.from_numpy(ents)[None, None].expand(1, 64, 37, 512), scale=1 / math.sqrt(512))
+    assert np.allclose(out, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    from scipy.special import logsumexp
+    assert np.allclose(lse, logsumexp(q @ ents.T / math.sqrt(512), axis=1), rtol=1e-12)
+
+
+def test_attention_closed_forms_and_convex_hull():
+    rng = np.random.default_rng(14)
+    ents = rng.standard_normal((20, 512))
+    out, _ = O.sparse_attention(np.zeros((64, 512)), ents, 0.1)
+    assert np.allclose(out, ents.mean(axis=0)[None])
+    one, lse1 = O.sparse_attention(rng.standard_normal((64, 512)), ents[3:4], 0.1)
+    assert np.array_equal(one, np.repeat(ents[3:4], 64, axis=0))
+    out, _ = O.sparse_attention(5 * rng.standard_normal((64, 512)), ents, 1.0)
+    assert np.all(out <= ents.max(axis=0) + 1e-12) and np.all(out >= ents.min(axis=0) - 1e-12)
+    empty, lse0 = O.sparse_attention(np.ones((64, 512)), np.zeros((0, 512)), 1.0)
+    assert np.all(empty == 0) and np.all(lse0 == -np.inf)
+
+
+def _tiny_sequence(seed, n, n_swa=128):
+    rng = np.random.default_rng(seed)
+    k_cache = rng.integers(0, 0x7E, size=(n, 128)).astype(np.uint8) | (rng.integers(0, 2, size=(n, 128)).astype(np.uint8) << 7)
+    from compressed_kv_cache_csa2_amd import synth
+    p, s = synth.encode_fp4_rows(torch.from_numpy(rng.standard_normal((n, 512))).float())
+    win = synth.encode_e4m3(torch.from_numpy(rng.standard_normal((n_swa, 512))).float()).numpy()
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q_idx = bf(rng.standard_normal((32, 128)))
+    w = rng.random(32).astype(np.float32)
+    q = bf(rng.standard_normal((64, 512)))
+    return k_cache, p.numpy(), s.numpy(), win, q_idx, w, q
+
+
+def test_full_layer_with_k_covering_context_is_dense_attention():
+    n = 300
+    k_cache, p, s, win, q_idx, w, q = _tiny_sequence(15, n)
+    res = O.full_layer(q_idx, w, k_cache, 0, n, q, p, s, win, 0, 128, 1 / math.sqrt(512), k=512)
+    assert np.array_equal(res["idx"], np.arange(n))
+    dense = np.concatenate([O.fp4_latent_decode(p, s), O.e4m3_decode(win)], axis=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(O.bf16_decode(q))[None, :, None, :],
+        torch.from_numpy(dense)[None, None].expand(1, 64, -1, 512),
+        torch.from_numpy(dense)[None, None].expand(1, 64, -1, 512), scale=1 / math.sqrt(512))
+    assert np.allclose(res["out"], ref[0, :, 0].numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_reuse_with_full_inputs_reproduces_full_layer():
+    n = 5000
+    k_cache, p, s, win, q_idx, w, q = _tiny_sequence(16, n)
+    full = O.full_layer(q_idx, w, k_cache, 0, n, q, p, s, win, 0, 128, 0.05, with_pool=True)
+    reuse = O.reuse_layer(full["idx"], q, p, s, 0, win, 0, 128, 0.05)
+    assert np.array_equal(reuse["out"], full["out"]) and np.array_equal(reuse["lse"], full["lse"])
+    assert len(full["idx"]) == 512 and len(full["pool"]) == 625
+
+
+def test_model_constants_and_entry_bytes():
+    c = {k: int(v) for k, v in _golden("model_constants.txt")}
+    assert c["candidate_topk_blocks"] * c["candidate_block_size"] == c["pool_positions"]
+    # an FP4 main entry: 512 codes of 4 bits + one scale byte per 16 channels
+    main = c["head_dim"] // 2 + c["head_dim"] // 16
+    assert main == c["main_entry_bytes"]
+    # the pages' 890 B/token: (main entry + MXFP4 indexer entry of 128/2 + 128/32 bytes)
+    # times 2.5 entries per token (3 encoder copies at ratio 2, 1 decoder copy at ratio 1)
+    idx_mxfp4 = c["idx_dim"] // 2 + c["idx_dim"] // 32
+    assert (main + idx_mxfp4) * (3 / 2 + 1) == c["global_kv_bytes_per_token"]
+    # the same constants are compiled into the C ABI header
+    hdr = open(os.path.join(os.path.dirname(GOLDEN), "..", "include", "csa2.h")).read()
+    for key, name in [("n_heads", "CSA2_N_HEADS"), ("head_dim", "CSA2_HEAD_DIM"),
+                      ("idx_heads", "CSA2_IDX_HEADS"), ("idx_dim", "CSA2_IDX_DIM"),
+                      ("index_topk", "CSA2_INDEX_TOPK"), ("sliding_window", "CSA2_SLIDING_WINDOW"),
+                      ("candidate_block_size", "CSA2_CANDIDATE_BLOCK_SIZE"),
+                      ("candidate_topk_blocks", "CSA2_CANDIDATE_TOPK_BLOCKS")]:
+        assert f"#define {name} {c[key]} " in hdr or f"#define {name} {c[key]}\n" in hdr, name
