@@ -1,0 +1,254 @@
+"""Benchmark of the CSA2 read path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_256k]
+
+A step is one pass of the whole layer stack of the workload over its batch: for
+decode_256k, 32 queries each over its own 262,144-entry cache through Full (indexer over
+the whole context, Top-512, HSI pool of 2,048 blocks, attention), Reindex (indexer over
+the pool, Top-512, attention) and three Reuse layers (attention). The step's kernels are
+captured once into a HIP graph and replayed; W untimed replays, then K timed replays
+bracketed by device synchronisation. Inputs are seeded synthetic tensors already resident
+in HBM. Prints one JSON line.
+
+roofline: the dominant kernel is the Full-layer indexer. Its algorithmic bytes per launch
+are 128 B of indexer K read + 4 B of score and 0.5 B of block maximum written per
+(query, entry) pair, plus the indexer queries and weights; its average launch duration is
+measured with HIP events on its own stream over K back-to-back launches.
+
+cpu_baseline: the fp64 oracle (oracle/) run on the host over a bounded sample of the same
+workload's queries (whole layer stack per query), scaled to queries/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def algorithmic_bytes(wl, k=512):
+    """Bytes the method must move per step: every visible indexer-K row of a Full layer,
+    the pool's rows of a Reindex layer, and per attention layer the selected FP4 rows
+    (288 B), the 128 FP8 window rows (512 B), the 64x512 bf16 query and output."""
+    import torch
+    nv = wl.n_visible.to(torch.int64).cpu()
+    total = 0
+    for lay in wl.layers:
+        if lay.mode == "full":
+            total += int(nv.sum()) * 128
+        elif lay.mode == "reindex":
+            total += int(torch.clamp(nv, max=16384).sum()) * 128
+        sel = torch.clamp(nv, max=k)
+        total += int(sel.sum()) * 288 + wl.n_q * (128 * 512 + 2 * 64 * 512 * 2)
+    return total
+
+
+def indexer_bytes_per_launch(wl):
+    import torch
+    pairs = int(wl.n_visible.to(torch.int64).sum())
+    return pairs * (128 + 4 + 0.5) + wl.n_q * (32 * 128 * 2 + 32 * 4)
+
+
+def cpu_baseline(wl, target_s, max_q):
+    """Time the oracle stack on queries 0, 1, ... until target_s seconds have passed."""
+    import numpy as np
+
+    import oracle.csa2_oracle as O
+    from compressed_kv_cache_csa2_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    done = 0
+    t_total = 0.0
+    while done < min(max_q, wl.n_q) and t_total < target_s:
+        seq = synth.sequence_to_host(wl, done)
+        t0 = time.perf_counter()
+        nv = seq["n_visible"]
+        idx = pool = None
+        for lay in seq["layers"]:
+            if lay["mode"] == "full":
+                r = O.full_layer(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, lay["q"],
+                                 seq["kv_fp4"], seq["kv_scale"], lay["window_kv"], 0, lay["n_swa"],
+                                 wl.softmax_scale, with_pool=wl.with_pool)
+                pool = r.get("pool")
+            elif lay["mode"] == "reindex":
+                r = O.reindex_layer(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, pool, lay["q"],
+                                    seq["kv_fp4"], seq["kv_scale"], lay["window_kv"], 0,
+                                    lay["n_swa"], wl.softmax_scale)
+            else:
+                r = O.reuse_layer(idx, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
+                                  lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
+            idx = r["idx"]
+        t_total += time.perf_counter() - t0
+        done += 1
+        np.asarray(r["out"]).sum()
+    return {"value": done / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.n_q} queries of {wl.name}, whole layer stack per query, "
+                      f"{t_total:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_256k")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--breakdown", action="store_true", help="per-call timings to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode batch "
+              "shards by sequence with no exchange, so one GPU's throughput is the figure; see "
+              "the design notes for the multi-GPU layout.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import layers, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl = synth.make_workload(args.workload, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: generated in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    buf = layers.alloc_buffers(wl)
+    stream = torch.cuda.Stream()
+
+    def step():
+        layers.run_layers(wl, buf, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            layers.run_layers(wl, buf, stream=stream)
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall "
+          f"{wall / args.steps * 1e6:.1f} us/step)", file=sys.stderr, flush=True)
+
+    # Dominant kernel: the Full-layer indexer, launched back to back on `stream`.
+    full = wl.layers[0]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                           buf.scores, buf.block_max, stream=stream)
+        e0.record(stream)
+        for _ in range(args.steps):
+            C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start,
+                               wl.n_visible, buf.scores, buf.block_max, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    idx_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    idx_bytes = indexer_bytes_per_launch(wl)
+    achieved = idx_bytes / (idx_us * 1e-6) / 1e9
+
+    if args.breakdown:
+        names = []
+        evs = []
+        with torch.cuda.stream(stream):
+            for li, lay in enumerate(wl.layers):
+                for part in ("score", "topk", "pool", "attn"):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    if part == "score" and lay.mode == "full":
+                        C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                           wl.n_visible, buf.scores, buf.block_max, stream=stream)
+                    elif part == "score" and lay.mode == "reindex":
+                        C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                           wl.n_visible, buf.re_scores, None,
+                                           pool_blocks=buf.pool, stream=stream)
+                    elif part == "topk" and lay.mode == "full":
+                        C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
+                                    block_max=buf.block_max, stream=stream)
+                    elif part == "topk" and lay.mode == "reindex":
+                        C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool, stream=stream)
+                    elif part == "pool" and lay.mode == "full" and wl.with_pool:
+                        C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, stream=stream)
+                    elif part == "attn":
+                        C.csa2_sparse_attn(lay.q, wl.kv_fp4, wl.kv_scale, wl.kv_start,
+                                           buf.published[li], lay.window_kv, lay.swa_start,
+                                           lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
+                                           buf.workspace, stream=stream)
+                    else:
+                        continue
+                    b.record(stream)
+                    names.append(f"L{li}:{lay.mode}:{part}")
+                    evs.append((a, b))
+        torch.cuda.synchronize()
+        for n, (a, b) in zip(names, evs):
+            print(f"[bench] {n:24s} {a.elapsed_time(b) * 1e3:9.1f} us", file=sys.stderr)
+
+    step_bytes = algorithmic_bytes(wl)
+    value = wl.n_q / (ms_step * 1e-3)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds, wl.n_q)
+    line = {
+        "metric": "decode queries/sec + achieved HBM GB/s (% of peak)",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wl.n_q, "context_entries": wl.n_ctx,
+                   "layers": [l.mode for l in wl.layers], "index_topk": 512,
+                   "sliding_window": 128, "pool_blocks": 2048 if wl.with_pool else 0,
+                   "launch": "eager" if args.no_graph else "hip_graph"},
+        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "kernel": "index_score_kernel<false> (Full-layer indexer)",
+                     "launch_us": idx_us, "bytes_per_launch": idx_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+"""Python binding of libcsa2.so: the C ABI calls under the same names.
+
+Argument marshalling only: dtype/device/shape checks, raw pointers, the current HIP
+stream. Every step of the path runs in the HIP library; if the library is missing the
+import fails (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+
+FULL, REINDEX, REUSE = 0, 1, 2
+OP_INDEX_SCORE, OP_BLOCK_POOL, OP_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
+CSA2_OK = 0
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m compressed_kv_cache_csa2_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
+    lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, P, I, I, P, L, P, Z, P]
+    lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
+                                     P, Z, P]
+    for f in ("csa2_index_score", "csa2_block_pool", "csa2_topk", "csa2_sparse_attn"):
+        getattr(lib, f).restype = I
+    lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
+    lib.csa2_workspace_bytes.restype = Z
+    lib.csa2_version.restype = ctypes.c_char_p
+    lib.csa2_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != CSA2_OK:
+        raise Csa2Error(status, lib.csa2_last_error().decode())
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def version() -> str:
+    return lib.csa2_version().decode()
+
+
+def workspace_bytes(op: int, n_q: int, max_cols: int, k: int) -> int:
+    return int(lib.csa2_workspace_bytes(op, n_q, max_cols, k))
+
+
+def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block_max=None,
+                     pool_blocks=None, stream=None):
+    """Indexer scores into `scores` [n_q, ld] (and block maxima into `block_max`)."""
+    n_q = q_idx.shape[0]
+    n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
+    _check(lib.csa2_index_score(
+        mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
+        _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+        _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
+        _ptr(scores, torch.float32, "scores"), scores.shape[1],
+        _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_block_pool(block_max, n_visible, pool_blocks, n_keep=2048, stream=None):
+    """HSI pool block ids (ascending, -1 padded) into `pool_blocks` [n_q, >= n_keep]."""
+    _check(lib.csa2_block_pool(
+        block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
+        _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), pool_blocks.shape[1], None, 0,
+        _stream(stream)))
+
+
+def csa2_topk(scores, topk_idx, k=512, n_cols=None, n_valid=None, block_max=None,
+              pool_blocks=None, stream=None):
+    """Top-k positions (ascending, -1 padded) into `topk_idx` [n_q, >= k]."""
+    n_cols = scores.shape[1] if n_cols is None else n_cols
+    _check(lib.csa2_topk(
+        scores.shape[0], _ptr(scores, torch.float32, "scores"), scores.shape[1], n_cols,
+        _ptr(n_valid, torch.int32, "n_valid"), _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, k,
+        _ptr(pool_blocks, torch.int32, "pool_blocks"),
+        pool_blocks.shape[1] if pool_blocks is not None else 0, 8,
+        _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], None, 0, _stream(stream)))
+
+
+def csa2_sparse_attn(q, kv_fp4, kv_scale, kv_start, topk_idx, window_kv, swa_start, n_swa,
+                     softmax_scale, out, lse=None, workspace=None, k=None, stream=None):
+    """Joint sparse attention into `out` [n_q, 64, 512] bf16 (and `lse` [n_q, 64])."""
+    n_q = q.shape[0]
+    k = topk_idx.shape[1] if k is None else k
+    ws = workspace
+    need = workspace_bytes(OP_SPARSE_ATTN, n_q, 0, k)
+    if need and ws is None:
+        raise ValueError(f"csa2_sparse_attn: a workspace of {need} bytes is required")
+    for name, t, row in (("kv_fp4", kv_fp4, 256), ("kv_scale", kv_scale, 32)):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected a device uint8 [rows, >= {row}] view")
+    _check(lib.csa2_sparse_attn(
+        n_q, q.shape[1], q.shape[2], _ptr(q, torch.bfloat16, "q"),
+        kv_fp4.data_ptr(), kv_fp4.stride(0), kv_scale.data_ptr(), kv_scale.stride(0),
+        kv_fp4.shape[0], _ptr(kv_start, torch.int64, "kv_start"),
+        _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], k,
+        _ptr(window_kv, torch.uint8, "window_kv"), window_kv.shape[0],
+        _ptr(swa_start, torch.int64, "swa_start"), _ptr(n_swa, torch.int32, "n_swa"),
+        float(softmax_scale), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(ws, None, "workspace"), ws.numel() * ws.element_size() if ws is not None else 0,
+        _stream(stream)))

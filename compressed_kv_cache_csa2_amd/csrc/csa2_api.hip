@@ -1,0 +1,203 @@
+// C ABI of the CSA2 read path (declared in include/csa2.h): host-side argument checks,
+// then kernel launches on the caller's stream. Every check runs before any HIP call, so
+// a rejected call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "csa2.h"
+#include "csa2_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return CSA2_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define REQUIRE(cond, code, ...)      \
+  do {                                \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_version(void) { return "csa2-gfx950 0.1.0"; }
+
+const char* csa2_last_error(void) { return g_err; }
+
+size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k) {
+  (void)max_cols;
+  switch (op) {
+    case CSA2_OP_SPARSE_ATTN:
+      if (n_q <= 0 || k < 0 || k > CSA2_MAX_K) return 0;
+      return csa2::attn_workspace_bytes(n_q, k);
+    default:
+      return 0;
+  }
+}
+
+int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
+                     const float* w, const void* k_cache, int64_t n_entries,
+                     const int64_t* kv_start, const int32_t* n_visible, const int32_t* pool_blocks,
+                     int n_pool, int block_size, float* scores, int64_t ld_scores,
+                     float* block_max, int64_t ld_block_max, void* stream) {
+  REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
+          "csa2_index_score: mode %d does no scoring (Reuse layers attend with published indices)",
+          (int)mode);
+  REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
+          "csa2_index_score: indexer shape %dx%d, only %dx%d is built", n_heads, d_idx,
+          CSA2_IDX_HEADS, CSA2_IDX_DIM);
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "csa2_index_score: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_q %d out of range", n_q);
+  if (n_q == 0) return ok();
+  REQUIRE(q_idx && w && k_cache && kv_start && n_visible && scores, CSA2_ERR_INVALID_ARG,
+          "csa2_index_score: null pointer argument");
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_entries < 0");
+  REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "csa2_index_score: ld_scores %lld out of range", (long long)ld_scores);
+  REQUIRE(aligned(q_idx, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
+          "csa2_index_score: q_idx and k_cache must be 16-byte aligned");
+  REQUIRE(aligned(w, 4) && aligned(scores, 4) && aligned(kv_start, 8) && aligned(n_visible, 4),
+          CSA2_ERR_INVALID_ARG, "csa2_index_score: misaligned argument");
+  if (mode == CSA2_REINDEX) {
+    REQUIRE(pool_blocks != nullptr, CSA2_ERR_INVALID_ARG, "csa2_index_score: REINDEX needs pool_blocks");
+    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+            "csa2_index_score: n_pool %d out of range", n_pool);
+    REQUIRE(ld_scores >= (int64_t)n_pool * block_size, CSA2_ERR_INVALID_ARG,
+            "csa2_index_score: ld_scores %lld < n_pool*block_size", (long long)ld_scores);
+  } else {
+    REQUIRE(pool_blocks == nullptr, CSA2_ERR_INVALID_ARG, "csa2_index_score: FULL takes no pool_blocks");
+  }
+  if (block_max != nullptr) {
+    REQUIRE(ld_block_max >= (ld_scores + 7) / 8, CSA2_ERR_INVALID_ARG,
+            "csa2_index_score: ld_block_max %lld < ceil(ld_scores/8)", (long long)ld_block_max);
+    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "csa2_index_score: misaligned block_max");
+  }
+  return hip_status(csa2::launch_index_score(
+                        mode == CSA2_REINDEX, n_q, static_cast<const uint16_t*>(q_idx), w,
+                        static_cast<const uint8_t*>(k_cache), n_entries, kv_start, n_visible,
+                        pool_blocks, mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
+                        ld_block_max, static_cast<hipStream_t>(stream)),
+                    "csa2_index_score");
+}
+
+int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
+                    int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "csa2_block_pool: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_block_pool: n_q %d out of range", n_q);
+  REQUIRE(n_keep >= 1 && n_keep <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+          "csa2_block_pool: n_keep %d out of range [1, %d]", n_keep, CSA2_MAX_K);
+  if (n_q == 0) return ok();
+  REQUIRE(block_max && n_visible && pool_blocks, CSA2_ERR_INVALID_ARG, "csa2_block_pool: null pointer argument");
+  REQUIRE(ld_bm >= 1 && ld_pool >= n_keep, CSA2_ERR_INVALID_ARG,
+          "csa2_block_pool: bad leading dimension (ld_bm %lld, ld_pool %lld)", (long long)ld_bm,
+          (long long)ld_pool);
+  REQUIRE(aligned(block_max, 4) && aligned(n_visible, 4) && aligned(pool_blocks, 4),
+          CSA2_ERR_INVALID_ARG, "csa2_block_pool: misaligned argument");
+  return hip_status(csa2::launch_block_pool(n_q, block_max, ld_bm, n_visible, n_keep, pool_blocks,
+                                            ld_pool, static_cast<hipStream_t>(stream)),
+                    "csa2_block_pool");
+}
+
+int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
+              const int32_t* n_valid, const float* block_max, int64_t ld_block_max, int k,
+              const int32_t* pool_blocks, int n_pool, int block_size, int32_t* topk_idx,
+              int64_t ld_idx, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "csa2_topk: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_topk: n_q %d out of range", n_q);
+  REQUIRE(k >= 1 && k <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG, "csa2_topk: k %d out of range [1, %d]", k,
+          CSA2_MAX_K);
+  if (n_q == 0) return ok();
+  REQUIRE(scores && topk_idx, CSA2_ERR_INVALID_ARG, "csa2_topk: null pointer argument");
+  REQUIRE(n_cols >= 0 && n_cols <= ld_scores && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "csa2_topk: need 0 <= n_cols <= ld_scores <= 2^31 (n_cols %lld, ld %lld)",
+          (long long)n_cols, (long long)ld_scores);
+  REQUIRE(ld_idx >= k, CSA2_ERR_INVALID_ARG, "csa2_topk: ld_idx %lld < k", (long long)ld_idx);
+  REQUIRE(aligned(scores, 4) && aligned(topk_idx, 4) && aligned(n_valid, 4) && aligned(block_max, 4),
+          CSA2_ERR_INVALID_ARG, "csa2_topk: misaligned argument");
+  if (block_max != nullptr)
+    REQUIRE(ld_block_max >= (n_cols + 7) / 8, CSA2_ERR_INVALID_ARG,
+            "csa2_topk: ld_block_max %lld < ceil(n_cols/8)", (long long)ld_block_max);
+  if (pool_blocks != nullptr)
+    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K && n_cols <= (int64_t)n_pool * block_size,
+            CSA2_ERR_INVALID_ARG, "csa2_topk: pool of %d blocks cannot cover %lld slots", n_pool,
+            (long long)n_cols);
+  return hip_status(csa2::launch_topk(n_q, scores, ld_scores, n_cols, n_valid, block_max, ld_block_max,
+                                      k, pool_blocks, pool_blocks ? n_pool : 0, topk_idx, ld_idx,
+                                      static_cast<hipStream_t>(stream)),
+                    "csa2_topk");
+}
+
+int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const void* kv_fp4,
+                     int64_t kv_fp4_stride, const void* kv_scale, int64_t kv_scale_stride,
+                     int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,
+                     int64_t ld_idx, int k, const void* window_kv, int64_t n_window_rows,
+                     const int64_t* swa_start, const int32_t* n_swa, float softmax_scale,
+                     void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(n_heads == CSA2_N_HEADS && head_dim == CSA2_HEAD_DIM, CSA2_ERR_UNSUPPORTED,
+          "csa2_sparse_attn: %d heads x %d, only %dx%d is built", n_heads, head_dim, CSA2_N_HEADS,
+          CSA2_HEAD_DIM);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: n_q %d out of range", n_q);
+  REQUIRE(k >= 0 && k <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: k %d out of range [0, %d]",
+          k, CSA2_MAX_K);
+  if (n_q == 0) return ok();
+  REQUIRE(q && kv_fp4 && kv_scale && kv_start && window_kv && swa_start && n_swa && out,
+          CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null pointer argument");
+  REQUIRE(k == 0 || topk_idx != nullptr, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null topk_idx");
+  REQUIRE(k == 0 || ld_idx >= k, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: ld_idx %lld < k", (long long)ld_idx);
+  REQUIRE(kv_fp4_stride >= CSA2_FP4_ROW_BYTES && kv_fp4_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_sparse_attn: kv_fp4_stride %lld must be >= 256 and a multiple of 16",
+          (long long)kv_fp4_stride);
+  REQUIRE(kv_scale_stride >= CSA2_SCALE_ROW_BYTES && kv_scale_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_sparse_attn: kv_scale_stride %lld must be >= 32 and a multiple of 16",
+          (long long)kv_scale_stride);
+  REQUIRE(n_entries >= 0 && n_window_rows >= 0, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: negative row count");
+  REQUIRE(aligned(q, 16) && aligned(kv_fp4, 16) && aligned(kv_scale, 16) && aligned(window_kv, 16) &&
+              aligned(out, 16) && aligned(kv_start, 8) && aligned(swa_start, 8) && aligned(n_swa, 4) &&
+              aligned(topk_idx, 4) && aligned(lse, 4),
+          CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: misaligned argument");
+  const size_t need = csa2::attn_workspace_bytes(n_q, k);
+  REQUIRE(need == 0 || (workspace != nullptr && ws_bytes >= need && aligned(workspace, 16)),
+          CSA2_ERR_WORKSPACE, "csa2_sparse_attn: workspace of %zu bytes needed, %zu given", need,
+          workspace ? ws_bytes : (size_t)0);
+  return hip_status(csa2::launch_sparse_attn(
+                        n_q, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv_fp4),
+                        kv_fp4_stride, static_cast<const uint8_t*>(kv_scale), kv_scale_stride,
+                        n_entries, kv_start, topk_idx, ld_idx, k,
+                        static_cast<const uint8_t*>(window_kv), n_window_rows, swa_start, n_swa,
+                        softmax_scale, static_cast<uint16_t*>(out), lse, workspace,
+                        static_cast<hipStream_t>(stream)),
+                    "csa2_sparse_attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Lightning-indexer score on gfx950 MFMA.
+//
+// Score of cache position j for query t (the indexer of "DeepSeek-v4.1 Flash: Pushing the
+// Limits of KV Cache Compression", 2.3.1 and 3.3.2, with 32 indexer heads of dim 128 per
+// "DeepSeek-V4.1-Flash - Architecture", section 2):
+//     s[t,j] = sum_h w[t,h] * ReLU(q_idx[t,h,:] . k_idx[row(t,j),:])
+//
+// One wavefront scores 32 positions per step with eight v_mfma_f32_32x32x16_bf16: the
+// 32 indexer heads are the M dimension, the 32 positions the N dimension and the 128
+// channels the K dimension. Lane l (n = l%32, half = l/32) streams bytes
+// [64*half, 64*half + 64) of row n straight from HBM (four 16-byte loads; a wave reads
+// 32 whole rows = 4 KiB), converts the E4M3 bytes to bf16 in registers (exact) and feeds
+// them as the B operand; the A operand holds q_idx with the same channel assignment, so
+// the K-sum is the plain dot product. The 32x32 fp32 result sits in 16 registers per
+// lane (row = 8*(r/4) + 4*half + r%4, column = l%32); ReLU, the per-head weight and the
+// sum over heads happen in registers plus one cross-half shuffle. Scores and optional
+// 8-slot block maxima are written with coalesced stores. Work per step is 8,192 flops
+// per position against 128 bytes read: HBM-bound at 64 flop/B.
+#include "csa2_device.h"
+#include "csa2_launch.h"
+
+namespace csa2 {
+
+constexpr int IS_THREADS = 256;
+constexpr int IS_STEPS_PER_WAVE = 16;                               // 32 slots each
+constexpr int IS_TILE = (IS_THREADS / 64) * IS_STEPS_PER_WAVE * 32;  // 2048 slots per WG
+
+template <bool REINDEX>
+__global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_cache, int64_t n_entries,
+    const int64_t* __restrict__ kv_start, const int32_t* __restrict__ n_visible,
+    const int32_t* __restrict__ pool_blocks, int n_pool,
+    float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int half = lane >> 5;
+
+  // A operand: head n, channels 64*half + 8*kb + (0..7) for k-block kb.
+  bf16x8 a[8];
+  const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+
+  const int64_t base = kv_start[t];
+  const int64_t nv = n_visible[t];
+  const int64_t tile0 = (int64_t)blockIdx.x * IS_TILE + (int64_t)wave * 32;
+
+  // Resolve the cache row of this lane's slot for a step; -1 when absent.
+  auto row_of = [&](int step, int64_t& slot) -> int64_t {
+    slot = tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n;
+    if (slot >= ld) return -1;
+    int64_t pos = slot;
+    if (REINDEX) {
+      const int64_t pb = slot >> 3;
+      const int b = pb < n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
+      if (b < 0) return -1;
+      pos = (int64_t)b * 8 + (slot & 7);
+    }
+    if (pos >= nv) return -1;
+    const int64_t row = base + pos;
+    return (row >= 0 && row < n_entries) ? row : -1;
+  };
+  auto load = [&](int64_t row, u32x4 (&raw)[4]) {
+    if (row >= 0) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + row * 128 + 64 * half);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = __builtin_nontemporal_load(p + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  int64_t slot_cur;
+  int64_t row_cur = row_of(0, slot_cur);
+  u32x4 raw[4];
+  load(row_cur, raw);
+
+#pragma unroll 1
+  for (int step = 0; step < IS_STEPS_PER_WAVE; ++step) {
+    // Prefetch the next step's rows while this one is multiplied.
+    int64_t slot_nxt = 0, row_nxt = -1;
+    u32x4 raw_nxt[4];
+    if (step + 1 < IS_STEPS_PER_WAVE) {
+      row_nxt = row_of(step + 1, slot_nxt);
+      load(row_nxt, raw_nxt);
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const uint32_t d0 = raw[kb >> 1][(kb & 1) * 2];
+      const uint32_t d1 = raw[kb >> 1][(kb & 1) * 2 + 1];
+      const u32x2 lo = e4m3x4_to_bf16x4(d0);
+      const u32x2 hi = e4m3x4_to_bf16x4(d1);
+      const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
+                                                    0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+    part += __shfl_xor(part, 32);
+    const float s = row_cur >= 0 ? part : -__builtin_inff();
+    if (slot_cur < ld) {
+      if (half == 0) scores[(int64_t)t * ld + slot_cur] = s;
+    }
+    if (block_max != nullptr) {
+      float m = s;
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      if (half == 0 && (n & 7) == 0 && slot_cur < ld)
+        block_max[(int64_t)t * ld_bm + (slot_cur >> 3)] = m;
+    }
+    slot_cur = slot_nxt;
+    row_cur = row_nxt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = raw_nxt[i];
+  }
+}
+
+hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, const float* w,
+                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
+                              const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
+                              float* scores, int64_t ld, float* block_max, int64_t ld_bm,
+                              hipStream_t stream) {
+  const int64_t tiles = (ld + IS_TILE - 1) / IS_TILE;
+  dim3 grid((unsigned)tiles, (unsigned)n_q);
+  if (reindex)
+    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
+                       k_cache, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
+                       block_max, ld_bm);
+  else
+    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
+                       k_cache, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
+                       block_max, ld_bm);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

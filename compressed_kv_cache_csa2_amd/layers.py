@@ -1,0 +1,75 @@
+"""Mode routing of CSA2 layers over the C ABI (caller side: buffers only, no arithmetic).
+
+Full:    index_score(FULL) -> topk (+ block_pool in the decoder's first layer) -> sparse_attn
+Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
+Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
+("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression", 2.3.2 and 3.3.3;
+"DeepSeek-V4.1-Flash - Architecture", section 2, mode table and decoder schedule.)
+All outputs live in buffers allocated once, so a step allocates nothing.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import csa2 as C
+from .synth import POOL_BLOCKS, TOPK, BLOCK
+
+
+@dataclass
+class Buffers:
+    scores: torch.Tensor        # f32 [n_q, ld]
+    block_max: torch.Tensor     # f32 [n_q, ceil(ld/8)]
+    pool: torch.Tensor          # i32 [n_q, 2048]
+    re_scores: torch.Tensor     # f32 [n_q, 16384]
+    idx: torch.Tensor           # i32 [n_layers, n_q, 512] (index layers write their slot)
+    out: torch.Tensor           # bf16 [n_layers, n_q, 64, 512]
+    lse: torch.Tensor           # f32 [n_layers, n_q, 64]
+    workspace: torch.Tensor | None
+    published: list             # per layer: the index tensor it attended with
+
+
+def alloc_buffers(wl, k: int = TOPK) -> Buffers:
+    dev = wl.k_cache.device
+    n_q, n_l = wl.n_q, len(wl.layers)
+    ld = max(8, wl.n_ctx)
+    ws_bytes = C.workspace_bytes(C.OP_SPARSE_ATTN, n_q, 0, k)
+    return Buffers(
+        scores=torch.empty((n_q, ld), dtype=torch.float32, device=dev),
+        block_max=torch.empty((n_q, (ld + BLOCK - 1) // BLOCK), dtype=torch.float32, device=dev),
+        pool=torch.full((n_q, POOL_BLOCKS), -1, dtype=torch.int32, device=dev),
+        re_scores=torch.empty((n_q, POOL_BLOCKS * BLOCK), dtype=torch.float32, device=dev),
+        idx=torch.full((n_l, n_q, k), -1, dtype=torch.int32, device=dev),
+        out=torch.empty((n_l, n_q, 64, 512), dtype=torch.bfloat16, device=dev),
+        lse=torch.empty((n_l, n_q, 64), dtype=torch.float32, device=dev),
+        workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None,
+        published=[None] * n_l,
+    )
+
+
+def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
+    """One pass of the whole layer stack of the workload (one decode or prefill step)."""
+    current = None
+    for li, lay in enumerate(wl.layers):
+        if lay.mode == "full":
+            C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                               buf.scores, buf.block_max, stream=stream)
+            C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
+                        block_max=buf.block_max, stream=stream)
+            if wl.with_pool:
+                C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, POOL_BLOCKS, stream=stream)
+            current = buf.idx[li]
+        elif lay.mode == "reindex":
+            C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                               buf.re_scores, None, pool_blocks=buf.pool, stream=stream)
+            C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
+            current = buf.idx[li]
+        elif lay.mode != "reuse":
+            raise ValueError(f"unknown mode {lay.mode!r}")
+        if current is None:
+            raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
+        buf.published[li] = current
+        C.csa2_sparse_attn(lay.q, wl.kv_fp4, wl.kv_scale, wl.kv_start, current, lay.window_kv,
+                           lay.swa_start, lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
+                           buf.workspace, k=k, stream=stream)

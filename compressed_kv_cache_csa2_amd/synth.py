@@ -71,6 +71,18 @@ class Workload:
     def n_entries(self) -> int:
         return int(self.k_cache.shape[0])
 
+    def to(self, device) -> "Workload":
+        """A copy with every tensor on `device` (same bytes)."""
+        mv = lambda x: None if x is None else x.to(device)
+        layers = [LayerInputs(mode=l.mode, q=mv(l.q), window_kv=mv(l.window_kv),
+                              swa_start=mv(l.swa_start), n_swa=mv(l.n_swa), q_idx=mv(l.q_idx),
+                              w=mv(l.w)) for l in self.layers]
+        return Workload(name=self.name, n_q=self.n_q, n_ctx=self.n_ctx, kv_start=mv(self.kv_start),
+                        n_visible=mv(self.n_visible), k_cache=mv(self.k_cache),
+                        kv_fp4=mv(self.kv_fp4), kv_scale=mv(self.kv_scale), layers=layers,
+                        with_pool=self.with_pool, planted=self.planted,
+                        softmax_scale=self.softmax_scale)
+
 
 # ----------------------------------------------------------------------------- encoders
 
@@ -157,9 +169,9 @@ def _make_layer(mode, n_q, device, seed, li, window_rows=None, swa_start=None, n
 def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, plant_pos,
                     full_layer: LayerInputs):
     """Draw the indexer-K and latent rows of every sequence, planting at plant_pos."""
-    k_cache = torch.empty((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
-    kv_fp4 = torch.empty((n_entries, HEAD_DIM // 2), dtype=torch.uint8, device=device)
-    kv_scale = torch.empty((n_entries, HEAD_DIM // 16), dtype=torch.uint8, device=device)
+    k_cache = torch.zeros((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
+    kv_fp4 = torch.zeros((n_entries, HEAD_DIM // 2), dtype=torch.uint8, device=device)
+    kv_scale = torch.zeros((n_entries, HEAD_DIM // 16), dtype=torch.uint8, device=device)
     starts = kv_start.tolist()
     counts = n_visible.tolist()
     shared = len(set(starts)) == 1 and n_q > 1

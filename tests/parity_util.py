@@ -1,0 +1,74 @@
+"""Helpers shared by the GPU parity tests: host copies, tolerance and band rules.
+
+Acceptance rules:
+  - index sets (Top-K positions, pool blocks) equal the oracle's except for elements whose
+    oracle value lies within 1e-3 relative of the K-th oracle value (1e-3 of the largest
+    magnitude when the K-th value is 0);
+  - attention outputs within max-abs error <= 2e-2 * max|ref|;
+  - indexer scores (fp32 MFMA accumulation of exact products) within 1e-5 of the sum of
+    the absolute values of their terms.
+"""
+import numpy as np
+import torch
+
+import oracle.csa2_oracle as O
+
+BAND_REL = 1e-3
+ATTN_TOL = 2e-2
+SCORE_REL = 1e-5
+
+
+def np_u16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def score_abs_terms(q_bits, w, k_codes):
+    """sum_h |w_h| sum_d |q_hd k_d| for every row: the scale of fp32 rounding in a score."""
+    qa = np.abs(O.bf16_decode(q_bits))
+    ka = np.abs(O.e4m3_decode(k_codes))
+    return (ka @ qa.T) @ np.abs(np.asarray(w, np.float64))
+
+
+def assert_scores_close(gpu, ref, abs_terms, what=""):
+    gpu = np.asarray(gpu, np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(gpu)), f"{what}: -inf pattern differs"
+    assert np.all(gpu[~fin] == ref[~fin]), what
+    err = np.abs(gpu[fin] - ref[fin])
+    lim = SCORE_REL * abs_terms[fin] + 1e-30
+    bad = np.nonzero(err > lim)[0]
+    assert bad.size == 0, f"{what}: {bad.size} scores off, worst {err.max():.3e}"
+
+
+def band_of(ref_values, k):
+    """K-th largest selectable oracle value and the tie band around it."""
+    v = np.asarray(ref_values, np.float64)
+    sel = O.topk_slots(v, k)
+    if sel.size == 0:
+        return None, 0.0
+    kth = v[sel].min()
+    fin = v[np.isfinite(v)]
+    scale = abs(kth) if kth != 0 and np.isfinite(kth) else (np.abs(fin).max() if fin.size else 0.0)
+    return kth, BAND_REL * scale
+
+
+def assert_set_band(gpu_items, ref_items, ref_value_of, kth, band, what=""):
+    """gpu_items and ref_items may differ only in elements whose oracle value is within the
+    band of the K-th value; sizes must agree."""
+    g = set(int(x) for x in gpu_items if x >= 0)
+    r = set(int(x) for x in ref_items if x >= 0)
+    assert len(g) == len([x for x in gpu_items if x >= 0]), f"{what}: duplicate selections"
+    assert len(g) == len(r), f"{what}: {len(g)} selected, oracle {len(r)}"
+    for x in g ^ r:
+        v = ref_value_of(x)
+        assert abs(v - kth) <= band, f"{what}: {x} (value {v}) differs outside the band of {kth}"
+    return g == r
+
+
+def assert_attn_close(gpu_out, ref_out, what=""):
+    gpu = np.asarray(gpu_out, np.float64)
+    ref = np.asarray(ref_out, np.float64)
+    scale = np.abs(ref).max()
+    err = np.abs(gpu - ref).max()
+    assert err <= ATTN_TOL * scale + 1e-30, f"{what}: max-abs err {err:.3e} vs {ATTN_TOL}*{scale:.3e}"
+    return err / scale if scale else 0.0

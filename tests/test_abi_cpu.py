@@ -1,0 +1,103 @@
+"""The C ABI library on the host: it loads, exports every call of include/csa2.h, and
+rejects bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+@pytest.fixture(scope="module")
+def C():
+    from compressed_kv_cache_csa2_amd import csa2
+    return csa2
+
+
+def test_header_symbols_are_exported(C):
+    text = open(HEADER).read()
+    names = set(re.findall(r"^(?:int|size_t|const char\*)\s+(csa2_\w+)\(", text, re.M))
+    assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_block_pool", "csa2_topk",
+                     "csa2_sparse_attn", "csa2_version", "csa2_last_error"}
+    lib = ctypes.CDLL(C._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert C.version().startswith("csa2-gfx950")
+
+
+FAKE = 0x10000   # a 64 KiB-aligned address: never dereferenced, validation fails first
+
+
+def _score(C, **kw):
+    a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE, k_cache=FAKE, n_entries=10,
+             kv_start=FAKE, n_visible=FAKE, pool_blocks=None, n_pool=0, block_size=8, scores=FAKE,
+             ld=16, block_max=None, ld_bm=0, stream=None)
+    a.update(kw)
+    return C.lib.csa2_index_score(*a.values())
+
+
+def test_index_score_rejections(C):
+    assert _score(C, mode=2) == 1 and b"no scoring" in C.lib.csa2_last_error()
+    assert _score(C, n_heads=64) == 2
+    assert _score(C, d_idx=64) == 2
+    assert _score(C, block_size=16) == 2
+    assert _score(C, n_q=-1) == 1
+    assert _score(C, q_idx=None) == 1
+    assert _score(C, q_idx=FAKE + 8) == 1                 # not 16-byte aligned
+    assert _score(C, ld=0) == 1
+    assert _score(C, mode=1) == 1                         # REINDEX without a pool
+    assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2048, ld=100) == 1
+    assert _score(C, pool_blocks=FAKE, n_pool=4) == 1     # FULL with a pool
+    assert _score(C, block_max=FAKE, ld_bm=1) == 1        # ld_bm < ceil(16/8)
+    assert _score(C, n_q=0, q_idx=None) == 0              # nothing to do, nothing launched
+
+
+def test_topk_and_pool_rejections(C):
+    L = C.lib
+    ok = dict(n_q=1, scores=FAKE, ld=100, n_cols=100, n_valid=None, bm=None, ld_bm=0, k=512,
+              pool=None, n_pool=0, bs=8, idx=FAKE, ld_idx=512, ws=None, ws_bytes=0, stream=None)
+
+    def topk(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.csa2_topk(*a.values())
+    assert topk(k=0) == 1 and topk(k=4096) == 1
+    assert topk(bs=4) == 2
+    assert topk(n_cols=101) == 1
+    assert topk(ld_idx=100) == 1
+    assert topk(bm=FAKE, ld_bm=3) == 1
+    assert topk(pool=FAKE, n_pool=4) == 1                # 4 blocks cannot cover 100 slots
+    assert topk(scores=None) == 1
+    assert topk(n_q=0, scores=None) == 0
+    assert L.csa2_block_pool(1, FAKE, 10, FAKE, 8, 0, FAKE, 2048, None, 0, None) == 1
+    assert L.csa2_block_pool(1, FAKE, 10, FAKE, 8, 2049, FAKE, 4096, None, 0, None) == 1
+    assert L.csa2_block_pool(1, FAKE, 10, FAKE, 4, 2048, FAKE, 2048, None, 0, None) == 2
+    assert L.csa2_block_pool(1, FAKE, 10, FAKE, 8, 2048, FAKE, 100, None, 0, None) == 1
+    assert L.csa2_block_pool(0, None, 10, None, 8, 2048, None, 2048, None, 0, None) == 0
+
+
+def test_sparse_attn_rejections_and_workspace(C):
+    L = C.lib
+    need = C.workspace_bytes(C.OP_SPARSE_ATTN, 32, 0, 512)
+    assert need > 0
+    assert C.workspace_bytes(C.OP_SPARSE_ATTN, 4096, 0, 512) == 0
+    assert C.workspace_bytes(C.OP_TOPK, 32, 262144, 512) == 0
+    ok = dict(n_q=32, heads=64, dim=512, q=FAKE, fp4=FAKE, fs=256, sc=FAKE, ss=32, ne=100,
+              kv_start=FAKE, idx=FAKE, ld_idx=512, k=512, win=FAKE, nw=10, swa_start=FAKE,
+              n_swa=FAKE, scale=0.04, out=FAKE, lse=None, ws=FAKE, ws_bytes=need, stream=None)
+
+    def attn(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.csa2_sparse_attn(*a.values())
+    assert attn(heads=32) == 2 and attn(dim=256) == 2
+    assert attn(k=-1) == 1 and attn(k=4096) == 1
+    assert attn(fs=128) == 1 and attn(fs=264) == 1
+    assert attn(ss=16) == 1
+    assert attn(q=FAKE + 4) == 1
+    assert attn(ws_bytes=need - 1) == 3 and b"workspace" in L.csa2_last_error()
+    assert attn(ws=None) == 3
+    assert attn(out=None) == 1
+    assert attn(n_q=0, q=None) == 0

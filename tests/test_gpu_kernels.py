@@ -1,0 +1,296 @@
+"""GPU parity of each C ABI call against the fp64 oracle, on seeded inputs at sizes the
+oracle finishes in seconds (several tiles, ragged tails, empty and degenerate cases)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.csa2_oracle as O
+from tests.parity_util import (assert_attn_close, assert_scores_close, np_u16,
+                               score_abs_terms)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def C(dev):
+    from compressed_kv_cache_csa2_amd import csa2
+    return csa2
+
+
+def _i32(x, dev):
+    return torch.tensor(x, dtype=torch.int32, device=dev)
+
+
+def _i64(x, dev):
+    return torch.tensor(x, dtype=torch.int64, device=dev)
+
+
+def _bf16(shape, gen, dev, scale=1.0):
+    return (torch.randn(shape, generator=gen) * scale).to(torch.bfloat16).to(dev)
+
+
+def _e4m3(shape, gen, dev):
+    from compressed_kv_cache_csa2_amd.synth import encode_e4m3
+    return encode_e4m3(torch.randn(shape, generator=gen)).to(dev)
+
+
+# --------------------------------------------------------------------------- indexer
+
+def test_indexer_one_hot_reads_every_e4m3_code_in_place(C, dev):
+    """Row r, channel c holds code (r + 3c) % 256 (NaN codes replaced); a one-hot indexer
+    query on channel c with weight 1 scores ReLU(+-value): every code at every channel."""
+    rows = np.arange(256)[:, None]
+    chans = np.arange(128)[None, :]
+    codes = ((rows + 3 * chans) % 256).astype(np.uint8)
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0
+    k_cache = torch.from_numpy(codes).to(dev)
+    tests = [(c, h, s) for c, h, s in zip([0, 1, 2, 3, 8, 63, 64, 65, 100, 127] * 2,
+                                          list(range(0, 20)), [1.0] * 10 + [-1.0] * 10)]
+    n_q = len(tests)
+    q = torch.zeros((n_q, 32, 128), dtype=torch.float32)
+    w = torch.zeros((n_q, 32), dtype=torch.float32)
+    for t, (c, h, s) in enumerate(tests):
+        q[t, h, c] = s
+        w[t, h] = 1.0
+    q = q.to(torch.bfloat16).to(dev)
+    w = w.to(dev)
+    scores = torch.empty((n_q, 256), dtype=torch.float32, device=dev)
+    C.csa2_index_score(C.FULL, q, w, k_cache, _i64([0] * n_q, dev), _i32([256] * n_q, dev), scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    for t in range(n_q):
+        ref = O.full_scores(np_u16(q[t]), w[t].cpu().numpy(), codes, 0, 256, 256)
+        assert np.array_equal(got[t].astype(np.float64), ref), f"query {t} {tests[t]}"
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged"])
+def test_index_score_full_parity(C, dev, case):
+    from compressed_kv_cache_csa2_amd import synth
+    if case == "tiny":
+        wl = synth.make_workload("tiny_decode_4k").to(dev)
+        ld = 4096
+    else:
+        # ragged: empty, single, sub-block and multi-tile sequences with gaps; the last
+        # query's rows run past the end of the cache (absent rows score -inf)
+        wl = synth.make_decode("ragged", 6, 0, ("full",), False, 0,
+                               n_visible=[0, 1, 7, 4099, 2500, 9000], kv_gap=5, seed=3).to(dev)
+        wl.n_visible[5] = 9000 + 37
+        ld = 9100
+    lay = wl.layers[0]
+    scores = torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev)
+    bmax = torch.empty((wl.n_q, (ld + 7) // 8), dtype=torch.float32, device=dev)
+    C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, scores, bmax)
+    torch.cuda.synchronize()
+    k_all = wl.k_cache.cpu().numpy()
+    got = scores.cpu().numpy()
+    for t in range(wl.n_q):
+        start, nv = int(wl.kv_start[t]), int(wl.n_visible[t])
+        n_rows = max(0, min(nv, k_all.shape[0] - start))
+        ref = O.full_scores(np_u16(lay.q_idx[t]), lay.w[t].cpu().numpy(), k_all, start, n_rows, ld)
+        terms = np.zeros(ld)
+        if n_rows:
+            terms[:n_rows] = score_abs_terms(np_u16(lay.q_idx[t]), lay.w[t].cpu().numpy(),
+                                             k_all[start:start + n_rows])
+        assert_scores_close(got[t], ref, terms, f"query {t}")
+    # block maxima are the maxima of the kernel's own scores
+    pad = np.full((wl.n_q, bmax.shape[1] * 8), -np.inf, np.float32)
+    pad[:, :ld] = got
+    assert np.array_equal(bmax.cpu().numpy(), pad.reshape(wl.n_q, -1, 8).max(axis=2))
+
+
+def test_index_score_reindex_parity(C, dev):
+    from compressed_kv_cache_csa2_amd import synth
+    wl = synth.make_decode("pool", 3, 0, ("full",), False, 0, n_visible=[20000, 777, 16384],
+                           kv_gap=11, seed=4).to(dev)
+    g = torch.Generator().manual_seed(5)
+    pool = torch.full((3, 2048), -1, dtype=torch.int32)
+    for t, nv in enumerate([20000, 777, 16384]):
+        nb = (nv + 7) // 8
+        m = min(2048, nb)
+        ids = torch.randperm(nb, generator=g)[:m].sort().values.to(torch.int32)
+        pool[t, :m] = ids
+    pool[0, 5] = 2600          # beyond n_visible: -inf slots
+    pool[2, 2047] = -1
+    pool = pool.to(dev)
+    q_idx = _bf16((3, 32, 128), g, dev)
+    w = torch.rand((3, 32), generator=g).to(dev)
+    scores = torch.empty((3, 16384), dtype=torch.float32, device=dev)
+    C.csa2_index_score(C.REINDEX, q_idx, w, wl.k_cache, wl.kv_start, wl.n_visible, scores,
+                       pool_blocks=pool)
+    torch.cuda.synchronize()
+    k_all = wl.k_cache.cpu().numpy()
+    got = scores.cpu().numpy()
+    for t in range(3):
+        start, nv = int(wl.kv_start[t]), int(wl.n_visible[t])
+        ref = O.reindex_scores(np_u16(q_idx[t]), w[t].cpu().numpy(), k_all, start, nv,
+                               pool[t].cpu().numpy())
+        pos = O.slots_to_positions(np.arange(16384), pool[t].cpu().numpy())
+        ok = np.isfinite(ref)
+        terms = np.zeros(16384)
+        terms[ok] = score_abs_terms(np_u16(q_idx[t]), w[t].cpu().numpy(), k_all[start + pos[ok]])
+        assert_scores_close(got[t], ref, terms, f"query {t}")
+
+
+# --------------------------------------------------------------------------- selection
+
+def _score_rows(kind, n_q, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "normal":
+        s = torch.randn((n_q, n), generator=g) * 30 + 70
+    elif kind == "ties":
+        s = torch.randint(-3, 4, (n_q, n), generator=g).float()
+    elif kind == "zeros":
+        s = torch.zeros((n_q, n))
+    else:
+        raise ValueError(kind)
+    m = torch.rand((n_q, n), generator=g)
+    s[m < 0.05] = -math.inf
+    s[(m > 0.05) & (m < 0.052)] = math.inf
+    return s
+
+
+@pytest.mark.parametrize("kind,n,k,use_bmax", [
+    ("normal", 4096, 512, False), ("normal", 5000, 512, True), ("normal", 16384, 2048, False),
+    ("normal", 40000, 512, False), ("normal", 40000, 512, True), ("normal", 100003, 512, True),
+    ("ties", 3000, 512, False), ("ties", 70000, 512, True), ("ties", 70000, 100, False),
+    ("zeros", 50000, 512, True), ("normal", 300, 512, True), ("normal", 1, 512, False),
+])
+def test_topk_exact(C, dev, kind, n, k, use_bmax):
+    n_q = 3
+    s = _score_rows(kind, n_q, n, seed=n + k)
+    n_valid = torch.tensor([n, max(0, n - 13), n // 2], dtype=torch.int32)
+    sd = s.to(dev)
+    bm = None
+    if use_bmax:
+        nb = (n + 7) // 8
+        pad = torch.full((n_q, nb * 8), -math.inf)
+        pad[:, :n] = s
+        bm = pad.view(n_q, nb, 8).amax(dim=2).to(dev)
+    out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    C.csa2_topk(sd, out, k=k, n_valid=n_valid.to(dev), block_max=bm)
+    torch.cuda.synchronize()
+    for t in range(n_q):
+        nv = int(n_valid[t])
+        ref = O.topk_slots(s[t, :nv].double().numpy(), k)
+        want = np.full(k, -1, np.int64)
+        want[:len(ref)] = ref
+        assert np.array_equal(out[t].cpu().numpy(), want), f"row {t}"
+
+
+def test_topk_pool_mapping(C, dev):
+    n_q, k = 2, 512
+    s = _score_rows("normal", n_q, 16384, seed=9)
+    pool = torch.full((n_q, 2048), -1, dtype=torch.int32)
+    pool[0] = torch.arange(2048, dtype=torch.int32) * 3 + 1
+    pool[1, :1000] = torch.arange(1000, dtype=torch.int32) * 7
+    s[1, 8000:] = -math.inf
+    out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    C.csa2_topk(s.to(dev), out, k=k, pool_blocks=pool.to(dev))
+    torch.cuda.synchronize()
+    for t in range(n_q):
+        ref = O.slots_to_positions(O.topk_slots(s[t].double().numpy(), k), pool[t].numpy())
+        assert np.array_equal(out[t].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("kind,nvis", [("normal", [40000, 16385, 1000, 0, 7]),
+                                       ("ties", [200000, 9, 16384 * 8 + 3, 8, 17])])
+def test_block_pool_exact(C, dev, kind, nvis):
+    n_q = len(nvis)
+    width = max(nvis)
+    s = _score_rows(kind, n_q, width, seed=width)
+    s[s == math.inf] = 1e30
+    nb = (width + 7) // 8
+    pad = torch.full((n_q, nb * 8), -math.inf)
+    for t, nv in enumerate(nvis):
+        pad[t, :nv] = s[t, :nv]
+    bm = pad.view(n_q, nb, 8).amax(dim=2)
+    pool = torch.empty((n_q, 2048), dtype=torch.int32, device=dev)
+    C.csa2_block_pool(bm.to(dev), _i32(nvis, dev), pool)
+    torch.cuda.synchronize()
+    for t, nv in enumerate(nvis):
+        ref = O.hsi_pool(s[t, :nv].double().numpy(), nv)
+        want = np.full(2048, -1, np.int64)
+        want[:len(ref)] = ref
+        assert np.array_equal(pool[t].cpu().numpy(), want), f"row {t}"
+
+
+# --------------------------------------------------------------------------- attention
+
+def _attn_case(n_q, k, n_entries, n_swa, seed, dev, dup=False, holes=True):
+    from compressed_kv_cache_csa2_amd import synth
+    g = torch.Generator().manual_seed(seed)
+    lat = torch.randn((n_entries, 512), generator=g)
+    p, s = synth.encode_fp4_rows(lat)
+    q = _bf16((n_q, 64, 512), g, dev)
+    kv_start = torch.randint(0, max(1, n_entries // 4), (n_q,), generator=g)
+    idx = torch.full((n_q, max(k, 1)), -1, dtype=torch.int32)
+    for t in range(n_q):
+        span = n_entries - int(kv_start[t])
+        sel = torch.randint(0, span, (k,), generator=g) if dup else torch.randperm(span, generator=g)[:k]
+        idx[t, :len(sel)] = sel.to(torch.int32)
+        if holes and k > 4:
+            idx[t, 3] = -1
+            idx[t, 1] = span + 5     # row past the end of its sequence but maybe in the cache
+            idx[t, 2] = n_entries * 4  # row outside the cache: skipped
+    win_rows = n_q * 128 + 3
+    window = _e4m3((win_rows, 512), g, dev)
+    swa_start = torch.arange(n_q, dtype=torch.int64) * 128
+    nsw = torch.full((n_q,), n_swa, dtype=torch.int32)
+    return dict(q=q, kv_fp4=p.to(dev), kv_scale=s.to(dev), kv_start=kv_start.to(dev), idx=idx,
+                window=window, swa_start=swa_start.to(dev), n_swa=nsw.to(dev), k=k)
+
+
+@pytest.mark.parametrize("n_q,k,n_swa", [(1, 512, 128), (32, 512, 128), (3, 100, 0), (2, 0, 128),
+                                         (2, 0, 0), (600, 64, 17), (5, 2048, 128)])
+def test_sparse_attn_parity(C, dev, n_q, k, n_swa):
+    case = _attn_case(n_q, k, 6000, n_swa, seed=n_q * 1000 + k + n_swa, dev=dev, dup=(n_q == 3))
+    idx_d = case["idx"].to(dev)
+    out = torch.empty((n_q, 64, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+    need = C.workspace_bytes(C.OP_SPARSE_ATTN, n_q, 0, k)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    C.csa2_sparse_attn(case["q"], case["kv_fp4"], case["kv_scale"], case["kv_start"], idx_d,
+                       case["window"], case["swa_start"], case["n_swa"], 1 / math.sqrt(512), out,
+                       lse, ws, k=k)
+    torch.cuda.synchronize()
+    p_all, s_all = case["kv_fp4"].cpu().numpy(), case["kv_scale"].cpu().numpy()
+    win = case["window"].cpu().numpy()
+    n_entries = p_all.shape[0]
+    for t in list(range(n_q))[:40]:
+        start = int(case["kv_start"][t])
+        pos = case["idx"][t, :k].numpy().astype(np.int64)
+        pos = pos[(pos >= 0) & (start + pos < n_entries)]
+        ents = O.gather_attention_entries(pos, p_all, s_all, start, win,
+                                          int(case["swa_start"][t]), n_swa)
+        ref, ref_lse = O.sparse_attention(O.bf16_decode(np_u16(case["q"][t])), ents, 1 / math.sqrt(512))
+        got = out[t].float().cpu().numpy()
+        if ents.shape[0] == 0:
+            assert np.all(got == 0) and np.all(np.isneginf(lse[t].cpu().numpy()))
+            continue
+        assert_attn_close(got, ref, f"query {t}")
+        assert np.allclose(lse[t].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+
+
+def test_sparse_attn_single_entry_and_constant_query(C, dev):
+    """Closed forms through the kernel: one attended entry is returned exactly (bf16 of an
+    exactly representable vector); q = 0 gives the mean of the attended entries."""
+    case = _attn_case(2, 16, 500, 0, seed=77, dev=dev, holes=False)
+    idx = torch.full((2, 16), -1, dtype=torch.int32)
+    idx[0, 7] = 42
+    idx[1, :16] = case["idx"][1, :16]
+    q = case["q"].clone()
+    q[1].zero_()
+    out = torch.empty((2, 64, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(1, C.workspace_bytes(C.OP_SPARSE_ATTN, 2, 0, 16)), dtype=torch.uint8, device=dev)
+    C.csa2_sparse_attn(q, case["kv_fp4"], case["kv_scale"], case["kv_start"], idx.to(dev),
+                       case["window"], case["swa_start"], case["n_swa"], 0.1, out, None, ws)
+    torch.cuda.synchronize()
+    p_all, s_all = case["kv_fp4"].cpu().numpy(), case["kv_scale"].cpu().numpy()
+    row = int(case["kv_start"][0]) + 42
+    one = O.fp4_latent_decode(p_all[row], s_all[row])
+    assert np.array_equal(out[0].float().cpu().numpy(), np.repeat(one[None], 64, 0))
+    start = int(case["kv_start"][1])
+    ents = O.fp4_latent_decode(p_all[start + idx[1].numpy()], s_all[start + idx[1].numpy()])
+    assert_attn_close(out[1].float().cpu().numpy(), np.repeat(ents.mean(0)[None], 64, 0), "q=0")
