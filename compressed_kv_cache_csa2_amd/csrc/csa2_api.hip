@@ -119,8 +119,10 @@ int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm, const int32_
   REQUIRE(ld_bm >= 1 && ld_pool >= n_keep, CSA2_ERR_INVALID_ARG,
           "csa2_block_pool: bad leading dimension (ld_bm %lld, ld_pool %lld)", (long long)ld_bm,
           (long long)ld_pool);
-  REQUIRE(aligned(block_max, 4) && aligned(n_visible, 4) && aligned(pool_blocks, 4),
-          CSA2_ERR_INVALID_ARG, "csa2_block_pool: misaligned argument");
+  REQUIRE(aligned(block_max, 16) && ld_bm % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_block_pool: block_max must be 16-byte aligned with ld_bm a multiple of 4");
+  REQUIRE(aligned(n_visible, 4) && aligned(pool_blocks, 4), CSA2_ERR_INVALID_ARG,
+          "csa2_block_pool: misaligned argument");
   return hip_status(csa2::launch_block_pool(n_q, block_max, ld_bm, n_visible, n_keep, pool_blocks,
                                             ld_pool, static_cast<hipStream_t>(stream)),
                     "csa2_block_pool");
@@ -143,11 +145,15 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
           "csa2_topk: need 0 <= n_cols <= ld_scores <= 2^31 (n_cols %lld, ld %lld)",
           (long long)n_cols, (long long)ld_scores);
   REQUIRE(ld_idx >= k, CSA2_ERR_INVALID_ARG, "csa2_topk: ld_idx %lld < k", (long long)ld_idx);
-  REQUIRE(aligned(scores, 4) && aligned(topk_idx, 4) && aligned(n_valid, 4) && aligned(block_max, 4),
-          CSA2_ERR_INVALID_ARG, "csa2_topk: misaligned argument");
+  REQUIRE(aligned(scores, 16) && ld_scores % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_topk: scores must be 16-byte aligned with ld_scores a multiple of 4");
+  REQUIRE(aligned(topk_idx, 4) && aligned(n_valid, 4), CSA2_ERR_INVALID_ARG,
+          "csa2_topk: misaligned argument");
   if (block_max != nullptr)
-    REQUIRE(ld_block_max >= (n_cols + 7) / 8, CSA2_ERR_INVALID_ARG,
-            "csa2_topk: ld_block_max %lld < ceil(n_cols/8)", (long long)ld_block_max);
+    REQUIRE(ld_block_max >= (n_cols + 7) / 8 && ld_block_max % 4 == 0 && aligned(block_max, 16),
+            CSA2_ERR_INVALID_ARG,
+            "csa2_topk: block_max must be 16-byte aligned with ld_block_max >= ceil(n_cols/8) "
+            "and a multiple of 4 (got %lld)", (long long)ld_block_max);
   if (pool_blocks != nullptr)
     REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K && n_cols <= (int64_t)n_pool * block_size,
             CSA2_ERR_INVALID_ARG, "csa2_topk: pool of %d blocks cannot cover %lld slots", n_pool,

@@ -22,8 +22,11 @@
 namespace csa2 {
 
 constexpr int IS_THREADS = 256;
-constexpr int IS_STEPS_PER_WAVE = 16;                               // 32 slots each
-constexpr int IS_TILE = (IS_THREADS / 64) * IS_STEPS_PER_WAVE * 32;  // 2048 slots per WG
+// Steps of 32 slots per wave: a Full-layer workgroup scores 4 x 16 x 32 = 2,048 slots;
+// a Reindex workgroup 512 (the pool is only 16,384 slots per query, so smaller tiles keep
+// every CU busy).
+constexpr int IS_STEPS_FULL = 16;
+constexpr int IS_STEPS_REINDEX = 4;
 
 template <bool REINDEX>
 __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
@@ -49,6 +52,8 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
 
   const int64_t base = kv_start[t];
   const int64_t nv = n_visible[t];
+  constexpr int IS_STEPS_PER_WAVE = REINDEX ? IS_STEPS_REINDEX : IS_STEPS_FULL;
+  constexpr int IS_TILE = (IS_THREADS / 64) * IS_STEPS_PER_WAVE * 32;
   const int64_t tile0 = (int64_t)blockIdx.x * IS_TILE + (int64_t)wave * 32;
 
   // Resolve the cache row of this lane's slot for a step; -1 when absent.
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     if (row >= 0) {
       const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + row * 128 + 64 * half);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = __builtin_nontemporal_load(p + i);
+      for (int i = 0; i < 4; ++i) raw[i] = p[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
@@ -130,7 +135,8 @@ hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, cons
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream) {
-  const int64_t tiles = (ld + IS_TILE - 1) / IS_TILE;
+  const int tile = (IS_THREADS / 64) * (reindex ? IS_STEPS_REINDEX : IS_STEPS_FULL) * 32;
+  const int64_t tiles = (ld + tile - 1) / tile;
   dim3 grid((unsigned)tiles, (unsigned)n_q);
   if (reindex)
     hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_THREADS), 0, stream, q_idx, w,

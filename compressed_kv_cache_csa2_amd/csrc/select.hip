@@ -6,42 +6,53 @@
 // Hierarchical Sparse Indexer ("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache
 // Compression", 2.3.4; "DeepSeek-V4.1-Flash - Architecture", section 3).
 //
-// One 1024-thread workgroup per query row:
-//   1. radix select on order-preserving 32-bit keys, three passes of 11/11/10 bits with
-//      an LDS histogram each, finds the k-th largest key tau and how many keys exceed it;
-//   2. one ordered pass keeps every key > tau and the first (k - #greater) keys == tau in
-//      index order. Ranks come from wave ballots and a 16-wave prefix, so the output is
-//      deterministic and already sorted.
-// Rows that fit in LDS are staged there once; longer rows are streamed from global
-// memory (L2/MALL-resident right after the indexer wrote them).
+// One 512-thread workgroup per query row. Values become order-preserving 32-bit keys
+// (0 marks an element that cannot be selected); thread t owns 64 consecutive elements and
+// keeps their keys in registers (rows longer than 32,768 are walked in segments).
+//   1. A block reduction gives the count, the smallest and the largest key.
+//   2. Range refinement: the live key interval [A, B] is split into at most 2,048 equal
+//      power-of-two bins, an LDS histogram of the keys inside [A, B] is taken, and the bin
+//      holding the k-th largest key becomes the new interval. Bins follow the data's own
+//      key range, so the first histogram spreads over many bins (few atomic collisions);
+//      the interval shrinks by 2^11 per pass, so three passes at most reach one key tau.
+//   3. Emission: every key > tau is kept, and of the keys == tau the lowest-indexed
+//      (k - #greater). Two block-wide prefix sums (ties, then kept) give each thread its
+//      output offsets; output is deterministic and sorted by index.
 //
-// Block prefilter for Top-K: if block maxima of 8-slot blocks are given, the k-th largest
-// block maximum m_k bounds the k-th largest score from below (k blocks each hold a score
-// >= m_k), so every winner lies in a block whose maximum is >= m_k. Only those blocks'
-// scores are gathered (usually k*8 = 4,096 slots instead of the whole row) and selected
-// exactly; ties at the threshold keep every tied block, and if more than 2,048 blocks
-// tie the kernel falls back to the full row.
+// Block prefilter for Top-K: with maxima of 8-slot blocks, any threshold T such that at
+// least k blocks have maximum >= T bounds the k-th largest score from below (each of those
+// blocks holds a score >= T), so every winner lies in a block whose maximum is >= T. One
+// or two refinement passes over the block maxima give such a T with few extra blocks;
+// only those blocks' scores (typically ~600 blocks instead of the whole row) are then
+// selected exactly. If more than 2,048 blocks tie at the threshold the full row is used.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
 namespace csa2 {
 
-constexpr int SEL_THREADS = 1024;
+constexpr int SEL_THREADS = 512;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int KEYS_CAP = 16384;
+constexpr int SEL_R = 64;                       // keys per thread per segment
+constexpr int SEL_SEG = SEL_THREADS * SEL_R;    // 32,768 keys per segment
+constexpr int NBINS = 2048;
 constexpr int CAND_BLOCKS_CAP = 2048;
+constexpr int BINS_PER_THREAD = NBINS / SEL_THREADS;
 
 struct SelShared {
-  uint32_t hist[2048];
-  uint32_t keys[KEYS_CAP];
-  int32_t cblocks[CAND_BLOCKS_CAP];
+  uint32_t hist[NBINS];
   uint32_t wsum[SEL_WAVES];
-  uint32_t wsum2[SEL_WAVES];
+  uint32_t wmin[SEL_WAVES];
+  uint32_t wmax[SEL_WAVES];
   uint32_t scal[4];
+  int32_t cblocks[CAND_BLOCKS_CAP];
 };
 
-// Inclusive prefix sum over the 1024 threads of the block; *total receives the sum.
-__device__ uint32_t block_inclusive_scan(uint32_t v, SelShared& sh, uint32_t* total) {
+// Unsigned minimum / maximum (the device min/max overloads compare as signed int).
+__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Exclusive prefix sum over the block's threads; *total receives the block sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, SelShared& sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -52,6 +63,7 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, SelShared& sh, uint32_t* to
   if (lane == 63) sh.wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
+#pragma unroll
   for (int i = 0; i < SEL_WAVES; ++i) {
     const uint32_t s = sh.wsum[i];
     before += i < wave ? s : 0u;
@@ -59,114 +71,258 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, SelShared& sh, uint32_t* to
   }
   __syncthreads();
   *total = all;
-  return before + x;
+  return before + x - v;
 }
 
-struct KthResult {
-  uint32_t tau;     // k-th largest key (0 when total <= k: every valid key qualifies)
-  uint32_t n_take_eq;  // how many keys equal to tau are kept
-  uint32_t total;   // number of valid keys
+// The keys of one row: thread tid holds elements seg*SEG + tid*R + r in keys[r].
+template <class Src>
+struct KeyRow {
+  Src src;
+  int64_t n;
+  int nseg;
+  uint32_t keys[SEL_R];
+  int loaded;
+
+  __device__ __forceinline__ KeyRow(const Src& s, int64_t n_) : src(s), n(n_), nseg((int)((n_ + SEL_SEG - 1) / SEL_SEG)), loaded(-1) {}
+
+  __device__ __forceinline__ void load(int seg) {
+    if (seg == loaded) return;
+    const int64_t base = (int64_t)seg * SEL_SEG + (int64_t)threadIdx.x * SEL_R;
+    src.load(base, n, keys);
+    loaded = seg;
+  }
 };
 
-// Key source: get(i, &key) returns false for an element that cannot be selected.
-template <class Get>
-__device__ KthResult radix_kth(Get get, int64_t n, uint32_t k, SelShared& sh) {
+// Refinement passes over [A, B], which holds the k-th largest key; `need` is how many
+// keys to take from [A, B] (so k - need keys lie above B). Stops when A == B (then A is
+// the k-th largest key and `need` keys equal to it are taken), or, when cap > 0, as soon
+// as at most cap keys are >= A (A is then a lower bound of the k-th largest key).
+template <class Row>
+__device__ __forceinline__ void refine(Row& row, uint32_t& A, uint32_t& B, uint32_t& need, uint32_t k,
+                       uint32_t cap, SelShared& sh) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, need = k;
-  KthResult res{0u, 0u, 0u};
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int width = pass == 2 ? 10 : 11;
-    const uint32_t dmask = (1u << width) - 1u;
-    sh.hist[tid] = 0;
-    sh.hist[tid + SEL_THREADS] = 0;
+  while (A != B) {
+    const uint32_t span = B - A;
+    const int bits = 32 - __clz(span);                 // span < 2^bits
+    const int s = bits > 11 ? bits - 11 : 0;           // (span >> s) < 2048
+#pragma unroll
+    for (int j = 0; j < BINS_PER_THREAD; ++j) sh.hist[tid + j * SEL_THREADS] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += SEL_THREADS) {
-      uint32_t key;
-      if (get(i, key) && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    for (int seg = 0; seg < row.nseg; ++seg) {
+      row.load(seg);
+#pragma unroll
+      for (int r = 0; r < SEL_R; ++r) {
+        const uint32_t key = row.keys[r];
+        if (key != 0u && key >= A && key <= B) atomicAdd(&sh.hist[(key - A) >> s], 1u);
+      }
     }
     __syncthreads();
-    // Thread tid owns bins 2*tid and 2*tid+1 (bins beyond the digit range are zero).
-    const uint32_t h0 = sh.hist[2 * tid], h1 = sh.hist[2 * tid + 1];
+    // Thread tid owns bins BPT*tid .. BPT*tid + BPT-1.
+    uint32_t h[BINS_PER_THREAD];
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < BINS_PER_THREAD; ++j) {
+      h[j] = sh.hist[BINS_PER_THREAD * tid + j];
+      local += h[j];
+    }
     uint32_t total;
-    const uint32_t incl = block_inclusive_scan(h0 + h1, sh, &total);
-    if (pass == 0) {
-      res.total = total;
-      if (total <= k) return res;  // every valid key is kept
-    }
-    const uint32_t above1 = total - incl;      // keys in bins above 2*tid+1
-    const uint32_t above0 = above1 + h1;       // keys in bins above 2*tid
-    if (above1 < need && need <= above1 + h1) {
-      sh.scal[0] = 2 * tid + 1;
-      sh.scal[1] = above1;
-    } else if (above0 < need && need <= above0 + h0) {
-      sh.scal[0] = 2 * tid;
-      sh.scal[1] = above0;
+    const uint32_t excl = block_exclusive_scan(local, sh, &total);
+    uint32_t above = total - excl - local;   // keys in bins above this thread's bins
+#pragma unroll
+    for (int j = BINS_PER_THREAD - 1; j >= 0; --j) {
+      if (above < need && need <= above + h[j]) {
+        sh.scal[0] = BINS_PER_THREAD * tid + j;
+        sh.scal[1] = above;
+        sh.scal[2] = above + h[j];
+      }
+      above += h[j];
     }
     __syncthreads();
-    const uint32_t d = sh.scal[0];
-    need -= sh.scal[1];
-    prefix |= d << shift;
-    mask |= dmask << shift;
+    const uint32_t b = sh.scal[0];
+    const uint32_t above_b = sh.scal[1];
+    const uint32_t through = sh.scal[2];
     __syncthreads();
+    const uint64_t lo = (uint64_t)A + ((uint64_t)b << s);
+    const uint64_t hi = lo + (1ull << s) - 1;
+    const uint32_t ge = (k - need) + through;   // keys >= the new A
+    need -= above_b;
+    A = (uint32_t)lo;
+    B = hi < (uint64_t)B ? (uint32_t)hi : B;
+    if (cap != 0u && ge <= cap) break;
   }
-  res.tau = prefix;
-  res.n_take_eq = need;
-  return res;
 }
 
-// Keeps keys > tau and the first n_take_eq keys == tau in index order; emit(rank, i) is
-// called with consecutive ranks in ascending i. Returns the number kept. With
-// take_all_eq every key >= tau is kept.
-template <class Get, class Emit>
-__device__ uint32_t collect_ordered(Get get, int64_t n, uint32_t tau, uint32_t n_take_eq,
-                                    bool take_all_eq, SelShared& sh, Emit emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+// Count / min / max of the valid keys of the row.
+template <class Row>
+__device__ __forceinline__ void row_stats(Row& row, uint32_t& count, uint32_t& kmin, uint32_t& kmax,
+                          SelShared& sh) {
+  uint32_t c = 0, mn = 0xFFFFFFFFu, mx = 0u;
+  for (int seg = 0; seg < row.nseg; ++seg) {
+    row.load(seg);
+#pragma unroll
+    for (int r = 0; r < SEL_R; ++r) {
+      const uint32_t key = row.keys[r];
+      if (key != 0u) {
+        ++c;
+        mn = umin32(mn, key);
+        mx = umax32(mx, key);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    c += __shfl_xor(c, off);
+    mn = umin32(mn, (uint32_t)__shfl_xor(mn, off));
+    mx = umax32(mx, (uint32_t)__shfl_xor(mx, off));
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sh.wsum[wave] = c;
+    sh.wmin[wave] = mn;
+    sh.wmax[wave] = mx;
+  }
+  __syncthreads();
+  c = 0;
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < SEL_WAVES; ++i) {
+    c += sh.wsum[i];
+    mn = umin32(mn, sh.wmin[i]);
+    mx = umax32(mx, sh.wmax[i]);
+  }
+  __syncthreads();
+  count = c;
+  kmin = mn;
+  kmax = mx;
+}
+
+// Emit, in ascending index order, every key > tau and the first n_eq keys == tau
+// (tau = 0 with n_eq = 0 keeps every valid key). emit(rank, index). Returns the count.
+template <class Row, class Emit>
+__device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_t n_eq, SelShared& sh,
+                                 Emit emit) {
   uint32_t eq_base = 0, out_base = 0;
-#pragma unroll 1
-  for (int64_t c0 = 0; c0 < n; c0 += SEL_THREADS) {
-    const int64_t i = c0 + tid;
-    uint32_t key = 0;
-    const bool valid = i < n && get(i, key);
-    const bool gt = valid && key > tau;
-    const bool eq = valid && key == tau;
-    const uint64_t m_eq = __ballot(eq);
-    if (lane == 0) sh.wsum[wave] = __popcll(m_eq);
-    __syncthreads();
-    uint32_t eq_before = 0, eq_total = 0;
-    for (int w = 0; w < SEL_WAVES; ++w) {
-      const uint32_t s = sh.wsum[w];
-      eq_before += w < wave ? s : 0u;
-      eq_total += s;
+  for (int seg = 0; seg < row.nseg; ++seg) {
+    row.load(seg);
+    uint64_t gt_mask = 0, eq_mask = 0;
+#pragma unroll
+    for (int r = 0; r < SEL_R; ++r) {
+      const uint32_t key = row.keys[r];
+      gt_mask |= (uint64_t)(key != 0u && key > tau) << r;
+      eq_mask |= (uint64_t)(key != 0u && key == tau) << r;
     }
-    const uint32_t eq_rank = eq_base + eq_before + __popcll(m_eq & lt_mask);
-    const bool take = gt || (eq && (take_all_eq || eq_rank < n_take_eq));
-    const uint64_t m_take = __ballot(take);
-    if (lane == 0) sh.wsum2[wave] = __popcll(m_take);
-    __syncthreads();
-    uint32_t take_before = 0, take_total = 0;
-    for (int w = 0; w < SEL_WAVES; ++w) {
-      const uint32_t s = sh.wsum2[w];
-      take_before += w < wave ? s : 0u;
-      take_total += s;
+    const uint32_t n_e = __popcll(eq_mask);
+    uint32_t eq_total;
+    const uint32_t eq_before = eq_base + block_exclusive_scan(n_e, sh, &eq_total);
+    // ties kept by this thread: ranks eq_before .. eq_before + n_e - 1 below n_eq
+    const uint32_t eq_keep = eq_before >= n_eq ? 0u : umin32(n_e, n_eq - eq_before);
+    // keep the first eq_keep set bits of eq_mask
+    uint64_t take = gt_mask;
+    uint32_t seen = 0;
+#pragma unroll
+    for (int r = 0; r < SEL_R; ++r) {
+      const uint32_t bit = (uint32_t)(eq_mask >> r) & 1u;
+      take |= (uint64_t)(bit != 0u && seen < eq_keep) << r;
+      seen += bit;
     }
-    if (take) emit(out_base + take_before + (uint32_t)__popcll(m_take & lt_mask), i);
+    uint32_t take_total;
+    uint32_t pos = out_base + block_exclusive_scan(__popcll(take), sh, &take_total);
+    const int64_t base = (int64_t)seg * SEL_SEG + (int64_t)threadIdx.x * SEL_R;
+    while (take != 0ull) {
+      const int r = __builtin_ctzll(take);
+      take &= take - 1ull;
+      emit(pos++, base + r);
+    }
     eq_base += eq_total;
     out_base += take_total;
-    __syncthreads();
   }
   return out_base;
 }
 
-// Selects the k best of a row given by `get` and writes mapped indices in ascending order.
-template <class Get, class Emit>
-__device__ uint32_t select_row(Get get, int64_t n, uint32_t k, SelShared& sh, Emit emit) {
-  const KthResult r = radix_kth(get, n, k, sh);
-  if (r.total <= k) return collect_ordered(get, n, 0u, 0u, true, sh, emit);
-  return collect_ordered(get, n, r.tau, r.n_take_eq, false, sh, emit);
+// Full exact selection of the k best keys of a row.
+template <class Row, class Emit>
+__device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& sh, Emit emit) {
+  uint32_t count, A, B;
+  row_stats(row, count, A, B, sh);
+  if (count <= k) return emit_ordered(row, 0u, 0u, sh, emit);
+  uint32_t need = k;
+  refine(row, A, B, need, k, 0u, sh);
+  return emit_ordered(row, A, need, sh, emit);
 }
+
+// --------------------------------------------------------------------------- key sources
+
+// Rows are 16-byte aligned with a leading dimension that is a multiple of 4 (checked by
+// the C ABI), so a float4 starting below n never leaves its row.
+__device__ __forceinline__ void keys4(float4 v, int64_t i0, int64_t n, uint32_t* k) {
+  const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k[j] = (i0 + j < n && selectable(f[j])) ? float_key(f[j]) : 0u;
+}
+
+// Scores of a row (float array), keys of slots i < n.
+struct ScoreSrc {
+  const float* row;
+  __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) {
+      const int64_t i0 = base + 4 * q;
+      const float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      keys4(v, i0, n, &keys[4 * q]);
+    }
+  }
+};
+
+// Block maxima with an override for one block (forced +inf for the pool, or a recomputed
+// maximum for a partial last block in the Top-K prefilter).
+struct BlockSrc {
+  const float* bm;
+  int64_t special;
+  float special_value;
+  __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) {
+      const int64_t i0 = base + 4 * q;
+      float4 v = i0 < n ? *reinterpret_cast<const float4*>(bm + i0)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (special >= i0 && special < i0 + 4) {
+        const int j = (int)(special - i0);
+        if (j == 0) v.x = special_value;
+        if (j == 1) v.y = special_value;
+        if (j == 2) v.z = special_value;
+        if (j == 3) v.w = special_value;
+      }
+      keys4(v, i0, n, &keys[4 * q]);
+    }
+  }
+};
+
+// Scores of the candidate blocks' slots: element i is slot cblocks[i/8]*8 + i%8.
+struct CandSrc {
+  const float* row;
+  const int32_t* cblocks;   // LDS
+  int64_t n_slots;          // slots >= n_slots are outside the selection
+  __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) {
+      const int64_t i0 = base + 4 * q;   // 4 consecutive elements of one block
+      int64_t s0 = 0;
+      bool ok = i0 < n;
+      if (ok) {
+        s0 = (int64_t)cblocks[i0 >> 3] * 8 + (i0 & 7);
+        ok = s0 < n_slots;
+      }
+      const float4 v = ok ? *reinterpret_cast<const float4*>(row + s0)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      keys4(v, ok ? s0 : 0, ok ? n_slots : 0, &keys[4 * q]);
+    }
+  }
+};
+
+// --------------------------------------------------------------------------- kernels
 
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
@@ -182,6 +338,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
     n = v < 0 ? 0 : (v < n ? v : n);
   }
   int32_t* orow = out + (int64_t)t * ld_idx;
+  const uint32_t kk = (uint32_t)k;
   auto map = [&](int64_t slot) -> int32_t {
     if (pool_blocks == nullptr) return (int32_t)slot;
     const int64_t pb = slot >> 3;
@@ -191,62 +348,46 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
   uint32_t kept = 0;
   bool done = false;
 
-  if (n <= KEYS_CAP) {
-    for (int64_t i = threadIdx.x; i < n; i += SEL_THREADS) {
-      const float v = row[i];
-      sh.keys[i] = selectable(v) ? float_key(v) : 0u;
-    }
-    __syncthreads();
-    auto get = [&](int64_t i, uint32_t& key) { key = sh.keys[i]; return key != 0u; };
-    kept = select_row(get, n, (uint32_t)k, sh, [&](uint32_t rank, int64_t i) {
-      if (rank < (uint32_t)k) orow[rank] = map(i);
-    });
-    done = true;
-  } else if (block_max != nullptr) {
-    // Phase A: threshold on block maxima. The last block may be partial (slots >= n are
-    // outside this selection), so its maximum is recomputed from the scores.
+  if (block_max != nullptr && n > (int64_t)CAND_BLOCKS_CAP * 8) {
+    // Phase A: a threshold on block maxima leaving at most CAND_BLOCKS_CAP blocks.
     const int64_t nb = (n + 7) >> 3;
-    const float* bmrow = block_max + (int64_t)t * ld_bm;
     const int64_t tail = n & 7;
     float tail_max = -__builtin_inff();
     if (tail) {
       for (int64_t s = (nb - 1) * 8; s < n; ++s) tail_max = fmaxf(tail_max, row[s]);
     }
-    auto getb = [&](int64_t b, uint32_t& key) {
-      const float v = (tail && b == nb - 1) ? tail_max : bmrow[b];
-      key = float_key(v);
-      return selectable(v);
-    };
-    const KthResult rb = radix_kth(getb, nb, (uint32_t)k, sh);
-    const uint32_t tau_b = rb.total <= (uint32_t)k ? 0u : rb.tau;
-    const uint32_t n_cand = collect_ordered(getb, nb, tau_b, 0u, true, sh,
-                                            [&](uint32_t rank, int64_t b) {
-                                              if (rank < CAND_BLOCKS_CAP) sh.cblocks[rank] = (int32_t)b;
-                                            });
-    if (n_cand <= CAND_BLOCKS_CAP) {
-      // Phase B: exact selection over the candidate blocks' slots, in slot order.
-      const int64_t nc = (int64_t)n_cand * 8;
-      for (int64_t i = threadIdx.x; i < nc; i += SEL_THREADS) {
-        const int64_t slot = (int64_t)sh.cblocks[i >> 3] * 8 + (i & 7);
-        const float v = slot < n ? row[slot] : -__builtin_inff();
-        sh.keys[i] = selectable(v) ? float_key(v) : 0u;
-      }
-      __syncthreads();
-      auto get = [&](int64_t i, uint32_t& key) { key = sh.keys[i]; return key != 0u; };
-      kept = select_row(get, nc, (uint32_t)k, sh, [&](uint32_t rank, int64_t i) {
-        if (rank < (uint32_t)k) orow[rank] = map((int64_t)sh.cblocks[i >> 3] * 8 + (i & 7));
+    const BlockSrc bsrc{block_max + (int64_t)t * ld_bm, tail ? nb - 1 : -1, tail_max};
+    KeyRow<BlockSrc> brow(bsrc, nb);
+    uint32_t count, A, B;
+    row_stats(brow, count, A, B, sh);
+    uint32_t thr = 0;   // keep blocks with key >= thr (0: every valid block)
+    bool fits = count <= (uint32_t)CAND_BLOCKS_CAP;
+    if (count > kk) {
+      uint32_t need = kk;
+      refine(brow, A, B, need, kk, (uint32_t)CAND_BLOCKS_CAP, sh);
+      thr = A;
+      fits = true;
+    }
+    // Collect candidate blocks (ascending); count them to check the cap.
+    const uint32_t n_cand = emit_ordered(brow, thr == 0u ? 0u : thr - 1u, 0u, sh,
+                                         [&](uint32_t rank, int64_t b) {
+                                           if (rank < CAND_BLOCKS_CAP) sh.cblocks[rank] = (int32_t)b;
+                                         });
+    __syncthreads();
+    if (fits && n_cand <= (uint32_t)CAND_BLOCKS_CAP) {
+      const CandSrc csrc{row, sh.cblocks, n};
+      KeyRow<CandSrc> crow(csrc, (int64_t)n_cand * 8);
+      kept = select_row(crow, kk, sh, [&](uint32_t rank, int64_t i) {
+        if (rank < kk) orow[rank] = map((int64_t)sh.cblocks[i >> 3] * 8 + (i & 7));
       });
       done = true;
     }
   }
   if (!done) {
-    auto get = [&](int64_t i, uint32_t& key) {
-      const float v = row[i];
-      key = float_key(v);
-      return selectable(v);
-    };
-    kept = select_row(get, n, (uint32_t)k, sh, [&](uint32_t rank, int64_t i) {
-      if (rank < (uint32_t)k) orow[rank] = map(i);
+    const ScoreSrc ssrc{row};
+    KeyRow<ScoreSrc> srow(ssrc, n);
+    kept = select_row(srow, kk, sh, [&](uint32_t rank, int64_t i) {
+      if (rank < kk) orow[rank] = map(i);
     });
   }
   for (int64_t r = kept + threadIdx.x; r < k; r += SEL_THREADS) orow[r] = -1;
@@ -260,28 +401,12 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
   const int64_t nv = n_visible[t];
   int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
   if (nb > ld_bm) nb = ld_bm;
-  const float* bmrow = block_max + (int64_t)t * ld_bm;
   int32_t* prow = pool + (int64_t)t * ld_pool;
-  auto emit = [&](uint32_t rank, int64_t b) {
+  const BlockSrc src{block_max + (int64_t)t * ld_bm, nb - 1, __builtin_inff()};
+  KeyRow<BlockSrc> row(src, nb);
+  const uint32_t kept = select_row(row, (uint32_t)n_keep, sh, [&](uint32_t rank, int64_t b) {
     if (rank < (uint32_t)n_keep) prow[rank] = (int32_t)b;
-  };
-  uint32_t kept;
-  if (nb <= KEYS_CAP) {
-    for (int64_t b = threadIdx.x; b < nb; b += SEL_THREADS) {
-      const float v = b == nb - 1 ? __builtin_inff() : bmrow[b];
-      sh.keys[b] = selectable(v) ? float_key(v) : 0u;
-    }
-    __syncthreads();
-    auto get = [&](int64_t i, uint32_t& key) { key = sh.keys[i]; return key != 0u; };
-    kept = select_row(get, nb, (uint32_t)n_keep, sh, emit);
-  } else {
-    auto get = [&](int64_t b, uint32_t& key) {
-      const float v = b == nb - 1 ? __builtin_inff() : bmrow[b];
-      key = float_key(v);
-      return selectable(v);
-    };
-    kept = select_row(get, nb, (uint32_t)n_keep, sh, emit);
-  }
+  });
   for (int64_t r = kept + threadIdx.x; r < n_keep; r += SEL_THREADS) prow[r] = -1;
 }
 

@@ -105,50 +105,67 @@ __global__ __launch_bounds__(AT_THREADS, 2) void sparse_attn_kernel(
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
+  // Gather mapping: thread (e = tid % 32, gpart = tid / 32) converts channels
+  // 64*gpart .. 64*gpart+63 of entry e of the chunk: 32 payload bytes + 4 scale bytes of a
+  // main row, or 64 bytes of a window row. The entry's index is fetched one chunk ahead.
+  const int ge = tid & 31;
+  const int gpart = tid >> 5;
+  auto load_idx = [&](int c0) -> int32_t {
+    const int item = c0 + ge;
+    return (item < i_end && item < k) ? topk_idx[(int64_t)t * ld_idx + item] : -1;
+  };
+  int32_t p_next = load_idx(i_begin);
+
 #pragma unroll 1
   for (int c0 = i_begin; c0 < i_end; c0 += AT_CHUNK) {
-    __syncthreads();
-    // Gather and dequantise: unit u = tid + 256*j covers entry e = u % 32, channels
-    // 8*c8 .. 8*c8+7 with c8 = u / 32.
-#pragma unroll 2
-    for (int j = 0; j < (AT_CHUNK * 64) / AT_THREADS; ++j) {
-      const int u = tid + AT_THREADS * j;
-      const int e = u & 31;
-      const int c8 = u >> 5;
-      const int item = c0 + e;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      bool ok = false;
-      if (item < i_end) {
-        if (item < k) {
-          const int32_t p = topk_idx[(int64_t)t * ld_idx + item];
-          const int64_t row = base + p;
-          if (p >= 0 && row >= 0 && row < n_entries) {
-            const uint32_t codes =
-                *reinterpret_cast<const uint32_t*>(kv_fp4 + row * fp4_stride + 4 * c8);
-            const uint32_t sb = kv_scale[row * sc_stride + (c8 >> 1)];
-            v = fp4x8_to_bf16x8(codes, e4m3_to_f32(sb));
-            ok = true;
-          }
-        } else {
-          const int64_t wr = wbase + (item - k);
-          if (wr >= 0 && wr < n_win_rows) {
-            const u32x2 b8 = *reinterpret_cast<const u32x2*>(window_kv + wr * 512 + 8 * c8);
-            const u32x2 lo = e4m3x4_to_bf16x4(b8.x);
-            const u32x2 hi = e4m3x4_to_bf16x4(b8.y);
-            v = u32x4{lo.x, lo.y, hi.x, hi.y};
-            ok = true;
-          }
+    const int32_t p = p_next;
+    if (c0 + AT_CHUNK < i_end) p_next = load_idx(c0 + AT_CHUNK);
+    const int item = c0 + ge;
+    u32x4 raw[4] = {};
+    uint32_t sc = 0;
+    int kind = 0;   // 0 absent, 1 main FP4 row, 2 window FP8 row
+    if (item < i_end) {
+      if (item < k) {
+        const int64_t row = base + p;
+        if (p >= 0 && row >= 0 && row < n_entries) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(kv_fp4 + row * fp4_stride + 32 * gpart);
+          raw[0] = src[0];
+          raw[1] = src[1];
+          sc = *reinterpret_cast<const uint32_t*>(kv_scale + row * sc_stride + 4 * gpart);
+          kind = 1;
+        }
+      } else {
+        const int64_t wr = wbase + (item - k);
+        if (wr >= 0 && wr < n_win_rows) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(window_kv + wr * 512 + 64 * gpart);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) raw[i] = src[i];
+          kind = 2;
         }
       }
-      *reinterpret_cast<u32x4*>(&crow[e * CROW + 8 * c8]) = v;
+    }
+    __syncthreads();   // the previous chunk's LDS tiles are no longer read
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // channels 64*gpart + 8j .. +7
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (kind == 1) {
+        v = fp4x8_to_bf16x8(raw[j >> 2][j & 3], e4m3_to_f32((sc >> (8 * (j >> 1))) & 0xFFu));
+      } else if (kind == 2) {
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[(2 * j) >> 2][(2 * j) & 3]);
+        const u32x2 hi = e4m3x4_to_bf16x4(raw[(2 * j + 1) >> 2][(2 * j + 1) & 3]);
+        v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      const int ch = 64 * gpart + 8 * j;
+      *reinterpret_cast<u32x4*>(&crow[ge * CROW + ch]) = v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t pair = v[i];
-        ccol[(8 * c8 + 2 * i) * CCOL + e] = (uint16_t)(pair & 0xFFFFu);
-        ccol[(8 * c8 + 2 * i + 1) * CCOL + e] = (uint16_t)(pair >> 16);
+        ccol[(ch + 2 * i) * CCOL + ge] = (uint16_t)(pair & 0xFFFFu);
+        ccol[(ch + 2 * i + 1) * CCOL + ge] = (uint16_t)(pair >> 16);
       }
-      if (c8 == 0) valid_e[e] = ok ? 1 : 0;
     }
+    if (gpart == 0) valid_e[ge] = kind != 0 ? 1 : 0;
     __syncthreads();
 
     // Logits S^T[e][h] for the chunk's two 16-entry tiles.

@@ -33,7 +33,7 @@ class Buffers:
 def alloc_buffers(wl, k: int = TOPK) -> Buffers:
     dev = wl.k_cache.device
     n_q, n_l = wl.n_q, len(wl.layers)
-    ld = max(8, wl.n_ctx)
+    ld = -(-max(8, wl.n_ctx) // 32) * 32          # block-max rows stay a multiple of 4
     ws_bytes = C.workspace_bytes(C.OP_SPARSE_ATTN, n_q, 0, k)
     return Buffers(
         scores=torch.empty((n_q, ld), dtype=torch.float32, device=dev),

@@ -78,8 +78,7 @@ enum {
 
 /* Workspace sizing. `op` is one of the CSA2_OP_* values; `n_q` queries, `max_cols` the
  * largest row length (scores columns or block count) and `k` the selection size the
- * call will be made with. Returns 0 when the op needs no workspace. The workspace must
- * be zero-filled once when it is allocated; every call leaves it zero-filled again. */
+ * call will be made with. Returns 0 when the op needs no workspace. */
 enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BLOCK_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
 size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);
 
@@ -125,7 +124,8 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
  * values are kept, ties broken towards the lower block id; blocks whose value is -inf
  * are never kept. pool_blocks[t, 0..n_keep) receives the kept ids in ascending order,
  * then -1. n = 0 gives an all -1 row.
- *   block_max [n_q,ld_bm] f32 (as written by csa2_index_score FULL), n_visible [n_q].
+ *   block_max [n_q,ld_bm] f32 (as written by csa2_index_score FULL), 16-byte aligned,
+ *   ld_bm a multiple of 4; n_visible [n_q] (clipped to 8*ld_bm).
  *   block_size must be 8; 1 <= n_keep <= CSA2_MAX_K; ld_pool >= n_keep.
  *   Positions of the pool are {8b .. 8b+7} of every kept block b, clipped to n. */
 int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm,
@@ -141,10 +141,12 @@ int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm,
  * pool_blocks is NULL, else pool_blocks[t*n_pool + r/block_size]*block_size
  * + r%block_size. topk_idx[t, 0..k) receives the positions in ascending order of
  * slot, then -1.
- *   scores [n_q,ld_scores] f32; n_cols <= ld_scores.
+ *   scores [n_q,ld_scores] f32, 16-byte aligned, ld_scores a multiple of 4;
+ *       n_cols <= ld_scores.
  *   block_max [n_q,ld_block_max] f32, may be NULL: when given it must hold the maxima
- *       of 8-slot blocks of these scores (as csa2_index_score writes them); it lets the
- *       kernel examine only blocks that can hold a winner. The result is identical.
+ *       of 8-slot blocks of these scores (as csa2_index_score writes them), 16-byte
+ *       aligned with ld_block_max a multiple of 4; it lets the kernel examine only blocks
+ *       that can hold a winner. The result is identical.
  *   1 <= k <= CSA2_MAX_K; ld_idx >= k; block_size must be 8. */
 int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
               const int32_t* n_valid,

@@ -139,6 +139,8 @@ def _score_rows(kind, n_q, n, seed):
     g = torch.Generator().manual_seed(seed)
     if kind == "normal":
         s = torch.randn((n_q, n), generator=g) * 30 + 70
+    elif kind == "signed":                      # both signs: keys on both sides of 2^31
+        s = torch.randn((n_q, n), generator=g)
     elif kind == "ties":
         s = torch.randint(-3, 4, (n_q, n), generator=g).float()
     elif kind == "zeros":
@@ -156,20 +158,26 @@ def _score_rows(kind, n_q, n, seed):
     ("normal", 40000, 512, False), ("normal", 40000, 512, True), ("normal", 100003, 512, True),
     ("ties", 3000, 512, False), ("ties", 70000, 512, True), ("ties", 70000, 100, False),
     ("zeros", 50000, 512, True), ("normal", 300, 512, True), ("normal", 1, 512, False),
+    ("signed", 20000, 512, True), ("signed", 9000, 700, False), ("signed", 70000, 2048, True),
 ])
 def test_topk_exact(C, dev, kind, n, k, use_bmax):
     n_q = 3
     s = _score_rows(kind, n_q, n, seed=n + k)
     n_valid = torch.tensor([n, max(0, n - 13), n // 2], dtype=torch.int32)
-    sd = s.to(dev)
+    ld = -(-n // 4) * 4 + 4                       # rows padded to a multiple of 4 (+ spare)
+    sd = torch.full((n_q, ld), 7.0)               # padding never read as a score
+    sd[:, :n] = s
+    sd = sd.to(dev)
     bm = None
     if use_bmax:
         nb = (n + 7) // 8
         pad = torch.full((n_q, nb * 8), -math.inf)
         pad[:, :n] = s
-        bm = pad.view(n_q, nb, 8).amax(dim=2).to(dev)
+        bmv = torch.full((n_q, -(-nb // 4) * 4), 1e30)
+        bmv[:, :nb] = pad.view(n_q, nb, 8).amax(dim=2)
+        bm = bmv.to(dev)
     out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
-    C.csa2_topk(sd, out, k=k, n_valid=n_valid.to(dev), block_max=bm)
+    C.csa2_topk(sd, out, k=k, n_cols=n, n_valid=n_valid.to(dev), block_max=bm)
     torch.cuda.synchronize()
     for t in range(n_q):
         nv = int(n_valid[t])
@@ -205,7 +213,8 @@ def test_block_pool_exact(C, dev, kind, nvis):
     pad = torch.full((n_q, nb * 8), -math.inf)
     for t, nv in enumerate(nvis):
         pad[t, :nv] = s[t, :nv]
-    bm = pad.view(n_q, nb, 8).amax(dim=2)
+    bm = torch.full((n_q, -(-nb // 4) * 4), 1e30)     # padding beyond a row's blocks unused
+    bm[:, :nb] = pad.view(n_q, nb, 8).amax(dim=2)
     pool = torch.empty((n_q, 2048), dtype=torch.int32, device=dev)
     C.csa2_block_pool(bm.to(dev), _i32(nvis, dev), pool)
     torch.cuda.synchronize()
