@@ -181,11 +181,15 @@ int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const vo
           CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null pointer argument");
   REQUIRE(k == 0 || topk_idx != nullptr, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null topk_idx");
   REQUIRE(k == 0 || ld_idx >= k, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: ld_idx %lld < k", (long long)ld_idx);
-  REQUIRE(kv_fp4_stride >= CSA2_FP4_ROW_BYTES && kv_fp4_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
-          "csa2_sparse_attn: kv_fp4_stride %lld must be >= 256 and a multiple of 16",
+  // The gathers use buffer descriptors whose record stride field holds at most 16,383.
+  REQUIRE(kv_fp4_stride >= CSA2_FP4_ROW_BYTES && kv_fp4_stride <= 16368 && kv_fp4_stride % 16 == 0,
+          CSA2_ERR_INVALID_ARG,
+          "csa2_sparse_attn: kv_fp4_stride %lld must be in [256, 16368] and a multiple of 16",
           (long long)kv_fp4_stride);
-  REQUIRE(kv_scale_stride >= CSA2_SCALE_ROW_BYTES && kv_scale_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
-          "csa2_sparse_attn: kv_scale_stride %lld must be >= 32 and a multiple of 16",
+  REQUIRE(kv_scale_stride >= CSA2_SCALE_ROW_BYTES && kv_scale_stride <= 16368 &&
+              kv_scale_stride % 16 == 0,
+          CSA2_ERR_INVALID_ARG,
+          "csa2_sparse_attn: kv_scale_stride %lld must be in [32, 16368] and a multiple of 16",
           (long long)kv_scale_stride);
   REQUIRE(n_entries >= 0 && n_window_rows >= 0, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: negative row count");
   REQUIRE(aligned(q, 16) && aligned(kv_fp4, 16) && aligned(kv_scale, 16) && aligned(window_kv, 16) &&

@@ -12,6 +12,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Two E4M3 bytes (the low or high 16-bit half of `src`) -> two bf16, exactly: every E4M3
 // value is a bf16 value. Element 0 comes from the lower byte.
@@ -36,31 +39,79 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80) ? -v : v;
 }
 
-// E2M1 code (4 bits) -> float bits. Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: for codes >= 2
-// the exponent/mantissa fields are (code + 252) << 22; code 1 is 0.5.
-__device__ __forceinline__ uint32_t e2m1_to_f32_bits(uint32_t c) {
-  const uint32_t mag = c & 7u;
-  uint32_t bits = mag >= 2u ? ((mag + 252u) << 22) : (mag ? 0x3F000000u : 0u);
-  return bits | ((c & 8u) << 28);
+// Two E2M1 codes (byte BYTE of `codes`, low nibble first) -> two bf16, exactly. The
+// conversion runs with a unit scale: the instruction applies only the exponent of its
+// scale operand, so the E4M3 group scale is multiplied in separately.
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t codes) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, BYTE);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two bf16 (packed) times a float scale -> two bf16, by truncation. Exact when every
+// product fits in bf16's 8 significant bits, which holds for an E2M1 value (<= 2
+// significant bits) times an E4M3 scale (<= 4), in [2^-10, 2688].
+__device__ __forceinline__ uint32_t bf16x2_scale_exact(uint32_t pair, float scale) {
+  const float lo = __uint_as_float(pair << 16) * scale;
+  const float hi = __uint_as_float(pair & 0xFFFF0000u) * scale;
+  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
 }
 
 // Eight E2M1 codes of one dword (low nibble first) times a scale -> eight bf16 packed in
-// four dwords. The product of a 2-significant-bit code and a 4-significant-bit scale has
-// at most 5 significant bits and lies in [2^-10, 2688], so truncating the float to its
-// upper half is exact.
+// four dwords, exactly.
 __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
-  uint32_t h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float v = __uint_as_float(e2m1_to_f32_bits((codes >> (4 * i)) & 0xFu)) * scale;
-    h[i] = __float_as_uint(v) >> 16;
-  }
   u32x4 r;
-  r.x = h[0] | (h[1] << 16);
-  r.y = h[2] | (h[3] << 16);
-  r.z = h[4] | (h[5] << 16);
-  r.w = h[6] | (h[7] << 16);
+  r.x = bf16x2_scale_exact(e2m1x2_to_bf16x2<0>(codes), scale);
+  r.y = bf16x2_scale_exact(e2m1x2_to_bf16x2<1>(codes), scale);
+  r.z = bf16x2_scale_exact(e2m1x2_to_bf16x2<2>(codes), scale);
+  r.w = bf16x2_scale_exact(e2m1x2_to_bf16x2<3>(codes), scale);
   return r;
+}
+
+// ---- fp16 forms (the attention works in fp16: every E2M1 x E4M3 product, and every E4M3
+// value, is exact in fp16, and packed fp16 multiplies halve the conversion work) ----
+
+// Two E2M1 codes (byte BYTE of `codes`, low nibble first) -> two fp16, exactly (unit scale).
+template <int BYTE>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16x2(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, BYTE);
+}
+
+// Two E4M3 bytes (low or high 16-bit half of `src`) -> two fp16, exactly.
+template <bool HIGH_HALF>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t src) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, HIGH_HALF);
+}
+
+// Eight E2M1 codes (low nibble first) times a scale held in both halves of `s2` ->
+// eight fp16. Products have <= 6 significant bits and lie in [2^-10, 2688]: exact.
+__device__ __forceinline__ u32x4 fp4x8_to_f16x8(uint32_t codes, f16x2 s2) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<0>(codes) * s2);
+  r.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<1>(codes) * s2);
+  r.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<2>(codes) * s2);
+  r.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16x2<3>(codes) * s2);
+  return r;
+}
+
+// Eight E4M3 bytes (two dwords, channel order kept) -> eight fp16, exactly.
+__device__ __forceinline__ u32x4 fp8x8_to_f16x8(uint32_t a, uint32_t b) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, e4m3x2_to_f16x2<false>(a));
+  r.y = __builtin_bit_cast(uint32_t, e4m3x2_to_f16x2<true>(a));
+  r.z = __builtin_bit_cast(uint32_t, e4m3x2_to_f16x2<false>(b));
+  r.w = __builtin_bit_cast(uint32_t, e4m3x2_to_f16x2<true>(b));
+  return r;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, output lane c
+// receives, as item r, element c%4 of the 4 x 16-bit row that lane 4r + c/4 of the group
+// addressed. `p` must point into LDS and be 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16x4(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // float -> bf16 bits, round to nearest even (inputs are finite).
@@ -78,5 +129,20 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 // A score takes part in a selection unless it is -inf or NaN.
 __device__ __forceinline__ bool selectable(float f) { return f > -__builtin_inff(); }
+
+// Indexed ("structured") buffer loads: address = base + index * stride + offset. A load
+// whose index is at or past the record count returns zeros without touching memory, so a
+// gather can always issue the same loads and mark absent rows with an out-of-range index.
+__device__ u32x4 sbuf_load_b128(__amdgpu_buffer_rsrc_t rsrc, int index, int offset, int soffset,
+                                int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+__device__ u32x2 sbuf_load_b64(__amdgpu_buffer_rsrc_t rsrc, int index, int offset, int soffset,
+                               int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+
+// Buffer descriptor over n_rows records of `stride` bytes (stride < 16,384) from `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rows_rsrc(const void* base, int stride,
+                                                                 uint32_t n_rows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)stride, (int)n_rows,
+                                           0x00020000);
+}
 
 }  // namespace csa2

@@ -178,7 +178,14 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
  *   topk_idx [n_q,ld_idx] int32 with 0 <= k <= CSA2_MAX_K;
  *   window_kv [n_window_rows,512] E4M3; swa_start [n_q] int64; n_swa [n_q] int32 (values
  *   above 128 are clamped to 128);
- *   out [n_q,64,512] bf16; lse [n_q,64] f32 or NULL. */
+ *   out [n_q,64,512] bf16; lse [n_q,64] f32 or NULL.
+ * Workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, n_q, 0, k) bytes, 16-byte
+ * aligned (none when that is 0). When there are too few queries to fill the GPU, the
+ * attended set of each query is split over several workgroups; their partial softmax
+ * states go to the workspace and a second kernel on the same stream combines them in a
+ * fixed order, so results do not depend on timing. The workspace needs no initial
+ * contents; calls that share one must not run concurrently.
+ * Limits: kv_fp4_stride and kv_scale_stride at most 16,368 bytes. */
 int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q,
                      const void* kv_fp4, int64_t kv_fp4_stride,
                      const void* kv_scale, int64_t kv_scale_stride, int64_t n_entries,
