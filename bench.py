@@ -15,6 +15,12 @@ are 128 B of indexer K read + 4 B of score and 0.5 B of block maximum written pe
 (query, entry) pair, plus the indexer queries and weights; its average launch duration is
 measured with HIP events on its own stream over K back-to-back launches.
 
+roofline.traffic: HBM bytes per indexer launch from rocprofv3 counters (FETCH_SIZE and
+WRITE_SIZE, each divided by what the same counter reports per byte for a plain 1 GiB copy
+kernel), read from the committed counter summary; null when the indexer source has changed
+since the counters were taken. `--profile-kernel` runs only the indexer and the copy, for
+those counter runs.
+
 cpu_baseline: the fp64 oracle (oracle/) run on the host over a bounded sample of the same
 workload's queries (whole layer stack per query), scaled to queries/s.
 """
@@ -30,6 +36,48 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+INDEXER_SRC = os.path.join(ROOT, "compressed_kv_cache_csa2_amd", "csrc", "index_score.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_score_full_decode_256k.md")
+COPY_BYTES = 1 << 30
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per Full-indexer launch from the committed counter summary, if it was taken
+    on this workload with the current indexer source; else None."""
+    if workload != "decode_256k" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    try:
+        if fields.get("indexer source sha256") != source_sha256(INDEXER_SRC):
+            return None
+        return float(fields["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_kernels(wl, buf, C, launches):
+    """Only the Full-layer indexer and a plain copy of COPY_BYTES, for counter collection."""
+    import torch
+    full = wl.layers[0]
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                           buf.scores, buf.block_max)
+        torch.neg(src, out=dst)   # reads and writes COPY_BYTES each
+    torch.cuda.synchronize()
+    print(f"[bench] profile launches done: {launches} x (indexer, copy of {COPY_BYTES} B)",
+          file=sys.stderr, flush=True)
 
 
 def algorithmic_bytes(wl, k=512):
@@ -68,8 +116,10 @@ def cpu_baseline(wl, target_s, max_q):
         threads = os.cpu_count() or 1
     done = 0
     t_total = 0.0
-    while done < min(max_q, wl.n_q) and t_total < target_s:
-        seq = synth.sequence_to_host(wl, done)
+    # Queries are taken in order and cycled until target_s seconds of oracle time (the copy
+    # of each query's inputs to the host is outside the timed region).
+    while done < max_q and t_total < target_s:
+        seq = synth.sequence_to_host(wl, done % wl.n_q)
         t0 = time.perf_counter()
         nv = seq["n_visible"]
         idx = pool = None
@@ -91,8 +141,8 @@ def cpu_baseline(wl, target_s, max_q):
         done += 1
         np.asarray(r["out"]).sum()
     return {"value": done / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {wl.n_q} queries of {wl.name}, whole layer stack per query, "
-                      f"{t_total:.1f} s of oracle time"}
+            "sample": f"{done} query stacks of {wl.name} (its {wl.n_q} queries taken in order, "
+                      f"cycled), whole layer stack per query, {t_total:.1f} s of oracle time"}
 
 
 def main():
@@ -105,6 +155,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--breakdown", action="store_true", help="per-call timings to stderr")
+    ap.add_argument("--profile-kernel", type=int, default=0, metavar="N",
+                    help="only launch the Full indexer and a 1 GiB copy N times (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode batch "
@@ -125,6 +177,9 @@ def main():
     print(f"[bench] {args.workload}: generated in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     buf = layers.alloc_buffers(wl)
+    if args.profile_kernel:
+        profile_kernels(wl, buf, C, args.profile_kernel)
+        return
     stream = torch.cuda.Stream()
 
     def step():
@@ -220,7 +275,7 @@ def main():
     value = wl.n_q / (ms_step * 1e-3)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, wl.n_q)
+        cpu = cpu_baseline(wl, args.cpu_seconds, 100000)
     line = {
         "metric": "decode queries/sec + achieved HBM GB/s (% of peak)",
         "value": value,
@@ -242,7 +297,7 @@ def main():
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
                      "kernel": "index_score_kernel<false> (Full-layer indexer)",
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,
