@@ -72,3 +72,55 @@ def assert_attn_close(gpu_out, ref_out, what=""):
     err = np.abs(gpu - ref).max()
     assert err <= ATTN_TOL * scale + 1e-30, f"{what}: max-abs err {err:.3e} vs {ATTN_TOL}*{scale:.3e}"
     return err / scale if scale else 0.0
+
+
+def check_query(wl, buf, t, seq=None, report=None):
+    """Compare every layer of query t of a run (buffers `buf`) with the oracle.
+
+    Each step is judged on the GPU's own previous output, so a legitimate swap inside a
+    tie band never cascades: the Full Top-K and pool against the oracle's scores, the
+    Reindex Top-K against the oracle's rescoring of the GPU's pool, and every attention
+    (output and lse) against the oracle's attention over the GPU's published indices.
+    Returns the number of attention outputs compared."""
+    from compressed_kv_cache_csa2_amd import synth
+    seq = seq or synth.sequence_to_host(wl, t)
+    nv = seq["n_visible"]
+    scale = wl.softmax_scale
+    pool_gpu = None
+    n_cmp = 0
+    for li, lay in enumerate(seq["layers"]):
+        idx_gpu = buf.published[li][t].cpu().numpy()
+        if lay["mode"] == "full":
+            scores = O.full_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, nv)
+            ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), None)
+            kth, band = band_of(scores, 512)
+            assert_set_band(idx_gpu, ref_idx, lambda p: scores[p], kth, band,
+                            f"q{t} L{li} full top-k")
+            if wl.with_pool:
+                pool_gpu = buf.pool[t].cpu().numpy()
+                ref_pool = O.hsi_pool(scores, nv)
+                bm = O.block_max(scores[:nv])
+                bm[(nv - 1) // 8] = np.inf
+                kb, bb = band_of(bm, 2048)
+                assert_set_band(pool_gpu, ref_pool, lambda b: bm[b], kb, bb, f"q{t} pool")
+        elif lay["mode"] == "reindex":
+            padded = np.full(2048, -1, np.int64)
+            kept = pool_gpu[pool_gpu >= 0]
+            padded[:len(kept)] = kept
+            scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
+            ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), padded)
+            pos_of_slot = O.slots_to_positions(np.arange(len(scores)), padded)
+            score_at = dict(zip(pos_of_slot.tolist(), scores.tolist()))
+            kth, band = band_of(scores, 512)
+            assert_set_band(idx_gpu, ref_idx, lambda p: score_at[p], kth, band,
+                            f"q{t} L{li} reindex top-k")
+        res = O.reuse_layer(idx_gpu, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
+                            lay["window_kv"], 0, lay["n_swa"], scale)
+        rel = assert_attn_close(buf.out[li][t].float().cpu().numpy(), res["out"],
+                                f"q{t} L{li} {lay['mode']} attention")
+        lse_gpu = buf.lse[li][t].cpu().numpy().astype(np.float64)
+        assert np.allclose(lse_gpu, res["lse"], atol=2e-3, rtol=1e-4), f"q{t} L{li} lse"
+        n_cmp += 1
+        if report is not None:
+            report.append((t, li, rel))
+    return n_cmp

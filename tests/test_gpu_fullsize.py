@@ -1,0 +1,84 @@
+"""The named workloads at their full sizes on the GPU, checked against the oracle on
+sampled queries (every query for the 32K decode). decode_256k runs exactly as bench.py
+times it: the layer stack captured in a HIP graph on a side stream and replayed."""
+import sys
+import time
+
+import pytest
+import torch
+
+from tests.parity_util import check_query
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(f"[fullsize] {msg}", file=sys.stderr, flush=True)
+
+
+def _run(name, dev, graph=False):
+    from compressed_kv_cache_csa2_amd import layers, synth
+    t0 = time.time()
+    wl = synth.make_workload(name, device=dev)
+    torch.cuda.synchronize()
+    _log(f"{name}: generated {wl.n_q} queries in {time.time() - t0:.1f} s")
+    buf = layers.alloc_buffers(wl)
+    if graph:
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            layers.run_layers(wl, buf, stream=s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            layers.run_layers(wl, buf, stream=s)
+        buf.out.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                g.replay()
+        torch.cuda.synchronize()
+    else:
+        layers.run_layers(wl, buf)
+        torch.cuda.synchronize()
+    _log(f"{name}: layer stack ran")
+    return wl, buf
+
+
+def _check(wl, buf, queries):
+    n = 0
+    for t in queries:
+        t0 = time.time()
+        n += check_query(wl, buf, t)
+        _log(f"{wl.name}: query {t} checked ({time.time() - t0:.1f} s)")
+    return n
+
+
+def test_decode_32k_every_query(dev):
+    wl, buf = _run("decode_32k", dev)
+    assert _check(wl, buf, range(wl.n_q)) == wl.n_q
+    del wl, buf
+    torch.cuda.empty_cache()
+
+
+def test_decode_256k_sampled_as_benched(dev):
+    wl, buf = _run("decode_256k", dev, graph=True)
+    queries = [0, 13, wl.n_q - 1]
+    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    del wl, buf
+    torch.cuda.empty_cache()
+
+
+def test_prefill_128k_m2_sampled(dev):
+    wl, buf = _run("prefill_128k_m2", dev)
+    queries = [0, 1, 2047, wl.n_q - 1]
+    assert _check(wl, buf, queries) == len(queries)
+    del wl, buf
+    torch.cuda.empty_cache()
+
+
+def test_decode_1m_sampled(dev):
+    wl, buf = _run("decode_1m", dev)
+    queries = [0, wl.n_q - 1]
+    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    del wl, buf
+    torch.cuda.empty_cache()
