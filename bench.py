@@ -239,7 +239,7 @@ def main():
         evs = []
         with torch.cuda.stream(stream):
             for li, lay in enumerate(wl.layers):
-                for part in ("score", "topk", "pool", "attn"):
+                for part in ("score", "pool", "topk", "attn"):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
@@ -250,6 +250,10 @@ def main():
                         C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
                                            wl.n_visible, buf.re_scores, None,
                                            pool_blocks=buf.pool, stream=stream)
+                    elif part == "topk" and lay.mode == "full" and wl.with_pool:
+                        C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
+                                    pool_blocks=buf.pool, pool_use=C.POOL_CANDIDATES,
+                                    stream=stream)
                     elif part == "topk" and lay.mode == "full":
                         C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
                                     block_max=buf.block_max, stream=stream)

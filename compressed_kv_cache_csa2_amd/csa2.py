@@ -14,6 +14,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
+POOL_NONE, POOL_SLOTS, POOL_CANDIDATES = 0, 1, 2
 OP_INDEX_SCORE, OP_BLOCK_POOL, OP_TOPK, OP_SPARSE_ATTN = 0, 1, 2, 3
 CSA2_OK = 0
 
@@ -32,7 +33,7 @@ def _load():
     P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
-    lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, P, I, I, P, L, P, Z, P]
+    lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
     for f in ("csa2_index_score", "csa2_block_pool", "csa2_topk", "csa2_sparse_attn"):
@@ -104,13 +105,16 @@ def csa2_block_pool(block_max, n_visible, pool_blocks, n_keep=2048, stream=None)
 
 
 def csa2_topk(scores, topk_idx, k=512, n_cols=None, n_valid=None, block_max=None,
-              pool_blocks=None, stream=None):
-    """Top-k positions (ascending, -1 padded) into `topk_idx` [n_q, >= k]."""
+              pool_blocks=None, pool_use=None, stream=None):
+    """Top-k positions (ascending, -1 padded) into `topk_idx` [n_q, >= k]. pool_use defaults
+    to POOL_SLOTS when pool_blocks is given (a Reindex layer's scores), else POOL_NONE."""
     n_cols = scores.shape[1] if n_cols is None else n_cols
+    if pool_use is None:
+        pool_use = POOL_NONE if pool_blocks is None else POOL_SLOTS
     _check(lib.csa2_topk(
         scores.shape[0], _ptr(scores, torch.float32, "scores"), scores.shape[1], n_cols,
         _ptr(n_valid, torch.int32, "n_valid"), _ptr(block_max, torch.float32, "block_max"),
-        block_max.shape[1] if block_max is not None else 0, k,
+        block_max.shape[1] if block_max is not None else 0, k, pool_use,
         _ptr(pool_blocks, torch.int32, "pool_blocks"),
         pool_blocks.shape[1] if pool_blocks is not None else 0, 8,
         _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], None, 0, _stream(stream)))

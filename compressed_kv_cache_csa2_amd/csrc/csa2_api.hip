@@ -130,8 +130,9 @@ int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm, const int32_
 
 int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
               const int32_t* n_valid, const float* block_max, int64_t ld_block_max, int k,
-              const int32_t* pool_blocks, int n_pool, int block_size, int32_t* topk_idx,
-              int64_t ld_idx, void* workspace, size_t ws_bytes, void* stream) {
+              csa2_pool_use_t pool_use, const int32_t* pool_blocks, int n_pool, int block_size,
+              int32_t* topk_idx, int64_t ld_idx, void* workspace, size_t ws_bytes,
+              void* stream) {
   (void)workspace;
   (void)ws_bytes;
   REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
@@ -154,12 +155,21 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
             CSA2_ERR_INVALID_ARG,
             "csa2_topk: block_max must be 16-byte aligned with ld_block_max >= ceil(n_cols/8) "
             "and a multiple of 4 (got %lld)", (long long)ld_block_max);
-  if (pool_blocks != nullptr)
-    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K && n_cols <= (int64_t)n_pool * block_size,
-            CSA2_ERR_INVALID_ARG, "csa2_topk: pool of %d blocks cannot cover %lld slots", n_pool,
-            (long long)n_cols);
-  return hip_status(csa2::launch_topk(n_q, scores, ld_scores, n_cols, n_valid, block_max, ld_block_max,
-                                      k, pool_blocks, pool_blocks ? n_pool : 0, topk_idx, ld_idx,
+  REQUIRE(pool_use == CSA2_POOL_NONE || pool_use == CSA2_POOL_SLOTS ||
+              pool_use == CSA2_POOL_CANDIDATES,
+          CSA2_ERR_INVALID_ARG, "csa2_topk: pool_use %d unknown", (int)pool_use);
+  REQUIRE((pool_use == CSA2_POOL_NONE) == (pool_blocks == nullptr), CSA2_ERR_INVALID_ARG,
+          "csa2_topk: pool_blocks must be given exactly when a pool is used");
+  if (pool_use != CSA2_POOL_NONE)
+    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K && aligned(pool_blocks, 4), CSA2_ERR_INVALID_ARG,
+            "csa2_topk: n_pool %d out of range [1, %d]", n_pool, CSA2_MAX_K);
+  if (pool_use == CSA2_POOL_SLOTS)
+    REQUIRE(n_cols <= (int64_t)n_pool * block_size, CSA2_ERR_INVALID_ARG,
+            "csa2_topk: pool of %d blocks cannot cover %lld slots", n_pool, (long long)n_cols);
+  return hip_status(csa2::launch_topk(n_q, scores, ld_scores, n_cols, n_valid,
+                                      pool_use == CSA2_POOL_CANDIDATES ? nullptr : block_max,
+                                      ld_block_max, k, (int)pool_use, pool_blocks,
+                                      pool_use != CSA2_POOL_NONE ? n_pool : 0, topk_idx, ld_idx,
                                       static_cast<hipStream_t>(stream)),
                     "csa2_topk");
 }

@@ -18,10 +18,11 @@ hipError_t launch_block_pool(int n_q, const float* block_max, int64_t ld_bm,
                              const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
                              int64_t ld_pool, hipStream_t stream);
 
+// pool_use: 0 none, 1 scores indexed by pool slot, 2 pool blocks are the candidates.
 hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
                        const int32_t* n_valid, const float* block_max, int64_t ld_bm, int k,
-                       const int32_t* pool_blocks, int n_pool, int32_t* topk_idx, int64_t ld_idx,
-                       hipStream_t stream);
+                       int pool_use, const int32_t* pool_blocks, int n_pool, int32_t* topk_idx,
+                       int64_t ld_idx, hipStream_t stream);
 
 // Number of entry splits the attention kernel uses for n_q queries and k selected entries
 // (a pure function of its arguments, so workspace sizing and launch agree).

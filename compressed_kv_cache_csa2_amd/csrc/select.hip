@@ -255,7 +255,9 @@ __device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& 
 // --------------------------------------------------------------------------- key sources
 
 // Rows are 16-byte aligned with a leading dimension that is a multiple of 4 (checked by
-// the C ABI), so a float4 starting below n never leaves its row.
+// the C ABI), so a float4 starting below n never leaves its row. Every source issues all
+// of a segment's loads before using any (an element past the end reads the row's first
+// float4 and is masked afterwards), so a segment costs one memory round trip.
 __device__ __forceinline__ void keys4(float4 v, int64_t i0, int64_t n, uint32_t* k) {
   const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -266,13 +268,14 @@ __device__ __forceinline__ void keys4(float4 v, int64_t i0, int64_t n, uint32_t*
 struct ScoreSrc {
   const float* row;
   __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+    float4 v[SEL_R / 4];
 #pragma unroll
     for (int q = 0; q < SEL_R / 4; ++q) {
       const int64_t i0 = base + 4 * q;
-      const float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      keys4(v, i0, n, &keys[4 * q]);
+      v[q] = *reinterpret_cast<const float4*>(row + (i0 < n ? i0 : 0));
     }
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) keys4(v[q], base + 4 * q, n, &keys[4 * q]);
   }
 };
 
@@ -283,41 +286,49 @@ struct BlockSrc {
   int64_t special;
   float special_value;
   __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+    float4 v[SEL_R / 4];
 #pragma unroll
     for (int q = 0; q < SEL_R / 4; ++q) {
       const int64_t i0 = base + 4 * q;
-      float4 v = i0 < n ? *reinterpret_cast<const float4*>(bm + i0)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[q] = *reinterpret_cast<const float4*>(bm + (i0 < n ? i0 : 0));
+    }
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) {
+      const int64_t i0 = base + 4 * q;
       if (special >= i0 && special < i0 + 4) {
         const int j = (int)(special - i0);
-        if (j == 0) v.x = special_value;
-        if (j == 1) v.y = special_value;
-        if (j == 2) v.z = special_value;
-        if (j == 3) v.w = special_value;
+        if (j == 0) v[q].x = special_value;
+        if (j == 1) v[q].y = special_value;
+        if (j == 2) v[q].z = special_value;
+        if (j == 3) v[q].w = special_value;
       }
-      keys4(v, i0, n, &keys[4 * q]);
+      keys4(v[q], i0, n, &keys[4 * q]);
     }
   }
 };
 
-// Scores of the candidate blocks' slots: element i is slot cblocks[i/8]*8 + i%8.
+// Scores of the candidate blocks' slots: element i is slot cblocks[i/8]*8 + i%8 (a
+// negative block id, or a slot at or past n_slots, is absent).
 struct CandSrc {
   const float* row;
   const int32_t* cblocks;   // LDS
   int64_t n_slots;          // slots >= n_slots are outside the selection
   __device__ __forceinline__ void load(int64_t base, int64_t n, uint32_t (&keys)[SEL_R]) const {
+    float4 v[SEL_R / 4];
+    int64_t s0[SEL_R / 4];
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q) {   // 4 consecutive elements of one block
+      const int64_t i0 = base + 4 * q;
+      const int32_t b = i0 < n ? cblocks[i0 >> 3] : -1;
+      s0[q] = b >= 0 ? (int64_t)b * 8 + (i0 & 7) : n_slots;   // absent block: masked
+    }
+#pragma unroll
+    for (int q = 0; q < SEL_R / 4; ++q)
+      v[q] = *reinterpret_cast<const float4*>(row + (s0[q] < n_slots ? s0[q] : 0));
 #pragma unroll
     for (int q = 0; q < SEL_R / 4; ++q) {
-      const int64_t i0 = base + 4 * q;   // 4 consecutive elements of one block
-      int64_t s0 = 0;
-      bool ok = i0 < n;
-      if (ok) {
-        s0 = (int64_t)cblocks[i0 >> 3] * 8 + (i0 & 7);
-        ok = s0 < n_slots;
-      }
-      const float4 v = ok ? *reinterpret_cast<const float4*>(row + s0)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      keys4(v, ok ? s0 : 0, ok ? n_slots : 0, &keys[4 * q]);
+      const bool ok = s0[q] < n_slots;
+      keys4(v[q], ok ? s0[q] : 0, ok ? n_slots : 0, &keys[4 * q]);
     }
   }
 };
@@ -327,8 +338,8 @@ struct CandSrc {
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
     const int32_t* __restrict__ n_valid, const float* __restrict__ block_max, int64_t ld_bm,
-    int k, const int32_t* __restrict__ pool_blocks, int n_pool, int32_t* __restrict__ out,
-    int64_t ld_idx) {
+    int k, int pool_use, const int32_t* __restrict__ pool_blocks, int n_pool,
+    int32_t* __restrict__ out, int64_t ld_idx) {
   __shared__ SelShared sh;
   const int t = blockIdx.x;
   const float* row = scores + (int64_t)t * ld;
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
   int32_t* orow = out + (int64_t)t * ld_idx;
   const uint32_t kk = (uint32_t)k;
   auto map = [&](int64_t slot) -> int32_t {
-    if (pool_blocks == nullptr) return (int32_t)slot;
+    if (pool_use != 1) return (int32_t)slot;
     const int64_t pb = slot >> 3;
     const int32_t b = pb < n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
     return b < 0 ? -1 : (int32_t)((int64_t)b * 8 + (slot & 7));
@@ -348,7 +359,20 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
   uint32_t kept = 0;
   bool done = false;
 
-  if (block_max != nullptr && n > (int64_t)CAND_BLOCKS_CAP * 8) {
+  if (pool_use == 2) {
+    // Candidates: the slots of the pool's blocks (ascending block ids, so the winners come
+    // out in ascending position order; -1 entries are absent).
+    const int32_t* prow = pool_blocks + (int64_t)t * n_pool;
+    for (int i = threadIdx.x; i < n_pool; i += SEL_THREADS) sh.cblocks[i] = prow[i];
+    __syncthreads();
+    const CandSrc csrc{row, sh.cblocks, n};
+    KeyRow<CandSrc> crow(csrc, (int64_t)n_pool * 8);
+    kept = select_row(crow, kk, sh, [&](uint32_t rank, int64_t i) {
+      if (rank < kk) orow[rank] = (int32_t)((int64_t)sh.cblocks[i >> 3] * 8 + (i & 7));
+    });
+    done = true;
+  }
+  if (!done && block_max != nullptr && n > (int64_t)CAND_BLOCKS_CAP * 8) {
     // Phase A: a threshold on block maxima leaving at most CAND_BLOCKS_CAP blocks.
     const int64_t nb = (n + 7) >> 3;
     const int64_t tail = n & 7;
@@ -412,10 +436,11 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
 
 hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
                        const int32_t* n_valid, const float* block_max, int64_t ld_bm, int k,
-                       const int32_t* pool_blocks, int n_pool, int32_t* topk_idx, int64_t ld_idx,
-                       hipStream_t stream) {
+                       int pool_use, const int32_t* pool_blocks, int n_pool, int32_t* topk_idx,
+                       int64_t ld_idx, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(n_q), dim3(SEL_THREADS), 0, stream, scores, ld_scores,
-                     n_cols, n_valid, block_max, ld_bm, k, pool_blocks, n_pool, topk_idx, ld_idx);
+                     n_cols, n_valid, block_max, ld_bm, k, pool_use, pool_blocks, n_pool, topk_idx,
+                     ld_idx);
   return hipGetLastError();
 }
 

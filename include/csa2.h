@@ -133,14 +133,27 @@ int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm,
                     int32_t* pool_blocks, int64_t ld_pool,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/* How csa2_topk uses a pool of candidate blocks. */
+typedef enum {
+  CSA2_POOL_NONE = 0,        /* no pool: scores are indexed by cache position */
+  CSA2_POOL_SLOTS = 1,       /* scores are indexed by pool slot (a Reindex layer's scores) */
+  CSA2_POOL_CANDIDATES = 2   /* scores are indexed by cache position, and only positions in
+                                the pool's blocks compete (a Full layer after its pool) */
+} csa2_pool_use_t;
+
 /* Top-K selection ([V41F-BLOG] 2.3.4 and 3.3.1; [V41F-ARCH] 2 "Top-K global entries").
  * For query t the candidates are slots r < n_cols (and r < n_valid[t] when n_valid is
- * not NULL) whose score is finite or +inf (-inf and NaN are never selected). The
- * min(k, #candidates) slots with the largest scores are chosen, ties broken towards
- * the lower slot. Each chosen slot is mapped to a cache position: identity when
- * pool_blocks is NULL, else pool_blocks[t*n_pool + r/block_size]*block_size
- * + r%block_size. topk_idx[t, 0..k) receives the positions in ascending order of
- * slot, then -1.
+ * not NULL) whose score is finite or +inf (-inf and NaN are never selected); with
+ * CSA2_POOL_CANDIDATES only slots r with r/block_size among pool_blocks[t, ..] compete.
+ * The min(k, #candidates) slots with the largest scores are chosen, ties broken towards
+ * the lower slot. Each chosen slot is mapped to a cache position: identity, or with
+ * CSA2_POOL_SLOTS pool_blocks[t*n_pool + r/block_size]*block_size + r%block_size.
+ * topk_idx[t, 0..k) receives the positions in ascending order of slot, then -1.
+ * CSA2_POOL_CANDIDATES with the pool csa2_block_pool wrote from these scores' block
+ * maxima (n_keep > k) gives exactly the unrestricted Top-K: a block outside the pool
+ * has n_keep - 1 blocks ranked above it, each holding an entry that outranks all of its
+ * entries, so none of them can be among the k best; the kernel then examines only the
+ * pool's slots. The pool must be ascending with -1 padding (as csa2_block_pool writes).
  *   scores [n_q,ld_scores] f32, 16-byte aligned, ld_scores a multiple of 4;
  *       n_cols <= ld_scores.
  *   block_max [n_q,ld_block_max] f32, may be NULL: when given it must hold the maxima
@@ -151,8 +164,8 @@ int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm,
 int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
               const int32_t* n_valid,
               const float* block_max, int64_t ld_block_max,
-              int k, const int32_t* pool_blocks, int n_pool, int block_size,
-              int32_t* topk_idx, int64_t ld_idx,
+              int k, csa2_pool_use_t pool_use, const int32_t* pool_blocks, int n_pool,
+              int block_size, int32_t* topk_idx, int64_t ld_idx,
               void* workspace, size_t ws_bytes, void* stream);
 
 /* Joint sparse attention over the selected entries and the sliding window

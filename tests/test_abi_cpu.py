@@ -57,7 +57,8 @@ def test_index_score_rejections(C):
 def test_topk_and_pool_rejections(C):
     L = C.lib
     ok = dict(n_q=1, scores=FAKE, ld=100, n_cols=100, n_valid=None, bm=None, ld_bm=0, k=512,
-              pool=None, n_pool=0, bs=8, idx=FAKE, ld_idx=512, ws=None, ws_bytes=0, stream=None)
+              pool_use=0, pool=None, n_pool=0, bs=8, idx=FAKE, ld_idx=512, ws=None, ws_bytes=0,
+              stream=None)
 
     def topk(**kw):
         a = dict(ok)
@@ -68,7 +69,12 @@ def test_topk_and_pool_rejections(C):
     assert topk(n_cols=101) == 1
     assert topk(ld_idx=100) == 1
     assert topk(bm=FAKE, ld_bm=3) == 1
-    assert topk(pool=FAKE, n_pool=4) == 1                # 4 blocks cannot cover 100 slots
+    assert topk(pool_use=1, pool=FAKE, n_pool=4) == 1    # 4 blocks cannot cover 100 slots
+    assert topk(pool_use=3, pool=FAKE, n_pool=16) == 1   # unknown pool use
+    assert topk(pool_use=1, pool=None, n_pool=16) == 1   # pool use without a pool
+    assert topk(pool_use=0, pool=FAKE, n_pool=16) == 1   # a pool with no use
+    assert topk(pool_use=2, pool=FAKE, n_pool=0) == 1
+    assert topk(pool_use=2, pool=FAKE, n_pool=4096) == 1
     assert topk(scores=None) == 1
     assert topk(n_q=0, scores=None) == 0
     assert L.csa2_block_pool(1, FAKE, 10, FAKE, 8, 0, FAKE, 2048, None, 0, None) == 1

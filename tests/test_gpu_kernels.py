@@ -153,6 +153,27 @@ def _score_rows(kind, n_q, n, seed):
     return s
 
 
+def test_index_score_empty_cache(C, dev):
+    """No readable entry (n_entries = 0): every score and block maximum is -inf."""
+    import ctypes
+    n_q, ld = 2, 1000
+    q_idx = torch.zeros((n_q, 32, 128), dtype=torch.bfloat16, device=dev)
+    w = torch.ones((n_q, 32), dtype=torch.float32, device=dev)
+    k_cache = torch.zeros((1, 128), dtype=torch.uint8, device=dev)   # a valid pointer, 0 rows used
+    kv_start = torch.zeros(n_q, dtype=torch.int64, device=dev)
+    n_vis = torch.full((n_q,), 500, dtype=torch.int32, device=dev)
+    scores = torch.zeros((n_q, ld), dtype=torch.float32, device=dev)
+    bm = torch.zeros((n_q, (ld + 7) // 8), dtype=torch.float32, device=dev)
+    P = ctypes.c_void_p
+    rc = C.lib.csa2_index_score(C.FULL, n_q, 32, 128, P(q_idx.data_ptr()), P(w.data_ptr()),
+                                P(k_cache.data_ptr()), 0, P(kv_start.data_ptr()),
+                                P(n_vis.data_ptr()), None, 0, 8, P(scores.data_ptr()), ld,
+                                P(bm.data_ptr()), bm.shape[1], None)
+    assert rc == 0, C.lib.csa2_last_error()
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(scores)) and torch.all(torch.isneginf(bm))
+
+
 @pytest.mark.parametrize("kind,n,k,use_bmax", [
     ("normal", 4096, 512, False), ("normal", 5000, 512, True), ("normal", 16384, 2048, False),
     ("normal", 40000, 512, False), ("normal", 40000, 512, True), ("normal", 100003, 512, True),
@@ -185,6 +206,42 @@ def test_topk_exact(C, dev, kind, n, k, use_bmax):
         want = np.full(k, -1, np.int64)
         want[:len(ref)] = ref
         assert np.array_equal(out[t].cpu().numpy(), want), f"row {t}"
+
+
+@pytest.mark.parametrize("kind,n", [("normal", 300000), ("ties", 70000), ("normal", 9000),
+                                    ("signed", 20001), ("zeros", 50000)])
+def test_topk_among_pool_candidates_is_exact(C, dev, kind, n):
+    """With the pool csa2_block_pool builds from the same scores' block maxima, the Top-K
+    restricted to the pool's slots is exactly the unrestricted Top-K (bitwise, ties
+    included), also for short and ragged rows."""
+    n_q, k = 3, 512
+    s = _score_rows(kind, n_q, n, seed=n + 7)
+    ld = (n + 3) // 4 * 4 + 4
+    sd = torch.full((n_q, ld), 7.0, dtype=torch.float32, device=dev)
+    sd[:, :n] = s.to(dev)
+    n_valid = torch.tensor([n, n - 5, max(1, n // 3)], dtype=torch.int32, device=dev)
+    nb = (ld + 7) // 8
+    ld_bm = (nb + 3) // 4 * 4
+    bm = torch.full((n_q, ld_bm), 1e30, dtype=torch.float32, device=dev)
+    for t in range(n_q):
+        nv = int(n_valid[t])
+        row = torch.full((((nv + 7) // 8) * 8,), -math.inf, device=dev)
+        row[:nv] = sd[t, :nv]
+        bm[t, :(nv + 7) // 8] = row.view(-1, 8).amax(dim=1)
+    pool = torch.empty((n_q, 2048), dtype=torch.int32, device=dev)
+    C.csa2_block_pool(bm, n_valid, pool)
+    got = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    ref = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    C.csa2_topk(sd, got, k=k, n_cols=n, n_valid=n_valid, pool_blocks=pool,
+                pool_use=C.POOL_CANDIDATES)
+    C.csa2_topk(sd, ref, k=k, n_cols=n, n_valid=n_valid)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    for t in range(n_q):   # and against the oracle
+        nv = int(n_valid[t])
+        want = O.slots_to_positions(O.topk_slots(s[t, :nv].double().numpy(), k), None)
+        g = got[t].cpu().numpy()
+        assert np.array_equal(np.sort(g[g >= 0]), np.sort(want))
 
 
 def test_topk_pool_mapping(C, dev):
