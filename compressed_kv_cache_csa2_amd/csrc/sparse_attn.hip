@@ -9,22 +9,25 @@
 // dim 512, FP4 E2M1 main KV with an E4M3 scale per 16 channels, FP8 window).
 //
 // Work split: a query's selected entries and its window rows are cut into 16-item slices
-// (separately, so a slice never mixes the two formats); a workgroup owns one
-// group of 16 heads and one contiguous range of slices (a "split"), and its four
-// wavefronts take every fourth slice of that range and run independently (no barrier in
-// the main loop). Per slice a wavefront:
-//   - gathers the 16 rows (lane = item x quarter of the 512 channels) two slices ahead of
-//     their use, so each HBM round trip overlaps two slices of arithmetic. The gathers are
-//     indexed buffer loads: an absent item gets an index past the buffer's record count
-//     and reads zeros, so every slice issues the same loads into the same registers and
-//     the wait for a slice never includes the loads of the slices behind it;
+// (separately, so a slice never mixes the two formats); a workgroup owns one group of 16
+// heads and one contiguous range of slices (a "split"), and its eight wavefronts (two per
+// SIMD, so one's memory waits hide behind the other's arithmetic) take every eighth slice
+// of that range and run independently (no barrier in the main loop). Per slice a
+// wavefront:
+//   - gathers the 16 rows (lane = item x quarter of the 512 channels) one slice ahead of
+//     their use (the other wavefront on the SIMD covers the rest of the latency), with the
+//     selected positions loaded two slices before that. The gathers
+//     are indexed buffer loads: an absent item gets an index past the buffer's record
+//     count and reads zeros, so every slice issues the same loads into the same registers
+//     and the wait for a slice never includes the loads of the slices behind it;
 //   - converts them to fp16 with the hardware E2M1/E4M3 -> fp16 conversions and a packed
 //     fp16 multiply by the group scale; every value is exact (an E2M1 x E4M3 product has
 //     <= 6 significant bits in [2^-10, 2688]). The converted registers are directly the A
 //     operand of the logit product S^T (16 items x 16 heads) = C . Q^T
-//     (v_mfma_f32_16x16x32_f16, K = 512; B = this group's queries in registers, each head
-//     rescaled by a power of two into fp16's range, the inverse folded into the logit
-//     scale), and are also stored to the wavefront's own LDS tile;
+//     (v_mfma_f32_16x16x32_f16, K = 512; B = this group's queries, each head rescaled by a
+//     power of two into fp16's range with the inverse folded into the logit scale, held
+//     once in LDS in operand order so every read is one contiguous 1 KiB access), and are
+//     also stored to the wavefront's own LDS tile;
 //   - never rescales its accumulator: the reference max of each head is the largest logit
 //     of the first slice with a valid item, and later weights p = 2^(l - ref) may reach
 //     2^15 (fp16 holds them); a logit beyond that restarts the wavefront's slices with the
@@ -32,7 +35,7 @@
 //   - O^T (512 x 16 heads) += C^T . P^T with v_mfma_f32_16x16x16_f16: P^T is the logits'
 //     accumulator layout, A = C^T is read from the tile with LDS transpose reads
 //     (ds_read_b64_tr_b16).
-// The four wavefront partials are merged through LDS. With more than one split per head
+// The eight wavefront partials are merged through LDS. With more than one split per head
 // group, each workgroup stores its (max, sum, O) partial in the workspace and a second
 // kernel combines them in split order (no cross-workgroup synchronisation inside a
 // kernel). Workgroup ids put all workgroups of a query on one XCD, so they share its L2
@@ -42,13 +45,14 @@
 
 namespace csa2 {
 
-constexpr int AT_THREADS = 256;
-constexpr int AT_WAVES = 4;
+constexpr int AT_WAVES = 8;
+constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_SLICE = 16;                 // items per wavefront step
 constexpr int AT_HEADS = 16;                 // heads per workgroup
 constexpr int AT_GROUPS = 64 / AT_HEADS;     // head groups per query
-constexpr int AT_MAX_K = 2048;               // largest selection the index staging holds
+constexpr int MERGE_THREADS = AT_HEADS * 16;   // split merge: 16 threads per head
 constexpr int AT_WINDOW = 128;               // largest sliding window
+constexpr int AT_WIN_SLICES = AT_WINDOW / AT_SLICE;
 constexpr int AT_MAX_SPLITS = 8;
 constexpr int AT_TARGET_WGS = 256;           // one workgroup per compute unit
 constexpr int N_XCD = 8;
@@ -57,12 +61,12 @@ constexpr float AT_LOG2E = 1.4426950408889634f;
 constexpr float AT_LN2 = 0.6931471805599453f;
 
 int attn_splits(int n_q, int k) {
-  const int n_sl = (k + AT_WINDOW + AT_SLICE - 1) / AT_SLICE;
+  const int n_sl = (k + AT_SLICE - 1) / AT_SLICE + AT_WIN_SLICES;
   int s = 1;
   // Double the splits while the grid is below one workgroup per CU and every wavefront
-  // would still get at least two slices.
+  // would still get a slice.
   while (s < AT_MAX_SPLITS && (int64_t)n_q * AT_GROUPS * s < AT_TARGET_WGS &&
-         n_sl >= 2 * AT_WAVES * 2 * s)
+         n_sl >= AT_WAVES * 2 * s)
     s *= 2;
   return s;
 }
@@ -80,25 +84,20 @@ size_t attn_workspace_bytes(int n_q, int k) {
 
 // A wavefront's tile holds 16 rows C[e][0..512) in fp16. Row e starts at element
 // TILE_ROW * e and its channel quarter g (128 channels) at + TILE_QUARTER * g: rows are
-// 1,120 B apart and quarters 272 B apart. LDS has 128 four-byte banks; 16-byte accesses are
-// served 32 lanes at a time and 8-byte ones 64 at a time. With these strides the
-// conversion's stores (16 rows x 2 quarters x one 16-byte block per pass) and the
-// transpose reads (16 rows x one 32-byte chunk) each touch every bank exactly once, and
-// every address is a per-lane base plus a compile-time offset.
+// 1,120 B apart and quarters 272 B apart, which keeps the transpose reads (16 rows x one
+// 32-byte chunk) free of bank conflicts, and every address is a per-lane base plus a
+// compile-time offset.
 constexpr int TILE_ROW = 560;       // elements
 constexpr int TILE_QUARTER = 136;   // elements
 constexpr int TILE_ELEMS = AT_SLICE * TILE_ROW;
-// Merge buffer rows (one head, 256 channels) are padded to 264 floats so that the stores
-// (16 heads x 2 lane groups per pass) and the reads (16 heads x 2 channel groups) are free
-// of bank conflicts.
-constexpr int PART_ROW = 264;
 
 struct AttnShared {
   union {
-    uint16_t tile[AT_WAVES][TILE_ELEMS];         // 70 KiB: per-wave slice tiles
-    float part[AT_WAVES][AT_HEADS][PART_ROW];    // 66 KiB: merge buffer, half of d at a time
+    uint16_t tile[AT_WAVES][TILE_ELEMS];   // 140 KiB: per-wave slice tiles
+    u32x4 part[AT_WAVES][16][64];          // 128 KiB: merge buffer (half of d), lane order
   };
-  int32_t pidx[AT_MAX_K];                        // this split's selected positions
+  u32x4 qop[16][64];                       // 16 KiB: logit B operand per k-step, lane order
+  float qpart[AT_WAVES][AT_HEADS];         // per-wave partial |q| maxima
   float wm[AT_WAVES][AT_HEADS];
   float wl[AT_WAVES][AT_HEADS];
 };
@@ -111,20 +110,20 @@ struct Raw {
   bool valid;   // the item exists
 };
 
-// Converts block j (channels 128*gq + 8j .. +7) of the lane's gathered bytes to fp16.
-template <bool WINDOW>
-__device__ __forceinline__ u32x4 convert_block(const Raw& r, const f16x2 (&sq)[8], int j) {
-  if (WINDOW) return fp8x8_to_f16x8(r.v[j >> 1][2 * (j & 1)], r.v[j >> 1][2 * (j & 1) + 1]);
+// Converts block j (channels 128*gq + 8j .. +7) of the lane's gathered bytes to fp16. The
+// format is wavefront-uniform, so this is a scalar branch, not a select.
+__device__ __forceinline__ u32x4 convert_block(const Raw& r, const f16x2 (&sq)[8], int j,
+                                               bool window) {
+  if (window) return fp8x8_to_f16x8(r.v[j >> 1][2 * (j & 1)], r.v[j >> 1][2 * (j & 1) + 1]);
   return fp4x8_to_f16x8(r.v[j >> 2][j & 3], sq[j >> 1]);
 }
 
 // Converts the lane's 16 blocks, stores them to its row quarter of the tile (tile_row)
-// and accumulates the logits.
-template <bool WINDOW>
-__device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const f16x8 (&qb)[16],
-                                                   uint16_t* tile_row) {
+// and accumulates the logits against the query operand held in LDS.
+__device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const u32x4 (*qop)[64],
+                                                   int lane, uint16_t* tile_row, bool window) {
   f16x2 sq[8];
-  if (!WINDOW) {
+  {
     const f16x2 s01 = e4m3x2_to_f16x2<false>(r.sc0), s23 = e4m3x2_to_f16x2<true>(r.sc0);
     const f16x2 s45 = e4m3x2_to_f16x2<false>(r.sc1), s67 = e4m3x2_to_f16x2<true>(r.sc1);
     sq[0] = f16x2{s01.x, s01.x}; sq[1] = f16x2{s01.y, s01.y};
@@ -135,10 +134,11 @@ __device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const f16x8 (&q
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const u32x4 a = convert_block<WINDOW>(r, sq, j);
+    const u32x4 a = convert_block(r, sq, j, window);
     *reinterpret_cast<u32x4*>(tile_row + 8 * j) = a;
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), qb[j], sacc, 0,
-                                                  0, 0);
+    const u32x4 b = qop[j][lane];
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), sacc, 0, 0, 0);
   }
   return sacc;
 }
@@ -170,44 +170,44 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const int gq = lane >> 4;    // lane group 0..3; also the channel quarter a lane gathers
   const int h = hg * AT_HEADS + col;
 
-  int nsw = n_swa[t];
-  nsw = nsw < 0 ? 0 : (nsw > AT_WINDOW ? AT_WINDOW : nsw);
-  const int n_msl = (k + AT_SLICE - 1) / AT_SLICE;     // slices of selected entries
-  const int n_sl = n_msl + (nsw + AT_SLICE - 1) / AT_SLICE;
+  // Slices: the selected entries first (slice c < n_msl holds entries 16c .. 16c+15), then
+  // the window rows. Split ranges are sized for the largest window, so they (and the
+  // position loads below) do not wait for n_swa.
+  const int n_msl = (k + AT_SLICE - 1) / AT_SLICE;
+  const int n_sl = n_msl + AT_WIN_SLICES;
   const int lo = (int)((int64_t)sp * n_sl / n_split);
   const int hi = (int)((int64_t)(sp + 1) * n_sl / n_split);
+  const int c0 = lo + wave;
+
+  // Selected positions, through a buffer over this query's k entries: a slot past k (or
+  // a slice past the split) reads 0 without touching memory and is marked absent.
+  const __amdgpu_buffer_rsrc_t rs_idx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(topk_idx) + (int64_t)t * ld_idx, (short)0, k * 4, 0x00020000);
+  // The value is used only when the gather is issued, which re-derives whether the slot
+  // exists, so the load is never waited for early.
+  auto position = [&](int c) -> int32_t {   // position of this lane's item of slice c
+    const int item = AT_SLICE * c + col;
+    const bool in = c < hi && c < n_msl && item < k;
+    return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs_idx, in ? item * 4 : k * 4, 0, 0));
+  };
+  const int32_t p0 = position(c0);
+  int32_t pX = position(c0 + AT_WAVES);
+
+  // This wavefront's two k-steps of the logit B operand: Q^T for head h, channels
+  // 8*ks + 128*gq .. +7 with ks = 2*wave, 2*wave + 1 (the conversion produces the rows
+  // with the same channel assignment).
+  const uint16_t* qrow = q + ((int64_t)t * 64 + h) * 512 + 128 * gq;
+  const u32x4 qr0 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave));
+  const u32x4 qr1 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave + 1));
+
+  int nsw = n_swa[t];
+  nsw = nsw < 0 ? 0 : (nsw > AT_WINDOW ? AT_WINDOW : nsw);
   const int64_t base = kv_start[t];
   const int64_t wbase = swa_start[t];
 
-  // Stage this split's selected positions in LDS (one HBM round trip, overlapped with the
-  // query load below).
-  const int i_lo = AT_SLICE * lo;
-  const int i_hi = min(AT_SLICE * hi, k);
-  const int n_idx = i_hi > i_lo ? i_hi - i_lo : 0;
-  int32_t pstage[AT_MAX_K / AT_THREADS];
-#pragma unroll
-  for (int r = 0; r < AT_MAX_K / AT_THREADS; ++r) {
-    const int j = tid + AT_THREADS * r;
-    pstage[r] = j < n_idx ? topk_idx[(int64_t)t * ld_idx + i_lo + j] : -1;
-  }
-
-  // Logit B operand: Q^T for head h, k-step ks, lane group gq = channels 8*ks + 128*gq ..
-  // +7 (the conversion below produces the rows with the same channel assignment).
-  u32x4 qraw[16];
-  const uint16_t* qrow = q + ((int64_t)t * 64 + h) * 512 + 128 * gq;
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * ks);
-
-#pragma unroll
-  for (int r = 0; r < AT_MAX_K / AT_THREADS; ++r) {
-    const int j = tid + AT_THREADS * r;
-    if (j < n_idx) sh.pidx[j] = pstage[r];
-  }
-  __syncthreads();
-
   // Gather: lane (item col of slice c, quarter gq) -> channels 128*gq .. +127 of that item.
-  // Slice c < n_msl holds selected entries 16c .. 16c+15, later slices window rows. The
-  // buffers are indexed by row relative to the query's own base, so the 32-bit record
+  // The buffers are indexed by row relative to the query's own base, so the 32-bit record
   // index covers any sequence; absent items use an index past every record count.
   constexpr uint32_t ABSENT = 0xFFFFFFFFu;
   const int64_t kv_rows = n_entries - base;
@@ -217,14 +217,12 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const __amdgpu_buffer_rsrc_t rs_kv = make_rows_rsrc(kv_fp4 + base * fp4_stride, (int)fp4_stride, kv_n);
   const __amdgpu_buffer_rsrc_t rs_sc = make_rows_rsrc(kv_scale + base * sc_stride, (int)sc_stride, kv_n);
   const __amdgpu_buffer_rsrc_t rs_win = make_rows_rsrc(window_kv + wbase * 512, 512, win_n);
-  auto fetch = [&](int c, Raw& raw) {
+  auto fetch = [&](int c, int32_t p, Raw& raw) {
     const bool main = c < n_msl;   // wavefront-uniform
     uint32_t ridx;
     bool ok;
     if (main) {
       const int item = AT_SLICE * c + col;
-      const int li = item - i_lo;
-      const int32_t p = sh.pidx[li < 0 ? 0 : (li >= AT_MAX_K ? AT_MAX_K - 1 : li)];
       const int64_t row = base + p;
       ok = c < hi && item < k && p >= 0 && row >= 0 && row < n_entries;
       ridx = (uint32_t)p;
@@ -251,54 +249,69 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     raw.sc0 = s8.x;
     raw.sc1 = s8.y;
   };
-  Raw buf0, buf1;
-  const int c0 = lo + wave;
 
+  // Query scale: per head, the largest |q| over its 512 channels (spread over the eight
+  // wavefronts' k-steps), then a power of two that brings it to [2^14, 2^15).
+  float qm = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qm = fmaxf(qm, fabsf(__uint_as_float(qr0[i] << 16)));
+    qm = fmaxf(qm, fabsf(__uint_as_float(qr0[i] & 0xFFFF0000u)));
+    qm = fmaxf(qm, fabsf(__uint_as_float(qr1[i] << 16)));
+    qm = fmaxf(qm, fabsf(__uint_as_float(qr1[i] & 0xFFFF0000u)));
+  }
+  qm = fmaxf(qm, __shfl_xor(qm, 16));
+  qm = fmaxf(qm, __shfl_xor(qm, 32));
+  if (gq == 0) sh.qpart[wave][col] = qm;
+  __syncthreads();
   float qmax = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qmax = fmaxf(qmax, fabsf(__uint_as_float(qraw[ks][i] << 16)));
-      qmax = fmaxf(qmax, fabsf(__uint_as_float(qraw[ks][i] & 0xFFFF0000u)));
-    }
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+  for (int w = 0; w < AT_WAVES; ++w) qmax = fmaxf(qmax, sh.qpart[w][col]);
   const int qexp = qmax > 0.f ? (int)((__float_as_uint(qmax) >> 23) & 0xFFu) - 127 : 0;
   int kexp = 14 - qexp;
   kexp = kexp < -126 ? -126 : (kexp > 126 ? 126 : kexp);
   const float up = __uint_as_float((uint32_t)(127 + kexp) << 23);
   // logits in log2 units: l2 = acc * scale * 2^-kexp * log2(e)
   const float lscale = scale * AT_LOG2E * __uint_as_float((uint32_t)(127 - kexp) << 23);
-  f16x8 qb[16];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
+  {
+    f16x8 b0, b1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      qb[ks][2 * i] = (_Float16)(__uint_as_float(qraw[ks][i] << 16) * up);
-      qb[ks][2 * i + 1] = (_Float16)(__uint_as_float(qraw[ks][i] & 0xFFFF0000u) * up);
+      b0[2 * i] = (_Float16)(__uint_as_float(qr0[i] << 16) * up);
+      b0[2 * i + 1] = (_Float16)(__uint_as_float(qr0[i] & 0xFFFF0000u) * up);
+      b1[2 * i] = (_Float16)(__uint_as_float(qr1[i] << 16) * up);
+      b1[2 * i + 1] = (_Float16)(__uint_as_float(qr1[i] & 0xFFFF0000u) * up);
     }
+    sh.qop[2 * wave][lane] = __builtin_bit_cast(u32x4, b0);
+    sh.qop[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, b1);
+  }
+  Raw buf;
+  fetch(c0, p0, buf);
+  // Issued after the gather, like the position load that follows every gather in the
+  // loop, so the loop's waits for a gather can leave one position load in flight.
+  int32_t pY = position(c0 + 2 * AT_WAVES);
+  __syncthreads();   // the query operand is complete
 
   // Output accumulator: O^T[d = 16*dt + 4*gq + i][h], dt = 0..31.
   f32x4 oacc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();   // reference max of head col (log2 units)
+  bool ok_pass = true;               // no logit of this pass overflowed the reference
   float l_run = 0.f;                 // this lane's share of the sum for head col
-  uint16_t* tile = sh.tile[wave];
+  uint16_t* const tile = sh.tile[wave];
   uint16_t* const tile_w = tile + TILE_ROW * col + TILE_QUARTER * gq;
   const uint16_t* const tile_r = tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3);
 
-  // One slice (c may lie past the split: its items are all absent); returns false when a
-  // logit exceeds the reference by more than AT_GAP (the reference is raised, and the
-  // caller repeats the pass).
-  auto step = [&](int c, Raw& raw) -> bool {
+  // One slice (c may lie past the split: its items are all absent); pn is the position of
+  // the next slice in this wavefront's sequence (c + AT_WAVES), whose gather is started as
+  // soon as this slice's registers are free. A logit exceeding the reference by more than
+  // AT_GAP raises the reference and marks the pass for a repeat.
+  auto step = [&](int c, Raw& raw, int32_t pn) {
     const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
-    const f32x4 sacc = c < n_msl ? convert_and_score<false>(raw, qb, tile_w)
-                                 : convert_and_score<true>(raw, qb, tile_w);
-    // The registers are free again: start the gather two slices ahead.
-    fetch(c + 2 * AT_WAVES, raw);
-    if (valid == 0ull) return true;
+    const f32x4 sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
+    fetch(c + AT_WAVES, pn, raw);
+    if (valid == 0ull) return;
     // LDS operations of one wavefront complete in order; the fences keep the compiler from
     // moving the tile reads above the writes.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -321,12 +334,12 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
       // and the test below is wavefront-uniform.
       const bool first = m_ref == -__builtin_inff();
       m_ref = fmaxf(m_ref, cm);   // finite: the slice has a valid item
-      if (!first) return false;
+      ok_pass = ok_pass && first;
     }
     f16x4 pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pe = __builtin_amdgcn_exp2f(lg[i] - m_ref);
+      const float pe = lg[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(lg[i] - m_ref);
       l_run += pe;
       pv[i] = (_Float16)pe;
     }
@@ -340,32 +353,35 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), pv,
                                                        oacc[dt], 0, 0, 0);
     }
-    return true;
   };
 
   // Every step runs unconditionally (a slice past the split is all absent and its loads
-  // return zeros without touching memory), so each buffer is written by the same loads on
-  // every path and a step waits only for its own slice.
+  // return zeros without touching memory), so the buffer is written by the same loads on
+  // every path and a step waits only for its own slice. Positions are loaded two steps
+  // before their gather: pX and pY alternate so no register is copied.
   bool again;
 #pragma unroll 1
   do {
-    fetch(c0, buf0);
-    fetch(c0 + AT_WAVES, buf1);
-    bool ok = true;
+    ok_pass = true;
 #pragma unroll 1
     for (int c = c0; c < hi; c += 2 * AT_WAVES) {
-      ok &= step(c, buf0);
-      ok &= step(c + AT_WAVES, buf1);
+      step(c, buf, pX);
+      pX = position(c + 3 * AT_WAVES);
+      step(c + AT_WAVES, buf, pY);
+      pY = position(c + 4 * AT_WAVES);
     }
-    again = !ok;
+    again = !ok_pass;
     if (again) {   // a logit overflowed the reference: repeat with the raised one
 #pragma unroll
       for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       l_run = 0.f;
+      fetch(c0, position(c0), buf);
+      pX = position(c0 + AT_WAVES);
+      pY = position(c0 + 2 * AT_WAVES);
     }
   } while (again);
 
-  // Merge the four wavefronts: O = sum_w 2^{m_w - M} O_w, L = sum_w 2^{m_w - M} l_w.
+  // Merge the eight wavefronts: O = sum_w 2^{m_w - M} O_w, L = sum_w 2^{m_w - M} l_w.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (gq == 0) {
@@ -373,13 +389,10 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     sh.wl[wave][col] = l_run;
   }
   __syncthreads();   // also ends every wavefront's use of its tile
-  // For each half of d, every wave stores its partial [head][d]; then lane (head
-  // oh = lane%16, channel group dq = lane/16) of wave w sums channels
-  // 64*rep + 16*w + 4*dq .. +3 of the half, each partial weighted by 2^(m_w - M). (The
-  // weights are applied by the reader so that the accumulators only ever feed MFMAs and
-  // stores.)
-  const int oh = lane & 15;
-  const int od = 16 * wave + 4 * (lane >> 4);
+  // Thread tid reduces the entries (dt = tid/64 and 8 + tid/64, lane l = tid%64) of every
+  // wavefront's half-accumulator: O^T[16*dt + 4*(l/16) + i][head l%16], so its head is
+  // tid%16 for both.
+  const int oh = tid & 15;
   float fwh[AT_WAVES];
   float Mh = -__builtin_inff();
 #pragma unroll
@@ -391,35 +404,36 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     fwh[w] = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - Mh);
     Lh += fwh[w] * sh.wl[w][oh];
   }
-  f32x4 acc[2][4];
+  const int rl = tid & 63;
+  const int rdt = tid >> 6;
+  f32x4 acc[2][2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      *reinterpret_cast<f32x4*>(&sh.part[wave][col][16 * dt + 4 * gq]) = oacc[16 * hf + dt];
+    for (int dt = 0; dt < 16; ++dt) sh.part[wave][dt][lane] = __builtin_bit_cast(u32x4, oacc[16 * hf + dt]);
     __syncthreads();
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const int d = od + 64 * rep;
-      f32x4 a = *reinterpret_cast<const f32x4*>(&sh.part[0][oh][d]) * fwh[0];
+    for (int j = 0; j < 2; ++j) {
+      f32x4 a = __builtin_bit_cast(f32x4, sh.part[0][rdt + 8 * j][rl]) * fwh[0];
 #pragma unroll
       for (int w = 1; w < AT_WAVES; ++w)
-        a += *reinterpret_cast<const f32x4*>(&sh.part[w][oh][d]) * fwh[w];
-      acc[hf][rep] = a;
+        a += __builtin_bit_cast(f32x4, sh.part[w][rdt + 8 * j][rl]) * fwh[w];
+      acc[hf][j] = a;
     }
     __syncthreads();
   }
+  // Channel of acc[hf][j][i]: 256*hf + 16*(rdt + 8*j) + 4*(rl/16) + i.
+  auto chan = [&](int hf, int j) { return 256 * hf + 16 * (rdt + 8 * j) + 4 * (rl >> 4); };
 
   if (n_split > 1) {
     // Partial of this split: O relative to its own max, plus max and sum per head.
     const int64_t g = (int64_t)t * AT_GROUPS + hg;
-    float* po = ws_o + (g * n_split + sp) * (AT_HEADS * 512) + oh * 512 + od;
+    float* po = ws_o + (g * n_split + sp) * (AT_HEADS * 512) + oh * 512;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int rep = 0; rep < 4; ++rep)
-        *reinterpret_cast<f32x4*>(po + 256 * hf + 64 * rep) = acc[hf][rep];
-    if (wave == 0 && lane < 16) {
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<f32x4*>(po + chan(hf, j)) = acc[hf][j];
+    if (tid < 16) {
       ws_ml[(g * n_split + sp) * 32 + oh] = Mh;
       ws_ml[(g * n_split + sp) * 32 + 16 + oh] = Lh;
     }
@@ -427,24 +441,24 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   }
 
   const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
-  uint16_t* orow = out + ((int64_t)t * 64 + hg * AT_HEADS + oh) * 512 + od;
+  uint16_t* orow = out + ((int64_t)t * 64 + hg * AT_HEADS + oh) * 512;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const f32x4 a = acc[hf][rep];
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 a = acc[hf][j];
       const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
       const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
-      *reinterpret_cast<u32x2*>(orow + 256 * hf + 64 * rep) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      *reinterpret_cast<u32x2*>(orow + chan(hf, j)) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
     }
-  if (lse != nullptr && wave == 0 && lane < 16)
+  if (lse != nullptr && tid < 16)
     lse[(int64_t)t * 64 + hg * AT_HEADS + oh] =
         Lh > 0.f ? (Mh + __log2f(Lh)) * AT_LN2 : -__builtin_inff();
 }
 
 // Combines the split partials of one (query, head group) in split order. Thread (head
-// tid/16, channels 32*(tid%16) .. +31).
-__global__ __launch_bounds__(AT_THREADS) void attn_merge_kernel(
+// tid/16, channels 32*(tid%16) .. +31); MERGE_THREADS threads.
+__global__ __launch_bounds__(MERGE_THREADS) void attn_merge_kernel(
     int n_split, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int64_t g = blockIdx.x;   // query * 4 + head group
@@ -509,7 +523,7 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                      n_entries, kv_start, topk_idx, ld_idx, k, window_kv, n_window_rows,
                      swa_start, n_swa, softmax_scale, n_q, splits, ws_ml, ws_o, out, lse);
   if (splits > 1)
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(n_q * AT_GROUPS), dim3(AT_THREADS), 0, stream,
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(n_q * AT_GROUPS), dim3(MERGE_THREADS), 0, stream,
                        splits, ws_ml, ws_o, out, lse);
   return hipGetLastError();
 }
