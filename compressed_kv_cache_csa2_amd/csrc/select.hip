@@ -7,9 +7,10 @@
 // Compression", 2.3.4; "DeepSeek-V4.1-Flash - Architecture", section 3).
 //
 // One 1024-thread workgroup per query row. Values become order-preserving 32-bit keys
-// (0 marks an element that cannot be selected); thread t owns 16 consecutive elements
-// (rows up to 16,384) or 32 (longer rows, walked in segments of 32,768 past that) and
-// keeps their keys in registers.
+// (0 marks an element that cannot be selected) held in registers: R = 16 keys per thread
+// for rows up to 16,384 elements, else R = 32 (walked in segments of 32,768 past that).
+// Thread t holds the R/4 float4 groups starting at elements 4*(t + 1024*g), so each
+// wavefront load reads 1 KiB of consecutive memory.
 //   1. A block reduction gives the count, the smallest and the largest key.
 //   2. Range refinement: the live key interval [A, B] is split into at most 2,048 equal
 //      power-of-two bins, an LDS histogram of the keys inside [A, B] is taken, and the bin
@@ -19,9 +20,10 @@
 //      to LDS and the k-th largest, tau, is the one key with fewer than `need` keys
 //      above it and at least `need` at or above it; no further pass over the row.
 //   4. Emission: every key > tau is kept, and of the keys == tau the lowest-indexed
-//      (k - #greater). A block-wide prefix sum gives each thread its output offset (a
-//      second one orders the ties when only some of them are kept); output is
-//      deterministic and sorted by index.
+//      (k - #greater). One block-wide prefix sum over the per-group counts (four 16-bit
+//      fields per 64-bit word) gives every kept element its rank in index order (a second
+//      one orders the ties when only some of them are kept). Ranks go to LDS and the
+//      result is written out in one coalesced pass; output is sorted by index.
 //
 // Block prefilter for Top-K: with maxima of 8-slot blocks, any threshold T such that at
 // least k blocks have maximum >= T bounds the k-th largest score from below (each of those
@@ -39,18 +41,24 @@ constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int NBINS = 2048;
 constexpr int BINS_PER_THREAD = NBINS / SEL_THREADS;
 constexpr int CAND_BLOCKS_CAP = 2048;
+constexpr int OUT_CAP = 2048;          // the largest k / n_keep
 constexpr int LIST_CAP = 256;          // an interval this small is finished by counting
 constexpr uint32_t ALL_TIES = 0xFFFFFFFFu;
+constexpr uint32_t INF_KEY = 0xFF800000u;   // float_key(+inf)
 
 struct SelShared {
-  uint32_t hist[NBINS];
+  uint32_t hist[NBINS + 64];           // + one spill bin per lane for keys outside the interval
   uint32_t wsum[SEL_WAVES];
+  uint32_t wabove[SEL_WAVES];
   uint32_t wmin[SEL_WAVES];
   uint32_t wmax[SEL_WAVES];
+  uint32_t wcnt[SEL_WAVES];
   uint32_t scal[4];
   uint32_t list_n;
   uint32_t lkey[LIST_CAP];
   int32_t cblocks[CAND_BLOCKS_CAP];
+  int32_t obuf[OUT_CAP];
+  uint32_t gpos[8 * SEL_THREADS];      // per-group counts, then offsets, in index order
 };
 
 // Unsigned minimum / maximum (the device min/max overloads compare as signed int).
@@ -80,53 +88,103 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, SelShared& 
   return before + x - v;
 }
 
-// The keys of one row: thread tid holds elements seg*SEG + tid*R + r in keys[r]. Short
-// rows use R = 16 so that every thread of the block holds keys.
-template <class Src, int R>
+// Rank offsets in index order for a per-thread R-bit mask whose bit 4g + j stands for
+// element 4*(tid + SEL_THREADS*g) + j: index order runs over g, then tid, then j, so the
+// per-group counts are laid out in LDS in that order, each thread sums NG consecutive
+// ones, and one block scan gives every (g, tid) its offset. start[g] receives the rank of
+// this thread's first element of group g.
+template <int NG>
+__device__ __forceinline__ void group_offsets(uint32_t mask, SelShared& sh, uint32_t (&start)[NG],
+                                              uint32_t* total) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) sh.gpos[g * SEL_THREADS + tid] = __popc((mask >> (4 * g)) & 0xFu);
+  __syncthreads();
+  uint32_t e[NG];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    e[i] = sh.gpos[NG * tid + i];
+    local += e[i];
+  }
+  uint32_t excl = block_exclusive_scan(local, sh, total);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    sh.gpos[NG * tid + i] = excl;
+    excl += e[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < NG; ++g) start[g] = sh.gpos[g * SEL_THREADS + tid];
+  __syncthreads();
+}
+
+// The keys of one row. keys[4g + j] is element seg*SEG + 4*(tid + SEL_THREADS*g) + j.
+// A row of one segment is loaded once; a longer one (MULTI) is reloaded segment by
+// segment in every pass.
+template <class Src, int R, bool MULTI>
 struct KeyRow {
   static constexpr int SEG = SEL_THREADS * R;
   Src src;
-  int64_t n;
+  uint32_t n;
   int nseg;
   uint32_t keys[R];
-  int loaded;
 
-  __device__ __forceinline__ KeyRow(const Src& s, int64_t n_) : src(s), n(n_), nseg((int)((n_ + SEG - 1) / SEG)), loaded(-1) {}
-
+  __device__ __forceinline__ KeyRow(const Src& s, int64_t n_) : src(s), n((uint32_t)n_), nseg((int)((n_ + SEG - 1) / SEG)) {
+    if (!MULTI) src.template load<R>(first(0), 4u * SEL_THREADS, n, keys);
+  }
+  __device__ __forceinline__ int segs() const { return MULTI ? nseg : 1; }
+  __device__ __forceinline__ static uint32_t first(int seg) {
+    return (uint32_t)seg * SEG + 4u * threadIdx.x;
+  }
   __device__ __forceinline__ void load(int seg) {
-    if (seg == loaded) return;
-    const uint32_t base = (uint32_t)seg * SEG + threadIdx.x * R;
-    src.template load<R>(base, (uint32_t)n, keys);
-    loaded = seg;
+    if (MULTI) src.template load<R>(first(seg), 4u * SEL_THREADS, n, keys);
   }
   static constexpr int per_thread() { return R; }
 };
 
-// One histogram pass over the keys in [A, B], which holds the need-th largest of them:
-// [A, B] becomes the one of at most 2,048 equal power-of-two bins that holds it, and
-// `need` the rank within the new interval. Bins follow the interval's own span, so the
-// first pass spreads the keys over many bins (few atomic collisions) and each pass shrinks
-// the interval by 2^11. Returns the number of keys in the new interval.
+// The interval search. [A, B] is a key interval believed to hold the k-th largest key;
+// one pass histograms the keys inside it into at most 2,048 equal power-of-two bins
+// (keys outside land in per-lane spill bins) and counts the keys above B with a wave
+// ballot. If the k-th largest key lies in [A, B], the interval narrows to the bin holding
+// it (each pass divides the span by 2^11); otherwise the caller moves the interval.
+struct Interval {
+  uint32_t A, B;
+  uint32_t need;   // rank of the k-th largest key within [A, B] (1 = the largest there)
+  uint32_t cnt;    // keys in [A, B]
+  uint32_t ge;     // keys >= A
+};
+
+enum { PASS_NARROWED = 0, PASS_ABOVE = 1, PASS_BELOW = 2 };
+
 template <class Row>
-__device__ __forceinline__ uint32_t hist_pass(Row& row, uint32_t& A, uint32_t& B, uint32_t& need,
-                                              SelShared& sh) {
+__device__ __forceinline__ int hist_pass(Row& row, uint32_t k, Interval& iv, SelShared& sh) {
   constexpr int R = Row::per_thread();
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t A = iv.A, B = iv.B;
   const uint32_t span = B - A;
   const int bits = 32 - __clz(span);                 // span < 2^bits
   const int s = bits > 11 ? bits - 11 : 0;           // (span >> s) < 2048
+  const uint32_t spill = NBINS + lane;               // keys outside [A, B] (and 0) land here
 #pragma unroll
   for (int j = 0; j < BINS_PER_THREAD; ++j) sh.hist[tid + j * SEL_THREADS] = 0;
   __syncthreads();
-  for (int seg = 0; seg < row.nseg; ++seg) {
+  uint32_t above = 0;   // wave-uniform
+  for (int seg = 0; seg < row.segs(); ++seg) {
     row.load(seg);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t key = row.keys[r];
-      if (key != 0u && key >= A && key <= B) atomicAdd(&sh.hist[(key - A) >> s], 1u);
+      const uint32_t d = key - A;                    // A >= 1, so key 0 wraps past span
+      atomicAdd(&sh.hist[d <= span ? d >> s : spill], 1u);
+      above += __popcll(__ballot(key > B));
     }
   }
+  if (lane == 0) sh.wabove[wave] = above;
   __syncthreads();
+  uint32_t n_above = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_WAVES; ++i) n_above += sh.wabove[i];
   // Thread tid owns bins BPT*tid .. BPT*tid + BPT-1.
   uint32_t h[BINS_PER_THREAD];
   uint32_t local = 0;
@@ -137,15 +195,18 @@ __device__ __forceinline__ uint32_t hist_pass(Row& row, uint32_t& A, uint32_t& B
   }
   uint32_t total;
   const uint32_t excl = block_exclusive_scan(local, sh, &total);
-  uint32_t above = total - excl - local;   // keys in bins above this thread's bins
+  if (n_above >= k) return PASS_ABOVE;                // uniform
+  const uint32_t need = k - n_above;
+  if (need > total) return PASS_BELOW;
+  uint32_t hi_keys = total - excl - local;   // keys in bins above this thread's bins
 #pragma unroll
   for (int j = BINS_PER_THREAD - 1; j >= 0; --j) {
-    if (above < need && need <= above + h[j]) {
+    if (hi_keys < need && need <= hi_keys + h[j]) {
       sh.scal[0] = BINS_PER_THREAD * tid + j;
-      sh.scal[1] = above;
+      sh.scal[1] = hi_keys;
       sh.scal[2] = h[j];
     }
-    above += h[j];
+    hi_keys += h[j];
   }
   __syncthreads();
   const uint32_t b = sh.scal[0];
@@ -154,21 +215,35 @@ __device__ __forceinline__ uint32_t hist_pass(Row& row, uint32_t& A, uint32_t& B
   __syncthreads();
   const uint64_t lo = (uint64_t)A + ((uint64_t)b << s);
   const uint64_t hi = lo + (1ull << s) - 1;
-  need -= above_b;
-  A = (uint32_t)lo;
-  B = hi < (uint64_t)B ? (uint32_t)hi : B;
-  return in_b;
+  iv.A = (uint32_t)lo;
+  iv.B = hi < (uint64_t)B ? (uint32_t)hi : B;
+  iv.need = need - above_b;
+  iv.cnt = in_b;
+  iv.ge = n_above + above_b + in_b;
+  return PASS_NARROWED;
 }
 
-// Narrows [A, B] (holding the k-th largest key, with k - need keys above B) until A is
-// the k-th largest key or, once at most cap keys are >= A, a lower bound of it.
+// Narrows iv until [A, B] holds the k-th largest key and either A == B, or (cap_list)
+// at most LIST_CAP keys lie in [A, B], or (cap_ge) at most cap_ge keys are >= A. A first
+// interval that misses the k-th key is replaced by the part of the key range on its
+// side, which holds it; the search then always narrows, so it ends within a few passes.
 template <class Row>
-__device__ __forceinline__ void refine_cap(Row& row, uint32_t& A, uint32_t& B, uint32_t& need,
-                                           uint32_t k, uint32_t cap, SelShared& sh) {
+__device__ __forceinline__ void locate(Row& row, uint32_t k, Interval& iv, uint32_t cap_list,
+                                       uint32_t cap_ge, SelShared& sh) {
 #pragma unroll 1
-  while (A != B) {
-    const uint32_t in_new = hist_pass(row, A, B, need, sh);
-    if ((k - need) + in_new <= cap) break;   // keys >= the new A
+  for (int it = 0; it < 8; ++it) {
+    const int r = hist_pass(row, k, iv, sh);
+    if (r == PASS_ABOVE) {         // B < 0xFFFFFFFF here, since some key is above it
+      iv.A = iv.B + 1u;
+      iv.B = 0xFFFFFFFFu;
+      continue;
+    }
+    if (r == PASS_BELOW) {         // A > 1 here, since some valid key is below it
+      iv.B = iv.A - 1u;
+      iv.A = 1u;
+      continue;
+    }
+    if (iv.A == iv.B || iv.cnt <= cap_list || iv.ge <= cap_ge) return;
   }
 }
 
@@ -177,23 +252,27 @@ __device__ __forceinline__ void refine_cap(Row& row, uint32_t& A, uint32_t& B, u
 // large. tau receives it and n_eq how many keys equal to tau are taken (ALL_TIES when
 // every one of them is).
 template <class Row>
-__device__ __forceinline__ void rank_list(Row& row, uint32_t A, uint32_t B, uint32_t need,
-                                          uint32_t cnt, SelShared& sh, uint32_t& tau,
+__device__ __forceinline__ void rank_list(Row& row, const Interval& iv, SelShared& sh, uint32_t& tau,
                                           uint32_t& n_eq) {
   constexpr int R = Row::per_thread();
   const int tid = threadIdx.x;
   if (tid < LIST_CAP) sh.lkey[tid] = 0u;   // padding reads as "below every key"
   if (tid == 0) sh.list_n = 0u;
   __syncthreads();
-  for (int seg = 0; seg < row.nseg; ++seg) {
+  const uint32_t A = iv.A, span = iv.B - iv.A, cnt = iv.cnt, need = iv.need;
+  for (int seg = 0; seg < row.segs(); ++seg) {
     row.load(seg);
+    uint32_t in = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t key = row.keys[r];
-      if (key != 0u && key >= A && key <= B) {
-        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
-        if (slot < (uint32_t)LIST_CAP) sh.lkey[slot] = key;
-      }
+    for (int r = 0; r < R; ++r) in |= (uint32_t)(row.keys[r] - A <= span) << r;
+    while (in != 0u) {   // rare: only the few keys of the interval
+      const int r = __builtin_ctz(in);
+      in &= in - 1u;
+      uint32_t key = 0;
+#pragma unroll
+      for (int q = 0; q < R; ++q) key = q == r ? row.keys[q] : key;
+      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+      if (slot < (uint32_t)LIST_CAP) sh.lkey[slot] = key;
     }
   }
   __syncthreads();
@@ -217,31 +296,37 @@ __device__ __forceinline__ void rank_list(Row& row, uint32_t A, uint32_t B, uint
   __syncthreads();
 }
 
-// Count / min / max of the valid keys of the row.
+// Count of the valid keys of the row, and a first interval: the smallest and largest
+// finite key among each thread's first four (a 4,096-key sample of the first segment).
+// +inf keys stay out of it (a forced +inf block would stretch the first histogram over
+// the whole key range); a sample with no finite key gives the whole finite range.
 template <class Row>
-__device__ __forceinline__ void row_stats(Row& row, uint32_t& count, uint32_t& kmin, uint32_t& kmax,
-                          SelShared& sh) {
+__device__ __forceinline__ void row_prepare(Row& row, uint32_t& count, Interval& iv, SelShared& sh) {
   constexpr int R = Row::per_thread();
-  uint32_t c = 0, mn = 0xFFFFFFFFu, mx = 0u;
-  for (int seg = 0; seg < row.nseg; ++seg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t c = 0;   // wave-uniform
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int seg = 0; seg < row.segs(); ++seg) {
     row.load(seg);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t key = row.keys[r];
-      c += key != 0u;
-      mn = umin32(mn, key != 0u ? key : 0xFFFFFFFFu);
-      mx = umax32(mx, key);
+    for (int r = 0; r < R; ++r) c += __popcll(__ballot(row.keys[r] != 0u));
+    if (seg == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t key = row.keys[r];
+        const bool fin = key != 0u && key != INF_KEY;
+        mn = umin32(mn, fin ? key : 0xFFFFFFFFu);
+        mx = umax32(mx, fin ? key : 0u);
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    c += __shfl_xor(c, off);
     mn = umin32(mn, (uint32_t)__shfl_xor(mn, off));
     mx = umax32(mx, (uint32_t)__shfl_xor(mx, off));
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
-    sh.wsum[wave] = c;
+    sh.wcnt[wave] = c;
     sh.wmin[wave] = mn;
     sh.wmax[wave] = mx;
   }
@@ -251,57 +336,103 @@ __device__ __forceinline__ void row_stats(Row& row, uint32_t& count, uint32_t& k
   mx = 0u;
 #pragma unroll
   for (int i = 0; i < SEL_WAVES; ++i) {
-    c += sh.wsum[i];
+    c += sh.wcnt[i];
     mn = umin32(mn, sh.wmin[i]);
     mx = umax32(mx, sh.wmax[i]);
   }
   __syncthreads();
   count = c;
-  kmin = mn;
-  kmax = mx;
+  if (mx == 0u) {       // no finite key in the sample
+    mn = 1u;
+    mx = INF_KEY - 1u;
+  }
+  iv.A = mn;
+  iv.B = mx;
 }
 
-// Emit, in ascending index order, every key > tau and of the keys == tau the first n_eq
-// (every one for ALL_TIES). emit(rank, index). Returns the count.
+// Rank offsets in index order for a per-thread R-bit mask whose bit 4g + j stands for
+// element 4*(tid + SEL_THREADS*g) + j: index order runs over g, then tid, then j, so the
+// per-group counts are laid out in LDS in that order, each thread sums NG consecutive
+// ones, and one block scan turns them into offsets. Afterwards sh.gpos[g*SEL_THREADS +
+// tid] is the rank of this thread's first element of group g; the caller synchronises
+// before gpos is written again.
+template <int NG>
+__device__ __forceinline__ uint32_t group_offsets(uint32_t mask, SelShared& sh) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) sh.gpos[g * SEL_THREADS + tid] = __popc((mask >> (4 * g)) & 0xFu);
+  __syncthreads();
+  uint32_t e[NG];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    e[i] = sh.gpos[NG * tid + i];
+    local += e[i];
+  }
+  uint32_t total;
+  uint32_t excl = block_exclusive_scan(local, sh, &total);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    sh.gpos[NG * tid + i] = excl;
+    excl += e[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// Emit every key > tau and, of the keys == tau, the first n_eq in index order (every one
+// for ALL_TIES). emit(rank, index) with rank = position in ascending index order.
+// Returns the count.
 template <class Row, class Emit>
 __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_t n_eq, SelShared& sh,
                                  Emit emit) {
   constexpr int R = Row::per_thread();
+  constexpr int NG = R / 4;
+  const int tid = threadIdx.x;
   const bool split_ties = n_eq != 0u && n_eq != ALL_TIES;
   uint32_t eq_base = 0, out_base = 0;
-  for (int seg = 0; seg < row.nseg; ++seg) {
+  for (int seg = 0; seg < row.segs(); ++seg) {
     row.load(seg);
-    uint32_t gt_mask = 0, eq_mask = 0;
+    uint32_t take = 0, eq_mask = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t key = row.keys[r];
-      gt_mask |= (uint32_t)(key != 0u && key > tau) << r;
-      eq_mask |= (uint32_t)(key != 0u && key == tau) << r;
+    for (int r = 0; r < R; ++r) take |= (uint32_t)(row.keys[r] > tau) << r;   // tau >= 0
+    if (n_eq != 0u) {   // tau is then a valid key, so key == tau excludes key 0
+#pragma unroll
+      for (int r = 0; r < R; ++r) eq_mask |= (uint32_t)(row.keys[r] == tau) << r;
     }
-    uint32_t take = n_eq == ALL_TIES ? gt_mask | eq_mask : gt_mask;
-    if (split_ties) {   // uniform: keep the first n_eq ties of the row
-      const uint32_t n_e = __popc(eq_mask);
-      uint32_t eq_total;
-      const uint32_t eq_before = eq_base + block_exclusive_scan(n_e, sh, &eq_total);
-      const uint32_t eq_keep = eq_before >= n_eq ? 0u : umin32(n_e, n_eq - eq_before);
-      uint32_t seen = 0;
+    if (n_eq == ALL_TIES) take |= eq_mask;
+    if (split_ties) {   // uniform: keep the first n_eq ties of the row in index order
+      const uint32_t eq_total = group_offsets<NG>(eq_mask, sh);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t bit = (eq_mask >> r) & 1u;
-        take |= (uint32_t)(bit != 0u && seen < eq_keep) << r;
-        seen += bit;
+      for (int g = 0; g < NG; ++g) {
+        uint32_t rank = eq_base + sh.gpos[g * SEL_THREADS + tid];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          const uint32_t bit = (eq_mask >> r) & 1u;
+          take |= (uint32_t)(bit != 0u && rank < n_eq) << r;
+          rank += bit;
+        }
       }
       eq_base += eq_total;
+      __syncthreads();
     }
-    uint32_t take_total;
-    uint32_t pos = out_base + block_exclusive_scan(__popc(take), sh, &take_total);
-    const uint32_t base = (uint32_t)seg * Row::SEG + threadIdx.x * R;
-    while (take != 0u) {
-      const int r = __builtin_ctz(take);
-      take &= take - 1u;
-      emit(pos++, base + r);
+    const uint32_t take_total = group_offsets<NG>(take, sh);
+    // Recomputed here rather than kept from the loads: the opaque copy stops the compiler
+    // from holding R element indices live through every pass.
+    uint32_t first = Row::first(seg);
+    asm volatile("" : "+v"(first));
+    uint32_t rest = take;
+    while (rest != 0u) {
+      const int r = __builtin_ctz(rest);
+      rest &= rest - 1u;
+      const int g = r >> 2;
+      const uint32_t before = __popc(take & ((1u << r) - 1u) & (0xFu << (4 * g)));
+      emit(out_base + sh.gpos[g * SEL_THREADS + tid] + before,
+           first + 4u * SEL_THREADS * (uint32_t)g + (uint32_t)(r & 3));
     }
     out_base += take_total;
+    __syncthreads();
   }
   return out_base;
 }
@@ -309,19 +440,17 @@ __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_
 // Full exact selection of the k best keys of a row.
 template <class Row, class Emit>
 __device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& sh, Emit emit) {
-  uint32_t cnt, A, B;
-  row_stats(row, cnt, A, B, sh);
+  uint32_t cnt;
+  Interval iv;
+  row_prepare(row, cnt, iv, sh);
   if (cnt <= k) return emit_ordered(row, 0u, 0u, sh, emit);
-  // [A, B] holds cnt keys, of which the need-th largest is the k-th largest of the row.
-  uint32_t need = k;
-#pragma unroll 1
-  while (A != B && cnt > (uint32_t)LIST_CAP) cnt = hist_pass(row, A, B, need, sh);
+  locate(row, k, iv, (uint32_t)LIST_CAP, 0u, sh);
   uint32_t tau, n_eq;
-  if (A == B) {
-    tau = A;
-    n_eq = need == cnt ? ALL_TIES : need;
+  if (iv.A == iv.B) {
+    tau = iv.A;
+    n_eq = iv.need == iv.cnt ? ALL_TIES : iv.need;
   } else {
-    rank_list(row, A, B, need, cnt, sh, tau, n_eq);
+    rank_list(row, iv, sh, tau, n_eq);
   }
   return emit_ordered(row, tau, n_eq, sh, emit);
 }
@@ -330,10 +459,10 @@ __device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& 
 
 // Rows are 16-byte aligned with a leading dimension that is a multiple of 4 (checked by
 // the C ABI), so a float4 starting below n never leaves its row. Every source issues all
-// of a segment's loads before using any (an element past the end reads the row's first
+// of a segment's loads before using any (a group past the end reads the row's first
 // float4 and is masked afterwards), so a segment costs one memory round trip. Element
-// indices of a row are below 2^31 + 2^15 (rows hold at most 2^31 elements), so they are
-// kept in 32 bits.
+// indices of a row stay below 2^31 + 2^15 (rows hold at most 2^31 elements), so they are
+// kept in 32 bits. Group g of a thread starts at element first + g * stride.
 __device__ __forceinline__ void keys4(float4 v, uint32_t i0, uint32_t n, uint32_t* k) {
   const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -344,15 +473,16 @@ __device__ __forceinline__ void keys4(float4 v, uint32_t i0, uint32_t n, uint32_
 struct ScoreSrc {
   const float* row;
   template <int R>
-  __device__ __forceinline__ void load(uint32_t base, uint32_t n, uint32_t (&keys)[R]) const {
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
     float4 v[R / 4];
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const uint32_t i0 = base + 4 * q;
-      v[q] = *reinterpret_cast<const float4*>(row + (i0 < n ? i0 : 0u));
+    for (int g = 0; g < R / 4; ++g) {
+      const uint32_t i0 = first + g * stride;
+      v[g] = *reinterpret_cast<const float4*>(row + (i0 < n ? i0 : 0u));
     }
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) keys4(v[q], base + 4 * q, n, &keys[4 * q]);
+    for (int g = 0; g < R / 4; ++g) keys4(v[g], first + g * stride, n, &keys[4 * g]);
   }
 };
 
@@ -363,23 +493,24 @@ struct BlockSrc {
   int64_t special;
   float special_value;
   template <int R>
-  __device__ __forceinline__ void load(uint32_t base, uint32_t n, uint32_t (&keys)[R]) const {
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
     float4 v[R / 4];
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const uint32_t i0 = base + 4 * q;
-      v[q] = *reinterpret_cast<const float4*>(bm + (i0 < n ? i0 : 0u));
+    for (int g = 0; g < R / 4; ++g) {
+      const uint32_t i0 = first + g * stride;
+      v[g] = *reinterpret_cast<const float4*>(bm + (i0 < n ? i0 : 0u));
     }
     const uint32_t sp = special < 0 ? 0xFFFFFFFFu : (uint32_t)special;
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const uint32_t i0 = base + 4 * q;
+    for (int g = 0; g < R / 4; ++g) {
+      const uint32_t i0 = first + g * stride;
       const uint32_t j = sp - i0;   // < 4 only when the special block is in this float4
-      if (j == 0u) v[q].x = special_value;
-      if (j == 1u) v[q].y = special_value;
-      if (j == 2u) v[q].z = special_value;
-      if (j == 3u) v[q].w = special_value;
-      keys4(v[q], i0, n, &keys[4 * q]);
+      if (j == 0u) v[g].x = special_value;
+      if (j == 1u) v[g].y = special_value;
+      if (j == 2u) v[g].z = special_value;
+      if (j == 3u) v[g].w = special_value;
+      keys4(v[g], i0, n, &keys[4 * g]);
     }
   }
 };
@@ -391,23 +522,24 @@ struct CandSrc {
   const int32_t* cblocks;   // LDS
   int64_t n_slots;          // slots >= n_slots are outside the selection
   template <int R>
-  __device__ __forceinline__ void load(uint32_t base, uint32_t n, uint32_t (&keys)[R]) const {
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
     const uint32_t ns = (uint32_t)n_slots;
     float4 v[R / 4];
     uint32_t s0[R / 4];
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {   // 4 consecutive elements of one block
-      const uint32_t i0 = base + 4 * q;
+    for (int g = 0; g < R / 4; ++g) {   // 4 consecutive elements of one block
+      const uint32_t i0 = first + g * stride;
       const int32_t b = i0 < n ? cblocks[i0 >> 3] : -1;
-      s0[q] = b >= 0 ? (uint32_t)b * 8u + (i0 & 7u) : ns;   // absent block: masked
+      s0[g] = b >= 0 ? (uint32_t)b * 8u + (i0 & 7u) : ns;   // absent block: masked
     }
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q)
-      v[q] = *reinterpret_cast<const float4*>(row + (s0[q] < ns ? s0[q] : 0u));
+    for (int g = 0; g < R / 4; ++g)
+      v[g] = *reinterpret_cast<const float4*>(row + (s0[g] < ns ? s0[g] : 0u));
 #pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const bool ok = s0[q] < ns;
-      keys4(v[q], ok ? s0[q] : 0u, ok ? ns : 0u, &keys[4 * q]);
+    for (int g = 0; g < R / 4; ++g) {
+      const bool ok = s0[g] < ns;
+      keys4(v[g], ok ? s0[g] : 0u, ok ? ns : 0u, &keys[4 * g]);
     }
   }
 };
@@ -420,11 +552,20 @@ template <class Src, class Emit>
 __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32_t k, SelShared& sh,
                                                Emit emit) {
   if (n <= (int64_t)SEL_THREADS * 16) {
-    KeyRow<Src, 16> row(src, n);
+    KeyRow<Src, 16, false> row(src, n);
     return select_row(row, k, sh, emit);
   }
-  KeyRow<Src, 32> row(src, n);
+  if (n <= (int64_t)SEL_THREADS * 32) {
+    KeyRow<Src, 32, false> row(src, n);
+    return select_row(row, k, sh, emit);
+  }
+  KeyRow<Src, 32, true> row(src, n);
   return select_row(row, k, sh, emit);
+}
+
+// The first min(kept, k) entries of sh.obuf go out, then -1 up to k.
+__device__ __forceinline__ void write_out(const SelShared& sh, uint32_t kept, int k, int32_t* orow) {
+  for (int r = threadIdx.x; r < k; r += SEL_THREADS) orow[r] = (uint32_t)r < kept ? sh.obuf[r] : -1;
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
@@ -440,13 +581,12 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
     const int64_t v = n_valid[t];
     n = v < 0 ? 0 : (v < n ? v : n);
   }
-  int32_t* orow = out + (int64_t)t * ld_idx;
   const uint32_t kk = (uint32_t)k;
-  auto map = [&](int64_t slot) -> int32_t {
+  auto map = [&](uint32_t slot) -> int32_t {
     if (pool_use != 1) return (int32_t)slot;
-    const int64_t pb = slot >> 3;
-    const int32_t b = pb < n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
-    return b < 0 ? -1 : (int32_t)((int64_t)b * 8 + (slot & 7));
+    const uint32_t pb = slot >> 3;
+    const int32_t b = pb < (uint32_t)n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
+    return b < 0 ? -1 : (int32_t)((uint32_t)b * 8u + (slot & 7u));
   };
   uint32_t kept = 0;
   bool done = false;
@@ -458,8 +598,8 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
     for (int i = threadIdx.x; i < n_pool; i += SEL_THREADS) sh.cblocks[i] = prow[i];
     __syncthreads();
     const CandSrc csrc{row, sh.cblocks, n};
-    kept = select_any(csrc, (int64_t)n_pool * 8, kk, sh, [&](uint32_t rank, int64_t i) {
-      if (rank < kk) orow[rank] = (int32_t)((int64_t)sh.cblocks[i >> 3] * 8 + (i & 7));
+    kept = select_any(csrc, (int64_t)n_pool * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
+      if (rank < kk) sh.obuf[rank] = (int32_t)((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
     });
     done = true;
   }
@@ -472,38 +612,39 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
       for (int64_t s = (nb - 1) * 8; s < n; ++s) tail_max = fmaxf(tail_max, row[s]);
     }
     const BlockSrc bsrc{block_max + (int64_t)t * ld_bm, tail ? nb - 1 : -1, tail_max};
-    KeyRow<BlockSrc, 32> brow(bsrc, nb);
-    uint32_t count, A, B;
-    row_stats(brow, count, A, B, sh);
+    KeyRow<BlockSrc, 32, true> brow(bsrc, nb);
+    uint32_t count;
+    Interval iv;
+    row_prepare(brow, count, iv, sh);
     uint32_t thr = 0;   // keep blocks with key >= thr (0: every valid block)
     bool fits = count <= (uint32_t)CAND_BLOCKS_CAP;
     if (count > kk) {
-      uint32_t need = kk;
-      refine_cap(brow, A, B, need, kk, (uint32_t)CAND_BLOCKS_CAP, sh);
-      thr = A;
+      locate(brow, kk, iv, 0u, (uint32_t)CAND_BLOCKS_CAP, sh);
+      thr = iv.A;
       fits = true;
     }
     // Collect candidate blocks (ascending); count them to check the cap.
     const uint32_t n_cand = emit_ordered(brow, thr == 0u ? 0u : thr - 1u, 0u, sh,
-                                         [&](uint32_t rank, int64_t b) {
+                                         [&](uint32_t rank, uint32_t b) {
                                            if (rank < CAND_BLOCKS_CAP) sh.cblocks[rank] = (int32_t)b;
                                          });
     __syncthreads();
     if (fits && n_cand <= (uint32_t)CAND_BLOCKS_CAP) {
       const CandSrc csrc{row, sh.cblocks, n};
-      kept = select_any(csrc, (int64_t)n_cand * 8, kk, sh, [&](uint32_t rank, int64_t i) {
-        if (rank < kk) orow[rank] = map((int64_t)sh.cblocks[i >> 3] * 8 + (i & 7));
+      kept = select_any(csrc, (int64_t)n_cand * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
+        if (rank < kk) sh.obuf[rank] = map((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
       });
       done = true;
     }
   }
   if (!done) {
     const ScoreSrc ssrc{row};
-    kept = select_any(ssrc, n, kk, sh, [&](uint32_t rank, int64_t i) {
-      if (rank < kk) orow[rank] = map(i);
+    kept = select_any(ssrc, n, kk, sh, [&](uint32_t rank, uint32_t i) {
+      if (rank < kk) sh.obuf[rank] = map(i);
     });
   }
-  for (int64_t r = kept + threadIdx.x; r < k; r += SEL_THREADS) orow[r] = -1;
+  __syncthreads();
+  write_out(sh, kept, k, out + (int64_t)t * ld_idx);
 }
 
 __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
@@ -514,12 +655,12 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
   const int64_t nv = n_visible[t];
   int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
   if (nb > ld_bm) nb = ld_bm;
-  int32_t* prow = pool + (int64_t)t * ld_pool;
   const BlockSrc src{block_max + (int64_t)t * ld_bm, nb - 1, __builtin_inff()};
-  const uint32_t kept = select_any(src, nb, (uint32_t)n_keep, sh, [&](uint32_t rank, int64_t b) {
-    if (rank < (uint32_t)n_keep) prow[rank] = (int32_t)b;
+  const uint32_t kept = select_any(src, nb, (uint32_t)n_keep, sh, [&](uint32_t rank, uint32_t b) {
+    if (rank < (uint32_t)n_keep) sh.obuf[rank] = (int32_t)b;
   });
-  for (int64_t r = kept + threadIdx.x; r < n_keep; r += SEL_THREADS) prow[r] = -1;
+  __syncthreads();
+  write_out(sh, kept, n_keep, pool + (int64_t)t * ld_pool);
 }
 
 hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
