@@ -14,8 +14,9 @@
 // the K-sum is the plain dot product. The 32x32 fp32 result sits in 16 registers per
 // lane (row = 8*(r/4) + 4*half + r%4, column = l%32); ReLU, the per-head weight and the
 // sum over heads happen in registers plus one cross-half shuffle. Scores and optional
-// 8-slot block maxima are written with coalesced stores. Work per step is 8,192 flops
-// per position against 128 bytes read: HBM-bound at 64 flop/B.
+// 8-slot block maxima are kept in registers and written with coalesced stores after the
+// workgroup's rows have been read. Work per step is 8,192 flops per position against 128
+// bytes read: HBM-bound at 64 flop/B.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -27,6 +28,7 @@ constexpr int IS_THREADS = 256;
 // every CU busy).
 constexpr int IS_STEPS_FULL = 16;
 constexpr int IS_STEPS_REINDEX = 4;
+constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is multiplied
 
 template <bool REINDEX>
 __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
@@ -71,62 +73,76 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     const int64_t row = base + pos;
     return (row >= 0 && row < n_entries) ? row : -1;
   };
-  auto load = [&](int64_t row, u32x4 (&raw)[4]) {
-    if (row >= 0) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + row * 128 + 64 * half);
+  // Rows are loaded unconditionally (an absent slot loads the query's first row, which
+  // exists, and is masked afterwards) into buffers that rotate over the unrolled steps, so
+  // no load waits on another. A query with no visible row in the cache loads nothing.
+  // Reindex rows come through the pool and are resolved before streaming.
+  constexpr int NB = IS_PREFETCH + 1;
+  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  int64_t rows[REINDEX ? IS_STEPS_PER_WAVE : 1];
+  int64_t slots_unused;
+  if (REINDEX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = p[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int st = 0; st < IS_STEPS_PER_WAVE; ++st) rows[st] = row_of(st, slots_unused);
+  }
+  auto row_at = [&](int step) -> int64_t {
+    int64_t sl;
+    return REINDEX ? rows[REINDEX ? step : 0] : row_of(step, sl);
   };
-
-  int64_t slot_cur;
-  int64_t row_cur = row_of(0, slot_cur);
-  u32x4 raw[4];
-  load(row_cur, raw);
-
-#pragma unroll 1
+  auto slot_at = [&](int step) -> int64_t { return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n; };
+  u32x4 buf[NB][4];
+  float sc[IS_STEPS_PER_WAVE];
+  auto load_step = [&](int step, u32x4 (&raw)[4]) {
+    const int64_t r = row_at(step);
+    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : base) * 128 + 64 * half);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+  };
+  if (any) {
+#pragma unroll
+    for (int st = 0; st < IS_PREFETCH && st < IS_STEPS_PER_WAVE; ++st) load_step(st, buf[st % NB]);
+  }
+#pragma unroll
   for (int step = 0; step < IS_STEPS_PER_WAVE; ++step) {
-    // Prefetch the next step's rows while this one is multiplied.
-    int64_t slot_nxt = 0, row_nxt = -1;
-    u32x4 raw_nxt[4];
-    if (step + 1 < IS_STEPS_PER_WAVE) {
-      row_nxt = row_of(step + 1, slot_nxt);
-      load(row_nxt, raw_nxt);
-    }
-    f32x16 acc = {};
+    float sv = -__builtin_inff();
+    if (any) {
+      if (step + IS_PREFETCH < IS_STEPS_PER_WAVE)
+        load_step(step + IS_PREFETCH, buf[(step + IS_PREFETCH) % NB]);
+      u32x4 (&raw)[4] = buf[step % NB];
+      f32x16 acc = {};
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const uint32_t d0 = raw[kb >> 1][(kb & 1) * 2];
-      const uint32_t d1 = raw[kb >> 1][(kb & 1) * 2 + 1];
-      const u32x2 lo = e4m3x4_to_bf16x4(d0);
-      const u32x2 hi = e4m3x4_to_bf16x4(d1);
-      const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
-                                                    0, 0, 0);
-    }
-    float part = 0.f;
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint32_t d0 = raw[kb >> 1][(kb & 1) * 2];
+        const uint32_t d1 = raw[kb >> 1][(kb & 1) * 2 + 1];
+        const u32x2 lo = e4m3x4_to_bf16x4(d0);
+        const u32x2 hi = e4m3x4_to_bf16x4(d1);
+        const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
+                                                      0, 0, 0);
+      }
+      float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
-    part += __shfl_xor(part, 32);
-    const float s = row_cur >= 0 ? part : -__builtin_inff();
-    if (slot_cur < ld) {
-      if (half == 0) scores[(int64_t)t * ld + slot_cur] = s;
+      for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+      part += __shfl_xor(part, 32);
+      if (row_at(step) >= 0) sv = part;
     }
+    sc[step] = sv;
+  }
+  // Scores and block maxima go out once the tile has been streamed: small stores
+  // interleaved with the row reads cost read bandwidth.
+#pragma unroll
+  for (int step = 0; step < IS_STEPS_PER_WAVE; ++step) {
+    const int64_t slot = slot_at(step);
+    const float sv = sc[step];
+    if (slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
     if (block_max != nullptr) {
-      float m = s;
+      float m = sv;
       m = fmaxf(m, __shfl_xor(m, 1));
       m = fmaxf(m, __shfl_xor(m, 2));
       m = fmaxf(m, __shfl_xor(m, 4));
-      if (half == 0 && (n & 7) == 0 && slot_cur < ld)
-        block_max[(int64_t)t * ld_bm + (slot_cur >> 3)] = m;
+      if (half == 0 && (n & 7) == 0 && slot < ld)
+        block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
     }
-    slot_cur = slot_nxt;
-    row_cur = row_nxt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = raw_nxt[i];
   }
 }
 
