@@ -309,7 +309,9 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   // AT_GAP raises the reference and marks the pass for a repeat.
   auto step = [&](int c, Raw& raw, int32_t pn) {
     const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
-    const f32x4 sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
+    // A slice with no item (past the split) converts nothing; only its next gather starts.
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if (valid != 0ull) sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
     fetch(c + AT_WAVES, pn, raw);
     if (valid == 0ull) return;
     // LDS operations of one wavefront complete in order; the fences keep the compiler from
