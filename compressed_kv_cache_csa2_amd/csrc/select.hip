@@ -88,37 +88,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, SelShared& 
   return before + x - v;
 }
 
-// Rank offsets in index order for a per-thread R-bit mask whose bit 4g + j stands for
-// element 4*(tid + SEL_THREADS*g) + j: index order runs over g, then tid, then j, so the
-// per-group counts are laid out in LDS in that order, each thread sums NG consecutive
-// ones, and one block scan gives every (g, tid) its offset. start[g] receives the rank of
-// this thread's first element of group g.
-template <int NG>
-__device__ __forceinline__ void group_offsets(uint32_t mask, SelShared& sh, uint32_t (&start)[NG],
-                                              uint32_t* total) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int g = 0; g < NG; ++g) sh.gpos[g * SEL_THREADS + tid] = __popc((mask >> (4 * g)) & 0xFu);
-  __syncthreads();
-  uint32_t e[NG];
-  uint32_t local = 0;
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    e[i] = sh.gpos[NG * tid + i];
-    local += e[i];
-  }
-  uint32_t excl = block_exclusive_scan(local, sh, total);
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    sh.gpos[NG * tid + i] = excl;
-    excl += e[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < NG; ++g) start[g] = sh.gpos[g * SEL_THREADS + tid];
-  __syncthreads();
-}
-
 // The keys of one row. keys[4g + j] is element seg*SEG + 4*(tid + SEL_THREADS*g) + j.
 // A row of one segment is loaded once; a longer one (MULTI) is reloaded segment by
 // segment in every pass.
