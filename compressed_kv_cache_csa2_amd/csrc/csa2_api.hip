@@ -48,14 +48,13 @@ const char* csa2_version(void) { return "csa2-gfx950 0.1.0"; }
 const char* csa2_last_error(void) { return g_err; }
 
 size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k) {
+  // No call of this build needs scratch memory: the selections keep their state in LDS
+  // and the attention's workgroups write disjoint output channels.
+  (void)op;
+  (void)n_q;
   (void)max_cols;
-  switch (op) {
-    case CSA2_OP_SPARSE_ATTN:
-      if (n_q <= 0 || k < 0 || k > CSA2_MAX_K) return 0;
-      return csa2::attn_workspace_bytes(n_q, k);
-    default:
-      return 0;
-  }
+  (void)k;
+  return 0;
 }
 
 int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
@@ -206,16 +205,14 @@ int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const vo
               aligned(out, 16) && aligned(kv_start, 8) && aligned(swa_start, 8) && aligned(n_swa, 4) &&
               aligned(topk_idx, 4) && aligned(lse, 4),
           CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: misaligned argument");
-  const size_t need = csa2::attn_workspace_bytes(n_q, k);
-  REQUIRE(need == 0 || (workspace != nullptr && ws_bytes >= need && aligned(workspace, 16)),
-          CSA2_ERR_WORKSPACE, "csa2_sparse_attn: workspace of %zu bytes needed, %zu given", need,
-          workspace ? ws_bytes : (size_t)0);
+  (void)workspace;   // no scratch memory is needed (csa2_workspace_bytes returns 0)
+  (void)ws_bytes;
   return hip_status(csa2::launch_sparse_attn(
                         n_q, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv_fp4),
                         kv_fp4_stride, static_cast<const uint8_t*>(kv_scale), kv_scale_stride,
                         n_entries, kv_start, topk_idx, ld_idx, k,
                         static_cast<const uint8_t*>(window_kv), n_window_rows, swa_start, n_swa,
-                        softmax_scale, static_cast<uint16_t*>(out), lse, workspace,
+                        softmax_scale, static_cast<uint16_t*>(out), lse,
                         static_cast<hipStream_t>(stream)),
                     "csa2_sparse_attn");
 }

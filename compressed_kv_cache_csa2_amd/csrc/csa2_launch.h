@@ -24,17 +24,12 @@ hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t 
                        int pool_use, const int32_t* pool_blocks, int n_pool, int32_t* topk_idx,
                        int64_t ld_idx, hipStream_t stream);
 
-// Number of entry splits the attention kernel uses for n_q queries and k selected entries
-// (a pure function of its arguments, so workspace sizing and launch agree).
-int attn_splits(int n_q, int k);
-size_t attn_workspace_bytes(int n_q, int k);
-
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,
                               int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,
                               int64_t ld_idx, int k, const uint8_t* window_kv,
                               int64_t n_window_rows, const int64_t* swa_start,
                               const int32_t* n_swa, float softmax_scale, uint16_t* out,
-                              float* lse, void* workspace, hipStream_t stream);
+                              float* lse, hipStream_t stream);
 
 }  // namespace csa2

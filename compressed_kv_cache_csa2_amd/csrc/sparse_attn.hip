@@ -9,17 +9,20 @@
 // dim 512, FP4 E2M1 main KV with an E4M3 scale per 16 channels, FP8 window).
 //
 // Work split: a query's selected entries and its window rows are cut into 16-item slices
-// (separately, so a slice never mixes the two formats); a workgroup owns one group of 16
-// heads and one contiguous range of slices (a "split"), and its eight wavefronts (two per
-// SIMD, so one's memory waits hide behind the other's arithmetic) take every eighth slice
-// of that range and run independently (no barrier in the main loop). Per slice a
+// (separately, so a slice never mixes the two formats). A workgroup owns one group of 16
+// heads and one half (256 channels) of the output; its eight wavefronts (two per SIMD, so
+// one's memory waits hide behind the other's arithmetic) take every eighth slice of the
+// query and run independently (no barrier in the main loop). Both halves of a head group
+// compute the same full-width logits and softmax, so each writes its own channels with no
+// merge across workgroups, and each wavefront's accumulator is half as large as a
+// full-width one, which leaves the registers for a second gather buffer. Per slice a
 // wavefront:
-//   - gathers the 16 rows (lane = item x quarter of the 512 channels) one slice ahead of
-//     their use (the other wavefront on the SIMD covers the rest of the latency), with the
-//     selected positions loaded two slices before that. The gathers
-//     are indexed buffer loads: an absent item gets an index past the buffer's record
-//     count and reads zeros, so every slice issues the same loads into the same registers
-//     and the wait for a slice never includes the loads of the slices behind it;
+//   - gathers the 16 rows (lane = item x quarter of the 512 channels) two slices ahead of
+//     their use, alternating between two register buffers, with the selected positions
+//     loaded two slices before the gather. The gathers are indexed buffer loads: an
+//     absent item gets an index past the buffer's record count and reads zeros, so every
+//     slice issues the same loads into the same registers and the wait for a slice never
+//     includes the loads of the slices behind it;
 //   - converts them to fp16 with the hardware E2M1/E4M3 -> fp16 conversions and a packed
 //     fp16 multiply by the group scale; every value is exact (an E2M1 x E4M3 product has
 //     <= 6 significant bits in [2^-10, 2688]). The converted registers are directly the A
@@ -32,14 +35,11 @@
 //     of the first slice with a valid item, and later weights p = 2^(l - ref) may reach
 //     2^15 (fp16 holds them); a logit beyond that restarts the wavefront's slices with the
 //     raised reference (rare; the result does not depend on the reference);
-//   - O^T (512 x 16 heads) += C^T . P^T with v_mfma_f32_16x16x16_f16: P^T is the logits'
-//     accumulator layout, A = C^T is read from the tile with LDS transpose reads
-//     (ds_read_b64_tr_b16).
-// The eight wavefront partials are merged through LDS. With more than one split per head
-// group, each workgroup stores its (max, sum, O) partial in the workspace and a second
-// kernel combines them in split order (no cross-workgroup synchronisation inside a
-// kernel). Workgroup ids put all workgroups of a query on one XCD, so they share its L2
-// copy of the rows.
+//   - O^T (this half's 256 channels x 16 heads) += C^T . P^T with v_mfma_f32_16x16x16_f16:
+//     P^T is the logits' accumulator layout, A = C^T is read from the tile with LDS
+//     transpose reads (ds_read_b64_tr_b16).
+// The eight wavefront partials are merged through LDS. Workgroup ids put all workgroups
+// of a query on one XCD, so they share its L2 copy of the rows.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -50,37 +50,14 @@ constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_SLICE = 16;                 // items per wavefront step
 constexpr int AT_HEADS = 16;                 // heads per workgroup
 constexpr int AT_GROUPS = 64 / AT_HEADS;     // head groups per query
-constexpr int MERGE_THREADS = AT_HEADS * 16;   // split merge: 16 threads per head
+constexpr int AT_HALVES = 2;                // output channel halves per (query, head group)
+constexpr int AT_DT = 512 / 16 / AT_HALVES;  // 16-channel output tiles per half
 constexpr int AT_WINDOW = 128;               // largest sliding window
 constexpr int AT_WIN_SLICES = AT_WINDOW / AT_SLICE;
-constexpr int AT_MAX_SPLITS = 8;
-constexpr int AT_TARGET_WGS = 256;           // one workgroup per compute unit
 constexpr int N_XCD = 8;
 constexpr float AT_GAP = 15.f;               // largest log2 weight over the reference
 constexpr float AT_LOG2E = 1.4426950408889634f;
 constexpr float AT_LN2 = 0.6931471805599453f;
-
-int attn_splits(int n_q, int k) {
-  const int n_sl = (k + AT_SLICE - 1) / AT_SLICE + AT_WIN_SLICES;
-  int s = 1;
-  // Double the splits while the grid is below one workgroup per CU and every wavefront
-  // would still get a slice.
-  while (s < AT_MAX_SPLITS && (int64_t)n_q * AT_GROUPS * s < AT_TARGET_WGS &&
-         n_sl >= AT_WAVES * 2 * s)
-    s *= 2;
-  return s;
-}
-
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Workspace (only with more than one split): [max/sum: float (S x 2 x 16) per (query,
-// head group)] [O: float (S x 16 x 512) per group].
-size_t attn_workspace_bytes(int n_q, int k) {
-  const int s = attn_splits(n_q, k);
-  if (s == 1 || n_q <= 0) return 0;
-  const size_t groups = (size_t)n_q * AT_GROUPS;
-  return align256(groups * s * 2 * AT_HEADS * 4) + groups * s * AT_HEADS * 512 * 4;
-}
 
 // A wavefront's tile holds 16 rows C[e][0..512) in fp16. Row e starts at element
 // TILE_ROW * e and its channel quarter g (128 channels) at + TILE_QUARTER * g: rows are
@@ -149,19 +126,18 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     const int64_t* __restrict__ kv_start, const int32_t* __restrict__ topk_idx, int64_t ld_idx,
     int k, const uint8_t* __restrict__ window_kv, int64_t n_win_rows,
     const int64_t* __restrict__ swa_start, const int32_t* __restrict__ n_swa, float scale,
-    int n_q, int n_split, float* __restrict__ ws_ml, float* __restrict__ ws_o,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int n_q, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ AttnShared sh;
 
-  // id = (g * J + j) * 8 + t % 8 for queries 8g .. 8g+7 and J = 4 * n_split workgroups per
-  // query: every workgroup of query t has id % 8 = t % 8.
-  const int J = AT_GROUPS * n_split;
+  // id = (g * J + j) * 8 + t % 8 for queries 8g .. 8g+7 and J = 4 head groups x 2 channel
+  // halves workgroups per query: every workgroup of query t has id % 8 = t % 8.
+  constexpr int J = AT_GROUPS * AT_HALVES;
   const int id = blockIdx.x;
   const int t = (id / (N_XCD * J)) * N_XCD + id % N_XCD;
   if (t >= n_q) return;
   const int jj = (id / N_XCD) % J;
   const int hg = jj % AT_GROUPS;
-  const int sp = jj / AT_GROUPS;
+  const int dh = jj / AT_GROUPS;   // output channels 256*dh .. 256*dh + 255
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,16 +147,14 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const int h = hg * AT_HEADS + col;
 
   // Slices: the selected entries first (slice c < n_msl holds entries 16c .. 16c+15), then
-  // the window rows. Split ranges are sized for the largest window, so they (and the
-  // position loads below) do not wait for n_swa.
+  // the window rows, sized for the largest window so that the slice range (and the
+  // position loads below) does not wait for n_swa.
   const int n_msl = (k + AT_SLICE - 1) / AT_SLICE;
-  const int n_sl = n_msl + AT_WIN_SLICES;
-  const int lo = (int)((int64_t)sp * n_sl / n_split);
-  const int hi = (int)((int64_t)(sp + 1) * n_sl / n_split);
-  const int c0 = lo + wave;
+  const int hi = n_msl + AT_WIN_SLICES;
+  const int c0 = wave;
 
   // Selected positions, through a buffer over this query's k entries: a slot past k (or
-  // a slice past the split) reads 0 without touching memory and is marked absent.
+  // a slice past the last) reads 0 without touching memory and is marked absent.
   const __amdgpu_buffer_rsrc_t rs_idx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(topk_idx) + (int64_t)t * ld_idx, (short)0, k * 4, 0x00020000);
   // The value is used only when the gather is issued, which re-derives whether the slot
@@ -192,7 +166,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
                                            rs_idx, in ? item * 4 : k * 4, 0, 0));
   };
   const int32_t p0 = position(c0);
-  int32_t pX = position(c0 + AT_WAVES);
+  const int32_t p1 = position(c0 + AT_WAVES);
 
   // This wavefront's two k-steps of the logit B operand: Q^T for head h, channels
   // 8*ks + 128*gq .. +7 with ks = 2*wave, 2*wave + 1 (the conversion produces the rows
@@ -285,34 +259,39 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     sh.qop[2 * wave][lane] = __builtin_bit_cast(u32x4, b0);
     sh.qop[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, b1);
   }
-  Raw buf;
-  fetch(c0, p0, buf);
-  // Issued after the gather, like the position load that follows every gather in the
-  // loop, so the loop's waits for a gather can leave one position load in flight.
-  int32_t pY = position(c0 + 2 * AT_WAVES);
+  // Two gather buffers: a slice's rows are requested two steps before their use. Each
+  // gather is followed by the position load of the slice two steps after it, in the same
+  // order as in the loop, so the loop's waits match on every path.
+  Raw bufA, bufB;
+  fetch(c0, p0, bufA);
+  int32_t pX = position(c0 + 2 * AT_WAVES);
+  fetch(c0 + AT_WAVES, p1, bufB);
+  int32_t pY = position(c0 + 3 * AT_WAVES);
   __syncthreads();   // the query operand is complete
 
-  // Output accumulator: O^T[d = 16*dt + 4*gq + i][h], dt = 0..31.
-  f32x4 oacc[32];
+  // Output accumulator of this half: O^T[d = 256*dh + 16*dt + 4*gq + i][h], dt = 0..15.
+  f32x4 oacc[AT_DT];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < AT_DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();   // reference max of head col (log2 units)
   bool ok_pass = true;               // no logit of this pass overflowed the reference
   float l_run = 0.f;                 // this lane's share of the sum for head col
   uint16_t* const tile = sh.tile[wave];
   uint16_t* const tile_w = tile + TILE_ROW * col + TILE_QUARTER * gq;
-  const uint16_t* const tile_r = tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3);
+  // Transpose reads start at this half's first channel quarter (2*dh).
+  const uint16_t* const tile_r =
+      tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3) + TILE_QUARTER * (2 * dh);
 
-  // One slice (c may lie past the split: its items are all absent); pn is the position of
-  // the next slice in this wavefront's sequence (c + AT_WAVES), whose gather is started as
-  // soon as this slice's registers are free. A logit exceeding the reference by more than
+  // One slice (c may lie past the last: its items are all absent); pn is the position of
+  // the slice two steps later in this wavefront's sequence (c + 2*AT_WAVES), whose gather
+  // is started as soon as this slice's registers are free. A logit exceeding the reference by more than
   // AT_GAP raises the reference and marks the pass for a repeat.
   auto step = [&](int c, Raw& raw, int32_t pn) {
     const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
-    // A slice with no item (past the split) converts nothing; only its next gather starts.
+    // A slice with no item (past the last) converts nothing; only its next gather starts.
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     if (valid != 0ull) sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
-    fetch(c + AT_WAVES, pn, raw);
+    fetch(c + 2 * AT_WAVES, pn, raw);
     if (valid == 0ull) return;
     // LDS operations of one wavefront complete in order; the fences keep the compiler from
     // moving the tile reads above the writes.
@@ -350,36 +329,38 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     // of a 16-lane group addresses channels 16*dt + 4*(i%4) .. +3 of item 4*gq + i/4 and
     // receives channel 16*dt + i of items 4*gq .. 4*gq+3.
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
+    for (int dt = 0; dt < AT_DT; ++dt) {
       const u32x2 a = lds_read_tr16x4(tile_r + TILE_QUARTER * (dt >> 3) + 16 * (dt & 7));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), pv,
                                                        oacc[dt], 0, 0, 0);
     }
   };
 
-  // Every step runs unconditionally (a slice past the split is all absent and its loads
-  // return zeros without touching memory), so the buffer is written by the same loads on
-  // every path and a step waits only for its own slice. Positions are loaded two steps
-  // before their gather: pX and pY alternate so no register is copied.
+  // Every step runs unconditionally (a slice past the last is all absent and its loads
+  // return zeros without touching memory), so each buffer is written by the same loads on
+  // every path and a step waits only for its own slice. Steps alternate between the two
+  // buffers; positions are loaded two steps before their gather, pX and pY alternating so
+  // that no register is copied.
   bool again;
 #pragma unroll 1
   do {
     ok_pass = true;
 #pragma unroll 1
     for (int c = c0; c < hi; c += 2 * AT_WAVES) {
-      step(c, buf, pX);
-      pX = position(c + 3 * AT_WAVES);
-      step(c + AT_WAVES, buf, pY);
-      pY = position(c + 4 * AT_WAVES);
+      step(c, bufA, pX);
+      pX = position(c + 4 * AT_WAVES);
+      step(c + AT_WAVES, bufB, pY);
+      pY = position(c + 5 * AT_WAVES);
     }
     again = !ok_pass;
     if (again) {   // a logit overflowed the reference: repeat with the raised one
 #pragma unroll
-      for (int i = 0; i < 32; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < AT_DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       l_run = 0.f;
-      fetch(c0, position(c0), buf);
-      pX = position(c0 + AT_WAVES);
-      pY = position(c0 + 2 * AT_WAVES);
+      fetch(c0, position(c0), bufA);
+      pX = position(c0 + 2 * AT_WAVES);
+      fetch(c0 + AT_WAVES, position(c0 + AT_WAVES), bufB);
+      pY = position(c0 + 3 * AT_WAVES);
     }
   } while (again);
 
@@ -392,8 +373,8 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   }
   __syncthreads();   // also ends every wavefront's use of its tile
   // Thread tid reduces the entries (dt = tid/64 and 8 + tid/64, lane l = tid%64) of every
-  // wavefront's half-accumulator: O^T[16*dt + 4*(l/16) + i][head l%16], so its head is
-  // tid%16 for both.
+  // wavefront's accumulator: O^T[256*dh + 16*dt + 4*(l/16) + i][head l%16], so its head
+  // is tid%16 for both.
   const int oh = tid & 15;
   float fwh[AT_WAVES];
   float Mh = -__builtin_inff();
@@ -408,99 +389,34 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   }
   const int rl = tid & 63;
   const int rdt = tid >> 6;
-  f32x4 acc[2][2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int dt = 0; dt < AT_DT; ++dt) sh.part[wave][dt][lane] = __builtin_bit_cast(u32x4, oacc[dt]);
+  __syncthreads();
+  f32x4 acc[2];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) sh.part[wave][dt][lane] = __builtin_bit_cast(u32x4, oacc[16 * hf + dt]);
-    __syncthreads();
+  for (int j = 0; j < 2; ++j) {
+    f32x4 a = __builtin_bit_cast(f32x4, sh.part[0][rdt + 8 * j][rl]) * fwh[0];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x4 a = __builtin_bit_cast(f32x4, sh.part[0][rdt + 8 * j][rl]) * fwh[0];
-#pragma unroll
-      for (int w = 1; w < AT_WAVES; ++w)
-        a += __builtin_bit_cast(f32x4, sh.part[w][rdt + 8 * j][rl]) * fwh[w];
-      acc[hf][j] = a;
-    }
-    __syncthreads();
-  }
-  // Channel of acc[hf][j][i]: 256*hf + 16*(rdt + 8*j) + 4*(rl/16) + i.
-  auto chan = [&](int hf, int j) { return 256 * hf + 16 * (rdt + 8 * j) + 4 * (rl >> 4); };
-
-  if (n_split > 1) {
-    // Partial of this split: O relative to its own max, plus max and sum per head.
-    const int64_t g = (int64_t)t * AT_GROUPS + hg;
-    float* po = ws_o + (g * n_split + sp) * (AT_HEADS * 512) + oh * 512;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<f32x4*>(po + chan(hf, j)) = acc[hf][j];
-    if (tid < 16) {
-      ws_ml[(g * n_split + sp) * 32 + oh] = Mh;
-      ws_ml[(g * n_split + sp) * 32 + 16 + oh] = Lh;
-    }
-    return;
+    for (int w = 1; w < AT_WAVES; ++w)
+      a += __builtin_bit_cast(f32x4, sh.part[w][rdt + 8 * j][rl]) * fwh[w];
+    acc[j] = a;
   }
 
+  // Both halves compute the same logits, so their maxima and sums agree; each writes its
+  // own 256 channels, and the first the log-sum-exp.
   const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
   uint16_t* orow = out + ((int64_t)t * 64 + hg * AT_HEADS + oh) * 512;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x4 a = acc[hf][j];
-      const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
-      const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
-      *reinterpret_cast<u32x2*>(orow + chan(hf, j)) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-    }
-  if (lse != nullptr && tid < 16)
+  for (int j = 0; j < 2; ++j) {
+    const f32x4 a = acc[j];
+    const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
+    const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
+    const int ch = 256 * dh + 16 * (rdt + 8 * j) + 4 * (rl >> 4);
+    *reinterpret_cast<u32x2*>(orow + ch) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+  }
+  if (lse != nullptr && dh == 0 && tid < 16)
     lse[(int64_t)t * 64 + hg * AT_HEADS + oh] =
         Lh > 0.f ? (Mh + __log2f(Lh)) * AT_LN2 : -__builtin_inff();
-}
-
-// Combines the split partials of one (query, head group) in split order. Thread (head
-// tid/16, channels 32*(tid%16) .. +31); MERGE_THREADS threads.
-__global__ __launch_bounds__(MERGE_THREADS) void attn_merge_kernel(
-    int n_split, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int64_t g = blockIdx.x;   // query * 4 + head group
-  const int hh = threadIdx.x >> 4;
-  const int d0 = 32 * (threadIdx.x & 15);
-  float ms[AT_MAX_SPLITS], ls[AT_MAX_SPLITS];
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int s = 0; s < AT_MAX_SPLITS; ++s) {
-    if (s < n_split) {
-      ms[s] = ws_ml[(g * n_split + s) * 32 + hh];
-      ls[s] = ws_ml[(g * n_split + s) * 32 + 16 + hh];
-      M = fmaxf(M, ms[s]);
-    }
-  }
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-#pragma unroll
-  for (int s = 0; s < AT_MAX_SPLITS; ++s) {
-    if (s < n_split) {
-      const float wgt = ms[s] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
-      L += wgt * ls[s];
-      const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + (g * n_split + s) * (AT_HEADS * 512) +
-                                                        hh * 512 + d0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += src[i] * wgt;
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* orow = out + (g * AT_HEADS + hh) * 512 + d0;   // head = 16 * (g % 4) + hh of query g / 4
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t b0 = f32_to_bf16_rne(acc[i][0] * inv), b1 = f32_to_bf16_rne(acc[i][1] * inv);
-    const uint32_t b2 = f32_to_bf16_rne(acc[i][2] * inv), b3 = f32_to_bf16_rne(acc[i][3] * inv);
-    *reinterpret_cast<u32x2*>(orow + 4 * i) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-  }
-  if (lse != nullptr && (threadIdx.x & 15) == 0)
-    lse[g * AT_HEADS + hh] = L > 0.f ? (M + __log2f(L)) * AT_LN2 : -__builtin_inff();
 }
 
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
@@ -509,24 +425,12 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t ld_idx, int k, const uint8_t* window_kv,
                               int64_t n_window_rows, const int64_t* swa_start,
                               const int32_t* n_swa, float softmax_scale, uint16_t* out,
-                              float* lse, void* workspace, hipStream_t stream) {
-  const int splits = attn_splits(n_q, k);
-  float* ws_ml = nullptr;
-  float* ws_o = nullptr;
-  if (splits > 1) {
-    const size_t groups = (size_t)n_q * AT_GROUPS;
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    ws_ml = reinterpret_cast<float*>(w);
-    ws_o = reinterpret_cast<float*>(w + align256(groups * splits * 2 * AT_HEADS * 4));
-  }
+                              float* lse, hipStream_t stream) {
   const int groups8 = (n_q + N_XCD - 1) / N_XCD;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3(groups8 * N_XCD * AT_GROUPS * splits),
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3(groups8 * N_XCD * AT_GROUPS * AT_HALVES),
                      dim3(AT_THREADS), 0, stream, q, kv_fp4, fp4_stride, kv_scale, scale_stride,
                      n_entries, kv_start, topk_idx, ld_idx, k, window_kv, n_window_rows,
-                     swa_start, n_swa, softmax_scale, n_q, splits, ws_ml, ws_o, out, lse);
-  if (splits > 1)
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(n_q * AT_GROUPS), dim3(MERGE_THREADS), 0, stream,
-                       splits, ws_ml, ws_o, out, lse);
+                     swa_start, n_swa, softmax_scale, n_q, out, lse);
   return hipGetLastError();
 }
 

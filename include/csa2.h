@@ -23,9 +23,9 @@
  * Conventions shared by every call
  *   - Every call is stateless and re-entrant and returns an int status (CSA2_OK = 0).
  *   - Tensor arguments are caller-owned DEVICE pointers. The library never allocates,
- *     frees or keeps them past the enqueued work. Scratch memory is a caller-owned
- *     device workspace of at least csa2_workspace_bytes(...) bytes (NULL/0 allowed
- *     when that function returns 0).
+ *     frees or keeps them past the enqueued work. Calls that take a workspace accept a
+ *     caller-owned device workspace of csa2_workspace_bytes(...) bytes; in this build
+ *     that is 0 for every op, so NULL/0 may be passed.
  *   - Layouts are dense row-major with the leading dimensions given. bf16 values are
  *     passed as their 16-bit patterns; FP8 E4M3 and FP4 E2M1 as bytes.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only
@@ -78,7 +78,8 @@ enum {
 
 /* Workspace sizing. `op` is one of the CSA2_OP_* values; `n_q` queries, `max_cols` the
  * largest row length (scores columns or block count) and `k` the selection size the
- * call will be made with. Returns 0 when the op needs no workspace. */
+ * call will be made with. Returns 0 when the op needs no workspace, which in this build
+ * is every op. */
 enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BLOCK_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
 size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);
 
@@ -192,12 +193,10 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
  *   window_kv [n_window_rows,512] E4M3; swa_start [n_q] int64; n_swa [n_q] int32 (values
  *   above 128 are clamped to 128);
  *   out [n_q,64,512] bf16; lse [n_q,64] f32 or NULL.
- * Workspace: csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, n_q, 0, k) bytes, 16-byte
- * aligned (none when that is 0). When there are too few queries to fill the GPU, the
- * attended set of each query is split over several workgroups; their partial softmax
- * states go to the workspace and a second kernel on the same stream combines them in a
- * fixed order, so results do not depend on timing. The workspace needs no initial
- * contents; calls that share one must not run concurrently.
+ * Workspace: none (csa2_workspace_bytes returns 0; the arguments are ignored). Each
+ * (query, 16-head group) is computed by two workgroups, one per 256-channel half of the
+ * output, which repeat the same logits and softmax, so nothing is combined across
+ * workgroups and results do not depend on timing.
  * Limits: kv_fp4_stride and kv_scale_stride at most 16,368 bytes. */
 int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q,
                      const void* kv_fp4, int64_t kv_fp4_stride,
