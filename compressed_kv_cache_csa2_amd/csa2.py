@@ -34,9 +34,11 @@ def _load():
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
     lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
+    lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
-    for f in ("csa2_index_score", "csa2_block_pool", "csa2_topk", "csa2_sparse_attn"):
+    for f in ("csa2_index_score", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
+              "csa2_sparse_attn"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -118,6 +120,19 @@ def csa2_topk(scores, topk_idx, k=512, n_cols=None, n_valid=None, block_max=None
         _ptr(pool_blocks, torch.int32, "pool_blocks"),
         pool_blocks.shape[1] if pool_blocks is not None else 0, 8,
         _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], None, 0, _stream(stream)))
+
+
+def csa2_pool_topk(block_max, n_visible, pool_blocks, scores, topk_idx, n_keep=2048, k=512,
+                   n_cols=None, stream=None):
+    """csa2_block_pool then csa2_topk among the pool's candidates, in one kernel: pool ids
+    into `pool_blocks` [n_q, >= n_keep] and positions into `topk_idx` [n_q, >= k]."""
+    n_cols = scores.shape[1] if n_cols is None else n_cols
+    _check(lib.csa2_pool_topk(
+        block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
+        _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), pool_blocks.shape[1],
+        _ptr(scores, torch.float32, "scores"), scores.shape[1], n_cols, k,
+        _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], _stream(stream)))
 
 
 def csa2_sparse_attn(q, kv_fp4, kv_scale, kv_start, topk_idx, window_kv, swa_start, n_swa,

@@ -173,6 +173,39 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
                     "csa2_topk");
 }
 
+int csa2_pool_topk(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
+                   int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
+                   const float* scores, int64_t ld_scores, int64_t n_cols, int k,
+                   int32_t* topk_idx, int64_t ld_idx, void* stream) {
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "csa2_pool_topk: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_pool_topk: n_q %d out of range", n_q);
+  REQUIRE(n_keep >= 1 && n_keep <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: n_keep %d out of range [1, %d]", n_keep, CSA2_MAX_K);
+  REQUIRE(k >= 1 && k <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG, "csa2_pool_topk: k %d out of range [1, %d]",
+          k, CSA2_MAX_K);
+  if (n_q == 0) return ok();
+  REQUIRE(block_max && n_visible && pool_blocks && scores && topk_idx, CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: null pointer argument");
+  REQUIRE(ld_bm >= 1 && ld_pool >= n_keep, CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: bad leading dimension (ld_bm %lld, ld_pool %lld)", (long long)ld_bm,
+          (long long)ld_pool);
+  REQUIRE(aligned(block_max, 16) && ld_bm % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: block_max must be 16-byte aligned with ld_bm a multiple of 4");
+  REQUIRE(n_cols >= 0 && n_cols <= ld_scores && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: need 0 <= n_cols <= ld_scores <= 2^31 (n_cols %lld, ld %lld)",
+          (long long)n_cols, (long long)ld_scores);
+  REQUIRE(ld_idx >= k, CSA2_ERR_INVALID_ARG, "csa2_pool_topk: ld_idx %lld < k", (long long)ld_idx);
+  REQUIRE(aligned(scores, 16) && ld_scores % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_pool_topk: scores must be 16-byte aligned with ld_scores a multiple of 4");
+  REQUIRE(aligned(n_visible, 4) && aligned(pool_blocks, 4) && aligned(topk_idx, 4),
+          CSA2_ERR_INVALID_ARG, "csa2_pool_topk: misaligned argument");
+  return hip_status(csa2::launch_pool_topk(n_q, block_max, ld_bm, n_visible, n_keep, pool_blocks,
+                                           ld_pool, scores, ld_scores, n_cols, k, topk_idx,
+                                           ld_idx, static_cast<hipStream_t>(stream)),
+                    "csa2_pool_topk");
+}
+
 int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const void* kv_fp4,
                      int64_t kv_fp4_stride, const void* kv_scale, int64_t kv_scale_stride,
                      int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,

@@ -24,6 +24,13 @@ hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t 
                        int pool_use, const int32_t* pool_blocks, int n_pool, int32_t* topk_idx,
                        int64_t ld_idx, hipStream_t stream);
 
+// block_pool then topk with the pool's blocks as candidates, in one kernel.
+hipError_t launch_pool_topk(int n_q, const float* block_max, int64_t ld_bm,
+                            const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                            int64_t ld_pool, const float* scores, int64_t ld_scores,
+                            int64_t n_cols, int k, int32_t* topk_idx, int64_t ld_idx,
+                            hipStream_t stream);
+
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,
                               int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,

@@ -632,6 +632,51 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
   write_out(sh, kept, n_keep, pool + (int64_t)t * ld_pool);
 }
 
+// The HSI pool and the Top-K among its candidates in one workgroup per query: the pool is
+// written out and kept in LDS, and the candidate selection reads its block list from there
+// (the same results as block_pool_kernel followed by topk_kernel with pool_use 2).
+__global__ __launch_bounds__(SEL_THREADS) void pool_topk_kernel(
+    const float* __restrict__ block_max, int64_t ld_bm, const int32_t* __restrict__ n_visible,
+    int n_keep, int32_t* __restrict__ pool, int64_t ld_pool, const float* __restrict__ scores,
+    int64_t ld, int64_t n_cols, int k, int32_t* __restrict__ out, int64_t ld_idx) {
+  __shared__ SelShared sh;
+  const int t = blockIdx.x;
+  const int64_t nv = n_visible[t];
+  int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
+  if (nb > ld_bm) nb = ld_bm;
+  const BlockSrc bsrc{block_max + (int64_t)t * ld_bm, nb - 1, __builtin_inff()};
+  const uint32_t kept_pool = select_any(bsrc, nb, (uint32_t)n_keep, sh, [&](uint32_t rank, uint32_t b) {
+    if (rank < (uint32_t)n_keep) sh.obuf[rank] = (int32_t)b;
+  });
+  __syncthreads();
+  int32_t* prow = pool + (int64_t)t * ld_pool;
+  for (int r = threadIdx.x; r < n_keep; r += SEL_THREADS) {
+    const int32_t b = (uint32_t)r < kept_pool ? sh.obuf[r] : -1;
+    prow[r] = b;
+    sh.cblocks[r] = b;
+  }
+  __syncthreads();
+  const int64_t n = nv < 0 ? 0 : (nv < n_cols ? nv : n_cols);
+  const uint32_t kk = (uint32_t)k;
+  const CandSrc csrc{scores + (int64_t)t * ld, sh.cblocks, n};
+  const uint32_t kept = select_any(csrc, (int64_t)n_keep * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
+    if (rank < kk) sh.obuf[rank] = (int32_t)((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
+  });
+  __syncthreads();
+  write_out(sh, kept, k, out + (int64_t)t * ld_idx);
+}
+
+hipError_t launch_pool_topk(int n_q, const float* block_max, int64_t ld_bm,
+                            const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                            int64_t ld_pool, const float* scores, int64_t ld_scores,
+                            int64_t n_cols, int k, int32_t* topk_idx, int64_t ld_idx,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(pool_topk_kernel, dim3(n_q), dim3(SEL_THREADS), 0, stream, block_max, ld_bm,
+                     n_visible, n_keep, pool_blocks, ld_pool, scores, ld_scores, n_cols, k,
+                     topk_idx, ld_idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
                        const int32_t* n_valid, const float* block_max, int64_t ld_bm, int k,
                        int pool_use, const int32_t* pool_blocks, int n_pool, int32_t* topk_idx,

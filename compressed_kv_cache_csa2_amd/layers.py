@@ -56,10 +56,10 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
             C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
                                buf.scores, buf.block_max, stream=stream)
             if wl.with_pool:
-                # The pool holds every Full-layer winner, so the Top-K examines only its slots.
-                C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, POOL_BLOCKS, stream=stream)
-                C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
-                            pool_blocks=buf.pool, pool_use=C.POOL_CANDIDATES, stream=stream)
+                # The pool holds every Full-layer winner, so the Top-K examines only its slots;
+                # one kernel selects both.
+                C.csa2_pool_topk(buf.block_max, wl.n_visible, buf.pool, buf.scores, buf.idx[li],
+                                 n_keep=POOL_BLOCKS, k=k, stream=stream)
             else:
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
                             block_max=buf.block_max, stream=stream)

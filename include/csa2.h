@@ -169,6 +169,19 @@ int csa2_topk(int n_q, const float* scores, int64_t ld_scores, int64_t n_cols,
               int block_size, int32_t* topk_idx, int64_t ld_idx,
               void* workspace, size_t ws_bytes, void* stream);
 
+/* The Full layer's pool and its Top-K in one call ([V41F-BLOG] 2.3.4; [V41F-ARCH] 3):
+ * the same results as csa2_block_pool(n_q, block_max, ld_bm, n_visible, block_size,
+ * n_keep, pool_blocks, ld_pool, ...) followed by csa2_topk(n_q, scores, ld_scores, n_cols,
+ * n_visible, NULL, 0, k, CSA2_POOL_CANDIDATES, pool_blocks, n_keep, block_size, topk_idx,
+ * ld_idx, ...), in one kernel that keeps the pool in on-chip memory between the two
+ * selections. Both outputs are written. Arguments and limits are those of the two calls
+ * (block_max and scores as csa2_index_score FULL writes them). */
+int csa2_pool_topk(int n_q, const float* block_max, int64_t ld_bm,
+                   const int32_t* n_visible, int block_size, int n_keep,
+                   int32_t* pool_blocks, int64_t ld_pool,
+                   const float* scores, int64_t ld_scores, int64_t n_cols, int k,
+                   int32_t* topk_idx, int64_t ld_idx, void* stream);
+
 /* Joint sparse attention over the selected entries and the sliding window
  * ([V41F-BLOG] 2.2.2, 3.3.1 and 3.3.2 "the readout"; [V41F-ARCH] 2 and 4).
  * For query t let S be {valid positions in topk_idx[t, 0..k)} plus the SWA rows

@@ -20,7 +20,7 @@ def test_header_symbols_are_exported(C):
     text = open(HEADER).read()
     names = set(re.findall(r"^(?:int|size_t|const char\*)\s+(csa2_\w+)\(", text, re.M))
     assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_block_pool", "csa2_topk",
-                     "csa2_sparse_attn", "csa2_version", "csa2_last_error"}
+                     "csa2_pool_topk", "csa2_sparse_attn", "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -82,6 +82,27 @@ def test_topk_and_pool_rejections(C):
     assert L.csa2_block_pool(1, FAKE, 10, FAKE, 4, 2048, FAKE, 2048, None, 0, None) == 2
     assert L.csa2_block_pool(1, FAKE, 10, FAKE, 8, 2048, FAKE, 100, None, 0, None) == 1
     assert L.csa2_block_pool(0, None, 10, None, 8, 2048, None, 2048, None, 0, None) == 0
+
+
+def test_pool_topk_rejections(C):
+    L = C.lib
+    ok = dict(n_q=1, bm=FAKE, ld_bm=4096, nv=FAKE, bs=8, n_keep=2048, pool=FAKE, ld_pool=2048,
+              scores=FAKE, ld=32768, n_cols=32768, k=512, idx=FAKE, ld_idx=512, stream=None)
+
+    def pt(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.csa2_pool_topk(*a.values())
+    assert pt(bs=4) == 2
+    assert pt(n_keep=0) == 1 and pt(n_keep=4096) == 1
+    assert pt(k=0) == 1 and pt(k=4096) == 1
+    assert pt(ld_pool=100) == 1
+    assert pt(ld_bm=3) == 1
+    assert pt(n_cols=32769) == 1
+    assert pt(ld_idx=100) == 1
+    assert pt(scores=FAKE + 4) == 1
+    assert pt(idx=None) == 1
+    assert pt(n_q=0, bm=None) == 0
 
 
 def test_sparse_attn_rejections_and_workspace(C):

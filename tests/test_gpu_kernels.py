@@ -244,6 +244,43 @@ def test_topk_among_pool_candidates_is_exact(C, dev, kind, n):
         assert np.array_equal(np.sort(g[g >= 0]), np.sort(want))
 
 
+@pytest.mark.parametrize("kind,n", [("normal", 300000), ("ties", 70000), ("normal", 9000),
+                                    ("signed", 20001), ("zeros", 50000), ("normal", 7)])
+def test_pool_topk_fused_equals_two_calls(C, dev, kind, n):
+    """csa2_pool_topk writes the same pool and the same Top-K, bit for bit, as csa2_block_pool
+    followed by csa2_topk among the pool's candidates, and the Top-K is the oracle's."""
+    n_q, k = 3, 512
+    s = _score_rows(kind, n_q, n, seed=n + 11)
+    ld = (n + 3) // 4 * 4 + 4
+    sd = torch.full((n_q, ld), 7.0, dtype=torch.float32, device=dev)
+    sd[:, :n] = s.to(dev)
+    n_valid = torch.tensor([n, max(0, n - 5), max(1, n // 3)], dtype=torch.int32, device=dev)
+    nb = (ld + 7) // 8
+    ld_bm = (nb + 3) // 4 * 4
+    bm = torch.full((n_q, ld_bm), 1e30, dtype=torch.float32, device=dev)
+    for t in range(n_q):
+        nv = int(n_valid[t])
+        row = torch.full((((nv + 7) // 8) * 8,), -math.inf, device=dev)
+        row[:nv] = sd[t, :nv]
+        bm[t, :(nv + 7) // 8] = row.view(-1, 8).amax(dim=1)
+    pool_ref = torch.empty((n_q, 2048), dtype=torch.int32, device=dev)
+    idx_ref = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    C.csa2_block_pool(bm, n_valid, pool_ref)
+    C.csa2_topk(sd, idx_ref, k=k, n_cols=n, n_valid=n_valid, pool_blocks=pool_ref,
+                pool_use=C.POOL_CANDIDATES)
+    pool = torch.full((n_q, 2048), 12345, dtype=torch.int32, device=dev)
+    idx = torch.full((n_q, k), 12345, dtype=torch.int32, device=dev)
+    C.csa2_pool_topk(bm, n_valid, pool, sd, idx, k=k, n_cols=n)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool_ref)
+    assert torch.equal(idx, idx_ref)
+    for t in range(n_q):
+        nv = int(n_valid[t])
+        want = O.slots_to_positions(O.topk_slots(s[t, :nv].double().numpy(), k), None)
+        g = idx[t].cpu().numpy()
+        assert np.array_equal(np.sort(g[g >= 0]), np.sort(want)), f"row {t}"
+
+
 def test_topk_pool_mapping(C, dev):
     n_q, k = 2, 512
     s = _score_rows("normal", n_q, 16384, seed=9)
