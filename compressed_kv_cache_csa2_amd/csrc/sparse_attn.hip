@@ -10,16 +10,17 @@
 //
 // Work split: a query's selected entries and its window rows are cut into 16-item slices
 // (separately, so a slice never mixes the two formats). A workgroup owns one group of 16
-// heads and one half (256 channels) of the output; its eight wavefronts (two per SIMD, so
-// one's memory waits hide behind the other's arithmetic) take every eighth slice of the
-// query and run independently (no barrier in the main loop). Both halves of a head group
-// compute the same full-width logits and softmax, so each writes its own channels with no
-// merge across workgroups, and each wavefront's accumulator is half as large as a
-// full-width one, which leaves the registers for a second gather buffer. Per slice a
-// wavefront:
+// heads and, with at most 32 queries (too few to fill the GPU otherwise), one half (256
+// channels) of the output, else all of it; its eight wavefronts (two per SIMD, so one's
+// memory waits hide behind the other's arithmetic) take every eighth slice of the query
+// and run independently (no barrier in the main loop). Both halves of a head group compute
+// the same full-width logits and softmax, so each writes its own channels with no merge
+// across workgroups, and each wavefront's accumulator is half as large as a full-width
+// one, which leaves the registers for a second gather buffer. Per slice a wavefront:
 //   - gathers the 16 rows (lane = item x quarter of the 512 channels) two slices ahead of
-//     their use, alternating between two register buffers, with the selected positions
-//     loaded two slices before the gather. The gathers are indexed buffer loads: an
+//     their use, alternating between two register buffers (one slice ahead, in one
+//     buffer, at full width), with the selected positions loaded two slices before the
+//     gather. The gathers are indexed buffer loads: an
 //     absent item gets an index past the buffer's record count and reads zeros, so every
 //     slice issues the same loads into the same registers and the wait for a slice never
 //     includes the loads of the slices behind it;
@@ -35,7 +36,7 @@
 //     of the first slice with a valid item, and later weights p = 2^(l - ref) may reach
 //     2^15 (fp16 holds them); a logit beyond that restarts the wavefront's slices with the
 //     raised reference (rare; the result does not depend on the reference);
-//   - O^T (this half's 256 channels x 16 heads) += C^T . P^T with v_mfma_f32_16x16x16_f16:
+//   - O^T (the workgroup's channels x 16 heads) += C^T . P^T with v_mfma_f32_16x16x16_f16:
 //     P^T is the logits' accumulator layout, A = C^T is read from the tile with LDS
 //     transpose reads (ds_read_b64_tr_b16).
 // The eight wavefront partials are merged through LDS. Workgroup ids put all workgroups
@@ -50,8 +51,9 @@ constexpr int AT_THREADS = 64 * AT_WAVES;
 constexpr int AT_SLICE = 16;                 // items per wavefront step
 constexpr int AT_HEADS = 16;                 // heads per workgroup
 constexpr int AT_GROUPS = 64 / AT_HEADS;     // head groups per query
-constexpr int AT_HALVES = 2;                // output channel halves per (query, head group)
-constexpr int AT_DT = 512 / 16 / AT_HALVES;  // 16-channel output tiles per half
+// Up to this many queries, a (query, head group) is served by two workgroups, one per
+// output channel half (the grid would otherwise leave CUs idle); above it by one.
+constexpr int AT_HALVES_MAX_Q = 32;
 constexpr int AT_WINDOW = 128;               // largest sliding window
 constexpr int AT_WIN_SLICES = AT_WINDOW / AT_SLICE;
 constexpr int N_XCD = 8;
@@ -120,6 +122,9 @@ __device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const u32x4 (*q
   return sacc;
 }
 
+// HALVES = 2: the workgroup owns half of the output channels and keeps two gather buffers
+// (its accumulator is half as large); HALVES = 1: all channels, one gather buffer.
+template <int HALVES>
 __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4, int64_t fp4_stride,
     const uint8_t* __restrict__ kv_scale, int64_t sc_stride, int64_t n_entries,
@@ -131,13 +136,15 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 
   // id = (g * J + j) * 8 + t % 8 for queries 8g .. 8g+7 and J = 4 head groups x 2 channel
   // halves workgroups per query: every workgroup of query t has id % 8 = t % 8.
-  constexpr int J = AT_GROUPS * AT_HALVES;
+  constexpr int DT = 32 / HALVES;     // 16-channel output tiles of this workgroup
+  constexpr int NBUF = HALVES;        // gather buffers = slices of lead for a gather
+  constexpr int J = AT_GROUPS * HALVES;
   const int id = blockIdx.x;
   const int t = (id / (N_XCD * J)) * N_XCD + id % N_XCD;
   if (t >= n_q) return;
   const int jj = (id / N_XCD) % J;
   const int hg = jj % AT_GROUPS;
-  const int dh = jj / AT_GROUPS;   // output channels 256*dh .. 256*dh + 255
+  const int dh = jj / AT_GROUPS;   // output channels from 256*dh (0 with one workgroup)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -165,8 +172,14 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(
                                            rs_idx, in ? item * 4 : k * 4, 0, 0));
   };
+  // p0 is the first slice's position; the next one (p1 with two buffers, else the first
+  // look-ahead pX) is loaded up front as well.
   const int32_t p0 = position(c0);
-  const int32_t p1 = position(c0 + AT_WAVES);
+  int32_t p1 = 0, pX = 0;
+  if constexpr (NBUF == 2)
+    p1 = position(c0 + AT_WAVES);
+  else
+    pX = position(c0 + AT_WAVES);
 
   // This wavefront's two k-steps of the logit B operand: Q^T for head h, channels
   // 8*ks + 128*gq .. +7 with ks = 2*wave, 2*wave + 1 (the conversion produces the rows
@@ -259,39 +272,43 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     sh.qop[2 * wave][lane] = __builtin_bit_cast(u32x4, b0);
     sh.qop[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, b1);
   }
-  // Two gather buffers: a slice's rows are requested two steps before their use. Each
-  // gather is followed by the position load of the slice two steps after it, in the same
+  // NBUF gather buffers: a slice's rows are requested NBUF steps before their use. Each
+  // gather is followed by the position load of the slice NBUF steps after it, in the same
   // order as in the loop, so the loop's waits match on every path.
-  Raw bufA, bufB;
+  Raw bufs[NBUF];
+  Raw& bufA = bufs[0];          // buffer of the even steps
+  Raw& bufS = bufs[NBUF - 1];   // buffer of the odd steps
   fetch(c0, p0, bufA);
-  int32_t pX = position(c0 + 2 * AT_WAVES);
-  fetch(c0 + AT_WAVES, p1, bufB);
-  int32_t pY = position(c0 + 3 * AT_WAVES);
+  if constexpr (NBUF == 2) {
+    pX = position(c0 + 2 * AT_WAVES);
+    fetch(c0 + AT_WAVES, p1, bufS);
+  }
+  int32_t pY = position(c0 + (NBUF + 1) * AT_WAVES);
   __syncthreads();   // the query operand is complete
 
-  // Output accumulator of this half: O^T[d = 256*dh + 16*dt + 4*gq + i][h], dt = 0..15.
-  f32x4 oacc[AT_DT];
+  // Output accumulator: O^T[d = 256*dh + 16*dt + 4*gq + i][h], dt = 0..DT-1.
+  f32x4 oacc[DT];
 #pragma unroll
-  for (int i = 0; i < AT_DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();   // reference max of head col (log2 units)
   bool ok_pass = true;               // no logit of this pass overflowed the reference
   float l_run = 0.f;                 // this lane's share of the sum for head col
   uint16_t* const tile = sh.tile[wave];
   uint16_t* const tile_w = tile + TILE_ROW * col + TILE_QUARTER * gq;
-  // Transpose reads start at this half's first channel quarter (2*dh).
+  // Transpose reads start at this workgroup's first channel quarter (2*dh).
   const uint16_t* const tile_r =
       tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3) + TILE_QUARTER * (2 * dh);
 
   // One slice (c may lie past the last: its items are all absent); pn is the position of
-  // the slice two steps later in this wavefront's sequence (c + 2*AT_WAVES), whose gather
-  // is started as soon as this slice's registers are free. A logit exceeding the reference by more than
+  // the slice NBUF steps later in this wavefront's sequence (c + NBUF*AT_WAVES), whose
+  // gather is started as soon as this slice's registers are free. A logit exceeding the reference by more than
   // AT_GAP raises the reference and marks the pass for a repeat.
   auto step = [&](int c, Raw& raw, int32_t pn) {
     const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
     // A slice with no item (past the last) converts nothing; only its next gather starts.
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     if (valid != 0ull) sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
-    fetch(c + 2 * AT_WAVES, pn, raw);
+    fetch(c + NBUF * AT_WAVES, pn, raw);
     if (valid == 0ull) return;
     // LDS operations of one wavefront complete in order; the fences keep the compiler from
     // moving the tile reads above the writes.
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     // of a 16-lane group addresses channels 16*dt + 4*(i%4) .. +3 of item 4*gq + i/4 and
     // receives channel 16*dt + i of items 4*gq .. 4*gq+3.
 #pragma unroll
-    for (int dt = 0; dt < AT_DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
       const u32x2 a = lds_read_tr16x4(tile_r + TILE_QUARTER * (dt >> 3) + 16 * (dt & 7));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), pv,
                                                        oacc[dt], 0, 0, 0);
@@ -338,9 +355,9 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 
   // Every step runs unconditionally (a slice past the last is all absent and its loads
   // return zeros without touching memory), so each buffer is written by the same loads on
-  // every path and a step waits only for its own slice. Steps alternate between the two
-  // buffers; positions are loaded two steps before their gather, pX and pY alternating so
-  // that no register is copied.
+  // every path and a step waits only for its own slice. With two buffers the steps
+  // alternate between them; positions are loaded two steps before their gather, pX and pY
+  // alternating so that no register is copied.
   bool again;
 #pragma unroll 1
   do {
@@ -348,19 +365,19 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 #pragma unroll 1
     for (int c = c0; c < hi; c += 2 * AT_WAVES) {
       step(c, bufA, pX);
-      pX = position(c + 4 * AT_WAVES);
-      step(c + AT_WAVES, bufB, pY);
-      pY = position(c + 5 * AT_WAVES);
+      pX = position(c + (NBUF + 2) * AT_WAVES);
+      step(c + AT_WAVES, bufS, pY);
+      pY = position(c + (NBUF + 3) * AT_WAVES);
     }
     again = !ok_pass;
     if (again) {   // a logit overflowed the reference: repeat with the raised one
 #pragma unroll
-      for (int i = 0; i < AT_DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       l_run = 0.f;
       fetch(c0, position(c0), bufA);
-      pX = position(c0 + 2 * AT_WAVES);
-      fetch(c0 + AT_WAVES, position(c0 + AT_WAVES), bufB);
-      pY = position(c0 + 3 * AT_WAVES);
+      pX = position(c0 + NBUF * AT_WAVES);
+      if constexpr (NBUF == 2) fetch(c0 + AT_WAVES, position(c0 + AT_WAVES), bufS);
+      pY = position(c0 + (NBUF + 1) * AT_WAVES);
     }
   } while (again);
 
@@ -372,9 +389,10 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     sh.wl[wave][col] = l_run;
   }
   __syncthreads();   // also ends every wavefront's use of its tile
-  // Thread tid reduces the entries (dt = tid/64 and 8 + tid/64, lane l = tid%64) of every
-  // wavefront's accumulator: O^T[256*dh + 16*dt + 4*(l/16) + i][head l%16], so its head
-  // is tid%16 for both.
+  // In passes of 16 tiles (one with two halves, two with one workgroup), thread tid
+  // reduces the entries (dt = tid/64 and 8 + tid/64, lane l = tid%64) of every wavefront's
+  // accumulator: O^T[256*(dh + pass) + 16*dt + 4*(l/16) + i][head l%16], so its head is
+  // tid%16 throughout.
   const int oh = tid & 15;
   float fwh[AT_WAVES];
   float Mh = -__builtin_inff();
@@ -389,31 +407,42 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   }
   const int rl = tid & 63;
   const int rdt = tid >> 6;
+  constexpr int NPASS = DT / 16;
+  f32x4 acc[NPASS][2];
 #pragma unroll
-  for (int dt = 0; dt < AT_DT; ++dt) sh.part[wave][dt][lane] = __builtin_bit_cast(u32x4, oacc[dt]);
-  __syncthreads();
-  f32x4 acc[2];
+  for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    f32x4 a = __builtin_bit_cast(f32x4, sh.part[0][rdt + 8 * j][rl]) * fwh[0];
+    for (int dt = 0; dt < 16; ++dt)
+      sh.part[wave][dt][lane] = __builtin_bit_cast(u32x4, oacc[16 * ps + dt]);
+    __syncthreads();
 #pragma unroll
-    for (int w = 1; w < AT_WAVES; ++w)
-      a += __builtin_bit_cast(f32x4, sh.part[w][rdt + 8 * j][rl]) * fwh[w];
-    acc[j] = a;
+    for (int j = 0; j < 2; ++j) {
+      f32x4 a = __builtin_bit_cast(f32x4, sh.part[0][rdt + 8 * j][rl]) * fwh[0];
+#pragma unroll
+      for (int w = 1; w < AT_WAVES; ++w)
+        a += __builtin_bit_cast(f32x4, sh.part[w][rdt + 8 * j][rl]) * fwh[w];
+      acc[ps][j] = a;
+    }
+    // Before the buffer is written again; also after the last pass, which keeps the
+    // compiler from overlapping the passes (that runs the full-width variant out of
+    // registers).
+    __syncthreads();
   }
 
-  // Both halves compute the same logits, so their maxima and sums agree; each writes its
-  // own 256 channels, and the first the log-sum-exp.
+  // Two halves compute the same logits, so their maxima and sums agree; each writes its
+  // own channels, and the first the log-sum-exp.
   const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
   uint16_t* orow = out + ((int64_t)t * 64 + hg * AT_HEADS + oh) * 512;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const f32x4 a = acc[j];
-    const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
-    const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
-    const int ch = 256 * dh + 16 * (rdt + 8 * j) + 4 * (rl >> 4);
-    *reinterpret_cast<u32x2*>(orow + ch) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-  }
+  for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 a = acc[ps][j];
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
+      const int ch = 256 * (dh + ps) + 16 * (rdt + 8 * j) + 4 * (rl >> 4);
+      *reinterpret_cast<u32x2*>(orow + ch) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+    }
   if (lse != nullptr && dh == 0 && tid < 16)
     lse[(int64_t)t * 64 + hg * AT_HEADS + oh] =
         Lh > 0.f ? (Mh + __log2f(Lh)) * AT_LN2 : -__builtin_inff();
@@ -427,10 +456,16 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               const int32_t* n_swa, float softmax_scale, uint16_t* out,
                               float* lse, hipStream_t stream) {
   const int groups8 = (n_q + N_XCD - 1) / N_XCD;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3(groups8 * N_XCD * AT_GROUPS * AT_HALVES),
-                     dim3(AT_THREADS), 0, stream, q, kv_fp4, fp4_stride, kv_scale, scale_stride,
-                     n_entries, kv_start, topk_idx, ld_idx, k, window_kv, n_window_rows,
-                     swa_start, n_swa, softmax_scale, n_q, out, lse);
+  if (n_q <= AT_HALVES_MAX_Q)
+    hipLaunchKernelGGL(sparse_attn_kernel<2>, dim3(groups8 * N_XCD * AT_GROUPS * 2),
+                       dim3(AT_THREADS), 0, stream, q, kv_fp4, fp4_stride, kv_scale,
+                       scale_stride, n_entries, kv_start, topk_idx, ld_idx, k, window_kv,
+                       n_window_rows, swa_start, n_swa, softmax_scale, n_q, out, lse);
+  else
+    hipLaunchKernelGGL(sparse_attn_kernel<1>, dim3(groups8 * N_XCD * AT_GROUPS),
+                       dim3(AT_THREADS), 0, stream, q, kv_fp4, fp4_stride, kv_scale,
+                       scale_stride, n_entries, kv_start, topk_idx, ld_idx, k, window_kv,
+                       n_window_rows, swa_start, n_swa, softmax_scale, n_q, out, lse);
   return hipGetLastError();
 }
 
