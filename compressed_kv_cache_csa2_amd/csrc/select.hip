@@ -484,6 +484,78 @@ struct BlockSrc {
   }
 };
 
+// Key of one block maximum: the forced block reads special_value; a block at or past
+// n_blocks is absent.
+__device__ __forceinline__ uint32_t block_key(float v, uint32_t b, uint32_t special,
+                                              float special_value, uint32_t n_blocks) {
+  const float x = b == special ? special_value : v;
+  return (b < n_blocks && selectable(x)) ? float_key(x) : 0u;
+}
+
+// Maxima of aligned groups of four blocks ("quads"): element q is the largest key of
+// blocks 4q .. 4q+3, one float4 (0 when none is present). Loaded eight quads at a time to
+// bound the registers in flight.
+struct QuadSrc {
+  const float* bm;
+  uint32_t special;   // forced block, 0xFFFFFFFF for none
+  float special_value;
+  uint32_t n_blocks;
+  template <int R>
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
+#pragma unroll
+    for (int c = 0; c < R / 8; ++c) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = first + (uint32_t)((8 * c + u) / 4) * stride + (uint32_t)(u % 4);
+        v[u] = *reinterpret_cast<const float4*>(bm + 4u * (q < n ? q : 0u));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t q = first + (uint32_t)((8 * c + u) / 4) * stride + (uint32_t)(u % 4);
+        const uint32_t b = 4u * q;
+        uint32_t k = block_key(v[u].x, b, special, special_value, n_blocks);
+        k = umax32(k, block_key(v[u].y, b + 1u, special, special_value, n_blocks));
+        k = umax32(k, block_key(v[u].z, b + 2u, special, special_value, n_blocks));
+        k = umax32(k, block_key(v[u].w, b + 3u, special, special_value, n_blocks));
+        keys[8 * c + u] = q < n ? k : 0u;
+      }
+    }
+  }
+};
+
+// The blocks of the candidate quads: element i is block cquads[i/4]*4 + i%4 (a negative
+// quad id is absent).
+struct QuadBlockSrc {
+  const float* bm;
+  const int32_t* cquads;   // LDS
+  uint32_t special;
+  float special_value;
+  uint32_t n_blocks;
+  template <int R>
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
+    float4 v[R / 4];
+    int32_t qd[R / 4];
+#pragma unroll
+    for (int g = 0; g < R / 4; ++g) {   // 4 consecutive elements = one quad
+      const uint32_t i0 = first + g * stride;
+      qd[g] = i0 < n ? cquads[i0 >> 2] : -1;
+      v[g] = *reinterpret_cast<const float4*>(bm + 4u * (uint32_t)(qd[g] >= 0 ? qd[g] : 0));
+    }
+#pragma unroll
+    for (int g = 0; g < R / 4; ++g) {
+      const uint32_t b = 4u * (uint32_t)qd[g];
+      const bool ok = qd[g] >= 0;
+      keys[4 * g + 0] = ok ? block_key(v[g].x, b, special, special_value, n_blocks) : 0u;
+      keys[4 * g + 1] = ok ? block_key(v[g].y, b + 1u, special, special_value, n_blocks) : 0u;
+      keys[4 * g + 2] = ok ? block_key(v[g].z, b + 2u, special, special_value, n_blocks) : 0u;
+      keys[4 * g + 3] = ok ? block_key(v[g].w, b + 3u, special, special_value, n_blocks) : 0u;
+    }
+  }
+};
+
 // Scores of the candidate blocks' slots: element i is slot cblocks[i/8]*8 + i%8 (a
 // negative block id, or a slot at or past n_slots, is absent).
 struct CandSrc {
@@ -530,6 +602,37 @@ __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32
   }
   KeyRow<Src, 32, true> row(src, n);
   return select_row(row, k, sh, emit);
+}
+
+// The HSI pool of one query: the n_keep best of its nb block maxima (the forced block
+// nb - 1 reads +inf) into sh.obuf in ascending block order; returns how many. Rows of more
+// than 32,768 blocks first keep the n_keep best quads (aligned groups of four blocks,
+// ranked by their largest block): a quad left out has n_keep quads ranked above it, each
+// holding a block that outranks all of its blocks (ties go to the lower index at both
+// levels), so every pool block lies in a kept quad; the pool is then selected among their
+// blocks. This replaces several passes over the row by one.
+__device__ __forceinline__ uint32_t select_pool(const float* bm_row, int64_t nb, int n_keep,
+                                                SelShared& sh) {
+  const uint32_t kk = (uint32_t)n_keep;
+  auto to_obuf = [&](uint32_t rank, uint32_t b) {
+    if (rank < kk) sh.obuf[rank] = (int32_t)b;
+  };
+  if (nb <= (int64_t)SEL_THREADS * 32) {
+    const BlockSrc src{bm_row, nb - 1, __builtin_inff()};
+    return select_any(src, nb, kk, sh, to_obuf);
+  }
+  const uint32_t nbu = (uint32_t)nb;
+  const QuadSrc qsrc{bm_row, nbu - 1u, __builtin_inff(), nbu};
+  const uint32_t n_cq = select_any(qsrc, (nb + 3) >> 2, kk, sh, [&](uint32_t rank, uint32_t q) {
+    if (rank < kk) sh.cblocks[rank] = (int32_t)q;
+  });
+  __syncthreads();
+  const QuadBlockSrc bsrc{bm_row, sh.cblocks, nbu - 1u, __builtin_inff(), nbu};
+  const uint32_t n_c = n_cq < kk ? n_cq : kk;
+  // Element i of the second row is block cblocks[i/4]*4 + i%4.
+  return select_any(bsrc, (int64_t)n_c * 4, kk, sh, [&](uint32_t rank, uint32_t i) {
+    if (rank < kk) sh.obuf[rank] = sh.cblocks[i >> 2] * 4 + (int32_t)(i & 3u);
+  });
 }
 
 // The first min(kept, k) entries of sh.obuf go out, then -1 up to k.
@@ -624,10 +727,7 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_kernel(
   const int64_t nv = n_visible[t];
   int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
   if (nb > ld_bm) nb = ld_bm;
-  const BlockSrc src{block_max + (int64_t)t * ld_bm, nb - 1, __builtin_inff()};
-  const uint32_t kept = select_any(src, nb, (uint32_t)n_keep, sh, [&](uint32_t rank, uint32_t b) {
-    if (rank < (uint32_t)n_keep) sh.obuf[rank] = (int32_t)b;
-  });
+  const uint32_t kept = select_pool(block_max + (int64_t)t * ld_bm, nb, n_keep, sh);
   __syncthreads();
   write_out(sh, kept, n_keep, pool + (int64_t)t * ld_pool);
 }
@@ -644,10 +744,7 @@ __global__ __launch_bounds__(SEL_THREADS) void pool_topk_kernel(
   const int64_t nv = n_visible[t];
   int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
   if (nb > ld_bm) nb = ld_bm;
-  const BlockSrc bsrc{block_max + (int64_t)t * ld_bm, nb - 1, __builtin_inff()};
-  const uint32_t kept_pool = select_any(bsrc, nb, (uint32_t)n_keep, sh, [&](uint32_t rank, uint32_t b) {
-    if (rank < (uint32_t)n_keep) sh.obuf[rank] = (int32_t)b;
-  });
+  const uint32_t kept_pool = select_pool(block_max + (int64_t)t * ld_bm, nb, n_keep, sh);
   __syncthreads();
   int32_t* prow = pool + (int64_t)t * ld_pool;
   for (int r = threadIdx.x; r < n_keep; r += SEL_THREADS) {

@@ -297,7 +297,10 @@ def test_topk_pool_mapping(C, dev):
 
 
 @pytest.mark.parametrize("kind,nvis", [("normal", [40000, 16385, 1000, 0, 7]),
-                                       ("ties", [200000, 9, 16384 * 8 + 3, 8, 17])])
+                                       ("ties", [200000, 9, 16384 * 8 + 3, 8, 17]),
+                                       # more than 32,768 blocks: quads first, then blocks
+                                       ("ties", [600000, 262153, 300001, 8, 0]),
+                                       ("normal", [1048576, 524289, 262151])])
 def test_block_pool_exact(C, dev, kind, nvis):
     n_q = len(nvis)
     width = max(nvis)
