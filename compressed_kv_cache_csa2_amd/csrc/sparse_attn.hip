@@ -12,18 +12,20 @@
 // (separately, so a slice never mixes the two formats). A workgroup owns one group of 16
 // heads and, with at most 32 queries (too few to fill the GPU otherwise), one half (256
 // channels) of the output, else all of it; its eight wavefronts (two per SIMD, so one's
-// memory waits hide behind the other's arithmetic) take every eighth slice of the query
-// and run independently (no barrier in the main loop). Both halves of a head group compute
-// the same full-width logits and softmax, so each writes its own channels with no merge
-// across workgroups, and each wavefront's accumulator is half as large as a full-width
-// one, which leaves the registers for a second gather buffer. Per slice a wavefront:
-//   - gathers the 16 rows (lane = item x quarter of the 512 channels) two slices ahead of
-//     their use, alternating between two register buffers (one slice ahead, in one
-//     buffer, at full width), with the selected positions loaded two slices before the
-//     gather. The gathers are indexed buffer loads: an
-//     absent item gets an index past the buffer's record count and reads zeros, so every
-//     slice issues the same loads into the same registers and the wait for a slice never
-//     includes the loads of the slices behind it;
+// memory waits hide behind the other's arithmetic) each take one of the window's eight
+// slices and every eighth slice of the selected entries, and run independently (no
+// barrier in the main loop). Both halves of a head group compute the same full-width
+// logits and softmax, so each writes its own channels with no merge across workgroups,
+// and each wavefront's accumulator is half as large as a full-width one, which leaves the
+// registers for a second gather buffer. Per slice a wavefront:
+//   - gathers the 16 rows (lane = item x quarter of the 512 channels). The window slice
+//     needs no position, so its gather is issued first and it is processed first, while
+//     the selected rows are in flight; those are gathered two slices ahead of their use,
+//     alternating between two register buffers (one slice ahead, in one buffer, at full
+//     width), with the selected positions loaded two slices before the gather. The
+//     gathers are indexed buffer loads: an absent item gets an index past the buffer's
+//     record count and reads zeros, so every slice of a kind issues the same loads into
+//     the same registers and the wait for a slice never includes the loads behind it;
 //   - converts them to fp16 with the hardware E2M1/E4M3 -> fp16 conversions and a packed
 //     fp16 multiply by the group scale; every value is exact (an E2M1 x E4M3 product has
 //     <= 6 significant bits in [2^-10, 2688]). The converted registers are directly the A
@@ -81,28 +83,28 @@ struct AttnShared {
   float wl[AT_WAVES][AT_HEADS];
 };
 
-// One slice's gathered bytes for one lane: 64 B of an FP4 row plus its 8 scale bytes, or
-// 128 B of a window row. Absent items read as zeros.
-struct Raw {
-  u32x4 v[8];
+// One slice's gathered bytes for one lane: 64 B of an FP4 row plus its 8 scale bytes
+// (RawMain), or 128 B of a window row (RawWin). Absent items read as zeros.
+struct RawMain {
+  u32x4 v[4];
   uint32_t sc0, sc1;
   bool valid;   // the item exists
 };
+struct RawWin {
+  u32x4 v[8];
+  bool valid;
+};
 
-// Converts block j (channels 128*gq + 8j .. +7) of the lane's gathered bytes to fp16. The
-// format is wavefront-uniform, so this is a scalar branch, not a select.
-__device__ __forceinline__ u32x4 convert_block(const Raw& r, const f16x2 (&sq)[8], int j,
-                                               bool window) {
-  if (window) return fp8x8_to_f16x8(r.v[j >> 1][2 * (j & 1)], r.v[j >> 1][2 * (j & 1) + 1]);
-  return fp4x8_to_f16x8(r.v[j >> 2][j & 3], sq[j >> 1]);
-}
-
-// Converts the lane's 16 blocks, stores them to its row quarter of the tile (tile_row)
-// and accumulates the logits against the query operand held in LDS.
-__device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const u32x4 (*qop)[64],
-                                                   int lane, uint16_t* tile_row, bool window) {
+// Converts the lane's 16 blocks (block j = channels 128*gq + 8j .. +7) to fp16, stores
+// them to its row quarter of the tile (tile_row) and accumulates the logits against the
+// query operand held in LDS. The format is a template parameter: the caller branches once
+// per slice (a wavefront-uniform choice), so the 16 blocks have no branch between them and
+// the operand reads can be issued ahead of the products.
+template <bool WINDOW, class R>
+__device__ __forceinline__ f32x4 convert_and_score(const R& r, const u32x4 (*qop)[64],
+                                                   int lane, uint16_t* tile_row) {
   f16x2 sq[8];
-  {
+  if constexpr (!WINDOW) {
     const f16x2 s01 = e4m3x2_to_f16x2<false>(r.sc0), s23 = e4m3x2_to_f16x2<true>(r.sc0);
     const f16x2 s45 = e4m3x2_to_f16x2<false>(r.sc1), s67 = e4m3x2_to_f16x2<true>(r.sc1);
     sq[0] = f16x2{s01.x, s01.x}; sq[1] = f16x2{s01.y, s01.y};
@@ -111,13 +113,23 @@ __device__ __forceinline__ f32x4 convert_and_score(const Raw& r, const u32x4 (*q
     sq[6] = f16x2{s67.x, s67.x}; sq[7] = f16x2{s67.y, s67.y};
   }
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  // The operand of block j + QLEAD is read while block j is converted and multiplied.
+  constexpr int QLEAD = 2;
+  u32x4 b[QLEAD + 1];
+#pragma unroll
+  for (int j = 0; j < QLEAD; ++j) b[j] = qop[j][lane];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const u32x4 a = convert_block(r, sq, j, window);
+    if (j + QLEAD < 16) b[(j + QLEAD) % (QLEAD + 1)] = qop[j + QLEAD][lane];
+    u32x4 a;
+    if constexpr (WINDOW)
+      a = fp8x8_to_f16x8(r.v[j >> 1][2 * (j & 1)], r.v[j >> 1][2 * (j & 1) + 1]);
+    else
+      a = fp4x8_to_f16x8(r.v[j >> 2][j & 3], sq[j >> 1]);
     *reinterpret_cast<u32x4*>(tile_row + 8 * j) = a;
-    const u32x4 b = qop[j][lane];
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), sacc, 0, 0, 0);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b[j % (QLEAD + 1)]), sacc, 0,
+        0, 0);
   }
   return sacc;
 }
@@ -153,11 +165,10 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const int gq = lane >> 4;    // lane group 0..3; also the channel quarter a lane gathers
   const int h = hg * AT_HEADS + col;
 
-  // Slices: the selected entries first (slice c < n_msl holds entries 16c .. 16c+15), then
-  // the window rows, sized for the largest window so that the slice range (and the
-  // position loads below) does not wait for n_swa.
+  // Slices: the selected entries (slice c < n_msl holds entries 16c .. 16c+15), taken by
+  // wavefront c % 8, and the window's 8 slices, one per wavefront.
+  static_assert(AT_WIN_SLICES == AT_WAVES, "one window slice per wavefront");
   const int n_msl = (k + AT_SLICE - 1) / AT_SLICE;
-  const int hi = n_msl + AT_WIN_SLICES;
   const int c0 = wave;
 
   // Selected positions, through a buffer over this query's k entries: a slot past k (or
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   // exists, so the load is never waited for early.
   auto position = [&](int c) -> int32_t {   // position of this lane's item of slice c
     const int item = AT_SLICE * c + col;
-    const bool in = c < hi && c < n_msl && item < k;
+    const bool in = c < n_msl && item < k;
     return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(
                                            rs_idx, in ? item * 4 : k * 4, 0, 0));
   };
@@ -188,54 +199,23 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const u32x4 qr0 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave));
   const u32x4 qr1 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave + 1));
 
-  int nsw = n_swa[t];
-  nsw = nsw < 0 ? 0 : (nsw > AT_WINDOW ? AT_WINDOW : nsw);
-  const int64_t base = kv_start[t];
-  const int64_t wbase = swa_start[t];
-
-  // Gather: lane (item col of slice c, quarter gq) -> channels 128*gq .. +127 of that item.
-  // The buffers are indexed by row relative to the query's own base, so the 32-bit record
-  // index covers any sequence; absent items use an index past every record count.
-  constexpr uint32_t ABSENT = 0xFFFFFFFFu;
-  const int64_t kv_rows = n_entries - base;
-  const int64_t win_rows = n_win_rows - wbase;
-  const uint32_t kv_n = kv_rows <= 0 ? 0u : (kv_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)kv_rows);
-  const uint32_t win_n = win_rows <= 0 ? 0u : (win_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)win_rows);
-  const __amdgpu_buffer_rsrc_t rs_kv = make_rows_rsrc(kv_fp4 + base * fp4_stride, (int)fp4_stride, kv_n);
-  const __amdgpu_buffer_rsrc_t rs_sc = make_rows_rsrc(kv_scale + base * sc_stride, (int)sc_stride, kv_n);
-  const __amdgpu_buffer_rsrc_t rs_win = make_rows_rsrc(window_kv + wbase * 512, 512, win_n);
-  auto fetch = [&](int c, int32_t p, Raw& raw) {
-    const bool main = c < n_msl;   // wavefront-uniform
-    uint32_t ridx;
-    bool ok;
-    if (main) {
-      const int item = AT_SLICE * c + col;
-      const int64_t row = base + p;
-      ok = c < hi && item < k && p >= 0 && row >= 0 && row < n_entries;
-      ridx = (uint32_t)p;
-    } else {
-      const int wi = AT_SLICE * (c - n_msl) + col;
-      const int64_t wr = wbase + wi;
-      ok = c < hi && wi < nsw && wr >= 0 && wr < n_win_rows;
-      ridx = (uint32_t)wi;
-    }
-    raw.valid = ok;
-    const uint32_t i_main = ok && main ? ridx : ABSENT;
-    const uint32_t i_win = ok && !main ? ridx : ABSENT;
-    // Blocks 0..3: the FP4 row quarter (64 B) or the first half of the window row quarter;
-    // blocks 4..7: the second half of the window row quarter (zeros for FP4 slices).
-    const __amdgpu_buffer_rsrc_t r_lo = main ? rs_kv : rs_win;
-    const uint32_t i_lo4 = main ? i_main : i_win;
-    const int o_lo = main ? 64 * gq : 128 * gq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw.v[i] = sbuf_load_b128(r_lo, (int)i_lo4, o_lo + 16 * i, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      raw.v[4 + i] = sbuf_load_b128(rs_win, (int)i_win, 128 * gq + 64 + 16 * i, 0, 0);
-    const u32x2 s8 = sbuf_load_b64(rs_sc, (int)i_main, 8 * gq, 0, 0);
-    raw.sc0 = s8.x;
-    raw.sc1 = s8.y;
-  };
+  // The per-query scalars come through vector loads issued beside the query and position
+  // loads, so their latency overlaps with those; as scalar loads they would be waited for
+  // at the first barrier, which also drains the scalar-load counter.
+  int nsw, base_lo, base_hi, wbase_lo, wbase_hi;
+  {
+    const __amdgpu_buffer_rsrc_t rs_ks = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int64_t*>(kv_start) + t, (short)0, 8, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_ws = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int64_t*>(swa_start) + t, (short)0, 8, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_ns = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(n_swa) + t, (short)0, 4, 0x00020000);
+    base_lo = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rs_ks, 0, 0, 0));
+    base_hi = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rs_ks, 4, 0, 0));
+    wbase_lo = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rs_ws, 0, 0, 0));
+    wbase_hi = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rs_ws, 4, 0, 0));
+    nsw = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rs_ns, 0, 0, 0));
+  }
 
   // Query scale: per head, the largest |q| over its 512 channels (spread over the eight
   // wavefronts' k-steps), then a power of two that brings it to [2^14, 2^15).
@@ -254,6 +234,46 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   float qmax = 0.f;
 #pragma unroll
   for (int w = 0; w < AT_WAVES; ++w) qmax = fmaxf(qmax, sh.qpart[w][col]);
+  nsw = __builtin_amdgcn_readfirstlane(nsw);
+  nsw = nsw < 0 ? 0 : (nsw > AT_WINDOW ? AT_WINDOW : nsw);
+  const int64_t base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(base_hi) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane(base_lo));
+  const int64_t wbase = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(wbase_hi) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane(wbase_lo));
+  // Gather: lane (item col of slice c, quarter gq) -> channels 128*gq .. +127 of that item.
+  // The buffers are indexed by row relative to the query's own base, so the 32-bit record
+  // index covers any sequence; absent items use an index past every record count.
+  constexpr uint32_t ABSENT = 0xFFFFFFFFu;
+  const int64_t kv_rows = n_entries - base;
+  const int64_t win_rows = n_win_rows - wbase;
+  const uint32_t kv_n = kv_rows <= 0 ? 0u : (kv_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)kv_rows);
+  const uint32_t win_n = win_rows <= 0 ? 0u : (win_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)win_rows);
+  const __amdgpu_buffer_rsrc_t rs_kv = make_rows_rsrc(kv_fp4 + base * fp4_stride, (int)fp4_stride, kv_n);
+  const __amdgpu_buffer_rsrc_t rs_sc = make_rows_rsrc(kv_scale + base * sc_stride, (int)sc_stride, kv_n);
+  const __amdgpu_buffer_rsrc_t rs_win = make_rows_rsrc(window_kv + wbase * 512, 512, win_n);
+  auto fetch_main = [&](int c, int32_t p, RawMain& raw) {
+    const int item = AT_SLICE * c + col;
+    const int64_t row = base + p;
+    const bool ok = c < n_msl && item < k && p >= 0 && row >= 0 && row < n_entries;
+    raw.valid = ok;
+    const int ridx = ok ? p : (int)ABSENT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw.v[i] = sbuf_load_b128(rs_kv, ridx, 64 * gq + 16 * i, 0, 0);
+    const u32x2 s8 = sbuf_load_b64(rs_sc, ridx, 8 * gq, 0, 0);
+    raw.sc0 = s8.x;
+    raw.sc1 = s8.y;
+  };
+  // Window slice w (rows 16w .. 16w+15 of the query's window) belongs to wavefront w.
+  auto fetch_win = [&](RawWin& raw) {
+    const int wi = AT_SLICE * wave + col;
+    const int64_t wr = wbase + wi;
+    const bool ok = wi < nsw && wr >= 0 && wr < n_win_rows;
+    raw.valid = ok;
+    const int ridx = ok ? wi : (int)ABSENT;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw.v[i] = sbuf_load_b128(rs_win, ridx, 128 * gq + 16 * i, 0, 0);
+  };
+
   const int qexp = qmax > 0.f ? (int)((__float_as_uint(qmax) >> 23) & 0xFFu) - 127 : 0;
   int kexp = 14 - qexp;
   kexp = kexp < -126 ? -126 : (kexp > 126 ? 126 : kexp);
@@ -272,16 +292,20 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     sh.qop[2 * wave][lane] = __builtin_bit_cast(u32x4, b0);
     sh.qop[2 * wave + 1][lane] = __builtin_bit_cast(u32x4, b1);
   }
-  // NBUF gather buffers: a slice's rows are requested NBUF steps before their use. Each
-  // gather is followed by the position load of the slice NBUF steps after it, in the same
-  // order as in the loop, so the loop's waits match on every path.
-  Raw bufs[NBUF];
-  Raw& bufA = bufs[0];          // buffer of the even steps
-  Raw& bufS = bufs[NBUF - 1];   // buffer of the odd steps
-  fetch(c0, p0, bufA);
+  // The window slice is gathered first and processed first: its rows need no position
+  // load, so they arrive while the selected rows are still in flight. NBUF main buffers: a
+  // slice's rows are requested NBUF steps before their use (with one buffer, the first
+  // main gather starts once the window slice is converted). Each gather is followed by
+  // the position load of the slice NBUF steps after it, in the same order as in the loop.
+  RawWin rw;
+  RawMain bufs[NBUF];
+  RawMain& bufA = bufs[0];          // buffer of the even steps
+  RawMain& bufS = bufs[NBUF - 1];   // buffer of the odd steps
+  fetch_win(rw);
   if constexpr (NBUF == 2) {
+    fetch_main(c0, p0, bufA);
     pX = position(c0 + 2 * AT_WAVES);
-    fetch(c0 + AT_WAVES, p1, bufS);
+    fetch_main(c0 + AT_WAVES, p1, bufS);
   }
   int32_t pY = position(c0 + (NBUF + 1) * AT_WAVES);
   __syncthreads();   // the query operand is complete
@@ -299,17 +323,9 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   const uint16_t* const tile_r =
       tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3) + TILE_QUARTER * (2 * dh);
 
-  // One slice (c may lie past the last: its items are all absent); pn is the position of
-  // the slice NBUF steps later in this wavefront's sequence (c + NBUF*AT_WAVES), whose
-  // gather is started as soon as this slice's registers are free. A logit exceeding the reference by more than
-  // AT_GAP raises the reference and marks the pass for a repeat.
-  auto step = [&](int c, Raw& raw, int32_t pn) {
-    const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
-    // A slice with no item (past the last) converts nothing; only its next gather starts.
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    if (valid != 0ull) sacc = convert_and_score(raw, sh.qop, lane, tile_w, c >= n_msl);
-    fetch(c + NBUF * AT_WAVES, pn, raw);
-    if (valid == 0ull) return;
+  // The softmax and PV part of a slice with at least one valid item. A logit exceeding
+  // the reference by more than AT_GAP raises the reference and marks the pass for a repeat.
+  auto finish = [&](uint64_t valid, f32x4 sacc) {
     // LDS operations of one wavefront complete in order; the fences keep the compiler from
     // moving the tile reads above the writes.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -353,6 +369,25 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     }
   };
 
+  // A main slice (c may lie past the last: its items are all absent); pn is the position
+  // of the slice NBUF steps later in this wavefront's sequence (c + NBUF*AT_WAVES), whose
+  // gather starts as soon as this slice's registers are free. A slice with no item
+  // converts nothing; only its next gather starts.
+  auto step_main = [&](int c, RawMain& raw, int32_t pn) {
+    const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if (valid != 0ull) sacc = convert_and_score<false>(raw, sh.qop, lane, tile_w);
+    fetch_main(c + NBUF * AT_WAVES, pn, raw);
+    if (valid != 0ull) finish(valid, sacc);
+  };
+  auto step_win = [&]() {
+    const uint64_t valid = __ballot(rw.valid);
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if (valid != 0ull) sacc = convert_and_score<true>(rw, sh.qop, lane, tile_w);
+    if constexpr (NBUF == 1) fetch_main(c0, p0, bufA);
+    if (valid != 0ull) finish(valid, sacc);
+  };
+
   // Every step runs unconditionally (a slice past the last is all absent and its loads
   // return zeros without touching memory), so each buffer is written by the same loads on
   // every path and a step waits only for its own slice. With two buffers the steps
@@ -362,11 +397,12 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 #pragma unroll 1
   do {
     ok_pass = true;
+    step_win();
 #pragma unroll 1
-    for (int c = c0; c < hi; c += 2 * AT_WAVES) {
-      step(c, bufA, pX);
+    for (int c = c0; c < n_msl; c += 2 * AT_WAVES) {
+      step_main(c, bufA, pX);
       pX = position(c + (NBUF + 2) * AT_WAVES);
-      step(c + AT_WAVES, bufS, pY);
+      step_main(c + AT_WAVES, bufS, pY);
       pY = position(c + (NBUF + 3) * AT_WAVES);
     }
     again = !ok_pass;
@@ -374,9 +410,10 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 #pragma unroll
       for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       l_run = 0.f;
-      fetch(c0, position(c0), bufA);
+      fetch_win(rw);
+      if constexpr (NBUF == 2) fetch_main(c0, p0, bufA);
       pX = position(c0 + NBUF * AT_WAVES);
-      if constexpr (NBUF == 2) fetch(c0 + AT_WAVES, position(c0 + AT_WAVES), bufS);
+      if constexpr (NBUF == 2) fetch_main(c0 + AT_WAVES, p1, bufS);
       pY = position(c0 + (NBUF + 1) * AT_WAVES);
     }
   } while (again);
