@@ -46,6 +46,8 @@
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
+#include <type_traits>
+
 namespace csa2 {
 
 constexpr int AT_WAVES = 8;
@@ -83,34 +85,44 @@ struct AttnShared {
   float wl[AT_WAVES][AT_HEADS];
 };
 
-// One slice's gathered bytes for one lane: 64 B of an FP4 row plus its 8 scale bytes
-// (RawMain), or 128 B of a window row (RawWin). Absent items read as zeros.
+// Channel assignment: lane (item, g), g = lane / 16, holds channels 128i + 32g .. +31 for
+// i = 0..3, and its block j (8 channels) is channels 128(j/4) + 32g + 8(j%4) .. +7. Each
+// gather instruction then reads one contiguous 64-byte (FP4) or 128-byte (window) piece
+// per row across the item's four lanes, instead of four pieces spread over the row.
+//
+// One slice's gathered bytes for one lane: 64 B of an FP4 row plus the row's 32 scale
+// bytes (RawMain), or 128 B of a window row (RawWin). Absent items read as zeros.
 struct RawMain {
-  u32x4 v[4];
-  uint32_t sc0, sc1;
-  bool valid;   // the item exists
+  u32x4 v[4];    // v[i]: FP4 bytes 64i + 16g .. +15 = channels 128i + 32g .. +31
+  u32x4 sc[2];   // the row's 32 E4M3 group scales
+  bool valid;    // the item exists
 };
 struct RawWin {
-  u32x4 v[8];
+  u32x4 v[8];    // v[2i + h]: E4M3 bytes 128i + 32g + 16h .. +15
   bool valid;
 };
 
-// Converts the lane's 16 blocks (block j = channels 128*gq + 8j .. +7) to fp16, stores
-// them to its row quarter of the tile (tile_row) and accumulates the logits against the
-// query operand held in LDS. The format is a template parameter: the caller branches once
-// per slice (a wavefront-uniform choice), so the 16 blocks have no branch between them and
-// the operand reads can be issued ahead of the products.
-template <bool WINDOW, class R>
+// Converts the lane's 16 blocks to fp16, stores those of the tile quarters the workgroup
+// reads (quarters 0-1 if STORE_LO, 2-3 if STORE_HI) to the lane's place in the tile
+// (tile_row + TILE_QUARTER * (j/4) + 8 * (j%4) for block j), and accumulates the logits
+// against the query operand held in LDS. Format and stored quarters are template
+// parameters: the caller branches once per slice (wavefront-uniform choices), so the 16
+// blocks have no branch between them and the operand reads can be issued ahead of the
+// products. g is the lane's channel group (lane / 16).
+template <bool WINDOW, bool STORE_LO, bool STORE_HI, class R>
 __device__ __forceinline__ f32x4 convert_and_score(const R& r, const u32x4 (*qop)[64],
-                                                   int lane, uint16_t* tile_row) {
-  f16x2 sq[8];
+                                                   int lane, int g, uint16_t* tile_row) {
+  f16x2 sq[8];   // sq[m]: scale of blocks 2m, 2m+1 (group 8(m/2) + 2g + m%2), in both halves
   if constexpr (!WINDOW) {
-    const f16x2 s01 = e4m3x2_to_f16x2<false>(r.sc0), s23 = e4m3x2_to_f16x2<true>(r.sc0);
-    const f16x2 s45 = e4m3x2_to_f16x2<false>(r.sc1), s67 = e4m3x2_to_f16x2<true>(r.sc1);
-    sq[0] = f16x2{s01.x, s01.x}; sq[1] = f16x2{s01.y, s01.y};
-    sq[2] = f16x2{s23.x, s23.x}; sq[3] = f16x2{s23.y, s23.y};
-    sq[4] = f16x2{s45.x, s45.x}; sq[5] = f16x2{s45.y, s45.y};
-    sq[6] = f16x2{s67.x, s67.x}; sq[7] = f16x2{s67.y, s67.y};
+    // Groups 8i + 2g and 8i + 2g + 1 are the 16-bit half (g % 2) of scale dword 2i + g/2.
+    const int shift = 16 * (g & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (g & 2) ? r.sc[i >> 1][2 * (i & 1) + 1] : r.sc[i >> 1][2 * (i & 1)];
+      const f16x2 s2 = e4m3x2_to_f16x2<false>(lo >> shift);
+      sq[2 * i] = f16x2{s2.x, s2.x};
+      sq[2 * i + 1] = f16x2{s2.y, s2.y};
+    }
   }
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
   // The operand of block j + QLEAD is read while block j is converted and multiplied.
@@ -122,11 +134,14 @@ __device__ __forceinline__ f32x4 convert_and_score(const R& r, const u32x4 (*qop
   for (int j = 0; j < 16; ++j) {
     if (j + QLEAD < 16) b[(j + QLEAD) % (QLEAD + 1)] = qop[j + QLEAD][lane];
     u32x4 a;
-    if constexpr (WINDOW)
-      a = fp8x8_to_f16x8(r.v[j >> 1][2 * (j & 1)], r.v[j >> 1][2 * (j & 1) + 1]);
-    else
+    if constexpr (WINDOW) {
+      const u32x4& w = r.v[2 * (j >> 2) + ((j & 3) >> 1)];
+      a = fp8x8_to_f16x8(w[2 * (j & 1)], w[2 * (j & 1) + 1]);
+    } else {
       a = fp4x8_to_f16x8(r.v[j >> 2][j & 3], sq[j >> 1]);
-    *reinterpret_cast<u32x4*>(tile_row + 8 * j) = a;
+    }
+    if ((j < 8 && STORE_LO) || (j >= 8 && STORE_HI))
+      *reinterpret_cast<u32x4*>(tile_row + TILE_QUARTER * (j >> 2) + 8 * (j & 3)) = a;
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
         __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b[j % (QLEAD + 1)]), sacc, 0,
         0, 0);
@@ -192,12 +207,12 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   else
     pX = position(c0 + AT_WAVES);
 
-  // This wavefront's two k-steps of the logit B operand: Q^T for head h, channels
-  // 8*ks + 128*gq .. +7 with ks = 2*wave, 2*wave + 1 (the conversion produces the rows
-  // with the same channel assignment).
-  const uint16_t* qrow = q + ((int64_t)t * 64 + h) * 512 + 128 * gq;
-  const u32x4 qr0 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave));
-  const u32x4 qr1 = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * wave + 1));
+  // This wavefront's two k-steps of the logit B operand: Q^T for head h, the channels of
+  // blocks j = 2*wave, 2*wave + 1 of channel group gq (the assignment of the gathers).
+  const uint16_t* qrow = q + ((int64_t)t * 64 + h) * 512 + 32 * gq + 128 * (wave >> 1) +
+                         16 * (wave & 1);
+  const u32x4 qr0 = *reinterpret_cast<const u32x4*>(qrow);
+  const u32x4 qr1 = *reinterpret_cast<const u32x4*>(qrow + 8);
 
   // The per-query scalars come through vector loads issued beside the query and position
   // loads, so their latency overlaps with those; as scalar loads they would be waited for
@@ -258,10 +273,9 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     raw.valid = ok;
     const int ridx = ok ? p : (int)ABSENT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw.v[i] = sbuf_load_b128(rs_kv, ridx, 64 * gq + 16 * i, 0, 0);
-    const u32x2 s8 = sbuf_load_b64(rs_sc, ridx, 8 * gq, 0, 0);
-    raw.sc0 = s8.x;
-    raw.sc1 = s8.y;
+    for (int i = 0; i < 4; ++i) raw.v[i] = sbuf_load_b128(rs_kv, ridx, 64 * i + 16 * gq, 0, 0);
+    raw.sc[0] = sbuf_load_b128(rs_sc, ridx, 0, 0, 0);
+    raw.sc[1] = sbuf_load_b128(rs_sc, ridx, 16, 0, 0);
   };
   // Window slice w (rows 16w .. 16w+15 of the query's window) belongs to wavefront w.
   auto fetch_win = [&](RawWin& raw) {
@@ -271,7 +285,8 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
     raw.valid = ok;
     const int ridx = ok ? wi : (int)ABSENT;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) raw.v[i] = sbuf_load_b128(rs_win, ridx, 128 * gq + 16 * i, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      raw.v[i] = sbuf_load_b128(rs_win, ridx, 128 * (i >> 1) + 32 * gq + 16 * (i & 1), 0, 0);
   };
 
   const int qexp = qmax > 0.f ? (int)((__float_as_uint(qmax) >> 23) & 0xFFu) - 127 : 0;
@@ -318,7 +333,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   bool ok_pass = true;               // no logit of this pass overflowed the reference
   float l_run = 0.f;                 // this lane's share of the sum for head col
   uint16_t* const tile = sh.tile[wave];
-  uint16_t* const tile_w = tile + TILE_ROW * col + TILE_QUARTER * gq;
+  uint16_t* const tile_w = tile + TILE_ROW * col + 32 * gq;
   // Transpose reads start at this workgroup's first channel quarter (2*dh).
   const uint16_t* const tile_r =
       tile + TILE_ROW * (4 * gq + (col >> 2)) + 4 * (col & 3) + TILE_QUARTER * (2 * dh);
@@ -373,17 +388,27 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
   // of the slice NBUF steps later in this wavefront's sequence (c + NBUF*AT_WAVES), whose
   // gather starts as soon as this slice's registers are free. A slice with no item
   // converts nothing; only its next gather starts.
+  // Conversion and logits of a slice, storing only the tile quarters this workgroup reads.
+  auto convert_stored = [&](auto window, const auto& raw) -> f32x4 {
+    constexpr bool W = decltype(window)::value;
+    if constexpr (HALVES == 1)
+      return convert_and_score<W, true, true>(raw, sh.qop, lane, gq, tile_w);
+    else if (dh == 0)
+      return convert_and_score<W, true, false>(raw, sh.qop, lane, gq, tile_w);
+    else
+      return convert_and_score<W, false, true>(raw, sh.qop, lane, gq, tile_w);
+  };
   auto step_main = [&](int c, RawMain& raw, int32_t pn) {
     const uint64_t valid = __ballot(raw.valid);   // bit e: item e of the slice is present
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    if (valid != 0ull) sacc = convert_and_score<false>(raw, sh.qop, lane, tile_w);
+    if (valid != 0ull) sacc = convert_stored(std::false_type{}, raw);
     fetch_main(c + NBUF * AT_WAVES, pn, raw);
     if (valid != 0ull) finish(valid, sacc);
   };
   auto step_win = [&]() {
     const uint64_t valid = __ballot(rw.valid);
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    if (valid != 0ull) sacc = convert_and_score<true>(rw, sh.qop, lane, tile_w);
+    if (valid != 0ull) sacc = convert_stored(std::true_type{}, rw);
     if constexpr (NBUF == 1) fetch_main(c0, p0, bufA);
     if (valid != 0ull) finish(valid, sacc);
   };
