@@ -10,9 +10,10 @@ captured once into a HIP graph and replayed; W untimed replays, then K timed rep
 bracketed by device synchronisation. Inputs are seeded synthetic tensors already resident
 in HBM. Prints one JSON line.
 
-roofline: the dominant kernel is the Full-layer indexer. Its algorithmic bytes per launch
-are 128 B of indexer K read + 4 B of score and 0.5 B of block maximum written per
-(query, entry) pair, plus the indexer queries and weights; its average launch duration is
+roofline: the dominant kernel is the Full-layer indexer, launched as the step launches it.
+Its algorithmic bytes per launch are 128 B of indexer K read + 0.5 B of block maximum
+written per (query, entry) pair (+ 4 B of score where the step keeps the scores: stacks
+without a pool), plus the indexer queries and weights; its average launch duration is
 measured with HIP events on its own stream over K back-to-back launches.
 
 roofline.traffic: HBM bytes per indexer launch from rocprofv3 counters (FETCH_SIZE and
@@ -65,15 +66,21 @@ def measured_traffic(workload):
         return None
 
 
+def full_indexer(wl, buf, C, stream=None):
+    """The Full-layer indexer as the step launches it: block maxima only in a pooled stack."""
+    full = wl.layers[0]
+    C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                       None if wl.with_pool else buf.scores, buf.block_max,
+                       ld_scores=buf.scores.shape[1], stream=stream)
+
+
 def profile_kernels(wl, buf, C, launches):
     """Only the Full-layer indexer and a plain copy of COPY_BYTES, for counter collection."""
     import torch
-    full = wl.layers[0]
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(launches):
-        C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
-                           buf.scores, buf.block_max)
+        full_indexer(wl, buf, C)
         torch.neg(src, out=dst)   # reads and writes COPY_BYTES each
     torch.cuda.synchronize()
     print(f"[bench] profile launches done: {launches} x (indexer, copy of {COPY_BYTES} B)",
@@ -100,7 +107,8 @@ def algorithmic_bytes(wl, k=512):
 def indexer_bytes_per_launch(wl):
     import torch
     pairs = int(wl.n_visible.to(torch.int64).sum())
-    return pairs * (128 + 4 + 0.5) + wl.n_q * (32 * 128 * 2 + 32 * 4)
+    written = 0.5 if wl.with_pool else 4 + 0.5
+    return pairs * (128 + written) + wl.n_q * (32 * 128 * 2 + 32 * 4)
 
 
 def cpu_baseline(wl, target_s, max_q):
@@ -220,16 +228,13 @@ def main():
           f"{wall / args.steps * 1e6:.1f} us/step)", file=sys.stderr, flush=True)
 
     # Dominant kernel: the Full-layer indexer, launched back to back on `stream`.
-    full = wl.layers[0]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
-                           buf.scores, buf.block_max, stream=stream)
+        full_indexer(wl, buf, C, stream=stream)
         e0.record(stream)
         for _ in range(args.steps):
-            C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start,
-                               wl.n_visible, buf.scores, buf.block_max, stream=stream)
+            full_indexer(wl, buf, C, stream=stream)
         e1.record(stream)
     torch.cuda.synchronize()
     idx_us = e0.elapsed_time(e1) * 1e3 / args.steps
@@ -241,20 +246,22 @@ def main():
         evs = []
         with torch.cuda.stream(stream):
             for li, lay in enumerate(wl.layers):
-                for part in ("score", "pool", "topk", "attn"):
+                for part in ("score", "pool", "rescore", "topk", "attn"):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
                     if part == "score" and lay.mode == "full":
-                        C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                           wl.n_visible, buf.scores, buf.block_max, stream=stream)
+                        full_indexer(wl, buf, C, stream=stream)
+                    elif part == "rescore" and lay.mode == "full" and wl.with_pool:
+                        C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                           wl.n_visible, buf.re_scores, None,
+                                           pool_blocks=buf.pool, stream=stream)
                     elif part == "score" and lay.mode == "reindex":
                         C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
                                            wl.n_visible, buf.re_scores, None,
                                            pool_blocks=buf.pool, stream=stream)
                     elif part == "topk" and lay.mode == "full" and wl.with_pool:
-                        C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
-                                    pool_blocks=buf.pool, pool_use=C.POOL_CANDIDATES,
+                        C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
                                     stream=stream)
                     elif part == "topk" and lay.mode == "full":
                         C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
@@ -304,7 +311,8 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
-                     "kernel": "index_score_kernel<false> (Full-layer indexer)",
+                     "kernel": "index_score_kernel<false> (Full-layer indexer"
+                               + (", block maxima only)" if wl.with_pool else ")"),
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,
     }

@@ -83,16 +83,21 @@ def workspace_bytes(op: int, n_q: int, max_cols: int, k: int) -> int:
 
 
 def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block_max=None,
-                     pool_blocks=None, stream=None):
-    """Indexer scores into `scores` [n_q, ld] (and block maxima into `block_max`)."""
+                     pool_blocks=None, stream=None, ld_scores=None):
+    """Indexer scores into `scores` [n_q, ld] (and block maxima into `block_max`). With
+    scores=None (FULL mode only) just the block maxima of ld_scores slots are written."""
     n_q = q_idx.shape[0]
     n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
+    if scores is not None:
+        ld_scores = scores.shape[1]
+    elif ld_scores is None:
+        raise ValueError("csa2_index_score: ld_scores is required when scores is None")
     _check(lib.csa2_index_score(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
-        _ptr(scores, torch.float32, "scores"), scores.shape[1],
+        _ptr(scores, torch.float32, "scores"), ld_scores,
         _ptr(block_max, torch.float32, "block_max"),
         block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 

@@ -72,8 +72,10 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const vo
           "csa2_index_score: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
   REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_q %d out of range", n_q);
   if (n_q == 0) return ok();
-  REQUIRE(q_idx && w && k_cache && kv_start && n_visible && scores, CSA2_ERR_INVALID_ARG,
+  REQUIRE(q_idx && w && k_cache && kv_start && n_visible, CSA2_ERR_INVALID_ARG,
           "csa2_index_score: null pointer argument");
+  REQUIRE(scores != nullptr || (mode == CSA2_FULL && block_max != nullptr), CSA2_ERR_INVALID_ARG,
+          "csa2_index_score: scores may be NULL only in FULL mode with block_max");
   REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_entries < 0");
   REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
           "csa2_index_score: ld_scores %lld out of range", (long long)ld_scores);

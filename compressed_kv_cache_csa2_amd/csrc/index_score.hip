@@ -15,7 +15,8 @@
 // lane (row = 8*(r/4) + 4*half + r%4, column = l%32); ReLU, the per-head weight and the
 // sum over heads happen in registers plus one cross-half shuffle. Scores and optional
 // 8-slot block maxima are kept in registers and written with coalesced stores after the
-// workgroup's rows have been read. Work per step is 8,192 flops per position against 128
+// workgroup's rows have been read; a Full pass may write the block maxima alone (the 4-byte
+// score stores cost about a tenth of the pass's time against 3% of its bytes). Work per step is 8,192 flops per position against 128
 // bytes read: HBM-bound at 64 flop/B.
 #include "csa2_device.h"
 #include "csa2_launch.h"
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
   for (int step = 0; step < IS_STEPS_PER_WAVE; ++step) {
     const int64_t slot = slot_at(step);
     const float sv = sc[step];
-    if (slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+    if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
     if (block_max != nullptr) {
       float m = sv;
       m = fmaxf(m, __shfl_xor(m, 1));

@@ -1,6 +1,8 @@
 """Mode routing of CSA2 layers over the C ABI (caller side: buffers only, no arithmetic).
 
-Full:    index_score(FULL) -> topk (+ block_pool in the decoder's first layer) -> sparse_attn
+Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_score(FULL, block
+         maxima only) -> block_pool -> index_score over the pool with the same query -> topk
+         among the pool's slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
 ("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression", 2.3.2 and 3.3.3;
@@ -53,14 +55,23 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
     current = None
     for li, lay in enumerate(wl.layers):
         if lay.mode == "full":
-            C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
-                               buf.scores, buf.block_max, stream=stream)
             if wl.with_pool:
-                # The pool holds every Full-layer winner, so the Top-K examines only its slots;
-                # one kernel selects both.
-                C.csa2_pool_topk(buf.block_max, wl.n_visible, buf.pool, buf.scores, buf.idx[li],
-                                 n_keep=POOL_BLOCKS, k=k, stream=stream)
+                # Decoder Full layer: the pass over the whole context writes only the block
+                # maxima; the pool holds every Full-layer winner, so the Top-K is taken over
+                # the pool's slots, rescored with this layer's own indexer query (the same
+                # scores, bit for bit, at 2 MiB of reads per query).
+                C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                   wl.n_visible, None, buf.block_max,
+                                   ld_scores=buf.scores.shape[1], stream=stream)
+                C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, n_keep=POOL_BLOCKS,
+                                  stream=stream)
+                C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                   wl.n_visible, buf.re_scores, None, pool_blocks=buf.pool,
+                                   stream=stream)
+                C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
             else:
+                C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
+                                   wl.n_visible, buf.scores, buf.block_max, stream=stream)
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
                             block_max=buf.block_max, stream=stream)
             current = buf.idx[li]

@@ -103,11 +103,15 @@ size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);
  *   kv_start [n_q] int64 first cache row of query t's sequence; n_visible [n_q] int32.
  *   pool_blocks [n_q,n_pool] int32 (REINDEX), block ids with -1 padding.
  *   block_size          must be 8.
- *   scores   [n_q,ld_scores] f32 output.
+ *   scores   [n_q,ld_scores] f32 output. May be NULL in FULL mode when block_max is
+ *       given: only the block maxima are written (ld_scores still sets the slot range).
+ *       A decoder Full layer needs no more: its Top-K lies inside the pool, whose slots
+ *       a REINDEX call with the same q_idx and w scores bit-identically.
  *   block_max [n_q,ld_block_max] f32 output, may be NULL: block_max[t,b] is the max of
  *       scores[t, 8b .. 8b+7] over the slots that exist; requires
  *       ld_block_max >= ceil(ld_scores/8). These maxima are what csa2_block_pool ranks,
- *       and csa2_topk uses them to skip blocks that cannot hold a winner. */
+ *       and csa2_topk uses them to skip blocks that cannot hold a winner.
+ * Errors: CSA2_ERR_INVALID_ARG for NULL scores outside that case. */
 int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                      const void* q_idx, const float* w,
                      const void* k_cache, int64_t n_entries,

@@ -51,6 +51,10 @@ def test_index_score_rejections(C):
     assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2048, ld=100) == 1
     assert _score(C, pool_blocks=FAKE, n_pool=4) == 1     # FULL with a pool
     assert _score(C, block_max=FAKE, ld_bm=1) == 1        # ld_bm < ceil(16/8)
+    assert _score(C, scores=None) == 1                    # no scores and no block maxima
+    assert b"only in FULL mode with block_max" in C.lib.csa2_last_error()
+    assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2, scores=None,
+                  block_max=FAKE, ld_bm=2) == 1           # REINDEX always writes scores
     assert _score(C, n_q=0, q_idx=None) == 0              # nothing to do, nothing launched
 
 

@@ -98,6 +98,12 @@ def test_index_score_full_parity(C, dev, case):
     pad = np.full((wl.n_q, bmax.shape[1] * 8), -np.inf, np.float32)
     pad[:, :ld] = got
     assert np.array_equal(bmax.cpu().numpy(), pad.reshape(wl.n_q, -1, 8).max(axis=2))
+    # without a score buffer the same pass writes the same block maxima and nothing else
+    bmax2 = torch.full_like(bmax, 7.0)
+    C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, None,
+                       bmax2, ld_scores=ld)
+    torch.cuda.synchronize()
+    assert torch.equal(bmax2, bmax)
 
 
 def test_index_score_reindex_parity(C, dev):
