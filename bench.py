@@ -67,11 +67,11 @@ def measured_traffic(workload):
 
 
 def full_indexer(wl, buf, C, stream=None):
-    """The Full-layer indexer as the step launches it: block maxima only in a pooled stack."""
-    full = wl.layers[0]
-    C.csa2_index_score(C.FULL, full.q_idx, full.w, wl.k_cache, wl.kv_start, wl.n_visible,
-                       None if wl.with_pool else buf.scores, buf.block_max,
-                       ld_scores=buf.scores.shape[1], stream=stream)
+    """The Full-layer indexer as the step launches it: block maxima only in a pooled stack,
+    over the workload's key format."""
+    from compressed_kv_cache_csa2_amd import layers
+    layers.index_score(wl, C.FULL, wl.layers[0], None if wl.with_pool else buf.scores,
+                       buf.block_max, ld_scores=buf.scores.shape[1], stream=stream)
 
 
 def profile_kernels(wl, buf, C, launches):
@@ -96,19 +96,24 @@ def algorithmic_bytes(wl, k=512):
     total = 0
     for lay in wl.layers:
         if lay.mode == "full":
-            total += int(nv.sum()) * 128
+            total += int(nv.sum()) * key_bytes(wl)
         elif lay.mode == "reindex":
-            total += int(torch.clamp(nv, max=16384).sum()) * 128
+            total += int(torch.clamp(nv, max=16384).sum()) * key_bytes(wl)
         sel = torch.clamp(nv, max=k)
         total += int(sel.sum()) * 288 + wl.n_q * (128 * 512 + 2 * 64 * 512 * 2)
     return total
+
+
+def key_bytes(wl):
+    """Bytes of one indexer-key row: 128 (E4M3) or 64 + 4 (MXFP4)."""
+    return 68 if wl.k_codes is not None else 128
 
 
 def indexer_bytes_per_launch(wl):
     import torch
     pairs = int(wl.n_visible.to(torch.int64).sum())
     written = 0.5 if wl.with_pool else 4 + 0.5
-    return pairs * (128 + written) + wl.n_q * (32 * 128 * 2 + 32 * 4)
+    return pairs * (key_bytes(wl) + written) + wl.n_q * (32 * 128 * 2 + 32 * 4)
 
 
 def cpu_baseline(wl, target_s, max_q):
@@ -133,14 +138,16 @@ def cpu_baseline(wl, target_s, max_q):
         idx = pool = None
         for lay in seq["layers"]:
             if lay["mode"] == "full":
-                r = O.full_layer(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, lay["q"],
-                                 seq["kv_fp4"], seq["kv_scale"], lay["window_kv"], 0, lay["n_swa"],
-                                 wl.softmax_scale, with_pool=wl.with_pool)
+                r = O.full_layer(lay["q_idx"], lay["w"], seq.get("k_codes", seq["k_cache"]), 0,
+                                 nv, lay["q"], seq["kv_fp4"], seq["kv_scale"], lay["window_kv"],
+                                 0, lay["n_swa"], wl.softmax_scale, with_pool=wl.with_pool,
+                                 k_scales=seq.get("k_scales"))
                 pool = r.get("pool")
             elif lay["mode"] == "reindex":
-                r = O.reindex_layer(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, pool, lay["q"],
-                                    seq["kv_fp4"], seq["kv_scale"], lay["window_kv"], 0,
-                                    lay["n_swa"], wl.softmax_scale)
+                r = O.reindex_layer(lay["q_idx"], lay["w"], seq.get("k_codes", seq["k_cache"]), 0,
+                                    nv, pool, lay["q"], seq["kv_fp4"], seq["kv_scale"],
+                                    lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale,
+                                    k_scales=seq.get("k_scales"))
             else:
                 r = O.reuse_layer(idx, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
                                   lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
@@ -253,12 +260,10 @@ def main():
                     if part == "score" and lay.mode == "full":
                         full_indexer(wl, buf, C, stream=stream)
                     elif part == "rescore" and lay.mode == "full" and wl.with_pool:
-                        C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                           wl.n_visible, buf.re_scores, None,
+                        layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
                                            pool_blocks=buf.pool, stream=stream)
                     elif part == "score" and lay.mode == "reindex":
-                        C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                           wl.n_visible, buf.re_scores, None,
+                        layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
                                            pool_blocks=buf.pool, stream=stream)
                     elif part == "topk" and lay.mode == "full" and wl.with_pool:
                         C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
@@ -305,13 +310,15 @@ def main():
         "config": {"workload": wl.name, "queries": wl.n_q, "context_entries": wl.n_ctx,
                    "layers": [l.mode for l in wl.layers], "index_topk": 512,
                    "sliding_window": 128, "pool_blocks": 2048 if wl.with_pool else 0,
+                   "indexer_keys": "mxfp4" if wl.k_codes is not None else "e4m3",
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
-                     "kernel": "index_score_kernel<false> (Full-layer indexer"
+                     "kernel": "index_score_kernel (Full-layer indexer"
+                               + (", MXFP4 keys" if wl.k_codes is not None else ", E4M3 keys")
                                + (", block maxima only)" if wl.with_pool else ")"),
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,

@@ -32,12 +32,13 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
     lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
     lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
-    for f in ("csa2_index_score", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
+    for f in ("csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
@@ -95,6 +96,29 @@ def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block
     _check(lib.csa2_index_score(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+        _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
+        _ptr(scores, torch.float32, "scores"), ld_scores,
+        _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visible, scores,
+                           block_max=None, pool_blocks=None, stream=None, ld_scores=None):
+    """csa2_index_score over MXFP4 indexer keys: k_codes uint8 [E, 64] (two E2M1 codes per
+    byte, low nibble first) and k_scales uint8 [E, 4] (E8M0, one per 32 channels)."""
+    n_q = q_idx.shape[0]
+    n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
+    if scores is not None:
+        ld_scores = scores.shape[1]
+    elif ld_scores is None:
+        raise ValueError("csa2_index_score_mxfp4: ld_scores is required when scores is None")
+    if k_codes.shape[0] != k_scales.shape[0]:
+        raise ValueError("csa2_index_score_mxfp4: k_codes and k_scales row counts differ")
+    _check(lib.csa2_index_score_mxfp4(
+        mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
+        _ptr(w, torch.float32, "w"), _ptr(k_codes, torch.uint8, "k_codes"),
+        _ptr(k_scales, torch.uint8, "k_scales"), k_codes.shape[0],
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
         _ptr(scores, torch.float32, "scores"), ld_scores,

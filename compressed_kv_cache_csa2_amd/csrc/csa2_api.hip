@@ -57,52 +57,82 @@ size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k) {
   return 0;
 }
 
+// Both indexer-key formats: k_scales is NULL for E4M3 keys and the E8M0 scale rows for
+// MXFP4 keys (whose codes are then k_cache). `fn` names the entry point in messages.
+static int index_score_common(const char* fn, csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+                              const void* q_idx, const float* w, const void* k_cache,
+                              const void* k_scales, int64_t n_entries, const int64_t* kv_start,
+                              const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
+                              int block_size, float* scores, int64_t ld_scores, float* block_max,
+                              int64_t ld_block_max, void* stream) {
+  REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
+          "%s: mode %d does no scoring (Reuse layers attend with published indices)", fn,
+          (int)mode);
+  REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
+          "%s: indexer shape %dx%d, only %dx%d is built", fn, n_heads, d_idx,
+          CSA2_IDX_HEADS, CSA2_IDX_DIM);
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
+  if (n_q == 0) return ok();
+  REQUIRE(q_idx && w && k_cache && kv_start && n_visible, CSA2_ERR_INVALID_ARG,
+          "%s: null pointer argument", fn);
+  REQUIRE(scores != nullptr || (mode == CSA2_FULL && block_max != nullptr), CSA2_ERR_INVALID_ARG,
+          "%s: scores may be NULL only in FULL mode with block_max", fn);
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "%s: n_entries < 0", fn);
+  REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "%s: ld_scores %lld out of range", fn, (long long)ld_scores);
+  REQUIRE(k_scales == nullptr || aligned(k_scales, 4), CSA2_ERR_INVALID_ARG,
+          "%s: k_scales must be 4-byte aligned", fn);
+  REQUIRE(aligned(q_idx, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
+          "%s: q_idx and k_cache must be 16-byte aligned", fn);
+  REQUIRE(aligned(w, 4) && aligned(scores, 4) && aligned(kv_start, 8) && aligned(n_visible, 4),
+          CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
+  if (mode == CSA2_REINDEX) {
+    REQUIRE(pool_blocks != nullptr, CSA2_ERR_INVALID_ARG, "%s: REINDEX needs pool_blocks", fn);
+    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+            "%s: n_pool %d out of range", fn, n_pool);
+    REQUIRE(ld_scores >= (int64_t)n_pool * block_size, CSA2_ERR_INVALID_ARG,
+            "%s: ld_scores %lld < n_pool*block_size", fn, (long long)ld_scores);
+  } else {
+    REQUIRE(pool_blocks == nullptr, CSA2_ERR_INVALID_ARG, "%s: FULL takes no pool_blocks", fn);
+  }
+  if (block_max != nullptr) {
+    REQUIRE(ld_block_max >= (ld_scores + 7) / 8, CSA2_ERR_INVALID_ARG,
+            "%s: ld_block_max %lld < ceil(ld_scores/8)", fn, (long long)ld_block_max);
+    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
+  }
+  return hip_status(csa2::launch_index_score(
+                        mode == CSA2_REINDEX, n_q, static_cast<const uint16_t*>(q_idx), w,
+                        static_cast<const uint8_t*>(k_cache),
+                        static_cast<const uint8_t*>(k_scales), n_entries, kv_start, n_visible,
+                        pool_blocks, mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
+                        ld_block_max, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
                      const float* w, const void* k_cache, int64_t n_entries,
                      const int64_t* kv_start, const int32_t* n_visible, const int32_t* pool_blocks,
                      int n_pool, int block_size, float* scores, int64_t ld_scores,
                      float* block_max, int64_t ld_block_max, void* stream) {
-  REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
-          "csa2_index_score: mode %d does no scoring (Reuse layers attend with published indices)",
-          (int)mode);
-  REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
-          "csa2_index_score: indexer shape %dx%d, only %dx%d is built", n_heads, d_idx,
-          CSA2_IDX_HEADS, CSA2_IDX_DIM);
-  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
-          "csa2_index_score: block_size %d, only %d is built", block_size, CSA2_CANDIDATE_BLOCK_SIZE);
-  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_q %d out of range", n_q);
-  if (n_q == 0) return ok();
-  REQUIRE(q_idx && w && k_cache && kv_start && n_visible, CSA2_ERR_INVALID_ARG,
-          "csa2_index_score: null pointer argument");
-  REQUIRE(scores != nullptr || (mode == CSA2_FULL && block_max != nullptr), CSA2_ERR_INVALID_ARG,
-          "csa2_index_score: scores may be NULL only in FULL mode with block_max");
-  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "csa2_index_score: n_entries < 0");
-  REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
-          "csa2_index_score: ld_scores %lld out of range", (long long)ld_scores);
-  REQUIRE(aligned(q_idx, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
-          "csa2_index_score: q_idx and k_cache must be 16-byte aligned");
-  REQUIRE(aligned(w, 4) && aligned(scores, 4) && aligned(kv_start, 8) && aligned(n_visible, 4),
-          CSA2_ERR_INVALID_ARG, "csa2_index_score: misaligned argument");
-  if (mode == CSA2_REINDEX) {
-    REQUIRE(pool_blocks != nullptr, CSA2_ERR_INVALID_ARG, "csa2_index_score: REINDEX needs pool_blocks");
-    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
-            "csa2_index_score: n_pool %d out of range", n_pool);
-    REQUIRE(ld_scores >= (int64_t)n_pool * block_size, CSA2_ERR_INVALID_ARG,
-            "csa2_index_score: ld_scores %lld < n_pool*block_size", (long long)ld_scores);
-  } else {
-    REQUIRE(pool_blocks == nullptr, CSA2_ERR_INVALID_ARG, "csa2_index_score: FULL takes no pool_blocks");
-  }
-  if (block_max != nullptr) {
-    REQUIRE(ld_block_max >= (ld_scores + 7) / 8, CSA2_ERR_INVALID_ARG,
-            "csa2_index_score: ld_block_max %lld < ceil(ld_scores/8)", (long long)ld_block_max);
-    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "csa2_index_score: misaligned block_max");
-  }
-  return hip_status(csa2::launch_index_score(
-                        mode == CSA2_REINDEX, n_q, static_cast<const uint16_t*>(q_idx), w,
-                        static_cast<const uint8_t*>(k_cache), n_entries, kv_start, n_visible,
-                        pool_blocks, mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
-                        ld_block_max, static_cast<hipStream_t>(stream)),
-                    "csa2_index_score");
+  return index_score_common("csa2_index_score", mode, n_q, n_heads, d_idx, q_idx, w, k_cache,
+                            nullptr, n_entries, kv_start, n_visible, pool_blocks, n_pool,
+                            block_size, scores, ld_scores, block_max, ld_block_max, stream);
+}
+
+int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
+                           const float* w, const void* k_codes, const void* k_scales,
+                           int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
+                           const int32_t* pool_blocks, int n_pool, int block_size, float* scores,
+                           int64_t ld_scores, float* block_max, int64_t ld_block_max,
+                           void* stream) {
+  REQUIRE(n_q == 0 || k_scales != nullptr, CSA2_ERR_INVALID_ARG,
+          "csa2_index_score_mxfp4: null k_scales");
+  return index_score_common("csa2_index_score_mxfp4", mode, n_q, n_heads, d_idx, q_idx, w,
+                            k_codes, k_scales, n_entries, kv_start, n_visible, pool_blocks,
+                            n_pool, block_size, scores, ld_scores, block_max, ld_block_max,
+                            stream);
 }
 
 int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,

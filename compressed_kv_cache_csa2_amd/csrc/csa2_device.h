@@ -68,6 +68,19 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
   return r;
 }
 
+// Eight E2M1 codes of one dword (low nibble first) times a power-of-two scale -> eight
+// bf16 packed in four dwords. The conversion applies the exponent of `pow2` exactly, so an
+// E8M0 scale 2^(e-127) passed as the float with exponent field e gives exact products while
+// they stay in bf16's normal range.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8_pow2(uint32_t codes, float pow2) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, pow2, 3));
+  return r;
+}
+
 // ---- fp16 forms (the attention works in fp16: every E2M1 x E4M3 product, and every E4M3
 // value, is exact in fp16, and packed fp16 multiplies halve the conversion work) ----
 

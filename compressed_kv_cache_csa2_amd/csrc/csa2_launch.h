@@ -8,8 +8,11 @@
 
 namespace csa2 {
 
+// k_scales: NULL for E4M3 indexer keys ([E,128]); the E8M0 scale rows ([E,4]) for MXFP4
+// keys, whose codes ([E,64]) are then k_cache.
 hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
+                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
+                              const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream);

@@ -16,7 +16,15 @@
 // sum over heads happen in registers plus one cross-half shuffle. Scores and optional
 // 8-slot block maxima are kept in registers and written with coalesced stores after the
 // workgroup's rows have been read; a Full pass may write the block maxima alone (the 4-byte
-// score stores cost about a tenth of the pass's time against 3% of its bytes). Work per step is 8,192 flops per position against 128
+// score stores cost about a tenth of the pass's time against 3% of its bytes).
+//
+// Indexer keys come in one of two formats: E4M3 rows of 128 bytes, or MXFP4 rows (the
+// OCP microscaling format the pages name for the indexer cache, "DeepSeek-v4.1 Flash:
+// Pushing the Limits of KV Cache Compression", 2.4.4 and 3.1): 64 bytes of E2M1 codes
+// (channel 2m in the low nibble of byte m) and 4 E8M0 scale bytes, one per 32 channels.
+// An MXFP4 lane reads 32 bytes of codes (its 64 channels) and the row's scale word, and
+// converts with the hardware E2M1 -> bf16 conversion whose scale operand is the E8M0
+// scale as a power of two: exact while the products stay in bf16's normal range. Work per step is 8,192 flops per position against 128
 // bytes read: HBM-bound at 64 flop/B.
 #include "csa2_device.h"
 #include "csa2_launch.h"
@@ -31,10 +39,10 @@ constexpr int IS_STEPS_FULL = 16;
 constexpr int IS_STEPS_REINDEX = 4;
 constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is multiplied
 
-template <bool REINDEX>
+template <bool REINDEX, bool FP4K>
 __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint8_t* __restrict__ k_cache, int64_t n_entries,
+    const uint8_t* __restrict__ k_cache, const uint8_t* __restrict__ k_scales, int64_t n_entries,
     const int64_t* __restrict__ kv_start, const int32_t* __restrict__ n_visible,
     const int32_t* __restrict__ pool_blocks, int n_pool,
     float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
@@ -91,13 +99,23 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     return REINDEX ? rows[REINDEX ? step : 0] : row_of(step, sl);
   };
   auto slot_at = [&](int step) -> int64_t { return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n; };
+  // E4M3: raw[0..3] = bytes 64*half .. +63 of the row. MXFP4: raw[0..1] = code bytes
+  // 32*half .. +31 (channels 64*half .. +63) and raw[2].x = the row's four scale bytes.
   u32x4 buf[NB][4];
   float sc[IS_STEPS_PER_WAVE];
   auto load_step = [&](int step, u32x4 (&raw)[4]) {
     const int64_t r = row_at(step);
-    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : base) * 128 + 64 * half);
+    const int64_t rr = r >= 0 ? r : base;
+    if constexpr (FP4K) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 64 + 32 * half);
+      raw[0] = p[0];
+      raw[1] = p[1];
+      raw[2].x = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
+    } else {
+      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 128 + 64 * half);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+      for (int i = 0; i < 4; ++i) raw[i] = p[i];
+    }
   };
   if (any) {
 #pragma unroll
@@ -113,11 +131,17 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const uint32_t d0 = raw[kb >> 1][(kb & 1) * 2];
-        const uint32_t d1 = raw[kb >> 1][(kb & 1) * 2 + 1];
-        const u32x2 lo = e4m3x4_to_bf16x4(d0);
-        const u32x2 hi = e4m3x4_to_bf16x4(d1);
-        const u32x4 bv = {lo.x, lo.y, hi.x, hi.y};
+        u32x4 bv;
+        if constexpr (FP4K) {
+          // channels 64*half + 8*kb .. +7: code dword kb, scale group 2*half + kb/4
+          const uint32_t d = raw[kb >> 2][kb & 3];
+          const uint32_t e = (raw[2].x >> (8 * (2 * half + (kb >> 2)))) & 0xFFu;
+          bv = fp4x8_to_bf16x8_pow2(d, __uint_as_float(e << 23));
+        } else {
+          const u32x2 lo = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2]);
+          const u32x2 hi = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2 + 1]);
+          bv = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
                                                       0, 0, 0);
       }
@@ -148,21 +172,24 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
 }
 
 hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
+                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
+                              const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream) {
   const int tile = (IS_THREADS / 64) * (reindex ? IS_STEPS_REINDEX : IS_STEPS_FULL) * 32;
   const int64_t tiles = (ld + tile - 1) / tile;
   dim3 grid((unsigned)tiles, (unsigned)n_q);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w, k_cache, k_scales,
+                       n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld, block_max,
+                       ld_bm);
+  };
+  const bool fp4 = k_scales != nullptr;
   if (reindex)
-    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
-                       k_cache, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
-                       block_max, ld_bm);
+    fp4 ? go(index_score_kernel<true, true>) : go(index_score_kernel<true, false>);
   else
-    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
-                       k_cache, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
-                       block_max, ld_bm);
+    fp4 ? go(index_score_kernel<false, true>) : go(index_score_kernel<false, false>);
   return hipGetLastError();
 }
 

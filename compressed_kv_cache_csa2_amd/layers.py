@@ -50,6 +50,19 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
     )
 
 
+def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
+                stream=None):
+    """The indexer over the workload's keys: MXFP4 when it carries them, else E4M3."""
+    if wl.k_codes is not None:
+        C.csa2_index_score_mxfp4(mode, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                                 wl.n_visible, scores, block_max, pool_blocks=pool_blocks,
+                                 stream=stream, ld_scores=ld_scores)
+    else:
+        C.csa2_index_score(mode, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                           scores, block_max, pool_blocks=pool_blocks, stream=stream,
+                           ld_scores=ld_scores)
+
+
 def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
     """One pass of the whole layer stack of the workload (one decode or prefill step)."""
     current = None
@@ -60,24 +73,20 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
                 # maxima; the pool holds every Full-layer winner, so the Top-K is taken over
                 # the pool's slots, rescored with this layer's own indexer query (the same
                 # scores, bit for bit, at 2 MiB of reads per query).
-                C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                   wl.n_visible, None, buf.block_max,
-                                   ld_scores=buf.scores.shape[1], stream=stream)
+                index_score(wl, C.FULL, lay, None, buf.block_max,
+                            ld_scores=buf.scores.shape[1], stream=stream)
                 C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, n_keep=POOL_BLOCKS,
                                   stream=stream)
-                C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                   wl.n_visible, buf.re_scores, None, pool_blocks=buf.pool,
-                                   stream=stream)
+                index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool,
+                            stream=stream)
                 C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
             else:
-                C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start,
-                                   wl.n_visible, buf.scores, buf.block_max, stream=stream)
+                index_score(wl, C.FULL, lay, buf.scores, buf.block_max, stream=stream)
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
                             block_max=buf.block_max, stream=stream)
             current = buf.idx[li]
         elif lay.mode == "reindex":
-            C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
-                               buf.re_scores, None, pool_blocks=buf.pool, stream=stream)
+            index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool, stream=stream)
             C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
             current = buf.idx[li]
         elif lay.mode != "reuse":

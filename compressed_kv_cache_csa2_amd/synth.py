@@ -66,6 +66,9 @@ class Workload:
     with_pool: bool = False
     planted: torch.Tensor | None = None  # int64 [n_q, n_plant] positions (or None)
     softmax_scale: float = SOFTMAX_SCALE
+    # MXFP4 copy of the indexer keys (the same draws): codes [E, 64], E8M0 scales [E, 4]
+    k_codes: torch.Tensor | None = None
+    k_scales: torch.Tensor | None = None
 
     @property
     def n_entries(self) -> int:
@@ -81,7 +84,8 @@ class Workload:
                         n_visible=mv(self.n_visible), k_cache=mv(self.k_cache),
                         kv_fp4=mv(self.kv_fp4), kv_scale=mv(self.kv_scale), layers=layers,
                         with_pool=self.with_pool, planted=self.planted,
-                        softmax_scale=self.softmax_scale)
+                        softmax_scale=self.softmax_scale, k_codes=mv(self.k_codes),
+                        k_scales=mv(self.k_scales))
 
 
 # ----------------------------------------------------------------------------- encoders
@@ -114,15 +118,42 @@ def encode_fp4_rows(x: torch.Tensor):
     s_code = encode_e4m3(amax / 6.0)
     s = _e4m3_bytes_to_float(s_code)
     safe = torch.where(s > 0, s, torch.ones_like(s))
-    a = (g / safe.unsqueeze(-1)).abs()
+    code = _e2m1_codes(g / safe.unsqueeze(-1))
+    code = torch.where((s > 0).unsqueeze(-1), code, torch.zeros_like(code))
+    code = code.reshape(x.shape)
+    payload = code[..., 0::2] | (code[..., 1::2] << 4)
+    return payload.contiguous(), s_code.contiguous()
+
+
+def _e2m1_codes(y: torch.Tensor) -> torch.Tensor:
+    """E2M1 codes of y: nearest grid magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the
+    even code, saturating at 6; the sign bit only on nonzero codes."""
+    a = y.abs()
     code = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8) + (a > 1.25).to(torch.uint8)
             + (a >= 1.75).to(torch.uint8) + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
             + (a > 5.0).to(torch.uint8))
-    code = torch.where((s > 0).unsqueeze(-1), code, torch.zeros_like(code))
-    sign = ((g < 0) & (code > 0)).to(torch.uint8) << 3
-    code = (code | sign).reshape(x.shape)
-    payload = code[..., 0::2] | (code[..., 1::2] << 4)
-    return payload.contiguous(), s_code.contiguous()
+    sign = ((y < 0) & (code > 0)).to(torch.uint8) << 3
+    return code | sign
+
+
+def encode_mxfp4_rows(x: torch.Tensor):
+    """Encode rows of 128 values in OCP MXFP4: E2M1 codes with one E8M0 scale per 32.
+
+    Per group of 32 (the OCP microscaling recipe): shared exponent X = floor(log2 amax) - 2
+    (2 is E2M1's largest exponent), scale byte X + 127 kept in 1..254; each value x / 2^X
+    goes to the E2M1 grid (nearest, ties to the even code, saturating at 6). An all-zero
+    group gets scale byte 127 and zero codes. Codes 2m and 2m+1 share byte m, low nibble
+    first. Returns (codes uint8 [..., 64], scales uint8 [..., 4]).
+    """
+    x = x.float()
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // 32, 32)
+    amax = g.abs().amax(dim=-1)
+    e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2
+    code_s = torch.where(amax > 0, e + 127, torch.full_like(e, 127.0)).clamp(1, 254)
+    scale = torch.exp2(code_s - 127)
+    code = _e2m1_codes(g / scale.unsqueeze(-1)).reshape(x.shape)
+    codes = code[..., 0::2] | (code[..., 1::2] << 4)
+    return codes.contiguous(), code_s.to(torch.uint8).contiguous()
 
 
 # ----------------------------------------------------------------------------- random draws
@@ -167,9 +198,12 @@ def _make_layer(mode, n_q, device, seed, li, window_rows=None, swa_start=None, n
 
 
 def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, plant_pos,
-                    full_layer: LayerInputs):
-    """Draw the indexer-K and latent rows of every sequence, planting at plant_pos."""
+                    full_layer: LayerInputs, mxfp4=False):
+    """Draw the indexer-K and latent rows of every sequence, planting at plant_pos. With
+    mxfp4 the indexer keys are also encoded in MXFP4 (from the same draws)."""
     k_cache = torch.zeros((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
+    k_codes = torch.zeros((n_entries, IDX_DIM // 2), dtype=torch.uint8, device=device) if mxfp4 else None
+    k_scales = torch.full((n_entries, IDX_DIM // 32), 127, dtype=torch.uint8, device=device) if mxfp4 else None
     kv_fp4 = torch.zeros((n_entries, HEAD_DIM // 2), dtype=torch.uint8, device=device)
     kv_scale = torch.zeros((n_entries, HEAD_DIM // 16), dtype=torch.uint8, device=device)
     starts = kv_start.tolist()
@@ -190,14 +224,18 @@ def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, pl
             k[pos] += PLANT_SHIFT * u
             lat[pos] += PLANT_SHIFT * v
         k_cache[start:start + n] = encode_e4m3(k)
+        if mxfp4:
+            kc, ks = encode_mxfp4_rows(k)
+            k_codes[start:start + n] = kc
+            k_scales[start:start + n] = ks
         p, s = encode_fp4_rows(lat)
         kv_fp4[start:start + n] = p
         kv_scale[start:start + n] = s
-    return k_cache, kv_fp4, kv_scale
+    return k_cache, kv_fp4, kv_scale, k_codes, k_scales
 
 
 def make_decode(name, n_q, n_ctx, layers, with_pool, n_plant, needles="random",
-                device="cpu", seed=0, n_visible=None, kv_gap=0):
+                device="cpu", seed=0, n_visible=None, kv_gap=0, mxfp4=False):
     """Decode batch: every query owns a sequence of n_visible[t] entries (default n_ctx),
     laid out one after the other with kv_gap spare rows between them."""
     if n_visible is None:
@@ -226,13 +264,13 @@ def make_decode(name, n_q, n_ctx, layers, with_pool, n_plant, needles="random",
                 rows.append(torch.randperm(n, generator=g)[:n_plant].sort().values)
         planted = torch.stack([r[:n_plant] if r.numel() >= n_plant else
                                torch.cat([r, r.new_full((n_plant - r.numel(),), 0)]) for r in rows])
-    k_cache, kv_fp4, kv_scale = _fill_sequences(
+    k_cache, kv_fp4, kv_scale, k_codes, k_scales = _fill_sequences(
         n_q, n_ctx, kv_start_t, n_visible_t, n_entries, device, seed,
-        None if planted is None else planted.to(device), lay[0])
+        None if planted is None else planted.to(device), lay[0], mxfp4=mxfp4)
     return Workload(name=name, n_q=n_q, n_ctx=max(n_visible) if n_q else 0,
                     kv_start=kv_start_t.to(device), n_visible=n_visible_t.to(device),
                     k_cache=k_cache, kv_fp4=kv_fp4, kv_scale=kv_scale, layers=lay,
-                    with_pool=with_pool, planted=planted)
+                    with_pool=with_pool, planted=planted, k_codes=k_codes, k_scales=k_scales)
 
 
 def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
@@ -249,7 +287,7 @@ def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
     swa_start = torch.arange(n_q, dtype=torch.int64, device=device)
     n_swa = torch.full((n_q,), WINDOW, dtype=torch.int32, device=device)
     lay = [_make_layer("full", n_q, device, seed, 0, rows, swa_start, n_swa)]
-    k_cache, kv_fp4, kv_scale = _fill_sequences(
+    k_cache, kv_fp4, kv_scale, _, _ = _fill_sequences(
         n_q, n_entries, kv_start_t, n_visible_t, n_entries, device, seed, None, lay[0])
     return Workload(name=name, n_q=n_q, n_ctx=max(n_visible), kv_start=kv_start_t.to(device),
                     n_visible=n_visible_t.to(device), k_cache=k_cache, kv_fp4=kv_fp4,
@@ -257,7 +295,18 @@ def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
 
 
 def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
-    """One of the named workloads; n_q (optional) keeps only the first n_q queries."""
+    """One of the named workloads; n_q (optional) keeps only the first n_q queries. A
+    decode workload name with the suffix "_mxfp4" also carries MXFP4 indexer keys, which
+    its indexer passes then read instead of the E4M3 ones."""
+    if name.endswith("_mxfp4") and name[:-6] in ("tiny_decode_4k", "decode_32k", "decode_256k",
+                                                 "decode_1m"):
+        base = name[:-6]
+        args = {"tiny_decode_4k": (n_q or 1, 4096, ("full",), False, 16, "random"),
+                "decode_32k": (n_q or 16, 32768, ("full",), False, 64, "random"),
+                "decode_256k": (n_q or 32, 262144, DECODE_LAYERS, True, 64, "random"),
+                "decode_1m": (n_q or 64, 1048576, DECODE_LAYERS, True, 64, "even")}[base]
+        return make_decode(name, *args[:5], needles=args[5], device=device, seed=seed,
+                           mxfp4=True)
     if name == "tiny_decode_4k":
         return make_decode(name, n_q or 1, 4096, ("full",), False, 16, device=device, seed=seed)
     if name == "decode_32k":
@@ -289,6 +338,9 @@ def sequence_to_host(wl: Workload, t: int):
         "kv_scale": wl.kv_scale[sl].cpu().numpy(),
         "layers": [],
     }
+    if wl.k_codes is not None:
+        seq["k_codes"] = wl.k_codes[sl].cpu().numpy()
+        seq["k_scales"] = wl.k_scales[sl].cpu().numpy()
     for lay in wl.layers:
         s0 = int(lay.swa_start[t])
         ns = int(lay.n_swa[t])

@@ -121,6 +121,28 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                      float* block_max, int64_t ld_block_max,
                      void* stream);
 
+/* Lightning-indexer score over MXFP4 indexer keys ([V41F-BLOG] 2.4.4: the indexer cache
+ * is FP4 in the OCP MXFP4 format; 3.1: a 128-dimensional MXFP4 indexer K entry is its
+ * E2M1 payload plus one scale byte per 32 channels). Identical to csa2_index_score (same
+ * modes, slots, outputs, -inf rules and errors) except for the key rows:
+ *   k_codes  [n_entries,64] uint8: channel 2m is the low nibble of byte m, 2m+1 the high
+ *            nibble (E2M1: sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0);
+ *            16-byte aligned.
+ *   k_scales [n_entries,4] uint8 E8M0 (value 2^(e-127)); scale g covers channels
+ *            32g .. 32g+31; 4-byte aligned.
+ * Key value of channel c = E2M1(code c) * 2^(k_scales[c/32] - 127). Supported scale codes
+ * are 1..254 with every product inside bf16's normal range (|x| in [2^-126, 2^127]);
+ * 0xFF (NaN) is never passed. Errors: as csa2_index_score, plus CSA2_ERR_INVALID_ARG for
+ * a NULL or misaligned k_scales. */
+int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+                           const void* q_idx, const float* w,
+                           const void* k_codes, const void* k_scales, int64_t n_entries,
+                           const int64_t* kv_start, const int32_t* n_visible,
+                           const int32_t* pool_blocks, int n_pool, int block_size,
+                           float* scores, int64_t ld_scores,
+                           float* block_max, int64_t ld_block_max,
+                           void* stream);
+
 /* HSI candidate pool ([V41F-BLOG] 2.3.4 "How does the Full Mode layer build the
  * candidate pool"; [V41F-ARCH] 3). For query t with n = n_visible[t] > 0 there are
  * nb = ceil(n/8) visible blocks whose scores are block_max[t, 0..nb) (the last block's

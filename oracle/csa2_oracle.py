@@ -65,7 +65,21 @@ def e2m1_value(code: int) -> float:
     return s * (1.0 + 0.5 * m) * 2.0 ** (e - 1)
 
 
+def e8m0_value(code: int) -> float:
+    """OCP microscaling E8M0 scale: an unsigned 8-bit exponent with bias 127, value
+    2^(code - 127); 0xFF is NaN.
+
+    [V41F-BLOG] 2.4.4 (the indexer cache is FP4 in the OCP MXFP4 format) and 3.1 (an MXFP4
+    indexer K entry is its E2M1 payload plus one scale byte per 32 channels).
+    """
+    code = int(code) & 0xFF
+    if code == 0xFF:
+        return float("nan")
+    return 2.0 ** (code - 127)
+
+
 E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
 E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 
@@ -101,6 +115,21 @@ def fp4_latent_decode(payload: np.ndarray, scales: np.ndarray) -> np.ndarray:
     values = e2m1_decode(codes)
     scale_per_channel = np.repeat(e4m3_decode(scales), 16, axis=-1)
     return values * scale_per_channel
+
+
+def mxfp4_key_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 indexer-key rows to float64: k[c] = E2M1(code c) * E8M0(scale[c // 32]).
+
+    [V41F-BLOG] 2.4.4 and 3.1: 128 channels of E2M1 with one E8M0 scale per 32 channels
+    (OCP MXFP4). Reading R4's packing: channel 2m is the low nibble of byte m.
+    codes [..., 64] uint8, scales [..., 4] uint8 -> [..., 128] float64.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    lo = codes & 0xF
+    hi = codes >> 4
+    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    return e2m1_decode(c) * np.repeat(E8M0_TABLE[scales], 32, axis=-1)
 
 
 # --------------------------------------------------------------------------------------
@@ -157,6 +186,35 @@ def reindex_scores(q_idx: np.ndarray, w: np.ndarray, k_cache_codes: np.ndarray,
     ok = (block >= 0) & (pos < n_visible)
     if ok.any():
         rows = e4m3_decode(k_cache_codes[kv_start + pos[ok]])
+        out[ok] = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), rows)
+    return out
+
+
+def full_scores_mxfp4(q_idx: np.ndarray, w: np.ndarray, k_codes: np.ndarray,
+                      k_scales: np.ndarray, kv_start: int, n_visible: int, ld: int) -> np.ndarray:
+    """full_scores with MXFP4 indexer keys (mxfp4_key_decode rows)."""
+    out = np.full(ld, NEG_INF)
+    n = min(int(n_visible), int(ld))
+    if n > 0:
+        rows = mxfp4_key_decode(k_codes[kv_start:kv_start + n], k_scales[kv_start:kv_start + n])
+        out[:n] = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), rows)
+    return out
+
+
+def reindex_scores_mxfp4(q_idx: np.ndarray, w: np.ndarray, k_codes: np.ndarray,
+                         k_scales: np.ndarray, kv_start: int, n_visible: int,
+                         pool_blocks: np.ndarray, block_size: int = 8) -> np.ndarray:
+    """reindex_scores with MXFP4 indexer keys."""
+    pool_blocks = np.asarray(pool_blocks, dtype=np.int64)
+    n_slots = pool_blocks.shape[0] * block_size
+    out = np.full(n_slots, NEG_INF)
+    slot = np.arange(n_slots)
+    block = pool_blocks[slot // block_size]
+    pos = block * block_size + slot % block_size
+    ok = (block >= 0) & (pos < n_visible)
+    if ok.any():
+        r = kv_start + pos[ok]
+        rows = mxfp4_key_decode(k_codes[r], k_scales[r])
         out[ok] = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), rows)
     return out
 
@@ -281,10 +339,14 @@ def gather_attention_entries(topk_pos: np.ndarray, kv_fp4: np.ndarray, kv_scale:
 
 
 def full_layer(q_idx, w, k_cache, kv_start, n_visible, q, kv_fp4, kv_scale, window_kv,
-               swa_start, n_swa, softmax_scale, k=512, with_pool=False):
+               swa_start, n_swa, softmax_scale, k=512, with_pool=False, k_scales=None):
     """Full mode for one query: score everything visible, take the Top-K, optionally
-    build the HSI pool from the same scores, and attend. Returns a dict."""
-    scores = full_scores(q_idx, w, k_cache, kv_start, n_visible, n_visible)
+    build the HSI pool from the same scores, and attend. Returns a dict. With k_scales
+    the indexer keys are MXFP4 (k_cache holds their codes)."""
+    if k_scales is None:
+        scores = full_scores(q_idx, w, k_cache, kv_start, n_visible, n_visible)
+    else:
+        scores = full_scores_mxfp4(q_idx, w, k_cache, k_scales, kv_start, n_visible, n_visible)
     idx = slots_to_positions(topk_slots(scores, k), None)
     res = {"scores": scores, "idx": idx}
     if with_pool:
@@ -295,12 +357,15 @@ def full_layer(q_idx, w, k_cache, kv_start, n_visible, q, kv_fp4, kv_scale, wind
 
 
 def reindex_layer(q_idx, w, k_cache, kv_start, n_visible, pool, q, kv_fp4, kv_scale,
-                  window_kv, swa_start, n_swa, softmax_scale, k=512):
+                  window_kv, swa_start, n_swa, softmax_scale, k=512, k_scales=None):
     """Reindex mode for one query: rescore only the pool with this layer's indexer
-    query, take its own Top-K inside the pool, and attend."""
+    query, take its own Top-K inside the pool, and attend (MXFP4 keys with k_scales)."""
     padded = np.full(2048, -1, dtype=np.int64)
     padded[:len(pool)] = pool
-    scores = reindex_scores(q_idx, w, k_cache, kv_start, n_visible, padded)
+    if k_scales is None:
+        scores = reindex_scores(q_idx, w, k_cache, kv_start, n_visible, padded)
+    else:
+        scores = reindex_scores_mxfp4(q_idx, w, k_cache, k_scales, kv_start, n_visible, padded)
     idx = slots_to_positions(topk_slots(scores, k), padded)
     ents = gather_attention_entries(idx, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa)
     out, lse = sparse_attention(bf16_decode(q), ents, softmax_scale)

@@ -22,10 +22,14 @@ def np_u16(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def score_abs_terms(q_bits, w, k_codes):
-    """sum_h |w_h| sum_d |q_hd k_d| for every row: the scale of fp32 rounding in a score."""
+def score_abs_terms(q_bits, w, k_codes, k_scales=None):
+    """sum_h |w_h| sum_d |q_hd k_d| for every row: the scale of fp32 rounding in a score.
+    k_codes are E4M3 rows, or MXFP4 code rows when k_scales is given."""
     qa = np.abs(O.bf16_decode(q_bits))
-    ka = np.abs(O.e4m3_decode(k_codes))
+    if k_scales is None:
+        ka = np.abs(O.e4m3_decode(k_codes))
+    else:
+        ka = np.abs(O.mxfp4_key_decode(k_codes, k_scales))
     return (ka @ qa.T) @ np.abs(np.asarray(w, np.float64))
 
 
@@ -91,7 +95,11 @@ def check_query(wl, buf, t, seq=None, report=None):
     for li, lay in enumerate(seq["layers"]):
         idx_gpu = buf.published[li][t].cpu().numpy()
         if lay["mode"] == "full":
-            scores = O.full_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, nv)
+            if "k_codes" in seq:
+                scores = O.full_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
+                                             seq["k_scales"], 0, nv, nv)
+            else:
+                scores = O.full_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, nv)
             ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), None)
             kth, band = band_of(scores, 512)
             assert_set_band(idx_gpu, ref_idx, lambda p: scores[p], kth, band,
@@ -107,7 +115,11 @@ def check_query(wl, buf, t, seq=None, report=None):
             padded = np.full(2048, -1, np.int64)
             kept = pool_gpu[pool_gpu >= 0]
             padded[:len(kept)] = kept
-            scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
+            if "k_codes" in seq:
+                scores = O.reindex_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
+                                                seq["k_scales"], 0, nv, padded)
+            else:
+                scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
             ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), padded)
             pos_of_slot = O.slots_to_positions(np.arange(len(scores)), padded)
             score_at = dict(zip(pos_of_slot.tolist(), scores.tolist()))

@@ -19,8 +19,9 @@ def C():
 def test_header_symbols_are_exported(C):
     text = open(HEADER).read()
     names = set(re.findall(r"^(?:int|size_t|const char\*)\s+(csa2_\w+)\(", text, re.M))
-    assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_block_pool", "csa2_topk",
-                     "csa2_pool_topk", "csa2_sparse_attn", "csa2_version", "csa2_last_error"}
+    assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_index_score_mxfp4",
+                     "csa2_block_pool", "csa2_topk", "csa2_pool_topk", "csa2_sparse_attn",
+                     "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -56,6 +57,23 @@ def test_index_score_rejections(C):
     assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2, scores=None,
                   block_max=FAKE, ld_bm=2) == 1           # REINDEX always writes scores
     assert _score(C, n_q=0, q_idx=None) == 0              # nothing to do, nothing launched
+
+
+def test_index_score_mxfp4_rejections(C):
+    def call(**kw):
+        a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE, k_codes=FAKE,
+                 k_scales=FAKE, n_entries=10, kv_start=FAKE, n_visible=FAKE, pool_blocks=None,
+                 n_pool=0, block_size=8, scores=FAKE, ld=16, block_max=None, ld_bm=0,
+                 stream=None)
+        a.update(kw)
+        return C.lib.csa2_index_score_mxfp4(*a.values())
+    assert call(k_scales=None) == 1 and b"null k_scales" in C.lib.csa2_last_error()
+    assert call(k_scales=FAKE + 2) == 1 and b"4-byte aligned" in C.lib.csa2_last_error()
+    assert call(k_codes=FAKE + 8) == 1                    # codes not 16-byte aligned
+    assert call(mode=2) == 1 and b"csa2_index_score_mxfp4" in C.lib.csa2_last_error()
+    assert call(n_heads=64) == 2
+    assert call(scores=None) == 1
+    assert call(n_q=0, k_scales=None, q_idx=None) == 0    # nothing to do, nothing launched
 
 
 def test_topk_and_pool_rejections(C):

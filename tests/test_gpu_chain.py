@@ -79,3 +79,16 @@ def test_graph_replay_matches_eager(dev):
         assert torch.equal(buf.out.view(torch.int16), eager.out.view(torch.int16)), rep
         layers.run_layers(wl, eager)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_small_decode_stack_with_mxfp4_keys(dev):
+    """The decoder stack over MXFP4 indexer keys against the oracle's MXFP4 scoring."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    wl = synth.make_decode("small_stack_mxfp4", 3, 0, synth.DECODE_LAYERS, True, 32,
+                           n_visible=[40000, 17000, 3001], kv_gap=9, seed=24,
+                           mxfp4=True).to(dev)
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    compared = sum(check_query(wl, buf, t) for t in range(wl.n_q))
+    assert compared == wl.n_q * len(wl.layers)

@@ -406,3 +406,102 @@ def test_sparse_attn_single_entry_and_constant_query(C, dev):
     start = int(case["kv_start"][1])
     ents = O.fp4_latent_decode(p_all[start + idx[1].numpy()], s_all[start + idx[1].numpy()])
     assert_attn_close(out[1].float().cpu().numpy(), np.repeat(ents.mean(0)[None], 64, 0), "q=0")
+
+
+# --------------------------------------------------------------------------- MXFP4 keys
+
+def test_mxfp4_indexer_one_hot_reads_every_code_and_scale_in_place(C, dev):
+    """Row r, byte b holds (7r + 3b) % 256 (every pair of E2M1 codes) and scale group g of
+    row r one of nine E8M0 codes from 2 to 252 (products from 2^-126 to 1.5*2^127); a
+    one-hot indexer query on channel c with weight 1 scores ReLU(+-value), exactly."""
+    rows = np.arange(256)[:, None]
+    codes = ((7 * rows + 3 * np.arange(64)[None, :]) % 256).astype(np.uint8)
+    sc_list = np.array([2, 60, 100, 126, 127, 128, 140, 200, 252], np.uint8)
+    scales = sc_list[(rows + 2 * np.arange(4)[None, :]) % len(sc_list)].astype(np.uint8)
+    k_codes = torch.from_numpy(codes).to(dev)
+    k_scales = torch.from_numpy(scales).to(dev)
+    chans = [0, 1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 127]
+    tests = [(c, h, s) for s in (1.0, -1.0) for h, c in enumerate(chans)]
+    n_q = len(tests)
+    q = torch.zeros((n_q, 32, 128), dtype=torch.float32)
+    w = torch.zeros((n_q, 32), dtype=torch.float32)
+    for t, (c, h, s) in enumerate(tests):
+        q[t, h, c] = s
+        w[t, h] = 1.0
+    q = q.to(torch.bfloat16).to(dev)
+    w = w.to(dev)
+    scores = torch.empty((n_q, 256), dtype=torch.float32, device=dev)
+    C.csa2_index_score_mxfp4(C.FULL, q, w, k_codes, k_scales, _i64([0] * n_q, dev),
+                             _i32([256] * n_q, dev), scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    for t in range(n_q):
+        ref = O.full_scores_mxfp4(np_u16(q[t]), w[t].cpu().numpy(), codes, scales, 0, 256, 256)
+        assert np.array_equal(got[t].astype(np.float64), ref), f"query {t} {tests[t]}"
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged"])
+def test_mxfp4_index_score_full_parity(C, dev, case):
+    from compressed_kv_cache_csa2_amd import synth
+    if case == "tiny":
+        wl = synth.make_workload("tiny_decode_4k_mxfp4").to(dev)
+        ld = 4096
+    else:
+        wl = synth.make_decode("ragged", 6, 0, ("full",), False, 0,
+                               n_visible=[0, 1, 7, 4099, 2500, 9000], kv_gap=5, seed=3,
+                               mxfp4=True).to(dev)
+        wl.n_visible[5] = 9000 + 37   # rows past the end of the cache score -inf
+        ld = 9100
+    lay = wl.layers[0]
+    scores = torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev)
+    bmax = torch.empty((wl.n_q, (ld + 7) // 8), dtype=torch.float32, device=dev)
+    C.csa2_index_score_mxfp4(C.FULL, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, scores, bmax)
+    torch.cuda.synchronize()
+    kc, ks = wl.k_codes.cpu().numpy(), wl.k_scales.cpu().numpy()
+    got = scores.cpu().numpy()
+    for t in range(wl.n_q):
+        start, nv = int(wl.kv_start[t]), int(wl.n_visible[t])
+        n_rows = max(0, min(nv, kc.shape[0] - start))
+        ref = O.full_scores_mxfp4(np_u16(lay.q_idx[t]), lay.w[t].cpu().numpy(), kc, ks, start,
+                                  n_rows, ld)
+        terms = np.zeros(ld)
+        if n_rows:
+            terms[:n_rows] = score_abs_terms(np_u16(lay.q_idx[t]), lay.w[t].cpu().numpy(),
+                                             kc[start:start + n_rows], ks[start:start + n_rows])
+        assert_scores_close(got[t], ref, terms, f"query {t}")
+    pad = np.full((wl.n_q, bmax.shape[1] * 8), -np.inf, np.float32)
+    pad[:, :ld] = got
+    assert np.array_equal(bmax.cpu().numpy(), pad.reshape(wl.n_q, -1, 8).max(axis=2))
+
+
+def test_mxfp4_index_score_reindex_parity(C, dev):
+    from compressed_kv_cache_csa2_amd import synth
+    wl = synth.make_decode("pool", 3, 0, ("full",), False, 0, n_visible=[20000, 777, 16384],
+                           kv_gap=11, seed=4, mxfp4=True).to(dev)
+    g = torch.Generator().manual_seed(5)
+    pool = torch.full((3, 2048), -1, dtype=torch.int32)
+    for t, nv in enumerate([20000, 777, 16384]):
+        nb = (nv + 7) // 8
+        m = min(2048, nb)
+        pool[t, :m] = torch.randperm(nb, generator=g)[:m].sort().values.to(torch.int32)
+    pool[0, 5] = 2600
+    pool = pool.to(dev)
+    q_idx = _bf16((3, 32, 128), g, dev)
+    w = torch.rand((3, 32), generator=g).to(dev)
+    scores = torch.empty((3, 16384), dtype=torch.float32, device=dev)
+    C.csa2_index_score_mxfp4(C.REINDEX, q_idx, w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, scores, pool_blocks=pool)
+    torch.cuda.synchronize()
+    kc, ks = wl.k_codes.cpu().numpy(), wl.k_scales.cpu().numpy()
+    got = scores.cpu().numpy()
+    for t in range(3):
+        start, nv = int(wl.kv_start[t]), int(wl.n_visible[t])
+        ref = O.reindex_scores_mxfp4(np_u16(q_idx[t]), w[t].cpu().numpy(), kc, ks, start, nv,
+                                     pool[t].cpu().numpy())
+        pos = O.slots_to_positions(np.arange(16384), pool[t].cpu().numpy())
+        ok = np.isfinite(ref)
+        terms = np.zeros(16384)
+        terms[ok] = score_abs_terms(np_u16(q_idx[t]), w[t].cpu().numpy(), kc[start + pos[ok]],
+                                    ks[start + pos[ok]])
+        assert_scores_close(got[t], ref, terms, f"query {t}")

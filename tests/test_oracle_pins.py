@@ -315,3 +315,77 @@ def test_model_constants_and_entry_bytes():
                       ("candidate_block_size", "CSA2_CANDIDATE_BLOCK_SIZE"),
                       ("candidate_topk_blocks", "CSA2_CANDIDATE_TOPK_BLOCKS")]:
         assert f"#define {name} {c[key]} " in hdr or f"#define {name} {c[key]}\n" in hdr, name
+
+
+# --------------------------------------------------------------------------- MXFP4 keys
+
+def test_e8m0_every_code_against_torch():
+    """All 256 E8M0 scale codes against torch's float8_e8m0fnu decode (a library
+    cross-check of the OCP microscaling scale the pages name for the FP4 indexer cache)."""
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([O.e8m0_value(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+
+
+def test_mxfp4_unit_scale_is_plain_e2m1_and_scales_are_powers_of_two():
+    """Scale code 127 leaves the E2M1 values (pinned by the pages' magnitude set), and one
+    step of the scale code doubles every channel of its 32-channel group only."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(7, 64), dtype=np.uint8)
+    unit = O.mxfp4_key_decode(codes, np.full((7, 4), 127, np.uint8))
+    lo, hi = codes & 0xF, codes >> 4
+    plain = np.stack([O.e2m1_decode(lo), O.e2m1_decode(hi)], axis=-1).reshape(7, 128)
+    assert np.array_equal(unit, plain)
+    for g in range(4):
+        sc = np.full((7, 4), 127, np.uint8)
+        sc[:, g] = 128
+        v = O.mxfp4_key_decode(codes, sc)
+        assert np.array_equal(v[:, 32 * g:32 * g + 32], 2 * unit[:, 32 * g:32 * g + 32])
+        rest = np.ones(128, bool)
+        rest[32 * g:32 * g + 32] = False
+        assert np.array_equal(v[:, rest], unit[:, rest])
+
+
+def test_mxfp4_scores_equal_e4m3_scores_on_shared_values():
+    """Keys whose values are exact in both formats (E2M1 x 2^-2..2^1 all lie on the E4M3
+    grid) give bit-identical scores through the MXFP4 and the E4M3 oracle paths, pinning
+    the nibble order, the channel order and the 32-channel scale groups against the
+    pinned E4M3 path."""
+    rng = np.random.default_rng(11)
+    n = 300
+    codes = rng.integers(0, 256, size=(n, 64), dtype=np.uint8)
+    scales = rng.integers(125, 129, size=(n, 4), dtype=np.uint8)
+    vals = O.mxfp4_key_decode(codes, scales)
+    lookup = {v: c for c, v in enumerate(O.E4M3_TABLE) if not np.isnan(v)}
+    lookup[0.0] = 0
+    e4 = np.vectorize(lambda v: lookup[float(v)])(vals).astype(np.uint8)
+    assert np.array_equal(O.e4m3_decode(e4), vals)
+    q = (rng.standard_normal((32, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = rng.random(32).astype(np.float32)
+    a = O.full_scores(q, w, e4, 0, n - 3, n)
+    b = O.full_scores_mxfp4(q, w, codes, scales, 0, n - 3, n)
+    assert np.array_equal(a, b)
+    pool = np.array([3, 0, -1, 30, 36, 37], np.int64)
+    padded = np.full(2048, -1, np.int64)
+    padded[:len(pool)] = pool
+    assert np.array_equal(O.reindex_scores(q, w, e4, 0, n - 3, padded),
+                          O.reindex_scores_mxfp4(q, w, codes, scales, 0, n - 3, padded))
+
+
+def test_mxfp4_encoder_round_trip():
+    """The input generator's MXFP4 encoder against the oracle's decoder: decoding then
+    re-encoding a canonical row returns it, and encoding lands within half a grid step of
+    the scaled value (one full step of 2 where the top of the range saturates at 6)."""
+    import torch
+    from compressed_kv_cache_csa2_amd import synth
+    x = torch.randn(500, 128, generator=torch.Generator().manual_seed(3)) * 3
+    c, s = synth.encode_mxfp4_rows(x)
+    d = O.mxfp4_key_decode(c.numpy(), s.numpy())
+    step = np.repeat(O.E8M0_TABLE[s.numpy()], 32, axis=-1)
+    err = np.abs(d - x.double().numpy()) / step
+    assert err.max() <= 2.0 + 1e-12
+    assert np.all(err[np.abs(x.double().numpy()) / step <= 6.0] <= 1.0 + 1e-12)
+    c2, s2 = synth.encode_mxfp4_rows(torch.from_numpy(d).float())
+    assert np.array_equal(O.mxfp4_key_decode(c2.numpy(), s2.numpy()), d)
