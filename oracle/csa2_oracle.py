@@ -133,6 +133,90 @@ def mxfp4_key_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------
+# Cache writes (quantisers)
+# --------------------------------------------------------------------------------------
+#
+# [V41F-BLOG] 2.4.4: the main KV is stored as E2M1 with one E4M3 scale per 16 channels and
+# no global scale, quantised after RoPE; the sliding-window cache stays FP8; the indexer
+# cache is OCP MXFP4. The pages give no rounding rule: readings R16 (main KV) and R19
+# (MXFP4 keys) take round-to-nearest-even onto each grid, saturating at its largest value.
+# Every decision is taken on float32 values (the inputs are bf16, exact in float32, and
+# the quotients are float32 divisions), the precision the kernels decide in.
+
+E4M3_POS = E4M3_TABLE[:127]          # codes 0..126: the finite non-negative E4M3 values
+E2M1_POS = E2M1_TABLE[:8]            # codes 0..7
+
+
+def _round_to_grid(a: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """Index of the nearest value of an increasing grid to each a >= 0, ties to the even
+    index; values beyond the last grid point take the last index (saturation)."""
+    a = np.asarray(a, np.float64)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 1, len(grid) - 1)
+    lo = hi - 1
+    dlo = a - grid[lo]
+    dhi = grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    idx = np.where(pick_hi, hi, lo)
+    return np.where(a >= grid[-1], len(grid) - 1, idx).astype(np.int64)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """float32 values -> E4M3 bytes: nearest with ties to the even code, saturating at 448;
+    the sign bit is that of x (a negative value that rounds to zero gives 0x80)."""
+    x = np.asarray(x, np.float32)
+    code = _round_to_grid(np.abs(x).astype(np.float64), E4M3_POS).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 7)
+
+
+def e2m1_round(y: np.ndarray) -> np.ndarray:
+    """float32 values -> E2M1 codes: nearest grid magnitude with ties to the even code,
+    saturating at 6; the sign bit only on a nonzero code."""
+    y = np.asarray(y, np.float32)
+    mag = _round_to_grid(np.abs(y).astype(np.float64), E2M1_POS).astype(np.uint8)
+    return mag | (((y < 0) & (mag > 0)).astype(np.uint8) << 3)
+
+
+def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Codes [..., 2n] -> bytes [..., n], channel 2m in the low nibble of byte m (R4)."""
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def fp4_latent_quantize(x: np.ndarray):
+    """Main-KV rows (float32 view of bf16) -> (payload [..., 256], scales [..., 32]).
+
+    Reading R16 of [V41F-BLOG] 2.4.4: per 16-channel group the scale is E4M3(amax / 6) and
+    each value is E2M1(x / scale); a zero scale gives zero codes.
+    """
+    x = np.asarray(x, np.float32)
+    g = x.reshape(x.shape[:-1] + (x.shape[-1] // 16, 16))
+    amax = np.abs(g).max(axis=-1)
+    s_code = e4m3_round(amax / np.float32(6.0))
+    s = E4M3_TABLE[s_code].astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (g / safe[..., None]).astype(np.float32)
+    codes = np.where((s > 0)[..., None], e2m1_round(q), 0).astype(np.uint8)
+    return _pack_nibbles(codes.reshape(x.shape)), s_code
+
+
+def mxfp4_key_quantize(x: np.ndarray):
+    """Indexer-K rows (float32 view of bf16) -> (codes [..., 64], E8M0 scales [..., 4]).
+
+    Reading R19 (the OCP microscaling recipe for [V41F-BLOG] 2.4.4's MXFP4 indexer cache):
+    per 32-channel group the shared exponent is floor(log2 amax) - 2 (2 = E2M1's largest
+    exponent), stored as a biased byte kept in 1..254; values are E2M1(x / 2^X). An
+    all-zero group gets the unit scale byte 127.
+    """
+    x = np.asarray(x, np.float32)
+    g = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(g).max(axis=-1).astype(np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = m * 2^e, m in [0.5, 1)
+    code_s = np.where(amax > 0, np.clip(e - 1 - 2 + 127, 1, 254), 127).astype(np.int64)
+    q = (g.astype(np.float64) * np.ldexp(1.0, 127 - code_s)[..., None]).astype(np.float32)
+    codes = e2m1_round(q)
+    return _pack_nibbles(codes.reshape(x.shape)), code_s.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------------------
 # Indexer
 # --------------------------------------------------------------------------------------
 

@@ -389,3 +389,60 @@ def test_mxfp4_encoder_round_trip():
     assert np.all(err[np.abs(x.double().numpy()) / step <= 6.0] <= 1.0 + 1e-12)
     c2, s2 = synth.encode_mxfp4_rows(torch.from_numpy(d).float())
     assert np.array_equal(O.mxfp4_key_decode(c2.numpy(), s2.numpy()), d)
+
+
+# --------------------------------------------------------------------------- cache writes
+
+def test_e4m3_round_against_torch_with_ties_and_saturation():
+    """The oracle's E4M3 rounding against torch's float8_e4m3fn cast on random values,
+    exact midpoints between neighbouring codes and subnormals; above 448 it saturates."""
+    import torch
+    rng = np.random.default_rng(7)
+    vals = [rng.standard_normal(20000).astype(np.float32) * s for s in (1e-3, 0.05, 1, 30, 120)]
+    mags = O.E4M3_POS
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (mags[:-1] + mags[1:]) / 2)   # exact in fp32
+    x = np.concatenate(vals + [mids, -mids, mags.astype(np.float32), np.float32([0.0, -0.0])])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_round(x), ref)
+    assert np.array_equal(O.e4m3_round(np.float32([449, 470, 1e6, -1e6])),
+                          np.uint8([0x7E, 0x7E, 0x7E, 0xFE]))
+
+
+def test_e2m1_round_midpoints_and_saturation():
+    """Brute force: every value is mapped to the nearest E2M1 magnitude, exact midpoints go
+    to the even code, values past 6 saturate, the sign bit never marks a zero."""
+    grid = O.E2M1_POS
+    mids = (grid[:-1] + grid[1:]) / 2
+    want_mid = [0, 2, 2, 4, 4, 6, 6]      # even code of each neighbouring pair
+    assert list(O.e2m1_round(mids.astype(np.float32))) == want_mid
+    y = np.linspace(-9, 9, 7201).astype(np.float32)
+    got = O.e2m1_round(y)
+    mag = O.E2M1_TABLE[got & 7]
+    best = np.abs(np.abs(y)[:, None] - grid[None, :]).min(axis=1)
+    assert np.all(np.abs(np.abs(y) - mag) == np.where(np.abs(y) > 6, np.abs(y) - 6, best))
+    assert not np.any((got == 8))
+
+
+def test_write_quantisers_equal_the_input_generator():
+    """Two independent implementations of readings R16 and R19 agree bit for bit: the
+    oracle's numpy quantisers and the input generator's torch encoders."""
+    import torch
+    from compressed_kv_cache_csa2_amd import synth
+    g = torch.Generator().manual_seed(9)
+    lat = (torch.randn(400, 512, generator=g) * 2).to(torch.bfloat16).float()
+    lat[3] = 0.0
+    lat[5, 16:32] = 0.0
+    p, s = O.fp4_latent_quantize(lat.numpy())
+    p2, s2 = synth.encode_fp4_rows(lat)
+    assert np.array_equal(p, p2.numpy()) and np.array_equal(s, s2.numpy())
+    key = (torch.randn(400, 128, generator=g) * 3).to(torch.bfloat16).float()
+    key[7, :32] = 0.0
+    c, sc = O.mxfp4_key_quantize(key.numpy())
+    c2, sc2 = synth.encode_mxfp4_rows(key)
+    assert np.array_equal(c, c2.numpy()) and np.array_equal(sc, sc2.numpy())
+    # and decoding what was written stays within the grid step
+    d = O.fp4_latent_decode(p, s)
+    step = np.repeat(O.E4M3_TABLE[s], 16, axis=-1)
+    assert np.all(np.abs(d - lat.numpy()) <= step * 2.0 + 1e-30)
