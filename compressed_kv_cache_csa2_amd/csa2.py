@@ -33,12 +33,16 @@ def _load():
     P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
+    lib.csa2_write_e4m3.argtypes = [I, I, P, P, P, L, L, P]
+    lib.csa2_write_mxfp4_key.argtypes = [I, P, P, P, P, L, P]
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
     lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
     lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
-    for f in ("csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
+    for f in ("csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
+              "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
@@ -81,6 +85,50 @@ def version() -> str:
 
 def workspace_bytes(op: int, n_q: int, max_cols: int, k: int) -> int:
     return int(lib.csa2_workspace_bytes(op, n_q, max_cols, k))
+
+
+def _rows_view(t, width, name):
+    if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 \
+            or t.shape[1] < width:
+        raise ValueError(f"{name}: expected a device uint8 [rows, >= {width}] view")
+    return t.data_ptr(), t.stride(0)
+
+
+def csa2_write_latent(x, rows, kv_fp4, kv_scale, stream=None):
+    """Quantise bf16 latent rows x [n, 512] into kv_fp4 / kv_scale at cache rows `rows`."""
+    p_fp4, s_fp4 = _rows_view(kv_fp4, 256, "kv_fp4")
+    p_sc, s_sc = _rows_view(kv_scale, 32, "kv_scale")
+    if x.dim() != 2 or x.shape[1] != 512 or rows.shape[0] != x.shape[0]:
+        raise ValueError("csa2_write_latent: x must be [n, 512] with one row index per row")
+    if kv_fp4.shape[0] != kv_scale.shape[0]:
+        raise ValueError("csa2_write_latent: kv_fp4 and kv_scale row counts differ")
+    _check(lib.csa2_write_latent(x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                                 _ptr(rows, torch.int64, "rows"), p_fp4, s_fp4, p_sc, s_sc,
+                                 kv_fp4.shape[0], _stream(stream)))
+
+
+def csa2_write_e4m3(x, rows, dst, stream=None):
+    """E4M3 rows: window rows (x [n, 512]) or E4M3 indexer keys (x [n, 128]) into dst."""
+    d = x.shape[1]
+    p, st = _rows_view(dst, d, "dst")
+    if x.dim() != 2 or rows.shape[0] != x.shape[0]:
+        raise ValueError("csa2_write_e4m3: x must be [n, d] with one row index per row")
+    _check(lib.csa2_write_e4m3(x.shape[0], d, _ptr(x, torch.bfloat16, "x"),
+                               _ptr(rows, torch.int64, "rows"), p, st, dst.shape[0],
+                               _stream(stream)))
+
+
+def csa2_write_mxfp4_key(x, rows, k_codes, k_scales, stream=None):
+    """MXFP4 indexer keys: x [n, 128] bf16 into k_codes [E, 64] / k_scales [E, 4]."""
+    if x.dim() != 2 or x.shape[1] != 128 or rows.shape[0] != x.shape[0]:
+        raise ValueError("csa2_write_mxfp4_key: x must be [n, 128] with one row index per row")
+    if k_codes.shape[0] != k_scales.shape[0]:
+        raise ValueError("csa2_write_mxfp4_key: k_codes and k_scales row counts differ")
+    _check(lib.csa2_write_mxfp4_key(x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                                    _ptr(rows, torch.int64, "rows"),
+                                    _ptr(k_codes, torch.uint8, "k_codes"),
+                                    _ptr(k_scales, torch.uint8, "k_scales"), k_codes.shape[0],
+                                    _stream(stream)))
 
 
 def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block_max=None,

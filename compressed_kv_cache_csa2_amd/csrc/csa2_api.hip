@@ -135,6 +135,58 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx, co
                             stream);
 }
 
+int csa2_write_latent(int n, const void* x, const int64_t* rows, void* kv_fp4,
+                      int64_t kv_fp4_stride, void* kv_scale, int64_t kv_scale_stride,
+                      int64_t n_entries, void* stream) {
+  REQUIRE(n >= 0 && n <= (1 << 26), CSA2_ERR_INVALID_ARG, "csa2_write_latent: n %d out of range", n);
+  if (n == 0) return ok();
+  REQUIRE(x && rows && kv_fp4 && kv_scale, CSA2_ERR_INVALID_ARG, "csa2_write_latent: null pointer argument");
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "csa2_write_latent: n_entries < 0");
+  REQUIRE(kv_fp4_stride >= 256 && kv_fp4_stride % 4 == 0 && kv_scale_stride >= 32,
+          CSA2_ERR_INVALID_ARG, "csa2_write_latent: strides must be >= 256 (a multiple of 4) and >= 32");
+  REQUIRE(aligned(x, 16) && aligned(kv_fp4, 4) && aligned(rows, 8), CSA2_ERR_INVALID_ARG,
+          "csa2_write_latent: x must be 16-byte, kv_fp4 4-byte and rows 8-byte aligned");
+  return hip_status(csa2::launch_latent_write(n, static_cast<const uint16_t*>(x), rows,
+                                              static_cast<uint8_t*>(kv_fp4), kv_fp4_stride,
+                                              static_cast<uint8_t*>(kv_scale), kv_scale_stride,
+                                              n_entries, static_cast<hipStream_t>(stream)),
+                    "csa2_write_latent");
+}
+
+int csa2_write_e4m3(int n, int d, const void* x, const int64_t* rows, void* dst,
+                    int64_t dst_stride, int64_t n_rows, void* stream) {
+  REQUIRE(d == CSA2_IDX_DIM || d == CSA2_HEAD_DIM, CSA2_ERR_UNSUPPORTED,
+          "csa2_write_e4m3: d %d, only %d (indexer keys) and %d (window rows) are built", d,
+          CSA2_IDX_DIM, CSA2_HEAD_DIM);
+  REQUIRE(n >= 0 && n <= (1 << 26), CSA2_ERR_INVALID_ARG, "csa2_write_e4m3: n %d out of range", n);
+  if (n == 0) return ok();
+  REQUIRE(x && rows && dst, CSA2_ERR_INVALID_ARG, "csa2_write_e4m3: null pointer argument");
+  REQUIRE(n_rows >= 0 && dst_stride >= d && dst_stride % 8 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_write_e4m3: need n_rows >= 0 and dst_stride >= d, a multiple of 8");
+  REQUIRE(aligned(x, 16) && aligned(dst, 8) && aligned(rows, 8), CSA2_ERR_INVALID_ARG,
+          "csa2_write_e4m3: x must be 16-byte, dst and rows 8-byte aligned");
+  return hip_status(csa2::launch_e4m3_write(n, d, static_cast<const uint16_t*>(x), rows,
+                                            static_cast<uint8_t*>(dst), dst_stride, n_rows,
+                                            static_cast<hipStream_t>(stream)),
+                    "csa2_write_e4m3");
+}
+
+int csa2_write_mxfp4_key(int n, const void* x, const int64_t* rows, void* k_codes,
+                         void* k_scales, int64_t n_entries, void* stream) {
+  REQUIRE(n >= 0 && n <= (1 << 26), CSA2_ERR_INVALID_ARG, "csa2_write_mxfp4_key: n %d out of range", n);
+  if (n == 0) return ok();
+  REQUIRE(x && rows && k_codes && k_scales, CSA2_ERR_INVALID_ARG,
+          "csa2_write_mxfp4_key: null pointer argument");
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "csa2_write_mxfp4_key: n_entries < 0");
+  REQUIRE(aligned(x, 16) && aligned(k_codes, 4) && aligned(rows, 8), CSA2_ERR_INVALID_ARG,
+          "csa2_write_mxfp4_key: x must be 16-byte, k_codes 4-byte and rows 8-byte aligned");
+  return hip_status(csa2::launch_mxfp4_key_write(n, static_cast<const uint16_t*>(x), rows,
+                                                 static_cast<uint8_t*>(k_codes),
+                                                 static_cast<uint8_t*>(k_scales), n_entries,
+                                                 static_cast<hipStream_t>(stream)),
+                    "csa2_write_mxfp4_key");
+}
+
 int csa2_block_pool(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
                     int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
                     void* workspace, size_t ws_bytes, void* stream) {

@@ -42,4 +42,14 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               const int32_t* n_swa, float softmax_scale, uint16_t* out,
                               float* lse, hipStream_t stream);
 
+// Cache writes: quantise bf16 rows into the cache formats (destination rows outside
+// [0, n_rows) are skipped).
+hipError_t launch_latent_write(int n, const uint16_t* x, const int64_t* rows, uint8_t* kv_fp4,
+                               int64_t fp4_stride, uint8_t* kv_scale, int64_t sc_stride,
+                               int64_t n_entries, hipStream_t stream);
+hipError_t launch_e4m3_write(int n, int d, const uint16_t* x, const int64_t* rows,
+                             uint8_t* dst, int64_t dst_stride, int64_t n_rows, hipStream_t stream);
+hipError_t launch_mxfp4_key_write(int n, const uint16_t* x, const int64_t* rows, uint8_t* k_codes,
+                                  uint8_t* k_scales, int64_t n_entries, hipStream_t stream);
+
 }  // namespace csa2

@@ -143,6 +143,36 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                            float* block_max, int64_t ld_block_max,
                            void* stream);
 
+/* Cache writes ([V41F-BLOG] 2.4.4: the main KV is stored as E2M1 with one E4M3 scale per
+ * 16 channels and no global scale, quantised after RoPE; the sliding-window cache keeps
+ * FP8; the indexer cache is OCP MXFP4; [V41F-ARCH] 4). These produce the formats the
+ * calls above read. Inputs are bf16 rows, already rotated; row r goes to cache row
+ * rows[r]; a destination outside [0, n_entries) (or [0, n_rows)) is skipped, so the
+ * caller may pass -1 for a row to drop. Rounding (the pages give none; readings R16 and
+ * R19): nearest grid value, ties to the even code, saturating at the grid's largest
+ * value, decided on float32 values:
+ *   csa2_write_latent: per 16-channel group scale = E4M3(amax / 6) and code =
+ *       E2M1(x / scale) (IEEE float32 division); zero codes when the scale is 0. Writes
+ *       kv_fp4[row, 0..256) (channel 2m in the low nibble of byte m) and
+ *       kv_scale[row, 0..32). x [n,512] bf16, 16-byte aligned; rows [n] int64;
+ *       kv_fp4_stride >= 256 (multiple of 4), kv_scale_stride >= 32.
+ *   csa2_write_e4m3: dst[row, 0..d) = E4M3(x[r, :]) (saturating at +-448; a negative
+ *       value rounding to zero keeps its sign bit), d = 512 for window rows or 128 for
+ *       E4M3 indexer keys; dst_stride >= d, a multiple of 8.
+ *   csa2_write_mxfp4_key: per 32-channel group X = floor(log2 amax) - 2, scale byte
+ *       X + 127 kept in 1..254 (127 for an all-zero group), codes E2M1(x * 2^-X); writes
+ *       k_codes[row, 0..64) and k_scales[row, 0..4). x [n,128] bf16.
+ * Calls only enqueue work; overlapping destination rows in one call race.
+ * Errors: CSA2_ERR_INVALID_ARG (null pointer, n < 0, bad stride or alignment),
+ * CSA2_ERR_UNSUPPORTED (csa2_write_e4m3 with d other than 128 or 512). */
+int csa2_write_latent(int n, const void* x, const int64_t* rows, void* kv_fp4,
+                      int64_t kv_fp4_stride, void* kv_scale, int64_t kv_scale_stride,
+                      int64_t n_entries, void* stream);
+int csa2_write_e4m3(int n, int d, const void* x, const int64_t* rows, void* dst,
+                    int64_t dst_stride, int64_t n_rows, void* stream);
+int csa2_write_mxfp4_key(int n, const void* x, const int64_t* rows, void* k_codes,
+                         void* k_scales, int64_t n_entries, void* stream);
+
 /* HSI candidate pool ([V41F-BLOG] 2.3.4 "How does the Full Mode layer build the
  * candidate pool"; [V41F-ARCH] 3). For query t with n = n_visible[t] > 0 there are
  * nb = ceil(n/8) visible blocks whose scores are block_max[t, 0..nb) (the last block's

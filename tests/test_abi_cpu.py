@@ -21,6 +21,7 @@ def test_header_symbols_are_exported(C):
     names = set(re.findall(r"^(?:int|size_t|const char\*)\s+(csa2_\w+)\(", text, re.M))
     assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_index_score_mxfp4",
                      "csa2_block_pool", "csa2_topk", "csa2_pool_topk", "csa2_sparse_attn",
+                     "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
@@ -74,6 +75,23 @@ def test_index_score_mxfp4_rejections(C):
     assert call(n_heads=64) == 2
     assert call(scores=None) == 1
     assert call(n_q=0, k_scales=None, q_idx=None) == 0    # nothing to do, nothing launched
+
+
+def test_cache_write_rejections(C):
+    L = C.lib
+    assert L.csa2_write_latent(-1, FAKE, FAKE, FAKE, 256, FAKE, 32, 10, None) == 1
+    assert L.csa2_write_latent(1, None, FAKE, FAKE, 256, FAKE, 32, 10, None) == 1
+    assert L.csa2_write_latent(1, FAKE, FAKE, FAKE, 255, FAKE, 32, 10, None) == 1   # stride
+    assert L.csa2_write_latent(1, FAKE, FAKE, FAKE, 256, FAKE, 31, 10, None) == 1
+    assert L.csa2_write_latent(1, FAKE + 8, FAKE, FAKE, 256, FAKE, 32, 10, None) == 1
+    assert L.csa2_write_latent(0, None, None, None, 0, None, 0, 0, None) == 0
+    assert L.csa2_write_e4m3(1, 64, FAKE, FAKE, FAKE, 64, 10, None) == 2          # d
+    assert L.csa2_write_e4m3(1, 512, FAKE, FAKE, FAKE, 256, 10, None) == 1        # stride < d
+    assert L.csa2_write_e4m3(1, 128, FAKE, FAKE, FAKE + 4, 128, 10, None) == 1    # dst alignment
+    assert L.csa2_write_e4m3(1, 128, FAKE, None, FAKE, 128, 10, None) == 1
+    assert L.csa2_write_mxfp4_key(1, FAKE, FAKE, FAKE, None, 10, None) == 1
+    assert L.csa2_write_mxfp4_key(1, FAKE, FAKE, FAKE, FAKE, -1, None) == 1
+    assert L.csa2_write_mxfp4_key(0, None, None, None, None, 0, None) == 0
 
 
 def test_topk_and_pool_rejections(C):

@@ -505,3 +505,124 @@ def test_mxfp4_index_score_reindex_parity(C, dev):
         terms[ok] = score_abs_terms(np_u16(q_idx[t]), w[t].cpu().numpy(), kc[start + pos[ok]],
                                     ks[start + pos[ok]])
         assert_scores_close(got[t], ref, terms, f"query {t}")
+
+
+# --------------------------------------------------------------------------- cache writes
+
+def _hard_bf16_rows(n, d, seed):
+    """bf16 rows that exercise the rounding: normal draws at several magnitudes, exact
+    E4M3 and E2M1 midpoints, zeros, subnormal-range values and values past 448."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((n, d), generator=g) * torch.tensor([0.001, 0.1, 1, 10, 100])[
+        torch.randint(0, 5, (n, 1), generator=g)]
+    mags = torch.from_numpy(O.E4M3_POS.astype(np.float32))
+    mids = (mags[:-1] + mags[1:]) / 2
+    k = min(d, mids.numel())
+    x[0, :k] = mids[:k]
+    x[1, :k] = -mids[:k]
+    x[2] = 0.0
+    x[3, : d // 2] = 0.0
+    x[4] = torch.linspace(-600, 600, d)
+    x[5] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, -0.25, -0.75, -5.0, 1e-3,
+                         -1e-3, 2.0 ** -8, 2.0 ** -12]).repeat(d // 16)
+    return x.to(torch.bfloat16)
+
+
+def test_write_latent_exact(C, dev):
+    n, n_entries = 40, 64
+    x = _hard_bf16_rows(n, 512, 31)
+    rows = torch.randperm(n_entries, generator=torch.Generator().manual_seed(2))[:n].to(torch.int64)
+    rows[7] = -1            # dropped
+    rows[9] = n_entries     # out of range: dropped
+    kv_fp4 = torch.full((n_entries, 256), 0xAB, dtype=torch.uint8, device=dev)
+    kv_scale = torch.full((n_entries, 32), 0xCD, dtype=torch.uint8, device=dev)
+    C.csa2_write_latent(x.to(dev), rows.to(dev), kv_fp4, kv_scale)
+    torch.cuda.synchronize()
+    p, s = O.fp4_latent_quantize(x.float().numpy())
+    want_p = np.full((n_entries, 256), 0xAB, np.uint8)
+    want_s = np.full((n_entries, 32), 0xCD, np.uint8)
+    for r in range(n):
+        d = int(rows[r])
+        if 0 <= d < n_entries:
+            want_p[d], want_s[d] = p[r], s[r]
+    assert np.array_equal(kv_fp4.cpu().numpy(), want_p)
+    assert np.array_equal(kv_scale.cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("d", [512, 128])
+def test_write_e4m3_exact(C, dev, d):
+    n, n_rows = 37, 50
+    x = _hard_bf16_rows(n, d, 32 + d)
+    rows = torch.arange(n, dtype=torch.int64) * 3 % n_rows
+    rows[4] = -5
+    dst = torch.full((n_rows, d), 0x5A, dtype=torch.uint8, device=dev)
+    C.csa2_write_e4m3(x.to(dev), rows.to(dev), dst)
+    torch.cuda.synchronize()
+    want = np.full((n_rows, d), 0x5A, np.uint8)
+    q = O.e4m3_round(x.float().numpy())
+    for r in range(n):
+        if int(rows[r]) >= 0:
+            want[int(rows[r])] = q[r]
+    assert np.array_equal(dst.cpu().numpy(), want)
+
+
+def test_write_mxfp4_key_exact(C, dev):
+    n, n_entries = 45, 60
+    x = _hard_bf16_rows(n, 128, 33)
+    x[6] = x[6] * 2.0 ** 60          # large exponents
+    x[8] = x[8] * 2.0 ** -100        # tiny exponents (scale byte clamps at 1)
+    rows = torch.arange(n, dtype=torch.int64)
+    rows[10] = -1
+    k_codes = torch.full((n_entries, 64), 0x11, dtype=torch.uint8, device=dev)
+    k_scales = torch.full((n_entries, 4), 0x22, dtype=torch.uint8, device=dev)
+    C.csa2_write_mxfp4_key(x.to(dev), rows.to(dev), k_codes, k_scales)
+    torch.cuda.synchronize()
+    c, s = O.mxfp4_key_quantize(x.float().numpy())
+    want_c = np.full((n_entries, 64), 0x11, np.uint8)
+    want_s = np.full((n_entries, 4), 0x22, np.uint8)
+    for r in range(n):
+        if int(rows[r]) >= 0:
+            want_c[int(rows[r])], want_s[int(rows[r])] = c[r], s[r]
+    assert np.array_equal(k_codes.cpu().numpy(), want_c)
+    assert np.array_equal(k_scales.cpu().numpy(), want_s)
+
+
+def test_written_cache_reads_back_through_the_read_path(C, dev):
+    """Rows quantised on the GPU and read back by the indexer (MXFP4 keys) and by the
+    attention (FP4 latent, E4M3 window) give the oracle's results on the oracle's own
+    quantisation of the same rows."""
+    g = torch.Generator().manual_seed(40)
+    n = 600
+    lat = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    key = torch.randn((n, 128), generator=g).to(torch.bfloat16)
+    win = torch.randn((128, 512), generator=g).to(torch.bfloat16)
+    rows = torch.arange(n, dtype=torch.int64, device=dev)
+    kv_fp4 = torch.zeros((n, 256), dtype=torch.uint8, device=dev)
+    kv_scale = torch.zeros((n, 32), dtype=torch.uint8, device=dev)
+    k_codes = torch.zeros((n, 64), dtype=torch.uint8, device=dev)
+    k_scales = torch.zeros((n, 4), dtype=torch.uint8, device=dev)
+    window = torch.zeros((128, 512), dtype=torch.uint8, device=dev)
+    C.csa2_write_latent(lat.to(dev), rows, kv_fp4, kv_scale)
+    C.csa2_write_mxfp4_key(key.to(dev), rows, k_codes, k_scales)
+    C.csa2_write_e4m3(win.to(dev), rows[:128], window)
+    q_idx = _bf16((1, 32, 128), g, dev)
+    w = torch.rand((1, 32), generator=g).to(dev)
+    scores = torch.empty((1, n), dtype=torch.float32, device=dev)
+    C.csa2_index_score_mxfp4(C.FULL, q_idx, w, k_codes, k_scales, _i64([0], dev), _i32([n], dev),
+                             scores)
+    idx = torch.empty((1, 512), dtype=torch.int32, device=dev)
+    C.csa2_topk(scores, idx, k=512, n_cols=n)
+    q = _bf16((1, 64, 512), g, dev)
+    out = torch.empty((1, 64, 512), dtype=torch.bfloat16, device=dev)
+    C.csa2_sparse_attn(q, kv_fp4, kv_scale, _i64([0], dev), idx, window, _i64([0], dev),
+                       _i32([128], dev), 1.0 / math.sqrt(512), out)
+    torch.cuda.synchronize()
+    kc, ks = O.mxfp4_key_quantize(key.float().numpy())
+    ref_scores = O.full_scores_mxfp4(np_u16(q_idx[0]), w[0].cpu().numpy(), kc, ks, 0, n, n)
+    terms = score_abs_terms(np_u16(q_idx[0]), w[0].cpu().numpy(), kc, ks)
+    assert_scores_close(scores[0].cpu().numpy(), ref_scores, terms, "rescored keys")
+    p, s = O.fp4_latent_quantize(lat.float().numpy())
+    wq = O.e4m3_round(win.float().numpy())
+    ents = O.gather_attention_entries(idx[0].cpu().numpy(), p, s, 0, wq, 0, 128)
+    ref, _ = O.sparse_attention(O.bf16_decode(np_u16(q[0])), ents, 1.0 / math.sqrt(512))
+    assert_attn_close(out[0].float().cpu().numpy(), ref, "attention over written rows")
