@@ -9,8 +9,9 @@
 //     the subnormal multiple of 2^-9 is rounded the same way; 448 is the largest value;
 //   - E2M1 magnitude thresholds 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5 (the midpoints of
 //     0, .5, 1, 1.5, 2, 3, 4, 6), a midpoint going to the even code;
-//   - main KV: scale = E4M3(amax / 6) per 16 channels, codes = E2M1(x / scale) with an
-//     IEEE float32 division, zero codes for a zero scale;
+//   - main KV: scale = E4M3(amax / 6) per 16 channels (a float32 division), codes = the
+//     E2M1 rounding of the exact quotient x / scale (|x| against each midpoint times the
+//     scale, products that are exact in float32), zero codes for a zero scale;
 //   - MXFP4 keys: per 32 channels the exponent X = floor(log2 amax) - 2 stored as X + 127
 //     kept in 1..254 (127 for an all-zero group), codes = E2M1(x * 2^-X).
 // A destination row outside [0, n_rows) is skipped. Each wavefront lane handles eight
@@ -87,8 +88,17 @@ __global__ __launch_bounds__(CW_THREADS) void latent_write_kernel(
   const float s = e4m3_val(s_code);
   uint32_t packed = 0;
   if (s > 0.f) {
+    // the exact quotient x / s against each grid midpoint: |x| against midpoint * s, exact
+    const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s;
+    const float t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= f32_to_e2m1_rne(__fdiv_rn(f[i], s)) << (4 * i);
+    for (int i = 0; i < 8; ++i) {
+      const float a = fabsf(f[i]);
+      const uint32_t m = (uint32_t)(a > t0) + (uint32_t)(a >= t1) + (uint32_t)(a > t2) +
+                         (uint32_t)(a >= t3) + (uint32_t)(a > t4) + (uint32_t)(a >= t5) +
+                         (uint32_t)(a > t6);
+      packed |= (m | ((f[i] < 0.f && m != 0u) ? 8u : 0u)) << (4 * i);
+    }
   }
   *reinterpret_cast<uint32_t*>(kv_fp4 + dst * fp4_stride + 4 * lane) = packed;
   if ((lane & 1) == 0) kv_scale[dst * sc_stride + (lane >> 1)] = (uint8_t)s_code;

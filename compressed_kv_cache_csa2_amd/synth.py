@@ -107,8 +107,9 @@ def _e4m3_bytes_to_float(b: torch.Tensor) -> torch.Tensor:
 def encode_fp4_rows(x: torch.Tensor):
     """Encode rows of 512 values as E2M1 codes with one E4M3 scale per 16 channels.
 
-    Per group of 16: scale = E4M3(amax / 6); each value x/scale is rounded to the E2M1
-    grid {0, .5, 1, 1.5, 2, 3, 4, 6} (nearest, ties to the even code, saturating at 6).
+    Per group of 16: scale = E4M3(amax / 6); each value's exact quotient x/scale is
+    rounded to the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6} (nearest, ties to the even code,
+    saturating at 6).
     A zero scale gives zero codes. Codes 2m and 2m+1 share byte m, low nibble first.
     Returns (payload uint8 [..., 256], scales uint8 [..., 32]).
     """
@@ -116,10 +117,16 @@ def encode_fp4_rows(x: torch.Tensor):
     g = x.reshape(*x.shape[:-1], x.shape[-1] // 16, 16)
     amax = g.abs().amax(dim=-1)
     s_code = encode_e4m3(amax / 6.0)
-    s = _e4m3_bytes_to_float(s_code)
-    safe = torch.where(s > 0, s, torch.ones_like(s))
-    code = _e2m1_codes(g / safe.unsqueeze(-1))
-    code = torch.where((s > 0).unsqueeze(-1), code, torch.zeros_like(code))
+    s = _e4m3_bytes_to_float(s_code).unsqueeze(-1)
+    # nearest code of the exact quotient g / s: |g| against each grid midpoint times s
+    # (exact in float32), a midpoint going to the even code
+    a = g.abs()
+    code = ((a > 0.25 * s).to(torch.uint8) + (a >= 0.75 * s).to(torch.uint8)
+            + (a > 1.25 * s).to(torch.uint8) + (a >= 1.75 * s).to(torch.uint8)
+            + (a > 2.5 * s).to(torch.uint8) + (a >= 3.5 * s).to(torch.uint8)
+            + (a > 5.0 * s).to(torch.uint8))
+    code = code | (((g < 0) & (code > 0)).to(torch.uint8) << 3)
+    code = torch.where(s > 0, code, torch.zeros_like(code))
     code = code.reshape(x.shape)
     payload = code[..., 0::2] | (code[..., 1::2] << 4)
     return payload.contiguous(), s_code.contiguous()

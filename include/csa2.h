@@ -151,8 +151,9 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
  * caller may pass -1 for a row to drop. Rounding (the pages give none; readings R16 and
  * R19): nearest grid value, ties to the even code, saturating at the grid's largest
  * value, decided on float32 values:
- *   csa2_write_latent: per 16-channel group scale = E4M3(amax / 6) and code =
- *       E2M1(x / scale) (IEEE float32 division); zero codes when the scale is 0. Writes
+ *   csa2_write_latent: per 16-channel group scale = E4M3(amax / 6) (float32 division)
+ *       and code = E2M1 rounding of the exact quotient x / scale; zero codes when the
+ *       scale is 0. Writes
  *       kv_fp4[row, 0..256) (channel 2m in the low nibble of byte m) and
  *       kv_scale[row, 0..32). x [n,512] bf16, 16-byte aligned; rows [n] int64;
  *       kv_fp4_stride >= 256 (multiple of 4), kv_scale_stride >= 32.

@@ -176,6 +176,22 @@ def e2m1_round(y: np.ndarray) -> np.ndarray:
     return mag | (((y < 0) & (mag > 0)).astype(np.uint8) << 3)
 
 
+def e2m1_round_ratio(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """E2M1 codes of the exact quotient x / s (s > 0): nearest grid magnitude, ties to the
+    even code, saturating at 6. |x| is compared with each midpoint times s, which is exact
+    (a midpoint has at most 3 significant bits and an E4M3 scale 4)."""
+    a = np.abs(np.asarray(x, np.float64))
+    s = np.asarray(s, np.float64)
+    mids = (E2M1_POS[:-1] + E2M1_POS[1:]) / 2          # 0.25, 0.75, ..., 5
+    mag = np.zeros(np.broadcast(a, s).shape, np.int64)
+    for i, m in enumerate(mids):
+        t = m * s
+        # the midpoint between codes i and i+1 goes to the even one
+        mag += (a >= t) if (i + 1) % 2 == 0 else (a > t)
+    sign = (np.asarray(x) < 0) & (mag > 0)
+    return (mag | (sign.astype(np.int64) << 3)).astype(np.uint8)
+
+
 def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
     """Codes [..., 2n] -> bytes [..., n], channel 2m in the low nibble of byte m (R4)."""
     return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
@@ -184,17 +200,16 @@ def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
 def fp4_latent_quantize(x: np.ndarray):
     """Main-KV rows (float32 view of bf16) -> (payload [..., 256], scales [..., 32]).
 
-    Reading R16 of [V41F-BLOG] 2.4.4: per 16-channel group the scale is E4M3(amax / 6) and
-    each value is E2M1(x / scale); a zero scale gives zero codes.
+    Reading R16 of [V41F-BLOG] 2.4.4: per 16-channel group the scale is E4M3(amax / 6)
+    (amax / 6 as a float32 division) and each value is the E2M1 rounding of the exact
+    quotient x / scale; a zero scale gives zero codes.
     """
     x = np.asarray(x, np.float32)
     g = x.reshape(x.shape[:-1] + (x.shape[-1] // 16, 16))
     amax = np.abs(g).max(axis=-1)
     s_code = e4m3_round(amax / np.float32(6.0))
-    s = E4M3_TABLE[s_code].astype(np.float32)
-    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-    q = (g / safe[..., None]).astype(np.float32)
-    codes = np.where((s > 0)[..., None], e2m1_round(q), 0).astype(np.uint8)
+    s = E4M3_TABLE[s_code]
+    codes = np.where((s > 0)[..., None], e2m1_round_ratio(g, s[..., None]), 0).astype(np.uint8)
     return _pack_nibbles(codes.reshape(x.shape)), s_code
 
 
