@@ -36,12 +36,13 @@ def _load():
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
     lib.csa2_write_e4m3.argtypes = [I, I, P, P, P, L, L, P]
     lib.csa2_write_mxfp4_key.argtypes = [I, P, P, P, P, L, P]
+    lib.csa2_index_score_shared.argtypes = [I, I, I, P, P, P, L, L, P, P, L, P, L, P]
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
     lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
     lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
-    for f in ("csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
+    for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn"):
         getattr(lib, f).restype = I
@@ -147,6 +148,20 @@ def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
         _ptr(scores, torch.float32, "scores"), ld_scores,
+        _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_index_score_shared(q_idx, w, k_cache, kv_start: int, n_visible, scores,
+                            block_max=None, stream=None):
+    """Full-mode scores of queries that all read the cache from row kv_start (a host int),
+    each up to its own n_visible."""
+    n_q = q_idx.shape[0]
+    _check(lib.csa2_index_score_shared(
+        n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
+        _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+        int(kv_start), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(scores, torch.float32, "scores"), scores.shape[1],
         _ptr(block_max, torch.float32, "block_max"),
         block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 

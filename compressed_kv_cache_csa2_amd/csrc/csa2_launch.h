@@ -17,6 +17,12 @@ hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, cons
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream);
 
+// Full-mode scores of queries that all read the cache rows from one kv_start.
+hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float* w,
+                                     const uint8_t* k_cache, int64_t n_entries, int64_t kv_start,
+                                     const int32_t* n_visible, float* scores, int64_t ld,
+                                     float* block_max, int64_t ld_bm, hipStream_t stream);
+
 hipError_t launch_block_pool(int n_q, const float* block_max, int64_t ld_bm,
                              const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
                              int64_t ld_pool, hipStream_t stream);

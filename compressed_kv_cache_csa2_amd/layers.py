@@ -52,8 +52,13 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
 
 def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
                 stream=None):
-    """The indexer over the workload's keys: MXFP4 when it carries them, else E4M3."""
-    if wl.k_codes is not None:
+    """The indexer over the workload's keys: MXFP4 when it carries them, else E4M3; a Full
+    pass of queries sharing one sequence scores them in groups per cache tile."""
+    if (mode == C.FULL and wl.k_codes is None and wl.shared_start is not None
+            and scores is not None):
+        C.csa2_index_score_shared(lay.q_idx, lay.w, wl.k_cache, wl.shared_start, wl.n_visible,
+                                  scores, block_max, stream=stream)
+    elif wl.k_codes is not None:
         C.csa2_index_score_mxfp4(mode, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
                                  wl.n_visible, scores, block_max, pool_blocks=pool_blocks,
                                  stream=stream, ld_scores=ld_scores)

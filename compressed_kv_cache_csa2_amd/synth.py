@@ -69,6 +69,8 @@ class Workload:
     # MXFP4 copy of the indexer keys (the same draws): codes [E, 64], E8M0 scales [E, 4]
     k_codes: torch.Tensor | None = None
     k_scales: torch.Tensor | None = None
+    # every query reads the cache from this row (chunked prefill), else None
+    shared_start: int | None = None
 
     @property
     def n_entries(self) -> int:
@@ -85,7 +87,7 @@ class Workload:
                         kv_fp4=mv(self.kv_fp4), kv_scale=mv(self.kv_scale), layers=layers,
                         with_pool=self.with_pool, planted=self.planted,
                         softmax_scale=self.softmax_scale, k_codes=mv(self.k_codes),
-                        k_scales=mv(self.k_scales))
+                        k_scales=mv(self.k_scales), shared_start=self.shared_start)
 
 
 # ----------------------------------------------------------------------------- encoders
@@ -298,7 +300,8 @@ def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
         n_q, n_entries, kv_start_t, n_visible_t, n_entries, device, seed, None, lay[0])
     return Workload(name=name, n_q=n_q, n_ctx=max(n_visible), kv_start=kv_start_t.to(device),
                     n_visible=n_visible_t.to(device), k_cache=k_cache, kv_fp4=kv_fp4,
-                    kv_scale=kv_scale, layers=lay, with_pool=False, planted=None)
+                    kv_scale=kv_scale, layers=lay, with_pool=False, planted=None,
+                    shared_start=0)
 
 
 def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:

@@ -121,6 +121,19 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                      float* block_max, int64_t ld_block_max,
                      void* stream);
 
+/* Lightning-indexer score, FULL mode, for queries that share one sequence (chunked
+ * prefill: [V41F-BLOG] 2.3.1 and 3.3.2, with the causal visibility of each query's own
+ * position). Identical to csa2_index_score(CSA2_FULL, ...) with kv_start[t] = kv_start for
+ * every t: slot j < n_visible[t] of query t scores cache row kv_start + j; other slots
+ * hold -inf; block_max as there (nullable). The queries are scored in groups against
+ * each cache tile, so every row is read once per group instead of once per query.
+ * Arguments as csa2_index_score; kv_start is a host value. n_q <= 2^22.
+ * Errors: CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED as csa2_index_score. */
+int csa2_index_score_shared(int n_q, int n_heads, int d_idx, const void* q_idx, const float* w,
+                            const void* k_cache, int64_t n_entries, int64_t kv_start,
+                            const int32_t* n_visible, float* scores, int64_t ld_scores,
+                            float* block_max, int64_t ld_block_max, void* stream);
+
 /* Lightning-indexer score over MXFP4 indexer keys ([V41F-BLOG] 2.4.4: the indexer cache
  * is FP4 in the OCP MXFP4 format; 3.1: a 128-dimensional MXFP4 indexer K entry is its
  * E2M1 payload plus one scale byte per 32 channels). Identical to csa2_index_score (same

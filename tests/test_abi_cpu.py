@@ -22,6 +22,7 @@ def test_header_symbols_are_exported(C):
     assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_index_score_mxfp4",
                      "csa2_block_pool", "csa2_topk", "csa2_pool_topk", "csa2_sparse_attn",
                      "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
+                     "csa2_index_score_shared",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
@@ -75,6 +76,25 @@ def test_index_score_mxfp4_rejections(C):
     assert call(n_heads=64) == 2
     assert call(scores=None) == 1
     assert call(n_q=0, k_scales=None, q_idx=None) == 0    # nothing to do, nothing launched
+
+
+def test_index_score_shared_rejections(C):
+    L = C.lib
+    ok = [1, 32, 128, FAKE, FAKE, FAKE, 10, 0, FAKE, FAKE, 16, None, 0, None]
+    def call(**kw):
+        a = list(ok)
+        names = ["n_q", "n_heads", "d_idx", "q_idx", "w", "k_cache", "n_entries", "kv_start",
+                 "n_visible", "scores", "ld", "block_max", "ld_bm", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.csa2_index_score_shared(*a)
+    assert call(n_heads=16) == 2
+    assert call(scores=None) == 1
+    assert call(q_idx=FAKE + 8) == 1
+    assert call(ld=0) == 1
+    assert call(block_max=FAKE, ld_bm=1) == 1
+    assert call(n_q=-1) == 1
+    assert call(n_q=0, q_idx=None) == 0
 
 
 def test_cache_write_rejections(C):

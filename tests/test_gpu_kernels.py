@@ -626,3 +626,34 @@ def test_written_cache_reads_back_through_the_read_path(C, dev):
     ents = O.gather_attention_entries(idx[0].cpu().numpy(), p, s, 0, wq, 0, 128)
     ref, _ = O.sparse_attention(O.bf16_decode(np_u16(q[0])), ents, 1.0 / math.sqrt(512))
     assert_attn_close(out[0].float().cpu().numpy(), ref, "attention over written rows")
+
+
+def test_index_score_shared_equals_per_query_and_oracle(C, dev):
+    """Queries sharing one sequence (ragged causal n_visible, a batch that is not a multiple
+    of the group size, rows past the cache end): the grouped kernel writes the per-query
+    kernel's scores and block maxima bit for bit, and both match the oracle."""
+    g = torch.Generator().manual_seed(50)
+    n_q, n_entries, start, ld = 19, 9000, 300, 8800
+    k_cache = _e4m3((n_entries, 128), g, dev)
+    q_idx = _bf16((n_q, 32, 128), g, dev)
+    w = torch.rand((n_q, 32), generator=g).to(dev)
+    nv = [0, 1, 7, 8, 9, 2047, 2048, 2049, 4100, 6000, 8699, 8700, 8701, 8800, 123, 5000, 3,
+          8000, 8750]
+    n_vis = _i32(nv, dev)
+    a = torch.empty((n_q, ld), dtype=torch.float32, device=dev)
+    ab = torch.empty((n_q, (ld + 7) // 8), dtype=torch.float32, device=dev)
+    b, bb = torch.empty_like(a), torch.empty_like(ab)
+    C.csa2_index_score_shared(q_idx, w, k_cache, start, n_vis, a, ab)
+    C.csa2_index_score(C.FULL, q_idx, w, k_cache, _i64([start] * n_q, dev), n_vis, b, bb)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ab, bb)
+    k_all = k_cache.cpu().numpy()
+    got = a.cpu().numpy()
+    for t in (0, 1, 5, 7, 11, 12, 13, 18):
+        n_rows = max(0, min(nv[t], n_entries - start))
+        ref = O.full_scores(np_u16(q_idx[t]), w[t].cpu().numpy(), k_all, start, n_rows, ld)
+        terms = np.zeros(ld)
+        if n_rows:
+            terms[:n_rows] = score_abs_terms(np_u16(q_idx[t]), w[t].cpu().numpy(),
+                                             k_all[start:start + n_rows])
+        assert_scores_close(got[t], ref, terms, f"query {t}")
