@@ -174,124 +174,127 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
 // ---------------------------------------------------------------------------------------
 // Queries that share one sequence (chunked prefill: every query reads the same cache rows
 // from kv_start, each up to its own causal n_visible). A workgroup scores SQ_QT queries
-// against the same 2,048-row tile, so every row is read and converted once per SQ_QT
-// queries instead of once per query. The queries' MFMA operands sit in LDS in operand
-// order (one contiguous 1 KiB read per product) with the per-lane head weights; a
-// wavefront converts a 32-row step once and runs SQ_QT x 8 products on it. Scores go out
-// per query and step (the rows are cache hits here, so interleaved stores cost little).
-constexpr int SQ_QT = 8;
-
-struct SharedQ {
-  u32x4 qop[SQ_QT][8][64];     // 64 KiB: bf16x8 A operand of query q, k-block kb, lane
-  float4 wl[SQ_QT][2][4];      // head weights of lane half h, rows r = 4i + j
-  int nv[SQ_QT];
-};
+// (SQ_QW per wavefront, their MFMA operands and head weights held in registers) against
+// one 2,048-row tile. Per 32-row step the four wavefronts each load and convert a quarter
+// of the rows' channels into an LDS buffer in B-operand order (double-buffered, one barrier
+// per step); then every wavefront reads the step's 8 operands once and runs its queries'
+// products on them. Rows are read and converted once per SQ_QT queries, and the LDS
+// traffic is one 8 KiB operand read per wavefront and step.
+constexpr int SQ_QW = 2;
+constexpr int SQ_QT = (IS_THREADS / 64) * SQ_QW;
+constexpr int SQ_TILE = 2048;
 
 __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
     int n_q, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, int64_t n_entries, int64_t kv_start,
     const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
     float* __restrict__ block_max, int64_t ld_bm) {
-  __shared__ SharedQ sh;
+  __shared__ u32x4 bsh[2][8][64];   // converted rows of a step: k-block kb, lane
+  __shared__ int nv_sh[SQ_QT];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int half = lane >> 5;
   const int t0 = blockIdx.y * SQ_QT;
 
-  // Stage the group's queries: entry (q, kb, l) = channels 64*(l/32) + 8*kb .. +7 of head
-  // l%32 (the operand layout of the per-query kernel); absent queries are zeros.
-  for (int e = tid; e < SQ_QT * 8 * 64; e += IS_THREADS) {
-    const int q = e / 512, kb = (e / 64) % 8, l = e % 64;
-    const int t = t0 + q;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < n_q)
-      v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)t * 32 + (l & 31)) * 128 +
-                                          64 * (l >> 5) + 8 * kb);
-    sh.qop[q][kb][l] = v;
+  // This wavefront's queries: operands (channels 64*half + 8*kb .. +7 of head n), weights.
+  bf16x8 a[SQ_QW][8];
+  float wr[SQ_QW][16];
+  int nvq[SQ_QW];
+#pragma unroll
+  for (int j = 0; j < SQ_QW; ++j) {
+    const int t = t0 + SQ_QW * wave + j;
+    const bool ok = t < n_q;
+    const uint16_t* qrow = q_idx + ((int64_t)(ok ? t : 0) * 32 + n) * 128 + 64 * half;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+      a[j][kb] = ok ? v : bf16x8{};
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wr[j][r] = ok ? w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] : 0.f;
+    nvq[j] = ok ? n_visible[t] : 0;
   }
-  if (tid < SQ_QT * 2 * 16) {
-    const int q = tid / 32, h = (tid / 16) % 2, r = tid % 16;
-    const int t = t0 + q;
-    reinterpret_cast<float*>(&sh.wl[q][h][0])[r] =
-        t < n_q ? w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * h + (r & 3)] : 0.f;
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < SQ_QW; ++j) nv_sh[SQ_QW * wave + j] = nvq[j];
   }
-  if (tid < SQ_QT) sh.nv[tid] = t0 + tid < n_q ? n_visible[t0 + tid] : 0;
   __syncthreads();
-
   int nv_max = 0;
 #pragma unroll
-  for (int q = 0; q < SQ_QT; ++q) nv_max = max(nv_max, sh.nv[q]);
-  constexpr int IS_TILE = (IS_THREADS / 64) * IS_STEPS_FULL * 32;
-  const int64_t tile0 = (int64_t)blockIdx.x * IS_TILE + (int64_t)wave * 32;
-  auto slot_at = [&](int step) -> int64_t { return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n; };
-  // A row is read when some query of the group sees it; each query masks its own.
+  for (int q = 0; q < SQ_QT; ++q) nv_max = max(nv_max, nv_sh[q]);
+
+  const int64_t tile0 = (int64_t)blockIdx.x * SQ_TILE;
+  constexpr int STEPS = SQ_TILE / 32;
+  const bool any = nv_max > 0 && kv_start >= 0 && kv_start < n_entries;
+  // Lane (n, half) of wavefront w loads bytes 64*half + 16*w .. +15 of row n of a step:
+  // k-blocks 2w and 2w+1 of the B operand. A row is read when some query of the group sees
+  // it; each query masks its own.
   auto row_at = [&](int step) -> int64_t {
-    const int64_t slot = slot_at(step);
+    const int64_t slot = tile0 + (int64_t)step * 32 + n;
     if (slot >= ld || slot >= nv_max) return -1;
     const int64_t row = kv_start + slot;
     return (row >= 0 && row < n_entries) ? row : -1;
   };
-  const bool any = nv_max > 0 && kv_start >= 0 && kv_start < n_entries;
-  u32x4 buf[2][4];
-  auto load_step = [&](int step, u32x4 (&raw)[4]) {
+  constexpr int PF = 4;   // steps whose rows are in flight
+  u32x4 raw[PF];
+  auto load = [&](int step) -> u32x4 {
     const int64_t r = row_at(step);
-    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : kv_start) * 128 + 64 * half);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+    return *reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : kv_start) * 128 + 64 * half +
+                                           16 * wave);
   };
-  if (any) load_step(0, buf[0]);
+  if (any) {
 #pragma unroll
-  for (int step = 0; step < IS_STEPS_FULL; ++step) {
-    const int64_t slot = slot_at(step);
-    const bool row_ok = any && row_at(step) >= 0;
-    u32x4 bop[8];
-    if (any) {
-      if (step + 1 < IS_STEPS_FULL) load_step(step + 1, buf[(step + 1) & 1]);
-      u32x4 (&raw)[4] = buf[step & 1];
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const u32x2 lo = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2]);
-        const u32x2 hi = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2 + 1]);
-        bop[kb] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    }
+    for (int i = 0; i < PF; ++i) raw[i] = load(i);
+  }
 #pragma unroll 1
-    for (int q = 0; q < SQ_QT; ++q) {
-      const int t = t0 + q;
-      if (t >= n_q) break;   // uniform: queries past the batch
-      float sv = -__builtin_inff();
+  for (int step0 = 0; step0 < STEPS; step0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int step = step0 + i;
+      const int buf = step & 1;
+      const int64_t slot = tile0 + (int64_t)step * 32 + n;
+      const bool row_ok = any && row_at(step) >= 0;
       if (any) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, sh.qop[q][kb][lane]), __builtin_bit_cast(bf16x8, bop[kb]),
-              acc, 0, 0, 0);
-        // the same accumulation order as the per-query kernel, so the scores are identical
-        float wr[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 wv = sh.wl[q][half][i];
-          wr[4 * i] = wv.x;
-          wr[4 * i + 1] = wv.y;
-          wr[4 * i + 2] = wv.z;
-          wr[4 * i + 3] = wv.w;
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
-        part += __shfl_xor(part, 32);
-        if (row_ok && slot < sh.nv[q]) sv = part;
+        const u32x4 v = raw[i];
+        if (step + PF < STEPS) raw[i] = load(step + PF);
+        const u32x2 l0 = e4m3x4_to_bf16x4(v.x), h0 = e4m3x4_to_bf16x4(v.y);
+        const u32x2 l1 = e4m3x4_to_bf16x4(v.z), h1 = e4m3x4_to_bf16x4(v.w);
+        bsh[buf][2 * wave][lane] = u32x4{l0.x, l0.y, h0.x, h0.y};
+        bsh[buf][2 * wave + 1][lane] = u32x4{l1.x, l1.y, h1.x, h1.y};
       }
-      if (slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
-      if (block_max != nullptr) {
-        float m = sv;
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        if (half == 0 && (n & 7) == 0 && slot < ld) block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
+      __syncthreads();
+      u32x4 b[8];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) b[kb] = bsh[buf][kb][lane];
+#pragma unroll
+      for (int j = 0; j < SQ_QW; ++j) {
+        const int t = t0 + SQ_QW * wave + j;
+        float sv = -__builtin_inff();
+        if (any) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kb], __builtin_bit_cast(bf16x8, b[kb]),
+                                                          acc, 0, 0, 0);
+          // the same accumulation order as the per-query kernel: identical scores
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part += wr[j][r] * fmaxf(acc[r], 0.f);
+          part += __shfl_xor(part, 32);
+          if (row_ok && slot < nvq[j]) sv = part;
+        }
+        if (t < n_q && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+        if (block_max != nullptr) {
+          float m = sv;
+          m = fmaxf(m, __shfl_xor(m, 1));
+          m = fmaxf(m, __shfl_xor(m, 2));
+          m = fmaxf(m, __shfl_xor(m, 4));
+          if (t < n_q && half == 0 && (n & 7) == 0 && slot < ld)
+            block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
+        }
       }
     }
   }
@@ -301,8 +304,7 @@ hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float
                                      const uint8_t* k_cache, int64_t n_entries, int64_t kv_start,
                                      const int32_t* n_visible, float* scores, int64_t ld,
                                      float* block_max, int64_t ld_bm, hipStream_t stream) {
-  const int tile = (IS_THREADS / 64) * IS_STEPS_FULL * 32;
-  dim3 grid((unsigned)((ld + tile - 1) / tile), (unsigned)((n_q + SQ_QT - 1) / SQ_QT));
+  dim3 grid((unsigned)((ld + SQ_TILE - 1) / SQ_TILE), (unsigned)((n_q + SQ_QT - 1) / SQ_QT));
   hipLaunchKernelGGL(index_score_shared_kernel, grid, dim3(IS_THREADS), 0, stream, n_q, q_idx, w,
                      k_cache, n_entries, kv_start, n_visible, scores, ld, block_max, ld_bm);
   return hipGetLastError();
