@@ -379,6 +379,52 @@ def hsi_pool(scores: np.ndarray, n_visible: int, block_size: int = 8,
     return topk_slots(bm, n_keep)
 
 
+# --------------------------------------------------------------------------------------
+# HISA-style block-mean coarse filter (the alternative the pages contrast HSI with)
+# --------------------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values -> bf16 bit patterns, nearest with ties to even (finite inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def block_mean_keys(k_codes: np.ndarray, n_visible: int, block_size: int = 8) -> np.ndarray:
+    """Mean indexer key of each block of 8 visible positions, as bf16 bits [nb, 128].
+
+    [V41F-BLOG] 2.3.4 (the HISA paragraphs): the prefix is cut into blocks of consecutive
+    positions and each block keeps the mean of its indexer keys, which a first stage
+    scores. Reading R20: the mean runs over the block's visible positions (the last block
+    may be partial); the sum of E4M3 values is exact in float32, the division by the count
+    is a float32 division, and the mean is stored as bf16 (nearest even). The sum starts
+    from +0, so a block of negative zeros has mean +0.
+    """
+    n = int(n_visible)
+    nb = -(-n // block_size)
+    rows = e4m3_decode(np.asarray(k_codes, np.uint8)[:n])
+    out = np.zeros((nb, rows.shape[1]), np.uint16)
+    for b in range(nb):
+        blk = rows[block_size * b:min(n, block_size * b + block_size)]
+        mean32 = np.float32(blk.sum(axis=0)) / np.float32(blk.shape[0])
+        out[b] = f32_to_bf16_bits(mean32)
+    return out
+
+
+def hisa_pool(q_idx: np.ndarray, w: np.ndarray, km_bits: np.ndarray, n_visible: int,
+              block_size: int = 8, n_keep: int = 2048) -> np.ndarray:
+    """First stage of the block-mean filter for one query: score every block's mean key
+    with the indexer and keep the top min(n_keep, #blocks) blocks, the block holding the
+    latest visible position forced in as in the HSI pool (reading R13), ascending ids."""
+    n = int(n_visible)
+    if n <= 0:
+        return np.zeros(0, dtype=np.int64)
+    bs = index_score_rows(bf16_decode(q_idx), np.asarray(w, np.float64), bf16_decode(km_bits))
+    bs[(n - 1) // block_size] = np.inf
+    return topk_slots(bs, n_keep)
+
+
 def pool_bitmap(blocks: np.ndarray, n_visible: int, block_size: int = 8) -> np.ndarray:
     """The pool as a position bitmap: each kept block's flag repeated 8 times and cut to
     the visible width ([V41F-BLOG] 2.3.4)."""

@@ -446,3 +446,103 @@ def test_write_quantisers_equal_the_input_generator():
     d = O.fp4_latent_decode(p, s)
     step = np.repeat(O.E4M3_TABLE[s], 16, axis=-1)
     assert np.all(np.abs(d - lat.numpy()) <= step * 2.0 + 1e-30)
+
+
+# ------------------------------------------------------------------ block-mean (HISA) filter
+
+def _e4m3_codes_torch(values):
+    """E4M3 codes of values exactly representable in E4M3, through torch's cast."""
+    t = torch.as_tensor(np.asarray(values, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _bf16_bits_torch(values):
+    t = torch.as_tensor(np.asarray(values, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_block_mean_keys_closed_forms():
+    rng = np.random.default_rng(31)
+    # a block of 8 equal rows has that row as its mean (E4M3 values are exact in bf16; a
+    # sum starts from +0, so a block of negative zeros has mean +0)
+    row = rng.integers(0, 0x7E, size=128).astype(np.uint8) ^ (rng.integers(0, 2, 128).astype(np.uint8) << 7)
+    km = O.block_mean_keys(np.tile(row, (8, 1)), 8)
+    assert km.shape == (1, 128)
+    want = _bf16_bits_torch(torch.from_numpy(row).view(torch.float8_e4m3fn).float().numpy() + 0.0)
+    assert np.array_equal(km[0], want)
+    # channel 0 holds 1..8 in block 0 (mean 4.5) and 1, 1, 2 in a 3-row tail (4/3, rounded
+    # once to float32 and then to bf16); channel 1 holds -3 everywhere
+    vals = np.zeros((11, 128), np.float32)
+    vals[:8, 0] = np.arange(1, 9)
+    vals[8:, 0] = [1, 1, 2]
+    vals[:, 1] = -3
+    km = O.block_mean_keys(_e4m3_codes_torch(vals), 11)
+    assert km.shape == (2, 128)
+    got = torch.from_numpy(km.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert got[0, 0] == 4.5 and got[0, 1] == -3 and got[1, 1] == -3
+    assert km[1, 0] == _bf16_bits_torch([np.float32(4) / np.float32(3)])[0]
+    assert np.all(got[:, 2:] == 0)
+
+
+def test_block_mean_keys_within_half_a_bf16_step_of_the_exact_mean():
+    rng = np.random.default_rng(32)
+    n = 8 * 37 + 5
+    codes = rng.integers(0, 0x7E, size=(n, 128)).astype(np.uint8) ^ (rng.integers(0, 2, size=(n, 128)).astype(np.uint8) << 7)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    km = O.block_mean_keys(codes, n)
+    assert km.shape == (38, 128)
+    got = torch.from_numpy(km.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for b in range(38):
+        exact = vals[8 * b:min(n, 8 * b + 8)].mean(axis=0)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
+        assert np.all(np.abs(got[b] - exact) <= 0.5 * ulp * (1 + 2 ** -16) + 1e-300), b
+    # fewer visible positions than rows: the tail is ignored
+    assert np.array_equal(O.block_mean_keys(codes, 20), O.block_mean_keys(codes[:20], 20))
+    assert O.block_mean_keys(codes, 0).shape == (0, 128)
+
+
+def test_hisa_pool_reduces_to_the_hsi_pool_on_constant_blocks():
+    """When the 8 keys of every block are equal, each block mean is that key, so the
+    block-mean scores equal the position scores of the block and the two-stage filter's
+    pool is the HSI block-max pool."""
+    rng = np.random.default_rng(33)
+    n = 8 * 3000 + 5
+    nb = -(-n // 8)
+    blk = rng.integers(0, 0x7E, size=(nb, 128)).astype(np.uint8) ^ (rng.integers(0, 2, size=(nb, 128)).astype(np.uint8) << 7)
+    codes = np.repeat(blk, 8, axis=0)[:n]
+    q = torch.from_numpy(rng.standard_normal((32, 128)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().view(np.uint16)
+    w = rng.random(32).astype(np.float32)
+    km = O.block_mean_keys(codes, n)
+    pool = O.hisa_pool(q_bits, w, km, n)
+    s = O.full_scores(q_bits, w, codes, 0, n, n)
+    assert np.array_equal(pool, O.hsi_pool(s, n))
+    assert len(pool) == 2048 and nb - 1 in pool and np.all(np.diff(pool) > 0)
+    # zero keys in the latest block score 0, the lowest possible: it is still kept
+    codes0 = codes.copy()
+    codes0[8 * (nb - 1):] = 0
+    pool0 = O.hisa_pool(q_bits, w, O.block_mean_keys(codes0, n), n)
+    assert nb - 1 in pool0
+    # a short context keeps every block; an empty one keeps none
+    assert np.array_equal(O.hisa_pool(q_bits, w, O.block_mean_keys(codes, 1000), 1000),
+                          np.arange(125))
+    assert len(O.hisa_pool(q_bits, w, km[:0], 0)) == 0
+
+
+def test_block_mean_dilutes_an_isolated_peak():
+    """The property the HSI section contrasts with: one strong key among seven weak ones
+    keeps its full score under the block max but only a share of it under the block mean."""
+    q = np.zeros((32, 128), np.float32)
+    q[:, 0] = 1.0
+    q_bits = _bf16_bits_torch(q)
+    w = np.ones(32, np.float32)
+    vals = np.zeros((16, 128), np.float32)
+    vals[3, 0] = 8.0                       # block 0: one peak
+    vals[8:, 0] = 1.5                      # block 1: uniformly moderate
+    codes = _e4m3_codes_torch(vals)
+    s = O.full_scores(q_bits, w, codes, 0, 16, 16)
+    bm = O.block_max(s)
+    assert bm[0] > bm[1]                   # block max ranks the peak first
+    km = O.block_mean_keys(codes, 16)
+    bs = O.index_score_rows(O.bf16_decode(q_bits), w.astype(np.float64), O.bf16_decode(km))
+    assert bs[0] == 32 * 1.0 and bs[1] == 32 * 1.5 and bs[0] < bs[1]
