@@ -22,6 +22,12 @@ kernel), read from the committed counter summary; null when the indexer source h
 since the counters were taken. `--profile-kernel` runs only the indexer and the copy, for
 those counter runs.
 
+--coarse hisa swaps the HSI pool for the block-mean two-stage filter in every indexer layer
+(block means resident, as a decoder keeps them up to date); the dominant kernel is then the
+block-mean scorer (256 B of bf16 mean key read + 4 B of score written per (query, block)).
+--recall adds the planted-needle recall of the first indexer layer's pool and Top-K under
+both filters.
+
 cpu_baseline: the fp64 oracle (oracle/) run on the host over a bounded sample of the same
 workload's queries (whole layer stack per query), scaled to queries/s.
 """
@@ -74,6 +80,50 @@ def full_indexer(wl, buf, C, stream=None):
                        buf.block_max, ld_scores=buf.scores.shape[1], stream=stream)
 
 
+def hisa_stage1(wl, buf, C, means, stream=None):
+    """First stage of the block-mean filter for the first indexer layer."""
+    lay = wl.layers[0]
+    C.csa2_index_score_bf16(C.FULL, lay.q_idx, lay.w, means.km, means.km_start, means.n_blocks,
+                            buf.block_max, stream=stream)
+
+
+def hisa_stage1_bytes(wl):
+    import torch
+    blocks = int(((wl.n_visible.to(torch.int64) + 7) // 8).sum())
+    return blocks * (256 + 4) + wl.n_q * (32 * 128 * 2 + 32 * 4)
+
+
+def needle_recall(wl, buf, C, means):
+    """Share of the planted positions that the first indexer layer's pool and Top-K keep,
+    under the HSI pool and under the block-mean filter."""
+    import torch
+    from compressed_kv_cache_csa2_amd import layers
+    planted = wl.planted.cpu()
+    nv = wl.n_visible.cpu()
+    lay = wl.layers[0]
+    out = {}
+    for coarse in ("hsi", "hisa"):
+        if coarse == "hsi":
+            layers.index_score(wl, C.FULL, lay, None, buf.block_max,
+                               ld_scores=buf.scores.shape[1])
+            C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool)
+            layers.index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool)
+            C.csa2_topk(buf.re_scores, buf.idx[0], pool_blocks=buf.pool)
+        else:
+            layers.hisa_select(wl, lay, buf, means, buf.idx[0])
+        torch.cuda.synchronize()
+        pool, idx = buf.pool.cpu(), buf.idx[0].cpu()
+        n_in_pool = n_in_topk = n_all = 0
+        for t in range(wl.n_q):
+            p = torch.unique(planted[t][planted[t] < nv[t]])
+            n_all += p.numel()
+            n_in_pool += int(torch.isin(p // 8, pool[t]).sum())
+            n_in_topk += int(torch.isin(p, idx[t].to(torch.int64)).sum())
+        out[coarse] = {"pool": n_in_pool / max(1, n_all), "topk": n_in_topk / max(1, n_all),
+                       "needles": n_all}
+    return out
+
+
 def profile_kernels(wl, buf, C, launches):
     """Only the Full-layer indexer and a plain copy of COPY_BYTES, for counter collection."""
     import torch
@@ -87,15 +137,20 @@ def profile_kernels(wl, buf, C, launches):
           file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, k=512):
+def algorithmic_bytes(wl, k=512, coarse="hsi"):
     """Bytes the method must move per step: every visible indexer-K row of a Full layer,
     the pool's rows of a Reindex layer, and per attention layer the selected FP4 rows
-    (288 B), the 128 FP8 window rows (512 B), the 64x512 bf16 query and output."""
+    (288 B), the 128 FP8 window rows (512 B), the 64x512 bf16 query and output. Under the
+    block-mean filter every indexer layer reads its blocks' bf16 mean keys (256 B per 8
+    positions) and the pool's rows."""
     import torch
     nv = wl.n_visible.to(torch.int64).cpu()
     total = 0
     for lay in wl.layers:
-        if lay.mode == "full":
+        if coarse == "hisa" and lay.mode in ("full", "reindex"):
+            total += int(((nv + 7) // 8).sum()) * 256
+            total += int(torch.clamp(nv, max=16384).sum()) * key_bytes(wl)
+        elif lay.mode == "full":
             total += int(nv.sum()) * key_bytes(wl)
         elif lay.mode == "reindex":
             total += int(torch.clamp(nv, max=16384).sum()) * key_bytes(wl)
@@ -172,6 +227,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--breakdown", action="store_true", help="per-call timings to stderr")
+    ap.add_argument("--coarse", choices=("hsi", "hisa"), default="hsi",
+                    help="coarse filter of the indexer layers (pooled stacks)")
+    ap.add_argument("--recall", action="store_true",
+                    help="planted-needle recall of the first indexer layer under both filters")
     ap.add_argument("--profile-kernel", type=int, default=0, metavar="N",
                     help="only launch the Full indexer and a 1 GiB copy N times (counter runs)")
     args = ap.parse_args()
@@ -194,13 +253,22 @@ def main():
     print(f"[bench] {args.workload}: generated in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     buf = layers.alloc_buffers(wl)
+    hisa = args.coarse == "hisa"
+    means = None
+    if hisa or args.recall:
+        if not wl.with_pool or wl.k_codes is not None:
+            print("--coarse hisa / --recall need a pooled decoder workload with E4M3 keys",
+                  file=sys.stderr)
+            sys.exit(2)
+        means = layers.build_block_means(wl)
+        torch.cuda.synchronize()
     if args.profile_kernel:
         profile_kernels(wl, buf, C, args.profile_kernel)
         return
     stream = torch.cuda.Stream()
 
     def step():
-        layers.run_layers(wl, buf, stream=stream)
+        layers.run_layers(wl, buf, stream=stream, coarse=args.coarse, means=means)
 
     with torch.cuda.stream(stream):
         step()
@@ -210,7 +278,7 @@ def main():
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            layers.run_layers(wl, buf, stream=stream)
+            layers.run_layers(wl, buf, stream=stream, coarse=args.coarse, means=means)
         torch.cuda.synchronize()
         run = graph.replay
     else:
@@ -234,18 +302,25 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall "
           f"{wall / args.steps * 1e6:.1f} us/step)", file=sys.stderr, flush=True)
 
-    # Dominant kernel: the Full-layer indexer, launched back to back on `stream`.
+    # Dominant kernel: the Full-layer indexer (or the block-mean scorer), launched back to
+    # back on `stream`.
+    def dominant():
+        if hisa:
+            hisa_stage1(wl, buf, C, means, stream=stream)
+        else:
+            full_indexer(wl, buf, C, stream=stream)
+
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        full_indexer(wl, buf, C, stream=stream)
+        dominant()
         e0.record(stream)
         for _ in range(args.steps):
-            full_indexer(wl, buf, C, stream=stream)
+            dominant()
         e1.record(stream)
     torch.cuda.synchronize()
     idx_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    idx_bytes = indexer_bytes_per_launch(wl)
+    idx_bytes = hisa_stage1_bytes(wl) if hisa else indexer_bytes_per_launch(wl)
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
 
     if args.breakdown:
@@ -257,7 +332,21 @@ def main():
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    if part == "score" and lay.mode == "full":
+                    if hisa and lay.mode in ("full", "reindex") and part != "attn":
+                        if part == "score":
+                            C.csa2_index_score_bf16(C.FULL, lay.q_idx, lay.w, means.km,
+                                                    means.km_start, means.n_blocks,
+                                                    buf.block_max, stream=stream)
+                        elif part == "pool":
+                            C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool,
+                                              stream=stream)
+                        elif part == "rescore":
+                            layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
+                                               pool_blocks=buf.pool, stream=stream)
+                        else:
+                            C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
+                                        stream=stream)
+                    elif part == "score" and lay.mode == "full":
                         full_indexer(wl, buf, C, stream=stream)
                     elif part == "rescore" and lay.mode == "full" and wl.with_pool:
                         layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
@@ -289,7 +378,8 @@ def main():
         for n, (a, b) in zip(names, evs):
             print(f"[bench] {n:24s} {a.elapsed_time(b) * 1e3:9.1f} us", file=sys.stderr)
 
-    step_bytes = algorithmic_bytes(wl)
+    recall = needle_recall(wl, buf, C, means) if args.recall else None
+    step_bytes = algorithmic_bytes(wl, coarse=args.coarse)
     value = wl.n_q / (ms_step * 1e-3)
     cpu = None
     if not args.no_cpu_baseline:
@@ -311,18 +401,23 @@ def main():
                    "layers": [l.mode for l in wl.layers], "index_topk": 512,
                    "sliding_window": 128, "pool_blocks": 2048 if wl.with_pool else 0,
                    "indexer_keys": "mxfp4" if wl.k_codes is not None else "e4m3",
+                   "coarse_filter": args.coarse,
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name),
-                     "kernel": "index_score_kernel (Full-layer indexer"
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None if hisa else measured_traffic(wl.name),
+                     "kernel": "index_score_kernel (block-mean scorer, bf16 mean keys)" if hisa
+                               else "index_score_kernel (Full-layer indexer"
                                + (", MXFP4 keys" if wl.k_codes is not None else ", E4M3 keys")
                                + (", block maxima only)" if wl.with_pool else ")"),
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,
     }
+    if recall is not None:
+        line["needle_recall"] = recall
     print(json.dumps(line), flush=True)
 
 

@@ -33,6 +33,8 @@ def _load():
     P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
     lib.csa2_write_e4m3.argtypes = [I, I, P, P, P, L, L, P]
     lib.csa2_write_mxfp4_key.argtypes = [I, P, P, P, P, L, P]
@@ -44,7 +46,7 @@ def _load():
                                      P, Z, P]
     for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
-              "csa2_sparse_attn"):
+              "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -182,6 +184,42 @@ def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visibl
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_codes, torch.uint8, "k_codes"),
         _ptr(k_scales, torch.uint8, "k_scales"), k_codes.shape[0],
+        _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
+        _ptr(scores, torch.float32, "scores"), ld_scores,
+        _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_block_mean_keys(k_cache, kv_start, n_visible, km, km_start, n_blocks, max_blocks=None,
+                         stream=None):
+    """Block-mean keys (bf16, one row per 8 visible positions) of each query's E4M3 keys
+    into km [R, 128] from row km_start[t]; n_blocks [n_q] int32 receives ceil(n_visible/8).
+    max_blocks defaults to what fits in km."""
+    n_q = kv_start.shape[0]
+    if km.dim() != 2 or km.shape[1] != 128:
+        raise ValueError("csa2_block_mean_keys: km must be [rows, 128]")
+    if max_blocks is None:
+        max_blocks = max(1, km.shape[0])
+    _check(lib.csa2_block_mean_keys(
+        n_q, 128, 8, _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+        _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(km, torch.bfloat16, "km"), _ptr(km_start, torch.int64, "km_start"), km.shape[0],
+        int(max_blocks), _ptr(n_blocks, torch.int32, "n_blocks"), _stream(stream)))
+
+
+def csa2_index_score_bf16(mode, q_idx, w, k_rows, kv_start, n_visible, scores, block_max=None,
+                          pool_blocks=None, stream=None, ld_scores=None):
+    """csa2_index_score over bf16 key rows k_rows [E, 128] (the block-mean keys)."""
+    n_q = q_idx.shape[0]
+    n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
+    if scores is not None:
+        ld_scores = scores.shape[1]
+    elif ld_scores is None:
+        raise ValueError("csa2_index_score_bf16: ld_scores is required when scores is None")
+    _check(lib.csa2_index_score_bf16(
+        mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
+        _ptr(w, torch.float32, "w"), _ptr(k_rows, torch.bfloat16, "k_rows"), k_rows.shape[0],
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
         _ptr(scores, torch.float32, "scores"), ld_scores,

@@ -57,9 +57,11 @@ size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k) {
   return 0;
 }
 
-// Both indexer-key formats: k_scales is NULL for E4M3 keys and the E8M0 scale rows for
-// MXFP4 keys (whose codes are then k_cache). `fn` names the entry point in messages.
-static int index_score_common(const char* fn, csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+// Every indexer-key format: key_format 0 (E4M3 rows, k_scales NULL), 1 (MXFP4 codes in
+// k_cache, E8M0 scale rows in k_scales) or 2 (bf16 rows, k_scales NULL). `fn` names the
+// entry point in messages.
+static int index_score_common(const char* fn, int key_format, csa2_mode_t mode, int n_q,
+                              int n_heads, int d_idx,
                               const void* q_idx, const float* w, const void* k_cache,
                               const void* k_scales, int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
@@ -103,7 +105,8 @@ static int index_score_common(const char* fn, csa2_mode_t mode, int n_q, int n_h
     REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
   }
   return hip_status(csa2::launch_index_score(
-                        mode == CSA2_REINDEX, n_q, static_cast<const uint16_t*>(q_idx), w,
+                        mode == CSA2_REINDEX, key_format, n_q,
+                        static_cast<const uint16_t*>(q_idx), w,
                         static_cast<const uint8_t*>(k_cache),
                         static_cast<const uint8_t*>(k_scales), n_entries, kv_start, n_visible,
                         pool_blocks, mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
@@ -116,7 +119,7 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const vo
                      const int64_t* kv_start, const int32_t* n_visible, const int32_t* pool_blocks,
                      int n_pool, int block_size, float* scores, int64_t ld_scores,
                      float* block_max, int64_t ld_block_max, void* stream) {
-  return index_score_common("csa2_index_score", mode, n_q, n_heads, d_idx, q_idx, w, k_cache,
+  return index_score_common("csa2_index_score", 0, mode, n_q, n_heads, d_idx, q_idx, w, k_cache,
                             nullptr, n_entries, kv_start, n_visible, pool_blocks, n_pool,
                             block_size, scores, ld_scores, block_max, ld_block_max, stream);
 }
@@ -161,10 +164,48 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx, co
                            void* stream) {
   REQUIRE(n_q == 0 || k_scales != nullptr, CSA2_ERR_INVALID_ARG,
           "csa2_index_score_mxfp4: null k_scales");
-  return index_score_common("csa2_index_score_mxfp4", mode, n_q, n_heads, d_idx, q_idx, w,
+  return index_score_common("csa2_index_score_mxfp4", 1, mode, n_q, n_heads, d_idx, q_idx, w,
                             k_codes, k_scales, n_entries, kv_start, n_visible, pool_blocks,
                             n_pool, block_size, scores, ld_scores, block_max, ld_block_max,
                             stream);
+}
+
+int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
+                          const float* w, const void* k_rows, int64_t n_entries,
+                          const int64_t* kv_start, const int32_t* n_visible,
+                          const int32_t* pool_blocks, int n_pool, int block_size, float* scores,
+                          int64_t ld_scores, float* block_max, int64_t ld_block_max,
+                          void* stream) {
+  return index_score_common("csa2_index_score_bf16", 2, mode, n_q, n_heads, d_idx, q_idx, w,
+                            k_rows, nullptr, n_entries, kv_start, n_visible, pool_blocks, n_pool,
+                            block_size, scores, ld_scores, block_max, ld_block_max, stream);
+}
+
+int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache,
+                         int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
+                         void* km, const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
+                         int32_t* n_blocks, void* stream) {
+  const char* fn = "csa2_block_mean_keys";
+  REQUIRE(d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED, "%s: d_idx %d, only %d is built", fn,
+          d_idx, CSA2_IDX_DIM);
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
+  if (n_q == 0) return ok();
+  REQUIRE(k_cache && kv_start && n_visible && km && km_start && n_blocks, CSA2_ERR_INVALID_ARG,
+          "%s: null pointer argument", fn);
+  REQUIRE(n_entries >= 0 && n_km_rows >= 0, CSA2_ERR_INVALID_ARG,
+          "%s: n_entries and n_km_rows must be >= 0", fn);
+  REQUIRE(max_blocks >= 1 && max_blocks <= ((int64_t)1 << 28), CSA2_ERR_INVALID_ARG,
+          "%s: max_blocks %lld out of range", fn, (long long)max_blocks);
+  REQUIRE(aligned(k_cache, 8) && aligned(km, 16) && aligned(kv_start, 8) &&
+              aligned(km_start, 8) && aligned(n_visible, 4) && aligned(n_blocks, 4),
+          CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
+  return hip_status(csa2::launch_block_mean_keys(
+                        n_q, static_cast<const uint8_t*>(k_cache), n_entries, kv_start, n_visible,
+                        static_cast<uint16_t*>(km), km_start, n_km_rows, max_blocks, n_blocks,
+                        static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 int csa2_write_latent(int n, const void* x, const int64_t* rows, void* kv_fp4,

@@ -10,12 +10,19 @@ namespace csa2 {
 
 // k_scales: NULL for E4M3 indexer keys ([E,128]); the E8M0 scale rows ([E,4]) for MXFP4
 // keys, whose codes ([E,64]) are then k_cache.
-hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
-                              const int64_t* kv_start,
+// key_format: 0 E4M3, 1 MXFP4 (k_scales non-NULL), 2 bf16 rows of 256 bytes.
+hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint16_t* q_idx,
+                              const float* w, const uint8_t* k_cache, const uint8_t* k_scales,
+                              int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream);
+
+// Block-mean keys (bf16 [rows, 128]) of every visible 8-position block, and the block counts.
+hipError_t launch_block_mean_keys(int n_q, const uint8_t* k_cache, int64_t n_entries,
+                                  const int64_t* kv_start, const int32_t* n_visible, uint16_t* km,
+                                  const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
+                                  int32_t* n_blocks, hipStream_t stream);
 
 // Full-mode scores of queries that all read the cache rows from one kv_start.
 hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float* w,

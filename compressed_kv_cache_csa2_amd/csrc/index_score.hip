@@ -39,7 +39,12 @@ constexpr int IS_STEPS_FULL = 16;
 constexpr int IS_STEPS_REINDEX = 4;
 constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is multiplied
 
-template <bool REINDEX, bool FP4K>
+// Indexer-key formats: E4M3 rows of 128 bytes, MXFP4 rows (64 code bytes + 4 E8M0 scale
+// bytes in a separate array) and bf16 rows of 256 bytes (the block-mean keys of the
+// two-stage filter).
+enum { KF_E4M3 = 0, KF_MXFP4 = 1, KF_BF16 = 2 };
+
+template <bool REINDEX, int KF>
 __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, const uint8_t* __restrict__ k_scales, int64_t n_entries,
@@ -101,12 +106,18 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
   auto slot_at = [&](int step) -> int64_t { return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n; };
   // E4M3: raw[0..3] = bytes 64*half .. +63 of the row. MXFP4: raw[0..1] = code bytes
   // 32*half .. +31 (channels 64*half .. +63) and raw[2].x = the row's four scale bytes.
-  u32x4 buf[NB][4];
+  // bf16: raw[0..7] = channels 64*half .. +63.
+  constexpr int NR = KF == KF_BF16 ? 8 : 4;
+  u32x4 buf[NB][NR];
   float sc[IS_STEPS_PER_WAVE];
-  auto load_step = [&](int step, u32x4 (&raw)[4]) {
+  auto load_step = [&](int step, u32x4 (&raw)[NR]) {
     const int64_t r = row_at(step);
     const int64_t rr = r >= 0 ? r : base;
-    if constexpr (FP4K) {
+    if constexpr (KF == KF_BF16) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 256 + 128 * half);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = p[i];
+    } else if constexpr (KF == KF_MXFP4) {
       const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 64 + 32 * half);
       raw[0] = p[0];
       raw[1] = p[1];
@@ -127,12 +138,14 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     if (any) {
       if (step + IS_PREFETCH < IS_STEPS_PER_WAVE)
         load_step(step + IS_PREFETCH, buf[(step + IS_PREFETCH) % NB]);
-      u32x4 (&raw)[4] = buf[step % NB];
+      u32x4 (&raw)[NR] = buf[step % NB];
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
         u32x4 bv;
-        if constexpr (FP4K) {
+        if constexpr (KF == KF_BF16) {
+          bv = raw[kb];
+        } else if constexpr (KF == KF_MXFP4) {
           // channels 64*half + 8*kb .. +7: code dword kb, scale group 2*half + kb/4
           const uint32_t d = raw[kb >> 2][kb & 3];
           const uint32_t e = (raw[2].x >> (8 * (2 * half + (kb >> 2)))) & 0xFFu;
@@ -300,6 +313,66 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Block-mean indexer keys for the two-stage (HISA-style) filter: block b of query t holds the
+// mean of the E4M3 keys at positions 8b .. 8b+7 that are visible and in the cache, stored
+// as bf16 (nearest even) at row km_start[t] + b; n_blocks[t] receives ceil(n_visible / 8).
+// 16 lanes per block, lane c covering channels 8c .. 8c+7; sums of E4M3 values are exact
+// in float32 and the mean is one float32 division by the count.
+__global__ __launch_bounds__(IS_THREADS) void block_mean_keys_kernel(
+    const uint8_t* __restrict__ k_cache, int64_t n_entries, const int64_t* __restrict__ kv_start,
+    const int32_t* __restrict__ n_visible, uint16_t* __restrict__ km,
+    const int64_t* __restrict__ km_start, int64_t n_km_rows, int64_t max_blocks,
+    int32_t* __restrict__ n_blocks) {
+  const int t = blockIdx.y;
+  const int64_t nv = n_visible[t] > 0 ? n_visible[t] : 0;
+  const int64_t nb = (nv + 7) / 8;
+  if (blockIdx.x == 0 && threadIdx.x == 0) n_blocks[t] = (int32_t)nb;
+  const int64_t b = (int64_t)blockIdx.x * (IS_THREADS / 16) + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  if (b >= nb || b >= max_blocks) return;
+  const int64_t dst = km_start[t] + b;
+  if (dst < 0 || dst >= n_km_rows) return;
+  const int64_t base = kv_start[t];
+  float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int count = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t pos = 8 * b + i;
+    const int64_t row = base + pos;
+    if (pos < nv && row >= 0 && row < n_entries) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(k_cache + row * 128 + 8 * c);
+      const u32x2 lo = e4m3x4_to_bf16x4(v.x), hi = e4m3x4_to_bf16x4(v.y);
+      const uint32_t d[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sum[2 * j] += __uint_as_float(d[j] << 16);
+        sum[2 * j + 1] += __uint_as_float(d[j] & 0xFFFF0000u);
+      }
+      ++count;
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float m0 = count ? __fdiv_rn(sum[2 * j], (float)count) : 0.f;
+    const float m1 = count ? __fdiv_rn(sum[2 * j + 1], (float)count) : 0.f;
+    out[j] = f32_to_bf16_rne(m0) | (f32_to_bf16_rne(m1) << 16);
+  }
+  *reinterpret_cast<u32x4*>(km + dst * 128 + 8 * c) = out;
+}
+
+hipError_t launch_block_mean_keys(int n_q, const uint8_t* k_cache, int64_t n_entries,
+                                  const int64_t* kv_start, const int32_t* n_visible, uint16_t* km,
+                                  const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
+                                  int32_t* n_blocks, hipStream_t stream) {
+  const int per_block = IS_THREADS / 16;
+  dim3 grid((unsigned)((max_blocks + per_block - 1) / per_block), (unsigned)n_q);
+  hipLaunchKernelGGL(block_mean_keys_kernel, grid, dim3(IS_THREADS), 0, stream, k_cache,
+                     n_entries, kv_start, n_visible, km, km_start, n_km_rows, max_blocks, n_blocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float* w,
                                      const uint8_t* k_cache, int64_t n_entries, int64_t kv_start,
                                      const int32_t* n_visible, float* scores, int64_t ld,
@@ -310,9 +383,9 @@ hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float
   return hipGetLastError();
 }
 
-hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
-                              const int64_t* kv_start,
+hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint16_t* q_idx,
+                              const float* w, const uint8_t* k_cache, const uint8_t* k_scales,
+                              int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
                               hipStream_t stream) {
@@ -324,11 +397,13 @@ hipError_t launch_index_score(bool reindex, int n_q, const uint16_t* q_idx, cons
                        n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld, block_max,
                        ld_bm);
   };
-  const bool fp4 = k_scales != nullptr;
-  if (reindex)
-    fp4 ? go(index_score_kernel<true, true>) : go(index_score_kernel<true, false>);
-  else
-    fp4 ? go(index_score_kernel<false, true>) : go(index_score_kernel<false, false>);
+  if (key_format == KF_BF16) {
+    reindex ? go(index_score_kernel<true, KF_BF16>) : go(index_score_kernel<false, KF_BF16>);
+  } else if (k_scales != nullptr) {
+    reindex ? go(index_score_kernel<true, KF_MXFP4>) : go(index_score_kernel<false, KF_MXFP4>);
+  } else {
+    reindex ? go(index_score_kernel<true, KF_E4M3>) : go(index_score_kernel<false, KF_E4M3>);
+  }
   return hipGetLastError();
 }
 

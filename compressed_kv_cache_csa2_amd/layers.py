@@ -5,6 +5,10 @@ Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_scor
          among the pool's slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
+HISA-style coarse filter (coarse="hisa", the alternative the HSI section contrasts): every
+         Full and Reindex layer scores the block-mean keys with its own query, keeps the best
+         2,048 blocks (the latest one forced in, as for the HSI pool), rescores their
+         positions with the original keys and takes its Top-K there
 ("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression", 2.3.2 and 3.3.3;
 "DeepSeek-V4.1-Flash - Architecture", section 2, mode table and decoder schedule.)
 All outputs live in buffers allocated once, so a step allocates nothing.
@@ -30,6 +34,29 @@ class Buffers:
     lse: torch.Tensor           # f32 [n_layers, n_q, 64]
     workspace: torch.Tensor | None
     published: list             # per layer: the index tensor it attended with
+
+
+@dataclass
+class BlockMeans:
+    km: torch.Tensor            # bf16 [n_q * max_blocks, 128] block-mean indexer keys
+    km_start: torch.Tensor      # i64 [n_q] first km row of each query
+    n_blocks: torch.Tensor      # i32 [n_q] ceil(n_visible / 8)
+
+
+def build_block_means(wl, stream=None) -> BlockMeans:
+    """Block-mean keys of every query's visible E4M3 keys. In a decoder these summaries
+    are kept up to date as tokens arrive (a new token changes one block), so a decode step
+    reads them as resident data."""
+    if wl.k_codes is not None:
+        raise ValueError("block means are built from E4M3 indexer keys")
+    dev = wl.k_cache.device
+    max_blocks = -(-max(1, wl.n_ctx) // BLOCK)
+    km = torch.zeros((wl.n_q * max_blocks, 128), dtype=torch.bfloat16, device=dev)
+    km_start = torch.arange(wl.n_q, dtype=torch.int64, device=dev) * max_blocks
+    n_blocks = torch.zeros(wl.n_q, dtype=torch.int32, device=dev)
+    C.csa2_block_mean_keys(wl.k_cache, wl.kv_start, wl.n_visible, km, km_start, n_blocks,
+                           max_blocks=max_blocks, stream=stream)
+    return BlockMeans(km=km, km_start=km_start, n_blocks=n_blocks)
 
 
 def alloc_buffers(wl, k: int = TOPK) -> Buffers:
@@ -68,11 +95,32 @@ def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scor
                            ld_scores=ld_scores)
 
 
-def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None):
-    """One pass of the whole layer stack of the workload (one decode or prefill step)."""
+def hisa_select(wl, lay, buf: Buffers, means: BlockMeans, out_idx, k: int = TOPK,
+                stream=None):
+    """Two-stage selection from block means: block scores (into buf.block_max) -> the best
+    2,048 blocks -> rescoring of their positions with the original keys -> Top-K."""
+    C.csa2_index_score_bf16(C.FULL, lay.q_idx, lay.w, means.km, means.km_start, means.n_blocks,
+                            buf.block_max, stream=stream)
+    C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, n_keep=POOL_BLOCKS, stream=stream)
+    index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool, stream=stream)
+    C.csa2_topk(buf.re_scores, out_idx, k=k, pool_blocks=buf.pool, stream=stream)
+
+
+def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi",
+               means: BlockMeans | None = None):
+    """One pass of the whole layer stack of the workload (one decode or prefill step).
+    coarse="hisa" replaces every indexer layer's selection by the block-mean two-stage
+    filter over `means` (decoder stacks with a pool only)."""
+    if coarse not in ("hsi", "hisa"):
+        raise ValueError(f"unknown coarse filter {coarse!r}")
+    if coarse == "hisa" and (means is None or not wl.with_pool):
+        raise ValueError("coarse='hisa' needs a pooled decoder workload and its block means")
     current = None
     for li, lay in enumerate(wl.layers):
-        if lay.mode == "full":
+        if lay.mode in ("full", "reindex") and coarse == "hisa":
+            hisa_select(wl, lay, buf, means, buf.idx[li], k=k, stream=stream)
+            current = buf.idx[li]
+        elif lay.mode == "full":
             if wl.with_pool:
                 # Decoder Full layer: the pass over the whole context writes only the block
                 # maxima; the pool holds every Full-layer winner, so the Top-K is taken over

@@ -156,6 +156,46 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                            float* block_max, int64_t ld_block_max,
                            void* stream);
 
+/* Block-mean indexer keys for a HISA-style two-stage filter (the alternative
+ * [V41F-BLOG] 2.3.4 sets beside HSI: the prefix is cut into blocks of consecutive
+ * positions, each block keeps the mean of its indexer keys, a first stage scores those
+ * means with the same query and weights, the best blocks are expanded to their positions
+ * and a second stage scores them with the original keys). Block size 8 and bf16 storage
+ * are readings (R20); the pages fix neither.
+ * For query t with n = n_visible[t] (clipped below at 0), nb = ceil(n/8) and
+ * n_blocks[t] = nb. For b < min(nb, max_blocks), km[km_start[t] + b, c] = bf16 (nearest
+ * even) of the float32 quotient (sum over the visible positions p in 8b .. 8b+7 whose
+ * row kv_start[t] + p lies in [0, n_entries) of E4M3 value k_cache[row, c]) / (count of
+ * such positions); 0 when there are none. The sums are exact in float32.
+ *   d_idx must be 128, block_size 8. k_cache [n_entries,128] E4M3, 8-byte aligned;
+ *   kv_start [n_q] int64; n_visible [n_q] int32; km [n_km_rows,128] bf16 output,
+ *   16-byte aligned; km_start [n_q] int64 first km row of query t (a destination row
+ *   outside [0, n_km_rows) is skipped); 1 <= max_blocks <= 2^28 bounds the blocks
+ *   written per query; n_blocks [n_q] int32 output. Queries that share a sequence may
+ *   share km rows (the same values are written).
+ * The block means are what csa2_index_score_bf16 (FULL mode, n_visible = n_blocks,
+ * kv_start = km_start) scores; those block scores, passed to csa2_block_pool as its
+ * block_max with the position count n_visible, give the HISA pool.
+ * Errors: CSA2_ERR_INVALID_ARG (null pointer, bad size or alignment),
+ * CSA2_ERR_UNSUPPORTED (d_idx or block_size). */
+int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache,
+                         int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
+                         void* km, const int64_t* km_start, int64_t n_km_rows,
+                         int64_t max_blocks, int32_t* n_blocks, void* stream);
+
+/* Lightning-indexer score over bf16 key rows (the block-mean keys above). Identical to
+ * csa2_index_score (same modes, slots, outputs, -inf rules and errors) except that
+ * k_rows is [n_entries,128] bf16, 16-byte aligned, and the key values are those bf16
+ * values. */
+int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+                          const void* q_idx, const float* w,
+                          const void* k_rows, int64_t n_entries,
+                          const int64_t* kv_start, const int32_t* n_visible,
+                          const int32_t* pool_blocks, int n_pool, int block_size,
+                          float* scores, int64_t ld_scores,
+                          float* block_max, int64_t ld_block_max,
+                          void* stream);
+
 /* Cache writes ([V41F-BLOG] 2.4.4: the main KV is stored as E2M1 with one E4M3 scale per
  * 16 channels and no global scale, quantised after RoPE; the sliding-window cache keeps
  * FP8; the indexer cache is OCP MXFP4; [V41F-ARCH] 4). These produce the formats the

@@ -22,8 +22,8 @@ def test_header_symbols_are_exported(C):
     assert names == {"csa2_workspace_bytes", "csa2_index_score", "csa2_index_score_mxfp4",
                      "csa2_block_pool", "csa2_topk", "csa2_pool_topk", "csa2_sparse_attn",
                      "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
-                     "csa2_index_score_shared",
-                     "csa2_version", "csa2_last_error"}
+                     "csa2_index_score_shared", "csa2_index_score_bf16",
+                     "csa2_block_mean_keys", "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -95,6 +95,38 @@ def test_index_score_shared_rejections(C):
     assert call(block_max=FAKE, ld_bm=1) == 1
     assert call(n_q=-1) == 1
     assert call(n_q=0, q_idx=None) == 0
+
+
+def test_index_score_bf16_rejections(C):
+    def call(**kw):
+        a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE, k_rows=FAKE,
+                 n_entries=10, kv_start=FAKE, n_visible=FAKE, pool_blocks=None, n_pool=0,
+                 block_size=8, scores=FAKE, ld=16, block_max=None, ld_bm=0, stream=None)
+        a.update(kw)
+        return C.lib.csa2_index_score_bf16(*a.values())
+    assert call(mode=2) == 1 and b"csa2_index_score_bf16" in C.lib.csa2_last_error()
+    assert call(k_rows=FAKE + 8) == 1                     # rows not 16-byte aligned
+    assert call(d_idx=64) == 2
+    assert call(mode=1) == 1                              # REINDEX without a pool
+    assert call(scores=None) == 1
+    assert call(n_q=0, q_idx=None) == 0
+
+
+def test_block_mean_keys_rejections(C):
+    def call(**kw):
+        a = dict(n_q=1, d_idx=128, block_size=8, k_cache=FAKE, n_entries=10, kv_start=FAKE,
+                 n_visible=FAKE, km=FAKE, km_start=FAKE, n_km_rows=4, max_blocks=2,
+                 n_blocks=FAKE, stream=None)
+        a.update(kw)
+        return C.lib.csa2_block_mean_keys(*a.values())
+    assert call(d_idx=64) == 2
+    assert call(block_size=16) == 2
+    assert call(n_q=-1) == 1
+    assert call(km=None) == 1 and b"csa2_block_mean_keys" in C.lib.csa2_last_error()
+    assert call(km=FAKE + 8) == 1                         # km not 16-byte aligned
+    assert call(max_blocks=0) == 1
+    assert call(n_entries=-1) == 1
+    assert call(n_q=0, km=None) == 0
 
 
 def test_cache_write_rejections(C):
