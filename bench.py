@@ -124,13 +124,17 @@ def needle_recall(wl, buf, C, means):
     return out
 
 
-def profile_kernels(wl, buf, C, launches):
-    """Only the Full-layer indexer and a plain copy of COPY_BYTES, for counter collection."""
+def profile_kernels(wl, buf, C, launches, means=None):
+    """Only the dominant kernel (the Full-layer indexer, or the block-mean scorer when
+    `means` is given) and a plain copy of COPY_BYTES, for counter collection."""
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(launches):
-        full_indexer(wl, buf, C)
+        if means is not None:
+            hisa_stage1(wl, buf, C, means)
+        else:
+            full_indexer(wl, buf, C)
         torch.neg(src, out=dst)   # reads and writes COPY_BYTES each
     torch.cuda.synchronize()
     print(f"[bench] profile launches done: {launches} x (indexer, copy of {COPY_BYTES} B)",
@@ -263,7 +267,7 @@ def main():
         means = layers.build_block_means(wl)
         torch.cuda.synchronize()
     if args.profile_kernel:
-        profile_kernels(wl, buf, C, args.profile_kernel)
+        profile_kernels(wl, buf, C, args.profile_kernel, means if hisa else None)
         return
     stream = torch.cuda.Stream()
 
