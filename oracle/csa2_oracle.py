@@ -517,6 +517,15 @@ def reindex_layer(q_idx, w, k_cache, kv_start, n_visible, pool, q, kv_fp4, kv_sc
     return {"scores": scores, "idx": idx, "out": out, "lse": lse}
 
 
+def swa_layer(q, window_kv, swa_start, n_swa, softmax_scale):
+    """An SWA-only layer for one query (the causal encoder's first two layers,
+    [V41F-ARCH] 2 encoder schedule; [V41F-BLOG] 2.3.2): softmax attention over the window
+    rows alone, no main-KV entry."""
+    ents = e4m3_decode(window_kv[swa_start:swa_start + max(0, min(int(n_swa), 128))])
+    out, lse = sparse_attention(bf16_decode(q), ents.reshape(-1, 512), softmax_scale)
+    return {"idx": np.zeros(0, np.int64), "out": out, "lse": lse}
+
+
 def reuse_layer(idx, q, kv_fp4, kv_scale, kv_start, window_kv, swa_start, n_swa,
                 softmax_scale):
     """Reuse mode for one query: no scoring and no selection; attend with the latest

@@ -546,3 +546,29 @@ def test_block_mean_dilutes_an_isolated_peak():
     km = O.block_mean_keys(codes, 16)
     bs = O.index_score_rows(O.bf16_decode(q_bits), w.astype(np.float64), O.bf16_decode(km))
     assert bs[0] == 32 * 1.0 and bs[1] == 32 * 1.5 and bs[0] < bs[1]
+
+
+# ------------------------------------------------------------------ encoder schedule
+
+def test_swa_layer_is_dense_attention_over_the_window():
+    """An SWA-only layer is softmax attention over the window rows alone: torch's scaled
+    dot-product attention over the decoded rows, a Reuse layer with an empty selection,
+    and a single window row returned exactly."""
+    rng = np.random.default_rng(41)
+    win = rng.integers(0, 0x7E, size=(200, 512)).astype(np.uint8) ^ (rng.integers(0, 2, size=(200, 512)).astype(np.uint8) << 7)
+    q = torch.from_numpy(rng.standard_normal((64, 512)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().view(np.uint16)
+    res = O.swa_layer(q_bits, win, 30, 128, 1 / math.sqrt(512))
+    rows = torch.from_numpy(win[30:158]).view(torch.float8_e4m3fn).double()
+    qd = q.double()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qd[None, :, None, :], rows[None, None].expand(1, 64, 128, 512),
+        rows[None, None].expand(1, 64, 128, 512), scale=1 / math.sqrt(512))
+    assert np.allclose(res["out"], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    empty = np.zeros((0, 256), np.uint8), np.zeros((0, 32), np.uint8)
+    reuse = O.reuse_layer(np.zeros(0, np.int64), q_bits, *empty, 0, win, 30, 128,
+                          1 / math.sqrt(512))
+    assert np.array_equal(res["out"], reuse["out"]) and np.array_equal(res["lse"], reuse["lse"])
+    one = O.swa_layer(q_bits, win, 7, 1, 1.0)
+    row7 = torch.from_numpy(win[7:8]).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(one["out"], np.repeat(row7, 64, 0))
