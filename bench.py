@@ -11,6 +11,9 @@ bracketed by device synchronisation. Inputs are seeded synthetic tensors already
 in HBM. Prints one JSON line.
 
 roofline: the dominant kernel is the Full-layer indexer, launched as the step launches it.
+Queries that share one sequence (prefill_128k_m2, encoder_128k_m2) read each key row once
+per group of queries, so there the indexer is priced against the bf16 matrix peak
+(8,192 flops per (query, entry) pair) instead of HBM.
 Its algorithmic bytes per launch are 128 B of indexer K read + 0.5 B of block maximum
 written per (query, entry) pair (+ 4 B of score where the step keeps the scores: stacks
 without a pool), plus the indexer queries and weights; its average launch duration is
@@ -43,6 +46,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 matrix peak
+FLOPS_PER_PAIR = 32 * 128 * 2   # indexer multiply-adds of one (query, entry) pair
 INDEXER_SRC = os.path.join(ROOT, "compressed_kv_cache_csa2_amd", "csrc", "index_score.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_score_full_decode_256k.md")
 COPY_BYTES = 1 << 30
@@ -76,7 +81,8 @@ def full_indexer(wl, buf, C, stream=None):
     """The Full-layer indexer as the step launches it: block maxima only in a pooled stack,
     over the workload's key format."""
     from compressed_kv_cache_csa2_amd import layers
-    layers.index_score(wl, C.FULL, wl.layers[0], None if wl.with_pool else buf.scores,
+    lay = next(l for l in wl.layers if l.mode == "full")
+    layers.index_score(wl, C.FULL, lay, None if wl.with_pool else buf.scores,
                        buf.block_max, ld_scores=buf.scores.shape[1], stream=stream)
 
 
@@ -154,11 +160,13 @@ def algorithmic_bytes(wl, k=512, coarse="hsi"):
         if coarse == "hisa" and lay.mode in ("full", "reindex"):
             total += int(((nv + 7) // 8).sum()) * 256
             total += int(torch.clamp(nv, max=16384).sum()) * key_bytes(wl)
+        elif lay.mode == "full" and wl.shared_start is not None:
+            total += wl.n_ctx * key_bytes(wl)      # one sequence: each key row once
         elif lay.mode == "full":
             total += int(nv.sum()) * key_bytes(wl)
         elif lay.mode == "reindex":
             total += int(torch.clamp(nv, max=16384).sum()) * key_bytes(wl)
-        sel = torch.clamp(nv, max=k)
+        sel = torch.clamp(nv, max=k) if lay.mode != "swa" else torch.zeros_like(nv)
         total += int(sel.sum()) * 288 + wl.n_q * (128 * 512 + 2 * 64 * 512 * 2)
     return total
 
@@ -196,21 +204,24 @@ def cpu_baseline(wl, target_s, max_q):
         nv = seq["n_visible"]
         idx = pool = None
         for lay in seq["layers"]:
+            keys = seq["k_codes"] if "k_codes" in seq else lay["k_cache"]
             if lay["mode"] == "full":
-                r = O.full_layer(lay["q_idx"], lay["w"], seq.get("k_codes", seq["k_cache"]), 0,
-                                 nv, lay["q"], seq["kv_fp4"], seq["kv_scale"], lay["window_kv"],
-                                 0, lay["n_swa"], wl.softmax_scale, with_pool=wl.with_pool,
+                r = O.full_layer(lay["q_idx"], lay["w"], keys, 0, nv, lay["q"], lay["kv_fp4"],
+                                 lay["kv_scale"], lay["window_kv"], 0, lay["n_swa"],
+                                 wl.softmax_scale, with_pool=wl.with_pool,
                                  k_scales=seq.get("k_scales"))
                 pool = r.get("pool")
             elif lay["mode"] == "reindex":
-                r = O.reindex_layer(lay["q_idx"], lay["w"], seq.get("k_codes", seq["k_cache"]), 0,
-                                    nv, pool, lay["q"], seq["kv_fp4"], seq["kv_scale"],
-                                    lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale,
-                                    k_scales=seq.get("k_scales"))
+                r = O.reindex_layer(lay["q_idx"], lay["w"], keys, 0, nv, pool, lay["q"],
+                                    lay["kv_fp4"], lay["kv_scale"], lay["window_kv"], 0,
+                                    lay["n_swa"], wl.softmax_scale, k_scales=seq.get("k_scales"))
+            elif lay["mode"] == "swa":
+                r = O.swa_layer(lay["q"], lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
             else:
-                r = O.reuse_layer(idx, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
+                r = O.reuse_layer(idx, lay["q"], lay["kv_fp4"], lay["kv_scale"], 0,
                                   lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
-            idx = r["idx"]
+            if lay["mode"] != "swa":
+                idx = r["idx"]
         t_total += time.perf_counter() - t0
         done += 1
         np.asarray(r["out"]).sum()
@@ -369,7 +380,8 @@ def main():
                     elif part == "pool" and lay.mode == "full" and wl.with_pool:
                         C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, stream=stream)
                     elif part == "attn":
-                        C.csa2_sparse_attn(lay.q, wl.kv_fp4, wl.kv_scale, wl.kv_start,
+                        _, kv_fp4, kv_scale = wl.cache(lay.group)
+                        C.csa2_sparse_attn(lay.q, kv_fp4, kv_scale, wl.kv_start,
                                            buf.published[li], lay.window_kv, lay.swa_start,
                                            lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
                                            buf.workspace, stream=stream)
@@ -420,6 +432,14 @@ def main():
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,
     }
+    if wl.shared_start is not None:
+        pairs = int(wl.n_visible.to(torch.int64).sum())
+        tflops = pairs * FLOPS_PER_PAIR / (idx_us * 1e-6) / 1e12
+        line["roofline"].update({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                                 "flops_per_launch": pairs * FLOPS_PER_PAIR,
+                                 "kernel": "index_score_shared_kernel (grouped Full indexer)"})
+        del line["roofline"]["bytes_per_launch"]
     if recall is not None:
         line["needle_recall"] = recall
     print(json.dumps(line), flush=True)

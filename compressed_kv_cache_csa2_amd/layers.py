@@ -5,12 +5,15 @@ Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_scor
          among the pool's slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
+SWA:     sparse_attn over the sliding window alone (the encoder's first two layers)
 HISA-style coarse filter (coarse="hisa", the alternative the HSI section contrasts): every
          Full and Reindex layer scores the block-mean keys with its own query, keeps the best
          2,048 blocks (the latest one forced in, as for the HSI pool), rescores their
          positions with the original keys and takes its Top-K there
 ("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression", 2.3.2 and 3.3.3;
-"DeepSeek-V4.1-Flash - Architecture", section 2, mode table and decoder schedule.)
+"DeepSeek-V4.1-Flash - Architecture", section 2, mode table and the encoder and decoder
+schedules; in the encoder each group's Full layer reads its own cache set and its Reuse
+layers read the same one.)
 All outputs live in buffers allocated once, so a step allocates nothing.
 """
 from __future__ import annotations
@@ -79,18 +82,22 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
 
 def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
                 stream=None):
-    """The indexer over the workload's keys: MXFP4 when it carries them, else E4M3; a Full
-    pass of queries sharing one sequence scores them in groups per cache tile."""
+    """The indexer over the layer group's keys: MXFP4 when the workload carries them, else
+    E4M3; a Full pass of queries sharing one sequence scores them in groups per cache
+    tile."""
+    k_cache = wl.cache(lay.group)[0]
     if (mode == C.FULL and wl.k_codes is None and wl.shared_start is not None
             and scores is not None):
-        C.csa2_index_score_shared(lay.q_idx, lay.w, wl.k_cache, wl.shared_start, wl.n_visible,
+        C.csa2_index_score_shared(lay.q_idx, lay.w, k_cache, wl.shared_start, wl.n_visible,
                                   scores, block_max, stream=stream)
     elif wl.k_codes is not None:
+        if lay.group != 0:
+            raise ValueError("MXFP4 keys are carried for cache set 0 only")
         C.csa2_index_score_mxfp4(mode, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
                                  wl.n_visible, scores, block_max, pool_blocks=pool_blocks,
                                  stream=stream, ld_scores=ld_scores)
     else:
-        C.csa2_index_score(mode, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+        C.csa2_index_score(mode, lay.q_idx, lay.w, k_cache, wl.kv_start, wl.n_visible,
                            scores, block_max, pool_blocks=pool_blocks, stream=stream,
                            ld_scores=ld_scores)
 
@@ -116,7 +123,20 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
     if coarse == "hisa" and (means is None or not wl.with_pool):
         raise ValueError("coarse='hisa' needs a pooled decoder workload and its block means")
     current = None
+    current_group = 0
     for li, lay in enumerate(wl.layers):
+        _, kv_fp4, kv_scale = wl.cache(lay.group)
+        if lay.mode == "swa":
+            buf.published[li] = buf.idx[li][:, :0]
+            C.csa2_sparse_attn(lay.q, kv_fp4, kv_scale, wl.kv_start, buf.idx[li], lay.window_kv,
+                               lay.swa_start, lay.n_swa, wl.softmax_scale, buf.out[li],
+                               buf.lse[li], buf.workspace, k=0, stream=stream)
+            continue
+        if lay.mode in ("full", "reindex"):
+            current_group = lay.group
+        elif lay.group != current_group:
+            raise ValueError("a Reuse layer must read the cache set of the layer whose "
+                             "indices it reuses")
         if lay.mode in ("full", "reindex") and coarse == "hisa":
             hisa_select(wl, lay, buf, means, buf.idx[li], k=k, stream=stream)
             current = buf.idx[li]
@@ -147,6 +167,6 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
         if current is None:
             raise ValueError("a Reuse layer needs an earlier Full or Reindex layer")
         buf.published[li] = current
-        C.csa2_sparse_attn(lay.q, wl.kv_fp4, wl.kv_scale, wl.kv_start, current, lay.window_kv,
+        C.csa2_sparse_attn(lay.q, kv_fp4, kv_scale, wl.kv_start, current, lay.window_kv,
                            lay.swa_start, lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
                            buf.workspace, k=k, stream=stream)

@@ -22,6 +22,9 @@ blocks, 2,048 pool blocks):
                     visible from token p when 2e+1 <= p); Full only.
   decode_1m         64 queries x 1,048,576 entries; Full (+pool), Reindex, 3 x Reuse;
                     64 needles per query at evenly spaced positions.
+  encoder_128k_m2   the causal encoder's schedule over the prefill_128k_m2 chunk: two
+                    SWA-only layers, then three groups of one Full layer (with its own
+                    main-KV and indexer-K cache) and five Reuse layers.
 """
 from __future__ import annotations
 
@@ -39,17 +42,20 @@ SOFTMAX_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 PLANT_SHIFT = 3.0
 
 DECODE_LAYERS = ("full", "reindex", "reuse", "reuse", "reuse")
+ENCODER_LAYERS = ("swa", "swa") + ("full",) + ("reuse",) * 5 + ("full",) + ("reuse",) * 5 \
+    + ("full",) + ("reuse",) * 5
 
 
 @dataclass
 class LayerInputs:
-    mode: str                       # "full", "reindex" or "reuse"
+    mode: str                       # "full", "reindex", "reuse" or "swa" (window only)
     q: torch.Tensor                 # bf16 [n_q, 64, 512]
     window_kv: torch.Tensor         # uint8 [rows, 512] E4M3
     swa_start: torch.Tensor         # int64 [n_q]
     n_swa: torch.Tensor             # int32 [n_q]
     q_idx: torch.Tensor | None = None   # bf16 [n_q, 32, 128]
     w: torch.Tensor | None = None       # float32 [n_q, 32]
+    group: int = 0                  # which cache set the layer reads (encoder groups)
 
 
 @dataclass
@@ -71,6 +77,14 @@ class Workload:
     k_scales: torch.Tensor | None = None
     # every query reads the cache from this row (chunked prefill), else None
     shared_start: int | None = None
+    # cache sets of groups 1, 2, ... as (k_cache, kv_fp4, kv_scale); group 0 is the above
+    group_caches: list = field(default_factory=list)
+
+    def cache(self, group: int = 0):
+        """(k_cache, kv_fp4, kv_scale) of a layer group."""
+        if group == 0:
+            return self.k_cache, self.kv_fp4, self.kv_scale
+        return self.group_caches[group - 1]
 
     @property
     def n_entries(self) -> int:
@@ -81,13 +95,14 @@ class Workload:
         mv = lambda x: None if x is None else x.to(device)
         layers = [LayerInputs(mode=l.mode, q=mv(l.q), window_kv=mv(l.window_kv),
                               swa_start=mv(l.swa_start), n_swa=mv(l.n_swa), q_idx=mv(l.q_idx),
-                              w=mv(l.w)) for l in self.layers]
+                              w=mv(l.w), group=l.group) for l in self.layers]
         return Workload(name=self.name, n_q=self.n_q, n_ctx=self.n_ctx, kv_start=mv(self.kv_start),
                         n_visible=mv(self.n_visible), k_cache=mv(self.k_cache),
                         kv_fp4=mv(self.kv_fp4), kv_scale=mv(self.kv_scale), layers=layers,
                         with_pool=self.with_pool, planted=self.planted,
                         softmax_scale=self.softmax_scale, k_codes=mv(self.k_codes),
-                        k_scales=mv(self.k_scales), shared_start=self.shared_start)
+                        k_scales=mv(self.k_scales), shared_start=self.shared_start,
+                        group_caches=[tuple(mv(x) for x in c) for c in self.group_caches])
 
 
 # ----------------------------------------------------------------------------- encoders
@@ -207,9 +222,10 @@ def _make_layer(mode, n_q, device, seed, li, window_rows=None, swa_start=None, n
 
 
 def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, plant_pos,
-                    full_layer: LayerInputs, mxfp4=False):
+                    full_layer: LayerInputs, mxfp4=False, tag=()):
     """Draw the indexer-K and latent rows of every sequence, planting at plant_pos. With
-    mxfp4 the indexer keys are also encoded in MXFP4 (from the same draws)."""
+    mxfp4 the indexer keys are also encoded in MXFP4 (from the same draws). `tag` extends
+    the draw names (a second cache set of the same sequences)."""
     k_cache = torch.zeros((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
     k_codes = torch.zeros((n_entries, IDX_DIM // 2), dtype=torch.uint8, device=device) if mxfp4 else None
     k_scales = torch.full((n_entries, IDX_DIM // 32), 127, dtype=torch.uint8, device=device) if mxfp4 else None
@@ -222,8 +238,8 @@ def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, pl
     for t, start, n in seqs:
         if n <= 0:
             continue
-        k = _randn((n, IDX_DIM), device, seed, "k_idx", t)
-        lat = _randn((n, HEAD_DIM), device, seed, "latent", t)
+        k = _randn((n, IDX_DIM), device, seed, "k_idx", t, *tag)
+        lat = _randn((n, HEAD_DIM), device, seed, "latent", t, *tag)
         if plant_pos is not None and not shared:
             pos = plant_pos[t]
             pos = pos[pos < n]
@@ -304,6 +320,41 @@ def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,
                     shared_start=0)
 
 
+def make_encoder(name="encoder_128k_m2", n_q=4096, n_entries=131072, ratio=2,
+                 device="cpu", seed=0):
+    """The causal encoder's layer schedule over the same chunk as make_prefill: two SWA-only
+    layers, then three groups of (Full, 5 x Reuse). Each group's Full layer computes its
+    own main KV and indexer K, so group g reads cache set g (group 0: the workload's own
+    tensors, the same cache rows as make_prefill draws); its Reuse layers attend with that
+    Full layer's Top-K over the same cache set."""
+    p0 = ratio * n_entries - n_q
+    n_visible = [(p0 + i + 1) // ratio for i in range(n_q)]
+    n_visible_t = torch.tensor(n_visible, dtype=torch.int32)
+    kv_start_t = torch.zeros(n_q, dtype=torch.int64)
+    rows = n_q + WINDOW - 1
+    swa_start = torch.arange(n_q, dtype=torch.int64, device=device)
+    n_swa = torch.full((n_q,), WINDOW, dtype=torch.int32, device=device)
+    lay = []
+    group = -1
+    for li, mode in enumerate(ENCODER_LAYERS):
+        l = _make_layer(mode, n_q, device, seed, li, rows, swa_start, n_swa)
+        if mode == "full":
+            group += 1
+        l.group = max(group, 0)
+        lay.append(l)
+    caches = []
+    for g in range(group + 1):
+        k_cache, kv_fp4, kv_scale, _, _ = _fill_sequences(
+            n_q, n_entries, kv_start_t, n_visible_t, n_entries, device, seed, None, lay[0],
+            tag=() if g == 0 else ("group", g))
+        caches.append((k_cache, kv_fp4, kv_scale))
+    k_cache, kv_fp4, kv_scale = caches[0]
+    return Workload(name=name, n_q=n_q, n_ctx=max(n_visible), kv_start=kv_start_t.to(device),
+                    n_visible=n_visible_t.to(device), k_cache=k_cache, kv_fp4=kv_fp4,
+                    kv_scale=kv_scale, layers=lay, with_pool=False, planted=None,
+                    shared_start=0, group_caches=caches[1:])
+
+
 def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
     """One of the named workloads; n_q (optional) keeps only the first n_q queries. A
     decode workload name with the suffix "_mxfp4" also carries MXFP4 indexer keys, which
@@ -326,13 +377,16 @@ def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
                            seed=seed)
     if name == "prefill_128k_m2":
         return make_prefill(name, n_q=n_q or 4096, device=device, seed=seed)
+    if name == "encoder_128k_m2":
+        return make_encoder(name, n_q=n_q or 4096, device=device, seed=seed)
     if name == "decode_1m":
         return make_decode(name, n_q or 64, 1048576, DECODE_LAYERS, True, 64, needles="even",
                            device=device, seed=seed)
     raise ValueError(f"unknown workload {name!r}")
 
 
-WORKLOADS = ("tiny_decode_4k", "decode_32k", "decode_256k", "prefill_128k_m2", "decode_1m")
+WORKLOADS = ("tiny_decode_4k", "decode_32k", "decode_256k", "prefill_128k_m2", "decode_1m",
+             "encoder_128k_m2")
 
 
 def sequence_to_host(wl: Workload, t: int):
@@ -351,11 +405,19 @@ def sequence_to_host(wl: Workload, t: int):
     if wl.k_codes is not None:
         seq["k_codes"] = wl.k_codes[sl].cpu().numpy()
         seq["k_scales"] = wl.k_scales[sl].cpu().numpy()
+    groups = [(seq["k_cache"], seq["kv_fp4"], seq["kv_scale"])]
+    for kc, kf, ks in wl.group_caches:
+        groups.append((kc[sl].cpu().numpy(), kf[sl].cpu().numpy(), ks[sl].cpu().numpy()))
     for lay in wl.layers:
         s0 = int(lay.swa_start[t])
         ns = int(lay.n_swa[t])
+        kc, kf, ks = groups[lay.group]
         d = {
             "mode": lay.mode,
+            "group": lay.group,
+            "k_cache": kc,
+            "kv_fp4": kf,
+            "kv_scale": ks,
             "q": lay.q[t].view(torch.int16).cpu().numpy().view("uint16"),
             "window_kv": lay.window_kv[s0:s0 + max(0, min(ns, WINDOW))].cpu().numpy(),
             "n_swa": ns,

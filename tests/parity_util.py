@@ -93,13 +93,16 @@ def check_query(wl, buf, t, seq=None, report=None):
     pool_gpu = None
     n_cmp = 0
     for li, lay in enumerate(seq["layers"]):
+        k_cache, kv_fp4, kv_scale = lay["k_cache"], lay["kv_fp4"], lay["kv_scale"]
         idx_gpu = buf.published[li][t].cpu().numpy()
-        if lay["mode"] == "full":
+        if lay["mode"] == "swa":
+            assert idx_gpu.size == 0, f"q{t} L{li}: an SWA layer attends with no selection"
+        elif lay["mode"] == "full":
             if "k_codes" in seq:
                 scores = O.full_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                              seq["k_scales"], 0, nv, nv)
             else:
-                scores = O.full_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, nv)
+                scores = O.full_scores(lay["q_idx"], lay["w"], k_cache, 0, nv, nv)
             ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), None)
             kth, band = band_of(scores, 512)
             assert_set_band(idx_gpu, ref_idx, lambda p: scores[p], kth, band,
@@ -119,15 +122,18 @@ def check_query(wl, buf, t, seq=None, report=None):
                 scores = O.reindex_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                                 seq["k_scales"], 0, nv, padded)
             else:
-                scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
+                scores = O.reindex_scores(lay["q_idx"], lay["w"], k_cache, 0, nv, padded)
             ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), padded)
             pos_of_slot = O.slots_to_positions(np.arange(len(scores)), padded)
             score_at = dict(zip(pos_of_slot.tolist(), scores.tolist()))
             kth, band = band_of(scores, 512)
             assert_set_band(idx_gpu, ref_idx, lambda p: score_at[p], kth, band,
                             f"q{t} L{li} reindex top-k")
-        res = O.reuse_layer(idx_gpu, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
-                            lay["window_kv"], 0, lay["n_swa"], scale)
+        if lay["mode"] == "swa":
+            res = O.swa_layer(lay["q"], lay["window_kv"], 0, lay["n_swa"], scale)
+        else:
+            res = O.reuse_layer(idx_gpu, lay["q"], kv_fp4, kv_scale, 0, lay["window_kv"], 0,
+                                lay["n_swa"], scale)
         rel = assert_attn_close(buf.out[li][t].float().cpu().numpy(), res["out"],
                                 f"q{t} L{li} {lay['mode']} attention")
         lse_gpu = buf.lse[li][t].cpu().numpy().astype(np.float64)

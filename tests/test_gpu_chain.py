@@ -92,3 +92,19 @@ def test_small_decode_stack_with_mxfp4_keys(dev):
     torch.cuda.synchronize()
     compared = sum(check_query(wl, buf, t) for t in range(wl.n_q))
     assert compared == wl.n_q * len(wl.layers)
+
+
+def test_small_encoder_schedule(dev):
+    """The encoder's schedule (2 SWA-only layers, then 3 x (Full + 5 Reuse), each group on
+    its own cache set) over a small causal chunk: every layer of sampled queries against
+    the oracle."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    wl = synth.make_encoder("small_encoder", n_q=48, n_entries=3000, seed=24).to(dev)
+    assert len(wl.group_caches) == 2
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    compared = sum(check_query(wl, buf, t) for t in (0, 17, wl.n_q - 1))
+    assert compared == 3 * len(wl.layers)
+    # the groups really read different caches: group 1's Full layer selects differently
+    assert not torch.equal(buf.idx[2], buf.idx[8])

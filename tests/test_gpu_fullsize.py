@@ -76,6 +76,14 @@ def test_prefill_128k_m2_sampled(dev):
     torch.cuda.empty_cache()
 
 
+def test_encoder_128k_m2_sampled(dev):
+    wl, buf = _run("encoder_128k_m2", dev)
+    queries = [0, wl.n_q - 1]
+    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    del wl, buf
+    torch.cuda.empty_cache()
+
+
 def test_decode_1m_sampled(dev):
     wl, buf = _run("decode_1m", dev)
     queries = [0, wl.n_q - 1]
