@@ -6,7 +6,8 @@ baseline leg of the benchmark do. It shares no code with the HIP library and doe
 import the input generator; it receives plain numpy arrays.
 
 Every function is the plain definition of one step, written from the pages:
-  [V41F-ARCH] "DeepSeek-V4.1-Flash - Architecture" (reading notes), section 2 (CSA2 modes,
+  [V41F-ARCH] "DeepSeek-V4.1-Flash - Architecture" (reading notes), section 1 (the KV
+              and compression-weight projections), section 2 (CSA2 modes,
               layer schedule, main attention settings), section 3 (Hierarchical Sparse
               Indexer), section 4 (KV cache formats and storage).
   [V41F-BLOG] "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression",
@@ -377,6 +378,42 @@ def hsi_pool(scores: np.ndarray, n_visible: int, block_size: int = 8,
     bm = block_max(np.asarray(scores, dtype=np.float64)[:n], block_size)
     bm[(n - 1) // block_size] = np.inf
     return topk_slots(bm, n_keep)
+
+
+# --------------------------------------------------------------------------------------
+# Write side: the compressor and the indexer-key projection
+# --------------------------------------------------------------------------------------
+
+
+def compress_entries(c_bits: np.ndarray, z_bits: np.ndarray, m: int) -> np.ndarray:
+    """Main-KV entries from m adjacent tokens by gated pooling, fp64 [T // m, d].
+
+    [V41F-ARCH] 1 (the design): per layer the KV content C = H W_KV and the compression
+    weights Z = H W_Z are projections of the hidden state; [V41F-BLOG] 3.3.2: the
+    compressor is gated pooling that becomes a per-token projection at m = 1; 2.3.1: no
+    overlap between the tokens of adjacent entries and no absolute position embedding.
+    Reading R22: entry j, channel c = sum over the tokens i of group j (tokens jm .. jm+m-1)
+    of softmax_i(Z[., c]) * C[i, c]; only complete groups give an entry. c_bits and z_bits
+    are the bf16 projections [T, d]."""
+    cv = bf16_decode(np.asarray(c_bits, np.uint16))
+    zv = bf16_decode(np.asarray(z_bits, np.uint16))
+    n = cv.shape[0] // m
+    out = np.zeros((n, cv.shape[1]))
+    for j in range(n):
+        zg = zv[j * m:(j + 1) * m]
+        g = np.exp(zg - zg.max(axis=0))
+        g /= g.sum(axis=0)
+        out[j] = (g * cv[j * m:(j + 1) * m]).sum(axis=0)
+    return out
+
+
+def project_index_keys(entries: np.ndarray, w_ik_bits: np.ndarray) -> np.ndarray:
+    """Indexer keys as a projection of main-KV entries, fp64 [n, 128].
+
+    [V41F-BLOG] 2.3.1: CSA2 obtains the indexer K by projecting the main KV entries instead
+    of compressing the hidden state separately. Reading R23: k = entry . W_IK^T with W_IK
+    a bf16 [128, d] matrix (output channel major); entries are the bf16 main-KV rows."""
+    return np.asarray(entries, np.float64) @ bf16_decode(np.asarray(w_ik_bits, np.uint16)).T
 
 
 # --------------------------------------------------------------------------------------

@@ -572,3 +572,66 @@ def test_swa_layer_is_dense_attention_over_the_window():
     one = O.swa_layer(q_bits, win, 7, 1, 1.0)
     row7 = torch.from_numpy(win[7:8]).view(torch.float8_e4m3fn).double().numpy()
     assert np.array_equal(one["out"], np.repeat(row7, 64, 0))
+
+
+# ------------------------------------------------------------------ compressor (write side)
+
+def _bf16_bits_of(x):
+    return torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_compressor_special_cases():
+    rng = np.random.default_rng(51)
+    c = _bf16_bits_of(rng.standard_normal((9, 512)))
+    z = _bf16_bits_of(rng.standard_normal((9, 512)) * 3)
+    cv = torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).double().numpy()
+    # m = 1 is the per-token projection itself
+    assert np.array_equal(O.compress_entries(c, z, 1), cv)
+    # equal gates give the plain mean of each group; only complete groups give entries
+    e = O.compress_entries(c, _bf16_bits_of(np.zeros((9, 512))), 2)
+    assert e.shape == (4, 512)
+    assert np.allclose(e, (cv[0:8:2] + cv[1:8:2]) / 2, rtol=0, atol=1e-15)
+    # a dominant gate selects its token
+    zd = np.zeros((9, 512), np.float32)
+    zd[1::2, :256] = 80.0
+    zd[0::2, 256:] = 80.0
+    e = O.compress_entries(c, _bf16_bits_of(zd), 2)
+    assert np.allclose(e[:, :256], cv[1:8:2, :256], rtol=1e-30, atol=1e-30)
+    assert np.allclose(e[:, 256:], cv[0:8:2, 256:], rtol=1e-30, atol=1e-30)
+
+
+def test_compressor_matches_torch_softmax_pooling():
+    """Against torch's softmax over the group axis, and invariant under a per-channel shift
+    of the gates (softmax shift invariance)."""
+    rng = np.random.default_rng(52)
+    c = _bf16_bits_of(rng.standard_normal((12, 512)))
+    z = _bf16_bits_of(rng.standard_normal((12, 512)) * 2)
+    cv = torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).double()
+    zv = torch.from_numpy(z.view(np.int16)).view(torch.bfloat16).double()
+    for m in (2, 3, 4):
+        n = 12 // m
+        g = torch.softmax(zv[:n * m].reshape(n, m, 512), dim=1)
+        ref = (g * cv[:n * m].reshape(n, m, 512)).sum(dim=1).numpy()
+        assert np.allclose(O.compress_entries(c, z, m), ref, rtol=1e-13, atol=1e-14)
+    # gates on a 1/8 grid stay exact in bf16 after an integer shift
+    zq = rng.integers(-32, 33, size=(12, 512)).astype(np.float32) / 8
+    shift = np.tile(rng.integers(-4, 5, size=(1, 512)).astype(np.float32), (12, 1))
+    a = O.compress_entries(c, _bf16_bits_of(zq), 2)
+    b = O.compress_entries(c, _bf16_bits_of(zq + shift), 2)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_index_key_projection_brute_force():
+    rng = np.random.default_rng(53)
+    ent = rng.standard_normal((5, 512))
+    w = _bf16_bits_of(rng.standard_normal((128, 512)) * 0.05)
+    wv = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = O.project_index_keys(ent, w)
+    assert got.shape == (5, 128)
+    for i in range(5):
+        for o in (0, 17, 127):
+            assert abs(got[i, o] - sum(ent[i, c] * wv[o, c] for c in range(512))) < 1e-12
+    # one-hot weights pick channels
+    oh = np.zeros((128, 512), np.float32)
+    oh[np.arange(128), 4 * np.arange(128)] = 1.0
+    assert np.array_equal(O.project_index_keys(ent, _bf16_bits_of(oh)), ent[:, ::4])
