@@ -35,6 +35,8 @@ def _load():
     lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, P]
+    lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
+    lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
     lib.csa2_write_e4m3.argtypes = [I, I, P, P, P, L, L, P]
     lib.csa2_write_mxfp4_key.argtypes = [I, P, P, P, P, L, P]
@@ -46,7 +48,8 @@ def _load():
                                      P, Z, P]
     for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
-              "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys"):
+              "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
+              "csa2_compress_kv", "csa2_project_index_key"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -95,6 +98,29 @@ def _rows_view(t, width, name):
             or t.shape[1] < width:
         raise ValueError(f"{name}: expected a device uint8 [rows, >= {width}] view")
     return t.data_ptr(), t.stride(0)
+
+
+def csa2_compress_kv(c, z, out, m, stream=None):
+    """Gated pooling of m adjacent tokens: c, z bf16 [T, 512] -> out bf16 [T // m, 512]."""
+    if c.shape != z.shape or c.dim() != 2 or c.shape[1] != 512:
+        raise ValueError("csa2_compress_kv: c and z must both be [T, 512]")
+    if out.dim() != 2 or out.shape[0] < c.shape[0] // m or out.shape[1] != 512:
+        raise ValueError("csa2_compress_kv: out must be [>= T // m, 512]")
+    _check(lib.csa2_compress_kv(int(m), c.shape[0], 512, _ptr(c, torch.bfloat16, "c"),
+                                _ptr(z, torch.bfloat16, "z"), 512,
+                                _ptr(out, torch.bfloat16, "out"), 512, _stream(stream)))
+
+
+def csa2_project_index_key(entries, w_ik, out, stream=None):
+    """Indexer keys out bf16 [n, 128] = entries bf16 [n, 512] . w_ik^T, w_ik bf16 [128, 512]."""
+    if entries.dim() != 2 or entries.shape[1] != 512 or tuple(w_ik.shape) != (128, 512):
+        raise ValueError("csa2_project_index_key: entries [n, 512] and w_ik [128, 512]")
+    if out.dim() != 2 or out.shape[0] < entries.shape[0] or out.shape[1] != 128:
+        raise ValueError("csa2_project_index_key: out must be [>= n, 128]")
+    _check(lib.csa2_project_index_key(entries.shape[0], 512, 128,
+                                      _ptr(entries, torch.bfloat16, "entries"), 512,
+                                      _ptr(w_ik, torch.bfloat16, "w_ik"),
+                                      _ptr(out, torch.bfloat16, "out"), 128, _stream(stream)))
 
 
 def csa2_write_latent(x, rows, kv_fp4, kv_scale, stream=None):

@@ -160,6 +160,101 @@ __global__ __launch_bounds__(CW_THREADS) void mxfp4_key_write_kernel(
   if ((c & 3) == 0) k_scales[dst * 4 + (c >> 2)] = (uint8_t)code_s;
 }
 
+// ---------------------------------------------------------------------------------------
+// Compressor: main-KV entries by gated pooling of m adjacent tokens ("DeepSeek-V4.1-Flash -
+// Architecture", section 1: the KV content C and compression weights Z are projections of
+// the hidden state; "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression",
+// 3.3.2: gated pooling that is a per-token projection at m = 1, and 2.3.1: no overlap and
+// no absolute position embedding). Entry j, channel c = sum over tokens i = jm .. jm+m-1 of
+// softmax_i(Z[i, c]) * C[i, c], in float32, stored as bf16 (nearest even). One lane per 8
+// channels of one entry.
+__global__ __launch_bounds__(CW_THREADS) void compress_kernel(
+    int m, int n_out, const uint16_t* __restrict__ c, const uint16_t* __restrict__ z,
+    int64_t ld_in, uint16_t* __restrict__ out, int64_t ld_out) {
+  const int64_t gid = (int64_t)blockIdx.x * CW_THREADS + threadIdx.x;
+  const int64_t j = gid >> 6;
+  const int lane = (int)(gid & 63);
+  if (j >= n_out) return;
+  float zmax[8], den[8], num[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    zmax[k] = -__builtin_inff();
+    den[k] = 0.f;
+    num[k] = 0.f;
+  }
+  for (int i = 0; i < m; ++i) {
+    float zf[8];
+    bf16x8_to_f32(*reinterpret_cast<const u32x4*>(z + (j * m + i) * ld_in + 8 * lane), zf);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) zmax[k] = fmaxf(zmax[k], zf[k]);
+  }
+  for (int i = 0; i < m; ++i) {
+    float zf[8], cf[8];
+    bf16x8_to_f32(*reinterpret_cast<const u32x4*>(z + (j * m + i) * ld_in + 8 * lane), zf);
+    bf16x8_to_f32(*reinterpret_cast<const u32x4*>(c + (j * m + i) * ld_in + 8 * lane), cf);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float g = expf(zf[k] - zmax[k]);
+      den[k] += g;
+      num[k] += g * cf[k];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = num[2 * k] / den[2 * k];
+    const float hi = num[2 * k + 1] / den[2 * k + 1];
+    o[k] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  }
+  *reinterpret_cast<u32x4*>(out + j * ld_out + 8 * lane) = o;
+}
+
+// Indexer keys as a projection of main-KV entries ("DeepSeek-v4.1 Flash: Pushing the Limits
+// of KV Cache Compression", 2.3.1): k[r, o] = sum_c e[r, c] * W[o, c] with W bf16
+// [128, 512] (output channel major), fp32 accumulation on v_mfma_f32_32x32x16_bf16, bf16
+// output (nearest even). A wavefront computes 32 rows x 32 outputs; a workgroup 32 rows x
+// all 128 outputs. A operand: lane l holds row l%32, channels k0 + 8(l/32) .. +7; B: output
+// l%32 of the wavefront's quarter, the same channels; both are one 16-byte load.
+__global__ __launch_bounds__(CW_THREADS) void project_kernel(
+    int n, const uint16_t* __restrict__ e, int64_t ld_e, const uint16_t* __restrict__ wk,
+    uint16_t* __restrict__ out, int64_t ld_out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int64_t row0 = (int64_t)blockIdx.x * 32;
+  const int64_t my_row = row0 + (lane & 31);
+  const uint16_t* arow = e + (my_row < n ? my_row : row0) * ld_e + 8 * half;
+  const uint16_t* brow = wk + (int64_t)(32 * wave + (lane & 31)) * 512 + 8 * half;
+  f32x16 acc = {};
+#pragma unroll 8
+  for (int k0 = 0; k0 < 512; k0 += 16) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(arow + k0);
+    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + k0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+  const int o = 32 * wave + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (row < n) out[row * ld_out + o] = (uint16_t)f32_to_bf16_rne(acc[r]);
+  }
+}
+
+hipError_t launch_compress(int m, int n_out, const uint16_t* c, const uint16_t* z, int64_t ld_in,
+                           uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  const int64_t threads = (int64_t)n_out * 64;
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)((threads + CW_THREADS - 1) / CW_THREADS)),
+                     dim3(CW_THREADS), 0, stream, m, n_out, c, z, ld_in, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_index_key(int n, const uint16_t* e, int64_t ld_e, const uint16_t* wk,
+                                    uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  hipLaunchKernelGGL(project_kernel, dim3((unsigned)((n + 31) / 32)), dim3(CW_THREADS), 0, stream,
+                     n, e, ld_e, wk, out, ld_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_latent_write(int n, const uint16_t* x, const int64_t* rows, uint8_t* kv_fp4,
                                int64_t fp4_stride, uint8_t* kv_scale, int64_t sc_stride,
                                int64_t n_entries, hipStream_t stream) {

@@ -208,6 +208,47 @@ int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache
                     fn);
 }
 
+int csa2_compress_kv(int m, int n_tokens, int d, const void* c, const void* z, int64_t ld_in,
+                     void* out, int64_t ld_out, void* stream) {
+  const char* fn = "csa2_compress_kv";
+  REQUIRE(d == CSA2_HEAD_DIM, CSA2_ERR_UNSUPPORTED, "%s: d %d, only %d is built", fn, d,
+          CSA2_HEAD_DIM);
+  REQUIRE(m >= 1 && m <= 8, CSA2_ERR_UNSUPPORTED, "%s: m %d, only 1..8 is built", fn, m);
+  REQUIRE(n_tokens >= 0 && n_tokens <= (1 << 28), CSA2_ERR_INVALID_ARG,
+          "%s: n_tokens %d out of range", fn, n_tokens);
+  const int n_out = n_tokens / m;
+  if (n_out == 0) return ok();
+  REQUIRE(c && z && out, CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  REQUIRE(ld_in >= d && ld_in % 8 == 0 && ld_out >= d && ld_out % 8 == 0, CSA2_ERR_INVALID_ARG,
+          "%s: ld_in and ld_out must be >= d and multiples of 8", fn);
+  REQUIRE(aligned(c, 16) && aligned(z, 16) && aligned(out, 16), CSA2_ERR_INVALID_ARG,
+          "%s: c, z and out must be 16-byte aligned", fn);
+  return hip_status(csa2::launch_compress(m, n_out, static_cast<const uint16_t*>(c),
+                                          static_cast<const uint16_t*>(z), ld_in,
+                                          static_cast<uint16_t*>(out), ld_out,
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa2_project_index_key(int n, int d_in, int d_out, const void* entries, int64_t ld_entries,
+                           const void* w_ik, void* out, int64_t ld_out, void* stream) {
+  const char* fn = "csa2_project_index_key";
+  REQUIRE(d_in == CSA2_HEAD_DIM && d_out == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
+          "%s: %d -> %d, only %d -> %d is built", fn, d_in, d_out, CSA2_HEAD_DIM, CSA2_IDX_DIM);
+  REQUIRE(n >= 0 && n <= (1 << 28), CSA2_ERR_INVALID_ARG, "%s: n %d out of range", fn, n);
+  if (n == 0) return ok();
+  REQUIRE(entries && w_ik && out, CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  REQUIRE(ld_entries >= d_in && ld_entries % 8 == 0 && ld_out >= d_out, CSA2_ERR_INVALID_ARG,
+          "%s: ld_entries must be >= %d (a multiple of 8) and ld_out >= %d", fn, d_in, d_out);
+  REQUIRE(aligned(entries, 16) && aligned(w_ik, 16) && aligned(out, 2), CSA2_ERR_INVALID_ARG,
+          "%s: entries and w_ik must be 16-byte aligned", fn);
+  return hip_status(csa2::launch_project_index_key(n, static_cast<const uint16_t*>(entries),
+                                                   ld_entries, static_cast<const uint16_t*>(w_ik),
+                                                   static_cast<uint16_t*>(out), ld_out,
+                                                   static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int csa2_write_latent(int n, const void* x, const int64_t* rows, void* kv_fp4,
                       int64_t kv_fp4_stride, void* kv_scale, int64_t kv_scale_stride,
                       int64_t n_entries, void* stream) {

@@ -57,6 +57,12 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
 
 // Cache writes: quantise bf16 rows into the cache formats (destination rows outside
 // [0, n_rows) are skipped).
+// Gated-pooling compressor: n_out entries of 512 channels from m tokens each (bf16 in/out).
+hipError_t launch_compress(int m, int n_out, const uint16_t* c, const uint16_t* z, int64_t ld_in,
+                           uint16_t* out, int64_t ld_out, hipStream_t stream);
+// Indexer keys [n, 128] = entries [n, 512] . W^T, W bf16 [128, 512].
+hipError_t launch_project_index_key(int n, const uint16_t* e, int64_t ld_e, const uint16_t* wk,
+                                    uint16_t* out, int64_t ld_out, hipStream_t stream);
 hipError_t launch_latent_write(int n, const uint16_t* x, const int64_t* rows, uint8_t* kv_fp4,
                                int64_t fp4_stride, uint8_t* kv_scale, int64_t sc_stride,
                                int64_t n_entries, hipStream_t stream);

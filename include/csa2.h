@@ -156,6 +156,35 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                            float* block_max, int64_t ld_block_max,
                            void* stream);
 
+/* The compressor: main-KV entries from the per-token projections of the hidden state
+ * ([V41F-ARCH] 1: the KV content C = H W_KV and the compression weights Z = H W_Z;
+ * [V41F-BLOG] 3.3.2: gated pooling that is a per-token projection at m = 1; 2.3.1: no
+ * overlap between adjacent entries and no absolute position embedding). Reading R22:
+ * entry j, channel c = sum over the tokens i = jm .. jm+m-1 of softmax_i(z[i, c]) *
+ * c[i, c], evaluated in float32 (exp, one division per channel) and stored as bf16 (nearest
+ * even); n_tokens / m entries (rounded down: an incomplete group gives no entry). At
+ * m = 1 the entry is c itself.
+ *   m in 1..8 (the pages use 1 in the decoder and 2 in the encoder); d must be 512.
+ *   c, z [n_tokens, ld_in] bf16, 16-byte aligned; out [n_tokens / m, ld_out] bf16.
+ *   ld_in, ld_out >= 512, multiples of 8.
+ * The entries are what csa2_write_latent quantises (after RoPE, which is applied by the
+ * caller) and what csa2_project_index_key projects.
+ * Errors: CSA2_ERR_INVALID_ARG (null pointer, bad size or alignment), CSA2_ERR_UNSUPPORTED
+ * (m or d). */
+int csa2_compress_kv(int m, int n_tokens, int d, const void* c, const void* z, int64_t ld_in,
+                     void* out, int64_t ld_out, void* stream);
+
+/* Indexer keys as a projection of main-KV entries ([V41F-BLOG] 2.3.1: CSA2 projects the
+ * main KV entries to get the indexer K). Reading R23: out[r, o] = sum_c entries[r, c] *
+ * w_ik[o, c], fp32 accumulation, bf16 output (nearest even).
+ *   d_in must be 512 and d_out 128. entries [n, ld_entries] bf16 (ld_entries >= 512, a
+ *   multiple of 8), 16-byte aligned; w_ik [128, 512] bf16 (output channel major),
+ *   16-byte aligned; out [n, ld_out] bf16, ld_out >= 128.
+ * The keys are what csa2_write_e4m3 (d = 128) or csa2_write_mxfp4_key store.
+ * Errors: CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED (d_in, d_out). */
+int csa2_project_index_key(int n, int d_in, int d_out, const void* entries, int64_t ld_entries,
+                           const void* w_ik, void* out, int64_t ld_out, void* stream);
+
 /* Block-mean indexer keys for a HISA-style two-stage filter (the alternative
  * [V41F-BLOG] 2.3.4 sets beside HSI: the prefix is cut into blocks of consecutive
  * positions, each block keeps the mean of its indexer keys, a first stage scores those

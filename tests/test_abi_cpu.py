@@ -23,7 +23,8 @@ def test_header_symbols_are_exported(C):
                      "csa2_block_pool", "csa2_topk", "csa2_pool_topk", "csa2_sparse_attn",
                      "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
                      "csa2_index_score_shared", "csa2_index_score_bf16",
-                     "csa2_block_mean_keys", "csa2_version", "csa2_last_error"}
+                     "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
+                     "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -127,6 +128,24 @@ def test_block_mean_keys_rejections(C):
     assert call(max_blocks=0) == 1
     assert call(n_entries=-1) == 1
     assert call(n_q=0, km=None) == 0
+
+
+def test_compressor_and_projection_rejections(C):
+    L = C.lib
+    assert L.csa2_compress_kv(2, 10, 256, FAKE, FAKE, 512, FAKE, 512, None) == 2   # d
+    assert L.csa2_compress_kv(0, 10, 512, FAKE, FAKE, 512, FAKE, 512, None) == 2   # m
+    assert L.csa2_compress_kv(9, 10, 512, FAKE, FAKE, 512, FAKE, 512, None) == 2
+    assert L.csa2_compress_kv(2, 10, 512, None, FAKE, 512, FAKE, 512, None) == 1
+    assert L.csa2_compress_kv(2, 10, 512, FAKE + 8, FAKE, 512, FAKE, 512, None) == 1
+    assert L.csa2_compress_kv(2, 10, 512, FAKE, FAKE, 500, FAKE, 512, None) == 1   # ld_in
+    assert L.csa2_compress_kv(2, -1, 512, FAKE, FAKE, 512, FAKE, 512, None) == 1
+    assert L.csa2_compress_kv(2, 1, 512, None, None, 0, None, 0, None) == 0        # no entry
+    assert L.csa2_project_index_key(4, 512, 64, FAKE, 512, FAKE, FAKE, 128, None) == 2
+    assert L.csa2_project_index_key(4, 512, 128, FAKE, 512, None, FAKE, 128, None) == 1
+    assert L.csa2_project_index_key(4, 512, 128, FAKE, 256, FAKE, FAKE, 128, None) == 1
+    assert L.csa2_project_index_key(4, 512, 128, FAKE + 8, 512, FAKE, FAKE, 128, None) == 1
+    assert b"csa2_project_index_key" in L.csa2_last_error()
+    assert L.csa2_project_index_key(0, 512, 128, None, 0, None, None, 0, None) == 0
 
 
 def test_cache_write_rejections(C):
