@@ -212,31 +212,41 @@ __global__ __launch_bounds__(CW_THREADS) void compress_kernel(
 // Indexer keys as a projection of main-KV entries ("DeepSeek-v4.1 Flash: Pushing the Limits
 // of KV Cache Compression", 2.3.1): k[r, o] = sum_c e[r, c] * W[o, c] with W bf16
 // [128, 512] (output channel major), fp32 accumulation on v_mfma_f32_32x32x16_bf16, bf16
-// output (nearest even). A wavefront computes 32 rows x 32 outputs; a workgroup 32 rows x
-// all 128 outputs. A operand: lane l holds row l%32, channels k0 + 8(l/32) .. +7; B: output
-// l%32 of the wavefront's quarter, the same channels; both are one 16-byte load.
+// output (nearest even). A wavefront computes 32 rows x all 128 outputs as four 32 x 32
+// tiles (four independent accumulation chains sharing each A operand); a workgroup 128
+// rows. A operand: lane l holds row l%32, channels k0 + 8(l/32) .. +7; B of tile q: output
+// 32q + l%32, the same channels; each is one 16-byte load (W stays in cache).
+constexpr int PJ_ROWS = 32 * (CW_THREADS / 64);
+
 __global__ __launch_bounds__(CW_THREADS) void project_kernel(
     int n, const uint16_t* __restrict__ e, int64_t ld_e, const uint16_t* __restrict__ wk,
     uint16_t* __restrict__ out, int64_t ld_out) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
-  const int64_t row0 = (int64_t)blockIdx.x * 32;
+  const int64_t row0 = (int64_t)blockIdx.x * PJ_ROWS + 32 * wave;
+  if (row0 >= n) return;
   const int64_t my_row = row0 + (lane & 31);
   const uint16_t* arow = e + (my_row < n ? my_row : row0) * ld_e + 8 * half;
-  const uint16_t* brow = wk + (int64_t)(32 * wave + (lane & 31)) * 512 + 8 * half;
-  f32x16 acc = {};
-#pragma unroll 8
+  const uint16_t* brow = wk + (int64_t)(lane & 31) * 512 + 8 * half;
+  f32x16 acc[4] = {};
+#pragma unroll 4
   for (int k0 = 0; k0 < 512; k0 += 16) {
     const bf16x8 av = *reinterpret_cast<const bf16x8*>(arow + k0);
-    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-  }
-  const int o = 32 * wave + (lane & 31);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (row < n) out[row * ld_out + o] = (uint16_t)f32_to_bf16_rne(acc[r]);
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(brow + 32 * 512 * q + k0);
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[q], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int o = 32 * q + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (row < n) out[row * ld_out + o] = (uint16_t)f32_to_bf16_rne(acc[q][r]);
+    }
   }
 }
 
@@ -250,7 +260,8 @@ hipError_t launch_compress(int m, int n_out, const uint16_t* c, const uint16_t* 
 
 hipError_t launch_project_index_key(int n, const uint16_t* e, int64_t ld_e, const uint16_t* wk,
                                     uint16_t* out, int64_t ld_out, hipStream_t stream) {
-  hipLaunchKernelGGL(project_kernel, dim3((unsigned)((n + 31) / 32)), dim3(CW_THREADS), 0, stream,
+  hipLaunchKernelGGL(project_kernel, dim3((unsigned)((n + PJ_ROWS - 1) / PJ_ROWS)), dim3(CW_THREADS),
+                     0, stream,
                      n, e, ld_e, wk, out, ld_out);
   return hipGetLastError();
 }
