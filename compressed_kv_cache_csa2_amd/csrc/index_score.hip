@@ -188,14 +188,14 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
 // Queries that share one sequence (chunked prefill: every query reads the same cache rows
 // from kv_start, each up to its own causal n_visible). A workgroup scores SQ_QT queries
 // (SQ_QW per wavefront, their MFMA operands and head weights held in registers) against
-// one 2,048-row tile. Per 32-row step the four wavefronts each load and convert a quarter
+// one 4,096-row tile. Per 32-row step the four wavefronts each load and convert a quarter
 // of the rows' channels into an LDS buffer in B-operand order (double-buffered, one barrier
 // per step); then every wavefront reads the step's 8 operands once and runs its queries'
 // products on them. Rows are read and converted once per SQ_QT queries, and the LDS
 // traffic is one 8 KiB operand read per wavefront and step.
 constexpr int SQ_QW = 2;
 constexpr int SQ_QT = (IS_THREADS / 64) * SQ_QW;
-constexpr int SQ_TILE = 2048;
+constexpr int SQ_TILE = 4096;
 
 __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
     int n_q, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -251,7 +251,9 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
     const int64_t row = kv_start + slot;
     return (row >= 0 && row < n_entries) ? row : -1;
   };
-  constexpr int PF = 4;   // steps whose rows are in flight
+  // steps whose rows are in flight: the rows come mostly from cache (every query group reads
+  // the same sequence), and 16 steps of lead hide that latency at two waves per SIMD
+  constexpr int PF = 16;
   u32x4 raw[PF];
   auto load = [&](int step) -> u32x4 {
     const int64_t r = row_at(step);
