@@ -34,7 +34,7 @@ def _load():
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
-    lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, P]
+    lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, I, P]
     lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
     lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
@@ -218,10 +218,11 @@ def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visibl
 
 
 def csa2_block_mean_keys(k_cache, kv_start, n_visible, km, km_start, n_blocks, max_blocks=None,
-                         stream=None):
+                         last_only=False, stream=None):
     """Block-mean keys (bf16, one row per 8 visible positions) of each query's E4M3 keys
     into km [R, 128] from row km_start[t]; n_blocks [n_q] int32 receives ceil(n_visible/8).
-    max_blocks defaults to what fits in km."""
+    max_blocks defaults to what fits in km; last_only recomputes only each query's latest
+    block (after an append)."""
     n_q = kv_start.shape[0]
     if km.dim() != 2 or km.shape[1] != 128:
         raise ValueError("csa2_block_mean_keys: km must be [rows, 128]")
@@ -231,7 +232,8 @@ def csa2_block_mean_keys(k_cache, kv_start, n_visible, km, km_start, n_blocks, m
         n_q, 128, 8, _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
         _ptr(km, torch.bfloat16, "km"), _ptr(km_start, torch.int64, "km_start"), km.shape[0],
-        int(max_blocks), _ptr(n_blocks, torch.int32, "n_blocks"), _stream(stream)))
+        int(max_blocks), _ptr(n_blocks, torch.int32, "n_blocks"), 1 if last_only else 0,
+        _stream(stream)))
 
 
 def csa2_index_score_bf16(mode, q_idx, w, k_rows, kv_start, n_visible, scores, block_max=None,

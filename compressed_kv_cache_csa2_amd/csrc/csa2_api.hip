@@ -184,7 +184,7 @@ int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx, con
 int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache,
                          int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
                          void* km, const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
-                         int32_t* n_blocks, void* stream) {
+                         int32_t* n_blocks, int last_only, void* stream) {
   const char* fn = "csa2_block_mean_keys";
   REQUIRE(d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED, "%s: d_idx %d, only %d is built", fn,
           d_idx, CSA2_IDX_DIM);
@@ -204,7 +204,7 @@ int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache
   return hip_status(csa2::launch_block_mean_keys(
                         n_q, static_cast<const uint8_t*>(k_cache), n_entries, kv_start, n_visible,
                         static_cast<uint16_t*>(km), km_start, n_km_rows, max_blocks, n_blocks,
-                        static_cast<hipStream_t>(stream)),
+                        last_only != 0, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -22,7 +22,7 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
 hipError_t launch_block_mean_keys(int n_q, const uint8_t* k_cache, int64_t n_entries,
                                   const int64_t* kv_start, const int32_t* n_visible, uint16_t* km,
                                   const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
-                                  int32_t* n_blocks, hipStream_t stream);
+                                  int32_t* n_blocks, bool last_only, hipStream_t stream);
 
 // Full-mode scores of queries that all read the cache rows from one kv_start.
 hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float* w,

@@ -320,19 +320,22 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
 // mean of the E4M3 keys at positions 8b .. 8b+7 that are visible and in the cache, stored
 // as bf16 (nearest even) at row km_start[t] + b; n_blocks[t] receives ceil(n_visible / 8).
 // 16 lanes per block, lane c covering channels 8c .. 8c+7; sums of E4M3 values are exact
-// in float32 and the mean is one float32 division by the count.
+// in float32 and the mean is one float32 division by the count. With last_only, only the
+// block holding position n_visible - 1 is recomputed (the one a newly appended token
+// changes).
 __global__ __launch_bounds__(IS_THREADS) void block_mean_keys_kernel(
     const uint8_t* __restrict__ k_cache, int64_t n_entries, const int64_t* __restrict__ kv_start,
     const int32_t* __restrict__ n_visible, uint16_t* __restrict__ km,
     const int64_t* __restrict__ km_start, int64_t n_km_rows, int64_t max_blocks,
-    int32_t* __restrict__ n_blocks) {
+    int32_t* __restrict__ n_blocks, int last_only) {
   const int t = blockIdx.y;
   const int64_t nv = n_visible[t] > 0 ? n_visible[t] : 0;
   const int64_t nb = (nv + 7) / 8;
   if (blockIdx.x == 0 && threadIdx.x == 0) n_blocks[t] = (int32_t)nb;
-  const int64_t b = (int64_t)blockIdx.x * (IS_THREADS / 16) + (threadIdx.x >> 4);
+  if (last_only && (threadIdx.x >> 4) != 0) return;
+  const int64_t b = last_only ? nb - 1 : (int64_t)blockIdx.x * (IS_THREADS / 16) + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
-  if (b >= nb || b >= max_blocks) return;
+  if (b < 0 || b >= nb || b >= max_blocks) return;
   const int64_t dst = km_start[t] + b;
   if (dst < 0 || dst >= n_km_rows) return;
   const int64_t base = kv_start[t];
@@ -367,11 +370,12 @@ __global__ __launch_bounds__(IS_THREADS) void block_mean_keys_kernel(
 hipError_t launch_block_mean_keys(int n_q, const uint8_t* k_cache, int64_t n_entries,
                                   const int64_t* kv_start, const int32_t* n_visible, uint16_t* km,
                                   const int64_t* km_start, int64_t n_km_rows, int64_t max_blocks,
-                                  int32_t* n_blocks, hipStream_t stream) {
+                                  int32_t* n_blocks, bool last_only, hipStream_t stream) {
   const int per_block = IS_THREADS / 16;
-  dim3 grid((unsigned)((max_blocks + per_block - 1) / per_block), (unsigned)n_q);
+  dim3 grid(last_only ? 1u : (unsigned)((max_blocks + per_block - 1) / per_block), (unsigned)n_q);
   hipLaunchKernelGGL(block_mean_keys_kernel, grid, dim3(IS_THREADS), 0, stream, k_cache,
-                     n_entries, kv_start, n_visible, km, km_start, n_km_rows, max_blocks, n_blocks);
+                     n_entries, kv_start, n_visible, km, km_start, n_km_rows, max_blocks, n_blocks,
+                     last_only ? 1 : 0);
   return hipGetLastError();
 }
 

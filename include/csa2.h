@@ -202,6 +202,9 @@ int csa2_project_index_key(int n, int d_in, int d_out, const void* entries, int6
  *   outside [0, n_km_rows) is skipped); 1 <= max_blocks <= 2^28 bounds the blocks
  *   written per query; n_blocks [n_q] int32 output. Queries that share a sequence may
  *   share km rows (the same values are written).
+ *   last_only nonzero: only block nb - 1 (the one holding position n - 1) is recomputed,
+ *   for the decoder's append of one token per query (the pages: a new token changes one
+ *   block and completed blocks keep their summary); other km rows are left as they are.
  * The block means are what csa2_index_score_bf16 (FULL mode, n_visible = n_blocks,
  * kv_start = km_start) scores; those block scores, passed to csa2_block_pool as its
  * block_max with the position count n_visible, give the HISA pool.
@@ -210,7 +213,7 @@ int csa2_project_index_key(int n, int d_in, int d_out, const void* entries, int6
 int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache,
                          int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
                          void* km, const int64_t* km_start, int64_t n_km_rows,
-                         int64_t max_blocks, int32_t* n_blocks, void* stream);
+                         int64_t max_blocks, int32_t* n_blocks, int last_only, void* stream);
 
 /* Lightning-indexer score over bf16 key rows (the block-mean keys above). Identical to
  * csa2_index_score (same modes, slots, outputs, -inf rules and errors) except that

@@ -117,7 +117,7 @@ def test_block_mean_keys_rejections(C):
     def call(**kw):
         a = dict(n_q=1, d_idx=128, block_size=8, k_cache=FAKE, n_entries=10, kv_start=FAKE,
                  n_visible=FAKE, km=FAKE, km_start=FAKE, n_km_rows=4, max_blocks=2,
-                 n_blocks=FAKE, stream=None)
+                 n_blocks=FAKE, last_only=0, stream=None)
         a.update(kw)
         return C.lib.csa2_block_mean_keys(*a.values())
     assert call(d_idx=64) == 2

@@ -54,6 +54,40 @@ def test_block_mean_keys_exact(C, dev):
         assert not km3[row0 + m:row0 + 3 + 1].view(torch.int16).any()
 
 
+def test_block_mean_keys_append_updates_the_latest_block(C, dev):
+    """After one key is appended per query, recomputing only the latest block gives the same
+    means as a full rebuild (completed blocks keep their summary)."""
+    from compressed_kv_cache_csa2_amd import synth
+    nvis = [1000, 17, 8 * 50, 0]
+    wl = synth.make_decode("app", 4, 0, ("full",), False, 0, n_visible=nvis, kv_gap=16,
+                           seed=44).to(dev)
+    rows_per_q = 200
+    km = torch.zeros((4 * rows_per_q, 128), dtype=torch.bfloat16, device=dev)
+    km_start = torch.arange(4, dtype=torch.int64, device=dev) * rows_per_q
+    nb = torch.zeros(4, dtype=torch.int32, device=dev)
+    C.csa2_block_mean_keys(wl.k_cache, wl.kv_start, wl.n_visible, km, km_start, nb,
+                           max_blocks=rows_per_q)
+    g = torch.Generator().manual_seed(45)
+    for t, n in enumerate(nvis):
+        new = synth.encode_e4m3(torch.randn((1, 128), generator=g)).to(dev)
+        wl.k_cache[int(wl.kv_start[t]) + n] = new[0]
+    n_after = wl.n_visible + 1
+    C.csa2_block_mean_keys(wl.k_cache, wl.kv_start, n_after, km, km_start, nb,
+                           max_blocks=rows_per_q, last_only=True)
+    km_full = torch.zeros_like(km)
+    nb_full = torch.zeros_like(nb)
+    C.csa2_block_mean_keys(wl.k_cache, wl.kv_start, n_after, km_full, km_start, nb_full,
+                           max_blocks=rows_per_q)
+    torch.cuda.synchronize()
+    assert torch.equal(nb, nb_full)
+    assert torch.equal(km.view(torch.int16), km_full.view(torch.int16))
+    k_all = wl.k_cache.cpu().numpy()
+    for t, n in enumerate(nvis):
+        start = int(wl.kv_start[t])
+        ref = O.block_mean_keys(k_all[start:start + n + 1], n + 1)
+        assert np.array_equal(np_u16(km[t * rows_per_q:t * rows_per_q + len(ref)]), ref), t
+
+
 def test_index_score_bf16_parity(C, dev):
     """Full and Reindex scoring of bf16 key rows against the oracle's indexer score."""
     g = torch.Generator().manual_seed(43)
