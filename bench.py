@@ -28,8 +28,9 @@ those counter runs.
 --coarse hisa swaps the HSI pool for the block-mean two-stage filter in every indexer layer
 (block means resident, as a decoder keeps them up to date); the dominant kernel is then the
 block-mean scorer (256 B of bf16 mean key read + 4 B of score written per (query, block)).
---recall adds the planted-needle recall of the first indexer layer's pool and Top-K under
-both filters.
+needle_recall (decode workloads, which plant positions): the share of planted positions in
+the Full layer's Top-K, the pool and the Reindex layer's Top-K; --recall adds the same
+under the block-mean filter.
 
 cpu_baseline: the fp64 oracle (oracle/) run on the host over a bounded sample of the same
 workload's queries (whole layer stack per query), scaled to queries/s.
@@ -99,34 +100,50 @@ def hisa_stage1_bytes(wl):
     return blocks * (256 + 4) + wl.n_q * (32 * 128 * 2 + 32 * 4)
 
 
-def needle_recall(wl, buf, C, means):
-    """Share of the planted positions that the first indexer layer's pool and Top-K keep,
-    under the HSI pool and under the block-mean filter."""
+def _recall(planted, nv, pool=None, idx=None):
+    """Share of the planted positions inside a pool (block ids) or an index set."""
+    import torch
+    hit = total = 0
+    for t in range(planted.shape[0]):
+        p = torch.unique(planted[t][planted[t] < nv[t]])
+        total += p.numel()
+        if pool is not None:
+            hit += int(torch.isin(p // 8, pool[t]).sum())
+        else:
+            hit += int(torch.isin(p, idx[t].to(torch.int64)).sum())
+    return hit / max(1, total)
+
+
+def needle_recall(wl, buf, C, means=None):
+    """Share of the planted positions kept by each selection of the stack: the Full layer's
+    Top-K, the pool, and the Reindex layer's Top-K (which uses its own query, unrelated to
+    the planting). With block means, the same under the block-mean filter, whose every
+    indexer layer builds its own pool (the first layer's pool is taken on its own)."""
     import torch
     from compressed_kv_cache_csa2_amd import layers
     planted = wl.planted.cpu()
     nv = wl.n_visible.cpu()
-    lay = wl.layers[0]
+    li_full = next(i for i, l in enumerate(wl.layers) if l.mode == "full")
+    li_re = next((i for i, l in enumerate(wl.layers) if l.mode == "reindex"), None)
     out = {}
-    for coarse in ("hsi", "hisa"):
-        if coarse == "hsi":
-            layers.index_score(wl, C.FULL, lay, None, buf.block_max,
-                               ld_scores=buf.scores.shape[1])
-            C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool)
-            layers.index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool)
-            C.csa2_topk(buf.re_scores, buf.idx[0], pool_blocks=buf.pool)
-        else:
-            layers.hisa_select(wl, lay, buf, means, buf.idx[0])
+    for coarse in (("hsi", "hisa") if means is not None else ("hsi",)):
+        res = {}
+        if coarse == "hisa":
+            layers.hisa_select(wl, wl.layers[li_full], buf, means, buf.idx[li_full])
+            torch.cuda.synchronize()
+            res["full_topk"] = _recall(planted, nv, idx=buf.idx[li_full].cpu())
+            res["pool"] = _recall(planted, nv, pool=buf.pool.cpu())
+        layers.run_layers(wl, buf, coarse=coarse, means=means)
         torch.cuda.synchronize()
-        pool, idx = buf.pool.cpu(), buf.idx[0].cpu()
-        n_in_pool = n_in_topk = n_all = 0
-        for t in range(wl.n_q):
-            p = torch.unique(planted[t][planted[t] < nv[t]])
-            n_all += p.numel()
-            n_in_pool += int(torch.isin(p // 8, pool[t]).sum())
-            n_in_topk += int(torch.isin(p, idx[t].to(torch.int64)).sum())
-        out[coarse] = {"pool": n_in_pool / max(1, n_all), "topk": n_in_topk / max(1, n_all),
-                       "needles": n_all}
+        if coarse == "hsi":
+            res["full_topk"] = _recall(planted, nv, idx=buf.idx[li_full].cpu())
+            if wl.with_pool:
+                res["pool"] = _recall(planted, nv, pool=buf.pool.cpu())
+        if li_re is not None:
+            res["reindex_topk"] = _recall(planted, nv, idx=buf.idx[li_re].cpu())
+        res["needles"] = int(sum(torch.unique(planted[t][planted[t] < nv[t]]).numel()
+                                 for t in range(planted.shape[0])))
+        out[coarse] = res
     return out
 
 
@@ -245,7 +262,7 @@ def main():
     ap.add_argument("--coarse", choices=("hsi", "hisa"), default="hsi",
                     help="coarse filter of the indexer layers (pooled stacks)")
     ap.add_argument("--recall", action="store_true",
-                    help="planted-needle recall of the first indexer layer under both filters")
+                    help="also report needle recall under the block-mean filter")
     ap.add_argument("--profile-kernel", type=int, default=0, metavar="N",
                     help="only launch the Full indexer and a 1 GiB copy N times (counter runs)")
     args = ap.parse_args()
@@ -394,7 +411,8 @@ def main():
         for n, (a, b) in zip(names, evs):
             print(f"[bench] {n:24s} {a.elapsed_time(b) * 1e3:9.1f} us", file=sys.stderr)
 
-    recall = needle_recall(wl, buf, C, means) if args.recall else None
+    recall = needle_recall(wl, buf, C, means if args.recall else None) \
+        if wl.planted is not None else None
     step_bytes = algorithmic_bytes(wl, coarse=args.coarse)
     value = wl.n_q / (ms_step * 1e-3)
     cpu = None
