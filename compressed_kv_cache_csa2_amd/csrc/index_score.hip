@@ -18,14 +18,16 @@
 // workgroup's rows have been read; a Full pass may write the block maxima alone (the 4-byte
 // score stores cost about a tenth of the pass's time against 3% of its bytes).
 //
-// Indexer keys come in one of two formats: E4M3 rows of 128 bytes, or MXFP4 rows (the
+// Indexer keys come in one of three formats: E4M3 rows of 128 bytes, MXFP4 rows (the
 // OCP microscaling format the pages name for the indexer cache, "DeepSeek-v4.1 Flash:
 // Pushing the Limits of KV Cache Compression", 2.4.4 and 3.1): 64 bytes of E2M1 codes
 // (channel 2m in the low nibble of byte m) and 4 E8M0 scale bytes, one per 32 channels.
 // An MXFP4 lane reads 32 bytes of codes (its 64 channels) and the row's scale word, and
 // converts with the hardware E2M1 -> bf16 conversion whose scale operand is the E8M0
-// scale as a power of two: exact while the products stay in bf16's normal range. Work per step is 8,192 flops per position against 128
-// bytes read: HBM-bound at 64 flop/B.
+// scale as a power of two: exact while the products stay in bf16's normal range; or bf16
+// rows of 256 bytes (the block-mean keys of the two-stage filter, fed to the MFMA as they
+// are). Work per step is 8,192 flops per position against 128 bytes read (E4M3): HBM-bound
+// at 64 flop/B.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
