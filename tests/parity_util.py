@@ -142,3 +142,42 @@ def check_query(wl, buf, t, seq=None, report=None):
         if report is not None:
             report.append((t, li, rel))
     return n_cmp
+
+
+def check_query_hisa(wl, idx, pools, out, t):
+    """Compare query t of a stack run through the block-mean filter with the oracle: each
+    indexer layer's pool (pools[li], captured after that layer) against the oracle's
+    block-mean pool, its Top-K (idx[li]) against the oracle's rescoring of the GPU's pool,
+    and every layer's attention output against the oracle's attention over the GPU's
+    indices. Returns the number of attention outputs compared."""
+    from compressed_kv_cache_csa2_amd import synth
+    seq = synth.sequence_to_host(wl, t)
+    nv = seq["n_visible"]
+    km = O.block_mean_keys(seq["k_cache"], nv)
+    current = None
+    n_cmp = 0
+    for li, lay in enumerate(seq["layers"]):
+        if li in pools:
+            bs = O.index_score_rows(O.bf16_decode(lay["q_idx"]), np.asarray(lay["w"], np.float64),
+                                    O.bf16_decode(km))
+            bs[(nv - 1) // 8] = np.inf
+            pool_gpu = pools[li][t].cpu().numpy()
+            ref_pool = O.hisa_pool(lay["q_idx"], lay["w"], km, nv)
+            kb, bb = band_of(bs, 2048)
+            assert_set_band(pool_gpu, ref_pool, lambda b: bs[b], kb, bb, f"q{t} L{li} pool")
+            padded = np.full(2048, -1, np.int64)
+            kept = pool_gpu[pool_gpu >= 0]
+            padded[:len(kept)] = kept
+            scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
+            ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), padded)
+            pos_of_slot = O.slots_to_positions(np.arange(len(scores)), padded)
+            score_at = dict(zip(pos_of_slot.tolist(), scores.tolist()))
+            kth, band = band_of(scores, 512)
+            current = idx[li][t].cpu().numpy()
+            assert_set_band(current, ref_idx, lambda p: score_at[p], kth, band,
+                            f"q{t} L{li} top-k")
+        res = O.reuse_layer(current, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
+                            lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
+        assert_attn_close(out[li][t].float().cpu().numpy(), res["out"], f"q{t} L{li} attention")
+        n_cmp += 1
+    return n_cmp

@@ -68,6 +68,42 @@ def test_decode_256k_sampled_as_benched(dev):
     torch.cuda.empty_cache()
 
 
+def test_decode_256k_mxfp4_sampled(dev):
+    wl, buf = _run("decode_256k_mxfp4", dev)
+    queries = [0, wl.n_q - 1]
+    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    del wl, buf
+    torch.cuda.empty_cache()
+
+
+def test_decode_256k_block_mean_filter_sampled(dev):
+    """decode_256k through the block-mean filter (every indexer layer's pool captured),
+    checked on sampled queries; the whole stack then reproduces the same indices."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    from tests.parity_util import check_query_hisa
+    wl = synth.make_workload("decode_256k", device=dev)
+    means = layers.build_block_means(wl)
+    buf = layers.alloc_buffers(wl)
+    pools = {}
+    for li, lay in enumerate(wl.layers):
+        if lay.mode in ("full", "reindex"):
+            layers.hisa_select(wl, lay, buf, means, buf.idx[li])
+            pools[li] = buf.pool.clone()
+    torch.cuda.synchronize()
+    idx = buf.idx.clone()
+    layers.run_layers(wl, buf, coarse="hisa", means=means)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.idx, idx)
+    _log("decode_256k block-mean filter: stack ran")
+    n = 0
+    for t in (0, wl.n_q - 1):
+        n += check_query_hisa(wl, idx, pools, buf.out, t)
+        _log(f"decode_256k block-mean filter: query {t} checked")
+    assert n == 2 * len(wl.layers)
+    del wl, buf, means
+    torch.cuda.empty_cache()
+
+
 def test_prefill_128k_m2_sampled(dev):
     wl, buf = _run("prefill_128k_m2", dev)
     queries = [0, 1, 2047, wl.n_q - 1]

@@ -6,8 +6,7 @@ import pytest
 import torch
 
 import oracle.csa2_oracle as O
-from tests.parity_util import (assert_attn_close, assert_scores_close, assert_set_band,
-                               band_of, np_u16)
+from tests.parity_util import assert_scores_close, check_query_hisa, np_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -162,35 +161,5 @@ def test_hisa_decoder_stack_parity(C, dev):
     layers.run_layers(wl, buf2, coarse="hisa", means=means)
     torch.cuda.synchronize()
     assert torch.equal(buf2.idx, step_idx)
-    n_cmp = 0
-    for t in range(wl.n_q):
-        seq = synth.sequence_to_host(wl, t)
-        nv = seq["n_visible"]
-        km = O.block_mean_keys(seq["k_cache"], nv)
-        current = None
-        for li, lay in enumerate(seq["layers"]):
-            if li in pools:
-                bs = O.index_score_rows(O.bf16_decode(lay["q_idx"]),
-                                        np.asarray(lay["w"], np.float64), O.bf16_decode(km))
-                bs[(nv - 1) // 8] = np.inf
-                pool_gpu = pools[li][t].cpu().numpy()
-                ref_pool = O.hisa_pool(lay["q_idx"], lay["w"], km, nv)
-                kb, bb = band_of(bs, 2048)
-                assert_set_band(pool_gpu, ref_pool, lambda b: bs[b], kb, bb, f"q{t} L{li} pool")
-                padded = np.full(2048, -1, np.int64)
-                kept = pool_gpu[pool_gpu >= 0]
-                padded[:len(kept)] = kept
-                scores = O.reindex_scores(lay["q_idx"], lay["w"], seq["k_cache"], 0, nv, padded)
-                ref_idx = O.slots_to_positions(O.topk_slots(scores, 512), padded)
-                pos_of_slot = O.slots_to_positions(np.arange(len(scores)), padded)
-                score_at = dict(zip(pos_of_slot.tolist(), scores.tolist()))
-                kth, band = band_of(scores, 512)
-                current = step_idx[li][t].cpu().numpy()
-                assert_set_band(current, ref_idx, lambda p: score_at[p], kth, band,
-                                f"q{t} L{li} top-k")
-            res = O.reuse_layer(current, lay["q"], seq["kv_fp4"], seq["kv_scale"], 0,
-                                lay["window_kv"], 0, lay["n_swa"], wl.softmax_scale)
-            assert_attn_close(buf2.out[li][t].float().cpu().numpy(), res["out"],
-                              f"q{t} L{li} attention")
-            n_cmp += 1
+    n_cmp = sum(check_query_hisa(wl, step_idx, pools, buf2.out, t) for t in range(wl.n_q))
     assert n_cmp == wl.n_q * len(wl.layers)
