@@ -476,8 +476,9 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": None if hisa else measured_traffic(wl.name),
                      "kernel": "index_score_kernel (block-mean scorer, bf16 mean keys)" if hisa
-                               else "index_score_kernel (Full-layer indexer"
-                               + (", MXFP4 keys" if wl.k_codes is not None else ", E4M3 keys")
+                               else ("index_score_full_wide_fp4_kernel (Full-layer indexer, "
+                                     "MXFP4 keys" if wl.k_codes is not None else
+                                     "index_score_kernel (Full-layer indexer, E4M3 keys")
                                + (", block maxima only)" if wl.with_pool else ")"),
                      "launch_us": idx_us, "bytes_per_launch": idx_bytes},
         "cpu_baseline": cpu,
