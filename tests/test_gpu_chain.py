@@ -108,3 +108,43 @@ def test_small_encoder_schedule(dev):
     assert compared == 3 * len(wl.layers)
     # the groups really read different caches: group 1's Full layer selects differently
     assert not torch.equal(buf.idx[2], buf.idx[8])
+
+
+@pytest.mark.parametrize("kind", ["hisa", "encoder"])
+def test_graph_replay_of_the_other_stacks(dev, kind):
+    """The block-mean filter stack and the encoder schedule captured in a HIP graph give
+    the eager result bitwise on every replay (eager work in between)."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    if kind == "hisa":
+        wl = synth.make_decode("g_hisa", 3, 20000, synth.DECODE_LAYERS, True, 16, seed=25).to(dev)
+        means = layers.build_block_means(wl)
+        kw = dict(coarse="hisa", means=means)
+    else:
+        wl = synth.make_encoder("g_enc", n_q=40, n_entries=2500, seed=26).to(dev)
+        kw = {}
+    eager = layers.alloc_buffers(wl)
+    layers.run_layers(wl, eager, **kw)
+    torch.cuda.synchronize()
+    buf = layers.alloc_buffers(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        layers.run_layers(wl, buf, stream=s, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layers.run_layers(wl, buf, stream=s, **kw)
+    # the slots the indexer layers publish (Reuse and SWA layers publish none of their own)
+    rows = [li for li, lay in enumerate(wl.layers) if lay.mode in ("full", "reindex")]
+    for rep in range(3):
+        buf.out.zero_()
+        buf.lse.zero_()
+        for li in rows:
+            buf.idx[li].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li in rows:
+            assert torch.equal(buf.idx[li], eager.idx[li]), (rep, li)
+        assert torch.equal(buf.out.view(torch.int16), eager.out.view(torch.int16)), rep
+        assert torch.equal(buf.lse, eager.lse), rep
+        layers.run_layers(wl, eager, **kw)
