@@ -48,7 +48,7 @@ const char* csa2_version(void) { return "csa2-gfx950 0.1.0"; }
 const char* csa2_last_error(void) { return g_err; }
 
 size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k) {
-  // No call of this build needs scratch memory: the selections keep their state in LDS
+  // No call of this library needs scratch memory: the selections keep their state in LDS
   // and the attention's workgroups write disjoint output channels.
   (void)op;
   (void)n_q;

@@ -24,7 +24,7 @@
  *   - Every call is stateless and re-entrant and returns an int status (CSA2_OK = 0).
  *   - Tensor arguments are caller-owned DEVICE pointers. The library never allocates,
  *     frees or keeps them past the enqueued work. Calls that take a workspace accept a
- *     caller-owned device workspace of csa2_workspace_bytes(...) bytes; in this build
+ *     caller-owned device workspace of csa2_workspace_bytes(...) bytes; in this version
  *     that is 0 for every op, so NULL/0 may be passed.
  *   - Layouts are dense row-major with the leading dimensions given. bf16 values are
  *     passed as their 16-bit patterns; FP8 E4M3 and FP4 E2M1 as bytes.
@@ -78,7 +78,7 @@ enum {
 
 /* Workspace sizing. `op` is one of the CSA2_OP_* values; `n_q` queries, `max_cols` the
  * largest row length (scores columns or block count) and `k` the selection size the
- * call will be made with. Returns 0 when the op needs no workspace, which in this build
+ * call will be made with. Returns 0 when the op needs no workspace, which in this version
  * is every op. */
 enum { CSA2_OP_INDEX_SCORE = 0, CSA2_OP_BLOCK_POOL = 1, CSA2_OP_TOPK = 2, CSA2_OP_SPARSE_ATTN = 3 };
 size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);

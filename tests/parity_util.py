@@ -81,7 +81,7 @@ def assert_attn_close(gpu_out, ref_out, what=""):
 def check_query(wl, buf, t, seq=None, report=None):
     """Compare every layer of query t of a run (buffers `buf`) with the oracle.
 
-    Each step is judged on the GPU's own previous output, so a legitimate swap inside a
+    Each step is checked on the GPU's own previous output, so a legitimate swap inside a
     tie band never cascades: the Full Top-K and pool against the oracle's scores, the
     Reindex Top-K against the oracle's rescoring of the GPU's pool, and every attention
     (output and lse) against the oracle's attention over the GPU's published indices.
