@@ -380,6 +380,43 @@ def hsi_pool(scores: np.ndarray, n_visible: int, block_size: int = 8,
     return topk_slots(bm, n_keep)
 
 
+def mxfp8_quantize(x: np.ndarray):
+    """Rows of bf16 values (as float32) -> MXFP8 (E4M3 codes [..., d], E8M0 scales [..., d/32]).
+
+    The pages' V4 lineage runs the indexer in low precision (FP4 keys, [V41F-BLOG] 2.4.4,
+    3.1); reading R24 quantises the indexer query with the OCP microscaling recipe for
+    E4M3 elements: per 32-channel group the shared exponent is floor(log2 amax) - 8 (8 =
+    E4M3's largest exponent), stored biased and kept in 1..254 (127 for an all-zero group),
+    and each value is E4M3(x / 2^X), nearest even, saturating at 448."""
+    x = np.asarray(x, np.float32)
+    g = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.abs(g).max(axis=-1).astype(np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = m * 2^e, m in [0.5, 1)
+    code_s = np.where(amax > 0, np.clip(e - 1 - 8 + 127, 1, 254), 127).astype(np.int64)
+    q = (g.astype(np.float64) * np.ldexp(1.0, 127 - code_s)[..., None]).astype(np.float32)
+    return e4m3_round(q).reshape(x.shape), code_s.astype(np.uint8)
+
+
+def mxfp8_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 rows -> float64: E4M3 value of each code times 2^(scale - 127) of its group."""
+    v = e4m3_decode(np.asarray(codes, np.uint8))
+    sc = np.repeat(np.ldexp(1.0, np.asarray(scales, np.int64) - 127), 32, axis=-1)
+    return v * sc
+
+
+def full_scores_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n_visible, width):
+    """Full-mode scores with an MXFP8 indexer query over MXFP4 keys (reading R24): the
+    index score of [V41F-BLOG] 2.3.1 on the decoded query and keys; slots past n_visible
+    are -inf."""
+    out = np.full(int(width), NEG_INF)
+    n = min(int(n_visible), int(width))
+    if n > 0:
+        rows = np.arange(int(kv_start), int(kv_start) + n)
+        k = mxfp4_key_decode(np.asarray(k_codes)[rows], np.asarray(k_scales)[rows])
+        out[:n] = index_score_rows(mxfp8_decode(q_codes, q_scales), np.asarray(w, np.float64), k)
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # Write side: the compressor and the indexer-key projection
 # --------------------------------------------------------------------------------------

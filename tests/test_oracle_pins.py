@@ -635,3 +635,53 @@ def test_index_key_projection_brute_force():
     oh = np.zeros((128, 512), np.float32)
     oh[np.arange(128), 4 * np.arange(128)] = 1.0
     assert np.array_equal(O.project_index_keys(ent, _bf16_bits_of(oh)), ent[:, ::4])
+
+
+# ------------------------------------------------------------------ MXFP8 indexer query
+
+def test_mxfp8_quantize_against_torch_cast():
+    """Per 32-channel group: the exponent from torch's log2, the codes from torch's E4M3
+    cast of the clamped quotient (an independent rounding); saturation and zero groups."""
+    g = torch.Generator().manual_seed(61)
+    x = (torch.randn(40, 32, 128, generator=g) * 3).to(torch.bfloat16).float()
+    x[0, 0, :32] = 0.0
+    x[1, 2, 32:64] *= 2.0 ** 40
+    x[2, 3, 64:96] *= 2.0 ** -60
+    codes, scales = O.mxfp8_quantize(x.numpy())
+    grp = x.reshape(40, 32, 4, 32)
+    amax = grp.abs().amax(-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 8 + 127, torch.full_like(amax, 127.0))
+    e = e.clamp(1, 254)
+    assert np.array_equal(scales, e.to(torch.uint8).numpy())
+    quo = (grp * torch.exp2(127 - e).unsqueeze(-1)).clamp(-448, 448)
+    want = quo.to(torch.float8_e4m3fn).view(torch.uint8).reshape(40, 32, 128).numpy()
+    # a value that rounds to zero keeps its sign in both; compare the values' bits
+    assert np.array_equal(codes, want)
+
+
+def test_mxfp8_round_trip_and_exact_query_scores():
+    rng = np.random.default_rng(62)
+    x = torch.from_numpy(rng.standard_normal((6, 32, 128)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    codes, scales = O.mxfp8_quantize(x)
+    back = O.mxfp8_decode(codes, scales)
+    step = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+    # within half an E4M3 step of each value, or the saturation gap at the top
+    assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, step * 2.0 ** -9) + 64 * step)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -4 + step * 2.0 ** -10 + (np.abs(x) > 448 * step) * 64 * step)
+    # a query already on the E4M3 grid with group maxima in [256, 448] quantises exactly
+    # (scale byte 127), so its scores equal the bf16-query scores over the same MXFP4 keys
+    q = rng.integers(0, 0x7E, size=(32, 128)).astype(np.uint8) | (rng.integers(0, 2, size=(32, 128)).astype(np.uint8) << 7)
+    q[:, ::32] = 0x7E                                  # 448 in every group
+    qv = O.e4m3_decode(q)
+    qc, qs = O.mxfp8_quantize(qv.astype(np.float32))
+    assert np.all(qs == 127) and np.array_equal(O.e4m3_decode(qc), qv)
+    n = 300
+    kc = rng.integers(0, 256, size=(n, 64)).astype(np.uint8)
+    ks = rng.integers(120, 135, size=(n, 4)).astype(np.uint8)
+    w = rng.random(32)
+    q_bits = torch.from_numpy(qv.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ref = O.full_scores_mxfp4(q_bits, w, kc, ks, 0, n - 7, n)
+    got = O.full_scores_mxfp4_q8(qc, qs, w, kc, ks, 0, n - 7, n)
+    assert np.array_equal(np.isfinite(got), np.isfinite(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-9)
