@@ -35,6 +35,8 @@ def _load():
     lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, I, P]
+    lib.csa2_quantize_mxfp8.argtypes = [I, I, P, P, P, P]
+    lib.csa2_index_score_mxfp4_q8.argtypes = [I, I, I, I, P, P, P, P, P, L, P, P, P, L, P, L, P]
     lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
     lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
@@ -49,7 +51,8 @@ def _load():
     for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
-              "csa2_compress_kv", "csa2_project_index_key"):
+              "csa2_compress_kv", "csa2_project_index_key", "csa2_quantize_mxfp8",
+              "csa2_index_score_mxfp4_q8"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -98,6 +101,35 @@ def _rows_view(t, width, name):
             or t.shape[1] < width:
         raise ValueError(f"{name}: expected a device uint8 [rows, >= {width}] view")
     return t.data_ptr(), t.stride(0)
+
+
+def csa2_quantize_mxfp8(x, codes, scales, stream=None):
+    """MXFP8 rows: x bf16 [..., 128] -> codes uint8 [..., 128] (E4M3), scales uint8 [..., 4]."""
+    n = x.numel() // 128
+    if x.shape[-1] != 128 or codes.numel() != x.numel() or scales.numel() != n * 4:
+        raise ValueError("csa2_quantize_mxfp8: x [..., 128], codes like x, scales [..., 4]")
+    _check(lib.csa2_quantize_mxfp8(n, 128, _ptr(x, torch.bfloat16, "x"),
+                                   _ptr(codes, torch.uint8, "codes"),
+                                   _ptr(scales, torch.uint8, "scales"), _stream(stream)))
+
+
+def csa2_index_score_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n_visible,
+                              scores, block_max=None, stream=None, ld_scores=None):
+    """FULL-mode scores of an MXFP8 query (q_codes [n_q, 32, 128], q_scales [n_q, 32, 4])
+    over MXFP4 keys; scores may be None when block_max is given (then ld_scores is needed)."""
+    n_q = q_codes.shape[0]
+    if scores is not None:
+        ld_scores = scores.shape[1]
+    elif ld_scores is None:
+        raise ValueError("csa2_index_score_mxfp4_q8: ld_scores is required when scores is None")
+    _check(lib.csa2_index_score_mxfp4_q8(
+        FULL, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
+        _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
+        _ptr(k_codes, torch.uint8, "k_codes"), _ptr(k_scales, torch.uint8, "k_scales"),
+        k_codes.shape[0], _ptr(kv_start, torch.int64, "kv_start"),
+        _ptr(n_visible, torch.int32, "n_visible"), _ptr(scores, torch.float32, "scores"),
+        ld_scores, _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 
 
 def csa2_compress_kv(c, z, out, m, stream=None):

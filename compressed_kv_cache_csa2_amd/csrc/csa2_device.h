@@ -134,6 +134,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// float32 -> E4M3 byte, nearest even, saturating at 448 (0x7E); sign kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {           // < 2^-6: multiples of 2^-9
+    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, then RNE
+    code = (uint32_t)m;                   // 0..8 (8 is 2^-6, the first normal code)
+  } else {
+    const uint32_t e = a >> 23;           // biased exponent, 121..135
+    const uint32_t mant = a & 0x7FFFFFu;
+    uint32_t top = mant >> 20;            // 3 kept bits
+    const uint32_t rest = mant & 0xFFFFFu;
+    top += (rest > 0x80000u || (rest == 0x80000u && (top & 1u))) ? 1u : 0u;
+    code = ((e - 120u) << 3) + top;       // a carry into the exponent is the right value
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
 // Order-preserving key: a > b as floats <=> key(a) > key(b) as unsigned.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

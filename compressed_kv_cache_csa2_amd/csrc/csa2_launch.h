@@ -57,6 +57,15 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
 
 // Cache writes: quantise bf16 rows into the cache formats (destination rows outside
 // [0, n_rows) are skipped).
+// Full-mode scores of an MXFP8 indexer query over MXFP4 keys (scaled f8f6f4 MFMA).
+hipError_t launch_index_score_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
+                                 const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                                 int64_t n_entries, const int64_t* kv_start,
+                                 const int32_t* n_visible, float* scores, int64_t ld,
+                                 float* block_max, int64_t ld_bm, hipStream_t stream);
+// MXFP8 quantisation of bf16 rows of 128 channels.
+hipError_t launch_mxfp8_quantize(int n_rows, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
 // Gated-pooling compressor: n_out entries of 512 channels from m tokens each (bf16 in/out).
 hipError_t launch_compress(int m, int n_out, const uint16_t* c, const uint16_t* z, int64_t ld_in,
                            uint16_t* out, int64_t ld_out, hipStream_t stream);

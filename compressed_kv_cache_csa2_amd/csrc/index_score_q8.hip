@@ -1,0 +1,194 @@
+// Lightning-indexer score with an MXFP8 query over MXFP4 keys, on gfx950's scaled
+// f8f6f4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// The pages' V4 lineage runs the indexer in low precision ("DeepSeek-v4.1 Flash: Pushing
+// the Limits of KV Cache Compression", 2.4.4 and 3.1: FP4 indexer keys in OCP MXFP4). Here
+// the query is quantised too, to OCP MXFP8 (E4M3 elements, one E8M0 scale per 32
+// channels), so both operands go to the matrix core as they are stored and the hardware
+// applies both scales: no conversion instructions in the stream, two MFMAs per 32
+// positions instead of eight. Every product (E4M3 x E2M1 x two powers of two) is exact in
+// fp32; only the accumulation rounds.
+//
+// Operand layout of the 32x32x64 scaled MFMA on gfx950 (established with an in-bounds lane
+// probe): for lane l, row/column l % 32 and half h = l / 32,
+//   A (fp8, 32 bytes): byte j < 16 holds k = 16h + j, byte j >= 16 holds k = 32 + 16h + j - 16;
+//   B (fp4, 16 bytes, low nibble first): nibble q holds k = 32h + q;
+//   the A and B scale bytes of lane l cover k-block h (k = 32h .. 32h + 31) of its row or
+//   column; D as in the bf16 32x32 products (row 8(r/4) + 4h + r%4, column l % 32).
+// For MFMA i (channels 64i .. 64i+63) a key lane (position n, half h) therefore holds code
+// bytes 32i + 16h .. +15 of its row (channels 64i + 32h .. +31, one 16-byte load) with
+// scale byte 2i + h, and a query lane (head m, half h) holds E4M3 bytes 64i + 16h .. +15
+// and 64i + 32 + 16h .. +15 of its head with the head's scale byte 2i + h.
+#include "csa2_device.h"
+#include "csa2_launch.h"
+
+namespace csa2 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int Q8_THREADS = 256;
+constexpr int Q8_STEPS = 16;   // 32-position steps per wavefront: 2,048 slots per workgroup
+
+__global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_codes,
+    const uint8_t* __restrict__ k_scales, int64_t n_entries, const int64_t* __restrict__ kv_start,
+    const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
+    float* __restrict__ block_max, int64_t ld_bm) {
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int half = lane >> 5;
+
+  // A operands (head n) and their scale bytes for the two MFMAs.
+  i32x8 a[2];
+  uint32_t sa[2];
+  {
+    const uint8_t* qrow = q_codes + ((int64_t)t * 32 + n) * 128;
+    const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_scales + ((int64_t)t * 32 + n) * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow + 64 * i + 16 * half);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 64 * i + 32 + 16 * half);
+      a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa[i] = (qs >> (8 * (2 * i + half))) & 0xFFu;
+    }
+  }
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+
+  const int64_t base = kv_start[t];
+  const int64_t nv = n_visible[t];
+  constexpr int TILE = (Q8_THREADS / 64) * Q8_STEPS * 32;
+  const int64_t tile0 = (int64_t)blockIdx.x * TILE + (int64_t)wave * 32;
+  auto slot_at = [&](int step) -> int64_t {
+    return tile0 + (int64_t)step * (Q8_THREADS / 64) * 32 + n;
+  };
+  auto row_at = [&](int step) -> int64_t {
+    const int64_t slot = slot_at(step);
+    if (slot >= ld || slot >= nv) return -1;
+    const int64_t row = base + slot;
+    return (row >= 0 && row < n_entries) ? row : -1;
+  };
+  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  // Per step and lane: code bytes 16h .. +15 and 32 + 16h .. +15 of its row, scale word.
+  u32x4 kb[2][2];
+  uint32_t ks[2];
+  auto load_step = [&](int step, int b) {
+    const int64_t r = row_at(step);
+    const int64_t rr = r >= 0 ? r : base;
+    const uint8_t* row = k_codes + rr * 64;
+    kb[b][0] = *reinterpret_cast<const u32x4*>(row + 16 * half);
+    kb[b][1] = *reinterpret_cast<const u32x4*>(row + 32 + 16 * half);
+    ks[b] = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
+  };
+  float sc[Q8_STEPS];
+  if (any) load_step(0, 0);
+#pragma unroll
+  for (int step = 0; step < Q8_STEPS; ++step) {
+    float sv = -__builtin_inff();
+    if (any) {
+      const int b = step & 1;
+      if (step + 1 < Q8_STEPS) load_step(step + 1, b ^ 1);
+      f32x16 acc = {};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 c = kb[b][i];
+        const i32x8 bv = i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const uint32_t sb = (ks[b] >> (8 * (2 * i + half))) & 0xFFu;
+        // A format 0 (fp8 E4M3), B format 4 (fp4 E2M1)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc, 0, 4, 0, (int)sa[i],
+                                                              0, (int)sb);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+      part += __shfl_xor(part, 32);
+      if (row_at(step) >= 0) sv = part;
+    }
+    sc[step] = sv;
+  }
+#pragma unroll
+  for (int step = 0; step < Q8_STEPS; ++step) {
+    const int64_t slot = slot_at(step);
+    const float sv = sc[step];
+    if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+    if (block_max != nullptr) {
+      float m = sv;
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      if (half == 0 && (n & 7) == 0 && slot < ld) block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
+    }
+  }
+}
+
+// MXFP8 quantisation of bf16 rows of 128 channels (the OCP microscaling recipe): per 32
+// channels the exponent X = floor(log2 amax) - 8 (8 = E4M3's largest exponent), stored
+// as X + 127 kept in 1..254 (127 for an all-zero group), codes E4M3(x * 2^-X), nearest
+// even, saturating at 448. 16 lanes per row, lane c channels 8c .. 8c+7.
+__global__ __launch_bounds__(Q8_THREADS) void mxfp8_quantize_kernel(
+    int n_rows, const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t gid = (int64_t)blockIdx.x * Q8_THREADS + threadIdx.x;
+  const int64_t r = gid >> 4;
+  const int c = (int)(gid & 15);
+  // Every lane takes part in the shuffles; rows past n_rows only skip the stores.
+  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (r < n_rows) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + r * 128 + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int code_s = 127;
+  if (amax > 0.f) {
+    int e;
+    (void)frexpf(amax, &e);                 // amax = m * 2^e, m in [0.5, 1)
+    code_s = e - 1 - 8 + 127;
+    code_s = code_s < 1 ? 1 : (code_s > 254 ? 254 : code_s);
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= f32_to_e4m3_rne(ldexpf(f[i], 127 - code_s)) << (8 * i);
+    hi |= f32_to_e4m3_rne(ldexpf(f[4 + i], 127 - code_s)) << (8 * i);
+  }
+  if (r >= n_rows) return;
+  *reinterpret_cast<u32x2*>(codes + r * 128 + 8 * c) = u32x2{lo, hi};
+  if ((c & 3) == 0) scales[r * 4 + (c >> 2)] = (uint8_t)code_s;
+}
+
+hipError_t launch_index_score_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
+                                 const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                                 int64_t n_entries, const int64_t* kv_start,
+                                 const int32_t* n_visible, float* scores, int64_t ld,
+                                 float* block_max, int64_t ld_bm, hipStream_t stream) {
+  constexpr int tile = (Q8_THREADS / 64) * Q8_STEPS * 32;
+  dim3 grid((unsigned)((ld + tile - 1) / tile), (unsigned)n_q);
+  hipLaunchKernelGGL(index_score_q8_kernel, grid, dim3(Q8_THREADS), 0, stream, q_codes, q_scales,
+                     w, k_codes, k_scales, n_entries, kv_start, n_visible, scores, ld, block_max,
+                     ld_bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_quantize(int n_rows, const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  const int64_t threads = (int64_t)n_rows * 16;
+  hipLaunchKernelGGL(mxfp8_quantize_kernel,
+                     dim3((unsigned)((threads + Q8_THREADS - 1) / Q8_THREADS)), dim3(Q8_THREADS),
+                     0, stream, n_rows, x, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -24,6 +24,7 @@ def test_header_symbols_are_exported(C):
                      "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
                      "csa2_index_score_shared", "csa2_index_score_bf16",
                      "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
+                     "csa2_quantize_mxfp8", "csa2_index_score_mxfp4_q8",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
@@ -146,6 +147,27 @@ def test_compressor_and_projection_rejections(C):
     assert L.csa2_project_index_key(4, 512, 128, FAKE + 8, 512, FAKE, FAKE, 128, None) == 1
     assert b"csa2_project_index_key" in L.csa2_last_error()
     assert L.csa2_project_index_key(0, 512, 128, None, 0, None, None, 0, None) == 0
+
+
+def test_mxfp8_query_rejections(C):
+    L = C.lib
+    assert L.csa2_quantize_mxfp8(4, 64, FAKE, FAKE, FAKE, None) == 2
+    assert L.csa2_quantize_mxfp8(4, 128, None, FAKE, FAKE, None) == 1
+    assert L.csa2_quantize_mxfp8(4, 128, FAKE + 8, FAKE, FAKE, None) == 1
+    assert L.csa2_quantize_mxfp8(0, 128, None, None, None, None) == 0
+    def call(**kw):
+        a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_codes=FAKE, q_scales=FAKE, w=FAKE,
+                 k_codes=FAKE, k_scales=FAKE, n_entries=10, kv_start=FAKE, n_visible=FAKE,
+                 scores=FAKE, ld=16, block_max=None, ld_bm=0, stream=None)
+        a.update(kw)
+        return L.csa2_index_score_mxfp4_q8(*a.values())
+    assert call(mode=1) == 2 and b"only FULL" in L.csa2_last_error()
+    assert call(n_heads=16) == 2
+    assert call(q_scales=None) == 1
+    assert call(q_codes=FAKE + 8) == 1
+    assert call(scores=None) == 1
+    assert call(block_max=FAKE, ld_bm=1) == 1
+    assert call(n_q=0, q_codes=None) == 0
 
 
 def test_cache_write_rejections(C):

@@ -1,0 +1,73 @@
+"""MXFP8 indexer query over MXFP4 keys on the scaled f8f6f4 MFMA, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.csa2_oracle as O
+from tests.parity_util import assert_scores_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def C(dev):
+    from compressed_kv_cache_csa2_amd import csa2
+    return csa2
+
+
+def test_quantize_mxfp8_exact(C, dev):
+    g = torch.Generator().manual_seed(71)
+    x = (torch.randn(9, 32, 128, generator=g) * 2).to(torch.bfloat16)
+    x[0, 0, :32] = 0.0
+    x[1, 5, 32:64] = x[1, 5, 32:64] * 2.0 ** 50
+    x[2, 7, 64:96] = x[2, 7, 64:96] * 2.0 ** -70
+    x[3, 9, 96:] = -x[3, 9, 96:].abs()
+    codes = torch.full((9, 32, 128), 0x5A, dtype=torch.uint8, device=dev)
+    scales = torch.full((9, 32, 4), 0x5A, dtype=torch.uint8, device=dev)
+    C.csa2_quantize_mxfp8(x.to(dev), codes, scales)
+    torch.cuda.synchronize()
+    wc, ws = O.mxfp8_quantize(x.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), wc)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+
+
+def _abs_terms(qc, qs, w, kc, ks):
+    qa = np.abs(O.mxfp8_decode(qc, qs))
+    ka = np.abs(O.mxfp4_key_decode(kc, ks))
+    return (ka @ qa.T) @ np.abs(np.asarray(w, np.float64))
+
+
+@pytest.mark.parametrize("with_scores", [True, False])
+def test_index_score_mxfp4_q8_parity(C, dev, with_scores):
+    from compressed_kv_cache_csa2_amd import synth
+    nvis = [5000, 33, 2049, 0]
+    wl = synth.make_decode("q8", 4, 0, ("full",), False, 8, n_visible=nvis, kv_gap=5, seed=72,
+                           mxfp4=True).to(dev)
+    lay = wl.layers[0]
+    qc = torch.empty((4, 32, 128), dtype=torch.uint8, device=dev)
+    qs = torch.empty((4, 32, 4), dtype=torch.uint8, device=dev)
+    C.csa2_quantize_mxfp8(lay.q_idx, qc, qs)
+    ld = 5024
+    scores = torch.full((4, ld), 3.0, dtype=torch.float32, device=dev) if with_scores else None
+    bmax = torch.full((4, ld // 8), 3.0, dtype=torch.float32, device=dev)
+    C.csa2_index_score_mxfp4_q8(qc, qs, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                                wl.n_visible, scores, bmax, ld_scores=ld)
+    torch.cuda.synchronize()
+    kc_all, ks_all = wl.k_codes.cpu().numpy(), wl.k_scales.cpu().numpy()
+    qcn, qsn, w = qc.cpu().numpy(), qs.cpu().numpy(), lay.w.cpu().numpy()
+    bm = bmax.cpu().numpy()
+    for t, nv in enumerate(nvis):
+        start = int(wl.kv_start[t])
+        ref = O.full_scores_mxfp4_q8(qcn[t], qsn[t], w[t], kc_all, ks_all, start, nv, ld)
+        terms = np.zeros(ld)
+        if nv > 0:
+            terms[:nv] = _abs_terms(qcn[t], qsn[t], w[t], kc_all[start:start + nv],
+                                    ks_all[start:start + nv])
+        if with_scores:
+            assert_scores_close(scores[t].cpu().numpy(), ref, terms, f"q8 scores q{t}")
+        # block maxima: within the same bound of the oracle's block maxima
+        refb = ref.reshape(-1, 8).max(axis=1)
+        tb = terms.reshape(-1, 8).max(axis=1)
+        fin = np.isfinite(refb)
+        assert np.array_equal(np.isfinite(bm[t]), fin), t
+        assert np.all(np.abs(bm[t][fin] - refb[fin]) <= 1e-5 * tb[fin] + 1e-30), t
