@@ -417,6 +417,24 @@ def full_scores_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n_vi
     return out
 
 
+def reindex_scores_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n_visible,
+                            pool_blocks, block_size: int = 8) -> np.ndarray:
+    """reindex_scores with an MXFP8 query over MXFP4 keys (reading R24): slot s of the pool
+    scores position 8 * pool[s / 8] + s % 8 with the decoded query; absent slots -inf."""
+    pool_blocks = np.asarray(pool_blocks, dtype=np.int64)
+    n_slots = pool_blocks.shape[0] * block_size
+    out = np.full(n_slots, NEG_INF)
+    slot = np.arange(n_slots)
+    block = pool_blocks[slot // block_size]
+    pos = block * block_size + slot % block_size
+    ok = (block >= 0) & (pos < n_visible)
+    if ok.any():
+        r = kv_start + pos[ok]
+        rows = mxfp4_key_decode(np.asarray(k_codes)[r], np.asarray(k_scales)[r])
+        out[ok] = index_score_rows(mxfp8_decode(q_codes, q_scales), np.asarray(w, np.float64), rows)
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # Write side: the compressor and the indexer-key projection
 # --------------------------------------------------------------------------------------

@@ -685,3 +685,23 @@ def test_mxfp8_round_trip_and_exact_query_scores():
     assert np.array_equal(np.isfinite(got), np.isfinite(ref))
     fin = np.isfinite(ref)
     assert np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-9)
+
+
+def test_reindex_q8_over_every_block_equals_full_q8():
+    """A pool holding every block (in order) rescored with the MXFP8 query reproduces the
+    Full-mode MXFP8 scores slot for slot; absent and out-of-range blocks score -inf."""
+    rng = np.random.default_rng(63)
+    n = 203
+    kc = rng.integers(0, 256, size=(n + 5, 64)).astype(np.uint8)
+    ks = rng.integers(118, 136, size=(n + 5, 4)).astype(np.uint8)
+    q = torch.from_numpy(rng.standard_normal((32, 128)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    qc, qs = O.mxfp8_quantize(q)
+    w = rng.random(32)
+    nb = -(-n // 8)
+    full = O.full_scores_mxfp4_q8(qc, qs, w, kc, ks, 5, n, nb * 8)
+    pool = np.arange(nb)
+    re = O.reindex_scores_mxfp4_q8(qc, qs, w, kc, ks, 5, n, pool)
+    assert np.array_equal(re, full)
+    pool2 = np.array([3, -1, nb + 4])
+    re2 = O.reindex_scores_mxfp4_q8(qc, qs, w, kc, ks, 5, n, pool2)
+    assert np.array_equal(re2[:8], full[24:32]) and np.all(np.isneginf(re2[8:]))
