@@ -89,7 +89,7 @@ def full_indexer(wl, buf, C, stream=None):
     from compressed_kv_cache_csa2_amd import layers
     lay = next(l for l in wl.layers if l.mode == "full")
     layers.index_score(wl, C.FULL, lay, None if wl.with_pool else buf.scores,
-                       buf.block_max, ld_scores=buf.scores.shape[1], stream=stream)
+                       buf.block_max, ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
 
 
 def rotated_copies(wl):
@@ -406,7 +406,7 @@ def main():
                                               stream=stream)
                         elif part == "rescore":
                             layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                               pool_blocks=buf.pool, stream=stream)
+                                               pool_blocks=buf.pool, stream=stream, buf=buf)
                         else:
                             C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
                                         stream=stream)
@@ -414,10 +414,10 @@ def main():
                         full_indexer(wl, buf, C, stream=stream)
                     elif part == "rescore" and lay.mode == "full" and wl.with_pool:
                         layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                           pool_blocks=buf.pool, stream=stream)
+                                           pool_blocks=buf.pool, stream=stream, buf=buf)
                     elif part == "score" and lay.mode == "reindex":
                         layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                           pool_blocks=buf.pool, stream=stream)
+                                           pool_blocks=buf.pool, stream=stream, buf=buf)
                     elif part == "topk" and lay.mode == "full" and wl.with_pool:
                         C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
                                     stream=stream)
@@ -467,6 +467,7 @@ def main():
                    "layers": [l.mode for l in wl.layers], "index_topk": 512,
                    "sliding_window": 128, "pool_blocks": 2048 if wl.with_pool else 0,
                    "indexer_keys": "mxfp4" if wl.k_codes is not None else "e4m3",
+                   "indexer_query": "mxfp8" if wl.q8 else "bf16",
                    "coarse_filter": args.coarse, "rotated_copies": len(copies),
                    "launch": "eager" if args.no_graph else "hip_graph"},
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -476,7 +477,9 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": None if hisa else measured_traffic(wl.name),
                      "kernel": "index_score_kernel (block-mean scorer, bf16 mean keys)" if hisa
-                               else ("index_score_full_wide_fp4_kernel (Full-layer indexer, "
+                               else ("index_score_q8_kernel (Full-layer indexer, MXFP4 keys, "
+                                     "MXFP8 query" if wl.q8 else
+                                     "index_score_full_wide_fp4_kernel (Full-layer indexer, "
                                      "MXFP4 keys" if wl.k_codes is not None else
                                      "index_score_kernel (Full-layer indexer, E4M3 keys")
                                + (", block maxima only)" if wl.with_pool else ")"),

@@ -36,7 +36,8 @@ def _load():
     lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, I, P]
     lib.csa2_quantize_mxfp8.argtypes = [I, I, P, P, P, P]
-    lib.csa2_index_score_mxfp4_q8.argtypes = [I, I, I, I, P, P, P, P, P, L, P, P, P, L, P, L, P]
+    lib.csa2_index_score_mxfp4_q8.argtypes = [I, I, I, I, P, P, P, P, P, L, P, P, P, I, I, P, L, P,
+                                              L, P]
     lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
     lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
@@ -113,21 +114,25 @@ def csa2_quantize_mxfp8(x, codes, scales, stream=None):
                                    _ptr(scales, torch.uint8, "scales"), _stream(stream)))
 
 
-def csa2_index_score_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n_visible,
-                              scores, block_max=None, stream=None, ld_scores=None):
-    """FULL-mode scores of an MXFP8 query (q_codes [n_q, 32, 128], q_scales [n_q, 32, 4])
-    over MXFP4 keys; scores may be None when block_max is given (then ld_scores is needed)."""
+def csa2_index_score_mxfp4_q8(mode, q_codes, q_scales, w, k_codes, k_scales, kv_start, n_visible,
+                              scores, block_max=None, pool_blocks=None, stream=None,
+                              ld_scores=None):
+    """Scores of an MXFP8 query (q_codes [n_q, 32, 128], q_scales [n_q, 32, 4]) over MXFP4
+    keys, FULL or REINDEX (over pool_blocks); FULL scores may be None when block_max is
+    given (then ld_scores is needed)."""
     n_q = q_codes.shape[0]
+    n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
     if scores is not None:
         ld_scores = scores.shape[1]
     elif ld_scores is None:
         raise ValueError("csa2_index_score_mxfp4_q8: ld_scores is required when scores is None")
     _check(lib.csa2_index_score_mxfp4_q8(
-        FULL, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
+        mode, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
         _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
         _ptr(k_codes, torch.uint8, "k_codes"), _ptr(k_scales, torch.uint8, "k_scales"),
         k_codes.shape[0], _ptr(kv_start, torch.int64, "kv_start"),
-        _ptr(n_visible, torch.int32, "n_visible"), _ptr(scores, torch.float32, "scores"),
+        _ptr(n_visible, torch.int32, "n_visible"), _ptr(pool_blocks, torch.int32, "pool_blocks"),
+        n_pool, 8, _ptr(scores, torch.float32, "scores"),
         ld_scores, _ptr(block_max, torch.float32, "block_max"),
         block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 

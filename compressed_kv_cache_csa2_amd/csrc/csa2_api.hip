@@ -229,11 +229,16 @@ int csa2_quantize_mxfp8(int n_rows, int d, const void* x, void* codes, void* sca
 int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                               const void* q_codes, const void* q_scales, const float* w,
                               const void* k_codes, const void* k_scales, int64_t n_entries,
-                              const int64_t* kv_start, const int32_t* n_visible, float* scores,
-                              int64_t ld_scores, float* block_max, int64_t ld_block_max,
-                              void* stream) {
+                              const int64_t* kv_start, const int32_t* n_visible,
+                              const int32_t* pool_blocks, int n_pool, int block_size,
+                              float* scores, int64_t ld_scores, float* block_max,
+                              int64_t ld_block_max, void* stream) {
   const char* fn = "csa2_index_score_mxfp4_q8";
-  REQUIRE(mode == CSA2_FULL, CSA2_ERR_UNSUPPORTED, "%s: only FULL mode is built", fn);
+  REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
+          "%s: mode %d does no scoring (Reuse layers attend with published indices)", fn,
+          (int)mode);
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
   REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
           "%s: indexer shape %dx%d, only %dx%d is built", fn, n_heads, d_idx, CSA2_IDX_HEADS,
           CSA2_IDX_DIM);
@@ -241,13 +246,23 @@ int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
   if (n_q == 0) return ok();
   REQUIRE(q_codes && q_scales && w && k_codes && k_scales && kv_start && n_visible,
           CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
-  REQUIRE(scores != nullptr || block_max != nullptr, CSA2_ERR_INVALID_ARG,
-          "%s: scores may be NULL only with block_max", fn);
+  REQUIRE(scores != nullptr || (mode == CSA2_FULL && block_max != nullptr), CSA2_ERR_INVALID_ARG,
+          "%s: scores may be NULL only in FULL mode with block_max", fn);
   REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "%s: n_entries < 0", fn);
   REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
           "%s: ld_scores %lld out of range", fn, (long long)ld_scores);
   REQUIRE(aligned(q_codes, 16) && aligned(k_codes, 16), CSA2_ERR_INVALID_ARG,
           "%s: q_codes and k_codes must be 16-byte aligned", fn);
+  if (mode == CSA2_REINDEX) {
+    REQUIRE(pool_blocks != nullptr, CSA2_ERR_INVALID_ARG, "%s: REINDEX needs pool_blocks", fn);
+    REQUIRE(n_pool >= 1 && n_pool <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+            "%s: n_pool %d out of range", fn, n_pool);
+    REQUIRE(ld_scores >= (int64_t)n_pool * block_size, CSA2_ERR_INVALID_ARG,
+            "%s: ld_scores %lld < n_pool*block_size", fn, (long long)ld_scores);
+    REQUIRE(aligned(pool_blocks, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned pool_blocks", fn);
+  } else {
+    REQUIRE(pool_blocks == nullptr, CSA2_ERR_INVALID_ARG, "%s: FULL takes no pool_blocks", fn);
+  }
   REQUIRE(aligned(q_scales, 4) && aligned(k_scales, 4) && aligned(w, 4) && aligned(scores, 4) &&
               aligned(kv_start, 8) && aligned(n_visible, 4),
           CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
@@ -257,11 +272,12 @@ int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
     REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
   }
   return hip_status(csa2::launch_index_score_q8(
-                        n_q, static_cast<const uint8_t*>(q_codes),
+                        mode == CSA2_REINDEX, n_q, static_cast<const uint8_t*>(q_codes),
                         static_cast<const uint8_t*>(q_scales), w,
                         static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(k_scales),
-                        n_entries, kv_start, n_visible, scores, ld_scores, block_max, ld_block_max,
-                        static_cast<hipStream_t>(stream)),
+                        n_entries, kv_start, n_visible, pool_blocks,
+                        mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
+                        ld_block_max, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

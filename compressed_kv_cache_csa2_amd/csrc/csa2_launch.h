@@ -57,12 +57,14 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
 
 // Cache writes: quantise bf16 rows into the cache formats (destination rows outside
 // [0, n_rows) are skipped).
-// Full-mode scores of an MXFP8 indexer query over MXFP4 keys (scaled f8f6f4 MFMA).
-hipError_t launch_index_score_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
-                                 const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
-                                 int64_t n_entries, const int64_t* kv_start,
-                                 const int32_t* n_visible, float* scores, int64_t ld,
-                                 float* block_max, int64_t ld_bm, hipStream_t stream);
+// Full or Reindex scores of an MXFP8 indexer query over MXFP4 keys (scaled f8f6f4 MFMA).
+hipError_t launch_index_score_q8(bool reindex, int n_q, const uint8_t* q_codes,
+                                 const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                                 const uint8_t* k_scales, int64_t n_entries,
+                                 const int64_t* kv_start, const int32_t* n_visible,
+                                 const int32_t* pool_blocks, int n_pool, float* scores,
+                                 int64_t ld, float* block_max, int64_t ld_bm,
+                                 hipStream_t stream);
 // MXFP8 quantisation of bf16 rows of 128 channels.
 hipError_t launch_mxfp8_quantize(int n_rows, const uint16_t* x, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);

@@ -27,14 +27,19 @@ namespace csa2 {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int Q8_THREADS = 256;
-constexpr int Q8_STEPS = 16;   // 32-position steps per wavefront: 2,048 slots per workgroup
+// 32-position steps per wavefront: 2,048 slots per Full workgroup, 512 per Reindex one (the
+// pool is 16,384 slots per query, so smaller tiles keep every CU busy)
+constexpr int Q8_STEPS_FULL = 16;
+constexpr int Q8_STEPS_REINDEX = 4;
 
+template <bool REINDEX>
 __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, const uint8_t* __restrict__ k_codes,
     const uint8_t* __restrict__ k_scales, int64_t n_entries, const int64_t* __restrict__ kv_start,
-    const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
-    float* __restrict__ block_max, int64_t ld_bm) {
+    const int32_t* __restrict__ n_visible, const int32_t* __restrict__ pool_blocks, int n_pool,
+    float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
+  constexpr int Q8_STEPS = REINDEX ? Q8_STEPS_REINDEX : Q8_STEPS_FULL;
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -67,12 +72,26 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
   auto slot_at = [&](int step) -> int64_t {
     return tile0 + (int64_t)step * (Q8_THREADS / 64) * 32 + n;
   };
-  auto row_at = [&](int step) -> int64_t {
+  // The cache row of this lane's slot in a step, -1 when absent; Reindex slots map
+  // through the pool (slot s is position 8 * pool[s / 8] + s % 8).
+  auto row_of = [&](int step) -> int64_t {
     const int64_t slot = slot_at(step);
-    if (slot >= ld || slot >= nv) return -1;
-    const int64_t row = base + slot;
+    if (slot >= ld) return -1;
+    int64_t pos = slot;
+    if (REINDEX) {
+      const int64_t pb = slot >> 3;
+      const int b = pb < n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
+      if (b < 0) return -1;
+      pos = (int64_t)b * 8 + (slot & 7);
+    }
+    if (pos >= nv) return -1;
+    const int64_t row = base + pos;
     return (row >= 0 && row < n_entries) ? row : -1;
   };
+  int64_t rows[Q8_STEPS];
+#pragma unroll
+  for (int st = 0; st < Q8_STEPS; ++st) rows[st] = row_of(st);
+  auto row_at = [&](int step) -> int64_t { return rows[step]; };
   const bool any = nv > 0 && base >= 0 && base < n_entries;
   // Per step and lane: code bytes 16h .. +15 and 32 + 16h .. +15 of its row, scale word.
   u32x4 kb[2][2];
@@ -169,16 +188,21 @@ __global__ __launch_bounds__(Q8_THREADS) void mxfp8_quantize_kernel(
   if ((c & 3) == 0) scales[r * 4 + (c >> 2)] = (uint8_t)code_s;
 }
 
-hipError_t launch_index_score_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
-                                 const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
-                                 int64_t n_entries, const int64_t* kv_start,
-                                 const int32_t* n_visible, float* scores, int64_t ld,
-                                 float* block_max, int64_t ld_bm, hipStream_t stream) {
-  constexpr int tile = (Q8_THREADS / 64) * Q8_STEPS * 32;
+hipError_t launch_index_score_q8(bool reindex, int n_q, const uint8_t* q_codes,
+                                 const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                                 const uint8_t* k_scales, int64_t n_entries,
+                                 const int64_t* kv_start, const int32_t* n_visible,
+                                 const int32_t* pool_blocks, int n_pool, float* scores,
+                                 int64_t ld, float* block_max, int64_t ld_bm,
+                                 hipStream_t stream) {
+  const int tile = (Q8_THREADS / 64) * (reindex ? Q8_STEPS_REINDEX : Q8_STEPS_FULL) * 32;
   dim3 grid((unsigned)((ld + tile - 1) / tile), (unsigned)n_q);
-  hipLaunchKernelGGL(index_score_q8_kernel, grid, dim3(Q8_THREADS), 0, stream, q_codes, q_scales,
-                     w, k_codes, k_scales, n_entries, kv_start, n_visible, scores, ld, block_max,
-                     ld_bm);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(Q8_THREADS), 0, stream, q_codes, q_scales, w, k_codes,
+                       k_scales, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
+                       block_max, ld_bm);
+  };
+  reindex ? go(index_score_q8_kernel<true>) : go(index_score_q8_kernel<false>);
   return hipGetLastError();
 }
 

@@ -37,6 +37,8 @@ class Buffers:
     lse: torch.Tensor           # f32 [n_layers, n_q, 64]
     workspace: torch.Tensor | None
     published: list             # per layer: the index tensor it attended with
+    q8_codes: torch.Tensor | None = None    # u8 [n_q, 32, 128] the layer's MXFP8 query
+    q8_scales: torch.Tensor | None = None   # u8 [n_q, 32, 4]
 
 
 @dataclass
@@ -77,15 +79,22 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
         lse=torch.empty((n_l, n_q, 64), dtype=torch.float32, device=dev),
         workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None,
         published=[None] * n_l,
+        q8_codes=torch.empty((n_q, 32, 128), dtype=torch.uint8, device=dev) if wl.q8 else None,
+        q8_scales=torch.empty((n_q, 32, 4), dtype=torch.uint8, device=dev) if wl.q8 else None,
     )
 
 
 def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
-                stream=None):
-    """The indexer over the layer group's keys: MXFP4 when the workload carries them, else
-    E4M3; a Full pass of queries sharing one sequence scores them in groups per cache
-    tile."""
+                stream=None, buf=None):
+    """The indexer over the layer group's keys: MXFP4 when the workload carries them (with
+    the layer's query in MXFP8, already quantised into buf, when wl.q8), else E4M3; a Full
+    pass of queries sharing one sequence scores them in groups per cache tile."""
     k_cache = wl.cache(lay.group)[0]
+    if wl.q8:
+        C.csa2_index_score_mxfp4_q8(mode, buf.q8_codes, buf.q8_scales, lay.w, wl.k_codes,
+                                    wl.k_scales, wl.kv_start, wl.n_visible, scores, block_max,
+                                    pool_blocks=pool_blocks, stream=stream, ld_scores=ld_scores)
+        return
     if (mode == C.FULL and wl.k_codes is None and wl.shared_start is not None
             and scores is not None):
         C.csa2_index_score_shared(lay.q_idx, lay.w, k_cache, wl.shared_start, wl.n_visible,
@@ -122,6 +131,8 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
         raise ValueError(f"unknown coarse filter {coarse!r}")
     if coarse == "hisa" and (means is None or not wl.with_pool):
         raise ValueError("coarse='hisa' needs a pooled decoder workload and its block means")
+    if wl.q8 and (wl.k_codes is None or coarse != "hsi"):
+        raise ValueError("the MXFP8 query scores MXFP4 keys through the HSI pool only")
     current = None
     current_group = 0
     for li, lay in enumerate(wl.layers):
@@ -134,6 +145,8 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
             continue
         if lay.mode in ("full", "reindex"):
             current_group = lay.group
+            if wl.q8:
+                C.csa2_quantize_mxfp8(lay.q_idx, buf.q8_codes, buf.q8_scales, stream=stream)
         elif lay.group != current_group:
             raise ValueError("a Reuse layer must read the cache set of the layer whose "
                              "indices it reuses")
@@ -147,19 +160,20 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
                 # the pool's slots, rescored with this layer's own indexer query (the same
                 # scores, bit for bit, at 2 MiB of reads per query).
                 index_score(wl, C.FULL, lay, None, buf.block_max,
-                            ld_scores=buf.scores.shape[1], stream=stream)
+                            ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
                 C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, n_keep=POOL_BLOCKS,
                                   stream=stream)
                 index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool,
-                            stream=stream)
+                            stream=stream, buf=buf)
                 C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
             else:
-                index_score(wl, C.FULL, lay, buf.scores, buf.block_max, stream=stream)
+                index_score(wl, C.FULL, lay, buf.scores, buf.block_max, stream=stream, buf=buf)
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,
                             block_max=buf.block_max, stream=stream)
             current = buf.idx[li]
         elif lay.mode == "reindex":
-            index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool, stream=stream)
+            index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool, stream=stream,
+                        buf=buf)
             C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
             current = buf.idx[li]
         elif lay.mode != "reuse":

@@ -79,6 +79,8 @@ class Workload:
     shared_start: int | None = None
     # cache sets of groups 1, 2, ... as (k_cache, kv_fp4, kv_scale); group 0 is the above
     group_caches: list = field(default_factory=list)
+    # score the MXFP4 keys with the indexer query quantised to MXFP8 (scaled MFMA path)
+    q8: bool = False
 
     def cache(self, group: int = 0):
         """(k_cache, kv_fp4, kv_scale) of a layer group."""
@@ -102,7 +104,8 @@ class Workload:
                         with_pool=self.with_pool, planted=self.planted,
                         softmax_scale=self.softmax_scale, k_codes=mv(self.k_codes),
                         k_scales=mv(self.k_scales), shared_start=self.shared_start,
-                        group_caches=[tuple(mv(x) for x in c) for c in self.group_caches])
+                        group_caches=[tuple(mv(x) for x in c) for c in self.group_caches],
+                        q8=self.q8)
 
 
 # ----------------------------------------------------------------------------- encoders
@@ -358,7 +361,12 @@ def make_encoder(name="encoder_128k_m2", n_q=4096, n_entries=131072, ratio=2,
 def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
     """One of the named workloads; n_q (optional) keeps only the first n_q queries. A
     decode workload name with the suffix "_mxfp4" also carries MXFP4 indexer keys, which
-    its indexer passes then read instead of the E4M3 ones."""
+    its indexer passes then read instead of the E4M3 ones; with the suffix "_mxfp4_q8" those
+    passes also quantise the indexer query to MXFP8."""
+    if name.endswith("_mxfp4_q8"):
+        wl = make_workload(name[:-3], device=device, seed=seed, n_q=n_q)
+        wl.name, wl.q8 = name, True
+        return wl
     if name.endswith("_mxfp4") and name[:-6] in ("tiny_decode_4k", "decode_32k", "decode_256k",
                                                  "decode_1m"):
         base = name[:-6]

@@ -163,21 +163,22 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
  *       [n_rows, d/32] E8M0: per 32 channels X = floor(log2 amax) - 8, scale byte X + 127
  *       kept in 1..254 (127 for an all-zero group), code = E4M3(x * 2^-X), nearest even,
  *       saturating at 448. d must be 128; x and codes 16-byte aligned, scales 4-byte.
- *   csa2_index_score_mxfp4_q8: FULL mode only. As csa2_index_score_mxfp4 (same slots,
- *       -inf rules, block maxima, nullable scores) with the query given as q_codes
+ *   csa2_index_score_mxfp4_q8: as csa2_index_score_mxfp4 (FULL and REINDEX modes, same
+ *       slots, pool mapping, -inf rules, block maxima, nullable FULL scores) with the query
+ *       given as q_codes
  *       [n_q, 32, 128] E4M3 and q_scales [n_q, 32, 4] E8M0 (query value of head h, channel
  *       c = E4M3(q_codes[t,h,c]) * 2^(q_scales[t,h,c/32] - 127)). Products are exact; the
  *       accumulation is the matrix core's fp32 (not bit-identical to the bf16 path).
- * Errors: CSA2_ERR_INVALID_ARG (null pointer, bad size or alignment), CSA2_ERR_UNSUPPORTED
- * (REINDEX mode, shape). */
+ * Errors: as csa2_index_score_mxfp4. */
 int csa2_quantize_mxfp8(int n_rows, int d, const void* x, void* codes, void* scales,
                         void* stream);
 int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                               const void* q_codes, const void* q_scales, const float* w,
                               const void* k_codes, const void* k_scales, int64_t n_entries,
-                              const int64_t* kv_start, const int32_t* n_visible, float* scores,
-                              int64_t ld_scores, float* block_max, int64_t ld_block_max,
-                              void* stream);
+                              const int64_t* kv_start, const int32_t* n_visible,
+                              const int32_t* pool_blocks, int n_pool, int block_size,
+                              float* scores, int64_t ld_scores, float* block_max,
+                              int64_t ld_block_max, void* stream);
 
 /* The compressor: main-KV entries from the per-token projections of the hidden state
  * ([V41F-ARCH] 1: the KV content C = H W_KV and the compression weights Z = H W_Z;

@@ -95,10 +95,15 @@ def check_query(wl, buf, t, seq=None, report=None):
     for li, lay in enumerate(seq["layers"]):
         k_cache, kv_fp4, kv_scale = lay["k_cache"], lay["kv_fp4"], lay["kv_scale"]
         idx_gpu = buf.published[li][t].cpu().numpy()
+        if lay.get("q_idx") is not None and wl.q8:
+            qc, qs = O.mxfp8_quantize(O.bf16_decode(lay["q_idx"]).astype(np.float32))
         if lay["mode"] == "swa":
             assert idx_gpu.size == 0, f"q{t} L{li}: an SWA layer attends with no selection"
         elif lay["mode"] == "full":
-            if "k_codes" in seq:
+            if wl.q8:
+                scores = O.full_scores_mxfp4_q8(qc, qs, lay["w"], seq["k_codes"], seq["k_scales"],
+                                                0, nv, nv)
+            elif "k_codes" in seq:
                 scores = O.full_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                              seq["k_scales"], 0, nv, nv)
             else:
@@ -118,7 +123,10 @@ def check_query(wl, buf, t, seq=None, report=None):
             padded = np.full(2048, -1, np.int64)
             kept = pool_gpu[pool_gpu >= 0]
             padded[:len(kept)] = kept
-            if "k_codes" in seq:
+            if wl.q8:
+                scores = O.reindex_scores_mxfp4_q8(qc, qs, lay["w"], seq["k_codes"],
+                                                   seq["k_scales"], 0, nv, padded)
+            elif "k_codes" in seq:
                 scores = O.reindex_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                                 seq["k_scales"], 0, nv, padded)
             else:

@@ -158,10 +158,14 @@ def test_mxfp8_query_rejections(C):
     def call(**kw):
         a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_codes=FAKE, q_scales=FAKE, w=FAKE,
                  k_codes=FAKE, k_scales=FAKE, n_entries=10, kv_start=FAKE, n_visible=FAKE,
-                 scores=FAKE, ld=16, block_max=None, ld_bm=0, stream=None)
+                 pool_blocks=None, n_pool=0, block_size=8, scores=FAKE, ld=16, block_max=None,
+                 ld_bm=0, stream=None)
         a.update(kw)
         return L.csa2_index_score_mxfp4_q8(*a.values())
-    assert call(mode=1) == 2 and b"only FULL" in L.csa2_last_error()
+    assert call(mode=2) == 1 and b"no scoring" in L.csa2_last_error()
+    assert call(mode=1) == 1                              # REINDEX without a pool
+    assert call(pool_blocks=FAKE, n_pool=4) == 1          # FULL with a pool
+    assert call(block_size=16) == 2
     assert call(n_heads=16) == 2
     assert call(q_scales=None) == 1
     assert call(q_codes=FAKE + 8) == 1

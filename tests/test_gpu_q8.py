@@ -50,7 +50,7 @@ def test_index_score_mxfp4_q8_parity(C, dev, with_scores):
     ld = 5024
     scores = torch.full((4, ld), 3.0, dtype=torch.float32, device=dev) if with_scores else None
     bmax = torch.full((4, ld // 8), 3.0, dtype=torch.float32, device=dev)
-    C.csa2_index_score_mxfp4_q8(qc, qs, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+    C.csa2_index_score_mxfp4_q8(C.FULL, qc, qs, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
                                 wl.n_visible, scores, bmax, ld_scores=ld)
     torch.cuda.synchronize()
     kc_all, ks_all = wl.k_codes.cpu().numpy(), wl.k_scales.cpu().numpy()
@@ -71,3 +71,18 @@ def test_index_score_mxfp4_q8_parity(C, dev, with_scores):
         fin = np.isfinite(refb)
         assert np.array_equal(np.isfinite(bm[t]), fin), t
         assert np.all(np.abs(bm[t][fin] - refb[fin]) <= 1e-5 * tb[fin] + 1e-30), t
+
+
+def test_small_decode_stack_with_mxfp8_query(dev):
+    """A decoder stack (Full with pool, Reindex, Reuse) whose indexer passes quantise their
+    query to MXFP8 and score the MXFP4 keys on the scaled MFMA, checked layer by layer."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    from tests.parity_util import check_query
+    wl = synth.make_decode("q8_stack", 3, 0, synth.DECODE_LAYERS, True, 16,
+                           n_visible=[40000, 17000, 16384 + 8], kv_gap=9, seed=73,
+                           mxfp4=True).to(dev)
+    wl.q8 = True
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    assert sum(check_query(wl, buf, t) for t in range(wl.n_q)) == wl.n_q * len(wl.layers)
