@@ -170,18 +170,21 @@ __global__ __launch_bounds__(Q8_THREADS) void mxfp8_quantize_kernel(
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
+  // floor(log2 amax) is the exponent field minus 127 (a subnormal amax gives a field of 0
+  // and clamps to scale byte 1 either way); bf16 inputs keep the byte within 1..246
   int code_s = 127;
   if (amax > 0.f) {
-    int e;
-    (void)frexpf(amax, &e);                 // amax = m * 2^e, m in [0.5, 1)
-    code_s = e - 1 - 8 + 127;
+    code_s = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 8;
     code_s = code_s < 1 ? 1 : (code_s > 254 ? 254 : code_s);
   }
+  // 2^(127 - code_s) as a float (exponent field 254 - code_s, in 8 .. 253 for bytes up to
+  // 246): multiplying by it is exact, as ldexpf would be
+  const float inv = __uint_as_float((uint32_t)(254 - code_s) << 23);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lo |= f32_to_e4m3_rne(ldexpf(f[i], 127 - code_s)) << (8 * i);
-    hi |= f32_to_e4m3_rne(ldexpf(f[4 + i], 127 - code_s)) << (8 * i);
+    lo |= f32_to_e4m3_rne(f[i] * inv) << (8 * i);
+    hi |= f32_to_e4m3_rne(f[4 + i] * inv) << (8 * i);
   }
   if (r >= n_rows) return;
   *reinterpret_cast<u32x2*>(codes + r * 128 + 8 * c) = u32x2{lo, hi};
