@@ -435,6 +435,32 @@ def reindex_scores_mxfp4_q8(q_codes, q_scales, w, k_codes, k_scales, kv_start, n
     return out
 
 
+def full_scores_q8(q_codes, q_scales, w, k_cache_codes, kv_start, n_visible, width):
+    """Full-mode scores with an MXFP8 indexer query over E4M3 keys (reading R24)."""
+    out = np.full(int(width), NEG_INF)
+    n = min(int(n_visible), int(width))
+    if n > 0:
+        k = e4m3_decode(np.asarray(k_cache_codes)[int(kv_start):int(kv_start) + n])
+        out[:n] = index_score_rows(mxfp8_decode(q_codes, q_scales), np.asarray(w, np.float64), k)
+    return out
+
+
+def reindex_scores_q8(q_codes, q_scales, w, k_cache_codes, kv_start, n_visible, pool_blocks,
+                      block_size: int = 8) -> np.ndarray:
+    """reindex_scores with an MXFP8 query over E4M3 keys (reading R24)."""
+    pool_blocks = np.asarray(pool_blocks, dtype=np.int64)
+    n_slots = pool_blocks.shape[0] * block_size
+    out = np.full(n_slots, NEG_INF)
+    slot = np.arange(n_slots)
+    block = pool_blocks[slot // block_size]
+    pos = block * block_size + slot % block_size
+    ok = (block >= 0) & (pos < n_visible)
+    if ok.any():
+        rows = e4m3_decode(np.asarray(k_cache_codes)[kv_start + pos[ok]])
+        out[ok] = index_score_rows(mxfp8_decode(q_codes, q_scales), np.asarray(w, np.float64), rows)
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # Write side: the compressor and the indexer-key projection
 # --------------------------------------------------------------------------------------

@@ -705,3 +705,24 @@ def test_reindex_q8_over_every_block_equals_full_q8():
     pool2 = np.array([3, -1, nb + 4])
     re2 = O.reindex_scores_mxfp4_q8(qc, qs, w, kc, ks, 5, n, pool2)
     assert np.array_equal(re2[:8], full[24:32]) and np.all(np.isneginf(re2[8:]))
+
+
+def test_q8_scores_over_e4m3_keys_exact_query_and_pool_identity():
+    """An MXFP8 query that is exact (E4M3 grid, unit scales) scores E4M3 keys exactly as the
+    bf16 query does; Reindex over a pool of every block reproduces the Full scores."""
+    rng = np.random.default_rng(64)
+    q = rng.integers(0, 0x7E, size=(32, 128)).astype(np.uint8) | (rng.integers(0, 2, size=(32, 128)).astype(np.uint8) << 7)
+    q[:, ::32] = 0x7E
+    qv = O.e4m3_decode(q)
+    qc, qs = O.mxfp8_quantize(qv.astype(np.float32))
+    n = 150
+    k = rng.integers(0, 0x7E, size=(n + 3, 128)).astype(np.uint8) | (rng.integers(0, 2, size=(n + 3, 128)).astype(np.uint8) << 7)
+    w = rng.random(32)
+    q_bits = torch.from_numpy(qv.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ref = O.full_scores(q_bits, w, k, 3, n - 5, n)
+    got = O.full_scores_q8(qc, qs, w, k, 3, n - 5, n)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got)) and np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-9)
+    nb = -(-n // 8)
+    full = O.full_scores_q8(qc, qs, w, k, 3, n, nb * 8)
+    assert np.array_equal(O.reindex_scores_q8(qc, qs, w, k, 3, n, np.arange(nb)), full)
