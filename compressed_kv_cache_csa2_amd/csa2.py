@@ -38,6 +38,7 @@ def _load():
     lib.csa2_quantize_mxfp8.argtypes = [I, I, P, P, P, P]
     lib.csa2_index_score_mxfp4_q8.argtypes = [I, I, I, I, P, P, P, P, P, L, P, P, P, I, I, P, L, P,
                                               L, P]
+    lib.csa2_index_score_q8.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
     lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
@@ -53,7 +54,7 @@ def _load():
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
               "csa2_compress_kv", "csa2_project_index_key", "csa2_quantize_mxfp8",
-              "csa2_index_score_mxfp4_q8"):
+              "csa2_index_score_mxfp4_q8", "csa2_index_score_q8"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -134,6 +135,26 @@ def csa2_index_score_mxfp4_q8(mode, q_codes, q_scales, w, k_codes, k_scales, kv_
         _ptr(n_visible, torch.int32, "n_visible"), _ptr(pool_blocks, torch.int32, "pool_blocks"),
         n_pool, 8, _ptr(scores, torch.float32, "scores"),
         ld_scores, _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_index_score_q8(mode, q_codes, q_scales, w, k_cache, kv_start, n_visible, scores,
+                        block_max=None, pool_blocks=None, stream=None, ld_scores=None):
+    """csa2_index_score_mxfp4_q8 over E4M3 keys k_cache [E, 128]."""
+    n_q = q_codes.shape[0]
+    n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
+    if scores is not None:
+        ld_scores = scores.shape[1]
+    elif ld_scores is None:
+        raise ValueError("csa2_index_score_q8: ld_scores is required when scores is None")
+    _check(lib.csa2_index_score_q8(
+        mode, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
+        _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
+        _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+        _ptr(kv_start, torch.int64, "kv_start"), _ptr(n_visible, torch.int32, "n_visible"),
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
+        _ptr(scores, torch.float32, "scores"), ld_scores,
+        _ptr(block_max, torch.float32, "block_max"),
         block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 
 

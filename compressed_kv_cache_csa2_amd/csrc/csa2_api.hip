@@ -226,14 +226,14 @@ int csa2_quantize_mxfp8(int n_rows, int d, const void* x, void* codes, void* sca
                     fn);
 }
 
-int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
-                              const void* q_codes, const void* q_scales, const float* w,
-                              const void* k_codes, const void* k_scales, int64_t n_entries,
-                              const int64_t* kv_start, const int32_t* n_visible,
-                              const int32_t* pool_blocks, int n_pool, int block_size,
-                              float* scores, int64_t ld_scores, float* block_max,
-                              int64_t ld_block_max, void* stream) {
-  const char* fn = "csa2_index_score_mxfp4_q8";
+// MXFP8-query scoring over MXFP4 keys (k_scales given) or E4M3 keys (k_scales NULL).
+static int index_score_q8_common(const char* fn, csa2_mode_t mode, int n_q, int n_heads,
+                                 int d_idx, const void* q_codes, const void* q_scales,
+                                 const float* w, const void* k_codes, const void* k_scales,
+                                 int64_t n_entries, const int64_t* kv_start,
+                                 const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
+                                 int block_size, float* scores, int64_t ld_scores,
+                                 float* block_max, int64_t ld_block_max, void* stream) {
   REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
           "%s: mode %d does no scoring (Reuse layers attend with published indices)", fn,
           (int)mode);
@@ -244,7 +244,7 @@ int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
           CSA2_IDX_DIM);
   REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
   if (n_q == 0) return ok();
-  REQUIRE(q_codes && q_scales && w && k_codes && k_scales && kv_start && n_visible,
+  REQUIRE(q_codes && q_scales && w && k_codes && kv_start && n_visible,
           CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   REQUIRE(scores != nullptr || (mode == CSA2_FULL && block_max != nullptr), CSA2_ERR_INVALID_ARG,
           "%s: scores may be NULL only in FULL mode with block_max", fn);
@@ -272,13 +272,40 @@ int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
     REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
   }
   return hip_status(csa2::launch_index_score_q8(
-                        mode == CSA2_REINDEX, n_q, static_cast<const uint8_t*>(q_codes),
+                        mode == CSA2_REINDEX, k_scales != nullptr, n_q,
+                        static_cast<const uint8_t*>(q_codes),
                         static_cast<const uint8_t*>(q_scales), w,
                         static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(k_scales),
                         n_entries, kv_start, n_visible, pool_blocks,
                         mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
                         ld_block_max, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int csa2_index_score_mxfp4_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
+                              const void* q_codes, const void* q_scales, const float* w,
+                              const void* k_codes, const void* k_scales, int64_t n_entries,
+                              const int64_t* kv_start, const int32_t* n_visible,
+                              const int32_t* pool_blocks, int n_pool, int block_size,
+                              float* scores, int64_t ld_scores, float* block_max,
+                              int64_t ld_block_max, void* stream) {
+  REQUIRE(n_q == 0 || k_scales != nullptr, CSA2_ERR_INVALID_ARG,
+          "csa2_index_score_mxfp4_q8: null k_scales");
+  return index_score_q8_common("csa2_index_score_mxfp4_q8", mode, n_q, n_heads, d_idx, q_codes,
+                               q_scales, w, k_codes, k_scales, n_entries, kv_start, n_visible,
+                               pool_blocks, n_pool, block_size, scores, ld_scores, block_max,
+                               ld_block_max, stream);
+}
+
+int csa2_index_score_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_codes,
+                        const void* q_scales, const float* w, const void* k_cache,
+                        int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
+                        const int32_t* pool_blocks, int n_pool, int block_size, float* scores,
+                        int64_t ld_scores, float* block_max, int64_t ld_block_max, void* stream) {
+  return index_score_q8_common("csa2_index_score_q8", mode, n_q, n_heads, d_idx, q_codes,
+                               q_scales, w, k_cache, nullptr, n_entries, kv_start, n_visible,
+                               pool_blocks, n_pool, block_size, scores, ld_scores, block_max,
+                               ld_block_max, stream);
 }
 
 int csa2_compress_kv(int m, int n_tokens, int d, const void* c, const void* z, int64_t ld_in,

@@ -58,7 +58,8 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
 // Cache writes: quantise bf16 rows into the cache formats (destination rows outside
 // [0, n_rows) are skipped).
 // Full or Reindex scores of an MXFP8 indexer query over MXFP4 keys (scaled f8f6f4 MFMA).
-hipError_t launch_index_score_q8(bool reindex, int n_q, const uint8_t* q_codes,
+// fp4k: MXFP4 keys (codes + scales), else E4M3 rows of 128 bytes (k_scales unused).
+hipError_t launch_index_score_q8(bool reindex, bool fp4k, int n_q, const uint8_t* q_codes,
                                  const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
                                  const uint8_t* k_scales, int64_t n_entries,
                                  const int64_t* kv_start, const int32_t* n_visible,

@@ -19,6 +19,9 @@
 // bytes 32i + 16h .. +15 of its row (channels 64i + 32h .. +31, one 16-byte load) with
 // scale byte 2i + h, and a query lane (head m, half h) holds E4M3 bytes 64i + 16h .. +15
 // and 64i + 32 + 16h .. +15 of its head with the head's scale byte 2i + h.
+// E4M3 keys take the fp8 B form, which is laid out as the fp8 A operand (checked through
+// the scores against the oracle): a key lane holds bytes 64i + 16h .. +15 and
+// 64i + 32 + 16h .. +15 of its row, with the unit scale byte 127.
 #include "csa2_device.h"
 #include "csa2_launch.h"
 
@@ -32,7 +35,7 @@ constexpr int Q8_THREADS = 256;
 constexpr int Q8_STEPS_FULL = 16;
 constexpr int Q8_STEPS_REINDEX = 4;
 
-template <bool REINDEX>
+template <bool REINDEX, bool FP4K>
 __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ w, const uint8_t* __restrict__ k_codes,
@@ -93,16 +96,28 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
   for (int st = 0; st < Q8_STEPS; ++st) rows[st] = row_of(st);
   auto row_at = [&](int step) -> int64_t { return rows[step]; };
   const bool any = nv > 0 && base >= 0 && base < n_entries;
-  // Per step and lane: code bytes 16h .. +15 and 32 + 16h .. +15 of its row, scale word.
-  u32x4 kb[2][2];
+  // Per step and lane, MXFP4: code bytes 16h .. +15 and 32 + 16h .. +15 of its row and the
+  // scale word; E4M3: bytes 64i + 16h .. +15 and 64i + 32 + 16h .. +15 for i = 0, 1.
+  constexpr int NKB = FP4K ? 2 : 4;
+  u32x4 kb[2][NKB];
   uint32_t ks[2];
   auto load_step = [&](int step, int b) {
     const int64_t r = row_at(step);
     const int64_t rr = r >= 0 ? r : base;
-    const uint8_t* row = k_codes + rr * 64;
-    kb[b][0] = *reinterpret_cast<const u32x4*>(row + 16 * half);
-    kb[b][1] = *reinterpret_cast<const u32x4*>(row + 32 + 16 * half);
-    ks[b] = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
+    if constexpr (FP4K) {
+      const uint8_t* row = k_codes + rr * 64;
+      kb[b][0] = *reinterpret_cast<const u32x4*>(row + 16 * half);
+      kb[b][1] = *reinterpret_cast<const u32x4*>(row + 32 + 16 * half);
+      ks[b] = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
+    } else {
+      const uint8_t* row = k_codes + rr * 128;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        kb[b][2 * i] = *reinterpret_cast<const u32x4*>(row + 64 * i + 16 * half);
+        kb[b][2 * i + 1] = *reinterpret_cast<const u32x4*>(row + 64 * i + 32 + 16 * half);
+      }
+      ks[b] = 0x7F7F7F7Fu;
+    }
   };
   float sc[Q8_STEPS];
   if (any) load_step(0, 0);
@@ -115,12 +130,21 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
       f32x16 acc = {};
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const u32x4 c = kb[b][i];
-        const i32x8 bv = i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
         const uint32_t sb = (ks[b] >> (8 * (2 * i + half))) & 0xFFu;
-        // A format 0 (fp8 E4M3), B format 4 (fp4 E2M1)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc, 0, 4, 0, (int)sa[i],
-                                                              0, (int)sb);
+        if constexpr (FP4K) {
+          const u32x4 c = kb[b][i];
+          const i32x8 bv = i32x8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+          // A format 0 (fp8 E4M3), B format 4 (fp4 E2M1)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc, 0, 4, 0,
+                                                                (int)sa[i], 0, (int)sb);
+        } else {
+          const u32x4 c0 = kb[b][2 * i], c1 = kb[b][2 * i + 1];
+          const i32x8 bv = i32x8{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w,
+                                 (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+          // A and B format 0 (fp8 E4M3)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc, 0, 0, 0,
+                                                                (int)sa[i], 0, (int)sb);
+        }
       }
       float part = 0.f;
 #pragma unroll
@@ -191,7 +215,7 @@ __global__ __launch_bounds__(Q8_THREADS) void mxfp8_quantize_kernel(
   if ((c & 3) == 0) scales[r * 4 + (c >> 2)] = (uint8_t)code_s;
 }
 
-hipError_t launch_index_score_q8(bool reindex, int n_q, const uint8_t* q_codes,
+hipError_t launch_index_score_q8(bool reindex, bool fp4k, int n_q, const uint8_t* q_codes,
                                  const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
                                  const uint8_t* k_scales, int64_t n_entries,
                                  const int64_t* kv_start, const int32_t* n_visible,
@@ -205,7 +229,10 @@ hipError_t launch_index_score_q8(bool reindex, int n_q, const uint8_t* q_codes,
                        k_scales, n_entries, kv_start, n_visible, pool_blocks, n_pool, scores, ld,
                        block_max, ld_bm);
   };
-  reindex ? go(index_score_q8_kernel<true>) : go(index_score_q8_kernel<false>);
+  if (fp4k)
+    reindex ? go(index_score_q8_kernel<true, true>) : go(index_score_q8_kernel<false, true>);
+  else
+    reindex ? go(index_score_q8_kernel<true, false>) : go(index_score_q8_kernel<false, false>);
   return hipGetLastError();
 }
 

@@ -361,9 +361,10 @@ def make_encoder(name="encoder_128k_m2", n_q=4096, n_entries=131072, ratio=2,
 def make_workload(name: str, device="cpu", seed=0, n_q=None) -> Workload:
     """One of the named workloads; n_q (optional) keeps only the first n_q queries. A
     decode workload name with the suffix "_mxfp4" also carries MXFP4 indexer keys, which
-    its indexer passes then read instead of the E4M3 ones; with the suffix "_mxfp4_q8" those
-    passes also quantise the indexer query to MXFP8."""
-    if name.endswith("_mxfp4_q8"):
+    its indexer passes then read instead of the E4M3 ones; a further suffix "_q8" (on a
+    decode workload, E4M3 or MXFP4 keys) makes those passes quantise the indexer query to
+    MXFP8."""
+    if name.endswith("_q8"):
         wl = make_workload(name[:-3], device=device, seed=seed, n_q=n_q)
         wl.name, wl.q8 = name, True
         return wl

@@ -100,9 +100,11 @@ def check_query(wl, buf, t, seq=None, report=None):
         if lay["mode"] == "swa":
             assert idx_gpu.size == 0, f"q{t} L{li}: an SWA layer attends with no selection"
         elif lay["mode"] == "full":
-            if wl.q8:
+            if wl.q8 and "k_codes" in seq:
                 scores = O.full_scores_mxfp4_q8(qc, qs, lay["w"], seq["k_codes"], seq["k_scales"],
                                                 0, nv, nv)
+            elif wl.q8:
+                scores = O.full_scores_q8(qc, qs, lay["w"], k_cache, 0, nv, nv)
             elif "k_codes" in seq:
                 scores = O.full_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                              seq["k_scales"], 0, nv, nv)
@@ -123,9 +125,11 @@ def check_query(wl, buf, t, seq=None, report=None):
             padded = np.full(2048, -1, np.int64)
             kept = pool_gpu[pool_gpu >= 0]
             padded[:len(kept)] = kept
-            if wl.q8:
+            if wl.q8 and "k_codes" in seq:
                 scores = O.reindex_scores_mxfp4_q8(qc, qs, lay["w"], seq["k_codes"],
                                                    seq["k_scales"], 0, nv, padded)
+            elif wl.q8:
+                scores = O.reindex_scores_q8(qc, qs, lay["w"], k_cache, 0, nv, padded)
             elif "k_codes" in seq:
                 scores = O.reindex_scores_mxfp4(lay["q_idx"], lay["w"], seq["k_codes"],
                                                 seq["k_scales"], 0, nv, padded)

@@ -86,3 +86,16 @@ def test_small_decode_stack_with_mxfp8_query(dev):
     layers.run_layers(wl, buf)
     torch.cuda.synchronize()
     assert sum(check_query(wl, buf, t) for t in range(wl.n_q)) == wl.n_q * len(wl.layers)
+
+
+def test_small_decode_stack_with_mxfp8_query_over_e4m3_keys(dev):
+    """The same stack over E4M3 keys (the matrix core's fp8 B operand, unit key scales)."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    from tests.parity_util import check_query
+    wl = synth.make_decode("q8_e4m3", 3, 0, synth.DECODE_LAYERS, True, 16,
+                           n_visible=[40000, 17000, 16384 + 8], kv_gap=9, seed=74).to(dev)
+    wl.q8 = True
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    assert sum(check_query(wl, buf, t) for t in range(wl.n_q)) == wl.n_q * len(wl.layers)
