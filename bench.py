@@ -52,6 +52,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 matrix peak (the MXFP8-query indexer)
 FLOPS_PER_PAIR = 32 * 128 * 2   # indexer multiply-adds of one (query, entry) pair
 INDEXER_SRC = os.path.join(ROOT, "compressed_kv_cache_csa2_amd", "csrc", "index_score.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_score_full_decode_256k.md")
@@ -461,7 +462,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if wl.q8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.n_q, "context_entries": wl.n_ctx,
                    "layers": [l.mode for l in wl.layers], "index_topk": 512,
@@ -489,10 +490,13 @@ def main():
     if wl.shared_start is not None:
         pairs = int(wl.n_visible.to(torch.int64).sum())
         tflops = pairs * FLOPS_PER_PAIR / (idx_us * 1e-6) / 1e12
-        line["roofline"].update({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+        peak = PEAK_FP8_TFLOPS if wl.q8 else PEAK_BF16_TFLOPS
+        line["roofline"].update({"bound": "mfma", "achieved": tflops, "peak": peak,
+                                 "unit": "TFLOP/s", "frac": tflops / peak,
                                  "flops_per_launch": pairs * FLOPS_PER_PAIR,
-                                 "kernel": "index_score_shared_kernel (grouped Full indexer)"})
+                                 "kernel": "index_score_shared_q8_kernel (grouped Full indexer, "
+                                           "MXFP8 query, fp8 MFMA)" if wl.q8 else
+                                           "index_score_shared_kernel (grouped Full indexer)"})
         del line["roofline"]["bytes_per_launch"]
     if recall is not None:
         line["needle_recall"] = recall

@@ -39,6 +39,7 @@ def _load():
     lib.csa2_index_score_mxfp4_q8.argtypes = [I, I, I, I, P, P, P, P, P, L, P, P, P, I, I, P, L, P,
                                               L, P]
     lib.csa2_index_score_q8.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_index_score_shared_q8.argtypes = [I, I, I, P, P, P, P, L, L, P, P, L, P, L, P]
     lib.csa2_compress_kv.argtypes = [I, I, I, P, P, L, P, L, P]
     lib.csa2_project_index_key.argtypes = [I, I, I, P, L, P, P, L, P]
     lib.csa2_write_latent.argtypes = [I, P, P, P, L, P, L, L, P]
@@ -54,7 +55,7 @@ def _load():
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
               "csa2_compress_kv", "csa2_project_index_key", "csa2_quantize_mxfp8",
-              "csa2_index_score_mxfp4_q8", "csa2_index_score_q8"):
+              "csa2_index_score_mxfp4_q8", "csa2_index_score_q8", "csa2_index_score_shared_q8"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -155,6 +156,19 @@ def csa2_index_score_q8(mode, q_codes, q_scales, w, k_cache, kv_start, n_visible
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
         _ptr(scores, torch.float32, "scores"), ld_scores,
         _ptr(block_max, torch.float32, "block_max"),
+        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+
+
+def csa2_index_score_shared_q8(q_codes, q_scales, w, k_cache, kv_start: int, n_visible, scores,
+                               block_max=None, stream=None):
+    """csa2_index_score_shared with an MXFP8 query over E4M3 keys."""
+    n_q = q_codes.shape[0]
+    _check(lib.csa2_index_score_shared_q8(
+        n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
+        _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
+        _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0], int(kv_start),
+        _ptr(n_visible, torch.int32, "n_visible"), _ptr(scores, torch.float32, "scores"),
+        scores.shape[1], _ptr(block_max, torch.float32, "block_max"),
         block_max.shape[1] if block_max is not None else 0, _stream(stream)))
 
 

@@ -308,6 +308,40 @@ int csa2_index_score_q8(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const
                                ld_block_max, stream);
 }
 
+int csa2_index_score_shared_q8(int n_q, int n_heads, int d_idx, const void* q_codes,
+                               const void* q_scales, const float* w, const void* k_cache,
+                               int64_t n_entries, int64_t kv_start, const int32_t* n_visible,
+                               float* scores, int64_t ld_scores, float* block_max,
+                               int64_t ld_block_max, void* stream) {
+  const char* fn = "csa2_index_score_shared_q8";
+  REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
+          "%s: indexer shape %dx%d, only %dx%d is built", fn, n_heads, d_idx, CSA2_IDX_HEADS,
+          CSA2_IDX_DIM);
+  REQUIRE(n_q >= 0 && n_q <= (1 << 22), CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
+  if (n_q == 0) return ok();
+  REQUIRE(q_codes && q_scales && w && k_cache && n_visible && scores, CSA2_ERR_INVALID_ARG,
+          "%s: null pointer argument", fn);
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "%s: n_entries < 0", fn);
+  REQUIRE(ld_scores >= 1 && ld_scores <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "%s: ld_scores %lld out of range", fn, (long long)ld_scores);
+  REQUIRE(aligned(q_codes, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
+          "%s: q_codes and k_cache must be 16-byte aligned", fn);
+  REQUIRE(aligned(q_scales, 4) && aligned(w, 4) && aligned(scores, 4) && aligned(n_visible, 4),
+          CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
+  if (block_max != nullptr) {
+    REQUIRE(ld_block_max >= (ld_scores + 7) / 8, CSA2_ERR_INVALID_ARG,
+            "%s: ld_block_max %lld < ceil(ld_scores/8)", fn, (long long)ld_block_max);
+    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
+  }
+  return hip_status(csa2::launch_index_score_shared_q8(
+                        n_q, static_cast<const uint8_t*>(q_codes),
+                        static_cast<const uint8_t*>(q_scales), w,
+                        static_cast<const uint8_t*>(k_cache), n_entries, kv_start, n_visible,
+                        scores, ld_scores, block_max, ld_block_max,
+                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int csa2_compress_kv(int m, int n_tokens, int d, const void* c, const void* z, int64_t ld_in,
                      void* out, int64_t ld_out, void* stream) {
   const char* fn = "csa2_compress_kv";

@@ -66,6 +66,12 @@ hipError_t launch_index_score_q8(bool reindex, bool fp4k, int n_q, const uint8_t
                                  const int32_t* pool_blocks, int n_pool, float* scores,
                                  int64_t ld, float* block_max, int64_t ld_bm,
                                  hipStream_t stream);
+// Full-mode MXFP8-query scores over E4M3 keys for queries sharing one sequence.
+hipError_t launch_index_score_shared_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
+                                        const float* w, const uint8_t* k_cache,
+                                        int64_t n_entries, int64_t kv_start,
+                                        const int32_t* n_visible, float* scores, int64_t ld,
+                                        float* block_max, int64_t ld_bm, hipStream_t stream);
 // MXFP8 quantisation of bf16 rows of 128 channels.
 hipError_t launch_mxfp8_quantize(int n_rows, const uint16_t* x, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);

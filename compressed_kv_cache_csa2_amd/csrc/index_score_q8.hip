@@ -169,6 +169,149 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
   }
 }
 
+// Queries that share one sequence (chunked prefill), MXFP8 query over E4M3 keys: a
+// workgroup scores SQ8_QT queries (two per wavefront, operands and scales in registers)
+// against one 4,096-row tile. Per 32-row step each wavefront loads one 16-byte quarter of
+// every row's B operand straight into an LDS buffer in operand order (the keys need no
+// conversion: the matrix core takes the E4M3 bytes), one barrier per step, then every
+// wavefront reads the step's two operands and runs its queries' two MFMAs each. The
+// products and their order are those of index_score_q8_kernel: identical scores.
+constexpr int SQ8_QW = 2;
+constexpr int SQ8_QT = (Q8_THREADS / 64) * SQ8_QW;
+constexpr int SQ8_TILE = 4096;
+constexpr int SQ8_PF = 16;   // steps whose rows are in flight (they come mostly from cache)
+
+__global__ __launch_bounds__(Q8_THREADS) void index_score_shared_q8_kernel(
+    int n_q, const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_cache, int64_t n_entries,
+    int64_t kv_start, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
+    int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
+  // bsh[buf][2i + part][lane]: bytes 64i + 32 part + 16h .. +15 of row lane % 32
+  __shared__ u32x4 bsh[2][4][64];
+  __shared__ int nv_sh[SQ8_QT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int half = lane >> 5;
+  const int t0 = blockIdx.y * SQ8_QT;
+
+  i32x8 a[SQ8_QW][2];
+  uint32_t sa[SQ8_QW][2];
+  float wr[SQ8_QW][16];
+  int nvq[SQ8_QW];
+#pragma unroll
+  for (int j = 0; j < SQ8_QW; ++j) {
+    const int t = t0 + SQ8_QW * wave + j;
+    const bool ok = t < n_q;
+    const int64_t tq = ok ? t : 0;
+    const uint8_t* qrow = q_codes + (tq * 32 + n) * 128;
+    const uint32_t qs = *reinterpret_cast<const uint32_t*>(q_scales + (tq * 32 + n) * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow + 64 * i + 16 * half);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 64 * i + 32 + 16 * half);
+      a[j][i] = ok ? i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}
+                   : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sa[j][i] = (qs >> (8 * (2 * i + half))) & 0xFFu;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wr[j][r] = ok ? w[tq * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] : 0.f;
+    nvq[j] = ok ? n_visible[t] : 0;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < SQ8_QW; ++j) nv_sh[SQ8_QW * wave + j] = nvq[j];
+  }
+  __syncthreads();
+  int nv_max = 0;
+#pragma unroll
+  for (int q = 0; q < SQ8_QT; ++q) nv_max = max(nv_max, nv_sh[q]);
+
+  const int64_t tile0 = (int64_t)blockIdx.x * SQ8_TILE;
+  constexpr int STEPS = SQ8_TILE / 32;
+  const bool any = nv_max > 0 && kv_start >= 0 && kv_start < n_entries;
+  auto row_at = [&](int step) -> int64_t {
+    const int64_t slot = tile0 + (int64_t)step * 32 + n;
+    if (slot >= ld || slot >= nv_max) return -1;
+    const int64_t row = kv_start + slot;
+    return (row >= 0 && row < n_entries) ? row : -1;
+  };
+  // wavefront w loads operand part (w % 2) of MFMA w / 2: bytes 64(w/2) + 32(w%2) + 16h .. +15
+  const int boff = 64 * (wave >> 1) + 32 * (wave & 1) + 16 * half;
+  u32x4 raw[SQ8_PF];
+  auto load = [&](int step) -> u32x4 {
+    const int64_t r = row_at(step);
+    return *reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : kv_start) * 128 + boff);
+  };
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < SQ8_PF; ++i) raw[i] = load(i);
+  }
+#pragma unroll 1
+  for (int step0 = 0; step0 < STEPS; step0 += SQ8_PF) {
+#pragma unroll
+    for (int i = 0; i < SQ8_PF; ++i) {
+      const int step = step0 + i;
+      const int buf = step & 1;
+      const int64_t slot = tile0 + (int64_t)step * 32 + n;
+      const bool row_ok = any && row_at(step) >= 0;
+      if (any) {
+        bsh[buf][wave][lane] = raw[i];
+        if (step + SQ8_PF < STEPS) raw[i] = load(step + SQ8_PF);
+      }
+      __syncthreads();
+      i32x8 b[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const u32x4 lo = bsh[buf][2 * m][lane], hi = bsh[buf][2 * m + 1][lane];
+        b[m] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < SQ8_QW; ++j) {
+        const int t = t0 + SQ8_QW * wave + j;
+        float sv = -__builtin_inff();
+        if (any) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j][m], b[m], acc, 0, 0, 0,
+                                                                  (int)sa[j][m], 0, 127);
+          float part = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part += wr[j][r] * fmaxf(acc[r], 0.f);
+          part += __shfl_xor(part, 32);
+          if (row_ok && slot < nvq[j]) sv = part;
+        }
+        if (t < n_q && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+        if (block_max != nullptr) {
+          float mm = sv;
+          mm = fmaxf(mm, __shfl_xor(mm, 1));
+          mm = fmaxf(mm, __shfl_xor(mm, 2));
+          mm = fmaxf(mm, __shfl_xor(mm, 4));
+          if (t < n_q && half == 0 && (n & 7) == 0 && slot < ld)
+            block_max[(int64_t)t * ld_bm + (slot >> 3)] = mm;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_index_score_shared_q8(int n_q, const uint8_t* q_codes, const uint8_t* q_scales,
+                                        const float* w, const uint8_t* k_cache,
+                                        int64_t n_entries, int64_t kv_start,
+                                        const int32_t* n_visible, float* scores, int64_t ld,
+                                        float* block_max, int64_t ld_bm, hipStream_t stream) {
+  dim3 grid((unsigned)((ld + SQ8_TILE - 1) / SQ8_TILE), (unsigned)((n_q + SQ8_QT - 1) / SQ8_QT));
+  hipLaunchKernelGGL(index_score_shared_q8_kernel, grid, dim3(Q8_THREADS), 0, stream, n_q,
+                     q_codes, q_scales, w, k_cache, n_entries, kv_start, n_visible, scores, ld,
+                     block_max, ld_bm);
+  return hipGetLastError();
+}
+
 // MXFP8 quantisation of bf16 rows of 128 channels (the OCP microscaling recipe): per 32
 // channels the exponent X = floor(log2 amax) - 8 (8 = E4M3's largest exponent), stored
 // as X + 127 kept in 1..254 (127 for an all-zero group), codes E4M3(x * 2^-X), nearest

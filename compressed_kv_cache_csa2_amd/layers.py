@@ -95,6 +95,11 @@ def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scor
                                     wl.k_scales, wl.kv_start, wl.n_visible, scores, block_max,
                                     pool_blocks=pool_blocks, stream=stream, ld_scores=ld_scores)
         return
+    if (wl.q8 and mode == C.FULL and wl.shared_start is not None and scores is not None):
+        C.csa2_index_score_shared_q8(buf.q8_codes, buf.q8_scales, lay.w, k_cache,
+                                     wl.shared_start, wl.n_visible, scores, block_max,
+                                     stream=stream)
+        return
     if wl.q8:
         C.csa2_index_score_q8(mode, buf.q8_codes, buf.q8_scales, lay.w, k_cache, wl.kv_start,
                               wl.n_visible, scores, block_max, pool_blocks=pool_blocks,
@@ -136,8 +141,8 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
         raise ValueError(f"unknown coarse filter {coarse!r}")
     if coarse == "hisa" and (means is None or not wl.with_pool):
         raise ValueError("coarse='hisa' needs a pooled decoder workload and its block means")
-    if wl.q8 and (coarse != "hsi" or wl.shared_start is not None):
-        raise ValueError("the MXFP8 query is routed for decoder stacks with the HSI pool only")
+    if wl.q8 and coarse != "hsi":
+        raise ValueError("the MXFP8 query is routed with the HSI pool only")
     current = None
     current_group = 0
     for li, lay in enumerate(wl.layers):

@@ -172,6 +172,14 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
  * Errors: as csa2_index_score_mxfp4. */
 int csa2_quantize_mxfp8(int n_rows, int d, const void* x, void* codes, void* scales,
                         void* stream);
+/* csa2_index_score_shared_q8: csa2_index_score_shared (queries sharing one sequence, FULL
+ * mode, kv_start a host value, n_q <= 2^22) with the MXFP8 query over E4M3 keys; scores
+ * identical to csa2_index_score_q8's. */
+int csa2_index_score_shared_q8(int n_q, int n_heads, int d_idx, const void* q_codes,
+                               const void* q_scales, const float* w, const void* k_cache,
+                               int64_t n_entries, int64_t kv_start, const int32_t* n_visible,
+                               float* scores, int64_t ld_scores, float* block_max,
+                               int64_t ld_block_max, void* stream);
 /* csa2_index_score_q8: the same with E4M3 keys (k_cache [n_entries, 128], as
  * csa2_index_score reads them) instead of MXFP4 ones: the matrix core's fp8 B operand with
  * unit key scales. Arguments, modes and errors as csa2_index_score. */

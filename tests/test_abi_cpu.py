@@ -25,6 +25,7 @@ def test_header_symbols_are_exported(C):
                      "csa2_index_score_shared", "csa2_index_score_bf16",
                      "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
                      "csa2_quantize_mxfp8", "csa2_index_score_mxfp4_q8", "csa2_index_score_q8",
+                     "csa2_index_score_shared_q8",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:

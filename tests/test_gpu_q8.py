@@ -99,3 +99,32 @@ def test_small_decode_stack_with_mxfp8_query_over_e4m3_keys(dev):
     layers.run_layers(wl, buf)
     torch.cuda.synchronize()
     assert sum(check_query(wl, buf, t) for t in range(wl.n_q)) == wl.n_q * len(wl.layers)
+
+
+def test_index_score_shared_q8_equals_per_query_and_oracle(dev):
+    """Grouped scoring of queries sharing one sequence gives the per-query MXFP8-query
+    scores bit for bit, and the oracle's on sampled queries."""
+    from compressed_kv_cache_csa2_amd import csa2 as C, synth
+    wl = synth.make_prefill("pf_q8", n_q=45, n_entries=9000, device=dev, seed=75)
+    lay = wl.layers[0]
+    qc = torch.empty((45, 32, 128), dtype=torch.uint8, device=dev)
+    qs = torch.empty((45, 32, 4), dtype=torch.uint8, device=dev)
+    C.csa2_quantize_mxfp8(lay.q_idx, qc, qs)
+    ld = 9024
+    s1 = torch.empty((45, ld), dtype=torch.float32, device=dev)
+    s2 = torch.empty_like(s1)
+    b1 = torch.empty((45, ld // 8), dtype=torch.float32, device=dev)
+    b2 = torch.empty_like(b1)
+    C.csa2_index_score_shared_q8(qc, qs, lay.w, wl.k_cache, 0, wl.n_visible, s1, b1)
+    C.csa2_index_score_q8(C.FULL, qc, qs, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, s2, b2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(b1, b2)
+    k_all = wl.k_cache.cpu().numpy()
+    for t in (0, 22, 44):
+        nv = int(wl.n_visible[t])
+        q = (qc[t].cpu().numpy(), qs[t].cpu().numpy())
+        ref = O.full_scores_q8(q[0], q[1], lay.w[t].cpu().numpy(), k_all, 0, nv, ld)
+        qa = np.abs(O.mxfp8_decode(*q))
+        terms = np.zeros(ld)
+        terms[:nv] = (np.abs(O.e4m3_decode(k_all[:nv])) @ qa.T) @ np.abs(lay.w[t].cpu().numpy().astype(np.float64))
+        assert_scores_close(s1[t].cpu().numpy(), ref, terms, f"shared q8 q{t}")
