@@ -170,13 +170,13 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
 }
 
 // Queries that share one sequence (chunked prefill), MXFP8 query over E4M3 keys: a
-// workgroup scores SQ8_QT queries (two per wavefront, operands and scales in registers)
+// workgroup scores SQ8_QT queries (four per wavefront, operands and scales in registers)
 // against one 4,096-row tile. Per 32-row step each wavefront loads one 16-byte quarter of
 // every row's B operand straight into an LDS buffer in operand order (the keys need no
 // conversion: the matrix core takes the E4M3 bytes), one barrier per step, then every
 // wavefront reads the step's two operands and runs its queries' two MFMAs each. The
 // products and their order are those of index_score_q8_kernel: identical scores.
-constexpr int SQ8_QW = 2;
+constexpr int SQ8_QW = 4;
 constexpr int SQ8_QT = (Q8_THREADS / 64) * SQ8_QW;
 constexpr int SQ8_TILE = 4096;
 constexpr int SQ8_PF = 16;   // steps whose rows are in flight (they come mostly from cache)
