@@ -726,3 +726,147 @@ def test_q8_scores_over_e4m3_keys_exact_query_and_pool_identity():
     nb = -(-n // 8)
     full = O.full_scores_q8(qc, qs, w, k, 3, n, nb * 8)
     assert np.array_equal(O.reindex_scores_q8(qc, qs, w, k, 3, n, np.arange(nb)), full)
+
+
+# ------------------------------------------------- quantiser rules against brute force
+
+def _nearest_even_e2m1_mag(a):
+    """Brute force: index of the E2M1 magnitude nearest to each a >= 0 (float64), ties to
+    the even index, everything past 6 taking the last one. Distances to all eight grid
+    values are compared directly (no midpoint table)."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    d = np.abs(np.asarray(a, np.float64)[..., None] - grid)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among equally near grid points prefer the even index (at most two can tie)
+    even = cand & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return np.where(np.asarray(a) >= 6.0, 7, pick)
+
+
+def _all_bf16_in(lo_exp, hi_exp):
+    """Every positive bf16 value 2^lo_exp <= v < 2^hi_exp, as float32."""
+    e = np.arange(lo_exp, hi_exp, dtype=np.float64)[:, None]
+    m = 1.0 + np.arange(128, dtype=np.float64)[None, :] / 128.0
+    return (m * 2.0 ** e).ravel().astype(np.float32)
+
+
+def test_e2m1_ratio_rounding_is_the_exact_quotient_rounding():
+    """Reading R16 ("DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression",
+    2.4.4: E2M1 values under an E4M3 scale): each code is the nearest E2M1 magnitude to the
+    exact quotient x / s, ties to the even code. Checked over every signed bf16 in
+    [2^-31, 2^17) against every finite positive E4M3 scale (about 1.5M pairs). The fp64
+    quotient decides every comparison as the exact one does: x has 8 significant bits and
+    a midpoint times s at most 7, so x / s either equals a midpoint exactly or differs
+    from it by far more than an fp64 rounding."""
+    xs = _all_bf16_in(-31, 17)
+    xs = np.concatenate([xs, -xs])
+    scales = O.E4M3_POS[1:]                      # 126 finite positive scales
+    x = xs[:, None].astype(np.float64)
+    s = scales[None, :]
+    got = O.e2m1_round_ratio(x, s)
+    mag = _nearest_even_e2m1_mag(np.abs(x) / s)
+    want = mag | (((x < 0) & (mag > 0)).astype(np.int64) << 3)
+    assert np.array_equal(got, want.astype(np.uint8))
+
+
+def test_fp4_latent_quantize_on_exact_midpoints():
+    """Groups whose largest value is 6*s (so the scale is exactly s) and whose other values
+    sit exactly on the midpoints between neighbouring E2M1 magnitudes times s: every
+    midpoint must go to the even code, and the scale byte must decode to s."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    even_code = np.array([0, 2, 2, 4, 4, 6, 6])
+    rows = []
+    wants = []
+    s_vals = []
+    for s in O.E4M3_POS[1:]:
+        # 6*s has at most 5 significant bits and a midpoint times s at most 7, so every
+        # value is a bf16; (6*s)/6 in float32 is s itself, an E4M3 value
+        vals = np.concatenate([[6.0 * s], mids * s, -mids * s, [0.0]])
+        code = np.concatenate([[7], even_code, even_code | 8, [0]])
+        code = np.where(np.concatenate([[6.0], mids, -mids, [0.0]]) == 0, 0, code)
+        # the negative midpoint 0.25 rounds to magnitude 0: no sign bit on a zero code
+        code[8] = 0
+        rows.append(np.resize(vals, 16))
+        wants.append(np.resize(code, 16))
+        s_vals.append(s)
+    x = np.stack(rows).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), np.stack(rows))   # exact in float32 / bf16
+    x = np.concatenate([x] * 32, axis=1)                          # 512 channels per row
+    payload, scodes = O.fp4_latent_quantize(x)
+    assert np.array_equal(O.E4M3_TABLE[scodes], np.repeat(np.array(s_vals)[:, None], 32, 1))
+    lo, hi = payload & 0xF, payload >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(x.shape)
+    assert np.array_equal(codes, np.concatenate([np.stack(wants)] * 32, axis=1))
+
+
+def test_mxfp4_key_exponent_recipe_and_codes():
+    """Reading R19 (the OCP microscaling recipe for the MXFP4 indexer cache, "DeepSeek-v4.1
+    Flash: Pushing the Limits of KV Cache Compression", 2.4.4 and 3.1): for every nonzero
+    32-channel group the shared exponent X puts the group's largest magnitude in [4, 8)
+    after scaling by 2^-X, so its largest code is 4 or 6; an all-zero group gets byte 127;
+    every code is the nearest-even E2M1 rounding of x * 2^-X (brute force)."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((3000, 128)) * np.exp(rng.uniform(-20, 20, (3000, 1)))).astype(np.float32)
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    x[5, :32] = 0.0
+    x[6, 32:64] = -0.0
+    # amax exactly on powers of two and just below them
+    x[7, 0] = 4.0
+    x[8, 0] = np.float32(np.nextafter(np.float32(8.0), np.float32(0)))
+    x[8, 0] = torch.tensor(x[8, 0]).to(torch.bfloat16).float().item()
+    codes, scales = O.mxfp4_key_quantize(x)
+    g = x.reshape(3000, 4, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=-1)
+    X = scales.astype(np.int64) - 127
+    nz = amax > 0
+    scaled_max = amax * np.ldexp(1.0, -X)
+    assert np.all((scaled_max[nz] >= 4.0) & (scaled_max[nz] < 8.0))
+    assert np.all(scales[~nz] == 127)
+    assert scales[5, 0] == 127 and scales[6, 1] == 127
+    lo, hi = codes & 0xF, codes >> 4
+    c = np.stack([lo, hi], axis=-1).reshape(3000, 128).reshape(3000, 4, 32)
+    mag = _nearest_even_e2m1_mag(np.abs(g) * np.ldexp(1.0, -X)[..., None])
+    want = mag | (((g < 0) & (mag > 0)).astype(np.int64) << 3)
+    assert np.array_equal(c, want)
+    top = (c & 7).max(axis=-1)
+    assert set(np.unique(top[nz]).tolist()) <= {6, 7}          # magnitudes 4 and 6
+
+
+# ------------------------------------------------------------------ Reindex layer as a whole
+
+def test_reindex_layer_composition_and_full_query_identity():
+    """reindex_layer is the Reindex mode of "DeepSeek-v4.1 Flash: Pushing the Limits of KV
+    Cache Compression" 2.3.2 / 2.3.4: scores over the pool, its own Top-K inside the pool,
+    slots mapped through the pool, attention with those indices. (a) With a fresh query it
+    equals that chain built from the oracle's pieces; (b) given the Full layer's own
+    indexer query, weights, attention query and window it reproduces the Full layer's
+    indices and output exactly (every Full winner lies in the pool, and pool slots run in
+    ascending position order, so the gather order is the same)."""
+    n = 9001
+    k_cache, p, s, win, q_idx, w, q = _tiny_sequence(31, n)
+    scale = 1 / math.sqrt(512)
+    full = O.full_layer(q_idx, w, k_cache, 0, n, q, p, s, win, 0, 128, scale, with_pool=True)
+    same = O.reindex_layer(q_idx, w, k_cache, 0, n, full["pool"], q, p, s, win, 0, 128, scale)
+    assert np.array_equal(same["idx"], full["idx"])
+    assert np.array_equal(same["out"], full["out"]) and np.array_equal(same["lse"], full["lse"])
+    _, _, _, win2, q_idx2, w2, q2 = _tiny_sequence(32, 16)
+    fresh = O.reindex_layer(q_idx2, w2, k_cache, 0, n, full["pool"], q2, p, s, win2, 0, 100,
+                            scale)
+    padded = np.full(2048, -1, np.int64)
+    padded[:len(full["pool"])] = full["pool"]
+    rs = O.reindex_scores(q_idx2, w2, k_cache, 0, n, padded)
+    idx = O.slots_to_positions(O.topk_slots(rs, 512), padded)
+    ref = O.reuse_layer(idx, q2, p, s, 0, win2, 0, 100, scale)
+    assert np.array_equal(fresh["scores"], rs) and np.array_equal(fresh["idx"], idx)
+    assert np.array_equal(fresh["out"], ref["out"]) and np.array_equal(fresh["lse"], ref["lse"])
+    # every selected position lies in a pool block and is visible
+    assert np.all(np.isin(idx // 8, full["pool"])) and np.all(idx < n) and len(idx) == 512
+    # a short context (ragged last block): every visible position is selected by both
+    m = 301
+    short = O.full_layer(q_idx, w, k_cache, 0, m, q, p, s, win, 0, 128, scale, with_pool=True)
+    re_short = O.reindex_layer(q_idx, w, k_cache, 0, m, short["pool"], q, p, s, win, 0, 128,
+                               scale)
+    assert np.array_equal(short["idx"], np.arange(m))
+    assert np.array_equal(re_short["idx"], np.arange(m))
+    assert np.array_equal(re_short["out"], short["out"])
