@@ -49,13 +49,15 @@ def _load():
     lib.csa2_block_pool.argtypes = [I, P, L, P, I, I, P, L, P, Z, P]
     lib.csa2_topk.argtypes = [I, P, L, L, P, P, L, I, I, P, I, I, P, L, P, Z, P]
     lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
+    lib.csa2_pool_candidates.argtypes = [I, P, L, P, I, I, P, L, I, P, L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
     for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
               "csa2_index_score", "csa2_index_score_mxfp4", "csa2_block_pool", "csa2_topk", "csa2_pool_topk",
               "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
               "csa2_compress_kv", "csa2_project_index_key", "csa2_quantize_mxfp8",
-              "csa2_index_score_mxfp4_q8", "csa2_index_score_q8", "csa2_index_score_shared_q8"):
+              "csa2_index_score_mxfp4_q8", "csa2_index_score_q8", "csa2_index_score_shared_q8",
+              "csa2_pool_candidates"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -363,6 +365,18 @@ def csa2_pool_topk(block_max, n_visible, pool_blocks, scores, topk_idx, n_keep=2
         _ptr(pool_blocks, torch.int32, "pool_blocks"), pool_blocks.shape[1],
         _ptr(scores, torch.float32, "scores"), scores.shape[1], n_cols, k,
         _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], _stream(stream)))
+
+
+def csa2_pool_candidates(block_max, n_visible, pool_blocks, cand_blocks, n_keep=2048, k=512,
+                         stream=None):
+    """The HSI pool into `pool_blocks` [n_q, >= n_keep] and the Full layer's candidate blocks
+    (the pool blocks that can hold one of its k best entries) into `cand_blocks`
+    [n_q, >= n_keep], both ascending and -1 padded."""
+    _check(lib.csa2_pool_candidates(
+        block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
+        _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), pool_blocks.shape[1], k,
+        _ptr(cand_blocks, torch.int32, "cand_blocks"), cand_blocks.shape[1], _stream(stream)))
 
 
 def csa2_sparse_attn(q, kv_fp4, kv_scale, kv_start, topk_idx, window_kv, swa_start, n_swa,

@@ -538,6 +538,33 @@ int csa2_pool_topk(int n_q, const float* block_max, int64_t ld_bm, const int32_t
                     "csa2_pool_topk");
 }
 
+int csa2_pool_candidates(int n_q, const float* block_max, int64_t ld_bm,
+                         const int32_t* n_visible, int block_size, int n_keep,
+                         int32_t* pool_blocks, int64_t ld_pool, int k, int32_t* cand_blocks,
+                         int64_t ld_cand, void* stream) {
+  const char* fn = "csa2_pool_candidates";
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
+  REQUIRE(n_keep >= 1 && n_keep <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+          "%s: n_keep %d out of range [1, %d]", fn, n_keep, CSA2_MAX_K);
+  REQUIRE(k >= 1 && k < n_keep, CSA2_ERR_INVALID_ARG, "%s: k %d must lie in [1, n_keep)", fn, k);
+  if (n_q == 0) return ok();
+  REQUIRE(block_max && n_visible && pool_blocks && cand_blocks, CSA2_ERR_INVALID_ARG,
+          "%s: null pointer argument", fn);
+  REQUIRE(ld_bm >= 1 && ld_pool >= n_keep && ld_cand >= n_keep, CSA2_ERR_INVALID_ARG,
+          "%s: bad leading dimension (ld_bm %lld, ld_pool %lld, ld_cand %lld)", fn,
+          (long long)ld_bm, (long long)ld_pool, (long long)ld_cand);
+  REQUIRE(aligned(block_max, 16) && ld_bm % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "%s: block_max must be 16-byte aligned with ld_bm a multiple of 4", fn);
+  REQUIRE(aligned(n_visible, 4) && aligned(pool_blocks, 4) && aligned(cand_blocks, 4),
+          CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
+  return hip_status(csa2::launch_block_pool_cand(n_q, block_max, ld_bm, n_visible, n_keep,
+                                                 pool_blocks, ld_pool, k, cand_blocks, ld_cand,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const void* kv_fp4,
                      int64_t kv_fp4_stride, const void* kv_scale, int64_t kv_scale_stride,
                      int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,

@@ -47,6 +47,13 @@ hipError_t launch_pool_topk(int n_q, const float* block_max, int64_t ld_bm,
                             int64_t n_cols, int k, int32_t* topk_idx, int64_t ld_idx,
                             hipStream_t stream);
 
+// The HSI pool plus the Full layer's candidate blocks (a subset of the pool holding every
+// block with one of the k best entries), both ascending and -1 padded to n_keep.
+hipError_t launch_block_pool_cand(int n_q, const float* block_max, int64_t ld_bm,
+                                  const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                                  int64_t ld_pool, int k, int32_t* cand_blocks, int64_t ld_cand,
+                                  hipStream_t stream);
+
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,
                               int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,

@@ -95,12 +95,19 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
   // no load waits on another. A query with no visible row in the cache loads nothing.
   // Reindex rows come through the pool and are resolved before streaming.
   constexpr int NB = IS_PREFETCH + 1;
-  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  bool any = nv > 0 && base >= 0 && base < n_entries;
   int64_t rows[REINDEX ? IS_STEPS_PER_WAVE : 1];
   int64_t slots_unused;
   if (REINDEX) {
+    bool mine = false;
 #pragma unroll
-    for (int st = 0; st < IS_STEPS_PER_WAVE; ++st) rows[st] = row_of(st, slots_unused);
+    for (int st = 0; st < IS_STEPS_PER_WAVE; ++st) {
+      rows[st] = row_of(st, slots_unused);
+      mine |= rows[st] >= 0;
+    }
+    // A wavefront whose slots are all absent (past a compacted candidate list) loads and
+    // multiplies nothing; its slots score -inf.
+    any = any && __ballot(mine) != 0ull;
   }
   auto row_at = [&](int step) -> int64_t {
     int64_t sl;
@@ -173,6 +180,110 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
   // interleaved with the row reads cost read bandwidth.
 #pragma unroll
   for (int step = 0; step < IS_STEPS_PER_WAVE; ++step) {
+    const int64_t slot = slot_at(step);
+    const float sv = sc[step];
+    if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+    if (block_max != nullptr) {
+      float m = sv;
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      if (half == 0 && (n & 7) == 0 && slot < ld)
+        block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
+    }
+  }
+}
+
+
+// Full-mode scoring of E4M3 keys with coalesced row loads. A wavefront step still covers
+// 32 consecutive slots (4 KiB of rows), but each load instruction reads 1 KiB of them
+// contiguously: instruction i gives lane l the 16 bytes 16*(l%8) .. +15 of row 8i + l/8.
+// The pieces go through a per-wavefront LDS buffer (piece c of row r at r*128 +
+// ((c ^ (r%8)) * 16): eight lanes writing one row, or reading one piece of eight rows,
+// cover all banks) and come back as the operand layout of index_score_kernel: lane (n,
+// half) holds bytes 64*half .. +63 of row n. Conversion, products, their order and the
+// epilogue are that kernel's, so every score is bit-identical to it (and to the Reindex
+// form, which rescoring relies on). The row loads run one step ahead.
+__global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_cache, int64_t n_entries, const int64_t* __restrict__ kv_start,
+    const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
+    float* __restrict__ block_max, int64_t ld_bm) {
+  __shared__ u32x4 stage[IS_THREADS / 64][2][256];   // 8 KiB per wavefront
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;
+  const int half = lane >> 5;
+  bf16x8 a[8];
+  const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+  const int64_t base = kv_start[t];
+  const int64_t nv = n_visible[t];
+  constexpr int STEPS = IS_STEPS_FULL;
+  constexpr int TILE = (IS_THREADS / 64) * STEPS * 32;
+  const int64_t tile0 = (int64_t)blockIdx.x * TILE + (int64_t)wave * 32;
+  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  // Slots below `lim` have a row (visible, inside the row width and the cache); an absent
+  // row's piece is read from row `base`, which exists, and masked.
+  int64_t lim = ld < nv ? ld : nv;
+  if (any && n_entries - base < lim) lim = n_entries - base;
+  auto slot_at = [&](int step) -> int64_t { return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n; };
+  const int piece = lane & 7;
+  auto load_step = [&](int step, u32x4 (&g)[4]) {
+    const int64_t s0 = tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t slot = s0 + 8 * i;
+      g[i] = *reinterpret_cast<const u32x4*>(k_cache + (base + (slot < lim ? slot : 0)) * 128 +
+                                             16 * piece);
+    }
+  };
+  u32x4 g[4];
+  float sc[STEPS];
+  if (any) load_step(0, g);
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    float sv = -__builtin_inff();
+    if (any) {
+      u32x4* buf = stage[wave][step & 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        buf[r * 8 + (piece ^ (r & 7))] = g[i];
+      }
+      if (step + 1 < STEPS) load_step(step + 1, g);
+      // LDS operations of one wavefront complete in order; the fences keep the compiler
+      // from moving the reads above the writes.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      u32x4 raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = buf[n * 8 + ((4 * half + i) ^ (n & 7))];
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2]);
+        const u32x2 hi = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2 + 1]);
+        const u32x4 bv = u32x4{lo.x, lo.y, hi.x, hi.y};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
+                                                      0, 0, 0);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+      part += __shfl_xor(part, 32);
+      if (slot_at(step) < lim) sv = part;
+    }
+    sc[step] = sv;
+  }
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
     const int64_t slot = slot_at(step);
     const float sv = sc[step];
     if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
@@ -526,8 +637,11 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
       hipLaunchKernelGGL(index_score_full_wide_fp4_kernel, grid, dim3(IS_THREADS), 0, stream,
                          q_idx, w, k_cache, k_scales, n_entries, kv_start, n_visible, scores,
                          ld, block_max, ld_bm);
+  } else if (reindex) {
+    go(index_score_kernel<true, KF_E4M3>);
   } else {
-    reindex ? go(index_score_kernel<true, KF_E4M3>) : go(index_score_kernel<false, KF_E4M3>);
+    hipLaunchKernelGGL(index_score_full_e4m3_kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
+                       k_cache, n_entries, kv_start, n_visible, scores, ld, block_max, ld_bm);
   }
   return hipGetLastError();
 }

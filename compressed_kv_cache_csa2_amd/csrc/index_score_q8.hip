@@ -95,7 +95,15 @@ __global__ __launch_bounds__(Q8_THREADS) void index_score_q8_kernel(
 #pragma unroll
   for (int st = 0; st < Q8_STEPS; ++st) rows[st] = row_of(st);
   auto row_at = [&](int step) -> int64_t { return rows[step]; };
-  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  bool any = nv > 0 && base >= 0 && base < n_entries;
+  if (REINDEX) {
+    // A wavefront whose slots are all absent (past a compacted candidate list) loads and
+    // multiplies nothing; its slots score -inf.
+    bool mine = false;
+#pragma unroll
+    for (int st = 0; st < Q8_STEPS; ++st) mine |= rows[st] >= 0;
+    any = any && __ballot(mine) != 0ull;
+  }
   // Per step and lane, MXFP4: code bytes 16h .. +15 and 32 + 16h .. +15 of its row and the
   // scale word; E4M3: bytes 64i + 16h .. +15 and 64i + 32 + 16h .. +15 for i = 0, 1.
   constexpr int NKB = FP4K ? 2 : 4;

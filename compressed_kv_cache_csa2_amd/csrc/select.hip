@@ -47,13 +47,14 @@ constexpr uint32_t ALL_TIES = 0xFFFFFFFFu;
 constexpr uint32_t INF_KEY = 0xFF800000u;   // float_key(+inf)
 
 struct SelShared {
-  uint32_t hist[NBINS + 64];           // + one spill bin per lane for keys outside the interval
+  uint32_t hist[NBINS];
   uint32_t wsum[SEL_WAVES];
   uint32_t wabove[SEL_WAVES];
   uint32_t wmin[SEL_WAVES];
   uint32_t wmax[SEL_WAVES];
   uint32_t wcnt[SEL_WAVES];
   uint32_t scal[4];
+  uint32_t scal2[2];
   uint32_t list_n;
   uint32_t lkey[LIST_CAP];
   int32_t cblocks[CAND_BLOCKS_CAP];
@@ -114,14 +115,16 @@ struct KeyRow {
 
 // The interval search. [A, B] is a key interval believed to hold the k-th largest key;
 // one pass histograms the keys inside it into at most 2,048 equal power-of-two bins
-// (keys outside land in per-lane spill bins) and counts the keys above B with a wave
-// ballot. If the k-th largest key lies in [A, B], the interval narrows to the bin holding
+// and counts the keys above B with a wave ballot. If the k-th largest key lies in [A, B], the interval narrows to the bin holding
 // it (each pass divides the span by 2^11); otherwise the caller moves the interval.
 struct Interval {
   uint32_t A, B;
   uint32_t need;   // rank of the k-th largest key within [A, B] (1 = the largest there)
   uint32_t cnt;    // keys in [A, B]
   uint32_t ge;     // keys >= A
+  // Optional second rank k2 < k, answered by the first pass only: t2 becomes a key such
+  // that every key ranked k2 or better is >= t2 and at most cap2 keys are (0: not found).
+  uint32_t k2 = 0u, cap2 = 0u, t2 = 0u;
 };
 
 enum { PASS_NARROWED = 0, PASS_ABOVE = 1, PASS_BELOW = 2 };
@@ -134,7 +137,6 @@ __device__ __forceinline__ int hist_pass(Row& row, uint32_t k, Interval& iv, Sel
   const uint32_t span = B - A;
   const int bits = 32 - __clz(span);                 // span < 2^bits
   const int s = bits > 11 ? bits - 11 : 0;           // (span >> s) < 2048
-  const uint32_t spill = NBINS + lane;               // keys outside [A, B] (and 0) land here
 #pragma unroll
   for (int j = 0; j < BINS_PER_THREAD; ++j) sh.hist[tid + j * SEL_THREADS] = 0;
   __syncthreads();
@@ -145,7 +147,9 @@ __device__ __forceinline__ int hist_pass(Row& row, uint32_t k, Interval& iv, Sel
     for (int r = 0; r < R; ++r) {
       const uint32_t key = row.keys[r];
       const uint32_t d = key - A;                    // A >= 1, so key 0 wraps past span
-      atomicAdd(&sh.hist[d <= span ? d >> s : spill], 1u);
+      // only keys inside [A, B] touch LDS (an interval narrowed around the k-th key holds
+      // few of them, and absent slots none)
+      if (d <= span) atomicAdd(&sh.hist[d >> s], 1u);
       above += __popcll(__ballot(key > B));
     }
   }
@@ -164,20 +168,44 @@ __device__ __forceinline__ int hist_pass(Row& row, uint32_t k, Interval& iv, Sel
   }
   uint32_t total;
   const uint32_t excl = block_exclusive_scan(local, sh, &total);
-  if (n_above >= k) return PASS_ABOVE;                // uniform
-  const uint32_t need = k - n_above;
-  if (need > total) return PASS_BELOW;
+  // The second rank (uniform values): its key lies above B, or in one of this pass's bins
+  // (need2 > 0), whose lower edge is then the threshold.
+  uint32_t need2 = 0u;
+  if (iv.k2 != 0u) {
+    if (n_above >= iv.k2) {
+      iv.t2 = n_above <= iv.cap2 ? B + 1u : 0u;   // B < 0xFFFFFFFF: a key lies above it
+    } else if (iv.k2 - n_above <= total) {
+      need2 = iv.k2 - n_above;
+    }
+    iv.k2 = 0u;
+  }
+  const bool is_above = n_above >= k;
+  const uint32_t need = is_above ? 0u : k - n_above;
+  const bool is_below = !is_above && need > total;
+  if ((is_above || is_below) && need2 == 0u) return is_above ? PASS_ABOVE : PASS_BELOW;   // uniform
   uint32_t hi_keys = total - excl - local;   // keys in bins above this thread's bins
 #pragma unroll
   for (int j = BINS_PER_THREAD - 1; j >= 0; --j) {
-    if (hi_keys < need && need <= hi_keys + h[j]) {
+    if (!is_above && !is_below && hi_keys < need && need <= hi_keys + h[j]) {
       sh.scal[0] = BINS_PER_THREAD * tid + j;
       sh.scal[1] = hi_keys;
       sh.scal[2] = h[j];
     }
+    if (need2 != 0u && hi_keys < need2 && need2 <= hi_keys + h[j]) {
+      sh.scal2[0] = BINS_PER_THREAD * tid + j;
+      sh.scal2[1] = n_above + hi_keys + h[j];     // keys at or above the bin's lower edge
+    }
     hi_keys += h[j];
   }
   __syncthreads();
+  if (need2 != 0u) {
+    const uint32_t ge2 = sh.scal2[1];
+    iv.t2 = ge2 <= iv.cap2 ? (uint32_t)((uint64_t)A + ((uint64_t)sh.scal2[0] << s)) : 0u;
+  }
+  if (is_above || is_below) {
+    __syncthreads();
+    return is_above ? PASS_ABOVE : PASS_BELOW;
+  }
   const uint32_t b = sh.scal[0];
   const uint32_t above_b = sh.scal[1];
   const uint32_t in_b = sh.scal[2];
@@ -406,14 +434,22 @@ __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_
   return out_base;
 }
 
-// Full exact selection of the k best keys of a row.
+// Full exact selection of the k best keys of a row. With k2 > 0, *t2 receives a key
+// threshold that every key ranked k2 or better reaches, reached by at most cap2 keys, taken
+// from the first histogram pass (0 when that pass cannot give one, or every key is kept).
 template <class Row, class Emit>
-__device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& sh, Emit emit) {
+__device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& sh, Emit emit,
+                                               uint32_t k2 = 0u, uint32_t cap2 = 0u,
+                                               uint32_t* t2 = nullptr) {
   uint32_t cnt;
   Interval iv;
   row_prepare(row, cnt, iv, sh);
+  if (t2 != nullptr) *t2 = 0u;
   if (cnt <= k) return emit_ordered(row, 0u, 0u, sh, emit);
+  iv.k2 = k2 < k ? k2 : 0u;
+  iv.cap2 = cap2;
   locate(row, k, iv, (uint32_t)LIST_CAP, 0u, sh);
+  if (t2 != nullptr) *t2 = iv.t2;
   uint32_t tau, n_eq;
   if (iv.A == iv.B) {
     tau = iv.A;
@@ -591,17 +627,18 @@ struct CandSrc {
 // of 32,768 when longer still).
 template <class Src, class Emit>
 __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32_t k, SelShared& sh,
-                                               Emit emit) {
+                                               Emit emit, uint32_t k2 = 0u, uint32_t cap2 = 0u,
+                                               uint32_t* t2 = nullptr) {
   if (n <= (int64_t)SEL_THREADS * 16) {
     KeyRow<Src, 16, false> row(src, n);
-    return select_row(row, k, sh, emit);
+    return select_row(row, k, sh, emit, k2, cap2, t2);
   }
   if (n <= (int64_t)SEL_THREADS * 32) {
     KeyRow<Src, 32, false> row(src, n);
-    return select_row(row, k, sh, emit);
+    return select_row(row, k, sh, emit, k2, cap2, t2);
   }
   KeyRow<Src, 32, true> row(src, n);
-  return select_row(row, k, sh, emit);
+  return select_row(row, k, sh, emit, k2, cap2, t2);
 }
 
 // The HSI pool of one query: the n_keep best of its nb block maxima (the forced block
@@ -612,14 +649,15 @@ __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32
 // levels), so every pool block lies in a kept quad; the pool is then selected among their
 // blocks. This replaces several passes over the row by one.
 __device__ __forceinline__ uint32_t select_pool(const float* bm_row, int64_t nb, int n_keep,
-                                                SelShared& sh) {
+                                                SelShared& sh, uint32_t k2 = 0u,
+                                                uint32_t* t2 = nullptr) {
   const uint32_t kk = (uint32_t)n_keep;
   auto to_obuf = [&](uint32_t rank, uint32_t b) {
     if (rank < kk) sh.obuf[rank] = (int32_t)b;
   };
   if (nb <= (int64_t)SEL_THREADS * 32) {
     const BlockSrc src{bm_row, nb - 1, __builtin_inff()};
-    return select_any(src, nb, kk, sh, to_obuf);
+    return select_any(src, nb, kk, sh, to_obuf, k2, kk, t2);
   }
   const uint32_t nbu = (uint32_t)nb;
   const QuadSrc qsrc{bm_row, nbu - 1u, __builtin_inff(), nbu};
@@ -632,7 +670,7 @@ __device__ __forceinline__ uint32_t select_pool(const float* bm_row, int64_t nb,
   // Element i of the second row is block cblocks[i/4]*4 + i%4.
   return select_any(bsrc, (int64_t)n_c * 4, kk, sh, [&](uint32_t rank, uint32_t i) {
     if (rank < kk) sh.obuf[rank] = sh.cblocks[i >> 2] * 4 + (int32_t)(i & 3u);
-  });
+  }, k2, kk, t2);
 }
 
 // The first min(kept, k) entries of sh.obuf go out, then -1 up to k.
@@ -663,6 +701,22 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
   uint32_t kept = 0;
   bool done = false;
 
+  if (pool_use == 1) {
+    // Slots past the last live pool entry score nothing: the row ends there (a compacted
+    // candidate list fills only its first part).
+    const int32_t* prow = pool_blocks + (int64_t)t * n_pool;
+    int last = -1;
+    for (int i = threadIdx.x; i < n_pool; i += SEL_THREADS) last = prow[i] >= 0 ? i : last;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) last = max(last, __shfl_xor(last, off));
+    if ((threadIdx.x & 63) == 0) sh.wmax[threadIdx.x >> 6] = (uint32_t)(last + 1);
+    __syncthreads();
+    uint32_t live = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_WAVES; ++i) live = umax32(live, sh.wmax[i]);
+    __syncthreads();
+    if ((int64_t)live * 8 < n) n = (int64_t)live * 8;
+  }
   if (pool_use == 2) {
     // Candidates: the slots of the pool's blocks (ascending block ids, so the winners come
     // out in ascending position order; -1 entries are absent).
@@ -761,6 +815,70 @@ __global__ __launch_bounds__(SEL_THREADS) void pool_topk_kernel(
   });
   __syncthreads();
   write_out(sh, kept, k, out + (int64_t)t * ld_idx);
+}
+
+// The HSI pool and, for the Full layer of the same scores, its candidate blocks: the pool
+// blocks whose maximum reaches a threshold that the (k+1)-th best block (the forced block
+// counted first) reaches. A block holding one of the k best entries has fewer than k blocks
+// ranked above it by (maximum desc, id asc), each of which holds a better entry of its own,
+// so it is among the k best real blocks and reaches the threshold. The threshold comes from
+// the pool selection's first histogram pass at no extra pass over the row; when that pass
+// cannot give one, every pool block is a candidate. Candidates keep the pool's ascending
+// order and are -1 padded like it.
+__global__ __launch_bounds__(SEL_THREADS) void block_pool_cand_kernel(
+    const float* __restrict__ block_max, int64_t ld_bm, const int32_t* __restrict__ n_visible,
+    int n_keep, int32_t* __restrict__ pool, int64_t ld_pool, int k,
+    int32_t* __restrict__ cand, int64_t ld_cand) {
+  __shared__ SelShared sh;
+  const int t = blockIdx.x;
+  const int64_t nv = n_visible[t];
+  int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
+  if (nb > ld_bm) nb = ld_bm;
+  const float* bm_row = block_max + (int64_t)t * ld_bm;
+  uint32_t t2 = 0u;
+  const uint32_t kept = select_pool(bm_row, nb, n_keep, sh, (uint32_t)k + 1u, &t2);
+  __syncthreads();
+  int32_t* prow = pool + (int64_t)t * ld_pool;
+  int32_t* crow = cand + (int64_t)t * ld_cand;
+  if (t2 == 0u) {
+    for (int r = threadIdx.x; r < n_keep; r += SEL_THREADS) {
+      const int32_t b = (uint32_t)r < kept ? sh.obuf[r] : -1;
+      prow[r] = b;
+      crow[r] = b;
+    }
+    return;
+  }
+  // Thread tid flags the pool entries of ranks 2*tid and 2*tid + 1 (n_keep <= 2,048), so one
+  // block scan in thread order keeps the candidates in ascending block order.
+  const uint32_t forced = (uint32_t)nb - 1u;
+  uint32_t f[2];
+  int32_t bl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t r = 2u * threadIdx.x + j;
+    bl[j] = r < kept ? sh.obuf[r] : -1;
+    const float v = bl[j] >= 0 ? bm_row[bl[j]] : 0.f;
+    const uint32_t key = bl[j] < 0 ? 0u : block_key(v, (uint32_t)bl[j], forced, __builtin_inff(),
+                                                    (uint32_t)nb);
+    f[j] = key >= t2 ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan(f[0] + f[1], sh, &total);
+  if (f[0]) crow[excl] = bl[0];
+  if (f[1]) crow[excl + f[0]] = bl[1];
+  for (int r = threadIdx.x; r < n_keep; r += SEL_THREADS) {
+    prow[r] = (uint32_t)r < kept ? sh.obuf[r] : -1;
+    if ((uint32_t)r >= total) crow[r] = -1;
+  }
+}
+
+hipError_t launch_block_pool_cand(int n_q, const float* block_max, int64_t ld_bm,
+                                  const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                                  int64_t ld_pool, int k, int32_t* cand_blocks, int64_t ld_cand,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL(block_pool_cand_kernel, dim3(n_q), dim3(SEL_THREADS), 0, stream, block_max,
+                     ld_bm, n_visible, n_keep, pool_blocks, ld_pool, k, cand_blocks, ld_cand);
+  return hipGetLastError();
 }
 
 hipError_t launch_pool_topk(int n_q, const float* block_max, int64_t ld_bm,

@@ -1,8 +1,9 @@
 """Mode routing of CSA2 layers over the C ABI (caller side: buffers only, no arithmetic).
 
 Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_score(FULL, block
-         maxima only) -> block_pool -> index_score over the pool with the same query -> topk
-         among the pool's slots -> sparse_attn
+         maxima only) -> pool_candidates (the pool, and the pool blocks that can hold a Full
+         winner) -> index_score over those candidates with the same query -> topk among
+         their slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
 SWA:     sparse_attn over the sliding window alone (the encoder's first two layers)
@@ -31,6 +32,7 @@ class Buffers:
     scores: torch.Tensor        # f32 [n_q, ld]
     block_max: torch.Tensor     # f32 [n_q, ceil(ld/8)]
     pool: torch.Tensor          # i32 [n_q, 2048]
+    cand: torch.Tensor          # i32 [n_q, 2048] the Full layer's candidate blocks
     re_scores: torch.Tensor     # f32 [n_q, 16384]
     idx: torch.Tensor           # i32 [n_layers, n_q, 512] (index layers write their slot)
     out: torch.Tensor           # bf16 [n_layers, n_q, 64, 512]
@@ -73,6 +75,7 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
         scores=torch.empty((n_q, ld), dtype=torch.float32, device=dev),
         block_max=torch.empty((n_q, (ld + BLOCK - 1) // BLOCK), dtype=torch.float32, device=dev),
         pool=torch.full((n_q, POOL_BLOCKS), -1, dtype=torch.int32, device=dev),
+        cand=torch.full((n_q, POOL_BLOCKS), -1, dtype=torch.int32, device=dev),
         re_scores=torch.empty((n_q, POOL_BLOCKS * BLOCK), dtype=torch.float32, device=dev),
         idx=torch.full((n_l, n_q, k), -1, dtype=torch.int32, device=dev),
         out=torch.empty((n_l, n_q, 64, 512), dtype=torch.bfloat16, device=dev),
@@ -166,16 +169,18 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
         elif lay.mode == "full":
             if wl.with_pool:
                 # Decoder Full layer: the pass over the whole context writes only the block
-                # maxima; the pool holds every Full-layer winner, so the Top-K is taken over
-                # the pool's slots, rescored with this layer's own indexer query (the same
-                # scores, bit for bit, at 2 MiB of reads per query).
+                # maxima. The pool holds every Full-layer winner, and so do the pool's
+                # candidate blocks (those ranked near the top by maximum, about a quarter of
+                # the pool), so the Top-K is taken among the candidates' slots rescored with
+                # this layer's own indexer query: the same scores, bit for bit.
                 index_score(wl, C.FULL, lay, None, buf.block_max,
                             ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
-                C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool, n_keep=POOL_BLOCKS,
-                                  stream=stream)
-                index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.pool,
+                C.csa2_pool_candidates(buf.block_max, wl.n_visible, buf.pool, buf.cand,
+                                       n_keep=POOL_BLOCKS, k=k, stream=stream)
+                index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.cand,
                             stream=stream, buf=buf)
-                C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.pool, stream=stream)
+                C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.cand,
+                            stream=stream)
             else:
                 index_score(wl, C.FULL, lay, buf.scores, buf.block_max, stream=stream, buf=buf)
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,

@@ -364,6 +364,28 @@ int csa2_pool_topk(int n_q, const float* block_max, int64_t ld_bm,
                    const float* scores, int64_t ld_scores, int64_t n_cols, int k,
                    int32_t* topk_idx, int64_t ld_idx, void* stream);
 
+/* The HSI pool and the Full layer's candidate blocks in one call ([V41F-BLOG] 2.3.2 and
+ * 2.3.4, "How does the Full Mode layer build the candidate pool"; [V41F-ARCH] 3).
+ * pool_blocks receives exactly what csa2_block_pool writes for the same arguments.
+ * cand_blocks receives a subset of the pool, ascending and -1 padded to n_keep, that holds
+ * every block containing one of the k best entries of the scores whose 8-slot maxima
+ * block_max holds: a block holding such an entry has fewer than k blocks ranked above it
+ * by (maximum desc, id asc), each holding a better entry of its own, so it is among the k
+ * best blocks; the candidates are the pool blocks whose maximum reaches a threshold that
+ * the (k+1)-th best block (the forced latest block counted first) reaches. Rescoring the
+ * candidates' slots (csa2_index_score REINDEX with cand_blocks as the pool) and taking the
+ * Top-K among them (csa2_topk, CSA2_POOL_SLOTS) therefore gives exactly the Full layer's
+ * Top-K over its whole score row, from a quarter of the pool's rows. The threshold comes
+ * from the pool selection's first histogram pass; when that pass cannot give one, every
+ * pool block is a candidate (the result is the same, only slower).
+ *   block_max, ld_bm, n_visible, block_size, n_keep, pool_blocks, ld_pool: as
+ *       csa2_block_pool; 1 <= k < n_keep; cand_blocks [n_q,ld_cand] int32, ld_cand >= n_keep.
+ * Caller-owned device buffers, no scratch; errors as csa2_block_pool. */
+int csa2_pool_candidates(int n_q, const float* block_max, int64_t ld_bm,
+                         const int32_t* n_visible, int block_size, int n_keep,
+                         int32_t* pool_blocks, int64_t ld_pool, int k, int32_t* cand_blocks,
+                         int64_t ld_cand, void* stream);
+
 /* Joint sparse attention over the selected entries and the sliding window
  * ([V41F-BLOG] 2.2.2, 3.3.1 and 3.3.2 "the readout"; [V41F-ARCH] 2 and 4).
  * For query t let S be {valid positions in topk_idx[t, 0..k)} plus the SWA rows

@@ -25,7 +25,7 @@ def test_header_symbols_are_exported(C):
                      "csa2_index_score_shared", "csa2_index_score_bf16",
                      "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
                      "csa2_quantize_mxfp8", "csa2_index_score_mxfp4_q8", "csa2_index_score_q8",
-                     "csa2_index_score_shared_q8",
+                     "csa2_index_score_shared_q8", "csa2_pool_candidates",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
@@ -266,3 +266,23 @@ def test_sparse_attn_rejections_and_workspace(C):
     assert attn(out=None) == 1
     assert attn(ld_idx=100) == 1
     assert attn(n_q=0, q=None) == 0
+
+
+def _pool_cand(C, **kw):
+    a = dict(n_q=1, block_max=FAKE, ld_bm=4, n_visible=FAKE, block_size=8, n_keep=2048,
+             pool_blocks=FAKE, ld_pool=2048, k=512, cand_blocks=FAKE, ld_cand=2048, stream=None)
+    a.update(kw)
+    return C.lib.csa2_pool_candidates(*a.values())
+
+
+def test_pool_candidates_rejections(C):
+    assert _pool_cand(C, k=2048) == 1                        # k must stay below n_keep
+    assert _pool_cand(C, k=0) == 1
+    assert _pool_cand(C, n_keep=4096) == 1
+    assert _pool_cand(C, block_size=4) == 2
+    assert _pool_cand(C, cand_blocks=None) == 1
+    assert _pool_cand(C, block_max=FAKE + 4) == 1           # not 16-byte aligned
+    assert _pool_cand(C, ld_bm=6) == 1                      # not a multiple of 4
+    assert _pool_cand(C, ld_pool=100) == 1
+    assert _pool_cand(C, ld_cand=100) == 1
+    assert _pool_cand(C, n_q=0) == 0                        # nothing to do

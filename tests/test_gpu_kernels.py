@@ -139,6 +139,38 @@ def test_index_score_reindex_parity(C, dev):
         assert_scores_close(got[t], ref, terms, f"query {t}")
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "mxfp4"])
+def test_full_pass_and_reindex_form_score_bit_identically(C, dev, fmt):
+    """The Full pass and the Reindex form give every position the same fp32 score, bit for
+    bit: rescoring a pool (or the Full layer's candidate blocks) with the Full layer's own
+    query reproduces the values its block maxima came from. Ragged, empty and multi-tile
+    sequences; the pool lists every block of each sequence."""
+    from compressed_kv_cache_csa2_amd import synth
+    nvis = [0, 1, 7, 4099, 2500, 9000, 16384, 8 * 2048 - 3]
+    wl = synth.make_decode("fr", len(nvis), 0, ("full",), False, 0, n_visible=nvis, kv_gap=5,
+                           seed=6, mxfp4=(fmt == "mxfp4")).to(dev)
+    lay = wl.layers[0]
+    ld = 16384
+    full = torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev)
+    pool = torch.full((wl.n_q, 2048), -1, dtype=torch.int32)
+    for t, nv in enumerate(nvis):
+        nb = (nv + 7) // 8
+        pool[t, :nb] = torch.arange(nb, dtype=torch.int32)
+    pool = pool.to(dev)
+    re = torch.empty((wl.n_q, 16384), dtype=torch.float32, device=dev)
+    if fmt == "mxfp4":
+        C.csa2_index_score_mxfp4(C.FULL, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                                 wl.n_visible, full)
+        C.csa2_index_score_mxfp4(C.REINDEX, lay.q_idx, lay.w, wl.k_codes, wl.k_scales,
+                                 wl.kv_start, wl.n_visible, re, pool_blocks=pool)
+    else:
+        C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, full)
+        C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                           re, pool_blocks=pool)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int32), re.view(torch.int32))
+
+
 # --------------------------------------------------------------------------- selection
 
 def _score_rows(kind, n_q, n, seed):

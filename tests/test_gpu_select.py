@@ -1,0 +1,97 @@
+"""The decoder Full layer's pool and candidate blocks (csa2_pool_candidates) on the GPU: the
+pool equals csa2_block_pool's bit for bit, the candidates are a subset of it, and the Top-K
+taken among the candidates' rescored slots equals, bit for bit, the Top-K among all pool
+slots (the route the chain tests hold to the oracle) and the oracle's whole-row selection."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.csa2_oracle as O
+from tests.parity_util import assert_set_band, band_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _both_routes(wl, k=512):
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import layers
+    buf = layers.alloc_buffers(wl)
+    lay = wl.layers[0]
+    C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, None,
+                       buf.block_max, ld_scores=buf.scores.shape[1])
+    dev = wl.k_cache.device
+    pool_a = torch.full_like(buf.pool, -5)
+    cand = torch.full_like(buf.pool, -5)
+    idx_a = torch.full((wl.n_q, k), -5, dtype=torch.int32, device=dev)
+    C.csa2_pool_candidates(buf.block_max, wl.n_visible, pool_a, cand, n_keep=2048, k=k)
+    sc_a = torch.empty_like(buf.re_scores)
+    C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, sc_a,
+                       pool_blocks=cand)
+    C.csa2_topk(sc_a, idx_a, k=k, pool_blocks=cand)
+    pool_b = torch.full_like(buf.pool, -5)
+    idx_b = torch.full_like(idx_a, -5)
+    C.csa2_block_pool(buf.block_max, wl.n_visible, pool_b, n_keep=2048)
+    C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
+                       buf.re_scores, pool_blocks=pool_b)
+    C.csa2_topk(buf.re_scores, idx_b, k=k, pool_blocks=pool_b)
+    torch.cuda.synchronize()
+    return pool_a, cand, idx_a, pool_b, idx_b
+
+
+def _check_candidates(pool, cand):
+    for p, c in zip(pool.cpu().numpy(), cand.cpu().numpy()):
+        n = int((c >= 0).sum())
+        assert np.all(c[n:] == -1) and np.all(np.diff(c[:n]) > 0)
+        assert np.all(np.isin(c[:n], p[p >= 0]))
+
+
+@pytest.mark.parametrize("n_visible", [
+    [40000, 17000, 3001, 16384 + 8],            # ragged, short, exactly 2048 blocks + 1
+    [1, 8, 9, 4104, 4097, 0, 520, 262144],      # tiny, empty, 513 blocks, full 256K
+    [300000, 270001],                           # above 32,768 blocks: the quad path
+])
+def test_candidate_route_equals_pool_route(dev, n_visible):
+    from compressed_kv_cache_csa2_amd import synth
+    wl = synth.make_decode("fs", len(n_visible), 0, ("full",), True, 32, n_visible=n_visible,
+                           kv_gap=5, seed=41).to(dev)
+    for k in (512, 100):
+        pool_a, cand, idx_a, pool_b, idx_b = _both_routes(wl, k)
+        assert torch.equal(pool_a, pool_b), k
+        assert torch.equal(idx_a, idx_b), k
+        _check_candidates(pool_a, cand)
+        # long contexts: the threshold engages and keeps about k + 1 blocks
+        for t, nv in enumerate(n_visible):
+            if nv > 8 * 2048 * 4:
+                assert int((cand[t] >= 0).sum()) <= 2 * (k + 1), (t, k)
+
+
+def test_candidates_with_ties_everywhere(dev):
+    """Keys repeated in runs of 64 rows give equal scores and equal block maxima: ties go to
+    the lower position and lower block in both routes, and the result equals the oracle's
+    whole-row selection (up to the acceptance band between different runs' values)."""
+    from compressed_kv_cache_csa2_amd import synth
+    n_visible = [50000, 7777]
+    wl = synth.make_decode("fs_ties", 2, 0, ("full",), True, 0, n_visible=n_visible, kv_gap=3,
+                           seed=42).to(dev)
+    kc = wl.k_cache
+    wl.k_cache.copy_(kc[::64].repeat_interleave(64, dim=0)[:kc.shape[0]])
+    pool_a, cand, idx_a, pool_b, idx_b = _both_routes(wl)
+    assert torch.equal(pool_a, pool_b) and torch.equal(idx_a, idx_b)
+    _check_candidates(pool_a, cand)
+    lay = wl.layers[0]
+    q = lay.q_idx[0:2].view(torch.int16).cpu().numpy().view(np.uint16)
+    w = lay.w[0:2].cpu().numpy()
+    kch = wl.k_cache.cpu().numpy()
+    for t in range(2):
+        st = int(wl.kv_start[t])
+        s = O.full_scores(q[t], w[t], kch, st, n_visible[t], n_visible[t])
+        got = idx_a[t].cpu().numpy()
+        kth, band = band_of(s, 512)
+        assert_set_band(got[got >= 0], O.topk_slots(s, 512), lambda p: s[p], kth, band,
+                        f"query {t}")
+        bm = O.block_max(s[:n_visible[t]])
+        bm[(n_visible[t] - 1) // 8] = np.inf
+        kb, bb = band_of(bm, 2048)
+        gp = pool_a[t].cpu().numpy()
+        assert_set_band(gp[gp >= 0], O.hsi_pool(s, n_visible[t]), lambda b: bm[b], kb, bb,
+                        f"pool {t}")
