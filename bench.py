@@ -266,63 +266,71 @@ def cpu_baseline(wl, target_s, max_q):
         t_total += time.perf_counter() - t0
         done += 1
         np.asarray(r["out"]).sum()
+    note = (" with the bf16 indexer query (the oracle's MXFP8-query scorers are not timed)"
+            if wl.q8 else "")
     return {"value": done / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "threads": "BLAS threads of the numpy oracle (threadpoolctl)",
+            "host": host_cpu(),
             "sample": f"{done} query stacks of {wl.name} (its {wl.n_q} queries taken in order, "
-                      f"cycled), whole layer stack per query, {t_total:.1f} s of oracle time"}
+                      f"cycled), whole layer stack per query{note}, {t_total:.1f} s of oracle "
+                      "time"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    # A step is ~0.4 ms: 50 warm-up steps let clocks and caches settle, 200 timed steps
-    # take under 0.1 s.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode_256k")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="replay the step this long before the warm-up steps (clock settle)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--breakdown", action="store_true", help="per-call timings to stderr")
-    ap.add_argument("--coarse", choices=("hsi", "hisa"), default="hsi",
-                    help="coarse filter of the indexer layers (pooled stacks)")
-    ap.add_argument("--recall", action="store_true",
-                    help="also report needle recall under the block-mean filter")
-    ap.add_argument("--profile-kernel", type=int, default=0, metavar="N",
-                    help="only launch the Full indexer and a 1 GiB copy N times (counter runs)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode batch "
-              "shards by sequence with no exchange, so one GPU's throughput is the figure; see "
-              "the design notes for the multi-GPU layout.", file=sys.stderr)
-        sys.exit(2)
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo), its logical CPU count and the CPUs this
+    process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "allowed_cpus": allowed}
 
+
+def kernel_label(wl, hisa):
+    """Name of the dominant kernel as the step launches it."""
+    if hisa:
+        return "index_score_kernel (block-mean scorer, bf16 mean keys)"
+    keys = "MXFP4 keys" if wl.k_codes is not None else "E4M3 keys"
+    if wl.shared_start is not None:
+        name = ("index_score_shared_q8_kernel (grouped Full indexer, " if wl.q8 else
+                "index_score_shared_kernel (grouped Full indexer, ") + keys
+    elif wl.q8:
+        name = "index_score_q8_kernel (Full-layer indexer, " + keys + ", MXFP8 query"
+    elif wl.k_codes is not None:
+        name = "index_score_full_wide_fp4_kernel (Full-layer indexer, " + keys
+    else:
+        name = "index_score_full_e4m3_kernel (Full-layer indexer, " + keys
+    return name + (", block maxima only)" if wl.with_pool else ")")
+
+
+def measure(name, args, C, layers, synth, with_breakdown=False, with_recall=False):
+    """One workload: the step timed as a replayed HIP graph and the dominant kernel timed
+    back to back, both with HIP events on the step's stream. Returns the figures and the
+    workload."""
     import torch
-
-    from compressed_kv_cache_csa2_amd import csa2 as C
-    from compressed_kv_cache_csa2_amd import layers, synth
-
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
     t0 = time.time()
-    wl = synth.make_workload(args.workload, device=dev)
+    wl = synth.make_workload(name, device="cuda:0")
     torch.cuda.synchronize()
-    print(f"[bench] {args.workload}: generated in {time.time() - t0:.1f} s", file=sys.stderr,
-          flush=True)
+    print(f"[bench] {name}: generated in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     buf = layers.alloc_buffers(wl)
     hisa = args.coarse == "hisa"
     means = None
-    if hisa or args.recall:
+    if hisa or with_recall:
         if not wl.with_pool or wl.k_codes is not None:
             print("--coarse hisa / --recall need a pooled decoder workload with E4M3 keys",
                   file=sys.stderr)
             sys.exit(2)
         means = layers.build_block_means(wl)
         torch.cuda.synchronize()
-    if args.profile_kernel:
-        profile_kernels(wl, buf, C, args.profile_kernel, means if hisa else None)
-        return
     stream = torch.cuda.Stream()
     copies = rotated_copies(wl)
     turn = [0]
@@ -375,7 +383,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall "
+    print(f"[bench] {name}: timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (host wall "
           f"{wall / args.steps * 1e6:.1f} us/step)", file=sys.stderr, flush=True)
 
     # Dominant kernel: the Full-layer indexer (or the block-mean scorer), launched back to
@@ -400,78 +408,150 @@ def main():
     idx_bytes = hisa_stage1_bytes(wl) if hisa else indexer_bytes_per_launch(wl)
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
 
-    if args.breakdown:
-        names = []
-        evs = []
-        with torch.cuda.stream(stream):
-            for li, lay in enumerate(wl.layers):
-                for part in ("score", "pool", "rescore", "topk", "attn"):
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    if hisa and lay.mode in ("full", "reindex") and part != "attn":
-                        if part == "score":
-                            C.csa2_index_score_bf16(C.FULL, lay.q_idx, lay.w, means.km,
-                                                    means.km_start, means.n_blocks,
-                                                    buf.block_max, stream=stream)
-                        elif part == "pool":
-                            C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool,
-                                              stream=stream)
-                        elif part == "rescore":
-                            layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                               pool_blocks=buf.pool, stream=stream, buf=buf)
-                        else:
-                            C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
-                                        stream=stream)
-                    elif part == "score" and lay.mode == "full":
-                        full_indexer(wl, buf, C, stream=stream)
-                    elif part == "rescore" and lay.mode == "full" and wl.with_pool:
-                        layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                           pool_blocks=buf.cand, stream=stream, buf=buf)
-                    elif part == "score" and lay.mode == "reindex":
-                        layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
-                                           pool_blocks=buf.pool, stream=stream, buf=buf)
-                    elif part == "topk" and lay.mode == "full" and wl.with_pool:
-                        C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.cand,
-                                    stream=stream)
-                    elif part == "topk" and lay.mode == "full":
-                        C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
-                                    block_max=buf.block_max, stream=stream)
-                    elif part == "topk" and lay.mode == "reindex":
-                        C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool, stream=stream)
-                    elif part == "pool" and lay.mode == "full" and wl.with_pool:
-                        C.csa2_pool_candidates(buf.block_max, wl.n_visible, buf.pool, buf.cand,
-                                               stream=stream)
-                    elif part == "attn":
-                        _, kv_fp4, kv_scale = wl.cache(lay.group)
-                        C.csa2_sparse_attn(lay.q, kv_fp4, kv_scale, wl.kv_start,
-                                           buf.published[li], lay.window_kv, lay.swa_start,
-                                           lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
-                                           buf.workspace, stream=stream)
-                    else:
-                        continue
-                    b.record(stream)
-                    names.append(f"L{li}:{lay.mode}:{part}")
-                    evs.append((a, b))
-        torch.cuda.synchronize()
-        for n, (a, b) in zip(names, evs):
-            print(f"[bench] {n:24s} {a.elapsed_time(b) * 1e3:9.1f} us", file=sys.stderr)
-
-    recall = needle_recall(wl, buf, C, means if args.recall else None) \
+    if with_breakdown:
+        breakdown(wl, buf, C, layers, stream, hisa, means)
+    recall = needle_recall(wl, buf, C, means if with_recall else None) \
         if wl.planted is not None else None
     step_bytes = algorithmic_bytes(wl, coarse=args.coarse)
-    value = wl.n_q / (ms_step * 1e-3)
+    res = {
+        "workload": wl.name, "wl": wl, "copies": len(copies), "ms_step": ms_step,
+        "value": wl.n_q / (ms_step * 1e-3),
+        "step_bytes": step_bytes,
+        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None if hisa else measured_traffic(wl.name),
+                     "kernel": kernel_label(wl, hisa), "launch_us": idx_us,
+                     "bytes_per_launch": idx_bytes},
+        "recall": recall,
+    }
+    if wl.shared_start is not None:
+        pairs = int(wl.n_visible.to(torch.int64).sum())
+        tflops = pairs * FLOPS_PER_PAIR / (idx_us * 1e-6) / 1e12
+        peak = PEAK_FP8_TFLOPS if wl.q8 else PEAK_BF16_TFLOPS
+        res["roofline"].update({"bound": "mfma", "achieved": tflops, "peak": peak,
+                                "unit": "TFLOP/s", "frac": tflops / peak,
+                                "flops_per_launch": pairs * FLOPS_PER_PAIR})
+        del res["roofline"]["bytes_per_launch"]
+    return res
+
+
+def breakdown(wl, buf, C, layers, stream, hisa, means):
+    """Per-call event timings of one eager pass of the stack, to stderr."""
+    import torch
+    names = []
+    evs = []
+    with torch.cuda.stream(stream):
+        for li, lay in enumerate(wl.layers):
+            for part in ("score", "pool", "rescore", "topk", "attn"):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                if hisa and lay.mode in ("full", "reindex") and part != "attn":
+                    if part == "score":
+                        C.csa2_index_score_bf16(C.FULL, lay.q_idx, lay.w, means.km,
+                                                means.km_start, means.n_blocks,
+                                                buf.block_max, stream=stream)
+                    elif part == "pool":
+                        C.csa2_block_pool(buf.block_max, wl.n_visible, buf.pool,
+                                          stream=stream)
+                    elif part == "rescore":
+                        layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
+                                           pool_blocks=buf.pool, stream=stream, buf=buf)
+                    else:
+                        C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool,
+                                    stream=stream)
+                elif part == "score" and lay.mode == "full":
+                    full_indexer(wl, buf, C, stream=stream)
+                elif part == "rescore" and lay.mode == "full" and wl.with_pool:
+                    layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
+                                       pool_blocks=buf.cand, stream=stream, buf=buf)
+                elif part == "score" and lay.mode == "reindex":
+                    layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
+                                       pool_blocks=buf.pool, stream=stream, buf=buf)
+                elif part == "topk" and lay.mode == "full" and wl.with_pool:
+                    C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.cand,
+                                stream=stream)
+                elif part == "topk" and lay.mode == "full":
+                    C.csa2_topk(buf.scores, buf.idx[li], n_valid=wl.n_visible,
+                                block_max=buf.block_max, stream=stream)
+                elif part == "topk" and lay.mode == "reindex":
+                    C.csa2_topk(buf.re_scores, buf.idx[li], pool_blocks=buf.pool, stream=stream)
+                elif part == "pool" and lay.mode == "full" and wl.with_pool:
+                    C.csa2_pool_candidates(buf.block_max, wl.n_visible, buf.pool, buf.cand,
+                                           stream=stream)
+                elif part == "attn":
+                    _, kv_fp4, kv_scale = wl.cache(lay.group)
+                    C.csa2_sparse_attn(lay.q, kv_fp4, kv_scale, wl.kv_start,
+                                       buf.published[li], lay.window_kv, lay.swa_start,
+                                       lay.n_swa, wl.softmax_scale, buf.out[li], buf.lse[li],
+                                       buf.workspace, stream=stream)
+                else:
+                    continue
+                b.record(stream)
+                names.append(f"L{li}:{lay.mode}:{part}")
+                evs.append((a, b))
+    torch.cuda.synchronize()
+    for n, (a, b) in zip(names, evs):
+        print(f"[bench] {n:24s} {a.elapsed_time(b) * 1e3:9.1f} us", file=sys.stderr)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    # A step is ~0.4 ms: 50 warm-up steps let clocks and caches settle, 200 timed steps
+    # take under 0.1 s.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_256k")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="replay the step this long before the warm-up steps (clock settle)")
+    ap.add_argument("--no-1m", action="store_true",
+                    help="skip the decode_1m sub-record of the default decode_256k run")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--breakdown", action="store_true", help="per-call timings to stderr")
+    ap.add_argument("--coarse", choices=("hsi", "hisa"), default="hsi",
+                    help="coarse filter of the indexer layers (pooled stacks)")
+    ap.add_argument("--recall", action="store_true",
+                    help="also report needle recall under the block-mean filter")
+    ap.add_argument("--profile-kernel", type=int, default=0, metavar="N",
+                    help="only launch the Full indexer and a 1 GiB copy N times (counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the decode batch "
+              "shards by sequence with no exchange, so one GPU's throughput is the figure; see "
+              "the design notes for the multi-GPU layout.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import layers, synth
+
+    torch.cuda.set_device(0)
+    if args.profile_kernel:
+        wl = synth.make_workload(args.workload, device="cuda:0")
+        buf = layers.alloc_buffers(wl)
+        means = layers.build_block_means(wl) if args.coarse == "hisa" else None
+        torch.cuda.synchronize()
+        profile_kernels(wl, buf, C, args.profile_kernel, means)
+        return
+    head = measure(args.workload, args, C, layers, synth, with_breakdown=args.breakdown,
+                   with_recall=args.recall)
+    wl = head["wl"]
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, 100000)
     line = {
         "metric": "decode queries/sec + achieved HBM GB/s (% of peak)",
-        "value": value,
+        "value": head["value"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -482,37 +562,31 @@ def main():
                    "sliding_window": 128, "pool_blocks": 2048 if wl.with_pool else 0,
                    "indexer_keys": "mxfp4" if wl.k_codes is not None else "e4m3",
                    "indexer_query": "mxfp8" if wl.q8 else "bf16",
-                   "coarse_filter": args.coarse, "rotated_copies": len(copies),
+                   "coarse_filter": args.coarse, "rotated_copies": head["copies"],
                    "launch": "eager" if args.no_graph else "hip_graph"},
-        "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
-        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "step_algorithmic_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None if hisa else measured_traffic(wl.name),
-                     "kernel": "index_score_kernel (block-mean scorer, bf16 mean keys)" if hisa
-                               else ("index_score_q8_kernel (Full-layer indexer, MXFP4 keys, "
-                                     "MXFP8 query" if wl.q8 else
-                                     "index_score_full_wide_fp4_kernel (Full-layer indexer, "
-                                     "MXFP4 keys" if wl.k_codes is not None else
-                                     "index_score_kernel (Full-layer indexer, E4M3 keys")
-                               + (", block maxima only)" if wl.with_pool else ")"),
-                     "launch_us": idx_us, "bytes_per_launch": idx_bytes},
+        "step_hbm_gbps": head["step_hbm_gbps"],
+        "step_hbm_frac": head["step_hbm_gbps"] / PEAK_HBM_GBPS,
+        "step_algorithmic_bytes": head["step_bytes"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
     }
-    if wl.shared_start is not None:
-        pairs = int(wl.n_visible.to(torch.int64).sum())
-        tflops = pairs * FLOPS_PER_PAIR / (idx_us * 1e-6) / 1e12
-        peak = PEAK_FP8_TFLOPS if wl.q8 else PEAK_BF16_TFLOPS
-        line["roofline"].update({"bound": "mfma", "achieved": tflops, "peak": peak,
-                                 "unit": "TFLOP/s", "frac": tflops / peak,
-                                 "flops_per_launch": pairs * FLOPS_PER_PAIR,
-                                 "kernel": "index_score_shared_q8_kernel (grouped Full indexer, "
-                                           "MXFP8 query, fp8 MFMA)" if wl.q8 else
-                                           "index_score_shared_kernel (grouped Full indexer)"})
-        del line["roofline"]["bytes_per_launch"]
-    if recall is not None:
-        line["needle_recall"] = recall
+    if head["recall"] is not None:
+        line["needle_recall"] = head["recall"]
+    if args.workload == "decode_256k" and args.coarse == "hsi" and not args.no_1m:
+        # The metric's 1M half: the same measurement of decode_1m (64 queries of 1,048,576
+        # entries each) in the same run, on the same GPU.
+        del head, wl
+        torch.cuda.empty_cache()
+        sub = measure("decode_1m", args, C, layers, synth)
+        line["decode_1m"] = {
+            "value": sub["value"], "unit": "queries/s", "ms_per_step": sub["ms_step"],
+            "queries": sub["wl"].n_q, "context_entries": sub["wl"].n_ctx,
+            "step_hbm_gbps": sub["step_hbm_gbps"],
+            "step_hbm_frac": sub["step_hbm_gbps"] / PEAK_HBM_GBPS,
+            "step_algorithmic_bytes": sub["step_bytes"],
+            "roofline": sub["roofline"],
+            "needle_recall": sub["recall"],
+        }
     print(json.dumps(line), flush=True)
 
 

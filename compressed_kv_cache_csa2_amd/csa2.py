@@ -93,6 +93,39 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _dims(t, name, *dims):
+    """Raise ValueError unless tensor t (skipped when None) has len(dims) dimensions, each
+    equal to the given int, at least v for a ('>=', v) pair, or anything for None. The C
+    ABI receives only pointers and a few sizes, so every other shape is checked here,
+    before any pointer is passed on."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dim() != len(dims):
+        raise ValueError(f"{name}: expected {len(dims)} dimensions, got shape {tuple(t.shape)}")
+    for i, (have, want) in enumerate(zip(t.shape, dims)):
+        if want is None:
+            continue
+        if isinstance(want, tuple):
+            if have < want[1]:
+                raise ValueError(f"{name}: dimension {i} is {have}, needs >= {want[1]}")
+        elif have != want:
+            raise ValueError(f"{name}: dimension {i} is {have}, expected {want} "
+                             f"(shape {tuple(t.shape)})")
+
+
+def _index_common(name, n_q, w, kv_start, n_visible, scores, block_max, pool_blocks, ld_scores):
+    """Shapes shared by the indexer calls: per-query vectors of n_q, score rows of n_q, block
+    maxima covering ceil(ld/8) blocks, a pool of n_q rows."""
+    _dims(w, f"{name}: w", n_q, 32)
+    _dims(kv_start, f"{name}: kv_start", n_q)
+    _dims(n_visible, f"{name}: n_visible", n_q)
+    _dims(scores, f"{name}: scores", n_q, None)
+    _dims(block_max, f"{name}: block_max", n_q, (">=", (ld_scores + 7) // 8))
+    _dims(pool_blocks, f"{name}: pool_blocks", n_q, None)
+
+
 def version() -> str:
     return lib.csa2_version().decode()
 
@@ -130,6 +163,12 @@ def csa2_index_score_mxfp4_q8(mode, q_codes, q_scales, w, k_codes, k_scales, kv_
         ld_scores = scores.shape[1]
     elif ld_scores is None:
         raise ValueError("csa2_index_score_mxfp4_q8: ld_scores is required when scores is None")
+    _dims(q_codes, "csa2_index_score_mxfp4_q8: q_codes", n_q, 32, 128)
+    _dims(q_scales, "csa2_index_score_mxfp4_q8: q_scales", n_q, 32, 4)
+    _dims(k_codes, "csa2_index_score_mxfp4_q8: k_codes", None, 64)
+    _dims(k_scales, "csa2_index_score_mxfp4_q8: k_scales", k_codes.shape[0], 4)
+    _index_common("csa2_index_score_mxfp4_q8", n_q, w, kv_start, n_visible, scores, block_max,
+                  pool_blocks, ld_scores)
     _check(lib.csa2_index_score_mxfp4_q8(
         mode, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
         _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
@@ -150,6 +189,11 @@ def csa2_index_score_q8(mode, q_codes, q_scales, w, k_cache, kv_start, n_visible
         ld_scores = scores.shape[1]
     elif ld_scores is None:
         raise ValueError("csa2_index_score_q8: ld_scores is required when scores is None")
+    _dims(q_codes, "csa2_index_score_q8: q_codes", n_q, 32, 128)
+    _dims(q_scales, "csa2_index_score_q8: q_scales", n_q, 32, 4)
+    _dims(k_cache, "csa2_index_score_q8: k_cache", None, 128)
+    _index_common("csa2_index_score_q8", n_q, w, kv_start, n_visible, scores, block_max,
+                  pool_blocks, ld_scores)
     _check(lib.csa2_index_score_q8(
         mode, n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
         _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
@@ -165,6 +209,12 @@ def csa2_index_score_shared_q8(q_codes, q_scales, w, k_cache, kv_start: int, n_v
                                block_max=None, stream=None):
     """csa2_index_score_shared with an MXFP8 query over E4M3 keys."""
     n_q = q_codes.shape[0]
+    _dims(q_codes, "csa2_index_score_shared_q8: q_codes", n_q, 32, 128)
+    _dims(q_scales, "csa2_index_score_shared_q8: q_scales", n_q, 32, 4)
+    _dims(k_cache, "csa2_index_score_shared_q8: k_cache", None, 128)
+    _dims(scores, "csa2_index_score_shared_q8: scores", n_q, None)
+    _index_common("csa2_index_score_shared_q8", n_q, w, None, n_visible, scores, block_max,
+                  None, scores.shape[1])
     _check(lib.csa2_index_score_shared_q8(
         n_q, q_codes.shape[1], q_codes.shape[2], _ptr(q_codes, torch.uint8, "q_codes"),
         _ptr(q_scales, torch.uint8, "q_scales"), _ptr(w, torch.float32, "w"),
@@ -205,6 +255,7 @@ def csa2_write_latent(x, rows, kv_fp4, kv_scale, stream=None):
         raise ValueError("csa2_write_latent: x must be [n, 512] with one row index per row")
     if kv_fp4.shape[0] != kv_scale.shape[0]:
         raise ValueError("csa2_write_latent: kv_fp4 and kv_scale row counts differ")
+    _dims(rows, "csa2_write_latent: rows", x.shape[0])
     _check(lib.csa2_write_latent(x.shape[0], _ptr(x, torch.bfloat16, "x"),
                                  _ptr(rows, torch.int64, "rows"), p_fp4, s_fp4, p_sc, s_sc,
                                  kv_fp4.shape[0], _stream(stream)))
@@ -216,6 +267,7 @@ def csa2_write_e4m3(x, rows, dst, stream=None):
     p, st = _rows_view(dst, d, "dst")
     if x.dim() != 2 or rows.shape[0] != x.shape[0]:
         raise ValueError("csa2_write_e4m3: x must be [n, d] with one row index per row")
+    _dims(rows, "csa2_write_e4m3: rows", x.shape[0])
     _check(lib.csa2_write_e4m3(x.shape[0], d, _ptr(x, torch.bfloat16, "x"),
                                _ptr(rows, torch.int64, "rows"), p, st, dst.shape[0],
                                _stream(stream)))
@@ -227,6 +279,9 @@ def csa2_write_mxfp4_key(x, rows, k_codes, k_scales, stream=None):
         raise ValueError("csa2_write_mxfp4_key: x must be [n, 128] with one row index per row")
     if k_codes.shape[0] != k_scales.shape[0]:
         raise ValueError("csa2_write_mxfp4_key: k_codes and k_scales row counts differ")
+    _dims(k_codes, "csa2_write_mxfp4_key: k_codes", None, 64)
+    _dims(k_scales, "csa2_write_mxfp4_key: k_scales", None, 4)
+    _dims(rows, "csa2_write_mxfp4_key: rows", x.shape[0])
     _check(lib.csa2_write_mxfp4_key(x.shape[0], _ptr(x, torch.bfloat16, "x"),
                                     _ptr(rows, torch.int64, "rows"),
                                     _ptr(k_codes, torch.uint8, "k_codes"),
@@ -244,6 +299,10 @@ def csa2_index_score(mode, q_idx, w, k_cache, kv_start, n_visible, scores, block
         ld_scores = scores.shape[1]
     elif ld_scores is None:
         raise ValueError("csa2_index_score: ld_scores is required when scores is None")
+    _dims(q_idx, "csa2_index_score: q_idx", n_q, 32, 128)
+    _dims(k_cache, "csa2_index_score: k_cache", None, 128)
+    _index_common("csa2_index_score", n_q, w, kv_start, n_visible, scores, block_max,
+                  pool_blocks, ld_scores)
     _check(lib.csa2_index_score(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
@@ -259,6 +318,11 @@ def csa2_index_score_shared(q_idx, w, k_cache, kv_start: int, n_visible, scores,
     """Full-mode scores of queries that all read the cache from row kv_start (a host int),
     each up to its own n_visible."""
     n_q = q_idx.shape[0]
+    _dims(q_idx, "csa2_index_score_shared: q_idx", n_q, 32, 128)
+    _dims(k_cache, "csa2_index_score_shared: k_cache", None, 128)
+    _dims(scores, "csa2_index_score_shared: scores", n_q, None)
+    _index_common("csa2_index_score_shared", n_q, w, None, n_visible, scores, block_max, None,
+                  scores.shape[1])
     _check(lib.csa2_index_score_shared(
         n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
@@ -280,6 +344,11 @@ def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visibl
         raise ValueError("csa2_index_score_mxfp4: ld_scores is required when scores is None")
     if k_codes.shape[0] != k_scales.shape[0]:
         raise ValueError("csa2_index_score_mxfp4: k_codes and k_scales row counts differ")
+    _dims(q_idx, "csa2_index_score_mxfp4: q_idx", n_q, 32, 128)
+    _dims(k_codes, "csa2_index_score_mxfp4: k_codes", None, 64)
+    _dims(k_scales, "csa2_index_score_mxfp4: k_scales", k_codes.shape[0], 4)
+    _index_common("csa2_index_score_mxfp4", n_q, w, kv_start, n_visible, scores, block_max,
+                  pool_blocks, ld_scores)
     _check(lib.csa2_index_score_mxfp4(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_codes, torch.uint8, "k_codes"),
@@ -300,6 +369,10 @@ def csa2_block_mean_keys(k_cache, kv_start, n_visible, km, km_start, n_blocks, m
     n_q = kv_start.shape[0]
     if km.dim() != 2 or km.shape[1] != 128:
         raise ValueError("csa2_block_mean_keys: km must be [rows, 128]")
+    _dims(k_cache, "csa2_block_mean_keys: k_cache", None, 128)
+    _dims(n_visible, "csa2_block_mean_keys: n_visible", n_q)
+    _dims(km_start, "csa2_block_mean_keys: km_start", n_q)
+    _dims(n_blocks, "csa2_block_mean_keys: n_blocks", n_q)
     if max_blocks is None:
         max_blocks = max(1, km.shape[0])
     _check(lib.csa2_block_mean_keys(
@@ -319,6 +392,10 @@ def csa2_index_score_bf16(mode, q_idx, w, k_rows, kv_start, n_visible, scores, b
         ld_scores = scores.shape[1]
     elif ld_scores is None:
         raise ValueError("csa2_index_score_bf16: ld_scores is required when scores is None")
+    _dims(q_idx, "csa2_index_score_bf16: q_idx", n_q, 32, 128)
+    _dims(k_rows, "csa2_index_score_bf16: k_rows", None, 128)
+    _index_common("csa2_index_score_bf16", n_q, w, kv_start, n_visible, scores, block_max,
+                  pool_blocks, ld_scores)
     _check(lib.csa2_index_score_bf16(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_rows, torch.bfloat16, "k_rows"), k_rows.shape[0],
@@ -331,6 +408,10 @@ def csa2_index_score_bf16(mode, q_idx, w, k_rows, kv_start, n_visible, scores, b
 
 def csa2_block_pool(block_max, n_visible, pool_blocks, n_keep=2048, stream=None):
     """HSI pool block ids (ascending, -1 padded) into `pool_blocks` [n_q, >= n_keep]."""
+    n_q = block_max.shape[0]
+    _dims(block_max, "csa2_block_pool: block_max", n_q, None)
+    _dims(n_visible, "csa2_block_pool: n_visible", n_q)
+    _dims(pool_blocks, "csa2_block_pool: pool_blocks", n_q, (">=", n_keep))
     _check(lib.csa2_block_pool(
         block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
         _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
@@ -345,6 +426,12 @@ def csa2_topk(scores, topk_idx, k=512, n_cols=None, n_valid=None, block_max=None
     n_cols = scores.shape[1] if n_cols is None else n_cols
     if pool_use is None:
         pool_use = POOL_NONE if pool_blocks is None else POOL_SLOTS
+    n_q = scores.shape[0]
+    _dims(scores, "csa2_topk: scores", n_q, None)
+    _dims(topk_idx, "csa2_topk: topk_idx", n_q, (">=", k))
+    _dims(n_valid, "csa2_topk: n_valid", n_q)
+    _dims(block_max, "csa2_topk: block_max", n_q, (">=", (n_cols + 7) // 8))
+    _dims(pool_blocks, "csa2_topk: pool_blocks", n_q, None)
     _check(lib.csa2_topk(
         scores.shape[0], _ptr(scores, torch.float32, "scores"), scores.shape[1], n_cols,
         _ptr(n_valid, torch.int32, "n_valid"), _ptr(block_max, torch.float32, "block_max"),
@@ -359,6 +446,12 @@ def csa2_pool_topk(block_max, n_visible, pool_blocks, scores, topk_idx, n_keep=2
     """csa2_block_pool then csa2_topk among the pool's candidates, in one kernel: pool ids
     into `pool_blocks` [n_q, >= n_keep] and positions into `topk_idx` [n_q, >= k]."""
     n_cols = scores.shape[1] if n_cols is None else n_cols
+    n_q = block_max.shape[0]
+    _dims(block_max, "csa2_pool_topk: block_max", n_q, None)
+    _dims(n_visible, "csa2_pool_topk: n_visible", n_q)
+    _dims(pool_blocks, "csa2_pool_topk: pool_blocks", n_q, (">=", n_keep))
+    _dims(scores, "csa2_pool_topk: scores", n_q, None)
+    _dims(topk_idx, "csa2_pool_topk: topk_idx", n_q, (">=", k))
     _check(lib.csa2_pool_topk(
         block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
         _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
@@ -372,6 +465,11 @@ def csa2_pool_candidates(block_max, n_visible, pool_blocks, cand_blocks, n_keep=
     """The HSI pool into `pool_blocks` [n_q, >= n_keep] and the Full layer's candidate blocks
     (the pool blocks that can hold one of its k best entries) into `cand_blocks`
     [n_q, >= n_keep], both ascending and -1 padded."""
+    n_q = block_max.shape[0]
+    _dims(block_max, "csa2_pool_candidates: block_max", n_q, None)
+    _dims(n_visible, "csa2_pool_candidates: n_visible", n_q)
+    _dims(pool_blocks, "csa2_pool_candidates: pool_blocks", n_q, (">=", n_keep))
+    _dims(cand_blocks, "csa2_pool_candidates: cand_blocks", n_q, (">=", n_keep))
     _check(lib.csa2_pool_candidates(
         block_max.shape[0], _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
         _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
@@ -389,8 +487,20 @@ def csa2_sparse_attn(q, kv_fp4, kv_scale, kv_start, topk_idx, window_kv, swa_sta
     if need and ws is None:
         raise ValueError(f"csa2_sparse_attn: a workspace of {need} bytes is required")
     for name, t, row in (("kv_fp4", kv_fp4, 256), ("kv_scale", kv_scale, 32)):
-        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 \
+                or t.shape[1] < row:
             raise ValueError(f"{name}: expected a device uint8 [rows, >= {row}] view")
+    if kv_scale.shape[0] != kv_fp4.shape[0]:
+        raise ValueError("csa2_sparse_attn: kv_fp4 and kv_scale row counts differ")
+    _dims(q, "csa2_sparse_attn: q", n_q, 64, 512)
+    _dims(kv_start, "csa2_sparse_attn: kv_start", n_q)
+    if k > 0:
+        _dims(topk_idx, "csa2_sparse_attn: topk_idx", n_q, (">=", k))
+    _dims(window_kv, "csa2_sparse_attn: window_kv", None, 512)
+    _dims(swa_start, "csa2_sparse_attn: swa_start", n_q)
+    _dims(n_swa, "csa2_sparse_attn: n_swa", n_q)
+    _dims(out, "csa2_sparse_attn: out", n_q, 64, 512)
+    _dims(lse, "csa2_sparse_attn: lse", n_q, 64)
     _check(lib.csa2_sparse_attn(
         n_q, q.shape[1], q.shape[2], _ptr(q, torch.bfloat16, "q"),
         kv_fp4.data_ptr(), kv_fp4.stride(0), kv_scale.data_ptr(), kv_scale.stride(0),

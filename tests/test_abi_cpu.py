@@ -286,3 +286,66 @@ def test_pool_candidates_rejections(C):
     assert _pool_cand(C, ld_pool=100) == 1
     assert _pool_cand(C, ld_cand=100) == 1
     assert _pool_cand(C, n_q=0) == 0                        # nothing to do
+
+
+def test_wrappers_reject_mis_shaped_tensors_before_any_call(C):
+    """The Python binding checks every tensor's shape against the query count and the
+    compiled sizes before a pointer reaches the library (host tensors: a well-shaped one
+    would be refused as not on the device, also before any call)."""
+    import torch
+    f32, i32, i64, u8, bf = torch.float32, torch.int32, torch.int64, torch.uint8, torch.bfloat16
+    n = 4
+    q = torch.zeros((n, 32, 128), dtype=bf)
+    w = torch.zeros((n, 32), dtype=f32)
+    kc = torch.zeros((100, 128), dtype=u8)
+    ks = torch.zeros((n,), dtype=i64)
+    nv = torch.zeros((n,), dtype=i32)
+    sc = torch.zeros((n, 64), dtype=f32)
+    bm = torch.zeros((n, 8), dtype=f32)
+    cases = [
+        lambda: C.csa2_index_score(0, q, w[:3], kc, ks, nv, sc),                   # w rows
+        lambda: C.csa2_index_score(0, q, w, kc, ks[:2], nv, sc),                   # kv_start
+        lambda: C.csa2_index_score(0, q, w, kc, ks, nv, sc[:3]),                   # score rows
+        lambda: C.csa2_index_score(0, q, w, kc, ks, nv, sc, torch.zeros((n, 7))),  # bm width
+        lambda: C.csa2_index_score(0, q[:, :, :64], w, kc, ks, nv, sc),            # q width
+        lambda: C.csa2_index_score(0, q, w, kc[:, :64], ks, nv, sc),               # key width
+        lambda: C.csa2_index_score_q8(0, torch.zeros((n, 32, 128), dtype=u8),
+                                      torch.zeros((n, 32, 3), dtype=u8), w, kc, ks, nv, sc),
+        lambda: C.csa2_index_score_mxfp4(0, q, w, torch.zeros((100, 64), dtype=u8),
+                                         torch.zeros((99, 4), dtype=u8), ks, nv, sc),
+        lambda: C.csa2_index_score_shared(q, w, kc, 0, nv[:3], sc),
+        lambda: C.csa2_index_score_shared_q8(torch.zeros((n, 32, 128), dtype=u8),
+                                             torch.zeros((n, 32, 4), dtype=u8), w[:1], kc, 0,
+                                             nv, sc),
+        lambda: C.csa2_block_pool(bm, nv[:3], torch.zeros((n, 2048), dtype=i32)),
+        lambda: C.csa2_block_pool(bm, nv, torch.zeros((n, 100), dtype=i32)),
+        lambda: C.csa2_pool_candidates(bm, nv, torch.zeros((n, 2048), dtype=i32),
+                                       torch.zeros((n, 2047), dtype=i32)),
+        lambda: C.csa2_topk(sc, torch.zeros((n, 100), dtype=i32), k=512),
+        lambda: C.csa2_topk(sc, torch.zeros((3, 512), dtype=i32)),
+        lambda: C.csa2_sparse_attn(torch.zeros((n, 64, 512), dtype=bf),
+                                   torch.zeros((10, 256), dtype=u8),
+                                   torch.zeros((9, 32), dtype=u8), ks,
+                                   torch.zeros((n, 512), dtype=i32),
+                                   torch.zeros((10, 512), dtype=u8), ks, nv, 0.1,
+                                   torch.zeros((n, 64, 512), dtype=bf)),
+        lambda: C.csa2_sparse_attn(torch.zeros((n, 64, 512), dtype=bf),
+                                   torch.zeros((10, 256), dtype=u8),
+                                   torch.zeros((10, 32), dtype=u8), ks,
+                                   torch.zeros((n, 100), dtype=i32),
+                                   torch.zeros((10, 512), dtype=u8), ks, nv, 0.1,
+                                   torch.zeros((n, 64, 512), dtype=bf)),
+        lambda: C.csa2_sparse_attn(torch.zeros((n, 64, 512), dtype=bf),
+                                   torch.zeros((10, 256), dtype=u8),
+                                   torch.zeros((10, 32), dtype=u8), ks,
+                                   torch.zeros((n, 512), dtype=i32),
+                                   torch.zeros((10, 512), dtype=u8), ks, nv, 0.1,
+                                   torch.zeros((n, 64, 256), dtype=bf)),
+        lambda: C.csa2_write_mxfp4_key(torch.zeros((5, 128), dtype=bf), torch.zeros(5, dtype=i64),
+                                       torch.zeros((10, 32), dtype=u8),
+                                       torch.zeros((10, 4), dtype=u8)),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError) as e:
+            case()
+        assert "device tensor" not in str(e.value), f"case {i} passed the shape checks"

@@ -110,10 +110,31 @@ def test_small_encoder_schedule(dev):
     assert not torch.equal(buf.idx[2], buf.idx[8])
 
 
-@pytest.mark.parametrize("kind", ["hisa", "encoder"])
+@pytest.mark.parametrize("kind", ["prefill", "encoder"])
+def test_small_shared_sequence_stacks_with_the_mxfp8_query(dev, kind):
+    """The grouped MXFP8-query indexer (queries sharing one sequence) through whole stacks:
+    a small chunked prefill and the encoder schedule with the query quantised per layer,
+    every layer of sampled queries checked against the oracle's MXFP8-query scores, its
+    Top-K and attention over the GPU's indices."""
+    from compressed_kv_cache_csa2_amd import layers, synth
+    if kind == "prefill":
+        wl = synth.make_prefill("small_prefill_q8", n_q=70, n_entries=5000, seed=27).to(dev)
+    else:
+        wl = synth.make_encoder("small_encoder_q8", n_q=48, n_entries=3000, seed=28).to(dev)
+    wl.q8 = True
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    queries = (0, 23, wl.n_q - 1)
+    compared = sum(check_query(wl, buf, t) for t in queries)
+    assert compared == len(queries) * len(wl.layers)
+
+
+@pytest.mark.parametrize("kind", ["hisa", "encoder", "encoder_q8"])
 def test_graph_replay_of_the_other_stacks(dev, kind):
-    """The block-mean filter stack and the encoder schedule captured in a HIP graph give
-    the eager result bitwise on every replay (eager work in between)."""
+    """The block-mean filter stack and the encoder schedule (also with the MXFP8 query)
+    captured in a HIP graph give the eager result bitwise on every replay (eager work in
+    between)."""
     from compressed_kv_cache_csa2_amd import layers, synth
     if kind == "hisa":
         wl = synth.make_decode("g_hisa", 3, 20000, synth.DECODE_LAYERS, True, 16, seed=25).to(dev)
@@ -121,6 +142,7 @@ def test_graph_replay_of_the_other_stacks(dev, kind):
         kw = dict(coarse="hisa", means=means)
     else:
         wl = synth.make_encoder("g_enc", n_q=40, n_entries=2500, seed=26).to(dev)
+        wl.q8 = kind == "encoder_q8"
         kw = {}
     eager = layers.alloc_buffers(wl)
     layers.run_layers(wl, eager, **kw)
