@@ -302,7 +302,7 @@ def kernel_label(wl, hisa):
     keys = "MXFP4 keys" if wl.k_codes is not None else "E4M3 keys"
     if wl.shared_start is not None:
         name = ("index_score_shared_q8_kernel (grouped Full indexer, " if wl.q8 else
-                "index_score_shared_kernel (grouped Full indexer, ") + keys
+                "index_score_shared2_kernel (grouped Full indexer, ") + keys
     elif wl.q8:
         name = "index_score_q8_kernel (Full-layer indexer, " + keys + ", MXFP8 query"
     elif wl.k_codes is not None:

@@ -411,38 +411,64 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Queries that share one sequence (chunked prefill: every query reads the same cache rows
-// from kv_start, each up to its own causal n_visible). A workgroup scores SQ_QT queries
-// (SQ_QW per wavefront, their MFMA operands and head weights held in registers) against
-// one 4,096-row tile. Per 32-row step the four wavefronts each load and convert a quarter
-// of the rows' channels into an LDS buffer in B-operand order (double-buffered, one barrier
-// per step); then every wavefront reads the step's 8 operands once and runs its queries'
-// products on them. Rows are read and converted once per SQ_QT queries, and the LDS
-// traffic is one 8 KiB operand read per wavefront and step.
-constexpr int SQ_QW = 2;
-constexpr int SQ_QT = (IS_THREADS / 64) * SQ_QW;
-constexpr int SQ_TILE = 4096;
+// from kv_start, each up to its own causal n_visible). A workgroup scores SQ2_QT queries
+// (SQ2_QW per wavefront, their MFMA operands and head weights held in registers) against
+// one 4,096-row tile; rows are read and converted once per SQ2_QT queries.
+// SS steps of 32 rows are staged per LDS buffer (double-buffered), so one barrier serves
+// SS * QW * 8 products per wavefront. Wavefront w loads and converts k-blocks
+// 2w and 2w+1 of every row of a stage (bytes 64*half + 16*w .. +15 of row n), one stage
+// ahead of its use. Per step the QW product chains are issued k-block by k-block and their
+// epilogues follow, so one query's ReLU and head sum run while the other queries' products
+// are in the matrix core. Products, their order and the epilogue arithmetic are those of
+// the per-query kernel: identical scores.
+constexpr int SQ2_QW = 3;
+constexpr int SQ2_SS = 4;
+constexpr int SQ2_QT = (IS_THREADS / 64) * SQ2_QW;
+constexpr int SQ2_TILE = 4096;
 
-__global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
+// max(x, 0) in one integer instruction: a float with the sign bit set (negative, or -0) is
+// a negative integer and becomes +0, anything else is kept. For every finite x the value
+// is fmaxf(x, 0) up to the sign of a zero, which leaves the weighted head sum unchanged.
+__device__ __forceinline__ float relu1(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Largest of v over the 8 lanes of each aligned group of 8 (valid in each group's first
+// lane): two quad exchanges and one rotation by 12 within a 16-lane row (lane i reads lane
+// i + 4), taken on integer keys whose signed order is the float order (so the maxima need
+// no NaN canonicalisation); equal to the fmaxf reduction for scores, which are never -0.
+__device__ __forceinline__ float group8_max(float v) {
+  int k = __float_as_int(v);
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x12C, 0xF, 0xF, false));
+  k ^= (k >> 31) & 0x7FFFFFFF;
+  return __int_as_float(k);
+}
+
+template <int QW, int SS>
+__global__ __launch_bounds__(IS_THREADS, 2) void index_score_shared2_kernel(
     int n_q, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, int64_t n_entries, int64_t kv_start,
     const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
     float* __restrict__ block_max, int64_t ld_bm) {
-  __shared__ u32x4 bsh[2][8][64];   // converted rows of a step: k-block kb, lane
-  __shared__ int nv_sh[SQ_QT];
+  constexpr int QT = (IS_THREADS / 64) * QW;
+  __shared__ u32x4 bsh[2][SS][8][64];   // converted rows of a stage: step, k-block, lane
+  __shared__ int nv_sh[QT];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int half = lane >> 5;
-  const int t0 = blockIdx.y * SQ_QT;
+  const int t0 = blockIdx.y * QT;
 
-  // This wavefront's queries: operands (channels 64*half + 8*kb .. +7 of head n), weights.
-  bf16x8 a[SQ_QW][8];
-  float wr[SQ_QW][16];
-  int nvq[SQ_QW];
+  bf16x8 a[QW][8];
+  float wr[QW][16];
+  int nvq[QW];
 #pragma unroll
-  for (int j = 0; j < SQ_QW; ++j) {
-    const int t = t0 + SQ_QW * wave + j;
+  for (int j = 0; j < QW; ++j) {
+    const int t = t0 + QW * wave + j;
     const bool ok = t < n_q;
     const uint16_t* qrow = q_idx + ((int64_t)(ok ? t : 0) * 32 + n) * 128 + 64 * half;
 #pragma unroll
@@ -457,84 +483,116 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_shared_kernel(
   }
   if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < SQ_QW; ++j) nv_sh[SQ_QW * wave + j] = nvq[j];
+    for (int j = 0; j < QW; ++j) nv_sh[QW * wave + j] = nvq[j];
   }
   __syncthreads();
   int nv_max = 0;
 #pragma unroll
-  for (int q = 0; q < SQ_QT; ++q) nv_max = max(nv_max, nv_sh[q]);
+  for (int q = 0; q < QT; ++q) nv_max = max(nv_max, nv_sh[q]);
 
-  const int64_t tile0 = (int64_t)blockIdx.x * SQ_TILE;
-  constexpr int STEPS = SQ_TILE / 32;
-  const bool any = nv_max > 0 && kv_start >= 0 && kv_start < n_entries;
-  // Lane (n, half) of wavefront w loads bytes 64*half + 16*w .. +15 of row n of a step:
-  // k-blocks 2w and 2w+1 of the B operand. A row is read when some query of the group sees
-  // it; each query masks its own.
-  auto row_at = [&](int step) -> int64_t {
-    const int64_t slot = tile0 + (int64_t)step * 32 + n;
-    if (slot >= ld || slot >= nv_max) return -1;
-    const int64_t row = kv_start + slot;
-    return (row >= 0 && row < n_entries) ? row : -1;
-  };
-  // steps whose rows are in flight: the rows come mostly from cache (every query group reads
-  // the same sequence), and 16 steps of lead hide that latency at two waves per SIMD
-  constexpr int PF = 16;
-  u32x4 raw[PF];
-  auto load = [&](int step) -> u32x4 {
-    const int64_t r = row_at(step);
-    return *reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : kv_start) * 128 + 64 * half +
-                                           16 * wave);
-  };
-  if (any) {
+  const int64_t tile0 = (int64_t)blockIdx.x * SQ2_TILE;
+  constexpr int STAGES = SQ2_TILE / (32 * SS);
+  // Slots below lim have a row that some query of the group sees; each query masks its own.
+  int64_t lim = ld < nv_max ? ld : nv_max;
+  if (n_entries - kv_start < lim) lim = n_entries - kv_start;
+  const bool any = nv_max > 0 && kv_start >= 0 && kv_start < n_entries && lim > tile0;
+  // Stores through buffer descriptors over this tile's part of each query's score and
+  // block-maximum rows: a lane with nothing to store (the upper half-wave, a lane that is
+  // not first of its 8-slot block, a slot past the row or a query past n_q) uses an offset
+  // past the descriptor's end, which the hardware drops, so no store is predicated.
+  constexpr uint32_t DROP = 0xFFFFFFFFu;
+  const int64_t tile_slots = ld - tile0 < SQ2_TILE ? ld - tile0 : SQ2_TILE;   // > 0
+  __amdgpu_buffer_rsrc_t rs_s[QW], rs_b[QW];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) raw[i] = load(i);
+  for (int j = 0; j < QW; ++j) {
+    const int t = t0 + QW * wave + j;
+    const bool ok = t < n_q;
+    rs_s[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(ok ? t : 0) * ld + tile0,
+                                                (short)0, ok ? (int)(tile_slots * 4) : 0,
+                                                0x00020000);
+    rs_b[j] = __builtin_amdgcn_make_buffer_rsrc(
+        block_max + (block_max != nullptr ? (int64_t)(ok ? t : 0) * ld_bm + (tile0 >> 3) : 0),
+        (short)0, (ok && block_max != nullptr) ? (int)(((tile_slots + 7) >> 3) * 4) : 0,
+        0x00020000);
   }
-#pragma unroll 1
-  for (int step0 = 0; step0 < STEPS; step0 += PF) {
+  auto store = [&](int j, int64_t slot, float sv) {
+    const uint32_t rel = (uint32_t)(slot - tile0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), rs_s[j],
+                                          half == 0 ? 4u * rel : DROP, 0, 0);
+    if (block_max != nullptr) {
+      const float m = group8_max(sv);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_b[j],
+                                            (half == 0 && (n & 7) == 0) ? 4u * (rel >> 3) : DROP,
+                                            0, 0);
+    }
+  };
+  if (!any) {   // no row of this tile is visible to the group: every slot scores -inf
+    for (int step = 0; step < SQ2_TILE / 32; ++step)
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int step = step0 + i;
-      const int buf = step & 1;
-      const int64_t slot = tile0 + (int64_t)step * 32 + n;
-      const bool row_ok = any && row_at(step) >= 0;
-      if (any) {
-        const u32x4 v = raw[i];
-        if (step + PF < STEPS) raw[i] = load(step + PF);
-        const u32x2 l0 = e4m3x4_to_bf16x4(v.x), h0 = e4m3x4_to_bf16x4(v.y);
-        const u32x2 l1 = e4m3x4_to_bf16x4(v.z), h1 = e4m3x4_to_bf16x4(v.w);
-        bsh[buf][2 * wave][lane] = u32x4{l0.x, l0.y, h0.x, h0.y};
-        bsh[buf][2 * wave + 1][lane] = u32x4{l1.x, l1.y, h1.x, h1.y};
-      }
-      __syncthreads();
+      for (int j = 0; j < QW; ++j) store(j, tile0 + (int64_t)step * 32 + n, -__builtin_inff());
+    return;
+  }
+  // Visible limits relative to the tile, clamped to [0, tile]: slot < x <=> rel < x_rel.
+  auto rel_of = [&](int64_t x) -> int {
+    const int64_t r = x - tile0;
+    return r < 0 ? 0 : (r > SQ2_TILE ? SQ2_TILE : (int)r);
+  };
+  const int lim_rel = rel_of(lim);
+  int nvq_rel[QW];
+#pragma unroll
+  for (int j = 0; j < QW; ++j) nvq_rel[j] = rel_of(nvq[j]);
+  u32x4 raw[SS];
+  auto load = [&](int stage) {
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      const int64_t slot = tile0 + (int64_t)(stage * SS + s) * 32 + n;
+      raw[s] = *reinterpret_cast<const u32x4*>(k_cache + (kv_start + (slot < lim ? slot : 0)) * 128 +
+                                               64 * half + 16 * wave);
+    }
+  };
+  load(0);
+#pragma unroll 1
+  for (int stage = 0; stage < STAGES; ++stage) {
+    const int buf = stage & 1;
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      const u32x4 v = raw[s];
+      const u32x2 l0 = e4m3x4_to_bf16x4(v.x), h0 = e4m3x4_to_bf16x4(v.y);
+      const u32x2 l1 = e4m3x4_to_bf16x4(v.z), h1 = e4m3x4_to_bf16x4(v.w);
+      bsh[buf][s][2 * wave][lane] = u32x4{l0.x, l0.y, h0.x, h0.y};
+      bsh[buf][s][2 * wave + 1][lane] = u32x4{l1.x, l1.y, h1.x, h1.y};
+    }
+    if (stage + 1 < STAGES) load(stage + 1);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      // slot - tile0 and the limits relative to the tile fit in 32 bits
+      const int rel = (stage * SS + s) * 32 + n;
+      const int64_t slot = tile0 + rel;
+      const bool row_ok = rel < lim_rel;
       u32x4 b[8];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) b[kb] = bsh[buf][kb][lane];
+      for (int kb = 0; kb < 8; ++kb) b[kb] = bsh[buf][s][kb][lane];
+      f32x16 acc[QW];
 #pragma unroll
-      for (int j = 0; j < SQ_QW; ++j) {
-        const int t = t0 + SQ_QW * wave + j;
-        float sv = -__builtin_inff();
-        if (any) {
-          f32x16 acc = {};
+      for (int j = 0; j < QW; ++j) acc[j] = f32x16{};
+      // k-block-major: each operand read feeds QW products, and the chains interleave
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kb], __builtin_bit_cast(bf16x8, b[kb]),
-                                                          acc, 0, 0, 0);
-          // the same accumulation order as the per-query kernel: identical scores
-          float part = 0.f;
+      for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) part += wr[j][r] * fmaxf(acc[r], 0.f);
-          part += __shfl_xor(part, 32);
-          if (row_ok && slot < nvq[j]) sv = part;
-        }
-        if (t < n_q && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
-        if (block_max != nullptr) {
-          float m = sv;
-          m = fmaxf(m, __shfl_xor(m, 1));
-          m = fmaxf(m, __shfl_xor(m, 2));
-          m = fmaxf(m, __shfl_xor(m, 4));
-          if (t < n_q && half == 0 && (n & 7) == 0 && slot < ld)
-            block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
-        }
+        for (int j = 0; j < QW; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kb], __builtin_bit_cast(bf16x8, b[kb]),
+                                                           acc[j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        // the same accumulation order as the per-query kernel: identical scores
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += wr[j][r] * relu1(acc[j][r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                         __float_as_uint(part), false, false);
+        part += __uint_as_float(half ? sw[0] : sw[1]);   // the other half-wave's heads
+        store(j, slot, (row_ok && rel < nvq_rel[j]) ? part : -__builtin_inff());
       }
     }
   }
@@ -608,9 +666,10 @@ hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float
                                      const uint8_t* k_cache, int64_t n_entries, int64_t kv_start,
                                      const int32_t* n_visible, float* scores, int64_t ld,
                                      float* block_max, int64_t ld_bm, hipStream_t stream) {
-  dim3 grid((unsigned)((ld + SQ_TILE - 1) / SQ_TILE), (unsigned)((n_q + SQ_QT - 1) / SQ_QT));
-  hipLaunchKernelGGL(index_score_shared_kernel, grid, dim3(IS_THREADS), 0, stream, n_q, q_idx, w,
-                     k_cache, n_entries, kv_start, n_visible, scores, ld, block_max, ld_bm);
+  dim3 grid((unsigned)((ld + SQ2_TILE - 1) / SQ2_TILE), (unsigned)((n_q + SQ2_QT - 1) / SQ2_QT));
+  hipLaunchKernelGGL((index_score_shared2_kernel<SQ2_QW, SQ2_SS>), grid, dim3(IS_THREADS), 0,
+                     stream, n_q, q_idx, w, k_cache, n_entries, kv_start, n_visible, scores, ld,
+                     block_max, ld_bm);
   return hipGetLastError();
 }
 
