@@ -173,6 +173,8 @@ __device__ u32x4 sbuf_load_b128(__amdgpu_buffer_rsrc_t rsrc, int index, int offs
                                 int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
 __device__ u32x2 sbuf_load_b64(__amdgpu_buffer_rsrc_t rsrc, int index, int offset, int soffset,
                                int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+__device__ uint32_t sbuf_load_b32(__amdgpu_buffer_rsrc_t rsrc, int index, int offset, int soffset,
+                                  int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.i32");
 
 // Buffer descriptor over n_rows records of `stride` bytes (stride < 16,384) from `base`.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rows_rsrc(const void* base, int stride,

@@ -510,6 +510,300 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
         Lh > 0.f ? (Mh + __log2f(Lh)) * AT_LN2 : -__builtin_inff();
 }
 
+// --------------------------------------------------------------------------------------
+// Many queries (chunked prefill, the encoder): one workgroup per query covering all 64 heads,
+// so each attended row is gathered and converted once instead of once per head group.
+// Items go in slices of 32 (the window's slices first, then the selected entries'); per
+// slice:
+//   - wavefront w gathers items 4w .. 4w+3 (lane (item, p): channels 32p .. 32p+31) and
+//     stores them converted to fp16 (exact, as above) in an LDS tile, one 1,056-byte row per
+//     item, its 16-byte pieces swizzled (piece c of row r at c ^ ((r / 8) % 2)) so that the
+//     row reads of the logit product and the transposed reads of the value product are
+//     free of bank conflicts; barrier;
+//   - wavefront (head tile w % 4, item half w / 4) computes S (16 items x 16 heads) with
+//     v_mfma_f32_16x16x32_f16 (A = tile rows, B = its heads' queries, held in registers),
+//     turns it into weights p = 2^(l - ref) with a per-head reference ref and stores them,
+//     already in the value product's B layout, to LDS; barrier;
+//   - wavefront w accumulates O^T for output channels 64w .. 64w+63 of all 64 heads over the
+//     slice's 32 items with v_mfma_f32_16x16x16f16 (A = the tile read transposed, B = p),
+//     so no partial outputs are merged at the end.
+// The reference of a head is the largest logit of the first slice with a valid item (the
+// two item halves combine through LDS once); a later logit more than 15 above it (fp16
+// weights stay below 2^15) marks the pass, which is repeated with every head's largest
+// logit as the reference (rare; the result does not depend on the reference).
+constexpr int AH_WAVES = 8;
+constexpr int AH_THREADS = 64 * AH_WAVES;
+constexpr int AH_SLICE = 32;
+constexpr int AH_ROW = 528;        // fp16 elements per tile row (1,056 bytes)
+constexpr int AH_MIN_Q = 256;      // from this many queries on, this kernel runs
+
+struct AttnHeadsShared {
+  uint16_t tile[2][AH_SLICE * AH_ROW];   // 2 x 33 KiB: converted rows of a slice
+  u32x2 pw[2][4][2][64];                 // weights: buffer, head tile, item half, lane
+  uint32_t valid[2][AH_SLICE];           // item validity of a slice
+  float xch[2][64];                      // per item half and head: maxima or sums
+  int flag;                              // a logit overflowed the reference
+};
+
+// Element offset of channel ch (a multiple of 4) of tile row r, with the piece swizzle.
+__device__ __forceinline__ int ah_off(int r, int ch) {
+  return r * AH_ROW + ((((ch >> 3) ^ ((r >> 3) & 1))) << 3) + (ch & 7);
+}
+
+__global__ __launch_bounds__(AH_THREADS) void sparse_attn_heads_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4, int64_t fp4_stride,
+    const uint8_t* __restrict__ kv_scale, int64_t sc_stride, int64_t n_entries,
+    const int64_t* __restrict__ kv_start, const int32_t* __restrict__ topk_idx, int64_t ld_idx,
+    int k, const uint8_t* __restrict__ window_kv, int64_t n_win_rows,
+    const int64_t* __restrict__ swa_start, const int32_t* __restrict__ n_swa, float scale,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ AttnHeadsShared sh;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gcol = lane & 15;      // head within a tile (logits); row of an item (tile reads)
+  const int grp = lane >> 4;       // lane group
+  const int ht = wave & 3;         // logit role: head tile
+  const int ih = wave >> 2;        //             item half
+  const int h = 16 * ht + gcol;    // this lane's head in the logit role
+
+  // Per-query scalars through buffer loads (issued with the query loads).
+  const int64_t base = kv_start[t];
+  const int64_t wbase = swa_start[t];
+  int nsw = n_swa[t];
+  nsw = nsw < 0 ? 0 : (nsw > AT_WINDOW ? AT_WINDOW : nsw);
+
+  // Query operand: head h, k-step ks covers channels 32ks + 8grp .. +7 (16 bytes per lane).
+  const uint16_t* qh = q + ((int64_t)t * 64 + h) * 512 + 8 * grp;
+  u32x4 qraw[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qh + 32 * ks);
+  float qm = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qm = fmaxf(qm, fabsf(__uint_as_float(qraw[ks][i] << 16)));
+      qm = fmaxf(qm, fabsf(__uint_as_float(qraw[ks][i] & 0xFFFF0000u)));
+    }
+  qm = fmaxf(qm, __shfl_xor(qm, 16));
+  qm = fmaxf(qm, __shfl_xor(qm, 32));
+  const int qexp = qm > 0.f ? (int)((__float_as_uint(qm) >> 23) & 0xFFu) - 127 : 0;
+  int kexp = 14 - qexp;
+  kexp = kexp < -126 ? -126 : (kexp > 126 ? 126 : kexp);
+  const float up = __uint_as_float((uint32_t)(127 + kexp) << 23);
+  const float lscale = scale * AT_LOG2E * __uint_as_float((uint32_t)(127 - kexp) << 23);
+  f16x8 qop[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qop[ks][2 * i] = (_Float16)(__uint_as_float(qraw[ks][i] << 16) * up);
+      qop[ks][2 * i + 1] = (_Float16)(__uint_as_float(qraw[ks][i] & 0xFFFF0000u) * up);
+    }
+
+  // Slices: n_wsl window slices, then n_msl slices of selected entries.
+  const int n_wsl = (nsw + AH_SLICE - 1) / AH_SLICE;
+  const int n_msl = (k + AH_SLICE - 1) / AH_SLICE;
+  const int n_sl = n_wsl + n_msl;
+  // Gather role: item it of a slice, channels 32 * gcol .. +31.
+  const int it = 4 * wave + grp;
+  constexpr uint32_t ABSENT = 0xFFFFFFFFu;
+  const int64_t kv_rows = n_entries - base;
+  const int64_t win_rows = n_win_rows - wbase;
+  const uint32_t kv_n = kv_rows <= 0 ? 0u : (kv_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)kv_rows);
+  const uint32_t win_n = win_rows <= 0 ? 0u : (win_rows >= (int64_t)ABSENT ? ABSENT - 1u : (uint32_t)win_rows);
+  const __amdgpu_buffer_rsrc_t rs_kv = make_rows_rsrc(kv_fp4 + base * fp4_stride, (int)fp4_stride, kv_n);
+  const __amdgpu_buffer_rsrc_t rs_sc = make_rows_rsrc(kv_scale + base * sc_stride, (int)sc_stride, kv_n);
+  const __amdgpu_buffer_rsrc_t rs_win = make_rows_rsrc(window_kv + wbase * 512, 512, win_n);
+  const __amdgpu_buffer_rsrc_t rs_idx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(topk_idx) + (int64_t)t * ld_idx, (short)0, k * 4, 0x00020000);
+  // Position of this lane's item in slice s (main slices only; k reads as absent).
+  auto position = [&](int s) -> int32_t {
+    const int gi = AH_SLICE * (s - n_wsl) + it;
+    const bool in = s >= n_wsl && s < n_sl && gi < k;
+    return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs_idx, in ? gi * 4 : k * 4, 0, 0));
+  };
+  struct Raw {
+    u32x4 v0, v1;      // window: 32 E4M3 bytes; main: v0 = 16 bytes of E2M1 codes
+    uint32_t sc;       // main: the scale dword holding groups 2*gcol, 2*gcol + 1
+    bool ok;
+  };
+  auto fetch = [&](int s, int32_t pos, Raw& r) {
+    if (s < n_wsl) {
+      const int wi = AH_SLICE * s + it;
+      r.ok = wi < nsw && wbase + wi >= 0 && wbase + wi < n_win_rows;
+      const int idx = r.ok ? wi : (int)ABSENT;
+      r.v0 = sbuf_load_b128(rs_win, idx, 32 * gcol, 0, 0);
+      r.v1 = sbuf_load_b128(rs_win, idx, 32 * gcol + 16, 0, 0);
+      r.sc = 0u;
+    } else {
+      const int gi = AH_SLICE * (s - n_wsl) + it;
+      r.ok = s < n_sl && gi < k && pos >= 0 && base + pos < n_entries && base + pos >= 0;
+      const int idx = r.ok ? pos : (int)ABSENT;
+      r.v0 = sbuf_load_b128(rs_kv, idx, 16 * gcol, 0, 0);
+      r.v1 = u32x4{0u, 0u, 0u, 0u};
+      r.sc = sbuf_load_b32(rs_sc, idx, 4 * (gcol >> 1), 0, 0);
+    }
+  };
+  // Converts this lane's 32 channels of slice s to fp16 and stores them to the tile.
+  auto convert_store = [&](int s, const Raw& r, uint16_t* tile) {
+    u32x4 c[4];
+    if (s < n_wsl) {
+      c[0] = fp8x8_to_f16x8(r.v0.x, r.v0.y);
+      c[1] = fp8x8_to_f16x8(r.v0.z, r.v0.w);
+      c[2] = fp8x8_to_f16x8(r.v1.x, r.v1.y);
+      c[3] = fp8x8_to_f16x8(r.v1.z, r.v1.w);
+    } else {
+      // groups 2*gcol (codes of v0.x, v0.y) and 2*gcol + 1 (v0.z, v0.w): the 16-bit half
+      // (gcol % 2) of the scale dword
+      const uint32_t pair = r.sc >> (16 * (gcol & 1));
+      const f16x2 s2 = e4m3x2_to_f16x2<false>(pair);
+      const f16x2 sa = f16x2{s2.x, s2.x}, sb = f16x2{s2.y, s2.y};
+      c[0] = fp4x8_to_f16x8(r.v0.x, sa);
+      c[1] = fp4x8_to_f16x8(r.v0.y, sa);
+      c[2] = fp4x8_to_f16x8(r.v0.z, sb);
+      c[3] = fp4x8_to_f16x8(r.v0.w, sb);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(tile + ah_off(it, 32 * gcol + 8 * j)) = c[j];
+  };
+
+  // Output accumulators: O^T[64 * wave + 16 * ct + 4 * grp + i][16 * hh + gcol].
+  f32x4 oacc[4][4];
+  float ref = -__builtin_inff();   // reference of head h (log2 units)
+  float mx = -__builtin_inff();    // largest logit of head h seen by this lane's items
+  float l_run = 0.f;
+  bool ref_set = false;
+  if (tid == 0) sh.flag = 0;
+  bool again;
+#pragma unroll 1
+  do {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) oacc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    Raw cur;
+    int32_t pnext = position(1);
+    fetch(0, position(0), cur);
+#pragma unroll 1
+    for (int s = 0; s < n_sl; ++s) {
+      const int buf = s & 1;
+      uint16_t* tile = sh.tile[buf];
+      convert_store(s, cur, tile);
+      if (grp < 4 && gcol == 0) sh.valid[buf][it] = cur.ok ? 1u : 0u;
+      const int32_t pn = pnext;
+      pnext = position(s + 2);
+      fetch(s + 1, pn, cur);     // past the last slice every item is absent: no memory access
+      __syncthreads();
+
+      // Logits of items 16 * ih + 4 * grp + i for head h.
+      const int row = 16 * ih + gcol;
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(tile + ah_off(row, 32 * ks + 8 * grp));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), qop[ks], sacc,
+                                                      0, 0, 0);
+      }
+      float lg[4];
+      bool any_valid = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v = sh.valid[buf][16 * ih + 4 * grp + i] != 0u;
+        lg[i] = v ? sacc[i] * lscale : -__builtin_inff();
+        mx = fmaxf(mx, lg[i]);
+      }
+      if (!ref_set) {
+        // uniform: every wavefront reads the same validity words
+#pragma unroll
+        for (int i = 0; i < AH_SLICE; ++i) any_valid |= sh.valid[buf][i] != 0u;
+        if (any_valid) {
+          float m = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          if (grp == 0) sh.xch[ih][h] = m;
+          __syncthreads();
+          ref = fmaxf(sh.xch[0][h], sh.xch[1][h]);
+          ref_set = true;
+        }
+      }
+      bool over = false;
+      f16x4 pv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        over |= lg[i] > ref + AT_GAP;
+        const float pe = lg[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(lg[i] - ref);
+        l_run += pe;
+        pv[i] = (_Float16)pe;
+      }
+      if (over) sh.flag = 1;
+      sh.pw[buf][ht][ih][lane] = __builtin_bit_cast(u32x2, pv);
+      __syncthreads();
+
+      // O^T[channels 64 * wave + 16 * ct .. +15][heads] += C^T . P over both item halves.
+#pragma unroll
+      for (int ih2 = 0; ih2 < 2; ++ih2) {
+        u32x2 at[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          at[ct] = lds_read_tr16x4(tile + ah_off(16 * ih2 + 4 * grp + (gcol >> 2),
+                                                 64 * wave + 16 * ct + 4 * (gcol & 3)));
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          const u32x2 bw = sh.pw[buf][hh][ih2][lane];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            oacc[ct][hh] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(f16x4, at[ct]), __builtin_bit_cast(f16x4, bw), oacc[ct][hh], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    again = sh.flag != 0;   // uniform
+    if (again) {
+      // repeat with each head's largest logit as its reference (it cannot be exceeded)
+      float m = mx;
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (grp == 0) sh.xch[ih][h] = m;
+      __syncthreads();
+      ref = fmaxf(sh.xch[0][h], sh.xch[1][h]);
+      ref_set = true;
+      if (tid == 0) sh.flag = 0;
+      __syncthreads();
+    }
+  } while (again);
+
+  // Normalise: L[head] = the sum of both item halves' weights.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (grp == 0) sh.xch[ih][h] = l_run;
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    const int head = 16 * hh + gcol;
+    const float L = sh.xch[0][head] + sh.xch[1][head];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* orow = out + ((int64_t)t * 64 + head) * 512 + 64 * wave + 4 * grp;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 a = oacc[ct][hh];
+      const uint32_t b0 = f32_to_bf16_rne(a[0] * inv), b1 = f32_to_bf16_rne(a[1] * inv);
+      const uint32_t b2 = f32_to_bf16_rne(a[2] * inv), b3 = f32_to_bf16_rne(a[3] * inv);
+      *reinterpret_cast<u32x2*>(orow + 16 * ct) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+    }
+  }
+  if (lse != nullptr && ih == 0 && grp == 0) {
+    const float L = sh.xch[0][h] + sh.xch[1][h];
+    lse[(int64_t)t * 64 + h] = L > 0.f ? (ref + __log2f(L)) * AT_LN2 : -__builtin_inff();
+  }
+}
+
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,
                               int64_t n_entries, const int64_t* kv_start, const int32_t* topk_idx,
@@ -517,6 +811,13 @@ hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t n_window_rows, const int64_t* swa_start,
                               const int32_t* n_swa, float softmax_scale, uint16_t* out,
                               float* lse, hipStream_t stream) {
+  if (n_q >= AH_MIN_Q) {
+    hipLaunchKernelGGL(sparse_attn_heads_kernel, dim3(n_q), dim3(AH_THREADS), 0, stream, q,
+                       kv_fp4, fp4_stride, kv_scale, scale_stride, n_entries, kv_start, topk_idx,
+                       ld_idx, k, window_kv, n_window_rows, swa_start, n_swa, softmax_scale, out,
+                       lse);
+    return hipGetLastError();
+  }
   const int groups8 = (n_q + N_XCD - 1) / N_XCD;
   if (n_q <= AT_HALVES_MAX_Q)
     hipLaunchKernelGGL(sparse_attn_kernel<2>, dim3(groups8 * N_XCD * AT_GROUPS * 2),
