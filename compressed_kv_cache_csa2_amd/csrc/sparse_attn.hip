@@ -525,7 +525,7 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 //     turns it into weights p = 2^(l - ref) with a per-head reference ref and stores them,
 //     already in the value product's B layout, to LDS; barrier;
 //   - wavefront w accumulates O^T for output channels 64w .. 64w+63 of all 64 heads over the
-//     slice's 32 items with v_mfma_f32_16x16x16f16 (A = the tile read transposed, B = p),
+//     slice's 32 items with v_mfma_f32_16x16x32_f16 (A = the tile read transposed, B = p),
 //     so no partial outputs are merged at the end.
 // The reference of a head is the largest logit of the first slice with a valid item (the
 // two item halves combine through LDS once); a later logit more than 15 above it (fp16
@@ -745,22 +745,29 @@ __global__ __launch_bounds__(AH_THREADS) void sparse_attn_heads_kernel(
       sh.pw[buf][ht][ih][lane] = __builtin_bit_cast(u32x2, pv);
       __syncthreads();
 
-      // O^T[channels 64 * wave + 16 * ct .. +15][heads] += C^T . P over both item halves.
+      // O^T[channels 64 * wave + 16 * ct .. +15][heads] += C^T . P over the slice's 32 items
+      // (K = 32): lane group grp carries items 8*grp .. 8*grp+7 in both operands. A is two
+      // transpose reads (items 8*grp + r and 8*grp + 4 + r, r = gcol / 4); B is the weights
+      // written by the logit lanes of item half grp / 2, lane groups 2*(grp % 2) and
+      // 2*(grp % 2) + 1.
+      u32x4 at[4];
 #pragma unroll
-      for (int ih2 = 0; ih2 < 2; ++ih2) {
-        u32x2 at[4];
+      for (int ct = 0; ct < 4; ++ct) {
+        const int ch = 64 * wave + 16 * ct + 4 * (gcol & 3);
+        const u32x2 lo = lds_read_tr16x4(tile + ah_off(8 * grp + (gcol >> 2), ch));
+        const u32x2 hi = lds_read_tr16x4(tile + ah_off(8 * grp + 4 + (gcol >> 2), ch));
+        at[ct] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      const int pl = gcol + 32 * (grp & 1);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const u32x2 b0 = sh.pw[buf][hh][grp >> 1][pl];
+        const u32x2 b1 = sh.pw[buf][hh][grp >> 1][pl + 16];
+        const u32x4 bw = u32x4{b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-          at[ct] = lds_read_tr16x4(tile + ah_off(16 * ih2 + 4 * grp + (gcol >> 2),
-                                                 64 * wave + 16 * ct + 4 * (gcol & 3)));
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          const u32x2 bw = sh.pw[buf][hh][ih2][lane];
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            oacc[ct][hh] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(f16x4, at[ct]), __builtin_bit_cast(f16x4, bw), oacc[ct][hh], 0, 0, 0);
-        }
+          oacc[ct][hh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, at[ct]), __builtin_bit_cast(f16x8, bw), oacc[ct][hh], 0, 0, 0);
       }
     }
     __syncthreads();
