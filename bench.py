@@ -31,8 +31,10 @@ those counter runs.
 (block means resident, as a decoder keeps them up to date); the dominant kernel is then the
 block-mean scorer (256 B of bf16 mean key read + 4 B of score written per (query, block)).
 needle_recall (decode workloads, which plant positions): the share of planted positions in
-the Full layer's Top-K, the pool and the Reindex layer's Top-K; --recall adds the same
-under the block-mean filter.
+the Full layer's Top-K, the pool and the Reindex layer's Top-K; for the second needle set
+(planted along the Reindex layer's own indexer query) the share the pool keeps, the share
+the Reindex Top-K keeps and the share lost outside the pool; --recall adds the same under
+the block-mean filter.
 
 Workloads whose caches total less than 512 MiB (decode_32k, tiny_decode_4k) would otherwise
 be timed out of the 256 MiB last-level cache: their caches are copied until the copies
@@ -141,14 +143,24 @@ def _recall(planted, nv, pool=None, idx=None):
 def needle_recall(wl, buf, C, means=None):
     """Share of the planted positions kept by each selection of the stack: the Full layer's
     Top-K, the pool, and the Reindex layer's Top-K (which uses its own query, unrelated to
-    the planting). With block means, the same under the block-mean filter, whose every
-    indexer layer builds its own pool (the first layer's pool is taken on its own)."""
+    the Full-layer planting). Decoder stacks also carry needles planted along the Reindex
+    layer's own indexer query: "reindex_needles" gives the share of those whose block the
+    pool keeps (with HSI, the Full layer's pool; with the block-mean filter, the Reindex
+    layer's own), the share its Top-K keeps, and the share lost because the block lies
+    outside the pool (a later indexer cannot recover it). With block means, the same under
+    the block-mean filter, whose every indexer layer builds its own pool (the first layer's
+    pool is taken on its own)."""
     import torch
     from compressed_kv_cache_csa2_amd import layers
     planted = wl.planted.cpu()
+    planted_re = None if wl.planted_re is None else wl.planted_re.cpu()
     nv = wl.n_visible.cpu()
     li_full = next(i for i, l in enumerate(wl.layers) if l.mode == "full")
     li_re = next((i for i, l in enumerate(wl.layers) if l.mode == "reindex"), None)
+
+    def count(pl):
+        return int(sum(torch.unique(pl[t][pl[t] < nv[t]]).numel() for t in range(pl.shape[0])))
+
     out = {}
     for coarse in (("hsi", "hisa") if means is not None else ("hsi",)):
         res = {}
@@ -165,9 +177,53 @@ def needle_recall(wl, buf, C, means=None):
                 res["pool"] = _recall(planted, nv, pool=buf.pool.cpu())
         if li_re is not None:
             res["reindex_topk"] = _recall(planted, nv, idx=buf.idx[li_re].cpu())
-        res["needles"] = int(sum(torch.unique(planted[t][planted[t] < nv[t]]).numel()
-                                 for t in range(planted.shape[0])))
+        res["needles"] = count(planted)
+        if planted_re is not None and li_re is not None and wl.with_pool:
+            # after the pass, buf.pool is the pool the Reindex layer selected from
+            in_pool = _recall(planted_re, nv, pool=buf.pool.cpu())
+            res["reindex_needles"] = {
+                "pool": in_pool,
+                "reindex_topk": _recall(planted_re, nv, idx=buf.idx[li_re].cpu()),
+                "lost_outside_pool": 1.0 - in_pool,
+                "needles": count(planted_re),
+            }
         out[coarse] = res
+    return out
+
+
+def q8_selection_overlap(wl, buf):
+    """For a workload whose indexer query is quantised to MXFP8: the mean overlap of each
+    selection of the stack with the one the bf16 query makes on the same data (both run
+    through the library): the Full layer's Top-K, the pool (decoder stacks) and the Reindex
+    layer's Top-K."""
+    import torch
+    from compressed_kv_cache_csa2_amd import layers
+    li_full = next((i for i, l in enumerate(wl.layers) if l.mode == "full"), None)
+    li_re = next((i for i, l in enumerate(wl.layers) if l.mode == "reindex"), None)
+    if li_full is None:
+        return None
+    layers.run_layers(wl, buf)
+    ref = layers.alloc_buffers(wl)
+    wl.q8 = False
+    try:
+        layers.run_layers(wl, ref)
+    finally:
+        wl.q8 = True
+    torch.cuda.synchronize()
+
+    def mean_overlap(a, b):
+        a, b = a.cpu(), b.cpu()
+        tot = 0.0
+        for t in range(a.shape[0]):
+            x, y = a[t][a[t] >= 0], b[t][b[t] >= 0]
+            tot += int(torch.isin(x, y).sum()) / max(1, y.numel())
+        return tot / max(1, a.shape[0])
+
+    out = {"full_topk": mean_overlap(buf.idx[li_full], ref.idx[li_full])}
+    if wl.with_pool:
+        out["pool"] = mean_overlap(buf.pool, ref.pool)
+    if li_re is not None:
+        out["reindex_topk"] = mean_overlap(buf.idx[li_re], ref.idx[li_re])
     return out
 
 
@@ -412,6 +468,7 @@ def measure(name, args, C, layers, synth, with_breakdown=False, with_recall=Fals
         breakdown(wl, buf, C, layers, stream, hisa, means)
     recall = needle_recall(wl, buf, C, means if with_recall else None) \
         if wl.planted is not None else None
+    q8_overlap = q8_selection_overlap(wl, buf) if wl.q8 and not hisa else None
     step_bytes = algorithmic_bytes(wl, coarse=args.coarse)
     res = {
         "workload": wl.name, "wl": wl, "copies": len(copies), "ms_step": ms_step,
@@ -424,6 +481,7 @@ def measure(name, args, C, layers, synth, with_breakdown=False, with_recall=Fals
                      "kernel": kernel_label(wl, hisa), "launch_us": idx_us,
                      "bytes_per_launch": idx_bytes},
         "recall": recall,
+        "q8_overlap": q8_overlap,
     }
     if wl.shared_start is not None:
         pairs = int(wl.n_visible.to(torch.int64).sum())
@@ -572,6 +630,8 @@ def main():
     }
     if head["recall"] is not None:
         line["needle_recall"] = head["recall"]
+    if head["q8_overlap"] is not None:
+        line["q8_selection_overlap"] = head["q8_overlap"]
     if args.workload == "decode_256k" and args.coarse == "hsi" and not args.no_1m:
         # The metric's 1M half: the same measurement of decode_1m (64 queries of 1,048,576
         # entries each) in the same run, on the same GPU.

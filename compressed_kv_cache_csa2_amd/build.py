@@ -60,5 +60,37 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-check build: the C ABI's host code (csa2_api.hip compiled as C++ by g++, no device
+# code) with every kernel launcher stubbed out (hostcheck/launch_stubs.cpp), under
+# AddressSanitizer and UndefinedBehaviorSanitizer. The CPU tests load it in place of
+# libcsa2.so (CSA2_LIBRARY) with the sanitizer runtimes preloaded.
+HOSTCHECK_SRC = os.path.join(PKG, "hostcheck", "launch_stubs.cpp")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_hostcheck(out_path: str) -> str:
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-x", "c++", os.path.join(CSRC, "csa2_api.hip"), "-x", "c++", HOSTCHECK_SRC,
+           "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", out_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host-check build failed:\n{r.stdout}{r.stderr}")
+    return out_path
+
+
+def sanitizer_runtimes() -> list:
+    """Paths of g++'s ASan and UBSan runtimes (to preload into a Python process)."""
+    out = []
+    for name in ("libasan.so", "libubsan.so"):
+        p = subprocess.run(["g++", f"-print-file-name={name}"], capture_output=True,
+                           text=True).stdout.strip()
+        out.append(p)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

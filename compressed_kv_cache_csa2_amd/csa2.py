@@ -11,7 +11,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+# CSA2_LIBRARY names another build of the same C ABI (the sanitizer host-check build of the
+# CPU tests, whose launchers refuse every launch); by default the in-tree libcsa2.so.
+_LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 
 FULL, REINDEX, REUSE = 0, 1, 2
 POOL_NONE, POOL_SLOTS, POOL_CANDIDATES = 0, 1, 2

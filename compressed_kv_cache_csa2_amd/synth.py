@@ -17,6 +17,9 @@ blocks, 2,048 pool blocks):
   tiny_decode_4k    1 query, 4,096 entries, Full only, 16 planted positions.
   decode_32k        16 queries x 32,768 entries, Full only, 64 planted per query.
   decode_256k       32 queries x 262,144 entries; Full (+pool), Reindex, 3 x Reuse.
+                    Decoder stacks with a Reindex layer carry a second needle set, planted
+                    along that layer's own indexer query (its keys only), so that what the
+                    Full layer's pool loses for a later Reindex layer can be measured.
   prefill_128k_m2   4,096 causal queries over one sequence of 131,072 entries at
                     compression ratio 2 (entry e covers source tokens 2e and 2e+1 and is
                     visible from token p when 2e+1 <= p); Full only.
@@ -71,6 +74,8 @@ class Workload:
     layers: list = field(default_factory=list)
     with_pool: bool = False
     planted: torch.Tensor | None = None  # int64 [n_q, n_plant] positions (or None)
+    # positions planted along the first Reindex layer's indexer query (or None)
+    planted_re: torch.Tensor | None = None
     softmax_scale: float = SOFTMAX_SCALE
     # MXFP4 copy of the indexer keys (the same draws): codes [E, 64], E8M0 scales [E, 4]
     k_codes: torch.Tensor | None = None
@@ -102,8 +107,8 @@ class Workload:
                         n_visible=mv(self.n_visible), k_cache=mv(self.k_cache),
                         kv_fp4=mv(self.kv_fp4), kv_scale=mv(self.kv_scale), layers=layers,
                         with_pool=self.with_pool, planted=self.planted,
-                        softmax_scale=self.softmax_scale, k_codes=mv(self.k_codes),
-                        k_scales=mv(self.k_scales), shared_start=self.shared_start,
+                        planted_re=self.planted_re, softmax_scale=self.softmax_scale,
+                        k_codes=mv(self.k_codes), k_scales=mv(self.k_scales), shared_start=self.shared_start,
                         group_caches=[tuple(mv(x) for x in c) for c in self.group_caches],
                         q8=self.q8)
 
@@ -225,10 +230,13 @@ def _make_layer(mode, n_q, device, seed, li, window_rows=None, swa_start=None, n
 
 
 def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, plant_pos,
-                    full_layer: LayerInputs, mxfp4=False, tag=()):
-    """Draw the indexer-K and latent rows of every sequence, planting at plant_pos. With
-    mxfp4 the indexer keys are also encoded in MXFP4 (from the same draws). `tag` extends
-    the draw names (a second cache set of the same sequences)."""
+                    full_layer: LayerInputs, mxfp4=False, tag=(), plant_re=None,
+                    reindex_layer: LayerInputs | None = None):
+    """Draw the indexer-K and latent rows of every sequence, planting at plant_pos (indexer
+    key along the Full layer's weighted indexer query, latent along its summed main query)
+    and at plant_re (indexer key only, along the Reindex layer's weighted indexer query).
+    With mxfp4 the indexer keys are also encoded in MXFP4 (from the same draws). `tag`
+    extends the draw names (a second cache set of the same sequences)."""
     k_cache = torch.zeros((n_entries, IDX_DIM), dtype=torch.uint8, device=device)
     k_codes = torch.zeros((n_entries, IDX_DIM // 2), dtype=torch.uint8, device=device) if mxfp4 else None
     k_scales = torch.full((n_entries, IDX_DIM // 32), 127, dtype=torch.uint8, device=device) if mxfp4 else None
@@ -251,6 +259,11 @@ def _fill_sequences(n_q, n_ctx, kv_start, n_visible, n_entries, device, seed, pl
             v = _unit(full_layer.q[t].float().sum(0))
             k[pos] += PLANT_SHIFT * u
             lat[pos] += PLANT_SHIFT * v
+        if plant_re is not None and not shared:
+            pos = plant_re[t]
+            pos = pos[pos < n]
+            qi = reindex_layer.q_idx[t].float()
+            k[pos] += PLANT_SHIFT * _unit((reindex_layer.w[t].float()[:, None] * qi).sum(0))
         k_cache[start:start + n] = encode_e4m3(k)
         if mxfp4:
             kc, ks = encode_mxfp4_rows(k)
@@ -277,6 +290,16 @@ def make_decode(name, n_q, n_ctx, layers, with_pool, n_plant, needles="random",
     kv_start_t = torch.tensor(starts[:n_q], dtype=torch.int64)
     lay = [_make_layer(m, n_q, device, seed, li) for li, m in enumerate(layers)]
     planted = None
+    planted_re = None
+    li_re = next((i for i, m in enumerate(layers) if m == "reindex"), None)
+    if n_plant > 0 and n_q > 0 and li_re is not None:
+        rows = []
+        for t in range(n_q):
+            n = max(0, int(n_visible[t]))
+            g = _gen("cpu", seed, "plant_re", t)
+            r = torch.randperm(max(n, 1), generator=g)[:n_plant].sort().values
+            rows.append(torch.cat([r, r.new_full((n_plant - r.numel(),), 0)]) if r.numel() < n_plant else r)
+        planted_re = torch.stack(rows)
     if n_plant > 0 and n_q > 0:
         rows = []
         for t in range(n_q):
@@ -294,11 +317,14 @@ def make_decode(name, n_q, n_ctx, layers, with_pool, n_plant, needles="random",
                                torch.cat([r, r.new_full((n_plant - r.numel(),), 0)]) for r in rows])
     k_cache, kv_fp4, kv_scale, k_codes, k_scales = _fill_sequences(
         n_q, n_ctx, kv_start_t, n_visible_t, n_entries, device, seed,
-        None if planted is None else planted.to(device), lay[0], mxfp4=mxfp4)
+        None if planted is None else planted.to(device), lay[0], mxfp4=mxfp4,
+        plant_re=None if planted_re is None else planted_re.to(device),
+        reindex_layer=None if li_re is None else lay[li_re])
     return Workload(name=name, n_q=n_q, n_ctx=max(n_visible) if n_q else 0,
                     kv_start=kv_start_t.to(device), n_visible=n_visible_t.to(device),
                     k_cache=k_cache, kv_fp4=kv_fp4, kv_scale=kv_scale, layers=lay,
-                    with_pool=with_pool, planted=planted, k_codes=k_codes, k_scales=k_scales)
+                    with_pool=with_pool, planted=planted, planted_re=planted_re,
+                    k_codes=k_codes, k_scales=k_scales)
 
 
 def make_prefill(name="prefill_128k_m2", n_q=4096, n_entries=131072, ratio=2,

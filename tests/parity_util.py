@@ -6,7 +6,10 @@ Acceptance rules:
     magnitude when the K-th value is 0);
   - attention outputs within max-abs error <= 2e-2 * max|ref|;
   - indexer scores (fp32 MFMA accumulation of exact products) within 1e-5 of the sum of
-    the absolute values of their terms.
+    the absolute values of their terms;
+  - a selection made on MXFP8-query scores s8 against the configs' bf16-query selection
+    (scores s): with D the largest |s8 - s| of the row, the two differ only in elements
+    whose bf16 value lies within 2D (plus the tie band) of the bf16 K-th value.
 """
 import numpy as np
 import torch
@@ -67,6 +70,30 @@ def assert_set_band(gpu_items, ref_items, ref_value_of, kth, band, what=""):
         v = ref_value_of(x)
         assert abs(v - kth) <= band, f"{what}: {x} (value {v}) differs outside the band of {kth}"
     return g == r
+
+
+def q8_departure_band(s_bf16, s_q8, k):
+    """K-th largest bf16-query value, and the band outside which a selection on the MXFP8-
+    query values may not depart from the bf16 one, with D = max |s_q8 - s_bf16| over the
+    finite entries. Any k entries with s >= tau have s_q8 >= tau - D, so the q8 K-th value
+    tau8 >= tau - D, and symmetrically tau >= tau8 - D; an entry the q8 selection adds has
+    s >= s_q8 - D >= tau8 - D >= tau - 2D, one it drops has s <= s_q8 + D <= tau + 2D.
+    The band adds the tie band (the GPU's q8 scores carry fp32 rounding). Returns (tau,
+    band, D)."""
+    s = np.asarray(s_bf16, np.float64)
+    s8 = np.asarray(s_q8, np.float64)
+    fin = np.isfinite(s) & np.isfinite(s8)
+    assert np.array_equal(np.isfinite(s), np.isfinite(s8)), "finite patterns differ"
+    d = float(np.abs(s8[fin] - s[fin]).max()) if fin.any() else 0.0
+    kth, tie = band_of(s, k)
+    return kth, 2.0 * d + tie, d
+
+
+def overlap(a, b):
+    """|a & b| / |b| over the non-negative entries."""
+    a = set(int(x) for x in a if x >= 0)
+    b = set(int(x) for x in b if x >= 0)
+    return len(a & b) / max(1, len(b))
 
 
 def assert_attn_close(gpu_out, ref_out, what=""):

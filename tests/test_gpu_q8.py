@@ -128,3 +128,63 @@ def test_index_score_shared_q8_equals_per_query_and_oracle(dev):
         terms = np.zeros(ld)
         terms[:nv] = (np.abs(O.e4m3_decode(k_all[:nv])) @ qa.T) @ np.abs(lay.w[t].cpu().numpy().astype(np.float64))
         assert_scores_close(s1[t].cpu().numpy(), ref, terms, f"shared q8 q{t}")
+
+
+@pytest.fixture(scope="module")
+def decode_256k_q8(dev):
+    from compressed_kv_cache_csa2_amd import layers, synth
+    wl = synth.make_workload("decode_256k_q8", device=dev)
+    buf = layers.alloc_buffers(wl)
+    layers.run_layers(wl, buf)
+    torch.cuda.synchronize()
+    return wl, buf
+
+
+@pytest.mark.parametrize("t", [0, 13, 31])
+def test_mxfp8_query_selection_departs_only_inside_the_rounding_band(decode_256k_q8, t):
+    """decode_256k_q8 at full size: the GPU's MXFP8-query selections (the Full layer's
+    Top-512 and pool, then the Reindex layer's Top-512 over that pool) against the bf16-query
+    selections the configs specify, computed by the oracle on the same data. With D the
+    largest change the query's MXFP8 rounding makes to a score of the row (oracle q8 score
+    minus oracle bf16 score), every departure lies within 2D of the bf16 K-th value; the
+    overlaps are printed."""
+    from compressed_kv_cache_csa2_amd import synth
+    from tests.parity_util import assert_set_band, overlap, q8_departure_band
+    wl, buf = decode_256k_q8
+    seq = synth.sequence_to_host(wl, t)
+    nv = seq["n_visible"]
+    kc = seq["k_cache"]
+    full, re = seq["layers"][0], seq["layers"][1]
+    # Full layer over every position
+    qc, qs = O.mxfp8_quantize(O.bf16_decode(full["q_idx"]).astype(np.float32))
+    s = O.full_scores(full["q_idx"], full["w"], kc, 0, nv, nv)
+    s8 = O.full_scores_q8(qc, qs, full["w"], kc, 0, nv, nv)
+    tau, band, d = q8_departure_band(s, s8, 512)
+    ref_idx = O.topk_slots(s, 512)
+    got_idx = buf.idx[0][t].cpu().numpy()
+    assert_set_band(got_idx, ref_idx, lambda p: s[p], tau, band, f"q{t} full top-k (q8 vs bf16)")
+    # pool: block maxima (the latest block forced in), D bounded by the scores' D
+    bm = O.block_max(s[:nv])
+    bm8 = O.block_max(s8[:nv])
+    bm[(nv - 1) // 8] = bm8[(nv - 1) // 8] = np.inf
+    tau_b, band_b, _ = q8_departure_band(bm, bm8, 2048)
+    pool_gpu = buf.pool[t].cpu().numpy()
+    assert_set_band(pool_gpu, O.topk_slots(bm, 2048), lambda b: bm[b], tau_b, band_b,
+                    f"q{t} pool (q8 vs bf16)")
+    # Reindex layer over the GPU's pool
+    padded = np.full(2048, -1, np.int64)
+    kept = pool_gpu[pool_gpu >= 0]
+    padded[:len(kept)] = kept
+    qc2, qs2 = O.mxfp8_quantize(O.bf16_decode(re["q_idx"]).astype(np.float32))
+    r = O.reindex_scores(re["q_idx"], re["w"], kc, 0, nv, padded)
+    r8 = O.reindex_scores_q8(qc2, qs2, re["w"], kc, 0, nv, padded)
+    tau_r, band_r, d_r = q8_departure_band(r, r8, 512)
+    pos_of_slot = O.slots_to_positions(np.arange(len(r)), padded)
+    score_at = dict(zip(pos_of_slot.tolist(), r.tolist()))
+    ref_re = O.slots_to_positions(O.topk_slots(r, 512), padded)
+    got_re = buf.idx[1][t].cpu().numpy()
+    assert_set_band(got_re, ref_re, lambda p: score_at[p], tau_r, band_r,
+                    f"q{t} reindex top-k (q8 vs bf16)")
+    print(f"q{t}: D = {d:.3f} (K-th bf16 score {tau:.2f}), overlaps: full top-k "
+          f"{overlap(got_idx, ref_idx):.3f}, pool {overlap(pool_gpu, O.topk_slots(bm, 2048)):.3f}, "
+          f"reindex top-k {overlap(got_re, ref_re):.3f} (D = {d_r:.3f})")
