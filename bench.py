@@ -94,7 +94,8 @@ def full_indexer(wl, buf, C, stream=None):
     from compressed_kv_cache_csa2_amd import layers
     lay = next(l for l in wl.layers if l.mode == "full")
     layers.index_score(wl, C.FULL, lay, None if wl.with_pool else buf.scores,
-                       buf.block_max, ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
+                       buf.block_max, ld_scores=buf.scores.shape[1], stream=stream, buf=buf,
+                       block_aux=buf.block_aux if layers.fused_full_select(wl) else None)
 
 
 def rotated_copies(wl):
@@ -497,6 +498,7 @@ def measure(name, args, C, layers, synth, with_breakdown=False, with_recall=Fals
 def breakdown(wl, buf, C, layers, stream, hisa, means):
     """Per-call event timings of one eager pass of the stack, to stderr."""
     import torch
+    fused = layers.fused_full_select(wl)   # the Full layer's selection is one kernel
     names = []
     evs = []
     with torch.cuda.stream(stream):
@@ -521,6 +523,13 @@ def breakdown(wl, buf, C, layers, stream, hisa, means):
                                     stream=stream)
                 elif part == "score" and lay.mode == "full":
                     full_indexer(wl, buf, C, stream=stream)
+                elif (part in ("rescore", "topk") and lay.mode == "full" and wl.with_pool
+                      and fused):
+                    continue
+                elif part == "pool" and lay.mode == "full" and wl.with_pool and fused:
+                    C.csa2_full_select(buf.block_max, buf.block_aux, wl.n_visible, buf.pool,
+                                       lay.q_idx, lay.w, wl.cache(lay.group)[0], wl.kv_start,
+                                       buf.idx[li], stream=stream)
                 elif part == "rescore" and lay.mode == "full" and wl.with_pool:
                     layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
                                        pool_blocks=buf.cand, stream=stream, buf=buf)

@@ -66,7 +66,7 @@ static int index_score_common(const char* fn, int key_format, csa2_mode_t mode, 
                               const void* k_scales, int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               int block_size, float* scores, int64_t ld_scores, float* block_max,
-                              int64_t ld_block_max, void* stream) {
+                              int64_t ld_block_max, uint32_t* block_aux, void* stream) {
   REQUIRE(mode == CSA2_FULL || mode == CSA2_REINDEX, CSA2_ERR_INVALID_ARG,
           "%s: mode %d does no scoring (Reuse layers attend with published indices)", fn,
           (int)mode);
@@ -104,13 +104,18 @@ static int index_score_common(const char* fn, int key_format, csa2_mode_t mode, 
             "%s: ld_block_max %lld < ceil(ld_scores/8)", fn, (long long)ld_block_max);
     REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
   }
+  if (block_aux != nullptr) {
+    REQUIRE(key_format == 0 && mode == CSA2_FULL && block_max != nullptr, CSA2_ERR_INVALID_ARG,
+            "%s: block_aux is written by a FULL pass over E4M3 keys beside block_max", fn);
+    REQUIRE(aligned(block_aux, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_aux", fn);
+  }
   return hip_status(csa2::launch_index_score(
                         mode == CSA2_REINDEX, key_format, n_q,
                         static_cast<const uint16_t*>(q_idx), w,
                         static_cast<const uint8_t*>(k_cache),
                         static_cast<const uint8_t*>(k_scales), n_entries, kv_start, n_visible,
                         pool_blocks, mode == CSA2_REINDEX ? n_pool : 0, scores, ld_scores, block_max,
-                        ld_block_max, static_cast<hipStream_t>(stream)),
+                        ld_block_max, block_aux, static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -118,10 +123,12 @@ int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const vo
                      const float* w, const void* k_cache, int64_t n_entries,
                      const int64_t* kv_start, const int32_t* n_visible, const int32_t* pool_blocks,
                      int n_pool, int block_size, float* scores, int64_t ld_scores,
-                     float* block_max, int64_t ld_block_max, void* stream) {
+                     float* block_max, int64_t ld_block_max, uint32_t* block_aux,
+                     void* stream) {
   return index_score_common("csa2_index_score", 0, mode, n_q, n_heads, d_idx, q_idx, w, k_cache,
                             nullptr, n_entries, kv_start, n_visible, pool_blocks, n_pool,
-                            block_size, scores, ld_scores, block_max, ld_block_max, stream);
+                            block_size, scores, ld_scores, block_max, ld_block_max, block_aux,
+                            stream);
 }
 
 int csa2_index_score_shared(int n_q, int n_heads, int d_idx, const void* q_idx, const float* w,
@@ -167,7 +174,7 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx, co
   return index_score_common("csa2_index_score_mxfp4", 1, mode, n_q, n_heads, d_idx, q_idx, w,
                             k_codes, k_scales, n_entries, kv_start, n_visible, pool_blocks,
                             n_pool, block_size, scores, ld_scores, block_max, ld_block_max,
-                            stream);
+                            nullptr, stream);
 }
 
 int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
@@ -178,7 +185,7 @@ int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx, con
                           void* stream) {
   return index_score_common("csa2_index_score_bf16", 2, mode, n_q, n_heads, d_idx, q_idx, w,
                             k_rows, nullptr, n_entries, kv_start, n_visible, pool_blocks, n_pool,
-                            block_size, scores, ld_scores, block_max, ld_block_max, stream);
+                            block_size, scores, ld_scores, block_max, ld_block_max, nullptr, stream);
 }
 
 int csa2_block_mean_keys(int n_q, int d_idx, int block_size, const void* k_cache,
@@ -562,6 +569,45 @@ int csa2_pool_candidates(int n_q, const float* block_max, int64_t ld_bm,
   return hip_status(csa2::launch_block_pool_cand(n_q, block_max, ld_bm, n_visible, n_keep,
                                                  pool_blocks, ld_pool, k, cand_blocks, ld_cand,
                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
+                     int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
+                     int n_heads, int d_idx, const void* q_idx, const float* w,
+                     const void* k_cache, int64_t n_entries, const int64_t* kv_start,
+                     const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                     void* stream) {
+  const char* fn = "csa2_full_select";
+  REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
+          "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
+  REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
+          "%s: indexer shape %dx%d, only %dx%d is built", fn, n_heads, d_idx,
+          CSA2_IDX_HEADS, CSA2_IDX_DIM);
+  REQUIRE(n_q >= 0 && n_q <= 65535, CSA2_ERR_INVALID_ARG, "%s: n_q %d out of range", fn, n_q);
+  REQUIRE(n_keep >= 1 && n_keep <= CSA2_MAX_K, CSA2_ERR_INVALID_ARG,
+          "%s: n_keep %d out of range [1, %d]", fn, n_keep, CSA2_MAX_K);
+  REQUIRE(k >= 1 && k < n_keep, CSA2_ERR_INVALID_ARG, "%s: k %d must lie in [1, n_keep)", fn, k);
+  if (n_q == 0) return ok();
+  REQUIRE(block_max && n_visible && pool_blocks && q_idx && w && k_cache && kv_start && topk_idx &&
+              block_aux,
+          CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  REQUIRE(n_entries >= 0, CSA2_ERR_INVALID_ARG, "%s: n_entries < 0", fn);
+  REQUIRE(ld_bm >= 1 && ld_pool >= n_keep && ld_idx >= k, CSA2_ERR_INVALID_ARG,
+          "%s: bad leading dimension (ld_bm %lld, ld_pool %lld, ld_idx %lld)", fn,
+          (long long)ld_bm, (long long)ld_pool, (long long)ld_idx);
+  REQUIRE(aligned(block_max, 16) && ld_bm % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "%s: block_max must be 16-byte aligned with ld_bm a multiple of 4", fn);
+  REQUIRE(aligned(q_idx, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
+          "%s: q_idx and k_cache must be 16-byte aligned", fn);
+  REQUIRE(aligned(w, 4) && aligned(kv_start, 8) && aligned(n_visible, 4) &&
+              aligned(pool_blocks, 4) && aligned(topk_idx, 4) && aligned(block_aux, 4),
+          CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
+  return hip_status(csa2::launch_full_select(n_q, block_max, ld_bm, n_visible, n_keep, pool_blocks,
+                                             ld_pool, static_cast<const uint16_t*>(q_idx), w,
+                                             static_cast<const uint8_t*>(k_cache), n_entries,
+                                             kv_start, block_aux, k, topk_idx, ld_idx,
+                                             static_cast<hipStream_t>(stream)),
                     fn);
 }
 

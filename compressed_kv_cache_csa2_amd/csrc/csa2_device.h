@@ -81,6 +81,31 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8_pow2(uint32_t codes, float pow2
   return r;
 }
 
+// Indexer score of the 32 positions of one wavefront step over E4M3 keys: lane (n, half)
+// holds in raw the bytes 64*half .. +63 of position n's key row, a[kb] the A operand of
+// k-block kb (head n, channels 64*half + 8*kb .. +7) and wr the head weights of its rows of
+// the 32x32 accumulator. Eight v_mfma_f32_32x32x16_bf16 (exact E4M3 -> bf16 conversion),
+// then ReLU, weights and the head sum; both half-waves return the score of position n.
+// Every indexer path over E4M3 keys computes its scores with exactly these operations in
+// this order, so a score recomputed elsewhere is bit-identical.
+__device__ __forceinline__ float e4m3_step_score(const bf16x8 (&a)[8], const float (&wr)[16],
+                                                 const u32x4 (&raw)[4]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const u32x2 lo = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2]);
+    const u32x2 hi = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2 + 1]);
+    const u32x4 bv = u32x4{lo.x, lo.y, hi.x, hi.y};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc, 0,
+                                                  0, 0);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+  part += __shfl_xor(part, 32);
+  return part;
+}
+
 // ---- fp16 forms (the attention works in fp16: every E2M1 x E4M3 product, and every E4M3
 // value, is exact in fp16, and packed fp16 multiplies halve the conversion work) ----
 
@@ -165,6 +190,18 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 // A score takes part in a selection unless it is -inf or NaN.
 __device__ __forceinline__ bool selectable(float f) { return f > -__builtin_inff(); }
+
+// Unsigned minimum / maximum (the device min/max overloads compare as signed int).
+__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Block statistics of a Full pass beside each 8-slot block maximum: the block's argmax (the
+// lowest slot holding the largest key) in bits 0..2 and, above them, the selection key of
+// the largest score among its other seven slots (0 when none is selectable) rounded up to a
+// multiple of 8, so the stored word is never below that key.
+__device__ __forceinline__ uint32_t block_aux_word(uint32_t key2, uint32_t argmax) {
+  return ((key2 + 7u) & ~7u) | argmax;
+}
 
 // Indexed ("structured") buffer loads: address = base + index * stride + offset. A load
 // whose index is at or past the record count returns zeros without touching memory, so a

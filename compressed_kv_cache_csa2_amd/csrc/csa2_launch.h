@@ -16,7 +16,7 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
                               int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
-                              hipStream_t stream);
+                              uint32_t* block_aux, hipStream_t stream);
 
 // Block-mean keys (bf16 [rows, 128]) of every visible 8-position block, and the block counts.
 hipError_t launch_block_mean_keys(int n_q, const uint8_t* k_cache, int64_t n_entries,
@@ -53,6 +53,17 @@ hipError_t launch_block_pool_cand(int n_q, const float* block_max, int64_t ld_bm
                                   const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
                                   int64_t ld_pool, int k, int32_t* cand_blocks, int64_t ld_cand,
                                   hipStream_t stream);
+
+// The decoder Full layer's selection in one kernel: the pool (as launch_block_pool_cand) and
+// the Top-K among its candidates, from the Full pass's block statistics (block_aux) and the
+// rescoring, with the layer's indexer query over E4M3 keys, of the few candidate blocks
+// whose second score can reach it.
+hipError_t launch_full_select(int n_q, const float* block_max, int64_t ld_bm,
+                              const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                              int64_t ld_pool, const uint16_t* q_idx, const float* w,
+                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
+                              const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                              hipStream_t stream);
 
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,

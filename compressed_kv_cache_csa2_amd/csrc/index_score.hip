@@ -47,6 +47,22 @@ constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is 
 // two-stage filter).
 enum { KF_E4M3 = 0, KF_MXFP4 = 1, KF_BF16 = 2 };
 
+// Integer key of a float whose signed order is the float order (negative floats have their
+// magnitude bits flipped); the map is its own inverse on the key.
+__device__ __forceinline__ int order_key(float v) {
+  const int k = __float_as_int(v);
+  return k ^ ((k >> 31) & 0x7FFFFFFF);
+}
+
+// Largest key over each aligned group of 8 lanes, in every lane of the group: quad swaps of
+// 1 and 2 lanes, then the mirror within 8 lanes (lane i reads lane 7 - i), as DPP moves.
+__device__ __forceinline__ int group8_max_all(int k) {
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x141, 0xF, 0xF, false));
+  return k;
+}
+
 template <bool REINDEX, int KF>
 __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -204,11 +220,13 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_kernel(
 // half) holds bytes 64*half .. +63 of row n. Conversion, products, their order and the
 // epilogue are that kernel's, so every score is bit-identical to it (and to the Reindex
 // form, which rescoring relies on). The row loads run one step ahead.
+// Four wavefronts per SIMD (128 registers each) keep enough rows in flight.
+template <int MODE>
 __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, int64_t n_entries, const int64_t* __restrict__ kv_start,
     const int32_t* __restrict__ n_visible, float* __restrict__ scores, int64_t ld,
-    float* __restrict__ block_max, int64_t ld_bm) {
+    float* __restrict__ block_max, int64_t ld_bm, uint32_t* __restrict__ block_aux) {
   __shared__ u32x4 stage[IS_THREADS / 64][2][256];   // 8 KiB per wavefront
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -244,7 +262,16 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
     }
   };
   u32x4 g[4];
-  float sc[STEPS];
+  // MODE 0: scores and maxima go out after the tile (the score row is the bulk of the
+  // writes); MODE 1: block maxima only, reduced as each step completes and staged in LDS;
+  // MODE 2: as 1, plus the block statistics (scores, if asked, stored as each step ends).
+  constexpr bool AUX = MODE == 2;
+  constexpr bool STAGED = MODE != 0;
+  float sc[STAGED ? 1 : STEPS];
+  float sv_prev = 0.f;   // statistics: the previous step's score
+  static_assert(STEPS % 2 == 0, "block statistics pair the steps");
+  __shared__ float bm_st[STAGED ? TILE / 8 : 1];    // block maxima of the tile
+  __shared__ uint32_t aux_st[AUX ? TILE / 8 : 1];   // block statistics of the tile
   if (any) load_step(0, g);
 #pragma unroll
   for (int step = 0; step < STEPS; ++step) {
@@ -280,12 +307,62 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
       part += __shfl_xor(part, 32);
       if (slot_at(step) < lim) sv = part;
     }
-    sc[step] = sv;
+    if constexpr (MODE == 1) {
+      // Block maxima as each step completes, two steps at a time (both half-waves hold every
+      // score of a step: half 0 takes the previous step's slots, half 1 this step's), on
+      // integer keys whose signed order is the float order with DPP lane moves (equal to the
+      // fmaxf reduction: scores are never -0).
+      if (step & 1) {
+        const int m = group8_max_all(order_key(half ? sv : sv_prev));
+        if ((n & 7) == 0)
+          bm_st[16 * (step - 1 + half) + 4 * wave + (n >> 3)] =
+              __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+      } else {
+        sv_prev = sv;
+      }
+    } else if constexpr (AUX) {
+      // Block statistics, two steps at a time (both half-waves hold every score of a step,
+      // so half 0 takes the previous step's slots and half 1 this step's; no score array is
+      // kept): on integer keys whose signed order is the float order, with DPP lane moves,
+      // every lane of a block gets its maximum (equal to the fmaxf reduction: scores are
+      // never -0); the argmax is the lowest lane holding it (a ballot), the second key the
+      // largest of the others.
+      const int64_t slot = slot_at(step);
+      if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+      if (step & 1) {
+        const int k = order_key(half ? sv : sv_prev);
+        const int m = group8_max_all(k);
+        const uint64_t hit = __ballot(k == m);
+        const uint32_t am = (uint32_t)__builtin_ctzll((hit >> (lane & 56)) | 0x100ull);
+        const int k2 = group8_max_all((uint32_t)(n & 7) == am ? INT32_MIN : k);
+        const uint32_t key2 = k2 <= order_key(-__builtin_inff()) ? 0u : (uint32_t)k2 ^ 0x80000000u;
+        if ((n & 7) == 0) {
+          const int blk = 16 * (step - 1 + half) + 4 * wave + (n >> 3);
+          bm_st[blk] = __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+          aux_st[blk] = block_aux_word(key2, am);
+        }
+      } else {
+        sv_prev = sv;
+      }
+    } else {
+      sc[step] = sv;
+    }
+  }
+  if constexpr (STAGED) {
+    // one coalesced store per thread: thread i writes block i of the tile (small stores
+    // after every step measured slower)
+    __syncthreads();
+    const int64_t b = (int64_t)blockIdx.x * (TILE / 8) + threadIdx.x;
+    if (threadIdx.x < TILE / 8 && b * 8 < ld) {
+      block_max[(int64_t)t * ld_bm + b] = bm_st[threadIdx.x];
+      if constexpr (AUX) block_aux[(int64_t)t * ld_bm + b] = aux_st[threadIdx.x];
+    }
+    return;
   }
 #pragma unroll
   for (int step = 0; step < STEPS; ++step) {
     const int64_t slot = slot_at(step);
-    const float sv = sc[step];
+    const float sv = sc[STAGED ? 0 : step];
     if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
     if (block_max != nullptr) {
       float m = sv;
@@ -678,7 +755,7 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
                               int64_t n_entries, const int64_t* kv_start,
                               const int32_t* n_visible, const int32_t* pool_blocks, int n_pool,
                               float* scores, int64_t ld, float* block_max, int64_t ld_bm,
-                              hipStream_t stream) {
+                              uint32_t* block_aux, hipStream_t stream) {
   const int tile = (IS_THREADS / 64) * (reindex ? IS_STEPS_REINDEX : IS_STEPS_FULL) * 32;
   const int64_t tiles = (ld + tile - 1) / tile;
   dim3 grid((unsigned)tiles, (unsigned)n_q);
@@ -699,8 +776,16 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
   } else if (reindex) {
     go(index_score_kernel<true, KF_E4M3>);
   } else {
-    hipLaunchKernelGGL(index_score_full_e4m3_kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w,
-                       k_cache, n_entries, kv_start, n_visible, scores, ld, block_max, ld_bm);
+    auto full = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w, k_cache, n_entries,
+                         kv_start, n_visible, scores, ld, block_max, ld_bm, block_aux);
+    };
+    if (block_aux != nullptr)
+      full(index_score_full_e4m3_kernel<2>);
+    else if (scores == nullptr && block_max != nullptr)
+      full(index_score_full_e4m3_kernel<1>);
+    else
+      full(index_score_full_e4m3_kernel<0>);
   }
   return hipGetLastError();
 }

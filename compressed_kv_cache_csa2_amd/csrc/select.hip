@@ -62,9 +62,6 @@ struct SelShared {
   uint32_t gpos[8 * SEL_THREADS];      // per-group counts, then offsets, in index order
 };
 
-// Unsigned minimum / maximum (the device min/max overloads compare as signed int).
-__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
-__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // Exclusive prefix sum over the block's threads; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, SelShared& sh, uint32_t* total) {
@@ -870,6 +867,245 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_cand_kernel(
     prow[r] = (uint32_t)r < kept ? sh.obuf[r] : -1;
     if ((uint32_t)r >= total) crow[r] = -1;
   }
+}
+
+// The decoder Full layer's whole selection in one workgroup per query: the HSI pool and
+// its candidate blocks (as block_pool_cand_kernel), then the Top-K among the candidates'
+// positions (as topk_kernel with pool_use 2 over their rescored slots would give it) from
+// the Full pass's block statistics. A winner of the Top-K lies in a candidate block and is
+// either the block's argmax, whose score is the block maximum, or another slot, whose score
+// is at most the block's second score; and the k-th best score is at least the threshold t2
+// that the candidates reach (k real blocks reach it, each through its own argmax). So each
+// candidate block contributes its argmax with its maximum, except the few whose stored
+// second key reaches t2: those are rescored, all 8 slots, with the layer's indexer query
+// (e4m3_step_score, the Full pass's own arithmetic, so bit-identical scores). The elements
+// are laid out in ascending position order, so ties go to the lower position and the
+// winners come out ascending, exactly as from the separate calls. Without a threshold, or
+// with more elements than fit, every candidate block is rescored.
+constexpr int FS_SLOTS = CAND_BLOCKS_CAP * 8;   // 16,384: every slot of every candidate
+constexpr int FS_ELEMS = FS_SLOTS / 2;          // element scores and positions side by side
+
+struct FullSelShared {
+  SelShared sel;
+  union {
+    float cscore[FS_SLOTS];   // all rescored: score of candidate slot i
+    struct {
+      float escore[FS_ELEMS];   // element scores, ascending position order
+      int32_t epos[FS_ELEMS];   // their positions
+    } el;
+  };
+};
+
+// Scores held in LDS, read as a key row.
+struct LdsScoreSrc {
+  const float* s;
+  template <int R>
+  __device__ __forceinline__ void load(uint32_t first, uint32_t stride, uint32_t n,
+                                       uint32_t (&keys)[R]) const {
+#pragma unroll
+    for (int g = 0; g < R / 4; ++g) {
+      const uint32_t i0 = first + g * stride;
+      const float4 v = *reinterpret_cast<const float4*>(s + (i0 < n ? i0 : 0u));
+      keys4(v, i0, n, &keys[4 * g]);
+    }
+  }
+};
+
+__global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
+    const float* __restrict__ block_max, int64_t ld_bm, const int32_t* __restrict__ n_visible,
+    int n_keep, int32_t* __restrict__ pool, int64_t ld_pool, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_cache, int64_t n_entries,
+    const int64_t* __restrict__ kv_start, const uint32_t* __restrict__ block_aux, int k,
+    int32_t* __restrict__ out, int64_t ld_idx) {
+  __shared__ FullSelShared fs;
+  SelShared& sh = fs.sel;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int half = lane >> 5;
+
+  const int64_t nv = n_visible[t];
+  const int64_t base = kv_start[t];
+  int64_t nb = nv > 0 ? (nv + 7) >> 3 : 0;
+  if (nb > ld_bm) nb = ld_bm;
+  const float* bm_row = block_max + (int64_t)t * ld_bm;
+  const uint32_t* aux_row = block_aux + (int64_t)t * ld_bm;
+  uint32_t t2 = 0u;
+  const uint32_t kept = select_pool(bm_row, nb, n_keep, sh, (uint32_t)k + 1u, &t2);
+  __syncthreads();
+
+  // Indexer operands (issued here, after the pool selection's registers are free).
+  bf16x8 a[8];
+  const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+
+  // The pool goes out; its candidate blocks (all of it when the first pass gave no
+  // threshold) stay in LDS in ascending order.
+  int32_t* prow = pool + (int64_t)t * ld_pool;
+  uint32_t n_c;
+  if (t2 == 0u) {
+    for (int r = tid; r < n_keep; r += SEL_THREADS) {
+      const int32_t b = (uint32_t)r < kept ? sh.obuf[r] : -1;
+      prow[r] = b;
+      sh.cblocks[r] = b;
+    }
+    n_c = kept < (uint32_t)n_keep ? kept : (uint32_t)n_keep;
+  } else {
+    const uint32_t forced = (uint32_t)nb - 1u;
+    uint32_t f[2];
+    int32_t bl[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t r = 2u * tid + j;
+      bl[j] = r < kept ? sh.obuf[r] : -1;
+      const float v = bl[j] >= 0 ? bm_row[bl[j]] : 0.f;
+      const uint32_t key = bl[j] < 0 ? 0u : block_key(v, (uint32_t)bl[j], forced,
+                                                      __builtin_inff(), (uint32_t)nb);
+      f[j] = key >= t2 ? 1u : 0u;
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan(f[0] + f[1], sh, &total);
+    if (f[0]) sh.cblocks[excl] = bl[0];
+    if (f[1]) sh.cblocks[excl + f[0]] = bl[1];
+    for (int r = tid; r < n_keep; r += SEL_THREADS)
+      prow[r] = (uint32_t)r < kept ? sh.obuf[r] : -1;
+    n_c = total;
+  }
+  __syncthreads();
+
+  // Elements: thread tid lays out candidate ranks 2*tid and 2*tid + 1. One scan gives the
+  // element offsets (low 16 bits) and the rescored-block ranks (high 16 bits).
+  int32_t cb[2];
+  uint32_t cnt[2], rs[2], amax[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t r = 2u * tid + j;
+    cb[j] = r < n_c ? sh.cblocks[r] : -1;
+    const uint32_t word = cb[j] >= 0 ? aux_row[cb[j]] : 0u;
+    rs[j] = cb[j] >= 0 && (t2 == 0u || (word & ~7u) >= t2) ? 1u : 0u;
+    cnt[j] = cb[j] < 0 ? 0u : (rs[j] ? 8u : 1u);
+    amax[j] = word & 7u;   // the block's argmax slot
+  }
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan((cnt[0] + cnt[1]) | ((rs[0] + rs[1]) << 16), sh,
+                                             &total);
+  const uint32_t n_el = total & 0xFFFFu;
+  const uint32_t n_r = total >> 16;
+  const bool mixed = n_el <= (uint32_t)FS_ELEMS;
+  int32_t* rblk = sh.obuf;                               // rescored blocks (mixed layout)
+  uint32_t* roff = sh.gpos;                              // their first element
+  if (mixed) {
+    uint32_t e = excl & 0xFFFFu;
+    uint32_t rr = excl >> 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (cb[j] < 0) continue;
+      if (rs[j]) {
+        rblk[rr] = cb[j];
+        roff[rr] = e;
+        ++rr;
+      } else {
+        fs.el.escore[e] = bm_row[cb[j]];
+        fs.el.epos[e] = cb[j] * 8 + (int32_t)amax[j];
+      }
+      e += cnt[j];
+    }
+  }
+  __syncthreads();
+
+  // Rescoring: 32-slot steps of four blocks (the rescored ones, or every candidate), taken
+  // by the 16 wavefronts in turn, each loading its next step's rows while it multiplies the
+  // current one.
+  const uint32_t n_blk = mixed ? n_r : n_c;
+  const int n_steps = (int)((n_blk + 3) / 4);
+  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  auto block_of = [&](int step) -> int32_t {
+    const uint32_t j = 4u * (uint32_t)step + (uint32_t)(n >> 3);
+    if (j >= n_blk) return -1;
+    return mixed ? rblk[j] : sh.cblocks[j];
+  };
+  auto row_of = [&](int32_t b) -> int64_t {
+    if (b < 0) return -1;
+    const int64_t pos = (int64_t)b * 8 + (n & 7);
+    if (pos >= nv) return -1;
+    const int64_t row = base + pos;
+    return (row >= 0 && row < n_entries) ? row : -1;
+  };
+  auto load_rows = [&](int64_t r, u32x4 (&raw)[4]) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : base) * 128 + 64 * half);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = p[i];
+  };
+  auto put = [&](int step, int32_t b, float sv) {
+    const uint32_t j = 4u * (uint32_t)step + (uint32_t)(n >> 3);
+    if (half != 0 || j >= n_blk) return;
+    if (mixed) {
+      const uint32_t e = roff[j] + (uint32_t)(n & 7);
+      fs.el.escore[e] = sv;
+      fs.el.epos[e] = b * 8 + (n & 7);
+    } else {
+      fs.cscore[8 * j + (uint32_t)(n & 7)] = sv;
+    }
+  };
+  if (any) {
+    u32x4 cur[4], nxt[4];
+    int32_t bc = wave < n_steps ? block_of(wave) : -1;
+    int64_t rc = row_of(bc);
+    if (wave < n_steps) load_rows(rc, cur);
+    for (int st = wave; st < n_steps; st += SEL_WAVES) {
+      int32_t bn = -1;
+      int64_t rn = -1;
+      if (st + SEL_WAVES < n_steps) {
+        bn = block_of(st + SEL_WAVES);
+        rn = row_of(bn);
+        load_rows(rn, nxt);
+      }
+      const float sv = e4m3_step_score(a, wr, cur);
+      put(st, bc, rc >= 0 ? sv : -__builtin_inff());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+      bc = bn;
+      rc = rn;
+    }
+  } else {
+    for (int st = wave; st < n_steps; st += SEL_WAVES) put(st, block_of(st), -__builtin_inff());
+  }
+  __syncthreads();
+
+  // The Top-K among the elements (ascending position order), emitted ascending.
+  const uint32_t kk = (uint32_t)k;
+  uint32_t kept_k;
+  if (mixed) {
+    const LdsScoreSrc src{fs.el.escore};
+    kept_k = select_any(src, (int64_t)n_el, kk, sh, [&](uint32_t rank, uint32_t i) {
+      if (rank < kk) sh.obuf[rank] = fs.el.epos[i];
+    });
+  } else {
+    const LdsScoreSrc src{fs.cscore};
+    kept_k = select_any(src, (int64_t)n_c * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
+      if (rank < kk) sh.obuf[rank] = (int32_t)((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
+    });
+  }
+  __syncthreads();
+  write_out(sh, kept_k, k, out + (int64_t)t * ld_idx);
+}
+
+hipError_t launch_full_select(int n_q, const float* block_max, int64_t ld_bm,
+                              const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
+                              int64_t ld_pool, const uint16_t* q_idx, const float* w,
+                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
+                              const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(full_select_kernel, dim3(n_q), dim3(SEL_THREADS), 0, stream, block_max,
+                     ld_bm, n_visible, n_keep, pool_blocks, ld_pool, q_idx, w, k_cache, n_entries,
+                     kv_start, block_aux, k, topk_idx, ld_idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_pool_cand(int n_q, const float* block_max, int64_t ld_bm,

@@ -13,7 +13,7 @@ hipError_t stub() { return hipErrorNotSupported; }
 
 hipError_t launch_index_score(bool, int, int, const uint16_t*, const float*, const uint8_t*,
                               const uint8_t*, int64_t, const int64_t*, const int32_t*,
-                              const int32_t*, int, float*, int64_t, float*, int64_t,
+                              const int32_t*, int, float*, int64_t, float*, int64_t, uint32_t*,
                               hipStream_t) { return stub(); }
 hipError_t launch_block_mean_keys(int, const uint8_t*, int64_t, const int64_t*, const int32_t*,
                                   uint16_t*, const int64_t*, int64_t, int64_t, int32_t*, bool,
@@ -32,6 +32,12 @@ hipError_t launch_pool_topk(int, const float*, int64_t, const int32_t*, int, int
                             hipStream_t) { return stub(); }
 hipError_t launch_block_pool_cand(int, const float*, int64_t, const int32_t*, int, int32_t*,
                                   int64_t, int, int32_t*, int64_t, hipStream_t) { return stub(); }
+hipError_t launch_full_select(int, const float*, int64_t, const int32_t*, int, int32_t*, int64_t,
+                              const uint16_t*, const float*, const uint8_t*, int64_t,
+                              const int64_t*, const uint32_t*, int, int32_t*, int64_t,
+                              hipStream_t) {
+  return stub();
+}
 hipError_t launch_sparse_attn(int, const uint16_t*, const uint8_t*, int64_t, const uint8_t*,
                               int64_t, int64_t, const int64_t*, const int32_t*, int64_t, int,
                               const uint8_t*, int64_t, const int64_t*, const int32_t*, float,

@@ -1,9 +1,10 @@
 """Mode routing of CSA2 layers over the C ABI (caller side: buffers only, no arithmetic).
 
 Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_score(FULL, block
-         maxima only) -> pool_candidates (the pool, and the pool blocks that can hold a Full
-         winner) -> index_score over those candidates with the same query -> topk among
-         their slots -> sparse_attn
+         maxima and block statistics) -> full_select (the pool and the Top-K among the
+         pool blocks that can hold a Full winner; E4M3 keys and bf16 query) or, for other
+         formats, block maxima only -> pool_candidates -> index_score over the candidates
+         -> topk among their slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
 SWA:     sparse_attn over the sliding window alone (the encoder's first two layers)
@@ -31,6 +32,7 @@ from .synth import POOL_BLOCKS, TOPK, BLOCK
 class Buffers:
     scores: torch.Tensor        # f32 [n_q, ld]
     block_max: torch.Tensor     # f32 [n_q, ceil(ld/8)]
+    block_aux: torch.Tensor     # i32 [n_q, ceil(ld/8)] block statistics of a Full pass
     pool: torch.Tensor          # i32 [n_q, 2048]
     cand: torch.Tensor          # i32 [n_q, 2048] the Full layer's candidate blocks
     re_scores: torch.Tensor     # f32 [n_q, 16384]
@@ -74,6 +76,7 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
     return Buffers(
         scores=torch.empty((n_q, ld), dtype=torch.float32, device=dev),
         block_max=torch.empty((n_q, (ld + BLOCK - 1) // BLOCK), dtype=torch.float32, device=dev),
+        block_aux=torch.empty((n_q, (ld + BLOCK - 1) // BLOCK), dtype=torch.int32, device=dev),
         pool=torch.full((n_q, POOL_BLOCKS), -1, dtype=torch.int32, device=dev),
         cand=torch.full((n_q, POOL_BLOCKS), -1, dtype=torch.int32, device=dev),
         re_scores=torch.empty((n_q, POOL_BLOCKS * BLOCK), dtype=torch.float32, device=dev),
@@ -87,8 +90,23 @@ def alloc_buffers(wl, k: int = TOPK) -> Buffers:
     )
 
 
+# Above this many (query, position) pairs per Full pass the block statistics' extra write
+# costs the pass more than the one-kernel selection saves (measured: 32 x 262,144 pairs,
+# statistics +5 us against a 12 us faster selection; 64 x 1,048,576 pairs, +51 us against
+# 23 us), so larger passes take the three calls.
+FUSED_SELECT_MAX_PAIRS = 1 << 24
+
+
+def fused_full_select(wl) -> bool:
+    """Whether a pooled decoder Full layer of this workload takes its pool and Top-K from
+    one csa2_full_select call (E4M3 keys, bf16 indexer query, at most
+    FUSED_SELECT_MAX_PAIRS scored pairs)."""
+    return (wl.with_pool and wl.k_codes is None and not wl.q8
+            and wl.n_q * wl.n_ctx <= FUSED_SELECT_MAX_PAIRS)
+
+
 def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
-                stream=None, buf=None):
+                stream=None, buf=None, block_aux=None):
     """The indexer over the layer group's keys: MXFP4 when the workload carries them (with
     the layer's query in MXFP8, already quantised into buf, when wl.q8), else E4M3; a Full
     pass of queries sharing one sequence scores them in groups per cache tile."""
@@ -121,7 +139,7 @@ def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scor
     else:
         C.csa2_index_score(mode, lay.q_idx, lay.w, k_cache, wl.kv_start, wl.n_visible,
                            scores, block_max, pool_blocks=pool_blocks, stream=stream,
-                           ld_scores=ld_scores)
+                           ld_scores=ld_scores, block_aux=block_aux)
 
 
 def hisa_select(wl, lay, buf: Buffers, means: BlockMeans, out_idx, k: int = TOPK,
@@ -172,15 +190,27 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
                 # maxima. The pool holds every Full-layer winner, and so do the pool's
                 # candidate blocks (those ranked near the top by maximum, about a quarter of
                 # the pool), so the Top-K is taken among the candidates' slots rescored with
-                # this layer's own indexer query: the same scores, bit for bit.
-                index_score(wl, C.FULL, lay, None, buf.block_max,
-                            ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
-                C.csa2_pool_candidates(buf.block_max, wl.n_visible, buf.pool, buf.cand,
-                                       n_keep=POOL_BLOCKS, k=k, stream=stream)
-                index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.cand,
-                            stream=stream, buf=buf)
-                C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.cand,
-                            stream=stream)
+                # this layer's own indexer query: the same scores, bit for bit. With E4M3
+                # keys and the bf16 query the pass also writes each block's argmax and second
+                # score, and one kernel takes the pool and the Top-K from them, rescoring only
+                # the few blocks whose second score can win (csa2_full_select); the other
+                # key and query formats take the three calls.
+                if fused_full_select(wl):
+                    index_score(wl, C.FULL, lay, None, buf.block_max,
+                                ld_scores=buf.scores.shape[1], stream=stream, buf=buf,
+                                block_aux=buf.block_aux)
+                    C.csa2_full_select(buf.block_max, buf.block_aux, wl.n_visible, buf.pool,
+                                       lay.q_idx, lay.w, wl.cache(lay.group)[0], wl.kv_start,
+                                       buf.idx[li], n_keep=POOL_BLOCKS, k=k, stream=stream)
+                else:
+                    index_score(wl, C.FULL, lay, None, buf.block_max,
+                                ld_scores=buf.scores.shape[1], stream=stream, buf=buf)
+                    C.csa2_pool_candidates(buf.block_max, wl.n_visible, buf.pool, buf.cand,
+                                           n_keep=POOL_BLOCKS, k=k, stream=stream)
+                    index_score(wl, C.REINDEX, lay, buf.re_scores, pool_blocks=buf.cand,
+                                stream=stream, buf=buf)
+                    C.csa2_topk(buf.re_scores, buf.idx[li], k=k, pool_blocks=buf.cand,
+                                stream=stream)
             else:
                 index_score(wl, C.FULL, lay, buf.scores, buf.block_max, stream=stream, buf=buf)
                 C.csa2_topk(buf.scores, buf.idx[li], k=k, n_valid=wl.n_visible,

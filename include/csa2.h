@@ -111,14 +111,22 @@ size_t csa2_workspace_bytes(int op, int n_q, int64_t max_cols, int k);
  *       scores[t, 8b .. 8b+7] over the slots that exist; requires
  *       ld_block_max >= ceil(ld_scores/8). These maxima are what csa2_block_pool ranks,
  *       and csa2_topk uses them to skip blocks that cannot hold a winner.
- * Errors: CSA2_ERR_INVALID_ARG for NULL scores outside that case. */
+ *   block_aux [n_q,ld_block_max] uint32 output, may be NULL; FULL mode with block_max only:
+ *       the block statistics csa2_full_select reads. Bits 0..2 hold the block's argmax (the
+ *       lowest slot whose score equals block_max[t,b]); the bits above hold the selection
+ *       key of the largest score among its other slots (the order-preserving image of the
+ *       float: sign bit flipped for non-negative values, all bits flipped for negative
+ *       ones; 0 when no other slot has a score other than -inf), rounded up to a multiple
+ *       of 8, so the stored word, masked to its upper bits, is never below that key.
+ * Errors: CSA2_ERR_INVALID_ARG for NULL scores outside that case, or block_aux outside
+ *   it. */
 int csa2_index_score(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                      const void* q_idx, const float* w,
                      const void* k_cache, int64_t n_entries,
                      const int64_t* kv_start, const int32_t* n_visible,
                      const int32_t* pool_blocks, int n_pool, int block_size,
                      float* scores, int64_t ld_scores,
-                     float* block_max, int64_t ld_block_max,
+                     float* block_max, int64_t ld_block_max, uint32_t* block_aux,
                      void* stream);
 
 /* Lightning-indexer score, FULL mode, for queries that share one sequence (chunked
@@ -385,6 +393,32 @@ int csa2_pool_candidates(int n_q, const float* block_max, int64_t ld_bm,
                          const int32_t* n_visible, int block_size, int n_keep,
                          int32_t* pool_blocks, int64_t ld_pool, int k, int32_t* cand_blocks,
                          int64_t ld_cand, void* stream);
+
+/* The decoder Full layer's whole selection in one call, for E4M3 indexer keys and a bf16
+ * indexer query ([V41F-BLOG] 2.3.1, 2.3.2 and 2.3.4; [V41F-ARCH] 2 and 3): the HSI pool
+ * (exactly what csa2_block_pool writes into pool_blocks) and the Full layer's Top-K
+ * (exactly what csa2_topk returns over the whole score row of csa2_index_score (FULL) for
+ * the same query: the k best visible positions, ties to the lower position, ascending, -1
+ * padded), from the Full pass's block maxima and block statistics. The Top-K lies in the
+ * pool's candidate blocks (as csa2_pool_candidates defines them, with threshold t2); in
+ * each, a winner is the argmax (score = the block maximum) or another slot scoring at most
+ * the block's second score, while the k-th best score reaches t2; so only the candidate
+ * blocks whose second key reaches t2 are rescored (with q_idx and w against k_cache,
+ * repeating the Full pass's arithmetic step for step) and every other candidate enters
+ * with its argmax alone. It replaces csa2_pool_candidates + csa2_index_score (REINDEX over
+ * the candidates) + csa2_topk.
+ *   block_max, ld_bm, n_visible, block_size, n_keep, pool_blocks, ld_pool: as
+ *       csa2_block_pool; block_max and block_aux [n_q, ld_bm] (uint32) are those written
+ *       by one csa2_index_score (FULL) pass of this q_idx and w;
+ *   n_heads, d_idx, q_idx, w, k_cache, n_entries, kv_start: as csa2_index_score (E4M3 keys);
+ *   1 <= k < n_keep; topk_idx [n_q, ld_idx] int32, ld_idx >= k.
+ * Caller-owned device buffers, no scratch; errors as csa2_block_pool and csa2_index_score. */
+int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
+                     int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
+                     int n_heads, int d_idx, const void* q_idx, const float* w,
+                     const void* k_cache, int64_t n_entries, const int64_t* kv_start,
+                     const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                     void* stream);
 
 /* Joint sparse attention over the selected entries and the sliding window
  * ([V41F-BLOG] 2.2.2, 3.3.1 and 3.3.2 "the readout"; [V41F-ARCH] 2 and 4).

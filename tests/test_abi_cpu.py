@@ -25,7 +25,7 @@ def test_header_symbols_are_exported(C):
                      "csa2_index_score_shared", "csa2_index_score_bf16",
                      "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
                      "csa2_quantize_mxfp8", "csa2_index_score_mxfp4_q8", "csa2_index_score_q8",
-                     "csa2_index_score_shared_q8", "csa2_pool_candidates",
+                     "csa2_index_score_shared_q8", "csa2_pool_candidates", "csa2_full_select",
                      "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
@@ -39,7 +39,7 @@ FAKE = 0x10000   # a 64 KiB-aligned address: never dereferenced, validation fail
 def _score(C, **kw):
     a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE, k_cache=FAKE, n_entries=10,
              kv_start=FAKE, n_visible=FAKE, pool_blocks=None, n_pool=0, block_size=8, scores=FAKE,
-             ld=16, block_max=None, ld_bm=0, stream=None)
+             ld=16, block_max=None, ld_bm=0, block_aux=None, stream=None)
     a.update(kw)
     return C.lib.csa2_index_score(*a.values())
 
@@ -59,6 +59,10 @@ def test_index_score_rejections(C):
     assert _score(C, block_max=FAKE, ld_bm=1) == 1        # ld_bm < ceil(16/8)
     assert _score(C, scores=None) == 1                    # no scores and no block maxima
     assert b"only in FULL mode with block_max" in C.lib.csa2_last_error()
+    assert _score(C, block_aux=FAKE) == 1                 # block statistics need block_max
+    assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2, block_max=FAKE, ld_bm=2,
+                  block_aux=FAKE) == 1                    # ... and a FULL pass
+    assert _score(C, block_max=FAKE, ld_bm=2, block_aux=FAKE + 2) == 1   # misaligned
     assert _score(C, mode=1, pool_blocks=FAKE, n_pool=2, scores=None,
                   block_max=FAKE, ld_bm=2) == 1           # REINDEX always writes scores
     assert _score(C, n_q=0, q_idx=None) == 0              # nothing to do, nothing launched
@@ -288,6 +292,36 @@ def test_pool_candidates_rejections(C):
     assert _pool_cand(C, n_q=0) == 0                        # nothing to do
 
 
+def _full_select(C, **kw):
+    a = dict(n_q=2, block_max=FAKE, ld_bm=8, n_visible=FAKE, block_size=8, n_keep=2048,
+             pool_blocks=FAKE, ld_pool=2048, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE,
+             k_cache=FAKE, n_entries=100, kv_start=FAKE, block_aux=FAKE, k=512, topk_idx=FAKE,
+             ld_idx=512, stream=None)
+    a.update(kw)
+    return C.lib.csa2_full_select(*a.values())
+
+
+def test_full_select_rejections(C):
+    assert _full_select(C, k=2048) == 1                      # k must stay below n_keep
+    assert _full_select(C, k=0) == 1
+    assert _full_select(C, n_keep=4096) == 1
+    assert _full_select(C, block_size=4) == 2
+    assert _full_select(C, n_heads=64) == 2
+    assert _full_select(C, d_idx=64) == 2
+    assert _full_select(C, q_idx=None) == 1
+    assert _full_select(C, topk_idx=None) == 1
+    assert _full_select(C, block_aux=None) == 1
+    assert _full_select(C, block_aux=FAKE + 2) == 1         # misaligned
+    assert _full_select(C, q_idx=FAKE + 8) == 1             # not 16-byte aligned
+    assert _full_select(C, k_cache=FAKE + 4) == 1
+    assert _full_select(C, block_max=FAKE + 4) == 1
+    assert _full_select(C, ld_bm=6) == 1                    # not a multiple of 4
+    assert _full_select(C, ld_pool=100) == 1
+    assert _full_select(C, ld_idx=100) == 1
+    assert _full_select(C, n_entries=-1) == 1
+    assert _full_select(C, n_q=0) == 0                      # nothing to do
+
+
 def test_wrappers_reject_mis_shaped_tensors_before_any_call(C):
     """The Python binding checks every tensor's shape against the query count and the
     compiled sizes before a pointer reaches the library (host tensors: a well-shaped one
@@ -321,6 +355,21 @@ def test_wrappers_reject_mis_shaped_tensors_before_any_call(C):
         lambda: C.csa2_block_pool(bm, nv, torch.zeros((n, 100), dtype=i32)),
         lambda: C.csa2_pool_candidates(bm, nv, torch.zeros((n, 2048), dtype=i32),
                                        torch.zeros((n, 2047), dtype=i32)),
+        lambda: C.csa2_full_select(bm, torch.zeros(bm.shape, dtype=i32), nv,
+                                   torch.zeros((n, 2048), dtype=i32), q[:3], w, kc, ks,
+                                   torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_full_select(bm, torch.zeros(bm.shape, dtype=i32), nv,
+                                   torch.zeros((n, 2048), dtype=i32), q, w,
+                                   torch.zeros((100, 64), dtype=u8), ks,
+                                   torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_full_select(bm, torch.zeros(bm.shape, dtype=i32), nv,
+                                   torch.zeros((n, 2048), dtype=i32), q, w, kc, ks,
+                                   torch.zeros((n, 100), dtype=i32)),
+        lambda: C.csa2_full_select(bm, torch.zeros((n, 7), dtype=i32), nv,
+                                   torch.zeros((n, 2048), dtype=i32), q, w, kc, ks,
+                                   torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_index_score(0, q, w, kc, ks, nv, sc, block_max=bm,
+                                   block_aux=torch.zeros((n, 3), dtype=i32)),
         lambda: C.csa2_topk(sc, torch.zeros((n, 100), dtype=i32), k=512),
         lambda: C.csa2_topk(sc, torch.zeros((3, 512), dtype=i32)),
         lambda: C.csa2_sparse_attn(torch.zeros((n, 64, 512), dtype=bf),

@@ -202,14 +202,16 @@ def test_index_score_empty_cache(C, dev):
     n_vis = torch.full((n_q,), 500, dtype=torch.int32, device=dev)
     scores = torch.zeros((n_q, ld), dtype=torch.float32, device=dev)
     bm = torch.zeros((n_q, (ld + 7) // 8), dtype=torch.float32, device=dev)
+    aux = torch.full((n_q, (ld + 7) // 8), 5, dtype=torch.int32, device=dev)
     P = ctypes.c_void_p
     rc = C.lib.csa2_index_score(C.FULL, n_q, 32, 128, P(q_idx.data_ptr()), P(w.data_ptr()),
                                 P(k_cache.data_ptr()), 0, P(kv_start.data_ptr()),
                                 P(n_vis.data_ptr()), None, 0, 8, P(scores.data_ptr()), ld,
-                                P(bm.data_ptr()), bm.shape[1], None)
+                                P(bm.data_ptr()), bm.shape[1], P(aux.data_ptr()), None)
     assert rc == 0, C.lib.csa2_last_error()
     torch.cuda.synchronize()
     assert torch.all(torch.isneginf(scores)) and torch.all(torch.isneginf(bm))
+    assert torch.all(aux == 0)   # argmax slot 0, no selectable second score
 
 
 @pytest.mark.parametrize("kind,n,k,use_bmax", [

@@ -1,7 +1,9 @@
 """The decoder Full layer's pool and candidate blocks (csa2_pool_candidates) on the GPU: the
 pool equals csa2_block_pool's bit for bit, the candidates are a subset of it, and the Top-K
 taken among the candidates' rescored slots equals, bit for bit, the Top-K among all pool
-slots (the route the chain tests hold to the oracle) and the oracle's whole-row selection."""
+slots (the route the chain tests hold to the oracle) and the oracle's whole-row selection.
+The one-kernel route (csa2_full_select: pool, rescoring and Top-K on chip) gives the same
+pool and Top-K bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +36,22 @@ def _both_routes(wl, k=512):
     C.csa2_index_score(C.REINDEX, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible,
                        buf.re_scores, pool_blocks=pool_b)
     C.csa2_topk(buf.re_scores, idx_b, k=k, pool_blocks=pool_b)
+    # the one-kernel route: a Full pass that also writes the block statistics (its block
+    # maxima must equal the plain pass's bit for bit), then csa2_full_select
+    bm_c = torch.full_like(buf.block_max, 7.0)
+    aux_c = torch.full_like(buf.block_aux, -5)
+    C.csa2_index_score(C.FULL, lay.q_idx, lay.w, wl.k_cache, wl.kv_start, wl.n_visible, None,
+                       bm_c, ld_scores=buf.scores.shape[1], block_aux=aux_c)
+    pool_c = torch.full_like(buf.pool, -5)
+    idx_c = torch.full_like(idx_a, -5)
+    C.csa2_full_select(bm_c, aux_c, wl.n_visible, pool_c, lay.q_idx, lay.w, wl.k_cache,
+                       wl.kv_start, idx_c, n_keep=2048, k=k)
     torch.cuda.synchronize()
+    nb = buf.block_max.shape[1]
+    for t in range(wl.n_q):
+        live = min(nb, (int(wl.n_visible[t]) + 7) // 8)
+        assert torch.equal(bm_c[t, :live], buf.block_max[t, :live]), "block maxima differ"
+    assert torch.equal(pool_c, pool_b) and torch.equal(idx_c, idx_b), "one-kernel route differs"
     return pool_a, cand, idx_a, pool_b, idx_b
 
 
@@ -95,3 +112,49 @@ def test_candidates_with_ties_everywhere(dev):
         gp = pool_a[t].cpu().numpy()
         assert_set_band(gp[gp >= 0], O.hsi_pool(s, n_visible[t]), lambda b: bm[b], kb, bb,
                         f"pool {t}")
+
+
+def _key(v):
+    """Selection key of float32 values (0 for -inf): the order-preserving unsigned image."""
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    k = np.where(u & 0x80000000, ~u & 0xFFFFFFFF, u | 0x80000000)
+    return np.where(np.isfinite(v) | (v > 0), k, 0).astype(np.uint64)
+
+
+def test_block_statistics_match_the_pass_scores(dev):
+    """One Full pass writing scores, block maxima and block statistics: every block's
+    maximum is the largest of its 8 scores, the argmax is the lowest slot holding it, and the
+    stored second key is the largest key of the other slots rounded up to a multiple of 8
+    (the pass's own scores, bit for bit; ties and partial last blocks included)."""
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import synth
+    n_visible = [40000, 17, 8, 0, 4099]
+    wl = synth.make_decode("bs", len(n_visible), 0, ("full",), True, 16, n_visible=n_visible,
+                           kv_gap=3, seed=43).to(dev)
+    kc = wl.k_cache
+    # runs of equal keys in the second query: ties inside blocks
+    st = int(wl.kv_start[1])
+    kc[st:st + 16] = kc[st:st + 1].expand(16, -1)
+    lay = wl.layers[0]
+    ld = 40000
+    scores = torch.empty((len(n_visible), ld), dtype=torch.float32, device=dev)
+    bm = torch.empty((len(n_visible), ld // 8), dtype=torch.float32, device=dev)
+    aux = torch.empty((len(n_visible), ld // 8), dtype=torch.int32, device=dev)
+    C.csa2_index_score(C.FULL, lay.q_idx, lay.w, kc, wl.kv_start, wl.n_visible, scores, bm,
+                       block_aux=aux)
+    torch.cuda.synchronize()
+    s_all, bm_all = scores.cpu().numpy(), bm.cpu().numpy()
+    aux_all = aux.cpu().numpy().view(np.uint32).astype(np.uint64)
+    for t, nv in enumerate(n_visible):
+        nb = (nv + 7) // 8
+        if nb == 0:
+            continue
+        s = s_all[t, :nb * 8].reshape(nb, 8)
+        keys = _key(s)
+        arg = np.argmax(keys, axis=1)                       # first (lowest) maximal slot
+        assert np.array_equal(bm_all[t, :nb], s[np.arange(nb), arg])
+        assert np.array_equal(aux_all[t, :nb] & 7, arg)
+        others = keys.copy()
+        others[np.arange(nb), arg] = 0
+        k2 = others.max(axis=1)
+        assert np.array_equal(aux_all[t, :nb] & ~np.uint64(7), (k2 + 7) & ~np.uint64(7)), t

@@ -21,7 +21,7 @@ import ctypes, os
 from compressed_kv_cache_csa2_amd import csa2 as C
 assert C._LIB_PATH == os.environ["CSA2_LIBRARY"], C._LIB_PATH
 F = 0x10000
-st = C.lib.csa2_index_score(0, 1, 32, 128, F, F, F, 10, F, F, None, 0, 8, F, 16, None, 0, None)
+st = C.lib.csa2_index_score(0, 1, 32, 128, F, F, F, 10, F, F, None, 0, 8, F, 16, None, 0, None, None)
 msg = C.lib.csa2_last_error()
 assert st != 0 and b"launch failed" in msg, (st, msg)
 print("stub reached:", msg.decode())
