@@ -41,6 +41,7 @@ constexpr int IS_THREADS = 256;
 constexpr int IS_STEPS_FULL = 16;
 constexpr int IS_STEPS_REINDEX = 4;
 constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is multiplied
+constexpr int FULL_PF_STAGED = 2;   // the same for the Full E4M3 pass without a score row
 
 // Indexer-key formats: E4M3 rows of 128 bytes, MXFP4 rows (64 code bytes + 4 E8M0 scale
 // bytes in a separate array) and bf16 rows of 256 bytes (the block-mean keys of the
@@ -261,7 +262,10 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
                                              16 * piece);
     }
   };
-  u32x4 g[4];
+  // Rows of PF steps are in flight while a step is multiplied (more for the staged modes,
+  // which keep no score array).
+  constexpr int PF = MODE != 0 ? FULL_PF_STAGED : 1;
+  u32x4 g[PF][4];
   // MODE 0: scores and maxima go out after the tile (the score row is the bulk of the
   // writes); MODE 1: block maxima only, reduced as each step completes and staged in LDS;
   // MODE 2: as 1, plus the block statistics (scores, if asked, stored as each step ends).
@@ -272,7 +276,10 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
   static_assert(STEPS % 2 == 0, "block statistics pair the steps");
   __shared__ float bm_st[STAGED ? TILE / 8 : 1];    // block maxima of the tile
   __shared__ uint32_t aux_st[AUX ? TILE / 8 : 1];   // block statistics of the tile
-  if (any) load_step(0, g);
+  if (any) {
+#pragma unroll
+    for (int p0 = 0; p0 < PF; ++p0) load_step(p0, g[p0]);
+  }
 #pragma unroll
   for (int step = 0; step < STEPS; ++step) {
     float sv = -__builtin_inff();
@@ -281,9 +288,9 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + (lane >> 3);
-        buf[r * 8 + (piece ^ (r & 7))] = g[i];
+        buf[r * 8 + (piece ^ (r & 7))] = g[step % PF][i];
       }
-      if (step + 1 < STEPS) load_step(step + 1, g);
+      if (step + PF < STEPS) load_step(step + PF, g[step % PF]);
       // LDS operations of one wavefront complete in order; the fences keep the compiler
       // from moving the reads above the writes.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -516,10 +516,10 @@ __global__ __launch_bounds__(AT_THREADS) void sparse_attn_kernel(
 // Items go in slices of 32 (the window's slices first, then the selected entries'); per
 // slice:
 //   - wavefront w gathers items 4w .. 4w+3 (lane (item, p): channels 32p .. 32p+31) and
-//     stores them converted to fp16 (exact, as above) in an LDS tile, one 1,056-byte row per
-//     item, its 16-byte pieces swizzled (piece c of row r at c ^ ((r / 8) % 2)) so that the
-//     row reads of the logit product and the transposed reads of the value product are
-//     free of bank conflicts; barrier;
+//     stores them converted to fp16 (exact, as above) in an LDS tile, one 1,056-byte row
+//     per item, its 16-byte pieces permuted (ah_off) so that these stores, the row reads of
+//     the logit product and the transposed reads of the value product are free of bank
+//     conflicts; barrier;
 //   - wavefront (head tile w % 4, item half w / 4) computes S (16 items x 16 heads) with
 //     v_mfma_f32_16x16x32_f16 (A = tile rows, B = its heads' queries, held in registers),
 //     turns it into weights p = 2^(l - ref) with a per-head reference ref and stores them,
@@ -545,9 +545,15 @@ struct AttnHeadsShared {
   int flag;                              // a logit overflowed the reference
 };
 
-// Element offset of channel ch (a multiple of 4) of tile row r, with the piece swizzle.
+// Element offset of channel ch (a multiple of 4) of tile row r. Rows are 1,056 bytes apart
+// (8 dwords past a multiple of 32 banks) and the 16-byte pieces of a row are permuted,
+// piece p of row r at p ^ ((p / 8) % 4) ^ ((r / 4) % 2). Then the conversion's stores (16
+// lanes of a row write pieces 4g + j, g = 0..15), the logit operand reads (8 rows, one
+// piece each) and the transpose reads (two adjacent pieces of 4 rows) each reach 32
+// distinct banks per group of lanes served together.
 __device__ __forceinline__ int ah_off(int r, int ch) {
-  return r * AH_ROW + ((((ch >> 3) ^ ((r >> 3) & 1))) << 3) + (ch & 7);
+  const int p = ch >> 3;
+  return r * AH_ROW + ((p ^ ((p >> 3) & 3) ^ ((r >> 2) & 1)) << 3) + (ch & 7);
 }
 
 __global__ __launch_bounds__(AH_THREADS) void sparse_attn_heads_kernel(
