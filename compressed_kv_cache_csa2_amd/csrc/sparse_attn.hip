@@ -708,14 +708,25 @@ __global__ __launch_bounds__(AH_THREADS) void sparse_attn_heads_kernel(
       __syncthreads();
 
       // Logits of items 16 * ih + 4 * grp + i for head h.
+      // Operand reads four k-steps at a time into two independent product chains (even and
+      // odd k-steps), so LDS latency and the matrix core's result latency overlap.
       const int row = 16 * ih + gcol;
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 s_even = {0.f, 0.f, 0.f, 0.f}, s_odd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(tile + ah_off(row, 32 * ks + 8 * grp));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), qop[ks], sacc,
-                                                      0, 0, 0);
+      for (int k4 = 0; k4 < 16; k4 += 4) {
+        u32x4 av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          av[i] = *reinterpret_cast<const u32x4*>(tile + ah_off(row, 32 * (k4 + i) + 8 * grp));
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          s_even = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[i]),
+                                                          qop[k4 + i], s_even, 0, 0, 0);
+          s_odd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[i + 1]),
+                                                         qop[k4 + i + 1], s_odd, 0, 0, 0);
+        }
       }
+      const f32x4 sacc = s_even + s_odd;
       float lg[4];
       bool any_valid = false;
 #pragma unroll
