@@ -18,7 +18,8 @@ per group of queries, so there the indexer is priced against the bf16 matrix pea
 (8,192 flops per (query, entry) pair) instead of HBM.
 Its algorithmic bytes per launch are 128 B of indexer K read + 0.5 B of block maximum
 written per (query, entry) pair (+ 4 B of score where the step keeps the scores: stacks
-without a pool), plus the indexer queries and weights; its average launch duration is
+without a pool; + 0.5 B of block statistics where the decoder Full layer's one-kernel
+selection reads them), plus the indexer queries and weights; its average launch duration is
 measured with HIP events on its own stream over K back-to-back launches.
 
 roofline.traffic: HBM bytes per indexer launch from rocprofv3 counters (FETCH_SIZE and
@@ -89,8 +90,9 @@ def measured_traffic(workload):
 
 
 def full_indexer(wl, buf, C, stream=None):
-    """The Full-layer indexer as the step launches it: block maxima only in a pooled stack,
-    over the workload's key format."""
+    """The Full-layer indexer as the step launches it: block maxima only in a pooled stack
+    (with the block statistics where the one-kernel selection follows), over the workload's
+    key format."""
     from compressed_kv_cache_csa2_amd import layers
     lay = next(l for l in wl.layers if l.mode == "full")
     layers.index_score(wl, C.FULL, lay, None if wl.with_pool else buf.scores,
@@ -276,8 +278,13 @@ def key_bytes(wl):
 
 def indexer_bytes_per_launch(wl):
     import torch
+    from compressed_kv_cache_csa2_amd import layers
     pairs = int(wl.n_visible.to(torch.int64).sum())
+    # Per pair: the key row read, 4 B of score where the row is kept, 0.5 B of block
+    # maximum, and 0.5 B of block statistics where the one-kernel selection reads them.
     written = 0.5 if wl.with_pool else 4 + 0.5
+    if layers.fused_full_select(wl):
+        written += 0.5
     return pairs * (key_bytes(wl) + written) + wl.n_q * (32 * 128 * 2 + 32 * 4)
 
 
@@ -366,6 +373,9 @@ def kernel_label(wl, hisa):
         name = "index_score_full_wide_fp4_kernel (Full-layer indexer, " + keys
     else:
         name = "index_score_full_e4m3_kernel (Full-layer indexer, " + keys
+    from compressed_kv_cache_csa2_amd import layers
+    if layers.fused_full_select(wl):
+        return name + ", block maxima and block statistics)"
     return name + (", block maxima only)" if wl.with_pool else ")")
 
 
