@@ -63,15 +63,24 @@ struct SelShared {
 };
 
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP lane moves: shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes (a lane with no source adds 0), then the last lane
+// of row 0 added to row 1 and of row 2 to row 3 (row_bcast:15), and the last lane of row 1
+// to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the block's threads; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, SelShared& sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_add(v);
   if (lane == 63) sh.wsum[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
