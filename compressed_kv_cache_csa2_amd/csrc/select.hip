@@ -7,8 +7,9 @@
 // Compression", 2.3.4; "DeepSeek-V4.1-Flash - Architecture", section 3).
 //
 // One 1024-thread workgroup per query row. Values become order-preserving 32-bit keys
-// (0 marks an element that cannot be selected) held in registers: R = 16 keys per thread
-// for rows up to 16,384 elements, else R = 32 (walked in segments of 32,768 past that).
+// (0 marks an element that cannot be selected) held in registers: R = 4, 8 or 16 keys per
+// thread for rows up to 4,096, 8,192 or 16,384 elements, else R = 32 (walked in segments
+// of 32,768 past that).
 // Thread t holds the R/4 float4 groups starting at elements 4*(t + 1024*g), so each
 // wavefront load reads 1 KiB of consecutive memory.
 //   1. A block reduction gives the count, the smallest and the largest key.
@@ -33,6 +34,8 @@
 // selected exactly. If more than 2,048 blocks tie at the threshold the full row is used.
 #include "csa2_device.h"
 #include "csa2_launch.h"
+
+#include <type_traits>
 
 namespace csa2 {
 
@@ -384,11 +387,12 @@ __device__ __forceinline__ uint32_t group_offsets(uint32_t mask, SelShared& sh) 
 }
 
 // Emit every key > tau and, of the keys == tau, the first n_eq in index order (every one
-// for ALL_TIES). emit(rank, index) with rank = position in ascending index order.
-// Returns the count.
+// for ALL_TIES). emit(rank, index) with rank = position in ascending index order, or
+// emit(rank, index, flag) when the callback takes a third argument: flag = 1 when the
+// key reaches t_flag. Returns the count.
 template <class Row, class Emit>
 __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_t n_eq, SelShared& sh,
-                                 Emit emit) {
+                                 Emit emit, uint32_t t_flag = 0u) {
   constexpr int R = Row::per_thread();
   constexpr int NG = R / 4;
   const int tid = threadIdx.x;
@@ -421,6 +425,11 @@ __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_
       __syncthreads();
     }
     const uint32_t take_total = group_offsets<NG>(take, sh);
+    uint32_t fmask = 0u;
+    if constexpr (std::is_invocable_v<Emit&, uint32_t, uint32_t, uint32_t>) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) fmask |= (uint32_t)(row.keys[r] >= t_flag) << r;
+    }
     // Recomputed here rather than kept from the loads: the opaque copy stops the compiler
     // from holding R element indices live through every pass.
     uint32_t first = Row::first(seg);
@@ -431,8 +440,13 @@ __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_
       rest &= rest - 1u;
       const int g = r >> 2;
       const uint32_t before = __popc(take & ((1u << r) - 1u) & (0xFu << (4 * g)));
-      emit(out_base + sh.gpos[g * SEL_THREADS + tid] + before,
-           first + 4u * SEL_THREADS * (uint32_t)g + (uint32_t)(r & 3));
+      const uint32_t rank = out_base + sh.gpos[g * SEL_THREADS + tid] + before;
+      const uint32_t index = first + 4u * SEL_THREADS * (uint32_t)g + (uint32_t)(r & 3);
+      if constexpr (std::is_invocable_v<Emit&, uint32_t, uint32_t, uint32_t>) {
+        emit(rank, index, (fmask >> r) & 1u);
+      } else {
+        emit(rank, index);
+      }
     }
     out_base += take_total;
     __syncthreads();
@@ -463,7 +477,7 @@ __device__ __forceinline__ uint32_t select_row(Row& row, uint32_t k, SelShared& 
   } else {
     rank_list(row, iv, sh, tau, n_eq);
   }
-  return emit_ordered(row, tau, n_eq, sh, emit);
+  return emit_ordered(row, tau, n_eq, sh, emit, iv.t2);
 }
 
 // --------------------------------------------------------------------------- key sources
@@ -629,12 +643,22 @@ struct CandSrc {
 
 // --------------------------------------------------------------------------- kernels
 
-// Rows of at most 16,384 elements hold 16 keys per thread, longer ones 32 (in segments
-// of 32,768 when longer still).
+// Rows hold the fewest keys per thread that cover them: 4 up to 4,096 elements, 8 up to
+// 8,192, 16 up to 16,384, else 32 (in segments of 32,768 when longer still), so that a
+// short row (the decoder Full layer's few hundred elements) costs few ballots, loads and
+// emission steps per thread.
 template <class Src, class Emit>
 __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32_t k, SelShared& sh,
                                                Emit emit, uint32_t k2 = 0u, uint32_t cap2 = 0u,
                                                uint32_t* t2 = nullptr) {
+  if (n <= (int64_t)SEL_THREADS * 4) {
+    KeyRow<Src, 4, false> row(src, n);
+    return select_row(row, k, sh, emit, k2, cap2, t2);
+  }
+  if (n <= (int64_t)SEL_THREADS * 8) {
+    KeyRow<Src, 8, false> row(src, n);
+    return select_row(row, k, sh, emit, k2, cap2, t2);
+  }
   if (n <= (int64_t)SEL_THREADS * 16) {
     KeyRow<Src, 16, false> row(src, n);
     return select_row(row, k, sh, emit, k2, cap2, t2);
@@ -648,7 +672,8 @@ __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32
 }
 
 // The HSI pool of one query: the n_keep best of its nb block maxima (the forced block
-// nb - 1 reads +inf) into sh.obuf in ascending block order; returns how many. Rows of more
+// nb - 1 reads +inf) into sh.obuf in ascending block order; returns how many. With oflag,
+// oflag[rank] = 1 marks the pool blocks whose key reaches *t2 (a nonzero *t2). Rows of more
 // than 32,768 blocks first keep the n_keep best quads (aligned groups of four blocks,
 // ranked by their largest block): a quad left out has n_keep quads ranked above it, each
 // holding a block that outranks all of its blocks (ties go to the lower index at both
@@ -656,10 +681,13 @@ __device__ __forceinline__ uint32_t select_any(const Src& src, int64_t n, uint32
 // blocks. This replaces several passes over the row by one.
 __device__ __forceinline__ uint32_t select_pool(const float* bm_row, int64_t nb, int n_keep,
                                                 SelShared& sh, uint32_t k2 = 0u,
-                                                uint32_t* t2 = nullptr) {
+                                                uint32_t* t2 = nullptr, uint32_t* oflag = nullptr) {
   const uint32_t kk = (uint32_t)n_keep;
-  auto to_obuf = [&](uint32_t rank, uint32_t b) {
-    if (rank < kk) sh.obuf[rank] = (int32_t)b;
+  auto to_obuf = [&](uint32_t rank, uint32_t b, uint32_t f) {
+    if (rank < kk) {
+      sh.obuf[rank] = (int32_t)b;
+      if (oflag != nullptr) oflag[rank] = f;
+    }
   };
   if (nb <= (int64_t)SEL_THREADS * 32) {
     const BlockSrc src{bm_row, nb - 1, __builtin_inff()};
@@ -674,8 +702,11 @@ __device__ __forceinline__ uint32_t select_pool(const float* bm_row, int64_t nb,
   const QuadBlockSrc bsrc{bm_row, sh.cblocks, nbu - 1u, __builtin_inff(), nbu};
   const uint32_t n_c = n_cq < kk ? n_cq : kk;
   // Element i of the second row is block cblocks[i/4]*4 + i%4.
-  return select_any(bsrc, (int64_t)n_c * 4, kk, sh, [&](uint32_t rank, uint32_t i) {
-    if (rank < kk) sh.obuf[rank] = sh.cblocks[i >> 2] * 4 + (int32_t)(i & 3u);
+  return select_any(bsrc, (int64_t)n_c * 4, kk, sh, [&](uint32_t rank, uint32_t i, uint32_t f) {
+    if (rank < kk) {
+      sh.obuf[rank] = sh.cblocks[i >> 2] * 4 + (int32_t)(i & 3u);
+      if (oflag != nullptr) oflag[rank] = f;
+    }
   }, k2, kk, t2);
 }
 
@@ -942,7 +973,9 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
   const float* bm_row = block_max + (int64_t)t * ld_bm;
   const uint32_t* aux_row = block_aux + (int64_t)t * ld_bm;
   uint32_t t2 = 0u;
-  const uint32_t kept = select_pool(bm_row, nb, n_keep, sh, (uint32_t)k + 1u, &t2);
+  // The pool's candidate flags go to the element area, free until the elements are laid out.
+  uint32_t* pflag = reinterpret_cast<uint32_t*>(fs.el.escore);
+  const uint32_t kept = select_pool(bm_row, nb, n_keep, sh, (uint32_t)k + 1u, &t2, pflag);
   __syncthreads();
 
   // Indexer operands (issued here, after the pool selection's registers are free).
@@ -954,49 +987,55 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
 
-  // The pool goes out; its candidate blocks (all of it when the first pass gave no
-  // threshold) stay in LDS in ascending order.
+  // The pool goes out. Its candidate blocks (those whose key reaches t2, or all of it when
+  // the first pass gave no threshold) stay in LDS in ascending order with their block
+  // maxima and statistics words, whose loads are issued before the scan that places them.
+  float* cval = reinterpret_cast<float*>(sh.gpos);  // candidate block maxima
+  uint32_t* caux = sh.gpos + CAND_BLOCKS_CAP;       // candidate statistics words
   int32_t* prow = pool + (int64_t)t * ld_pool;
   uint32_t n_c;
-  if (t2 == 0u) {
-    for (int r = tid; r < n_keep; r += SEL_THREADS) {
-      const int32_t b = (uint32_t)r < kept ? sh.obuf[r] : -1;
-      prow[r] = b;
-      sh.cblocks[r] = b;
-    }
-    n_c = kept < (uint32_t)n_keep ? kept : (uint32_t)n_keep;
-  } else {
-    const uint32_t forced = (uint32_t)nb - 1u;
-    uint32_t f[2];
+  {
+    uint32_t f[2], word[2];
+    float val[2];
     int32_t bl[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t r = 2u * tid + j;
-      bl[j] = r < kept ? sh.obuf[r] : -1;
-      const float v = bl[j] >= 0 ? bm_row[bl[j]] : 0.f;
-      const uint32_t key = bl[j] < 0 ? 0u : block_key(v, (uint32_t)bl[j], forced,
-                                                      __builtin_inff(), (uint32_t)nb);
-      f[j] = key >= t2 ? 1u : 0u;
+      bl[j] = r < kept && r < (uint32_t)n_keep ? sh.obuf[r] : -1;
+      f[j] = bl[j] >= 0 && (t2 == 0u || pflag[r] != 0u) ? 1u : 0u;
+      word[j] = f[j] ? aux_row[bl[j]] : 0u;
+      val[j] = f[j] ? bm_row[bl[j]] : 0.f;
     }
     uint32_t total;
     const uint32_t excl = block_exclusive_scan(f[0] + f[1], sh, &total);
-    if (f[0]) sh.cblocks[excl] = bl[0];
-    if (f[1]) sh.cblocks[excl + f[0]] = bl[1];
     for (int r = tid; r < n_keep; r += SEL_THREADS)
       prow[r] = (uint32_t)r < kept ? sh.obuf[r] : -1;
+    uint32_t c = excl;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (f[j]) {
+        sh.cblocks[c] = bl[j];
+        cval[c] = val[j];
+        caux[c] = word[j];
+        ++c;
+      }
+    }
     n_c = total;
   }
   __syncthreads();
 
   // Elements: thread tid lays out candidate ranks 2*tid and 2*tid + 1. One scan gives the
-  // element offsets (low 16 bits) and the rescored-block ranks (high 16 bits).
+  // element offsets (low 16 bits) and the rescored-block ranks (high 16 bits). A block that
+  // is not rescored contributes its argmax with the block maximum.
   int32_t cb[2];
   uint32_t cnt[2], rs[2], amax[2];
+  float cv[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t r = 2u * tid + j;
     cb[j] = r < n_c ? sh.cblocks[r] : -1;
-    const uint32_t word = cb[j] >= 0 ? aux_row[cb[j]] : 0u;
+    const uint32_t word = cb[j] >= 0 ? caux[r] : 0u;
+    cv[j] = cb[j] >= 0 ? cval[r] : 0.f;
     rs[j] = cb[j] >= 0 && (t2 == 0u || (word & ~7u) >= t2) ? 1u : 0u;
     cnt[j] = cb[j] < 0 ? 0u : (rs[j] ? 8u : 1u);
     amax[j] = word & 7u;   // the block's argmax slot
@@ -1008,7 +1047,7 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
   const uint32_t n_r = total >> 16;
   const bool mixed = n_el <= (uint32_t)FS_ELEMS;
   int32_t* rblk = sh.obuf;                               // rescored blocks (mixed layout)
-  uint32_t* roff = sh.gpos;                              // their first element
+  uint32_t* roff = sh.gpos + 2 * CAND_BLOCKS_CAP;        // their first element
   if (mixed) {
     uint32_t e = excl & 0xFFFFu;
     uint32_t rr = excl >> 16;
@@ -1020,7 +1059,7 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
         roff[rr] = e;
         ++rr;
       } else {
-        fs.el.escore[e] = bm_row[cb[j]];
+        fs.el.escore[e] = cv[j];
         fs.el.epos[e] = cb[j] * 8 + (int32_t)amax[j];
       }
       e += cnt[j];
