@@ -537,9 +537,7 @@ def breakdown(wl, buf, C, layers, stream, hisa, means):
                       and fused):
                     continue
                 elif part == "pool" and lay.mode == "full" and wl.with_pool and fused:
-                    C.csa2_full_select(buf.block_max, buf.block_aux, wl.n_visible, buf.pool,
-                                       lay.q_idx, lay.w, wl.cache(lay.group)[0], wl.kv_start,
-                                       buf.idx[li], stream=stream)
+                    layers.full_select(wl, lay, buf, buf.idx[li], stream=stream)
                 elif part == "rescore" and lay.mode == "full" and wl.with_pool:
                     layers.index_score(wl, C.REINDEX, lay, buf.re_scores,
                                        pool_blocks=buf.cand, stream=stream, buf=buf)

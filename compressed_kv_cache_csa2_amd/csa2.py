@@ -35,7 +35,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, L, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.csa2_index_score.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P, P]
-    lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
+    lib.csa2_index_score_mxfp4.argtypes = [I, I, I, I, P, P, P, P, L, P, P, P, I, I, P, L, P, L, P,
+                                           P]
     lib.csa2_index_score_bf16.argtypes = [I, I, I, I, P, P, P, L, P, P, P, I, I, P, L, P, L, P]
     lib.csa2_block_mean_keys.argtypes = [I, I, I, P, L, P, P, P, P, L, L, P, I, P]
     lib.csa2_quantize_mxfp8.argtypes = [I, I, P, P, P, P]
@@ -54,6 +55,8 @@ def _load():
     lib.csa2_pool_topk.argtypes = [I, P, L, P, I, I, P, L, P, L, L, I, P, L, P]
     lib.csa2_pool_candidates.argtypes = [I, P, L, P, I, I, P, L, I, P, L, P]
     lib.csa2_full_select.argtypes = [I, P, L, P, I, I, P, L, I, I, P, P, P, L, P, P, I, P, L, P]
+    lib.csa2_full_select_mxfp4.argtypes = [I, P, L, P, I, I, P, L, I, I, P, P, P, P, L, P, P, I, P,
+                                           L, P]
     lib.csa2_sparse_attn.argtypes = [I, I, I, P, P, L, P, L, L, P, P, L, I, P, L, P, P, F, P, P,
                                      P, Z, P]
     for f in ("csa2_index_score_shared", "csa2_write_latent", "csa2_write_e4m3", "csa2_write_mxfp4_key",
@@ -61,7 +64,7 @@ def _load():
               "csa2_sparse_attn", "csa2_index_score_bf16", "csa2_block_mean_keys",
               "csa2_compress_kv", "csa2_project_index_key", "csa2_quantize_mxfp8",
               "csa2_index_score_mxfp4_q8", "csa2_index_score_q8", "csa2_index_score_shared_q8",
-              "csa2_pool_candidates", "csa2_full_select"):
+              "csa2_pool_candidates", "csa2_full_select", "csa2_full_select_mxfp4"):
         getattr(lib, f).restype = I
     lib.csa2_workspace_bytes.argtypes = [I, I, L, I]
     lib.csa2_workspace_bytes.restype = Z
@@ -342,9 +345,11 @@ def csa2_index_score_shared(q_idx, w, k_cache, kv_start: int, n_visible, scores,
 
 
 def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visible, scores,
-                           block_max=None, pool_blocks=None, stream=None, ld_scores=None):
+                           block_max=None, pool_blocks=None, stream=None, ld_scores=None,
+                           block_aux=None):
     """csa2_index_score over MXFP4 indexer keys: k_codes uint8 [E, 64] (two E2M1 codes per
-    byte, low nibble first) and k_scales uint8 [E, 4] (E8M0, one per 32 channels)."""
+    byte, low nibble first) and k_scales uint8 [E, 4] (E8M0, one per 32 channels). block_aux
+    as csa2_index_score's, for csa2_full_select_mxfp4."""
     n_q = q_idx.shape[0]
     n_pool = pool_blocks.shape[1] if pool_blocks is not None else 0
     if scores is not None:
@@ -358,6 +363,8 @@ def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visibl
     _dims(k_scales, "csa2_index_score_mxfp4: k_scales", k_codes.shape[0], 4)
     _index_common("csa2_index_score_mxfp4", n_q, w, kv_start, n_visible, scores, block_max,
                   pool_blocks, ld_scores)
+    if block_aux is not None and (block_max is None or block_aux.shape != block_max.shape):
+        raise ValueError("csa2_index_score_mxfp4: block_aux needs block_max and its shape")
     _check(lib.csa2_index_score_mxfp4(
         mode, n_q, q_idx.shape[1], q_idx.shape[2], _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(k_codes, torch.uint8, "k_codes"),
@@ -366,7 +373,8 @@ def csa2_index_score_mxfp4(mode, q_idx, w, k_codes, k_scales, kv_start, n_visibl
         _ptr(pool_blocks, torch.int32, "pool_blocks"), n_pool, 8,
         _ptr(scores, torch.float32, "scores"), ld_scores,
         _ptr(block_max, torch.float32, "block_max"),
-        block_max.shape[1] if block_max is not None else 0, _stream(stream)))
+        block_max.shape[1] if block_max is not None else 0,
+        _ptr(block_aux, torch.int32, "block_aux"), _stream(stream)))
 
 
 def csa2_block_mean_keys(k_cache, kv_start, n_visible, km, km_start, n_blocks, max_blocks=None,
@@ -486,23 +494,30 @@ def csa2_pool_candidates(block_max, n_visible, pool_blocks, cand_blocks, n_keep=
         _ptr(cand_blocks, torch.int32, "cand_blocks"), cand_blocks.shape[1], _stream(stream)))
 
 
+def _full_select_args(fn, block_max, block_aux, n_visible, pool_blocks, q_idx, w, kv_start,
+                      topk_idx, n_keep, k):
+    n_q = block_max.shape[0]
+    _dims(block_max, f"{fn}: block_max", n_q, None)
+    if not isinstance(block_aux, torch.Tensor) or block_aux.shape != block_max.shape:
+        raise ValueError(f"{fn}: block_aux must have block_max's shape")
+    _dims(n_visible, f"{fn}: n_visible", n_q)
+    _dims(pool_blocks, f"{fn}: pool_blocks", n_q, (">=", n_keep))
+    _dims(q_idx, f"{fn}: q_idx", n_q, 32, 128)
+    _dims(w, f"{fn}: w", n_q, 32)
+    _dims(kv_start, f"{fn}: kv_start", n_q)
+    _dims(topk_idx, f"{fn}: topk_idx", n_q, (">=", k))
+    return n_q
+
+
 def csa2_full_select(block_max, block_aux, n_visible, pool_blocks, q_idx, w, k_cache, kv_start,
                      topk_idx, n_keep=2048, k=512, stream=None):
     """The decoder Full layer's selection in one call (E4M3 keys, bf16 query): the HSI pool
     into `pool_blocks` [n_q, >= n_keep] and the Full Top-K into `topk_idx` [n_q, >= k], from
     the block maxima and statistics (block_aux) of the Full pass of q_idx [n_q, 32, 128] and
     w [n_q, 32] over k_cache [E, 128]."""
-    n_q = block_max.shape[0]
-    _dims(block_max, "csa2_full_select: block_max", n_q, None)
-    if not isinstance(block_aux, torch.Tensor) or block_aux.shape != block_max.shape:
-        raise ValueError("csa2_full_select: block_aux must have block_max's shape")
-    _dims(n_visible, "csa2_full_select: n_visible", n_q)
-    _dims(pool_blocks, "csa2_full_select: pool_blocks", n_q, (">=", n_keep))
-    _dims(q_idx, "csa2_full_select: q_idx", n_q, 32, 128)
-    _dims(w, "csa2_full_select: w", n_q, 32)
+    n_q = _full_select_args("csa2_full_select", block_max, block_aux, n_visible, pool_blocks,
+                            q_idx, w, kv_start, topk_idx, n_keep, k)
     _dims(k_cache, "csa2_full_select: k_cache", None, 128)
-    _dims(kv_start, "csa2_full_select: kv_start", n_q)
-    _dims(topk_idx, "csa2_full_select: topk_idx", n_q, (">=", k))
     _check(lib.csa2_full_select(
         n_q, _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
         _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
@@ -511,6 +526,27 @@ def csa2_full_select(block_max, block_aux, n_visible, pool_blocks, q_idx, w, k_c
         _ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
         _ptr(kv_start, torch.int64, "kv_start"), _ptr(block_aux, torch.int32, "block_aux"), k,
         _ptr(topk_idx, torch.int32, "topk_idx"), topk_idx.shape[1], _stream(stream)))
+
+
+def csa2_full_select_mxfp4(block_max, block_aux, n_visible, pool_blocks, q_idx, w, k_codes,
+                           k_scales, kv_start, topk_idx, n_keep=2048, k=512, stream=None):
+    """csa2_full_select over MXFP4 indexer keys (k_codes uint8 [E, 64], k_scales uint8
+    [E, 4]), from the block maxima and statistics of the csa2_index_score_mxfp4 Full pass."""
+    n_q = _full_select_args("csa2_full_select_mxfp4", block_max, block_aux, n_visible,
+                            pool_blocks, q_idx, w, kv_start, topk_idx, n_keep, k)
+    if k_codes.shape[0] != k_scales.shape[0]:
+        raise ValueError("csa2_full_select_mxfp4: k_codes and k_scales row counts differ")
+    _dims(k_codes, "csa2_full_select_mxfp4: k_codes", None, 64)
+    _dims(k_scales, "csa2_full_select_mxfp4: k_scales", k_codes.shape[0], 4)
+    _check(lib.csa2_full_select_mxfp4(
+        n_q, _ptr(block_max, torch.float32, "block_max"), block_max.shape[1],
+        _ptr(n_visible, torch.int32, "n_visible"), 8, n_keep,
+        _ptr(pool_blocks, torch.int32, "pool_blocks"), pool_blocks.shape[1], 32, 128,
+        _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
+        _ptr(k_codes, torch.uint8, "k_codes"), _ptr(k_scales, torch.uint8, "k_scales"),
+        k_codes.shape[0], _ptr(kv_start, torch.int64, "kv_start"),
+        _ptr(block_aux, torch.int32, "block_aux"), k, _ptr(topk_idx, torch.int32, "topk_idx"),
+        topk_idx.shape[1], _stream(stream)))
 
 
 def csa2_sparse_attn(q, kv_fp4, kv_scale, kv_start, topk_idx, window_kv, swa_start, n_swa,

@@ -105,8 +105,9 @@ static int index_score_common(const char* fn, int key_format, csa2_mode_t mode, 
     REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_max", fn);
   }
   if (block_aux != nullptr) {
-    REQUIRE(key_format == 0 && mode == CSA2_FULL && block_max != nullptr, CSA2_ERR_INVALID_ARG,
-            "%s: block_aux is written by a FULL pass over E4M3 keys beside block_max", fn);
+    REQUIRE(key_format != 2 && mode == CSA2_FULL && block_max != nullptr, CSA2_ERR_INVALID_ARG,
+            "%s: block_aux is written by a FULL pass over E4M3 or MXFP4 keys beside block_max",
+            fn);
     REQUIRE(aligned(block_aux, 4), CSA2_ERR_INVALID_ARG, "%s: misaligned block_aux", fn);
   }
   return hip_status(csa2::launch_index_score(
@@ -168,13 +169,13 @@ int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx, co
                            int64_t n_entries, const int64_t* kv_start, const int32_t* n_visible,
                            const int32_t* pool_blocks, int n_pool, int block_size, float* scores,
                            int64_t ld_scores, float* block_max, int64_t ld_block_max,
-                           void* stream) {
+                           uint32_t* block_aux, void* stream) {
   REQUIRE(n_q == 0 || k_scales != nullptr, CSA2_ERR_INVALID_ARG,
           "csa2_index_score_mxfp4: null k_scales");
   return index_score_common("csa2_index_score_mxfp4", 1, mode, n_q, n_heads, d_idx, q_idx, w,
                             k_codes, k_scales, n_entries, kv_start, n_visible, pool_blocks,
                             n_pool, block_size, scores, ld_scores, block_max, ld_block_max,
-                            nullptr, stream);
+                            block_aux, stream);
 }
 
 int csa2_index_score_bf16(csa2_mode_t mode, int n_q, int n_heads, int d_idx, const void* q_idx,
@@ -572,13 +573,13 @@ int csa2_pool_candidates(int n_q, const float* block_max, int64_t ld_bm,
                     fn);
 }
 
-int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
-                     int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
-                     int n_heads, int d_idx, const void* q_idx, const float* w,
-                     const void* k_cache, int64_t n_entries, const int64_t* kv_start,
-                     const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
-                     void* stream) {
-  const char* fn = "csa2_full_select";
+static int full_select_common(const char* fn, int n_q, const float* block_max, int64_t ld_bm,
+                              const int32_t* n_visible, int block_size, int n_keep,
+                              int32_t* pool_blocks, int64_t ld_pool, int n_heads, int d_idx,
+                              const void* q_idx, const float* w, const void* k_cache,
+                              const void* k_scales, int64_t n_entries, const int64_t* kv_start,
+                              const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                              void* stream) {
   REQUIRE(block_size == CSA2_CANDIDATE_BLOCK_SIZE, CSA2_ERR_UNSUPPORTED,
           "%s: block_size %d, only %d is built", fn, block_size, CSA2_CANDIDATE_BLOCK_SIZE);
   REQUIRE(n_heads == CSA2_IDX_HEADS && d_idx == CSA2_IDX_DIM, CSA2_ERR_UNSUPPORTED,
@@ -599,16 +600,45 @@ int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32
   REQUIRE(aligned(block_max, 16) && ld_bm % 4 == 0, CSA2_ERR_INVALID_ARG,
           "%s: block_max must be 16-byte aligned with ld_bm a multiple of 4", fn);
   REQUIRE(aligned(q_idx, 16) && aligned(k_cache, 16), CSA2_ERR_INVALID_ARG,
-          "%s: q_idx and k_cache must be 16-byte aligned", fn);
+          "%s: q_idx and the key rows must be 16-byte aligned", fn);
+  REQUIRE(k_scales == nullptr || aligned(k_scales, 4), CSA2_ERR_INVALID_ARG,
+          "%s: misaligned k_scales", fn);
   REQUIRE(aligned(w, 4) && aligned(kv_start, 8) && aligned(n_visible, 4) &&
               aligned(pool_blocks, 4) && aligned(topk_idx, 4) && aligned(block_aux, 4),
           CSA2_ERR_INVALID_ARG, "%s: misaligned argument", fn);
   return hip_status(csa2::launch_full_select(n_q, block_max, ld_bm, n_visible, n_keep, pool_blocks,
                                              ld_pool, static_cast<const uint16_t*>(q_idx), w,
-                                             static_cast<const uint8_t*>(k_cache), n_entries,
+                                             static_cast<const uint8_t*>(k_cache),
+                                             static_cast<const uint8_t*>(k_scales), n_entries,
                                              kv_start, block_aux, k, topk_idx, ld_idx,
                                              static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32_t* n_visible,
+                     int block_size, int n_keep, int32_t* pool_blocks, int64_t ld_pool,
+                     int n_heads, int d_idx, const void* q_idx, const float* w,
+                     const void* k_cache, int64_t n_entries, const int64_t* kv_start,
+                     const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                     void* stream) {
+  return full_select_common("csa2_full_select", n_q, block_max, ld_bm, n_visible, block_size,
+                            n_keep, pool_blocks, ld_pool, n_heads, d_idx, q_idx, w, k_cache,
+                            nullptr, n_entries, kv_start, block_aux, k, topk_idx, ld_idx, stream);
+}
+
+int csa2_full_select_mxfp4(int n_q, const float* block_max, int64_t ld_bm,
+                           const int32_t* n_visible, int block_size, int n_keep,
+                           int32_t* pool_blocks, int64_t ld_pool, int n_heads, int d_idx,
+                           const void* q_idx, const float* w, const void* k_codes,
+                           const void* k_scales, int64_t n_entries, const int64_t* kv_start,
+                           const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                           void* stream) {
+  REQUIRE(n_q == 0 || k_scales != nullptr, CSA2_ERR_INVALID_ARG,
+          "csa2_full_select_mxfp4: null k_scales");
+  return full_select_common("csa2_full_select_mxfp4", n_q, block_max, ld_bm, n_visible,
+                            block_size, n_keep, pool_blocks, ld_pool, n_heads, d_idx, q_idx, w,
+                            k_codes, k_scales, n_entries, kv_start, block_aux, k, topk_idx,
+                            ld_idx, stream);
 }
 
 int csa2_sparse_attn(int n_q, int n_heads, int head_dim, const void* q, const void* kv_fp4,

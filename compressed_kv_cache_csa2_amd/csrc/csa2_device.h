@@ -106,6 +106,28 @@ __device__ __forceinline__ float e4m3_step_score(const bf16x8 (&a)[8], const flo
   return part;
 }
 
+// The same over MXFP4 keys: lane (n, half) holds in raw[0..1] the code bytes 32*half .. +31
+// of position n's row (channels 64*half .. +63) and in raw[2].x the row's four E8M0 scale
+// bytes; k-block kb is code dword kb with the scale of group 2*half + kb/4. Every indexer
+// path over MXFP4 keys with a bf16 query uses exactly these operations in this order.
+__device__ __forceinline__ float mxfp4_step_score(const bf16x8 (&a)[8], const float (&wr)[16],
+                                                  const u32x4 (&raw)[4], int half) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    const uint32_t d = raw[kb >> 2][kb & 3];
+    const uint32_t e = (raw[2].x >> (8 * (2 * half + (kb >> 2)))) & 0xFFu;
+    const u32x4 bv = fp4x8_to_bf16x8_pow2(d, __uint_as_float(e << 23));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc, 0,
+                                                  0, 0);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+  part += __shfl_xor(part, 32);
+  return part;
+}
+
 // ---- fp16 forms (the attention works in fp16: every E2M1 x E4M3 product, and every E4M3
 // value, is exact in fp16, and packed fp16 multiplies halve the conversion work) ----
 

@@ -56,14 +56,15 @@ hipError_t launch_block_pool_cand(int n_q, const float* block_max, int64_t ld_bm
 
 // The decoder Full layer's selection in one kernel: the pool (as launch_block_pool_cand) and
 // the Top-K among its candidates, from the Full pass's block statistics (block_aux) and the
-// rescoring, with the layer's indexer query over E4M3 keys, of the few candidate blocks
-// whose second score can reach it.
+// rescoring, with the layer's indexer query, of the few candidate blocks whose second score
+// can reach it. k_scales: NULL for E4M3 keys ([E,128] in k_cache); the E8M0 scale rows
+// ([E,4]) for MXFP4 keys, whose codes ([E,64]) are then k_cache.
 hipError_t launch_full_select(int n_q, const float* block_max, int64_t ld_bm,
                               const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
                               int64_t ld_pool, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
-                              const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
-                              hipStream_t stream);
+                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
+                              const int64_t* kv_start, const uint32_t* block_aux, int k,
+                              int32_t* topk_idx, int64_t ld_idx, hipStream_t stream);
 
 hipError_t launch_sparse_attn(int n_q, const uint16_t* q, const uint8_t* kv_fp4,
                               int64_t fp4_stride, const uint8_t* kv_scale, int64_t scale_stride,

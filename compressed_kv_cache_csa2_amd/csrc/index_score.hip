@@ -392,13 +392,18 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
 // holds), after which code dwords 0..7 are the operands of rows 0..31 and dwords 8..15
 // those of rows 32..63. Twice the bytes per load instruction of index_score_kernel's MXFP4
 // path and the same products in the same order: identical scores, about 10% faster.
+// AUX: the block maxima and block statistics (as the E4M3 pass's mode 2 writes them) are
+// reduced as each step completes, staged in LDS and written once per workgroup; scores, if
+// asked, go out as each step ends.
 constexpr int IW_STEPS = IS_STEPS_FULL / 2;   // 64-slot steps per wavefront (same tile)
 
+template <bool AUX>
 __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, int64_t n_entries,
     const int64_t* __restrict__ kv_start, const int32_t* __restrict__ n_visible,
-    float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
+    float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm,
+    uint32_t* __restrict__ block_aux) {
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -435,7 +440,9 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
     for (int i = 0; i < 4; ++i) raw[i] = p[i];
     sw = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
   };
-  float sc[IW_STEPS];
+  float sc[AUX ? 1 : IW_STEPS];
+  __shared__ float bm_st[AUX ? TILE / 8 : 1];       // block maxima of the tile
+  __shared__ uint32_t aux_st[AUX ? TILE / 8 : 1];   // block statistics of the tile
   if (any) load_step(0, buf[0], sbuf[0]);
 #pragma unroll
   for (int step = 0; step < IW_STEPS; ++step) {
@@ -476,12 +483,41 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
       const float mine = half ? part[1] : part[0];
       if (row_at(step) >= 0) sv = mine;
     }
-    sc[step] = sv;
+    if constexpr (AUX) {
+      // The block of 8 consecutive slots lies in 8 consecutive lanes: maximum, argmax (the
+      // lowest lane holding it) and the largest other key, on order-preserving integer
+      // keys with DPP lane moves, as in the E4M3 pass.
+      const int64_t slot = slot_at(step);
+      if (scores != nullptr && slot < ld) scores[(int64_t)t * ld + slot] = sv;
+      const int k = order_key(sv);
+      const int m = group8_max_all(k);
+      const uint64_t hit = __ballot(k == m);
+      const uint32_t am = (uint32_t)__builtin_ctzll((hit >> (lane & 56)) | 0x100ull);
+      const int k2 = group8_max_all((uint32_t)(lane & 7) == am ? INT32_MIN : k);
+      const uint32_t key2 = k2 <= order_key(-__builtin_inff()) ? 0u : (uint32_t)k2 ^ 0x80000000u;
+      if ((lane & 7) == 0) {
+        const int blk = 32 * step + 8 * wave + (lane >> 3);
+        bm_st[blk] = __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+        aux_st[blk] = block_aux_word(key2, am);
+      }
+    } else {
+      sc[step] = sv;
+    }
+  }
+  if constexpr (AUX) {
+    // one coalesced store per thread: thread i writes block i of the tile
+    __syncthreads();
+    const int64_t b = (int64_t)blockIdx.x * (TILE / 8) + threadIdx.x;
+    if (threadIdx.x < TILE / 8 && b * 8 < ld) {
+      block_max[(int64_t)t * ld_bm + b] = bm_st[threadIdx.x];
+      block_aux[(int64_t)t * ld_bm + b] = aux_st[threadIdx.x];
+    }
+    return;
   }
 #pragma unroll
   for (int step = 0; step < IW_STEPS; ++step) {
     const int64_t slot = slot_at(step);
-    const float sv = sc[step];
+    const float sv = sc[AUX ? 0 : step];
     if (scores != nullptr && slot < ld) scores[(int64_t)t * ld + slot] = sv;
     if (block_max != nullptr) {
       float m = sv;
@@ -774,12 +810,19 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
   if (key_format == KF_BF16) {
     reindex ? go(index_score_kernel<true, KF_BF16>) : go(index_score_kernel<false, KF_BF16>);
   } else if (k_scales != nullptr) {
-    if (reindex)
+    if (reindex) {
       go(index_score_kernel<true, KF_MXFP4>);
-    else
-      hipLaunchKernelGGL(index_score_full_wide_fp4_kernel, grid, dim3(IS_THREADS), 0, stream,
-                         q_idx, w, k_cache, k_scales, n_entries, kv_start, n_visible, scores,
-                         ld, block_max, ld_bm);
+    } else {
+      auto wide = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w, k_cache,
+                           k_scales, n_entries, kv_start, n_visible, scores, ld, block_max,
+                           ld_bm, block_aux);
+      };
+      if (block_aux != nullptr)
+        wide(index_score_full_wide_fp4_kernel<true>);
+      else
+        wide(index_score_full_wide_fp4_kernel<false>);
+    }
   } else if (reindex) {
     go(index_score_kernel<true, KF_E4M3>);
   } else {

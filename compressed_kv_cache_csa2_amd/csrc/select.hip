@@ -918,7 +918,8 @@ __global__ __launch_bounds__(SEL_THREADS) void block_pool_cand_kernel(
 // that the candidates reach (k real blocks reach it, each through its own argmax). So each
 // candidate block contributes its argmax with its maximum, except the few whose stored
 // second key reaches t2: those are rescored, all 8 slots, with the layer's indexer query
-// (e4m3_step_score, the Full pass's own arithmetic, so bit-identical scores). The elements
+// (e4m3_step_score or mxfp4_step_score, the Full pass's own arithmetic, so bit-identical
+// scores; FP4K selects MXFP4 keys, codes in k_cache and scales in k_scales). The elements
 // are laid out in ascending position order, so ties go to the lower position and the
 // winners come out ascending, exactly as from the separate calls. Without a threshold, or
 // with more elements than fit, every candidate block is rescored.
@@ -951,10 +952,12 @@ struct LdsScoreSrc {
   }
 };
 
+template <bool FP4K>
 __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
     const float* __restrict__ block_max, int64_t ld_bm, const int32_t* __restrict__ n_visible,
     int n_keep, int32_t* __restrict__ pool, int64_t ld_pool, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w, const uint8_t* __restrict__ k_cache, int64_t n_entries,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_cache,
+    const uint8_t* __restrict__ k_scales, int64_t n_entries,
     const int64_t* __restrict__ kv_start, const uint32_t* __restrict__ block_aux, int k,
     int32_t* __restrict__ out, int64_t ld_idx) {
   __shared__ FullSelShared fs;
@@ -1086,7 +1089,15 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
     return (row >= 0 && row < n_entries) ? row : -1;
   };
   auto load_rows = [&](int64_t r, u32x4 (&raw)[4]) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + (r >= 0 ? r : base) * 128 + 64 * half);
+    const int64_t rr = r >= 0 ? r : base;
+    if constexpr (FP4K) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 64 + 32 * half);
+      raw[0] = p[0];
+      raw[1] = p[1];
+      raw[2].x = *reinterpret_cast<const uint32_t*>(k_scales + rr * 4);
+      return;
+    }
+    const u32x4* p = reinterpret_cast<const u32x4*>(k_cache + rr * 128 + 64 * half);
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[i] = p[i];
   };
@@ -1114,7 +1125,7 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
         rn = row_of(bn);
         load_rows(rn, nxt);
       }
-      const float sv = e4m3_step_score(a, wr, cur);
+      const float sv = FP4K ? mxfp4_step_score(a, wr, cur, half) : e4m3_step_score(a, wr, cur);
       put(st, bc, rc >= 0 ? sv : -__builtin_inff());
 #pragma unroll
       for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
@@ -1147,12 +1158,17 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
 hipError_t launch_full_select(int n_q, const float* block_max, int64_t ld_bm,
                               const int32_t* n_visible, int n_keep, int32_t* pool_blocks,
                               int64_t ld_pool, const uint16_t* q_idx, const float* w,
-                              const uint8_t* k_cache, int64_t n_entries, const int64_t* kv_start,
-                              const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
-                              hipStream_t stream) {
-  hipLaunchKernelGGL(full_select_kernel, dim3(n_q), dim3(SEL_THREADS), 0, stream, block_max,
-                     ld_bm, n_visible, n_keep, pool_blocks, ld_pool, q_idx, w, k_cache, n_entries,
-                     kv_start, block_aux, k, topk_idx, ld_idx);
+                              const uint8_t* k_cache, const uint8_t* k_scales, int64_t n_entries,
+                              const int64_t* kv_start, const uint32_t* block_aux, int k,
+                              int32_t* topk_idx, int64_t ld_idx, hipStream_t stream) {
+  if (k_scales != nullptr)
+    hipLaunchKernelGGL(full_select_kernel<true>, dim3(n_q), dim3(SEL_THREADS), 0, stream,
+                       block_max, ld_bm, n_visible, n_keep, pool_blocks, ld_pool, q_idx, w,
+                       k_cache, k_scales, n_entries, kv_start, block_aux, k, topk_idx, ld_idx);
+  else
+    hipLaunchKernelGGL(full_select_kernel<false>, dim3(n_q), dim3(SEL_THREADS), 0, stream,
+                       block_max, ld_bm, n_visible, n_keep, pool_blocks, ld_pool, q_idx, w,
+                       k_cache, k_scales, n_entries, kv_start, block_aux, k, topk_idx, ld_idx);
   return hipGetLastError();
 }
 

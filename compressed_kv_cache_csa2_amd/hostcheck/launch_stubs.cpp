@@ -33,8 +33,8 @@ hipError_t launch_pool_topk(int, const float*, int64_t, const int32_t*, int, int
 hipError_t launch_block_pool_cand(int, const float*, int64_t, const int32_t*, int, int32_t*,
                                   int64_t, int, int32_t*, int64_t, hipStream_t) { return stub(); }
 hipError_t launch_full_select(int, const float*, int64_t, const int32_t*, int, int32_t*, int64_t,
-                              const uint16_t*, const float*, const uint8_t*, int64_t,
-                              const int64_t*, const uint32_t*, int, int32_t*, int64_t,
+                              const uint16_t*, const float*, const uint8_t*, const uint8_t*,
+                              int64_t, const int64_t*, const uint32_t*, int, int32_t*, int64_t,
                               hipStream_t) {
   return stub();
 }

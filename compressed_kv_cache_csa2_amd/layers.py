@@ -2,9 +2,9 @@
 
 Full:    index_score(FULL) -> topk -> sparse_attn; in a decoder stack index_score(FULL, block
          maxima and block statistics) -> full_select (the pool and the Top-K among the
-         pool blocks that can hold a Full winner; E4M3 keys and bf16 query) or, for other
-         formats, block maxima only -> pool_candidates -> index_score over the candidates
-         -> topk among their slots -> sparse_attn
+         pool blocks that can hold a Full winner; E4M3 or MXFP4 keys, bf16 query) or, with
+         the MXFP8 query, block maxima only -> pool_candidates -> index_score over the
+         candidates -> topk among their slots -> sparse_attn
 Reindex: index_score(REINDEX, over the pool) -> topk inside the pool -> sparse_attn
 Reuse:   sparse_attn with the indices published by the latest Full or Reindex layer
 SWA:     sparse_attn over the sliding window alone (the encoder's first two layers)
@@ -99,10 +99,24 @@ FUSED_SELECT_MAX_PAIRS = 1 << 24
 
 def fused_full_select(wl) -> bool:
     """Whether a pooled decoder Full layer of this workload takes its pool and Top-K from
-    one csa2_full_select call (E4M3 keys, bf16 indexer query, at most
-    FUSED_SELECT_MAX_PAIRS scored pairs)."""
-    return (wl.with_pool and wl.k_codes is None and not wl.q8
-            and wl.n_q * wl.n_ctx <= FUSED_SELECT_MAX_PAIRS)
+    one csa2_full_select (E4M3 keys) or csa2_full_select_mxfp4 call (bf16 indexer query, at
+    most FUSED_SELECT_MAX_PAIRS scored pairs)."""
+    return wl.with_pool and not wl.q8 and wl.n_q * wl.n_ctx <= FUSED_SELECT_MAX_PAIRS
+
+
+def full_select(wl, lay, buf: Buffers, out_idx, k: int = TOPK, stream=None):
+    """The pool and the Top-K of a pooled decoder Full layer from the block maxima and block
+    statistics its Full pass left in buf, over the layer group's key format."""
+    if wl.k_codes is not None:
+        if lay.group != 0:
+            raise ValueError("MXFP4 keys are carried for cache set 0 only")
+        C.csa2_full_select_mxfp4(buf.block_max, buf.block_aux, wl.n_visible, buf.pool,
+                                 lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                                 out_idx, n_keep=POOL_BLOCKS, k=k, stream=stream)
+    else:
+        C.csa2_full_select(buf.block_max, buf.block_aux, wl.n_visible, buf.pool, lay.q_idx,
+                           lay.w, wl.cache(lay.group)[0], wl.kv_start, out_idx,
+                           n_keep=POOL_BLOCKS, k=k, stream=stream)
 
 
 def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scores=None,
@@ -135,7 +149,7 @@ def index_score(wl, mode, lay, scores, block_max=None, pool_blocks=None, ld_scor
             raise ValueError("MXFP4 keys are carried for cache set 0 only")
         C.csa2_index_score_mxfp4(mode, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
                                  wl.n_visible, scores, block_max, pool_blocks=pool_blocks,
-                                 stream=stream, ld_scores=ld_scores)
+                                 stream=stream, ld_scores=ld_scores, block_aux=block_aux)
     else:
         C.csa2_index_score(mode, lay.q_idx, lay.w, k_cache, wl.kv_start, wl.n_visible,
                            scores, block_max, pool_blocks=pool_blocks, stream=stream,
@@ -191,17 +205,15 @@ def run_layers(wl, buf: Buffers, k: int = TOPK, stream=None, coarse: str = "hsi"
                 # candidate blocks (those ranked near the top by maximum, about a quarter of
                 # the pool), so the Top-K is taken among the candidates' slots rescored with
                 # this layer's own indexer query: the same scores, bit for bit. With E4M3
-                # keys and the bf16 query the pass also writes each block's argmax and second
-                # score, and one kernel takes the pool and the Top-K from them, rescoring only
-                # the few blocks whose second score can win (csa2_full_select); the other
-                # key and query formats take the three calls.
+                # the bf16 query the pass also writes each block's argmax and second score,
+                # and one kernel takes the pool and the Top-K from them, rescoring only the
+                # few blocks whose second score can win (csa2_full_select, or its MXFP4-key
+                # form); the MXFP8 query takes the three calls.
                 if fused_full_select(wl):
                     index_score(wl, C.FULL, lay, None, buf.block_max,
                                 ld_scores=buf.scores.shape[1], stream=stream, buf=buf,
                                 block_aux=buf.block_aux)
-                    C.csa2_full_select(buf.block_max, buf.block_aux, wl.n_visible, buf.pool,
-                                       lay.q_idx, lay.w, wl.cache(lay.group)[0], wl.kv_start,
-                                       buf.idx[li], n_keep=POOL_BLOCKS, k=k, stream=stream)
+                    full_select(wl, lay, buf, buf.idx[li], k=k, stream=stream)
                 else:
                     index_score(wl, C.FULL, lay, None, buf.block_max,
                                 ld_scores=buf.scores.shape[1], stream=stream, buf=buf)

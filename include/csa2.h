@@ -153,15 +153,17 @@ int csa2_index_score_shared(int n_q, int n_heads, int d_idx, const void* q_idx, 
  *            32g .. 32g+31; 4-byte aligned.
  * Key value of channel c = E2M1(code c) * 2^(k_scales[c/32] - 127). Supported scale codes
  * are 1..254 with every product inside bf16's normal range (|x| in [2^-126, 2^127]);
- * 0xFF (NaN) is never passed. Errors: as csa2_index_score, plus CSA2_ERR_INVALID_ARG for
- * a NULL or misaligned k_scales. */
+ * 0xFF (NaN) is never passed. block_aux (FULL mode with block_max only, nullable) holds the
+ * same block statistics as csa2_index_score's, here of the MXFP4 scores; csa2_full_select_mxfp4
+ * reads them. Errors: as csa2_index_score, plus CSA2_ERR_INVALID_ARG for a NULL or
+ * misaligned k_scales. */
 int csa2_index_score_mxfp4(csa2_mode_t mode, int n_q, int n_heads, int d_idx,
                            const void* q_idx, const float* w,
                            const void* k_codes, const void* k_scales, int64_t n_entries,
                            const int64_t* kv_start, const int32_t* n_visible,
                            const int32_t* pool_blocks, int n_pool, int block_size,
                            float* scores, int64_t ld_scores,
-                           float* block_max, int64_t ld_block_max,
+                           float* block_max, int64_t ld_block_max, uint32_t* block_aux,
                            void* stream);
 
 /* MXFP8 indexer query (reading R24: the pages' V4 lineage runs the indexer in low
@@ -419,6 +421,21 @@ int csa2_full_select(int n_q, const float* block_max, int64_t ld_bm, const int32
                      const void* k_cache, int64_t n_entries, const int64_t* kv_start,
                      const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
                      void* stream);
+
+/* csa2_full_select for MXFP4 indexer keys ([V41F-BLOG] 2.4.4 and 3.1): the same pool and
+ * Top-K, from the block maxima and block statistics of one csa2_index_score_mxfp4 (FULL)
+ * pass of this q_idx and w, with the rescored candidate slots computed from k_codes and
+ * k_scales exactly as that pass computes them. k_codes, k_scales as csa2_index_score_mxfp4;
+ * other arguments and errors as csa2_full_select, plus CSA2_ERR_INVALID_ARG for a NULL or
+ * misaligned k_scales. It replaces csa2_pool_candidates + csa2_index_score_mxfp4 (REINDEX
+ * over the candidates) + csa2_topk. */
+int csa2_full_select_mxfp4(int n_q, const float* block_max, int64_t ld_bm,
+                           const int32_t* n_visible, int block_size, int n_keep,
+                           int32_t* pool_blocks, int64_t ld_pool, int n_heads, int d_idx,
+                           const void* q_idx, const float* w, const void* k_codes,
+                           const void* k_scales, int64_t n_entries, const int64_t* kv_start,
+                           const uint32_t* block_aux, int k, int32_t* topk_idx, int64_t ld_idx,
+                           void* stream);
 
 /* Joint sparse attention over the selected entries and the sliding window
  * ([V41F-BLOG] 2.2.2, 3.3.1 and 3.3.2 "the readout"; [V41F-ARCH] 2 and 4).

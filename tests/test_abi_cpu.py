@@ -26,7 +26,7 @@ def test_header_symbols_are_exported(C):
                      "csa2_block_mean_keys", "csa2_compress_kv", "csa2_project_index_key",
                      "csa2_quantize_mxfp8", "csa2_index_score_mxfp4_q8", "csa2_index_score_q8",
                      "csa2_index_score_shared_q8", "csa2_pool_candidates", "csa2_full_select",
-                     "csa2_version", "csa2_last_error"}
+                     "csa2_full_select_mxfp4", "csa2_version", "csa2_last_error"}
     lib = ctypes.CDLL(C._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -73,7 +73,7 @@ def test_index_score_mxfp4_rejections(C):
         a = dict(mode=0, n_q=1, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE, k_codes=FAKE,
                  k_scales=FAKE, n_entries=10, kv_start=FAKE, n_visible=FAKE, pool_blocks=None,
                  n_pool=0, block_size=8, scores=FAKE, ld=16, block_max=None, ld_bm=0,
-                 stream=None)
+                 block_aux=None, stream=None)
         a.update(kw)
         return C.lib.csa2_index_score_mxfp4(*a.values())
     assert call(k_scales=None) == 1 and b"null k_scales" in C.lib.csa2_last_error()
@@ -82,6 +82,10 @@ def test_index_score_mxfp4_rejections(C):
     assert call(mode=2) == 1 and b"csa2_index_score_mxfp4" in C.lib.csa2_last_error()
     assert call(n_heads=64) == 2
     assert call(scores=None) == 1
+    assert call(block_aux=FAKE) == 1                      # block statistics need block_max
+    assert call(mode=1, pool_blocks=FAKE, n_pool=2, block_max=FAKE, ld_bm=2,
+                block_aux=FAKE) == 1                      # ... and a FULL pass
+    assert call(block_max=FAKE, ld_bm=2, block_aux=FAKE + 2) == 1   # misaligned
     assert call(n_q=0, k_scales=None, q_idx=None) == 0    # nothing to do, nothing launched
 
 
@@ -322,6 +326,26 @@ def test_full_select_rejections(C):
     assert _full_select(C, n_q=0) == 0                      # nothing to do
 
 
+def test_full_select_mxfp4_rejections(C):
+    def call(**kw):
+        a = dict(n_q=2, block_max=FAKE, ld_bm=8, n_visible=FAKE, block_size=8, n_keep=2048,
+                 pool_blocks=FAKE, ld_pool=2048, n_heads=32, d_idx=128, q_idx=FAKE, w=FAKE,
+                 k_codes=FAKE, k_scales=FAKE, n_entries=100, kv_start=FAKE, block_aux=FAKE,
+                 k=512, topk_idx=FAKE, ld_idx=512, stream=None)
+        a.update(kw)
+        return C.lib.csa2_full_select_mxfp4(*a.values())
+    assert call(k_scales=None) == 1 and b"null k_scales" in C.lib.csa2_last_error()
+    assert call(k_scales=FAKE + 2) == 1 and b"k_scales" in C.lib.csa2_last_error()
+    assert call(k_codes=FAKE + 8) == 1                      # codes not 16-byte aligned
+    assert call(k=2048) == 1
+    assert call(block_size=4) == 2
+    assert call(n_heads=64) == 2
+    assert call(block_aux=None) == 1
+    assert b"csa2_full_select_mxfp4" in C.lib.csa2_last_error()
+    assert call(ld_idx=100) == 1
+    assert call(n_q=0, k_scales=None) == 0                  # nothing to do
+
+
 def test_wrappers_reject_mis_shaped_tensors_before_any_call(C):
     """The Python binding checks every tensor's shape against the query count and the
     compiled sizes before a pointer reaches the library (host tensors: a well-shaped one
@@ -368,6 +392,18 @@ def test_wrappers_reject_mis_shaped_tensors_before_any_call(C):
         lambda: C.csa2_full_select(bm, torch.zeros((n, 7), dtype=i32), nv,
                                    torch.zeros((n, 2048), dtype=i32), q, w, kc, ks,
                                    torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_full_select_mxfp4(bm, torch.zeros(bm.shape, dtype=i32), nv,
+                                         torch.zeros((n, 2048), dtype=i32), q, w,
+                                         torch.zeros((100, 64), dtype=u8),
+                                         torch.zeros((99, 4), dtype=u8), ks,
+                                         torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_full_select_mxfp4(bm, torch.zeros(bm.shape, dtype=i32), nv,
+                                         torch.zeros((n, 2048), dtype=i32), q, w, kc,
+                                         torch.zeros((100, 4), dtype=u8), ks,
+                                         torch.zeros((n, 512), dtype=i32)),
+        lambda: C.csa2_index_score_mxfp4(0, q, w, torch.zeros((100, 64), dtype=u8),
+                                         torch.zeros((100, 4), dtype=u8), ks, nv, sc,
+                                         block_max=bm, block_aux=torch.zeros((n, 3), dtype=i32)),
         lambda: C.csa2_index_score(0, q, w, kc, ks, nv, sc, block_max=bm,
                                    block_aux=torch.zeros((n, 3), dtype=i32)),
         lambda: C.csa2_topk(sc, torch.zeros((n, 100), dtype=i32), k=512),

@@ -158,3 +158,121 @@ def test_block_statistics_match_the_pass_scores(dev):
         others[np.arange(nb), arg] = 0
         k2 = others.max(axis=1)
         assert np.array_equal(aux_all[t, :nb] & ~np.uint64(7), (k2 + 7) & ~np.uint64(7)), t
+
+
+def _mxfp4_routes(wl, k=512):
+    """MXFP4 indexer keys: the three-call route (pool_candidates, REINDEX rescoring of the
+    candidates, Top-K among their slots), the pool route (block_pool, REINDEX over the whole
+    pool, Top-K) and the one-kernel route (csa2_full_select_mxfp4 from a Full pass that also
+    writes the block statistics) must give the same pool and Top-K bit for bit."""
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import layers
+    buf = layers.alloc_buffers(wl)
+    lay = wl.layers[0]
+    ld = buf.scores.shape[1]
+    C.csa2_index_score_mxfp4(C.FULL, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, None, buf.block_max, ld_scores=ld)
+    dev = wl.k_codes.device
+    pool_a = torch.full_like(buf.pool, -5)
+    cand = torch.full_like(buf.pool, -5)
+    idx_a = torch.full((wl.n_q, k), -5, dtype=torch.int32, device=dev)
+    C.csa2_pool_candidates(buf.block_max, wl.n_visible, pool_a, cand, n_keep=2048, k=k)
+    sc_a = torch.empty_like(buf.re_scores)
+    C.csa2_index_score_mxfp4(C.REINDEX, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, sc_a, pool_blocks=cand)
+    C.csa2_topk(sc_a, idx_a, k=k, pool_blocks=cand)
+    pool_b = torch.full_like(buf.pool, -5)
+    idx_b = torch.full_like(idx_a, -5)
+    C.csa2_block_pool(buf.block_max, wl.n_visible, pool_b, n_keep=2048)
+    C.csa2_index_score_mxfp4(C.REINDEX, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, buf.re_scores, pool_blocks=pool_b)
+    C.csa2_topk(buf.re_scores, idx_b, k=k, pool_blocks=pool_b)
+    bm_c = torch.full_like(buf.block_max, 7.0)
+    aux_c = torch.full_like(buf.block_aux, -5)
+    C.csa2_index_score_mxfp4(C.FULL, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, None, bm_c, ld_scores=ld, block_aux=aux_c)
+    pool_c = torch.full_like(buf.pool, -5)
+    idx_c = torch.full_like(idx_a, -5)
+    C.csa2_full_select_mxfp4(bm_c, aux_c, wl.n_visible, pool_c, lay.q_idx, lay.w, wl.k_codes,
+                             wl.k_scales, wl.kv_start, idx_c, n_keep=2048, k=k)
+    torch.cuda.synchronize()
+    nb = buf.block_max.shape[1]
+    for t in range(wl.n_q):
+        live = min(nb, (int(wl.n_visible[t]) + 7) // 8)
+        assert torch.equal(bm_c[t, :live], buf.block_max[t, :live]), "block maxima differ"
+    assert torch.equal(pool_a, pool_b) and torch.equal(idx_a, idx_b), "candidate route differs"
+    assert torch.equal(pool_c, pool_b), "one-kernel pool differs"
+    assert torch.equal(idx_c, idx_b), "one-kernel Top-K differs"
+    return pool_b, idx_b
+
+
+@pytest.mark.parametrize("n_visible", [
+    [40000, 17000, 3001, 16384 + 8],            # ragged, short, exactly 2048 blocks + 1
+    [1, 8, 9, 4104, 0, 520, 262144],            # tiny, empty, 513 blocks, full 256K
+    [300000],                                   # above 32,768 blocks: the quad path
+])
+def test_full_select_mxfp4_equals_the_three_calls(dev, n_visible):
+    from compressed_kv_cache_csa2_amd import synth
+    wl = synth.make_decode("fs4", len(n_visible), 0, ("full",), True, 32, n_visible=n_visible,
+                           kv_gap=5, seed=44, mxfp4=True).to(dev)
+    for k in (512, 100):
+        _mxfp4_routes(wl, k)
+
+
+def test_full_select_mxfp4_with_ties(dev):
+    """MXFP4 key rows repeated in runs of 64 (equal scores and block maxima everywhere):
+    every route breaks the ties the same way, and the selection equals the oracle's."""
+    from compressed_kv_cache_csa2_amd import synth
+    n_visible = [50000, 7777]
+    wl = synth.make_decode("fs4_ties", 2, 0, ("full",), True, 0, n_visible=n_visible, kv_gap=3,
+                           seed=45, mxfp4=True).to(dev)
+    n = wl.k_codes.shape[0]
+    wl.k_codes.copy_(wl.k_codes[::64].repeat_interleave(64, dim=0)[:n])
+    wl.k_scales.copy_(wl.k_scales[::64].repeat_interleave(64, dim=0)[:n])
+    pool, idx = _mxfp4_routes(wl)
+    lay = wl.layers[0]
+    q = lay.q_idx[0:2].view(torch.int16).cpu().numpy().view(np.uint16)
+    w = lay.w[0:2].cpu().numpy()
+    codes, scales = wl.k_codes.cpu().numpy(), wl.k_scales.cpu().numpy()
+    for t in range(2):
+        st = int(wl.kv_start[t])
+        s = O.full_scores_mxfp4(q[t], w[t], codes, scales, st, n_visible[t], n_visible[t])
+        got = idx[t].cpu().numpy()
+        kth, band = band_of(s, 512)
+        assert_set_band(got[got >= 0], O.topk_slots(s, 512), lambda p: s[p], kth, band,
+                        f"query {t}")
+
+
+def test_block_statistics_mxfp4(dev):
+    """The MXFP4 Full pass's block statistics against its own scores, as for E4M3 keys."""
+    from compressed_kv_cache_csa2_amd import csa2 as C
+    from compressed_kv_cache_csa2_amd import synth
+    n_visible = [40000, 17, 8, 0, 4099]
+    wl = synth.make_decode("bs4", len(n_visible), 0, ("full",), True, 16, n_visible=n_visible,
+                           kv_gap=3, seed=46, mxfp4=True).to(dev)
+    st = int(wl.kv_start[1])
+    wl.k_codes[st:st + 16] = wl.k_codes[st:st + 1].expand(16, -1)
+    wl.k_scales[st:st + 16] = wl.k_scales[st:st + 1].expand(16, -1)
+    lay = wl.layers[0]
+    ld = 40000
+    scores = torch.empty((len(n_visible), ld), dtype=torch.float32, device=dev)
+    bm = torch.empty((len(n_visible), ld // 8), dtype=torch.float32, device=dev)
+    aux = torch.empty((len(n_visible), ld // 8), dtype=torch.int32, device=dev)
+    C.csa2_index_score_mxfp4(C.FULL, lay.q_idx, lay.w, wl.k_codes, wl.k_scales, wl.kv_start,
+                             wl.n_visible, scores, bm, block_aux=aux)
+    torch.cuda.synchronize()
+    s_all, bm_all = scores.cpu().numpy(), bm.cpu().numpy()
+    aux_all = aux.cpu().numpy().view(np.uint32).astype(np.uint64)
+    for t, nv in enumerate(n_visible):
+        nb = (nv + 7) // 8
+        if nb == 0:
+            continue
+        s = s_all[t, :nb * 8].reshape(nb, 8)
+        keys = _key(s)
+        arg = np.argmax(keys, axis=1)
+        assert np.array_equal(bm_all[t, :nb], s[np.arange(nb), arg])
+        assert np.array_equal(aux_all[t, :nb] & 7, arg)
+        others = keys.copy()
+        others[np.arange(nb), arg] = 0
+        k2 = others.max(axis=1)
+        assert np.array_equal(aux_all[t, :nb] & ~np.uint64(7), (k2 + 7) & ~np.uint64(7)), t
