@@ -42,6 +42,7 @@ constexpr int IS_STEPS_FULL = 16;
 constexpr int IS_STEPS_REINDEX = 4;
 constexpr int IS_PREFETCH = 1;   // steps whose rows are in flight while one is multiplied
 constexpr int FULL_PF_STAGED = 2;   // the same for the Full E4M3 pass without a score row
+constexpr int RE_PF = 1;           // the same for the coalesced E4M3 Reindex pass
 
 // Indexer-key formats: E4M3 rows of 128 bytes, MXFP4 rows (64 code bytes + 4 E8M0 scale
 // bytes in a separate array) and bf16 rows of 256 bytes (the block-mean keys of the
@@ -382,6 +383,136 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_e4m3_kernel(
   }
 }
 
+
+// Reindex-mode scoring of E4M3 keys with coalesced row loads. A pool block is eight
+// consecutive cache rows (1 KiB), and a wavefront step covers 32 slots, i.e. four pool
+// blocks: load instruction i reads block i of the step whole (lane l: the 16 bytes
+// 16*(l%8) .. +15 of the block's row l/8), and the pieces go through the per-wavefront LDS
+// buffer of index_score_full_e4m3_kernel into index_score_kernel's operand layout. The
+// block ids are wavefront-uniform, so a step whose four blocks are all absent (a compacted
+// candidate list's -1 tail) loads and multiplies nothing. Conversion, products, their
+// order and the epilogue are index_score_kernel's: identical scores. Rows of PF steps are
+// in flight while a step is multiplied; scores and block maxima go out after the tile.
+template <int STEPS, int PF>
+__global__ __launch_bounds__(IS_THREADS) void index_score_reindex_e4m3_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_cache, int64_t n_entries, const int64_t* __restrict__ kv_start,
+    const int32_t* __restrict__ n_visible, const int32_t* __restrict__ pool_blocks, int n_pool,
+    float* __restrict__ scores, int64_t ld, float* __restrict__ block_max, int64_t ld_bm) {
+  static_assert(PF >= 1 && PF <= STEPS, "prefetch depth");
+  __shared__ u32x4 stage[IS_THREADS / 64][2][256];   // 8 KiB per wavefront
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int half = lane >> 5;
+  bf16x8 a[8];
+  const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+  float wr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+  const int64_t base = kv_start[t];
+  const int64_t nv = n_visible[t];
+  constexpr int TILE = (IS_THREADS / 64) * STEPS * 32;
+  const int64_t tile0 = (int64_t)blockIdx.x * TILE + (int64_t)wave * 32;
+  const bool any = nv > 0 && base >= 0 && base < n_entries;
+  // A slot has a row when its position is below lim (visible and inside the cache).
+  int64_t lim = nv;
+  if (any && n_entries - base < lim) lim = n_entries - base;
+  // Block ids of each step's four blocks (-1: absent), the same in every lane.
+  int bid[STEPS][4];
+  bool live[STEPS];
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    const int64_t pb0 = (tile0 + (int64_t)step * (IS_THREADS / 64) * 32) >> 3;
+    bool l = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t pb = pb0 + i;
+      const int b = pb < n_pool ? pool_blocks[(int64_t)t * n_pool + pb] : -1;
+      bid[step][i] = b;
+      l |= b >= 0;
+    }
+    live[step] = any && l;
+  }
+  auto slot_at = [&](int step) -> int64_t {
+    return tile0 + (int64_t)step * (IS_THREADS / 64) * 32 + n;
+  };
+  const int piece = lane & 7;
+  const int rin = lane >> 3;   // row of the block this lane loads
+  auto load_step = [&](int step, u32x4 (&g)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = bid[step][i];
+      const int64_t pos = (int64_t)b * 8 + rin;
+      const bool ok = b >= 0 && pos < lim;
+      g[i] = *reinterpret_cast<const u32x4*>(k_cache + (base + (ok ? pos : 0)) * 128 +
+                                             16 * piece);
+    }
+  };
+  u32x4 g[PF][4];
+  float sc[STEPS];
+#pragma unroll
+  for (int p0 = 0; p0 < PF; ++p0)
+    if (live[p0]) load_step(p0, g[p0]);
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    float sv = -__builtin_inff();
+    if (live[step]) {
+      u32x4* buf = stage[wave][step & 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + rin;
+        buf[r * 8 + (piece ^ (r & 7))] = g[step % PF][i];
+      }
+      if (step + PF < STEPS && live[step + PF]) load_step(step + PF, g[step % PF]);
+      // LDS operations of one wavefront complete in order; the fences keep the compiler
+      // from moving the reads above the writes.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      u32x4 raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = buf[n * 8 + ((4 * half + i) ^ (n & 7))];
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2]);
+        const u32x2 hi = e4m3x4_to_bf16x4(raw[kb >> 1][(kb & 1) * 2 + 1]);
+        const u32x4 bv = u32x4{lo.x, lo.y, hi.x, hi.y};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], __builtin_bit_cast(bf16x8, bv), acc,
+                                                      0, 0, 0);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.f);
+      part += __shfl_xor(part, 32);
+      const int j = n >> 3;
+      const int b = j == 0 ? bid[step][0] : j == 1 ? bid[step][1] : j == 2 ? bid[step][2]
+                                                                           : bid[step][3];
+      if (b >= 0 && (int64_t)b * 8 + (n & 7) < lim) sv = part;
+    } else if (step + PF < STEPS && live[step + PF]) {
+      load_step(step + PF, g[step % PF]);
+    }
+    sc[step] = sv;
+  }
+#pragma unroll
+  for (int step = 0; step < STEPS; ++step) {
+    const int64_t slot = slot_at(step);
+    const float sv = sc[step];
+    if (scores != nullptr && slot < ld && half == 0) scores[(int64_t)t * ld + slot] = sv;
+    if (block_max != nullptr) {
+      float m = sv;
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      if (half == 0 && (n & 7) == 0 && slot < ld)
+        block_max[(int64_t)t * ld_bm + (slot >> 3)] = m;
+    }
+  }
+}
 
 // Full-mode scoring of MXFP4 keys with whole rows per lane: a wavefront step covers 64
 // slots, lane l loading row l of the step (its 64 code bytes as four 16-byte loads, and its
@@ -824,7 +955,11 @@ hipError_t launch_index_score(bool reindex, int key_format, int n_q, const uint1
         wide(index_score_full_wide_fp4_kernel<false>);
     }
   } else if (reindex) {
-    go(index_score_kernel<true, KF_E4M3>);
+    constexpr int RT = (IS_THREADS / 64) * IS_STEPS_REINDEX * 32;
+    hipLaunchKernelGGL((index_score_reindex_e4m3_kernel<IS_STEPS_REINDEX, RE_PF>),
+                       dim3((unsigned)((ld + RT - 1) / RT), (unsigned)n_q), dim3(IS_THREADS), 0,
+                       stream, q_idx, w, k_cache, n_entries, kv_start, n_visible, pool_blocks,
+                       n_pool, scores, ld, block_max, ld_bm);
   } else {
     auto full = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, grid, dim3(IS_THREADS), 0, stream, q_idx, w, k_cache, n_entries,
