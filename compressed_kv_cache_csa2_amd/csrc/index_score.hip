@@ -527,6 +527,7 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_reindex_e4m3_kernel(
 // reduced as each step completes, staged in LDS and written once per workgroup; scores, if
 // asked, go out as each step ends.
 constexpr int IW_STEPS = IS_STEPS_FULL / 2;   // 64-slot steps per wavefront (same tile)
+constexpr int IW_PF = 3;                      // steps whose rows are in flight
 
 template <bool AUX>
 __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
@@ -561,8 +562,9 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
     return (row >= 0 && row < n_entries) ? row : -1;
   };
   const bool any = nv > 0 && base >= 0 && base < n_entries;
-  u32x4 buf[2][4];
-  uint32_t sbuf[2];
+  constexpr int NB = IW_PF + 1;
+  u32x4 buf[NB][4];
+  uint32_t sbuf[NB];
   auto load_step = [&](int step, u32x4 (&raw)[4], uint32_t& sw) {
     const int64_t r = row_at(step);
     const int64_t rr = r >= 0 ? r : base;
@@ -574,13 +576,17 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
   float sc[AUX ? 1 : IW_STEPS];
   __shared__ float bm_st[AUX ? TILE / 8 : 1];       // block maxima of the tile
   __shared__ uint32_t aux_st[AUX ? TILE / 8 : 1];   // block statistics of the tile
-  if (any) load_step(0, buf[0], sbuf[0]);
+  if (any) {
+#pragma unroll
+    for (int p0 = 0; p0 < IW_PF; ++p0) load_step(p0, buf[p0], sbuf[p0]);
+  }
 #pragma unroll
   for (int step = 0; step < IW_STEPS; ++step) {
     float sv = -__builtin_inff();
     if (any) {
-      if (step + 1 < IW_STEPS) load_step(step + 1, buf[(step + 1) & 1], sbuf[(step + 1) & 1]);
-      u32x4 (&raw)[4] = buf[step & 1];
+      if (step + IW_PF < IW_STEPS)
+        load_step(step + IW_PF, buf[(step + IW_PF) % NB], sbuf[(step + IW_PF) % NB]);
+      u32x4 (&raw)[4] = buf[step % NB];
       // code dword d holds channels 8d .. 8d+7; dwords kb and 8+kb swap half-waves
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
@@ -589,7 +595,7 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
         raw[d >> 2][d & 3] = s[0];
         raw[2 + (d >> 2)][d & 3] = s[1];
       }
-      const auto ss = __builtin_amdgcn_permlane32_swap(sbuf[step & 1], sbuf[step & 1], false, false);
+      const auto ss = __builtin_amdgcn_permlane32_swap(sbuf[step % NB], sbuf[step % NB], false, false);
       const uint32_t scw[2] = {ss[0], ss[1]};
       float part[2];
 #pragma unroll
