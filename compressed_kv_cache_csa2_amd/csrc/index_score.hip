@@ -674,10 +674,11 @@ __global__ __launch_bounds__(IS_THREADS) void index_score_full_wide_fp4_kernel(
 // SS steps of 32 rows are staged per LDS buffer (double-buffered), so one barrier serves
 // SS * QW * 8 products per wavefront. Wavefront w loads and converts k-blocks
 // 2w and 2w+1 of every row of a stage (bytes 64*half + 16*w .. +15 of row n), one stage
-// ahead of its use. Per step the QW product chains are issued k-block by k-block and their
-// epilogues follow, so one query's ReLU and head sum run while the other queries' products
-// are in the matrix core. Products, their order and the epilogue arithmetic are those of
-// the per-query kernel: identical scores.
+// ahead of its use. Per step the QW product chains are issued one query after another, each
+// together with the previous query's epilogue (ReLU, head weights, head sum, stores), so
+// the epilogues run while products are in the matrix core; scheduling fences keep the
+// compiler from merging the chains back into one interleaved block. Products, their order
+// and the epilogue arithmetic are those of the per-query kernel: identical scores.
 constexpr int SQ2_QW = 3;
 constexpr int SQ2_SS = 4;
 constexpr int SQ2_QT = (IS_THREADS / 64) * SQ2_QW;
@@ -704,7 +705,7 @@ __device__ __forceinline__ float group8_max(float v) {
   return __int_as_float(k);
 }
 
-template <int QW, int SS>
+template <int QW, int SS, bool BM>
 __global__ __launch_bounds__(IS_THREADS, 2) void index_score_shared2_kernel(
     int n_q, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_cache, int64_t n_entries, int64_t kv_start,
@@ -776,7 +777,7 @@ __global__ __launch_bounds__(IS_THREADS, 2) void index_score_shared2_kernel(
     const uint32_t rel = (uint32_t)(slot - tile0);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), rs_s[j],
                                           half == 0 ? 4u * rel : DROP, 0, 0);
-    if (block_max != nullptr) {
+    if constexpr (BM) {
       const float m = group8_max(sv);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_b[j],
                                             (half == 0 && (n & 7) == 0) ? 4u * (rel >> 3) : DROP,
@@ -833,24 +834,30 @@ __global__ __launch_bounds__(IS_THREADS, 2) void index_score_shared2_kernel(
       f32x16 acc[QW];
 #pragma unroll
       for (int j = 0; j < QW; ++j) acc[j] = f32x16{};
-      // k-block-major: each operand read feeds QW products, and the chains interleave
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int j = 0; j < QW; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kb], __builtin_bit_cast(bf16x8, b[kb]),
-                                                           acc[j], 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < QW; ++j) {
-        // the same accumulation order as the per-query kernel: identical scores
+      // ReLU, head weights and head sum of query j, in the per-query kernel's order
+      // (identical scores), then the stores.
+      auto epilogue = [&](int j) {
         float part = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) part += wr[j][r] * relu1(acc[j][r]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                          __float_as_uint(part), false, false);
         part += __uint_as_float(half ? sw[0] : sw[1]);   // the other half-wave's heads
-        store(j, slot, (row_ok && rel < nvq_rel[j]) ? part : -__builtin_inff());
+        store(j, slot, (row_ok & (rel < nvq_rel[j])) ? part : -__builtin_inff());
+      };
+      // Query-major: query j's eight products run while query j-1's epilogue is computed
+      // (scheduling fences keep each query's products and the previous epilogue together),
+      // so only the last query's epilogue runs with no product of this wavefront in flight.
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kb], __builtin_bit_cast(bf16x8, b[kb]),
+                                                           acc[j], 0, 0, 0);
+        if (j > 0) epilogue(j - 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      epilogue(QW - 1);
     }
   }
 }
@@ -924,7 +931,9 @@ hipError_t launch_index_score_shared(int n_q, const uint16_t* q_idx, const float
                                      const int32_t* n_visible, float* scores, int64_t ld,
                                      float* block_max, int64_t ld_bm, hipStream_t stream) {
   dim3 grid((unsigned)((ld + SQ2_TILE - 1) / SQ2_TILE), (unsigned)((n_q + SQ2_QT - 1) / SQ2_QT));
-  hipLaunchKernelGGL((index_score_shared2_kernel<SQ2_QW, SQ2_SS>), grid, dim3(IS_THREADS), 0,
+  auto kernel = block_max != nullptr ? index_score_shared2_kernel<SQ2_QW, SQ2_SS, true>
+                                     : index_score_shared2_kernel<SQ2_QW, SQ2_SS, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(IS_THREADS), 0,
                      stream, n_q, q_idx, w, k_cache, n_entries, kv_start, n_visible, scores, ld,
                      block_max, ld_bm);
   return hipGetLastError();
