@@ -870,3 +870,63 @@ def test_reindex_layer_composition_and_full_query_identity():
     assert np.array_equal(short["idx"], np.arange(m))
     assert np.array_equal(re_short["idx"], np.arange(m))
     assert np.array_equal(re_short["out"], short["out"])
+
+
+# ------------------------------------------------------------------ helpers pinned directly
+
+def test_f32_to_bf16_bits_rounds_to_nearest_even():
+    """f32_to_bf16_bits against torch's float32 -> bfloat16 conversion (an independent
+    implementation of the same rounding) over random finite bit patterns, and the ties by
+    hand: a float32 exactly halfway between two bf16 values goes to the one whose last
+    mantissa bit is 0."""
+    rng = np.random.default_rng(61)
+    bits = rng.integers(0, 1 << 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    # keep values whose rounding stays finite (the largest bf16 is below float32's maximum)
+    x = x[np.abs(x) < np.float32(3.38e38)]
+    assert np.array_equal(O.f32_to_bf16_bits(x), _bf16_bits_torch(x))
+    one = 0x3F80
+    cases = [
+        (1.0 + 2.0 ** -8, one),                      # halfway, lower neighbour even
+        (1.0 + 2.0 ** -7 + 2.0 ** -8, one + 2),      # halfway, upper neighbour even
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, one + 1),     # just above halfway
+        (1.0 + 2.0 ** -8 - 2.0 ** -20, one),         # just below halfway
+        (-(1.0 + 2.0 ** -8), 0x8000 | one),          # sign carried through
+        (2.0 ** -130, 0x0008),                       # a bf16 subnormal, exact
+        (2.0 ** -140, 0x0000),                       # below half the smallest bf16 subnormal
+    ]
+    for v, want in cases:
+        got = int(O.f32_to_bf16_bits(np.array([v], np.float32))[0])
+        assert got == want, (v, hex(got), hex(want))
+
+
+def test_gather_attention_entries_brute_force():
+    """The attended set of a tiny query, built entry by entry from the scalar decoders:
+    main rows at the valid selected positions (in their order, -1 skipped, duplicates kept)
+    with c[i] = E2M1(code i) * E4M3(scale[i // 16]), code 2m the low nibble of byte m, then
+    the window rows as plain E4M3 values, at most 128 of them."""
+    rng = np.random.default_rng(62)
+    n_rows, kv_start = 12, 3
+    kv_fp4 = rng.integers(0, 256, size=(n_rows + kv_start, 256)).astype(np.uint8)
+    kv_scale = rng.integers(0, 0x7F, size=(n_rows + kv_start, 32)).astype(np.uint8)
+    window = rng.integers(0, 0x7F, size=(140, 512)).astype(np.uint8)
+    window ^= (rng.integers(0, 2, size=window.shape).astype(np.uint8) << 7)
+    topk = np.array([4, -1, 0, 11, 4, -1], np.int32)
+
+    def main_row(r):
+        out = np.empty(512)
+        for i in range(512):
+            byte = int(kv_fp4[r, i // 2])
+            code = byte & 0xF if i % 2 == 0 else byte >> 4
+            out[i] = O.e2m1_value(code) * O.e4m3_value(int(kv_scale[r, i // 16]))
+        return out
+
+    for swa_start, n_swa, n_win in ((5, 3, 3), (0, 0, 0), (2, 200, 128)):
+        got = O.gather_attention_entries(topk, kv_fp4, kv_scale, kv_start, window, swa_start,
+                                         n_swa)
+        want = [main_row(kv_start + p) for p in topk if p >= 0]
+        want += [np.array([O.e4m3_value(int(b)) for b in window[swa_start + j]])
+                 for j in range(n_win)]
+        assert got.shape == (4 + n_win, 512)
+        assert np.array_equal(got, np.array(want))
