@@ -775,29 +775,42 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_kernel(
       for (int64_t s = (nb - 1) * 8; s < n; ++s) tail_max = fmaxf(tail_max, row[s]);
     }
     const BlockSrc bsrc{block_max + (int64_t)t * ld_bm, tail ? nb - 1 : -1, tail_max};
-    KeyRow<BlockSrc, 32, true> brow(bsrc, nb);
-    uint32_t count;
-    Interval iv;
-    row_prepare(brow, count, iv, sh);
-    uint32_t thr = 0;   // keep blocks with key >= thr (0: every valid block)
-    bool fits = count <= (uint32_t)CAND_BLOCKS_CAP;
-    if (count > kk) {
-      locate(brow, kk, iv, 0u, (uint32_t)CAND_BLOCKS_CAP, sh);
-      thr = iv.A;
-      fits = true;
-    }
-    // Collect candidate blocks (ascending); count them to check the cap.
-    const uint32_t n_cand = emit_ordered(brow, thr == 0u ? 0u : thr - 1u, 0u, sh,
-                                         [&](uint32_t rank, uint32_t b) {
-                                           if (rank < CAND_BLOCKS_CAP) sh.cblocks[rank] = (int32_t)b;
-                                         });
-    __syncthreads();
-    if (fits && n_cand <= (uint32_t)CAND_BLOCKS_CAP) {
-      const CandSrc csrc{row, sh.cblocks, n};
-      kept = select_any(csrc, (int64_t)n_cand * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
-        if (rank < kk) sh.obuf[rank] = map((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
-      });
-      done = true;
+    auto phase_a = [&](auto& brow) {
+      uint32_t count;
+      Interval iv;
+      row_prepare(brow, count, iv, sh);
+      uint32_t thr = 0;   // keep blocks with key >= thr (0: every valid block)
+      bool fits = count <= (uint32_t)CAND_BLOCKS_CAP;
+      if (count > kk) {
+        locate(brow, kk, iv, 0u, (uint32_t)CAND_BLOCKS_CAP, sh);
+        thr = iv.A;
+        fits = true;
+      }
+      // Collect candidate blocks (ascending); count them to check the cap.
+      const uint32_t n_cand = emit_ordered(brow, thr == 0u ? 0u : thr - 1u, 0u, sh,
+                                           [&](uint32_t rank, uint32_t b) {
+                                             if (rank < CAND_BLOCKS_CAP) sh.cblocks[rank] = (int32_t)b;
+                                           });
+      __syncthreads();
+      if (fits && n_cand <= (uint32_t)CAND_BLOCKS_CAP) {
+        const CandSrc csrc{row, sh.cblocks, n};
+        kept = select_any(csrc, (int64_t)n_cand * 8, kk, sh, [&](uint32_t rank, uint32_t i) {
+          if (rank < kk) sh.obuf[rank] = map((uint32_t)sh.cblocks[i >> 3] * 8u + (i & 7u));
+        });
+        done = true;
+      }
+    };
+    // The block maxima stay in registers while they fit (every pass of the threshold
+    // search reads them again); longer rows are reloaded segment by segment.
+    if (nb <= (int64_t)SEL_THREADS * 16) {
+      KeyRow<BlockSrc, 16, false> brow(bsrc, nb);
+      phase_a(brow);
+    } else if (nb <= (int64_t)SEL_THREADS * 32) {
+      KeyRow<BlockSrc, 32, false> brow(bsrc, nb);
+      phase_a(brow);
+    } else {
+      KeyRow<BlockSrc, 32, true> brow(bsrc, nb);
+      phase_a(brow);
     }
   }
   if (!done) {
