@@ -46,6 +46,8 @@ constexpr int BINS_PER_THREAD = NBINS / SEL_THREADS;
 constexpr int CAND_BLOCKS_CAP = 2048;
 constexpr int OUT_CAP = 2048;          // the largest k / n_keep
 constexpr int LIST_CAP = 256;          // an interval this small is finished by counting
+constexpr int FS_EARLY_WAVES = 4;      // full_select_kernel: wavefronts that load the indexer
+                                       // operands before the candidate scan
 constexpr uint32_t ALL_TIES = 0xFFFFFFFFu;
 constexpr uint32_t INF_KEY = 0xFF800000u;   // float_key(+inf)
 
@@ -994,14 +996,22 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
   const uint32_t kept = select_pool(bm_row, nb, n_keep, sh, (uint32_t)k + 1u, &t2, pflag);
   __syncthreads();
 
-  // Indexer operands (issued here, after the pool selection's registers are free).
+  // Indexer operands. Rescoring steps go to wavefronts 0, 1, 2, ... in turn and are usually
+  // few (a handful of blocks), so only the first FS_EARLY_WAVES wavefronts load the operands
+  // here, after the pool selection's registers are free (every wavefront loading them costs
+  // the next phase thousands of cycles of memory-instruction issue); a later wavefront loads
+  // them when it is given a step.
   bf16x8 a[8];
-  const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
   float wr[16];
+  auto load_operands = [&]() {
+    const uint16_t* qrow = q_idx + ((int64_t)t * 32 + n) * 128 + 64 * half;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+    for (int kb = 0; kb < 8; ++kb) a[kb] = *reinterpret_cast<const bf16x8*>(qrow + 8 * kb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[r] = w[(int64_t)t * 32 + 8 * (r >> 2) + 4 * half + (r & 3)];
+  };
+  const bool early = wave < FS_EARLY_WAVES;   // uniform
+  if (early) load_operands();
 
   // The pool goes out. Its candidate blocks (those whose key reaches t2, or all of it when
   // the first pass gave no threshold) stay in LDS in ascending order with their block
@@ -1126,6 +1136,7 @@ __global__ __launch_bounds__(SEL_THREADS) void full_select_kernel(
     }
   };
   if (any) {
+    if (!early && wave < n_steps) load_operands();
     u32x4 cur[4], nxt[4];
     int32_t bc = wave < n_steps ? block_of(wave) : -1;
     int64_t rc = row_of(bc);
