@@ -403,14 +403,16 @@ __device__ __forceinline__ uint32_t emit_ordered(Row& row, uint32_t tau, uint32_
   for (int seg = 0; seg < row.segs(); ++seg) {
     row.load(seg);
     uint32_t take = 0, eq_mask = 0;
+    if (n_eq == ALL_TIES) {   // uniform; tau is then a valid key, so key >= tau excludes key 0
 #pragma unroll
-    for (int r = 0; r < R; ++r) take |= (uint32_t)(row.keys[r] > tau) << r;   // tau >= 0
-    if (n_eq != 0u) {   // tau is then a valid key, so key == tau excludes key 0
+      for (int r = 0; r < R; ++r) take |= (uint32_t)(row.keys[r] >= tau) << r;
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) take |= (uint32_t)(row.keys[r] > tau) << r;   // tau >= 0
+    }
+    if (split_ties) {   // uniform: keep the first n_eq ties of the row in index order
 #pragma unroll
       for (int r = 0; r < R; ++r) eq_mask |= (uint32_t)(row.keys[r] == tau) << r;
-    }
-    if (n_eq == ALL_TIES) take |= eq_mask;
-    if (split_ties) {   // uniform: keep the first n_eq ties of the row in index order
       const uint32_t eq_total = group_offsets<NG>(eq_mask, sh);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
