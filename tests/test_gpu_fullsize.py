@@ -1,6 +1,8 @@
-"""The named workloads at their full sizes on the GPU, checked against the oracle on
-sampled queries (every query for the 32K and 256K decodes). decode_256k runs exactly as bench.py
-times it: the layer stack captured in a HIP graph on a side stream and replayed."""
+"""The named workloads at their full sizes on the GPU, checked against the oracle: every
+query of the decodes (32K, 256K, 256K with MXFP4 indexer keys or the block-mean filter, 1M),
+and queries spread over the whole batch for the prefill and the encoder. decode_256k runs
+exactly as bench.py times it: the layer stack captured in a HIP graph on a side stream and
+replayed."""
 import sys
 import time
 
@@ -70,17 +72,16 @@ def test_decode_256k_every_query_as_benched(dev):
     torch.cuda.empty_cache()
 
 
-def test_decode_256k_mxfp4_sampled(dev):
+def test_decode_256k_mxfp4_every_query(dev):
     wl, buf = _run("decode_256k_mxfp4", dev)
-    queries = [0, wl.n_q - 1]
-    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    assert _check(wl, buf, range(wl.n_q)) == wl.n_q * len(wl.layers)
     del wl, buf
     torch.cuda.empty_cache()
 
 
-def test_decode_256k_block_mean_filter_sampled(dev):
+def test_decode_256k_block_mean_filter_every_query(dev):
     """decode_256k through the block-mean filter (every indexer layer's pool captured),
-    checked on sampled queries; the whole stack then reproduces the same indices."""
+    checked on every query; the whole stack then reproduces the same indices."""
     from compressed_kv_cache_csa2_amd import layers, synth
     from tests.parity_util import check_query_hisa
     wl = synth.make_workload("decode_256k", device=dev)
@@ -98,33 +99,35 @@ def test_decode_256k_block_mean_filter_sampled(dev):
     assert torch.equal(buf.idx, idx)
     _log("decode_256k block-mean filter: stack ran")
     n = 0
-    for t in (0, wl.n_q - 1):
+    queries = range(wl.n_q)
+    for t in queries:
         n += check_query_hisa(wl, idx, pools, buf.out, t)
         _log(f"decode_256k block-mean filter: query {t} checked")
-    assert n == 2 * len(wl.layers)
+    assert n == len(queries) * len(wl.layers)
     del wl, buf, means
     torch.cuda.empty_cache()
 
 
-def test_prefill_128k_m2_sampled(dev):
+def test_prefill_128k_m2_spread(dev):
+    """The first two queries, the last, and one in every 32 between (their visible
+    contexts grow along the chunk)."""
     wl, buf = _run("prefill_128k_m2", dev)
-    queries = [0, 1, 2047, wl.n_q - 1]
+    queries = sorted({0, 1, wl.n_q - 1} | set(range(31, wl.n_q, 32)))
     assert _check(wl, buf, queries) == len(queries)
     del wl, buf
     torch.cuda.empty_cache()
 
 
-def test_encoder_128k_m2_sampled(dev):
+def test_encoder_128k_m2_spread(dev):
     wl, buf = _run("encoder_128k_m2", dev)
-    queries = [0, wl.n_q - 1]
+    queries = sorted({wl.n_q - 1} | set(range(0, wl.n_q, 64)))
     assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
     del wl, buf
     torch.cuda.empty_cache()
 
 
-def test_decode_1m_sampled(dev):
+def test_decode_1m_every_query(dev):
     wl, buf = _run("decode_1m", dev)
-    queries = [0, wl.n_q - 1]
-    assert _check(wl, buf, queries) == len(queries) * len(wl.layers)
+    assert _check(wl, buf, range(wl.n_q)) == wl.n_q * len(wl.layers)
     del wl, buf
     torch.cuda.empty_cache()
